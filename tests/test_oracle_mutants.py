@@ -1,0 +1,91 @@
+"""The pins must catch plausible mistakes in the oracle.
+
+Each case plants one mistake in a copy of the oracle's C source (on the CPU),
+builds it, routes the oracle's Python wrapper through that build and runs the
+pin tests: at least one pin must fail.  A mutant that survives means the pins
+leave that part of the oracle unchecked.
+"""
+import subprocess
+from pathlib import Path
+
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+import test_oracle_stats as stats
+
+SRC = Path(oracle.__file__).resolve().parent / "spec_verify_ref.c"
+
+# (name, original text, planted mistake)
+MUTANTS = [
+    ("strict_acceptance", "accept = (u <= alpha);", "accept = (u < alpha);"),
+    ("ratio_inverted", "exp(fmin(0.0, log_px - log_qx))", "exp(fmin(0.0, log_qx - log_px))"),
+    ("no_positive_part", "W[v] = fmax(P[v] - Q[v], 0.0);", "W[v] = P[v] - Q[v];"),
+    ("residual_sign", "W[v] = fmax(P[v] - Q[v], 0.0);", "W[v] = fmax(Q[v] - P[v], 0.0);"),
+    ("correct_from_p", "int y = ref_invcdf(W, V,", "int y = ref_invcdf(P, V,"),
+    ("bonus_from_draft_row", "load_row(J->target, J->dtype, trow0 + G, V, zt);",
+     "load_row(J->draft, J->dtype, drow0 + G - 1, V, zt);"),
+    ("draft_row_shifted", "load_row(J->draft, J->dtype, drow0 + i, V, zd);\n    double logZp",
+     "load_row(J->draft, J->dtype, drow0 + (i + 1) % G, V, zd);\n    double logZp"),
+    ("cdf_closed_interval", "if (F > t) {", "if (F >= t) {"),
+    ("temperature_multiplies", "double e = kept ? exp(z[v] / T - m) : 0.0;",
+     "double e = kept ? exp(z[v] * T - m * T * T) : 0.0;"),
+    ("topk_drops_ties", "int kept = (z[v] >= tau) && (z[v] > -INFINITY);\n    double e",
+     "int kept = (z[v] > tau || v == 0) && (z[v] > -INFINITY);\n    double e"),
+    ("topk_off_by_one", "double tau = tmp[k - 1];", "double tau = tmp[k];"),
+    ("argmax_highest_index", "if (z[v] > z[a]) a = v;", "if (z[v] >= z[a]) a = v;"),
+    ("uniform_closed", "float u = J->u_accept[(size_t)b * G + i];\n      if (!(u >= 0.0f && u < 1.0f))",
+     "float u = J->u_accept[(size_t)b * G + i];\n      if (!(u >= 0.0f && u <= 1.0f))"),
+    ("no_p_support_test", "accept = 0; /* p(x) = 0", "accept = (u <= 1.0); /* p(x) = 0"),
+    ("greedy_keeps_draft_token", "out[i] = a; /* greedy correction", "out[i] = x[i]; /* greedy correction"),
+    ("no_padding", "fill_tokens(out + i + 1, G - i, -1);\n    return;\n  }\n\n  /* Every",
+     "return;\n  }\n\n  /* Every"),
+    ("accept_len_off_by_one", "J->accepted_len[b] = i;\n    fill_tokens(out + i + 1, G - i, -1);\n    return;\n  }\n\n  /* Every",
+     "J->accepted_len[b] = i + 1;\n    fill_tokens(out + i + 1, G - i, -1);\n    return;\n  }\n\n  /* Every"),
+]
+
+PIN_TESTS = [
+    lambda: pins.test_four_token_table_alpha_and_acceptance_mass(),
+    lambda: pins.test_four_token_table_residual(),
+    lambda: pins.test_three_token_example(),
+    lambda: pins.test_single_position_reference_checks(),
+    lambda: pins.test_acceptance_boundary_is_inclusive(),
+    lambda: pins.test_check_row_of_tiny_chain_config(),
+    lambda: pins.test_policy_matches_scipy_softmax("bf16", 0.7),
+    lambda: pins.test_topk_threshold_and_kept_set(5),
+    lambda: pins.test_topk_brute_force_tiny(),
+    lambda: pins.test_argmax_lowest_index(),
+    lambda: pins.test_invcdf_matches_searchsorted(),
+    lambda: pins.test_invcdf_boundary_distance(),
+    lambda: pins.test_p_equals_q_accepts_every_legal_token("f32", 0),
+    lambda: pins.test_disjoint_supports_correct_from_p(),
+    lambda: pins.test_chain_structure("f32", 1.0, 0),
+    lambda: pins.test_chain_structure("f32", 0.0, 0),
+    lambda: pins.test_g_zero_is_plain_target_sampling(),
+    lambda: pins.test_row_error_codes("u_one", oracle.ERR_UNIFORM),
+    lambda: stats.test_monte_carlo_law_matches_target(1.0, 0),
+    lambda: stats.test_expected_tokens_constant_rate(0.6, 4),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_kill_mutant(name, old, new, tmp_path):
+    src = SRC.read_text()
+    assert src.count(old) == 1, f"mutation site for {name} not unique"
+    mutated = tmp_path / f"{name}.c"
+    mutated.write_text(src.replace(old, new))
+    lib = tmp_path / f"lib_{name}.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-o", str(lib),
+                    str(mutated), "-lm"], check=True)
+    saved = oracle._swap_library(lib)
+    failures = 0
+    try:
+        for t in PIN_TESTS:
+            try:
+                t()
+            except Exception:  # an assertion (or any error) means the mistake was seen
+                failures += 1
+                break
+    finally:
+        oracle._lib = saved
+    assert failures, f"no pin detects the planted mistake '{name}'"
