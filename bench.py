@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Benchmark of batched speculative-sampling verification on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3]
+
+One step = one spec_verify call (the whole path: normaliser + acceptance scan +
+correction / bonus draw) over one batch of synthetic logits already resident in
+HBM.  Steps cycle through R distinct input sets (>= 1 GiB in total) so that the
+256 MB Infinity Cache cannot serve a repeated batch.  Prints one JSON line.
+
+Metric: verified draft positions per second (B*G per call; every submitted draft
+position is verified, including those after the first rejection, since all are
+processed in parallel), with the achieved HBM bandwidth of the dominant kernel
+against the 8 TB/s peak.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+import numpy as np
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "verified draft positions/sec and achieved HBM GB/s (% of peak) at B=64,V=128k"
+PEAK_HBM_GBS = 8000.0
+COUNTERS = ROOT / "profiles" / "k_norm_zipf_bf16_b64_counters.json"
+SOURCE = ROOT / "rejection_sampling_verify_02_amd" / "csrc" / "spec_verify.hip"
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime that torch has already loaded."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n: int) -> list[int]:
+        out = []
+        for _ in range(n):
+            ev = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(ev.value)
+        return out
+
+    def record(self, ev: int, stream: int) -> None:
+        self.hip.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream))
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        self.hip.hipEventSynchronize(ctypes.c_void_p(b))
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def destroy(self, evs) -> None:
+        for e in evs:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def make_sets(cid: int, n_sets: int, dev):
+    """R input sets of one workload on the device; draft tokens drawn by the library itself
+    (each draft row is its own G = 0 call: X ~ q by inverse CDF with the draft uniforms)."""
+    import torch
+    import rejection_sampling_verify_02_amd as sv
+    from rejection_sampling_verify_02_amd import workloads as wl
+
+    sets, host = [], []
+    for s in range(n_sets):
+        t0 = time.time()
+        raw = wl.make_config(cid, seed=wl.CONFIGS[cid].seed + 1000 * s)
+        cfg = raw.cfg
+        B, G, V = raw.B, raw.G, raw.V
+
+        def dev_t(a):
+            t = torch.from_numpy(np.ascontiguousarray(a))
+            return (t.view(torch.bfloat16) if a.dtype == np.uint16 else t).to(dev)
+
+        target, draft = dev_t(raw.target), dev_t(raw.draft)
+        if cfg.temperature == 0:
+            raise SystemExit("the benchmark times the sampling workloads (greedy is a parity case)")
+        if len(raw.disjoint_rows):
+            raise SystemExit("workload 5 needs the oracle to finish its recipe; it is a parity case")
+        drows = draft.reshape(B * G, 1, V)
+        u_draft = dev_t(raw.u_draft.reshape(B * G))
+        _, tok = sv.spec_verify(drows, None, None, None, u_draft, cfg.temperature, cfg.top_k)
+        tokens = tok.reshape(B, G).contiguous()
+        fixed = torch.from_numpy(raw.fixed_tokens).to(dev)
+        tokens = torch.where(fixed >= 0, fixed, tokens)
+        sets.append(dict(target=target, draft=draft, tokens=tokens, u_accept=dev_t(raw.u_accept),
+                         u_sample=dev_t(raw.u_sample)))
+        host.append(dict(target=raw.target, draft=raw.draft, u_accept=raw.u_accept,
+                         u_sample=raw.u_sample))
+        log(f"[bench] input set {s + 1}/{n_sets} ready ({time.time() - t0:.1f} s)")
+    torch.cuda.synchronize(dev)
+    for s, h in zip(sets, host):
+        h["tokens"] = s["tokens"].cpu().numpy()
+    return sets, host
+
+
+def counters_traffic(kernel_source_sha: str):
+    """HBM bytes per k_norm launch from the committed rocprofv3 counter summary, or None
+    when the summary is missing or was taken on a different kernel source."""
+    if not COUNTERS.exists():
+        return None, "no counter summary"
+    c = json.loads(COUNTERS.read_text())
+    if c.get("source_sha256") != kernel_source_sha:
+        return None, "kernel changed since the counters were taken"
+    return float(c["traffic_bytes_per_launch"]), c.get("note", "")
+
+
+def cpu_baseline(host_sets, cfg, seconds: float):
+    """The oracle (fp64, unmodified) on the host cores over whole input sets, for a bounded
+    wall time; its value is verified positions per second like the GPU's."""
+    import oracle
+
+    oracle._load()
+    threads = oracle.default_threads()
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        h = host_sets[calls % len(host_sets)]
+        oracle.spec_verify_ref(h["target"], h["draft"], h["tokens"], h["u_accept"], h["u_sample"],
+                               cfg.temperature, cfg.top_k, nthreads=threads)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    B, G = host_sets[0]["tokens"].shape
+    return {"value": B * G * calls / el, "unit": "positions/s", "cores": threads, "kind": "oracle",
+            "sample": f"{calls} full calls (B={B}, G={G}) over {min(calls, len(host_sets))} input sets, "
+                      f"{el:.1f} s; the oracle stops reading each sequence at its first rejection"}
+
+
+def copy_probe(nbytes: int, reps: int) -> None:
+    """A plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").uniform_()
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3])
+    ap.add_argument("--sets", type=int, default=0, help="input sets to rotate (default: >= 1 GiB)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stage-events", action="store_true",
+                    help="time the loop without per-kernel events")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain copy of BYTES (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        return 2
+    if args.copy_probe:
+        copy_probe(args.copy_probe, 10)
+        return 0
+
+    import torch
+    import rejection_sampling_verify_02_amd as sv
+    from rejection_sampling_verify_02_amd import workloads as wl
+
+    sv.load_library()  # raises if the HIP library is not built
+    dev = torch.device("cuda:0")
+    cfg = wl.CONFIGS[args.config]
+    B, G, V = cfg.B, cfg.G, cfg.V
+    esz = 2 if cfg.dtype == "bf16" else 4
+    rows = B * (2 * G + 1)
+    alg_bytes = rows * V * esz  # one read of every logit the result depends on
+    n_sets = args.sets or max(2, -(-(1 << 30) // alg_bytes))
+    log(f"[bench] workload {cfg.name}: B={B} G={G} V={V} {cfg.dtype}, {alg_bytes / 1e6:.2f} MB per call, "
+        f"{n_sets} input sets")
+    sets, host = make_sets(args.config, n_sets, dev)
+
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    dtc = sv.SV_BF16 if cfg.dtype == "bf16" else sv.SV_F32
+    plan = sv.sv_launch_plan(B, G, V, dtc, cfg.temperature, cfg.top_k)
+    nl = len(plan)
+    ws = sv.Workspace()
+    acc = torch.empty((B,), dtype=torch.int32, device=dev)
+    out = torch.empty((B, G + 1), dtype=torch.int32, device=dev)
+    hev = HipEvents()
+
+    def call(i, events=None):
+        s = sets[i % n_sets]
+        return sv.spec_verify(s["target"], s["draft"], s["tokens"], s["u_accept"], s["u_sample"],
+                              cfg.temperature, cfg.top_k, workspace=ws, stream=stream,
+                              out=(acc, out), events=events)
+
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize(dev)
+    log(f"[bench] warmup done ({args.warmup} calls)")
+
+    K = args.steps
+    stage = None if args.no_stage_events else [hev.create(nl + 1) for _ in range(K)]
+    loop_ev = hev.create(2)
+    emitted = torch.zeros((), dtype=torch.int64, device=dev)
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    hev.record(loop_ev[0], stream)
+    for i in range(K):
+        call(args.warmup + i, None if stage is None else stage[i])
+    hev.record(loop_ev[1], stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    gpu_ms = hev.elapsed_ms(loop_ev[0], loop_ev[1])
+    log(f"[bench] timed {K} calls: wall {wall * 1e3:.2f} ms, events {gpu_ms:.2f} ms")
+
+    per_kernel = {}
+    if stage is not None:
+        durs = np.array([[hev.elapsed_ms(ev[j], ev[j + 1]) for j in range(nl)] for ev in stage])
+        for j, name in enumerate(plan):
+            per_kernel[f"{j}:{name}"] = float(np.mean(durs[:, j]) * 1e3)
+        for ev in stage:
+            hev.destroy(ev)
+    hev.destroy(loop_ev)
+
+    # emitted tokens for the last call of each set (accepted + 1 per valid sequence)
+    for s_i in range(min(n_sets, K)):
+        call(s_i)
+        emitted += (acc.clamp(min=-1) + 1).sum()
+    torch.cuda.synchronize(dev)
+    mean_emitted = float(emitted.item()) / min(n_sets, K)
+
+    ms = wall * 1e3 / K
+    t_call = ms / 1e3
+    positions = B * G
+    value = positions / t_call
+    knorm_us = per_kernel.get("0:k_norm") or next((v for k, v in per_kernel.items() if k.endswith(":k_norm")), None)
+    sha = hashlib.sha256(SOURCE.read_bytes()).hexdigest()
+    traffic, tnote = counters_traffic(sha)
+    roof = None
+    if knorm_us:
+        achieved = alg_bytes / (knorm_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "kernel": "k_norm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": traffic, "algorithmic_bytes": alg_bytes,
+                "avg_launch_us": round(knorm_us, 3)}
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": "positions/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": cfg.name, "B": B, "G": G, "V": V, "logits": cfg.dtype,
+                   "temperature": cfg.temperature, "top_k": cfg.top_k, "input_sets": n_sets,
+                   "set_bytes": alg_bytes},
+        "call_GBs": round(alg_bytes / t_call / 1e9, 1),
+        "call_frac_of_peak": round(alg_bytes / t_call / 1e9 / PEAK_HBM_GBS, 4),
+        "emitted_tokens_per_s": round(mean_emitted / t_call, 1),
+        "mean_accepted_plus_one": round(mean_emitted / B, 4),
+        "gpu_event_ms_per_step": round(gpu_ms / K, 5),
+        "per_kernel_us": {k: round(v, 3) for k, v in per_kernel.items()},
+        "roofline": roof,
+        "traffic_note": tnote,
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] oracle CPU baseline (~{args.cpu_seconds:.0f} s)")
+        res["cpu_baseline"] = cpu_baseline(host, cfg, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,136 @@
+/*
+ * spec_verify.h -- C ABI of the MI355X (gfx950) library for batched
+ * speculative-sampling verification.
+ *
+ * The operation ("Speculative Decoding 的朴素思想", sections "一次 sampling 怎么执行",
+ * "Correction 为什么用正残差" and "从单个 token 接到一段 draft"; "推测解码：接受规则、
+ * 状态与收益边界", section "两模型精确采样"):
+ *
+ *   For each sequence b, a draft model proposed G tokens x_1..x_G, drawing x_i from
+ *   q_i; the target gave G+1 distributions p_1..p_{G+1} for the same prefixes.  Both
+ *   come in as logits and pass through the same policy (temperature T, optional
+ *   top-k).  Positions are tested in order: x_i is accepted when U_i <= min(1,
+ *   p_i(x_i)/q_i(x_i)) (and p_i(x_i) > 0).  At the first rejected position j a
+ *   correction token is drawn from norm([p_j - q_j]_+) by inverse CDF with u_sample[b];
+ *   if all G are accepted a bonus token is drawn from p_{G+1} the same way.  With
+ *   T == 0 the policy is greedy (argmax, lowest index on ties): acceptance is exact
+ *   match with the target argmax, and the correction / bonus is the target argmax
+ *   ("tannlonggtaoo" note, section "Greedy Sampling").
+ *
+ * Conventions shared by every entry point:
+ *   - All array arguments are DEVICE pointers to row-major, contiguous memory on the
+ *     current HIP device; sizes are element counts.  Logit rows must be aligned to
+ *     their element size (2 bytes for bf16, 4 for f32); rows whose byte length is a
+ *     multiple of 16 with 16-byte-aligned bases take the vector-load path.
+ *   - The caller owns every buffer.  The library allocates nothing, keeps no state
+ *     between calls, and never synchronises: work is enqueued on `stream` (a
+ *     hipStream_t; NULL is the default stream) and results are valid in stream order.
+ *   - On any status other than SV_OK nothing has been enqueued and outputs are
+ *     untouched.  Row-level data problems are not statuses: they are reported per
+ *     sequence in accepted_len (codes below).
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+
+typedef enum {
+  SV_OK = 0,
+  SV_ERR_NULL = 1,        /* a required pointer is NULL                                  */
+  SV_ERR_SHAPE = 2,       /* B < 1, G < 0, V < 1, or a size that overflows the launch    */
+  SV_ERR_DTYPE = 3,       /* dtype is not SV_F32 / SV_BF16                               */
+  SV_ERR_TEMPERATURE = 4, /* temperature negative, NaN or infinite                       */
+  SV_ERR_WORKSPACE = 5,   /* workspace smaller than sv_workspace_bytes() or misaligned    */
+  SV_ERR_ALIGN = 6,       /* a logit pointer is not aligned to its element size           */
+  SV_ERR_LAUNCH = 7       /* the HIP runtime refused a kernel launch                       */
+} sv_status;
+
+/* Row-level codes written into accepted_len[b] instead of a length; the whole row of
+ * out_tokens is then -1.  They follow the checks of the single-position reference
+ * ("推测解码：接受规则、状态与收益边界", section "单位置接受 reference"), tested in this
+ * order over all G positions of the sequence, whether or not a position is reached: */
+#define SV_ROW_BAD_TOKEN (-1)   /* a drafted token lies outside [0, V)                      */
+#define SV_ROW_Q_ZERO (-2)      /* sampling: q_i(x_i) = 0 (logit -inf or cut by top-k), so   */
+                                /* the draft cannot have proposed x_i                        */
+#define SV_ROW_BAD_LOGITS (-3)  /* a row of the sequence holds NaN or +inf, or no finite logit */
+#define SV_ROW_BAD_UNIFORM (-4) /* sampling: a u_accept or u_sample value outside [0, 1)    */
+
+/* Bytes of device workspace spec_verify needs for these arguments (0 never occurs). */
+size_t sv_workspace_bytes(int32_t B, int32_t G, int32_t V, sv_dtype dtype, float temperature,
+                          int32_t top_k);
+
+/* Leading bytes of the workspace (self-resetting counters) that must be zero when a call
+ * with these arguments starts; 0 for arguments spec_verify would reject.  A completed
+ * call leaves exactly its own leading sv_workspace_zero_bytes(...) bytes at zero and may
+ * overwrite everything after them.  So one zero-fill serves any number of calls with
+ * the same arguments; before a call whose zero prefix is longer than the previous call's
+ * on the same workspace, zero the longer prefix again (a fill kernel on the same stream
+ * suffices).  Calls that share a workspace must not overlap in time. */
+size_t sv_workspace_zero_bytes(int32_t B, int32_t G, int32_t V, sv_dtype dtype,
+                               float temperature, int32_t top_k);
+
+/* Batched verification.
+ *   target_logits [B, G+1, V] dtype   target logits for positions 1..G+1
+ *   draft_logits  [B, G,   V] dtype   draft logits for positions 1..G; not read (may be
+ *                                     NULL) when temperature == 0 or G == 0
+ *   draft_tokens  [B, G]  int32       drafted tokens; may be NULL when G == 0
+ *   u_accept      [B, G]  float32     acceptance uniforms in [0,1); not read when
+ *                                     temperature == 0 (may then be NULL)
+ *   u_sample      [B]     float32     one uniform per sequence for the correction or
+ *                                     bonus draw; not read when temperature == 0
+ *   temperature   T > 0 samples from softmax(z/T); T == 0 is greedy
+ *   top_k         0 < top_k < V keeps every logit >= the top_k-th largest raw logit
+ *                 (ties kept) in target and draft rows alike; otherwise no cut.
+ *                 Ignored when temperature == 0.
+ *   accepted_len  [B]     int32 out   0..G, or a negative row code
+ *   out_tokens    [B, G+1] int32 out  accepted drafts, then the correction / bonus
+ *                                     token at index accepted_len, then -1
+ *   row_stats     [B, 2G+1, 2] float32 out, nullable: for each target row (0..G) then
+ *                 draft row (0..G-1) of a sequence, (m, S) with m + ln S the natural
+ *                 log-partition of the kept logits divided by T.  Not written when
+ *                 temperature == 0.
+ *   workspace     device buffer of at least sv_workspace_bytes(...) bytes, 256-byte
+ *                 aligned, whose first sv_workspace_zero_bytes(...) bytes are zero.
+ */
+sv_status spec_verify(const void *target_logits, const void *draft_logits, sv_dtype dtype,
+                      const int32_t *draft_tokens, const float *u_accept, const float *u_sample,
+                      int32_t B, int32_t G, int32_t V, float temperature, int32_t top_k,
+                      int32_t *accepted_len, int32_t *out_tokens, float *row_stats,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* spec_verify that also records HIP events around its kernels, for per-kernel timing.
+ * events: array of n_events hipEvent_t handles (created by the caller, with timing
+ * enabled); events[0] is recorded before the first launch and events[i] after the
+ * i-th launch.  *n_launched receives the number of kernels enqueued (at most
+ * SV_MAX_LAUNCHES); if n_events < *n_launched + 1 the trailing events are not
+ * recorded.  Otherwise identical to spec_verify. */
+#define SV_MAX_LAUNCHES 8
+sv_status spec_verify_timed(const void *target_logits, const void *draft_logits, sv_dtype dtype,
+                            const int32_t *draft_tokens, const float *u_accept,
+                            const float *u_sample, int32_t B, int32_t G, int32_t V,
+                            float temperature, int32_t top_k, int32_t *accepted_len,
+                            int32_t *out_tokens, float *row_stats, void *workspace,
+                            size_t workspace_bytes, void *stream, void *const *events,
+                            int32_t n_events, int32_t *n_launched);
+
+/* Names of the kernels spec_verify would launch for these arguments, in launch order,
+ * as one string separated by ';' (static storage).  Used to match per-kernel timings
+ * with profiler output. */
+const char *sv_launch_plan(int32_t B, int32_t G, int32_t V, sv_dtype dtype, float temperature,
+                           int32_t top_k);
+
+/* Human-readable text of a status (static storage). */
+const char *sv_status_string(sv_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

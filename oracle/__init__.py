@@ -94,7 +94,7 @@ def _swap_library(path):
 
 def default_threads() -> int:
     try:
-        return max(1, len(os.sched_getaffinity(0)))
+        return max(1, min(16, len(os.sched_getaffinity(0))))
     except AttributeError:  # pragma: no cover
         return max(1, os.cpu_count() or 1)
 

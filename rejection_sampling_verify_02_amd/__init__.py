@@ -1,1 +1,219 @@
-"""MI355X-native batched speculative-sampling verification (placeholder; binding follows)."""
+"""MI355X-native batched speculative-sampling verification.
+
+Thin binding over the C ABI in ``include/spec_verify.h`` (library
+``libspec_verify.so`` built in-tree by ``rejection_sampling_verify_02_amd.build``).
+Every step of the verification runs in the library's HIP kernels; this module
+only checks and marshals arguments.  PyTorch is used for device memory and the
+current stream.  There is no CPU fallback: if the library is not built, every
+call raises.
+
+    acc, out = spec_verify(target_logits, draft_logits, draft_tokens,
+                           u_accept, u_sample, temperature, top_k)
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+_PKG = Path(__file__).resolve().parent
+LIB_PATH = _PKG / "libspec_verify.so"
+
+SV_F32, SV_BF16 = 0, 1
+ROW_BAD_TOKEN, ROW_Q_ZERO, ROW_BAD_LOGITS, ROW_BAD_UNIFORM = -1, -2, -3, -4
+MAX_LAUNCHES = 8
+
+_STATUS = {0: "SV_OK", 1: "SV_ERR_NULL", 2: "SV_ERR_SHAPE", 3: "SV_ERR_DTYPE",
+           4: "SV_ERR_TEMPERATURE", 5: "SV_ERR_WORKSPACE", 6: "SV_ERR_ALIGN", 7: "SV_ERR_LAUNCH"}
+
+EXPORTED = ("spec_verify", "spec_verify_timed", "sv_workspace_bytes", "sv_workspace_zero_bytes",
+            "sv_status_string", "sv_launch_plan")
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, status: int, text: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {text}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: Path | str | None = None) -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = Path(path) if path else LIB_PATH
+    if not p.exists():
+        raise RuntimeError(f"{p} is not built; run `python -m rejection_sampling_verify_02_amd.build`")
+    lib = ctypes.CDLL(str(p))
+    V, I32, F32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    common = [V, V, I32, V, V, V, I32, I32, I32, F32, I32, V, V, V, V, SZ, V]
+    lib.spec_verify.argtypes = common
+    lib.spec_verify.restype = I32
+    lib.spec_verify_timed.argtypes = common + [V, I32, V]
+    lib.spec_verify_timed.restype = I32
+    lib.sv_workspace_bytes.argtypes = [I32, I32, I32, I32, F32, I32]
+    lib.sv_workspace_bytes.restype = SZ
+    lib.sv_workspace_zero_bytes.argtypes = [I32, I32, I32, I32, F32, I32]
+    lib.sv_workspace_zero_bytes.restype = SZ
+    lib.sv_status_string.argtypes = [I32]
+    lib.sv_status_string.restype = ctypes.c_char_p
+    lib.sv_launch_plan.argtypes = [I32, I32, I32, I32, F32, I32]
+    lib.sv_launch_plan.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def sv_status_string(status: int) -> str:
+    return load_library().sv_status_string(int(status)).decode()
+
+
+def sv_workspace_bytes(B: int, G: int, V: int, dtype: int, temperature: float, top_k: int = 0) -> int:
+    return int(load_library().sv_workspace_bytes(B, G, V, dtype, float(temperature), int(top_k)))
+
+
+def sv_workspace_zero_bytes(B: int, G: int, V: int, dtype: int, temperature: float,
+                            top_k: int = 0) -> int:
+    return int(load_library().sv_workspace_zero_bytes(B, G, V, dtype, float(temperature), int(top_k)))
+
+
+def sv_launch_plan(B: int, G: int, V: int, dtype: int, temperature: float, top_k: int = 0) -> list[str]:
+    s = load_library().sv_launch_plan(B, G, V, dtype, float(temperature), int(top_k)).decode()
+    return s.split(";")
+
+
+# ------------------------------------------------------------------ workspace
+
+class Workspace:
+    """A device buffer for the library's scratch data, one per device, grown on demand.
+
+    The library keeps self-resetting counters in the first
+    ``sv_workspace_zero_bytes(...)`` bytes: they must be zero when a call starts, a
+    call leaves exactly its own prefix at zero, and it may overwrite what lies after
+    it.  This class remembers how long the zero prefix is and, before a call that
+    needs a longer one, zeroes it with a fill kernel on the call's stream.  Calls
+    sharing a workspace must be ordered on one stream.
+    """
+
+    def __init__(self):
+        self._buf = {}
+        self._zero = {}
+
+    def get(self, nbytes: int, zero_bytes: int, device, stream: int):
+        import torch
+        key = torch.device(device).index
+        buf = self._buf.get(key)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+            torch.cuda.synchronize(device)
+            self._buf[key] = buf
+            self._zero[key] = buf.numel()
+        if zero_bytes > self._zero[key]:
+            with torch.cuda.stream(torch.cuda.ExternalStream(stream, device=device)):
+                buf[:zero_bytes].zero_()
+            self._zero[key] = zero_bytes
+        return buf
+
+    def called(self, device, zero_bytes: int) -> None:
+        """Record that a call with this zero prefix was enqueued."""
+        import torch
+        self._zero[torch.device(device).index] = zero_bytes
+
+
+_default_ws = Workspace()
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return SV_BF16
+    if t.dtype == torch.float32:
+        return SV_F32
+    raise TypeError(f"logits must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, shape, dtype, device):
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def spec_verify(target_logits, draft_logits, draft_tokens, u_accept, u_sample, temperature: float,
+                top_k: int = 0, *, row_stats: bool = False, workspace: Workspace | None = None,
+                stream=None, out=None, events=None):
+    """Batched verification on the GPU (see include/spec_verify.h for the semantics).
+
+    target_logits [B, G+1, V] and draft_logits [B, G, V] (bfloat16 or float32, same dtype),
+    draft_tokens [B, G] int32, u_accept [B, G] and u_sample [B] float32; with
+    temperature 0 the draft logits and uniforms may be None.
+
+    Returns (accepted_len [B], out_tokens [B, G+1]) int32 tensors, plus row_stats
+    [B, 2G+1, 2] float32 when requested.  ``out`` may supply preallocated output
+    tensors (accepted_len, out_tokens[, row_stats]).  ``events`` (a list of raw
+    hipEvent_t handles) records per-kernel timing events; the number of kernels
+    launched is then returned as the last element.
+    """
+    import torch
+    lib = load_library()
+    dev = target_logits.device
+    if dev.type != "cuda":
+        raise ValueError("target_logits must be a device tensor")
+    dt = _dtype_code(target_logits)
+    if target_logits.dim() != 3:
+        raise ValueError("target_logits must be [B, G+1, V]")
+    B, G1, V = target_logits.shape
+    G = G1 - 1
+    _check(target_logits, "target_logits", (B, G + 1, V), target_logits.dtype, dev)
+    greedy = float(temperature) == 0.0
+    if draft_tokens is not None and draft_tokens.dtype == torch.int64:
+        draft_tokens = draft_tokens.to(torch.int32)
+    if G > 0 or draft_tokens is not None:
+        _check(draft_tokens, "draft_tokens", (B, G), torch.int32, dev)
+    if not greedy:
+        if G > 0 or draft_logits is not None:
+            _check(draft_logits, "draft_logits", (B, G, V), target_logits.dtype, dev)
+        if G > 0 or u_accept is not None:
+            _check(u_accept, "u_accept", (B, G), torch.float32, dev)
+        _check(u_sample, "u_sample", (B,), torch.float32, dev)
+    else:
+        draft_logits = u_accept = u_sample = None
+    if out is not None:
+        acc, toks = out[0], out[1]
+        stats = out[2] if row_stats else None
+    else:
+        acc = torch.empty((B,), dtype=torch.int32, device=dev)
+        toks = torch.empty((B, G + 1), dtype=torch.int32, device=dev)
+        stats = torch.empty((B, 2 * G + 1, 2), dtype=torch.float32, device=dev) if row_stats else None
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    nbytes = int(lib.sv_workspace_bytes(B, G, V, dt, float(temperature), int(top_k)))
+    zbytes = int(lib.sv_workspace_zero_bytes(B, G, V, dt, float(temperature), int(top_k)))
+    wso = workspace or _default_ws
+    ws = wso.get(nbytes, zbytes, dev, stream)
+    args = [_ptr(target_logits), _ptr(draft_logits), dt, _ptr(draft_tokens), _ptr(u_accept),
+            _ptr(u_sample), B, G, V, float(temperature), int(top_k), _ptr(acc), _ptr(toks),
+            _ptr(stats), _ptr(ws), ws.numel(), ctypes.c_void_p(stream)]
+    if events is None:
+        st = lib.spec_verify(*args)
+        nl = None
+    else:
+        arr = (ctypes.c_void_p * len(events))(*events)
+        n = ctypes.c_int32(0)
+        st = lib.spec_verify_timed(*args, arr, len(events), ctypes.byref(n))
+        nl = n.value
+    if st != 0:
+        raise SpecVerifyError(st, sv_status_string(st))
+    wso.called(dev, zbytes)
+    res = (acc, toks) + ((stats,) if row_stats else ())
+    return res + ((nl,) if events is not None else ())

@@ -1,0 +1,114 @@
+"""The C-ABI library loads, exports every declared symbol, and validates host
+arguments without touching a GPU (every status below is decided before any HIP call)."""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+import rejection_sampling_verify_02_amd as sv
+
+ROOT = Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "spec_verify.h"
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not sv.LIB_PATH.exists():
+        from rejection_sampling_verify_02_amd import build
+        build.build()
+    return sv.load_library()
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"if", "sizeof"})
+
+
+def test_header_declares_expected_entry_points():
+    assert set(declared_functions()) == set(sv.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    nm = __import__("subprocess").run(["nm", "-D", "--defined-only", str(sv.LIB_PATH)],
+                                      capture_output=True, text=True, check=True).stdout
+    for name in declared_functions():
+        assert re.search(rf"\bT {name}$", nm, re.M), f"{name} not exported with C linkage"
+
+
+def test_status_strings(lib):
+    for code in range(8):
+        s = sv.sv_status_string(code)
+        assert s and s != "unknown status"
+    assert sv.sv_status_string(99) == "unknown status"
+
+
+def test_launch_plan(lib):
+    assert sv.sv_launch_plan(64, 4, 128256, sv.SV_BF16, 1.0, 0) == ["k_norm", "k_sample"]
+    assert sv.sv_launch_plan(256, 7, 152064, sv.SV_BF16, 0.0, 50) == ["k_argmax"]
+    assert sv.sv_launch_plan(128, 6, 128256, sv.SV_BF16, 0.8, 50) == \
+        ["k_topk_digit", "k_topk_digit", "k_norm", "k_sample"]
+    assert len(sv.sv_launch_plan(8, 5, 32000, sv.SV_F32, 0.7, 5)) == 6
+    assert sv.sv_launch_plan(8, 5, 32000, sv.SV_F32, 0.7, 32000) == ["k_norm", "k_sample"]
+
+
+def test_workspace_bytes(lib):
+    small = sv.sv_workspace_bytes(1, 1, 32, sv.SV_F32, 1.0, 0)
+    big = sv.sv_workspace_bytes(64, 4, 128256, sv.SV_BF16, 1.0, 0)
+    topk = sv.sv_workspace_bytes(64, 4, 128256, sv.SV_BF16, 1.0, 50)
+    assert 0 < small < big < topk
+    assert big % 256 == 0
+    # 576 rows x 16 chunks of (float + double) partials at least
+    assert big >= 576 * 16 * 12
+
+
+V_, I_, F_, Z_ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+FAKE = 1 << 20  # never dereferenced: argument checks reject before any launch
+
+
+def call(lib, **kw):
+    a = dict(target=FAKE, draft=FAKE, dt=sv.SV_BF16, tokens=FAKE, ua=FAKE, us=FAKE, B=4, G=3,
+             V=1024, T=1.0, k=0, acc=FAKE, out=FAKE, stats=None, ws=FAKE, nbytes=1 << 30,
+             stream=None)
+    a.update(kw)
+    return lib.spec_verify(V_(a["target"]), V_(a["draft"]), a["dt"], V_(a["tokens"]), V_(a["ua"]),
+                           V_(a["us"]), a["B"], a["G"], a["V"], F_(a["T"]), a["k"], V_(a["acc"]),
+                           V_(a["out"]), V_(a["stats"]), V_(a["ws"]), Z_(a["nbytes"]),
+                           V_(a["stream"]))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), 2), (dict(G=-1), 2), (dict(V=0), 2),
+    (dict(dt=7), 3),
+    (dict(T=-1.0), 4), (dict(T=float("nan")), 4), (dict(T=float("inf")), 4),
+    (dict(target=None), 1), (dict(acc=None), 1), (dict(out=None), 1), (dict(ws=None), 1),
+    (dict(tokens=None), 1), (dict(draft=None), 1), (dict(ua=None), 1), (dict(us=None), 1),
+    (dict(nbytes=100), 5), (dict(ws=FAKE + 64), 5),
+    (dict(target=FAKE + 1), 6), (dict(draft=FAKE + 2, dt=sv.SV_F32), 6),
+])
+def test_host_argument_errors(lib, kw, status):
+    assert call(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw", [
+    dict(T=0.0, draft=None, ua=None, us=None),   # greedy reads no draft logits or uniforms
+    dict(G=0, tokens=None, draft=None, ua=None),  # no drafts: only u_sample is read
+])
+def test_optional_pointers_are_optional(lib, kw):
+    # with a too-small workspace the call stops at the workspace check, after the
+    # pointer checks have passed
+    assert call(lib, nbytes=16, **kw) == 5
+
+
+def test_zero_prefix_covers_only_the_counters(lib):
+    for args in [(1, 1, 32, sv.SV_F32, 1.0, 0), (64, 4, 128256, sv.SV_BF16, 1.0, 0),
+                 (256, 7, 152064, sv.SV_BF16, 0.0, 0), (128, 6, 128256, sv.SV_BF16, 0.8, 50)]:
+        z, n = sv.sv_workspace_zero_bytes(*args), sv.sv_workspace_bytes(*args)
+        assert 0 < z < n and z % 256 == 0
+    assert sv.sv_workspace_zero_bytes(0, 1, 32, sv.SV_F32, 1.0, 0) == 0
+    # more rows need more counters
+    assert sv.sv_workspace_zero_bytes(64, 4, 128256, sv.SV_BF16, 1.0, 0) > \
+        sv.sv_workspace_zero_bytes(8, 5, 32000, sv.SV_F32, 0.7, 0)

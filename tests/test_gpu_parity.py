@@ -1,0 +1,247 @@
+"""GPU parity: the HIP library against the fp64 oracle on the same seeded inputs.
+
+All calls go through the C ABI (ctypes binding).  Sizes: the five workloads at full
+size (the configuration the benchmark times), plus small shapes that span several
+chunks with a ragged tail, unaligned rows, and the method's degenerate cases.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import parity
+from rejection_sampling_verify_02_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import rejection_sampling_verify_02_amd as sv
+    sv.load_library()
+    return torch.device("cuda:0")
+
+
+def check(res, what):
+    print(f"[parity] {what}: {res.summary()} acc_hist={res.acc_hist}", flush=True)
+    assert not res.failures, f"{what}: {res.failures[:5]}"
+
+
+# ------------------------------------------------------------------ the five workloads
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_workload_full_size(dev, cid):
+    raw = wl.make_config(cid)
+    cfg = raw.cfg
+    res, gpu, ref = parity.run_both(raw, cfg.temperature, cfg.top_k, dev)
+    check(res, f"config {cid} ({cfg.name})")
+    if cid == 1:  # the worked two-token row: reject, correction 0
+        assert gpu[0][-1] == 0 and gpu[1][-1].tolist() == [0, -1, -1, -1, -1]
+    if cid == 4:
+        assert res.exact == res.n  # greedy: bit-exact
+    if cid == 5:
+        acc = gpu[0]
+        g1 = 43
+        assert np.all(acc[:g1] == cfg.G)            # draft == target: every draft accepted
+        assert np.all(acc[raw.disjoint_rows] == 0)  # disjoint support: first position rejects
+    # boundary cases must stay rare
+    assert res.boundary <= max(1, res.n // 100)
+
+
+# ------------------------------------------------------------------ shapes and edges
+
+SHAPES = [
+    # B, G, V, dtype, T, k
+    (8, 3, 20000, "bf16", 1.0, 0),     # three chunks, partial last chunk, vector path
+    (8, 3, 20001, "bf16", 1.0, 0),     # odd V: element-wise path
+    (8, 3, 9000, "f32", 0.7, 0),
+    (8, 3, 9003, "f32", 0.7, 0),
+    (6, 2, 17, "f32", 1.0, 0),         # V smaller than one wave's vectors
+    (5, 4, 1, "bf16", 1.0, 0),         # a single token
+    (16, 0, 5000, "bf16", 1.0, 0),     # no drafts: plain draw from p_1
+    (7, 6, 70000, "bf16", 0.05, 0),    # very low temperature
+    (7, 6, 70000, "bf16", 5.0, 0),     # very high temperature
+    (300, 2, 64, "bf16", 1.0, 0),      # many short rows
+    (8, 3, 20000, "bf16", 0.8, 1),     # top-1
+    (8, 3, 20000, "bf16", 0.8, 50),
+    (8, 3, 20000, "bf16", 0.8, 19999),
+    (8, 3, 20001, "bf16", 0.8, 50),
+    (8, 3, 9003, "f32", 0.8, 7),
+    (8, 3, 9000, "f32", 1.2, 4095),
+]
+
+
+@pytest.mark.parametrize("B,G,V,dtype,T,k", SHAPES)
+def test_shapes(dev, B, G, V, dtype, T, k):
+    raw = wl.make_random(B, G, V, dtype, seed=B * 1000 + V + G, draft_noise=0.6)
+    res, _, _ = parity.run_both(raw, T, k, dev)
+    check(res, f"B={B} G={G} V={V} {dtype} T={T} k={k}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_topk_with_ties(dev, dtype):
+    """Coarse logits put many ties at the k-th value: all of them are kept."""
+    rng = np.random.default_rng(17)
+    B, G, V = 6, 3, 12000
+    raw = wl.make_random(B, G, V, dtype, seed=91)
+    zt = np.round(rng.standard_normal((B, G + 1, V)) * 2).astype(np.float32) / 2
+    zd = zt[:, :G] + np.round(rng.standard_normal((B, G, V))).astype(np.float32) / 2
+    if dtype == "bf16":
+        raw.target, raw.draft = wl.bf16_bits(zt), wl.bf16_bits(zd)
+    else:
+        raw.target, raw.draft = zt, zd.astype(np.float32)
+    for k in (1, 3, 40, 700):
+        res, _, _ = parity.run_both(raw, 0.9, k, dev)
+        check(res, f"ties {dtype} k={k}")
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 20001), ("bf16", 152064), ("f32", 9000)])
+def test_greedy_ties_lowest_index(dev, dtype, V):
+    """Greedy: exact duplicates of the maximum (and -0 vs +0) resolve to the lowest index."""
+    B, G = 24, 5
+    raw = wl.make_random(B, G, V, dtype, seed=V + 3)
+    rng = np.random.default_rng(5)
+    flat_t = raw.target.reshape(-1, V)
+    big = wl.bf16_bits(np.array([30.0], np.float32))[0] if dtype == "bf16" else np.float32(30.0)
+    for r in range(0, flat_t.shape[0], 2):
+        i1, i2 = rng.choice(V, 2, replace=False)
+        flat_t[r, i1] = flat_t[r, i2] = big
+    # a row whose maximum is zero, present as both -0 and +0
+    neg = np.uint16(0xC000) if dtype == "bf16" else np.float32(-2.0)
+    flat_t[1, :] = neg
+    flat_t[1, 7] = np.uint16(0x8000) if dtype == "bf16" else np.float32(-0.0)
+    flat_t[1, 3] = np.uint16(0x0000) if dtype == "bf16" else np.float32(0.0)
+    tokens = oracle.argmax_rows(raw.draft)
+    tokens[::3, 0] = oracle.argmax_rows(raw.target[::3, :G])[:, 0]
+    res, gpu, _ = parity.run_both(raw, 0.0, 0, dev, tokens=tokens)
+    check(res, f"greedy ties {dtype} V={V}")
+    assert res.exact == res.n
+
+
+def test_p_equals_q_accepts_everything(dev):
+    """Identical target and draft rows: alpha == 1 bitwise, every draft accepted, bonus drawn."""
+    raw = wl.make_random(32, 5, 30000, "bf16", seed=3)
+    raw.draft[:] = raw.target[:, :5]
+    res, gpu, _ = parity.run_both(raw, 1.0, 0, dev)
+    check(res, "p == q")
+    assert np.all(gpu[0] == 5)
+    raw.u_accept[:] = np.nextafter(np.float32(1), np.float32(0))
+    res, gpu, _ = parity.run_both(raw, 0.7, 20, dev)
+    check(res, "p == q, U = 1 - 2^-24, top-k")
+    assert np.all(gpu[0] == 5)
+
+
+def test_disjoint_support_correction_is_target_draw(dev):
+    """Disjoint supports: reject at position 0 and the correction is a draw from p."""
+    raw = wl.make_random(16, 3, 4096, "f32", seed=8)
+    raw.target[:, :, 2048:] = -np.inf
+    raw.draft[:, :, :2048] = -np.inf
+    res, gpu, ref = parity.run_both(raw, 1.0, 0, dev)
+    check(res, "disjoint")
+    assert np.all(gpu[0] == 0) and np.all(gpu[1][:, 0] < 2048)
+
+
+ERR_CASES = ["token_high", "token_neg", "nan_target", "nan_draft_late", "posinf", "all_neginf",
+             "u_one", "u_neg", "u_sample_one", "q_zero", "q_outside_topk"]
+
+
+@pytest.mark.parametrize("case", ERR_CASES)
+def test_row_error_codes(dev, case):
+    B, G, V = 6, 4, 3000
+    raw = wl.make_random(B, G, V, "f32", seed=44)
+    k = 10 if case == "q_outside_topk" else 0
+    tokens = parity.prepare(raw, 1.0, k)
+    b = 2
+    if case == "token_high": tokens[b, 3] = V
+    if case == "token_neg": tokens[b, 0] = -5
+    if case == "nan_target": raw.target[b, 4, 17] = np.nan
+    if case == "nan_draft_late": raw.draft[b, 3, 2999] = np.nan
+    if case == "posinf": raw.target[b, 1, 5] = np.inf
+    if case == "all_neginf": raw.draft[b, 2, :] = -np.inf
+    if case == "u_one": raw.u_accept[b, 2] = 1.0
+    if case == "u_neg": raw.u_accept[b, 0] = -0.5
+    if case == "u_sample_one": raw.u_sample[b] = 1.0
+    if case == "q_zero": raw.draft[b, 1, tokens[b, 1]] = -np.inf
+    if case == "q_outside_topk":
+        order = np.argsort(raw.draft[b, 2])
+        tokens[b, 2] = order[0]  # the smallest draft logit is never in the top 10
+    res, gpu, ref = parity.run_both(raw, 1.0, k, dev, tokens=tokens)
+    check(res, f"row error {case}")
+    assert ref[0][b] < 0 and gpu[0][b] == ref[0][b]
+    others = [i for i in range(B) if i != b]
+    assert np.all(gpu[0][others] >= 0)
+
+
+def test_workspace_shape_changes(dev):
+    """One workspace across calls whose counter prefix grows and shrinks: every call still
+    matches the oracle (a longer prefix is zeroed again before the call that needs it)."""
+    import rejection_sampling_verify_02_amd as sv
+    ws = sv.Workspace()
+    shapes = [(2, 4, 32, "f32"), (8, 5, 3000, "f32"), (64, 4, 9000, "bf16"), (3, 1, 100, "bf16"),
+              (96, 3, 5000, "bf16"), (8, 5, 3000, "f32")]
+    for i, (B, G, V, dt) in enumerate(shapes):
+        raw = wl.make_random(B, G, V, dt, seed=700 + i)
+        tok = parity.prepare(raw, 1.0, 0)
+        acc_r, out_r, diag = oracle.spec_verify_ref(raw.target, raw.draft, tok, raw.u_accept,
+                                                    raw.u_sample, 1.0, 0, with_diagnostics=True)
+        args = [parity.to_device(a, dev) for a in (raw.target, raw.draft, tok, raw.u_accept, raw.u_sample)]
+        acc, out = sv.spec_verify(*args, 1.0, 0, workspace=ws)
+        res = parity.compare(tok, V, 1.0, acc.cpu().numpy(), out.cpu().numpy(), acc_r, out_r, diag)
+        check(res, f"workspace reuse step {i} B={B} G={G} V={V}")
+
+
+def test_repeat_calls_are_deterministic_and_counters_reset(dev):
+    """Many calls of changing shapes on one workspace: identical results every time."""
+    import torch
+    import rejection_sampling_verify_02_amd as sv
+    cases = []
+    for i, (B, G, V, dt) in enumerate([(4, 3, 5000, "bf16"), (9, 1, 20001, "bf16"), (3, 5, 777, "f32")]):
+        raw = wl.make_random(B, G, V, dt, seed=600 + i)
+        tok = parity.prepare(raw, 1.0, 0)
+        args = [parity.to_device(a, dev) for a in (raw.target, raw.draft, tok, raw.u_accept, raw.u_sample)]
+        cases.append(args)
+    ws = sv.Workspace()
+    first = [None] * len(cases)
+    for rep in range(40):
+        for ci, args in enumerate(cases):
+            acc, out, st = sv.spec_verify(*args, 1.0, 0 if ci != 1 else 30, row_stats=True, workspace=ws)
+            got = (acc.cpu().numpy(), out.cpu().numpy(), st.cpu().numpy())
+            if first[ci] is None:
+                first[ci] = got
+            else:
+                for g, f in zip(got, first[ci]):
+                    assert np.array_equal(g, f, equal_nan=True)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("T,k", [(1.0, 0), (0.7, 2)])
+def test_gpu_output_law_matches_target(dev, T, k):
+    """Monte Carlo through the GPU path (V = 4, G = 3): chi-square of the first emitted
+    token against the target's (processed) distribution."""
+    import scipy.stats
+    import test_oracle_stats as st
+    rng = np.random.default_rng(400 + k)
+    Pp, zp = st.policy_probs(st.P_TAB, T, k)
+    _, zq = st.policy_probs(st.Q_TAB, T, k)
+    n, G = 100_000, 3
+    last = np.zeros(n, np.int64)
+    x = np.empty((n, G), np.int32)
+    trows = np.empty((n, G + 1, 4), np.float32)
+    drows = np.empty((n, G, 4), np.float32)
+    for i in range(G):
+        drows[:, i], trows[:, i] = zq[last], zp[last]
+        x[:, i] = oracle.sample_rows(drows[:, i], rng.random(n, dtype=np.float32), T, k)
+        last = x[:, i]
+    trows[:, G] = zp[last]
+    raw = wl.Raw(wl.CONFIGS[1], trows, drows, np.zeros((n, G), np.float32),
+                 rng.random((n, G), dtype=np.float32), rng.random(n, dtype=np.float32),
+                 np.full((n, G), -1, np.int32))
+    res, gpu, _ = parity.run_both(raw, T, k, dev, tokens=x, stats=False)
+    check(res, f"law T={T} k={k}")
+    y1 = gpu[1][:, 0]
+    c1 = np.bincount(y1, minlength=4)
+    sup = Pp[0] > 0
+    assert np.all(c1[~sup] == 0)
+    assert scipy.stats.chisquare(c1[sup], n * Pp[0][sup]).pvalue > 1e-3
