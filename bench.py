@@ -219,7 +219,8 @@ def main() -> int:
     log(f"[bench] warmup done ({args.warmup} calls)")
 
     K = args.steps
-    stage = None if args.no_stage_events else [hev.create(nl + 1) for _ in range(K)]
+    # one (start, stop) event pair per kernel and step, attached to the dispatches themselves
+    stage = None if args.no_stage_events else [hev.create(2 * nl) for _ in range(K)]
     loop_ev = hev.create(2)
     emitted = torch.zeros((), dtype=torch.int64, device=dev)
     torch.cuda.synchronize(dev)
@@ -235,7 +236,7 @@ def main() -> int:
 
     per_kernel = {}
     if stage is not None:
-        durs = np.array([[hev.elapsed_ms(ev[j], ev[j + 1]) for j in range(nl)] for ev in stage])
+        durs = np.array([[hev.elapsed_ms(ev[2 * j], ev[2 * j + 1]) for j in range(nl)] for ev in stage])
         for j, name in enumerate(plan):
             per_kernel[f"{j}:{name}"] = float(np.mean(durs[:, j]) * 1e3)
         for ev in stage:
@@ -253,7 +254,7 @@ def main() -> int:
     t_call = ms / 1e3
     positions = B * G
     value = positions / t_call
-    knorm_us = per_kernel.get("0:k_norm") or next((v for k, v in per_kernel.items() if k.endswith(":k_norm")), None)
+    knorm_us = next((v for k, v in per_kernel.items() if k.endswith(":k_norm")), None)
     sha = hashlib.sha256(SOURCE.read_bytes()).hexdigest()
     traffic, tnote = counters_traffic(sha)
     roof = None

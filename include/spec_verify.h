@@ -105,12 +105,13 @@ sv_status spec_verify(const void *target_logits, const void *draft_logits, sv_dt
                       int32_t *accepted_len, int32_t *out_tokens, float *row_stats,
                       void *workspace, size_t workspace_bytes, void *stream);
 
-/* spec_verify that also records HIP events around its kernels, for per-kernel timing.
+/* spec_verify that also times each of its kernels with HIP events.
  * events: array of n_events hipEvent_t handles (created by the caller, with timing
- * enabled); events[0] is recorded before the first launch and events[i] after the
- * i-th launch.  *n_launched receives the number of kernels enqueued (at most
- * SV_MAX_LAUNCHES); if n_events < *n_launched + 1 the trailing events are not
- * recorded.  Otherwise identical to spec_verify. */
+ * enabled); kernel i is launched with events[2i] as its start event and events[2i+1]
+ * as its stop event (hipExtLaunchKernel), so the pair brackets that dispatch alone.
+ * *n_launched receives the number of kernels enqueued (at most SV_MAX_LAUNCHES);
+ * kernels beyond n_events / 2 are launched untimed.  Otherwise identical to
+ * spec_verify. */
 #define SV_MAX_LAUNCHES 8
 sv_status spec_verify_timed(const void *target_logits, const void *draft_logits, sv_dtype dtype,
                             const int32_t *draft_tokens, const float *u_accept,

@@ -161,8 +161,8 @@ def spec_verify(target_logits, draft_logits, draft_tokens, u_accept, u_sample, t
     Returns (accepted_len [B], out_tokens [B, G+1]) int32 tensors, plus row_stats
     [B, 2G+1, 2] float32 when requested.  ``out`` may supply preallocated output
     tensors (accepted_len, out_tokens[, row_stats]).  ``events`` (a list of raw
-    hipEvent_t handles) records per-kernel timing events; the number of kernels
-    launched is then returned as the last element.
+    hipEvent_t handles, two per kernel: start and stop of that dispatch) times each
+    kernel; the number of kernels launched is then returned as the last element.
     """
     import torch
     lib = load_library()

@@ -7,32 +7,35 @@
 // first rejection draws a correction from norm([p - q]_+), an all-accept round draws a
 // bonus from the target's next distribution, both by inverse CDF.
 //
-// How it is laid out on the GPU.  Every logit row is cut into chunks of
-// CHUNK_VECS 16-byte vectors (8192 bf16 / 4096 f32 values); one 256-thread workgroup
-// (four wave64s) streams one chunk.  The work is HBM-bound streaming with one exp per
-// element, so there is no MFMA: the design goal is coalesced 128-bit loads, few VALU
-// operations per element, and no second pass over the bulk of the data.
+// How it is laid out on the GPU.  Every logit row is cut into chunks of CHUNK_VECS
+// 16-byte vectors (32 KiB: 16384 bf16 / 8192 f32 values); one 256-thread workgroup
+// (four wave64s) streams one chunk with non-temporal 128-bit loads, all issued before
+// any is used.  The work is HBM-bound streaming with one exp per element, so there is
+// no MFMA: the goals are memory-level parallelism, few VALU operations per element, and
+// no second pass over the bulk of the data.
 //
 //   k_topk_digit  (only with top-k)  radix select of the k-th largest raw logit per row,
 //                 one 8-bit digit per launch (2 launches for bf16, 4 for f32), LDS
 //                 histograms per chunk, the last chunk of a row picks the digit.
-//   k_norm        per chunk: max and sum of 2^(z*log2(e)/T - offset) (one v_exp_f32 per
-//                 element); the last chunk of a row combines the chunk partials into
-//                 the row's log-partition; the last row of a sequence runs the
-//                 acceptance scan (first rejection, row / token / uniform checks) and
-//                 leaves a job (reject at j, or bonus) for the second kernel.
-//   k_argmax      greedy (T == 0) counterpart of k_norm over the target rows only.
-//   k_sample      per chunk of a rejecting sequence: mass of [p_j - q_j]_+; the last
-//                 chunk chooses the chunk / 64-vector segment / lane / element where the
-//                 cumulative mass passes u*Z.  Bonus sequences choose the chunk from the
-//                 first kernel's partial sums and re-read only that chunk.
+//   k_norm        per chunk of every row: block max m_c and sum of
+//                 2^(z*log2(e)/T - m_c*log2(e)/T), one v_exp_f32 per element.  Then only
+//                 wave 0 stays: it publishes the chunk partial; the last chunk of a row
+//                 combines the row's partials into its log-partition; the last row of a
+//                 sequence runs the acceptance scan (first rejection; token / row /
+//                 uniform / support checks) and leaves the sequence's job.
+//   k_sample      per chunk of every sequence: for a rejection at j, the chunk's masses
+//                 of [p_j - q_j]_+ per 64-vector segment; the last chunk picks chunk,
+//                 segment, lane and element where the cumulative mass passes u*Z.  For
+//                 a bonus, the chunk picked from k_norm's partials re-reads itself.
+//   k_argmax      greedy (T == 0): per-chunk argmax, row combine and scan, one launch.
 //
 // "Last chunk / last row" is decided with self-resetting ticket counters (atomicInc
 // with wrap-around) kept at the start of the workspace: a call needs those leading
 // bytes at zero and leaves them at zero, so no host sync or memset happens between
-// kernels or between calls of one shape.  All reductions use fixed trees or fixed orders, so
-// results are bitwise reproducible run to run.
+// kernels or between calls of one shape.  All reductions use fixed trees or fixed
+// orders, so results are bitwise reproducible run to run.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -46,13 +49,17 @@ namespace sv {
 constexpr int NT = 256;                // threads per workgroup
 constexpr int WAVE = 64;               // gfx950 wavefront
 constexpr int NW = NT / WAVE;          // waves per workgroup
-constexpr int VPT = 4;                 // 16-byte vectors per thread per chunk
-constexpr int CHUNK_VECS = NT * VPT;   // vectors per chunk (16 KiB of logits)
+constexpr int VPT = 8;                 // 16-byte vectors per thread per chunk
+constexpr int CHUNK_VECS = NT * VPT;   // vectors per chunk (32 KiB of logits)
 constexpr int SEGS = VPT * NW;         // 64-vector segments per chunk
+constexpr int NSUB = 4;                // second-pass workgroups per chunk of a rejected pair
+constexpr int KSUB = VPT / NSUB;       // vectors per thread of each of them
 constexpr double LN2 = 0.69314718055994530942;
 constexpr double LOG2E = 1.44269504088896340736;
 
 enum : int { JOB_NONE = 0, JOB_REJECT = 1, JOB_BONUS = 2 };
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- element formats
 
@@ -63,8 +70,7 @@ template <>
 struct Fmt<uint16_t> {  // bf16 bit patterns: the upper half of an IEEE binary32
   static constexpr int VEC = 8;
   SVD static float at(const uint16_t *p, size_t i) { return __uint_as_float((uint32_t)p[i] << 16); }
-  SVD static void vec(const uint16_t *p, size_t v, float (&o)[8]) {
-    const uint4 w = reinterpret_cast<const uint4 *>(p)[v];
+  SVD static void unpack(u32x4 w, float (&o)[8]) {
     o[0] = __uint_as_float(w.x << 16);
     o[1] = __uint_as_float(w.x & 0xffff0000u);
     o[2] = __uint_as_float(w.y << 16);
@@ -80,38 +86,88 @@ template <>
 struct Fmt<float> {
   static constexpr int VEC = 4;
   SVD static float at(const float *p, size_t i) { return p[i]; }
-  SVD static void vec(const float *p, size_t v, float (&o)[4]) {
-    const float4 w = reinterpret_cast<const float4 *>(p)[v];
-    o[0] = w.x;
-    o[1] = w.y;
-    o[2] = w.z;
-    o[3] = w.w;
+  SVD static void unpack(u32x4 w, float (&o)[4]) {
+    o[0] = __uint_as_float(w.x);
+    o[1] = __uint_as_float(w.y);
+    o[2] = __uint_as_float(w.z);
+    o[3] = __uint_as_float(w.w);
   }
 };
 
 // Vector k of this thread in chunk c is vector c*CHUNK_VECS + k*NT + tid of the row, so
 // one wave's k-th load covers 64 consecutive vectors (a "segment") and segments are in
-// vocabulary order (k-major, then wave).  Vectors past the row end read as -inf.
-template <typename T, bool ALIGNED>
+// vocabulary order (k-major, then wave).  Elements past the row end read as -inf.
+// Every load is issued before any is used: past the end a load re-reads the row's last
+// vector (or element), and the tail is masked afterwards by a uniform branch.
+template <typename T, bool ALIGNED, bool STREAM>
 SVD void load_chunk(const T *row, int V, int nvec, int c, int tid, float (&x)[VPT][Fmt<T>::VEC]) {
   constexpr int VEC = Fmt<T>::VEC;
+  if (ALIGNED) {
+    u32x4 w[VPT];
+    const u32x4 *rv = reinterpret_cast<const u32x4 *>(row);
 #pragma unroll
-  for (int k = 0; k < VPT; ++k) {
-    const int v = c * CHUNK_VECS + k * NT + tid;
-    if (ALIGNED) {
-      if (v < nvec) {
-        Fmt<T>::vec(row, (size_t)v, x[k]);
-      } else {
+    for (int k = 0; k < VPT; ++k) {
+      const int v = c * CHUNK_VECS + k * NT + tid;
+      const u32x4 *p = rv + (v < nvec ? v : nvec - 1);
+      w[k] = STREAM ? __builtin_nontemporal_load(p) : *p;
+    }
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) x[k][e] = -INFINITY;
-      }
-    } else {
+    for (int k = 0; k < VPT; ++k) Fmt<T>::unpack(w[k], x[k]);
+    if ((c + 1) * CHUNK_VECS > nvec) {
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const long idx = (long)v * VEC + e;
-        x[k][e] = (v < nvec && idx < V) ? Fmt<T>::at(row, (size_t)idx) : -INFINITY;
+      for (int k = 0; k < VPT; ++k) {
+        const bool in = c * CHUNK_VECS + k * NT + tid < nvec;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) x[k][e] = in ? x[k][e] : -INFINITY;
       }
     }
+  } else {
+#pragma unroll
+    for (int k = 0; k < VPT; ++k)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const long idx = ((long)c * CHUNK_VECS + (long)k * NT + tid) * VEC + e;
+        const bool in = idx < V;
+        const float z = Fmt<T>::at(row, (size_t)(in ? idx : (long)V - 1));
+        x[k][e] = in ? z : -INFINITY;
+      }
+  }
+}
+
+// Vectors k0..k0+NK-1 of this thread in chunk c, as load_chunk does for all VPT of them.
+template <typename T, bool ALIGNED, bool STREAM, int NK>
+SVD void load_vectors(const T *row, int V, int nvec, int c, int k0, int tid,
+                      float (&x)[NK][Fmt<T>::VEC]) {
+  constexpr int VEC = Fmt<T>::VEC;
+  if (ALIGNED) {
+    u32x4 w[NK];
+    const u32x4 *rv = reinterpret_cast<const u32x4 *>(row);
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+      const int v = c * CHUNK_VECS + (k0 + k) * NT + tid;
+      const u32x4 *p = rv + (v < nvec ? v : nvec - 1);
+      w[k] = STREAM ? __builtin_nontemporal_load(p) : *p;
+    }
+#pragma unroll
+    for (int k = 0; k < NK; ++k) Fmt<T>::unpack(w[k], x[k]);
+    if ((c + 1) * CHUNK_VECS > nvec) {
+#pragma unroll
+      for (int k = 0; k < NK; ++k) {
+        const bool in = c * CHUNK_VECS + (k0 + k) * NT + tid < nvec;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) x[k][e] = in ? x[k][e] : -INFINITY;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < NK; ++k)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const long idx = ((long)c * CHUNK_VECS + (long)(k0 + k) * NT + tid) * VEC + e;
+        const bool in = idx < V;
+        const float z = Fmt<T>::at(row, (size_t)(in ? idx : (long)V - 1));
+        x[k][e] = in ? z : -INFINITY;
+      }
   }
 }
 
@@ -123,23 +179,34 @@ SVD long elem_index(int c, int k, int tid, int e) {
 
 // ---------------------------------------------------------------- arguments
 
+// What the acceptance scan of a sequence hands to the second kernel, in one record.
+struct SeqJob {
+  int j, kind;                 // first rejected position (G: all accepted); JOB_*
+  int c_bonus, pad;            // bonus: the chunk of p_G holding u*S, picked from partials
+  float mt_hi, mt_lo, md_hi, md_lo;  // rejection: log2-partitions of p_j and q_j, head + tail
+  float tau_t, tau_d;          // rejection: top-k thresholds of rows j (or -inf)
+  float off_bonus, pad2;       // bonus: offset of chunk c_bonus
+  double t_bonus;              // bonus: u*S minus the mass before c_bonus, in the chunk's scale
+};
+
 struct Work {                  // carved from the caller's workspace
-  float *part_off;             // [R*C] chunk offset (log2 units) / greedy: chunk best value
+  float *part_off;             // [R*C] chunk offset m_c*k2 / greedy: chunk best value
   double *part_sum;            // [R*C] chunk sum of 2^(z*k2 - off)
-  int *part_idx;               // [R*C] greedy: chunk best index; bit flags in part_flag
+  int *part_idx;               // [R*C] greedy: chunk best index
   int *part_flag;              // [R*C] greedy: 1 = NaN/+inf seen, 2 = finite seen
   float *row_off;              // [R] row offset
   double *row_l2s;             // [R] log2 of the row sum: log2-partition = off + l2s
   int *row_ok;                 // [R] row usable
   int *row_arg;                // [R] greedy argmax
   float *row_tau;              // [R] top-k threshold (raw logit); rows with no cut: -inf
+  float *row_zx;               // [R] the row's logit at its position's drafted token (NaN if none)
   uint2 *tk_state;             // [R] radix-select prefix and remaining rank
   unsigned *tk_hist;           // [R*C*256] per-chunk digit histograms
   unsigned *t_row;             // [R] tickets (self-resetting)
   unsigned *t_seq;             // [B]
   unsigned *t_p2;              // [B]
-  int2 *job;                   // [B] (j, kind)
-  double *p2_chunk;            // [B*C] residual mass per chunk
+  struct SeqJob *job;          // [B] the acceptance scan's result for the second kernel
+  double *p2_seg;              // [B*C*SEGS] residual mass per 64-vector segment
 };
 
 struct Args {
@@ -154,8 +221,7 @@ struct Args {
   Work w;
 };
 
-// Row r of the flattened (sequence, row) list: rows 0..G of a sequence are target rows
-// 0..G, rows G+1..2G are draft rows 0..G-1.
+// Row j of sequence b: rows 0..G are target rows 0..G, rows G+1..2G draft rows 0..G-1.
 template <typename T>
 SVD const T *seq_row(const Args &a, int b, int j) {
   if (j <= a.G) return static_cast<const T *>(a.target) + ((size_t)b * (a.G + 1) + j) * (size_t)a.V;
@@ -165,10 +231,11 @@ SVD const T *seq_row(const Args &a, int b, int j) {
 // ---------------------------------------------------------------- small helpers
 
 SVD float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }  // v_exp_f32; 0 for x < -126
+SVD int lane_id() { return (int)(threadIdx.x & (WAVE - 1)); }
 
-// (off, s) pairs stand for s * 2^off; combining keeps the larger offset.  Chunks that
+// (off, s) pairs stand for s * 2^off; combining keeps the larger offset.  Parts that
 // hold only -inf have off = -inf and s = 0 (or NaN when a NaN was seen); the rule never
-// forms (-inf) - (-inf).
+// forms (-inf) - (-inf).  The combine is commutative bit for bit.
 SVD void lse_combine(float &off, double &s, float off2, double s2) {
   const float mx = fmaxf(off, off2);
   const double w1 = (off == mx) ? 1.0 : (double)fast_exp2(off - mx);
@@ -177,34 +244,118 @@ SVD void lse_combine(float &off, double &s, float off2, double s2) {
   off = mx;
 }
 
+// ---- cross-lane primitives (DPP) ----
+// Wave-wide scans and reductions use DPP lane moves (row_shr within 16-lane rows, then
+// row_bcast:15 / row_bcast:31 across rows) instead of LDS-routed shuffles: each step is
+// one VALU move.  A move leaves `id` in lanes that have no source, so every scan below
+// is an inclusive scan with identity id; a reduction is the scan's lane 63 read back.
+template <int CTRL, int ROWM>
+SVD unsigned dpp_u(unsigned v, unsigned id) {
+  return (unsigned)__builtin_amdgcn_update_dpp((int)id, (int)v, CTRL, ROWM, 0xf, false);
+}
+template <int CTRL, int ROWM>
+SVD float dpp_f(float v, float id) { return __uint_as_float(dpp_u<CTRL, ROWM>(__float_as_uint(v), __float_as_uint(id))); }
+template <int CTRL, int ROWM>
+SVD double dpp_d(double v, double id) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+  const unsigned long long ib = (unsigned long long)__double_as_longlong(id);
+  const unsigned lo = dpp_u<CTRL, ROWM>((unsigned)b, (unsigned)ib);
+  const unsigned hi = dpp_u<CTRL, ROWM>((unsigned)(b >> 32), (unsigned)(ib >> 32));
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+template <int CTRL, int ROWM>
+SVD int dpp_i(int v, int id) { return (int)dpp_u<CTRL, ROWM>((unsigned)v, (unsigned)id); }
+
+// The six steps of a 64-lane inclusive scan; STEP(ctrl, rowmask) applies one lane move.
+#define SV_SCAN_STEPS(STEP) \
+  STEP(0x111, 0xf) /* row_shr:1 */ \
+  STEP(0x112, 0xf) /* row_shr:2 */ \
+  STEP(0x114, 0xf) /* row_shr:4 */ \
+  STEP(0x118, 0xf) /* row_shr:8 */ \
+  STEP(0x142, 0xa) /* row_bcast:15 into rows 1 and 3 */ \
+  STEP(0x143, 0xc) /* row_bcast:31 into rows 2 and 3 */
+
+SVD double scan_sum(double x) {
+#define STEP(C, R) x += dpp_d<C, R>(x, 0.0);
+  SV_SCAN_STEPS(STEP)
+#undef STEP
+  return x;
+}
+SVD float scan_max(float x) {
+#define STEP(C, R) x = fmaxf(x, dpp_f<C, R>(x, -INFINITY));
+  SV_SCAN_STEPS(STEP)
+#undef STEP
+  return x;
+}
+SVD unsigned scan_or(unsigned x) {
+#define STEP(C, R) x |= dpp_u<C, R>(x, 0u);
+  SV_SCAN_STEPS(STEP)
+#undef STEP
+  return x;
+}
+
+SVD double readlane_d(double v, int l) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)b, l);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(b >> 32), l);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+SVD float readlane_f(float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); }
+
+SVD double wave_sum(double v) { return readlane_d(scan_sum(v), WAVE - 1); }
+SVD float wave_max(float v) { return readlane_f(scan_max(v), WAVE - 1); }
+SVD unsigned wave_or(unsigned v) { return (unsigned)__builtin_amdgcn_readlane((int)scan_or(v), WAVE - 1); }
+
+// (off, s) pairs over the wave, combined with lse_combine (identity (-inf, 0)).
 SVD void wave_lse(float &off, double &s) {
-#pragma unroll
-  for (int o = WAVE / 2; o > 0; o >>= 1) {
-    const float off2 = __shfl_xor(off, o);
-    const double s2 = __shfl_xor(s, o);
-    lse_combine(off, s, off2, s2);
+#define STEP(C, R)                                  \
+  {                                                 \
+    const float o2 = dpp_f<C, R>(off, -INFINITY);   \
+    const double s2 = dpp_d<C, R>(s, 0.0);          \
+    lse_combine(off, s, o2, s2);                    \
   }
+  SV_SCAN_STEPS(STEP)
+#undef STEP
+  off = readlane_f(off, WAVE - 1);
+  s = readlane_d(s, WAVE - 1);
 }
 
-SVD double wave_sum(double v) {
-#pragma unroll
-  for (int o = WAVE / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+// Results that one workgroup hands to another inside a kernel are written and read with
+// device-scope (agent) atomic stores and loads: on gfx950 these are ordinary vector
+// memory instructions with the device scope bit set, so they are complete device-wide
+// (across the XCDs' separate L2s) when the store counter drains, and the loads observe
+// them.  This avoids the whole-L2 write-back that a device-scope release fence costs.
+template <typename T>
+SVD void st_dev(T *p, T v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+template <typename T>
+SVD T ld_dev(const T *p) {
+  return __hip_atomic_load(const_cast<T *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Is this workgroup the last of n to arrive at *ctr?  The counter wraps back to zero on
-// the last arrival, so it is ready for the next call.  Release / acquire fences at
-// device scope make the partial results of the other workgroups (possibly on other
-// XCDs) visible to the winner.
-SVD bool last_arrival(unsigned *ctr, unsigned n) {
+// Is this the last of n arrivals at *ctr?  The caller's device-scope stores have
+// completed (s_waitcnt on all counters) before the ticket is taken, so the winner sees
+// every other arrival's published results.  The counter wraps back to zero on the last
+// arrival, ready for the next call.  wave_last_arrival is taken by one wave alone;
+// block_last_arrival by a whole workgroup.
+SVD bool wave_last_arrival(unsigned *ctr, unsigned n) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  unsigned old = 0;
+  if (lane_id() == 0) old = __builtin_amdgcn_atomic_inc32(ctr, n - 1, __ATOMIC_RELAXED, "agent");
+  return (unsigned)__builtin_amdgcn_readlane((int)old, 0) == n - 1;
+}
+
+SVD bool block_last_arrival(unsigned *ctr, unsigned n) {
   __shared__ int s_last;
-  __threadfence();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __syncthreads();
-  if (threadIdx.x == 0) s_last = (atomicInc(ctr, n - 1) == n - 1);
+  if (threadIdx.x == 0)
+    s_last = (__builtin_amdgcn_atomic_inc32(ctr, n - 1, __ATOMIC_RELAXED, "agent") == n - 1);
   __syncthreads();
-  const bool last = s_last != 0;
-  if (last) __threadfence();
-  return last;
+  return s_last != 0;
 }
 
 // Order-preserving 32-bit key of a float (bf16 values are floats with zero low half);
@@ -215,6 +366,56 @@ SVD uint32_t f2key(float f) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 SVD float key2f(uint32_t k) { return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k); }
+
+// Inverse CDF over n ordered items, by one whole wave: masses come from mfn(i); the
+// prefix runs in index order (groups of 64 lanes, inclusive scan, carried), so the same
+// masses always give the same total and prefixes.  wave_total returns the total;
+// wave_pick returns the first item whose inclusive prefix exceeds t and, in *t_rem,
+// t minus the prefix before it.  When rounding leaves t at or past the total it returns
+// the last item with positive mass and *t_rem = +inf (which makes the finer levels take
+// their last positive entry too).  -1 if no item has positive mass.
+template <typename MFn>
+SVD double wave_scan_group(int n, int i0, const MFn &mfn, double carry, double &m, double &cum) {
+  const int i = i0 + lane_id();
+  m = (i < n) ? mfn(i) : 0.0;
+  cum = scan_sum(m) + carry;
+  return readlane_d(cum, WAVE - 1);
+}
+
+template <typename MFn>
+SVD double wave_total(int n, const MFn &mfn) {
+  double carry = 0.0, m, cum;
+  for (int i0 = 0; i0 < n; i0 += WAVE) carry = wave_scan_group(n, i0, mfn, carry, m, cum);
+  return carry;
+}
+
+template <typename MFn>
+SVD int wave_pick(int n, double t, const MFn &mfn, double *t_rem) {
+  double carry = 0.0, m, cum;
+  int pick = -1, lastpos = -1;
+  double trem = INFINITY;
+  for (int i0 = 0; i0 < n; i0 += WAVE) {
+    const double carry_in = carry;
+    carry = wave_scan_group(n, i0, mfn, carry, m, cum);
+    const unsigned long long pos = __ballot(m > 0.0);
+    if (pos) lastpos = i0 + 63 - __clzll((long long)pos);
+    if (pick < 0) {
+      const unsigned long long cr = __ballot(m > 0.0 && cum > t);
+      if (cr) {
+        const int l = __ffsll((long long)cr) - 1;
+        const double prev = (l == 0) ? carry_in : readlane_d(cum, l - 1);
+        pick = i0 + l;
+        trem = t - prev;
+      }
+    }
+  }
+  if (pick < 0) {
+    pick = lastpos;
+    trem = INFINITY;
+  }
+  *t_rem = trem;
+  return pick;
+}
 
 // ---------------------------------------------------------------- top-k threshold
 
@@ -237,7 +438,7 @@ __global__ __launch_bounds__(NT) void k_topk_digit(const Args a, int pass, int l
   hist[tid] = 0u;
   __syncthreads();
   float x[VPT][VEC];
-  load_chunk<T, ALIGNED>(seq_row<T>(a, b, jr), a.V, a.nvec, c, tid, x);
+  load_chunk<T, ALIGNED, true>(seq_row<T>(a, b, jr), a.V, a.nvec, c, tid, x);
 #pragma unroll
   for (int k = 0; k < VPT; ++k)
 #pragma unroll
@@ -248,12 +449,12 @@ __global__ __launch_bounds__(NT) void k_topk_digit(const Args a, int pass, int l
       }
     }
   __syncthreads();
-  a.w.tk_hist[((size_t)r * a.C + c) * 256 + tid] = hist[tid];
-  if (!last_arrival(&a.w.t_row[r], (unsigned)a.C)) return;
+  st_dev(&a.w.tk_hist[((size_t)r * a.C + c) * 256 + tid], hist[tid]);
+  if (!block_last_arrival(&a.w.t_row[r], (unsigned)a.C)) return;
 
   // Row total of digit d = tid, then counts of keys with digit >= d.
   unsigned tot = 0;
-  for (int cc = 0; cc < a.C; ++cc) tot += a.w.tk_hist[((size_t)r * a.C + cc) * 256 + tid];
+  for (int cc = 0; cc < a.C; ++cc) tot += ld_dev(&a.w.tk_hist[((size_t)r * a.C + cc) * 256 + tid]);
   s_ge[tid] = tot;
   __syncthreads();
   for (int o = 1; o < 256; o <<= 1) {  // suffix sums (Hillis-Steele)
@@ -276,102 +477,317 @@ __global__ __launch_bounds__(NT) void k_topk_digit(const Args a, int pass, int l
 
 // ---------------------------------------------------------------- acceptance scan
 
-// Run by the last-finishing row of sequence b, after every row's statistics are in
-// the workspace.  Position i of the chain: token range, row validity, uniform range,
-// draft support, then the test U_i <= min(1, p_i(x)/q_i(x)) with p_i(x) > 0 ([WY]
-// "一次 sampling 怎么执行" step 4; the ratio is formed from log2-probabilities in double).
-template <typename T, bool GREEDY>
-SVD void sequence_scan(const Args &a, int b) {
-  __shared__ int s_j, s_flags;
-  const int tid = threadIdx.x;
-  const int G = a.G, rps = a.rps;
-  if (tid == 0) {
-    s_j = G;
-    s_flags = 0;
+// Largest value wins, ties go to the lower index; NaN and +inf mark the row unusable.
+SVD void best_combine(float &v, int &i, float v2, int i2) {
+  if (v2 > v || (v2 == v && i2 < i)) {
+    v = v2;
+    i = i2;
   }
-  __syncthreads();
-  int flags = 0;  // 1 bad token, 2 bad row, 4 bad uniform, 8 q(x) = 0
-  for (int i = tid; i < G; i += NT) {
-    const int x = a.tokens[(size_t)b * G + i];
-    const bool tok_ok = (x >= 0) && (x < a.V);
-    if (!tok_ok) flags |= 1;
-    const int rt = b * rps + i;
-    bool accept = false;
+}
+
+SVD void wave_best(float &v, int &i, int &fl) {
+#define STEP(C, R)                                   \
+  {                                                  \
+    const float v2 = dpp_f<C, R>(v, -INFINITY);      \
+    const int i2 = dpp_i<C, R>(i, 0x7fffffff);       \
+    fl |= dpp_i<C, R>(fl, 0);                        \
+    best_combine(v, i, v2, i2);                      \
+  }
+  SV_SCAN_STEPS(STEP)
+#undef STEP
+  v = readlane_f(v, WAVE - 1);
+  i = __builtin_amdgcn_readlane(i, WAVE - 1);
+  fl = __builtin_amdgcn_readlane(fl, WAVE - 1);
+}
+
+
+constexpr int SEQ_LDS_PARTS = 256;   // (row, chunk) partials of one sequence staged in LDS
+constexpr int SEQ_LDS_ROWS = 129;    // rows of one sequence kept in LDS (G <= 64)
+
+// The last chunk of sequence b to finish (one wave) combines every row of the sequence
+// from its chunk partials, then runs the acceptance scan.  Position i of the chain:
+// token range, row validity, uniform range, draft support, then the test
+// U_i <= min(1, p_i(x)/q_i(x)) with p_i(x) > 0 ("Speculative Decoding 的朴素思想",
+// "一次 sampling 怎么执行" step 4; the ratio is formed from log2-probabilities in double).
+// Greedy: acceptance is equality with the target argmax.  All partials and token
+// logits come in with one round of loads; the inputs (tokens, uniforms) are loaded
+// first so they arrive meanwhile.
+template <typename T, bool GREEDY, bool TOPK>
+SVD void sequence_finish(const Args &a, int b) {
+  constexpr int PG = GREEDY ? SEQ_LDS_PARTS : 1, PS = GREEDY ? 1 : SEQ_LDS_PARTS;
+  constexpr int RG = GREEDY ? SEQ_LDS_ROWS : 1, RS = GREEDY ? 1 : SEQ_LDS_ROWS;
+  __shared__ float s_po[SEQ_LDS_PARTS];
+  __shared__ double s_ps[PS];
+  __shared__ int s_pi[PG], s_pf[PG];
+  __shared__ float s_roff[RS], s_rzx[RS], s_rtau[RS];
+  __shared__ double s_rl2s[RS];
+  __shared__ int s_rok[SEQ_LDS_ROWS], s_rarg[RG];
+  const int lane = lane_id();
+  const int G = a.G, rps = a.rps, C = a.C;
+  const size_t r0 = (size_t)b * rps;
+  const bool lds = rps * C <= SEQ_LDS_PARTS && rps <= SEQ_LDS_ROWS;
+
+  // inputs of positions lane, lane+64, ... (first round only kept in registers)
+  const int x0 = (lane < G) ? a.tokens[(size_t)b * G + lane] : 0;
+  const float u0 = (!GREEDY && lane < G) ? a.u_accept[(size_t)b * G + lane] : 0.0f;
+  const float us = GREEDY ? 0.0f : a.u_sample[b];
+
+  // Stage the partials of every (row, chunk) of the sequence and the token logits in
+  // LDS: every lane issues all of its loads before any of them is waited for.
+  if (lds) {
+    constexpr int UNR = SEQ_LDS_PARTS / WAVE;
+    const int np = rps * C;
     if (GREEDY) {
-      if (!a.w.row_ok[rt]) flags |= 2;
-      accept = tok_ok && a.w.row_ok[rt] && (x == a.w.row_arg[rt]);
+      float vo[UNR];
+      int vi[UNR], vf[UNR];
+#pragma unroll
+      for (int k = 0; k < UNR; ++k) {
+        const int i = lane + k * WAVE;
+        const int ii = (i < np) ? i : 0;
+        vo[k] = ld_dev(&a.w.part_off[r0 * C + ii]);
+        vi[k] = ld_dev(&a.w.part_idx[r0 * C + ii]);
+        vf[k] = ld_dev(&a.w.part_flag[r0 * C + ii]);
+      }
+#pragma unroll
+      for (int k = 0; k < UNR; ++k) {
+        const int i = lane + k * WAVE;
+        if (i < np) {
+          s_po[i] = vo[k];
+          s_pi[i] = vi[k];
+          s_pf[i] = vf[k];
+        }
+      }
     } else {
-      const int rd = b * rps + G + 1 + i;
-      if (!a.w.row_ok[rt] || !a.w.row_ok[rd]) flags |= 2;
-      const float u = a.u_accept[(size_t)b * G + i];
-      if (!(u >= 0.0f && u < 1.0f)) flags |= 4;
-      if (tok_ok) {
-        const float tau_t = a.w.row_tau[rt], tau_d = a.w.row_tau[rd];
-        const float zt = Fmt<T>::at(seq_row<T>(a, b, i), (size_t)x);
-        const float zd = Fmt<T>::at(seq_row<T>(a, b, G + 1 + i), (size_t)x);
-        const bool supp_t = (zt > -INFINITY) && !(zt < tau_t);
-        const bool supp_d = (zd > -INFINITY) && !(zd < tau_d);
-        if (!supp_d) flags |= 8;
-        if (supp_t && supp_d && a.w.row_ok[rt] && a.w.row_ok[rd]) {
-          const double k2 = (double)a.k2;
-          const double l2p = (double)zt * k2 - ((double)a.w.row_off[rt] + a.w.row_l2s[rt]);
-          const double l2q = (double)zd * k2 - ((double)a.w.row_off[rd] + a.w.row_l2s[rd]);
-          const double alpha = exp2(fmin(0.0, l2p - l2q));
-          accept = (double)u <= alpha;
+      float vo[UNR];
+      double vs[UNR];
+#pragma unroll
+      for (int k = 0; k < UNR; ++k) {
+        const int i = lane + k * WAVE;
+        const int ii = (i < np) ? i : 0;
+        vo[k] = ld_dev(&a.w.part_off[r0 * C + ii]);
+        vs[k] = ld_dev(&a.w.part_sum[r0 * C + ii]);
+      }
+      constexpr int RUNR = (SEQ_LDS_ROWS + WAVE - 1) / WAVE;
+      float zx[RUNR], tau[RUNR];
+#pragma unroll
+      for (int k = 0; k < RUNR; ++k) {
+        const int jr = lane + k * WAVE;
+        const int jj = (jr < rps) ? jr : 0;
+        zx[k] = ld_dev(&a.w.row_zx[r0 + jj]);
+        tau[k] = TOPK ? a.w.row_tau[r0 + jj] : -INFINITY;  // top-k: the previous kernel's
+      }
+#pragma unroll
+      for (int k = 0; k < UNR; ++k) {
+        const int i = lane + k * WAVE;
+        if (i < np) {
+          s_po[i] = vo[k];
+          s_ps[i] = vs[k];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < RUNR; ++k) {
+        const int jr = lane + k * WAVE;
+        if (jr < rps) {
+          s_rzx[jr] = zx[k];
+          s_rtau[jr] = tau[k];
         }
       }
     }
-    if (!accept) atomicMin(&s_j, i);
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
   }
-  if (tid == 0) {
-    const int rg = b * rps + G;  // target row G (the bonus distribution)
-    if (!a.w.row_ok[rg]) flags |= 2;
-    if (!GREEDY) {
-      const float u = a.u_sample[b];
-      if (!(u >= 0.0f && u < 1.0f)) flags |= 4;
+  auto p_off = [&](int jr, int cc) { return lds ? s_po[jr * C + cc] : ld_dev(&a.w.part_off[(r0 + jr) * C + cc]); };
+  auto p_sum = [&](int jr, int cc) { return lds ? s_ps[jr * C + cc] : ld_dev(&a.w.part_sum[(r0 + jr) * C + cc]); };
+  auto p_idx = [&](int jr, int cc) { return lds ? s_pi[jr * C + cc] : ld_dev(&a.w.part_idx[(r0 + jr) * C + cc]); };
+  auto p_flag = [&](int jr, int cc) { return lds ? s_pf[jr * C + cc] : ld_dev(&a.w.part_flag[(r0 + jr) * C + cc]); };
+
+  // Row statistics: lane jr combines row jr's chunks in chunk order (rows in parallel).
+  for (int jr0 = 0; jr0 < rps; jr0 += WAVE) {
+    const int jr = jr0 + lane;
+    if (jr < rps) {
+      const size_t r = r0 + jr;
+      if (GREEDY) {
+        float best = -INFINITY;
+        int bi = 0x7fffffff, fl = 0;
+        for (int cc = 0; cc < C; ++cc) {
+          best_combine(best, bi, p_off(jr, cc), p_idx(jr, cc));
+          fl |= p_flag(jr, cc);
+        }
+        const int ok = (fl == 2) ? 1 : 0;
+        st_dev(&a.w.row_arg[r], bi);
+        st_dev(&a.w.row_ok[r], ok);
+        if (lds) {
+          s_rarg[jr] = bi;
+          s_rok[jr] = ok;
+        }
+      } else {
+        float o = -INFINITY;
+        double t = 0.0;
+        for (int cc = 0; cc < C; ++cc) lse_combine(o, t, p_off(jr, cc), p_sum(jr, cc));
+        const bool ok = isfinite(o) && isfinite(t) && t > 0.0;
+        const double l2s = ok ? log2(t) : 0.0;
+        st_dev(&a.w.row_off[r], o);
+        st_dev(&a.w.row_l2s[r], l2s);
+        st_dev(&a.w.row_ok[r], ok ? 1 : 0);
+        if (!TOPK) st_dev(&a.w.row_tau[r], -INFINITY);
+        if (a.row_stats) {
+          a.row_stats[r * 2 + 0] = (float)((double)o * LN2);
+          a.row_stats[r * 2 + 1] = (float)t;
+        }
+        if (lds) {
+          s_roff[jr] = o;
+          s_rl2s[jr] = l2s;
+          s_rok[jr] = ok ? 1 : 0;
+        }
+      }
     }
   }
-  if (flags) atomicOr(&s_flags, flags);
-  __syncthreads();
-  const int fl = s_flags, j = s_j;
-  const int err = (fl & 1) ? SV_ROW_BAD_TOKEN
-                : (fl & 2) ? SV_ROW_BAD_LOGITS
-                : (fl & 4) ? SV_ROW_BAD_UNIFORM
-                : (fl & 8) ? SV_ROW_Q_ZERO : 0;
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+
+  // The bonus draw's chunk, in case every draft is accepted: chunk masses of p_G,
+  // S_c * 2^(off_c - off_row) in chunk order, and the remainder in that chunk's scale.
+  int c_bonus = -1;
+  float off_bonus = 0.0f;
+  double t_bonus = 0.0;
+  if (!GREEDY) {
+    const float oG = lds ? s_roff[G] : ld_dev(&a.w.row_off[r0 + G]);
+    const int okG = lds ? s_rok[G] : ld_dev(&a.w.row_ok[r0 + G]);
+    if (okG) {
+      auto cm = [&](int cc) {
+        const double sc = p_sum(G, cc);
+        return (sc > 0.0) ? sc * (double)fast_exp2(p_off(G, cc) - oG) : 0.0;
+      };
+      const double total = wave_total(C, cm);
+      double trem;
+      c_bonus = wave_pick(C, (double)us * total, cm, &trem);
+      if (c_bonus >= 0) {
+        off_bonus = p_off(G, c_bonus);
+        t_bonus = trem * (double)fast_exp2(oG - off_bonus);
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+  auto r_ok = [&](int jr) { return lds ? s_rok[jr] : ld_dev(&a.w.row_ok[r0 + jr]); };
+  auto r_off = [&](int jr) { return lds ? s_roff[jr] : ld_dev(&a.w.row_off[r0 + jr]); };
+  auto r_l2s = [&](int jr) { return lds ? s_rl2s[jr] : ld_dev(&a.w.row_l2s[r0 + jr]); };
+  auto r_arg = [&](int jr) { return lds ? s_rarg[jr] : ld_dev(&a.w.row_arg[r0 + jr]); };
+  auto r_zx = [&](int jr) { return lds ? s_rzx[jr] : ld_dev(&a.w.row_zx[r0 + jr]); };
+  auto r_tau = [&](int jr) { return lds ? s_rtau[jr] : (TOPK ? a.w.row_tau[r0 + jr] : -INFINITY); };
+
+  int j = G;
+  unsigned flags = 0;  // 1 bad token, 2 bad row, 4 bad uniform, 8 q(x) = 0
+  for (int i0 = 0; i0 < G; i0 += WAVE) {
+    const int i = i0 + lane;
+    const bool act = i < G;
+    bool accept = false;
+    if (act) {
+      const int x = (i0 == 0) ? x0 : a.tokens[(size_t)b * G + i];
+      const bool tok_ok = (x >= 0) && (x < a.V);
+      if (!tok_ok) flags |= 1;
+      const bool ok_t = r_ok(i) != 0;
+      if (GREEDY) {
+        if (!ok_t) flags |= 2;
+        accept = tok_ok && ok_t && (x == r_arg(i));
+      } else {
+        const int id = G + 1 + i;
+        const bool ok_d = r_ok(id) != 0;
+        if (!ok_t || !ok_d) flags |= 2;
+        const float u = (i0 == 0) ? u0 : a.u_accept[(size_t)b * G + i];
+        if (!(u >= 0.0f && u < 1.0f)) flags |= 4;
+        if (tok_ok) {
+          const float zt = r_zx(i), zd = r_zx(id);
+          const bool supp_t = (zt > -INFINITY) && !(zt < r_tau(i));
+          const bool supp_d = (zd > -INFINITY) && !(zd < r_tau(id));
+          if (!supp_d) flags |= 8;
+          if (supp_t && supp_d && ok_t && ok_d) {
+            const double k2 = (double)a.k2;
+            const double l2p = (double)zt * k2 - ((double)r_off(i) + r_l2s(i));
+            const double l2q = (double)zd * k2 - ((double)r_off(id) + r_l2s(id));
+            const double alpha = exp2(fmin(0.0, l2p - l2q));
+            accept = (double)u <= alpha;
+          }
+        }
+      }
+    }
+    const unsigned long long rej = __ballot(act && !accept);
+    if (j == G && rej) j = i0 + __ffsll((long long)rej) - 1;
+  }
+  if (!r_ok(G)) flags |= 2;  // target row G: the bonus distribution
+  if (!GREEDY && !(us >= 0.0f && us < 1.0f)) flags |= 4;
+  flags = wave_or(flags);
+  const int err = (flags & 1) ? SV_ROW_BAD_TOKEN
+                : (flags & 2) ? SV_ROW_BAD_LOGITS
+                : (flags & 4) ? SV_ROW_BAD_UNIFORM
+                : (flags & 8) ? SV_ROW_Q_ZERO : 0;
   int32_t *out = a.out_tokens + (size_t)b * (G + 1);
-  for (int i = tid; i <= G; i += NT) {
+  for (int i = lane; i <= G; i += WAVE) {
     int32_t v;
     if (err) v = -1;
-    else if (i < j) v = a.tokens[(size_t)b * G + i];
+    else if (i < j) v = (i < WAVE) ? x0 : a.tokens[(size_t)b * G + i];
     else if (i > j) v = -1;
-    else if (GREEDY) v = a.w.row_arg[b * rps + j];  // the target's own choice
-    else continue;                                  // drawn by k_sample
+    else if (GREEDY) v = r_arg(j);  // the target's own choice
+    else continue;                  // drawn by the second kernel
     out[i] = v;
   }
-  if (tid == 0) {
+  if (lane == 0) {
     a.accepted_len[b] = err ? err : j;
-    a.w.job[b] = make_int2(j, (err || GREEDY) ? JOB_NONE : (j < G ? JOB_REJECT : JOB_BONUS));
+    if (!GREEDY) {
+      SeqJob jb;
+      jb.j = j;
+      jb.kind = err ? (int)JOB_NONE : (j < G ? (int)JOB_REJECT : (int)JOB_BONUS);
+      jb.c_bonus = c_bonus;
+      jb.pad = 0;
+      jb.off_bonus = off_bonus;
+      jb.pad2 = 0.0f;
+      jb.t_bonus = t_bonus;
+      jb.mt_hi = jb.mt_lo = jb.md_hi = jb.md_lo = 0.0f;
+      jb.tau_t = jb.tau_d = -INFINITY;
+      if (jb.kind == JOB_REJECT) {
+        const double mt = (double)r_off(j) + r_l2s(j);
+        const double md = (double)r_off(G + 1 + j) + r_l2s(G + 1 + j);
+        jb.mt_hi = (float)mt;
+        jb.mt_lo = (float)(mt - (double)jb.mt_hi);
+        jb.md_hi = (float)md;
+        jb.md_lo = (float)(md - (double)jb.md_hi);
+        jb.tau_t = r_tau(j);
+        jb.tau_d = r_tau(G + 1 + j);
+      }
+      a.w.job[b] = jb;
+    }
   }
 }
 
 // ---------------------------------------------------------------- pass 1: normaliser
 
-// Per chunk: m = max kept z, off = m*k2 (rounded once), s = sum 2^(fma(z, k2, -off)).
-// The log2-partition of the row is off_row + log2(s_row), with off_row the float actually
-// subtracted, so every consumer reproduces the same probabilities.
+// First-pass item (row r, chunk c).  Per chunk: m_c = block max of the kept z, off = m_c*k2 (rounded once, stored as is),
+// s = sum 2^(fma(z, k2, -off)).  The log2-partition of a row is off_row + log2(s_row)
+// with off_row the float actually subtracted, so every consumer reproduces the same
+// probabilities; the second pass recomputes a chunk's terms bit for bit from the same offset.
 template <typename T, bool ALIGNED, bool TOPK>
-__global__ __launch_bounds__(NT) void k_norm(const Args a) {
+SVD void norm_item(const Args &a, int item) {
   constexpr int VEC = Fmt<T>::VEC;
-  __shared__ float s_off[NW];
-  __shared__ double s_sum[NW];
-  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wid = tid / WAVE;
-  const int r = blockIdx.x / a.C, c = blockIdx.x - r * a.C;
+  __shared__ float s_m[NW];
+  __shared__ double s_s[NW];
+  const int tid = threadIdx.x, lane = lane_id(), wid = tid / WAVE;
+  const int r = item / a.C, c = item - r * a.C;
   const int b = r / a.rps, jr = r - b * a.rps;
 
+  // The drafted token of this row's position: its load is issued first and lands while
+  // the chunk streams in; the chunk holding the token publishes the logit there for the
+  // acceptance scan.  Thread 0 of every chunk issues that one-element load (at a safe
+  // index when the token lies elsewhere) after the streaming loads, and it is consumed
+  // only at publication time, so nothing waits for it on the way.
+  const int pos = (jr < a.G) ? jr : (jr > a.G ? jr - a.G - 1 : -1);
+  const int xt = (pos >= 0) ? a.tokens[(size_t)b * a.G + pos] : -1;
+  const T *row = seq_row<T>(a, b, jr);
   float x[VPT][VEC];
-  load_chunk<T, ALIGNED>(seq_row<T>(a, b, jr), a.V, a.nvec, c, tid, x);
+  load_chunk<T, ALIGNED, true>(row, a.V, a.nvec, c, tid, x);
+  const bool tok_here = xt >= 0 && xt < a.V && (xt / Fmt<T>::VEC) / CHUNK_VECS == c;
+  const float zx = Fmt<T>::at(row, (size_t)(tok_here ? xt : 0));
   if (TOPK) {
-    const float tau = a.w.row_tau[r];
+    const float tau = a.w.row_tau[r];  // written by the previous kernel
 #pragma unroll
     for (int k = 0; k < VPT; ++k)
 #pragma unroll
@@ -382,13 +798,19 @@ __global__ __launch_bounds__(NT) void k_norm(const Args a) {
   for (int k = 0; k < VPT; ++k)
 #pragma unroll
     for (int e = 0; e < VEC; ++e) m = fmaxf(m, x[k][e]);
+  m = wave_max(m);
+  if (lane == 0) s_m[wid] = m;
+  __syncthreads();
+  m = s_m[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) m = fmaxf(m, s_m[w]);
 
+  const float k2 = a.k2;
   float off;
   double s;
-  const float k2 = a.k2;
   if (m > -INFINITY) {
     off = m * k2;
-    float acc[VPT];
+    float acc = 0.0f;
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
       float t[VEC];
@@ -398,10 +820,10 @@ __global__ __launch_bounds__(NT) void k_norm(const Args a) {
       for (int h = VEC / 2; h > 0; h >>= 1)
 #pragma unroll
         for (int e = 0; e < h; ++e) t[e] += t[e + h];
-      acc[k] = t[0];
+      acc += t[0];
     }
-    s = (double)((acc[0] + acc[1]) + (acc[2] + acc[3]));
-  } else {  // nothing finite here: keep a NaN visible, otherwise an empty partial
+    s = (double)acc;
+  } else {  // nothing finite in the chunk: keep a NaN visible, otherwise an empty partial
     off = -INFINITY;
     bool nan = false;
 #pragma unroll
@@ -410,74 +832,38 @@ __global__ __launch_bounds__(NT) void k_norm(const Args a) {
       for (int e = 0; e < VEC; ++e) nan |= (x[k][e] != x[k][e]);
     s = nan ? (double)NAN : 0.0;
   }
-  wave_lse(off, s);
-  if (lane == 0) {
-    s_off[wid] = off;
-    s_sum[wid] = s;
-  }
+  s = wave_sum(s);
+  if (lane == 0) s_s[wid] = s;
   __syncthreads();
-  if (tid == 0) {
-    float o = s_off[0];
-    double t = s_sum[0];
-    for (int w = 1; w < NW; ++w) lse_combine(o, t, s_off[w], s_sum[w]);
-    a.w.part_off[(size_t)r * a.C + c] = o;
-    a.w.part_sum[(size_t)r * a.C + c] = t;
-  }
-  if (!last_arrival(&a.w.t_row[r], (unsigned)a.C)) return;
+  if (wid != 0) return;  // one wave finishes the workgroup
 
-  // Row: combine the C chunk partials (strided per thread, then a fixed tree).
-  {
-    float o = -INFINITY;
-    double t = 0.0;
-    for (int cc = tid; cc < a.C; cc += NT)
-      lse_combine(o, t, a.w.part_off[(size_t)r * a.C + cc], a.w.part_sum[(size_t)r * a.C + cc]);
-    wave_lse(o, t);
-    __syncthreads();
-    if (lane == 0) {
-      s_off[wid] = o;
-      s_sum[wid] = t;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      o = s_off[0];
-      t = s_sum[0];
-      for (int w = 1; w < NW; ++w) lse_combine(o, t, s_off[w], s_sum[w]);
-      const bool ok = isfinite(o) && isfinite(t) && t > 0.0;
-      a.w.row_off[r] = o;
-      a.w.row_l2s[r] = ok ? log2(t) : 0.0;
-      a.w.row_ok[r] = ok ? 1 : 0;
-      if (!TOPK) a.w.row_tau[r] = -INFINITY;
-      if (a.row_stats) {
-        a.row_stats[(size_t)r * 2 + 0] = (float)((double)o * LN2);
-        a.row_stats[(size_t)r * 2 + 1] = (float)t;
-      }
-    }
+  const double S = (s_s[0] + s_s[1]) + (s_s[2] + s_s[3]);
+  if (lane == 0) {
+    st_dev(&a.w.part_off[(size_t)r * a.C + c], off);
+    st_dev(&a.w.part_sum[(size_t)r * a.C + c], S);
+    if (tok_here) st_dev(&a.w.row_zx[r], zx);
   }
-  if (!last_arrival(&a.w.t_seq[b], (unsigned)a.rps)) return;
-  sequence_scan<T, false>(a, b);
+  // Two ticket levels (chunks of a row, then rows of a sequence) keep the number of
+  // arrivals on any one counter small; every partial was complete before its
+  // workgroup's row ticket, so the sequence's last arrival sees all of them.
+  if (!wave_last_arrival(&a.w.t_row[r], (unsigned)a.C)) return;
+  if (!wave_last_arrival(&a.w.t_seq[b], (unsigned)a.rps)) return;
+  sequence_finish<T, false, TOPK>(a, b);
 }
 
 // ---------------------------------------------------------------- pass 1: greedy argmax
-
-// Largest value wins, ties go to the lower index; NaN and +inf mark the row unusable.
-SVD void best_combine(float &v, int &i, float v2, int i2) {
-  if (v2 > v || (v2 == v && i2 < i)) {
-    v = v2;
-    i = i2;
-  }
-}
 
 template <typename T, bool ALIGNED>
 __global__ __launch_bounds__(NT) void k_argmax(const Args a) {
   constexpr int VEC = Fmt<T>::VEC;
   __shared__ float s_v[NW];
   __shared__ int s_i[NW], s_f[NW];
-  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wid = tid / WAVE;
+  const int tid = threadIdx.x, lane = lane_id(), wid = tid / WAVE;
   const int r = blockIdx.x / a.C, c = blockIdx.x - r * a.C;
   const int b = r / a.rps, jr = r - b * a.rps;
 
   float x[VPT][VEC];
-  load_chunk<T, ALIGNED>(seq_row<T>(a, b, jr), a.V, a.nvec, c, tid, x);
+  load_chunk<T, ALIGNED, true>(seq_row<T>(a, b, jr), a.V, a.nvec, c, tid, x);
   float best = -INFINITY;
   int bi = 0x7fffffff, fl = 0;
 #pragma unroll
@@ -492,63 +878,31 @@ __global__ __launch_bounds__(NT) void k_argmax(const Args a) {
       fl |= ((z != z) || (z == INFINITY)) ? 1 : 0;
     }
   if (best > -INFINITY && best < INFINITY) fl |= 2;
-#pragma unroll
-  for (int o = WAVE / 2; o > 0; o >>= 1) {
-    const float v2 = __shfl_xor(best, o);
-    const int i2 = __shfl_xor(bi, o);
-    fl |= __shfl_xor(fl, o);
-    best_combine(best, bi, v2, i2);
-  }
+  wave_best(best, bi, fl);
   if (lane == 0) {
     s_v[wid] = best;
     s_i[wid] = bi;
     s_f[wid] = fl;
   }
   __syncthreads();
-  if (tid == 0) {
-    for (int w = 1; w < NW; ++w) {
-      best_combine(best, bi, s_v[w], s_i[w]);
-      fl |= s_f[w];
-    }
-    a.w.part_off[(size_t)r * a.C + c] = best;
-    a.w.part_idx[(size_t)r * a.C + c] = bi;
-    a.w.part_flag[(size_t)r * a.C + c] = fl;
-  }
-  if (!last_arrival(&a.w.t_row[r], (unsigned)a.C)) return;
+  if (wid != 0) return;  // one wave finishes the workgroup
 
-  {
-    best = -INFINITY;
-    bi = 0x7fffffff;
-    fl = 0;
-    for (int cc = tid; cc < a.C; cc += NT) {
-      best_combine(best, bi, a.w.part_off[(size_t)r * a.C + cc], a.w.part_idx[(size_t)r * a.C + cc]);
-      fl |= a.w.part_flag[(size_t)r * a.C + cc];
-    }
+  best = s_v[0];
+  bi = s_i[0];
+  fl = s_f[0];
 #pragma unroll
-    for (int o = WAVE / 2; o > 0; o >>= 1) {
-      const float v2 = __shfl_xor(best, o);
-      const int i2 = __shfl_xor(bi, o);
-      fl |= __shfl_xor(fl, o);
-      best_combine(best, bi, v2, i2);
-    }
-    __syncthreads();
-    if (lane == 0) {
-      s_v[wid] = best;
-      s_i[wid] = bi;
-      s_f[wid] = fl;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      for (int w = 1; w < NW; ++w) {
-        best_combine(best, bi, s_v[w], s_i[w]);
-        fl |= s_f[w];
-      }
-      a.w.row_arg[r] = bi;
-      a.w.row_ok[r] = (fl == 2) ? 1 : 0;
-    }
+  for (int w = 1; w < NW; ++w) {
+    best_combine(best, bi, s_v[w], s_i[w]);
+    fl |= s_f[w];
   }
-  if (!last_arrival(&a.w.t_seq[b], (unsigned)a.rps)) return;
-  sequence_scan<T, true>(a, b);
+  if (lane == 0) {
+    st_dev(&a.w.part_off[(size_t)r * a.C + c], best);
+    st_dev(&a.w.part_idx[(size_t)r * a.C + c], bi);
+    st_dev(&a.w.part_flag[(size_t)r * a.C + c], fl);
+  }
+  if (!wave_last_arrival(&a.w.t_row[r], (unsigned)a.C)) return;
+  if (!wave_last_arrival(&a.w.t_seq[b], (unsigned)a.rps)) return;
+  sequence_finish<T, true, false>(a, b);
 }
 
 // ---------------------------------------------------------------- pass 2: the draw
@@ -567,8 +921,8 @@ struct ResidualW {
   }
 };
 
-// Weights of a draw from the target row itself (bonus, or the zero-residual fallback),
-// relative to one chunk's offset as in the first kernel.
+// Weights of a draw from a target row itself (bonus, or the zero-residual fallback):
+// the first pass's terms of one chunk, recomputed bit for bit from its offset.
 struct TargetW {
   float k2, off, tau;
   SVD float operator()(float zt, float) const {
@@ -577,250 +931,257 @@ struct TargetW {
   }
 };
 
-// Inverse CDF inside one chunk: the element whose cumulative weight (in vocabulary
-// order) first exceeds t.  Segment masses and lane masses are summed in fixed orders;
-// when rounding leaves t at or past the chunk's total, the last element with positive
-// weight is taken.  If `store_total`, also returns the chunk total through *total.
-// Returns the element index within the row (block-uniform), or -1 for a zero chunk.
-template <typename T, bool ALIGNED, typename WFn>
-SVD int chunk_draw(const Args &a, const T *rowA, const T *rowB, int c, const WFn &wf, double t,
-                   bool search, double *total) {
+// Segment masses of vectors kbeg..kbeg+NK-1 of chunk c (whole workgroup): weights
+// wf(zA, zB) per element, a lane mass per vector (elements summed in order), and the
+// wave sum of each 64-vector segment into s_seg[k*NW + wave].  Loads are issued KG
+// vectors per thread at a time (KG = NK: every load in flight at once).
+template <typename T, bool ALIGNED, int KG, int NK, typename WFn>
+SVD void chunk_masses(const Args &a, const T *rowA, const T *rowB, int c, int kbeg, const WFn &wf,
+                      double *s_seg) {
   constexpr int VEC = Fmt<T>::VEC;
-  __shared__ double s_seg[SEGS];
-  __shared__ double s_t;
-  __shared__ int s_seg_pick, s_last_mode, s_result;
-  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wid = tid / WAVE;
+  const int tid = threadIdx.x, lane = lane_id(), wid = tid / WAVE;
+#pragma unroll
+  for (int kg = 0; kg < NK; kg += KG) {
+    const int k0 = kbeg + kg;
+    float xa[KG][VEC], xb[KG][VEC];
+    load_vectors<T, ALIGNED, false, KG>(rowA, a.V, a.nvec, c, k0, tid, xa);
+    if (rowB) {
+      load_vectors<T, ALIGNED, false, KG>(rowB, a.V, a.nvec, c, k0, tid, xb);
+    } else {
+#pragma unroll
+      for (int k = 0; k < KG; ++k)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) xb[k][e] = -INFINITY;
+    }
+#pragma unroll
+    for (int k = 0; k < KG; ++k) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc += wf(xa[k][e], xb[k][e]);
+      const double seg = wave_sum((double)acc);
+      if (lane == 0) s_seg[(k0 + k) * NW + wid] = seg;
+    }
+  }
+  __syncthreads();
+}
 
-  float xa[VPT][VEC], xb[VPT][VEC];
-  load_chunk<T, ALIGNED>(rowA, a.V, a.nvec, c, tid, xa);
-  if (rowB) {
-    load_chunk<T, ALIGNED>(rowB, a.V, a.nvec, c, tid, xb);
+// Inverse CDF inside segment s of chunk c, by one wave: each lane re-reads its vector of
+// the segment (rows A and B), recomputes the element weights and its lane mass exactly
+// as chunk_masses did, then picks lane and element.  With t = +inf the last positive
+// element is taken.  Returns the element index in the row (same in every lane), or -1.
+template <typename T, bool ALIGNED, typename WFn>
+SVD int segment_draw(const Args &a, const T *rowA, const T *rowB, int c, int s, const WFn &wf,
+                     double t) {
+  constexpr int VEC = Fmt<T>::VEC;
+  const int lane = lane_id();
+  const int k = s / NW, w = s % NW;
+  const int tid_equiv = w * WAVE + lane;  // the thread that held this vector
+  float xa[VEC], xb[VEC];
+  if (ALIGNED) {  // one 16-byte vector per row
+    const int v = c * CHUNK_VECS + k * NT + tid_equiv;
+    const bool in = v < a.nvec;
+    const int vs = in ? v : a.nvec - 1;
+    Fmt<T>::unpack(reinterpret_cast<const u32x4 *>(rowA)[vs], xa);
+    if (rowB) Fmt<T>::unpack(reinterpret_cast<const u32x4 *>(rowB)[vs], xb);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      xa[e] = in ? xa[e] : -INFINITY;
+      xb[e] = (in && rowB) ? xb[e] : -INFINITY;
+    }
   } else {
 #pragma unroll
-    for (int k = 0; k < VPT; ++k)
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) xb[k][e] = -INFINITY;
+    for (int e = 0; e < VEC; ++e) {
+      const long idx = elem_index<T>(c, k, tid_equiv, e);
+      const bool in = idx < a.V;
+      const size_t ii = (size_t)(in ? idx : (long)a.V - 1);
+      xa[e] = in ? Fmt<T>::at(rowA, ii) : -INFINITY;
+      xb[e] = (in && rowB) ? Fmt<T>::at(rowB, ii) : -INFINITY;
+    }
   }
-  float wv[VPT][VEC], ls[VPT];
+  float we[VEC];
+  float acc = 0.0f;
 #pragma unroll
-  for (int k = 0; k < VPT; ++k) {
+  for (int e = 0; e < VEC; ++e) {
+    we[e] = wf(xa[e], xb[e]);
+    acc += we[e];
+  }
+  auto lanem = [&](int) { return (double)acc; };
+  double lrem;
+  const int pl = wave_pick(WAVE, t, lanem, &lrem);
+  int res = -1;
+  if (lane == pl) {
+    int pe = -1, lastpe = -1;
+    double run = 0.0;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      if (we[e] > 0.0f) lastpe = e;
+      run += (double)we[e];
+      if (pe < 0 && we[e] > 0.0f && run > lrem) pe = e;
+    }
+    if (pe < 0) pe = lastpe;
+    res = (pe < 0) ? -1 : (int)elem_index<T>(c, k, tid_equiv, pe);
+  }
+  return __builtin_amdgcn_readlane(res, pl < 0 ? 0 : pl);
+}
+
+// Whole-chunk inverse CDF by one wave (rare path: the zero-residual fallback, after
+// the other waves of the workgroup have finished): segment masses one segment at a
+// time, then segment_draw.
+template <typename T, bool ALIGNED, typename WFn>
+SVD int wave_chunk_draw(const Args &a, const T *rowA, const T *rowB, int c, const WFn &wf,
+                        double t) {
+  constexpr int VEC = Fmt<T>::VEC;
+  __shared__ double s_wseg[SEGS];
+  const int lane = lane_id();
+  for (int sg = 0; sg < SEGS; ++sg) {
+    const int k = sg / NW, w = sg % NW;
     float acc = 0.0f;
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-      wv[k][e] = wf(xa[k][e], xb[k][e]);
-      acc += wv[k][e];
+      const long idx = elem_index<T>(c, k, w * WAVE + lane, e);
+      const bool in = idx < a.V;
+      const size_t ii = (size_t)(in ? idx : (long)a.V - 1);
+      const float za = in ? Fmt<T>::at(rowA, ii) : -INFINITY;
+      const float zb = (in && rowB) ? Fmt<T>::at(rowB, ii) : -INFINITY;
+      acc += wf(za, zb);
     }
-    ls[k] = acc;
-    const double seg = wave_sum((double)acc);
-    if (lane == 0) s_seg[k * NW + wid] = seg;
+    const double m = wave_sum((double)acc);
+    if (lane == 0) s_wseg[sg] = m;
   }
-  __syncthreads();
-  if (tid == 0) {
-    double cum = 0.0;
-    int pick = -1, lastpos = -1;
-    for (int sidx = 0; sidx < SEGS; ++sidx) {
-      const double m = s_seg[sidx];
-      if (m > 0.0) lastpos = sidx;
-      if (pick < 0 && search && cum + m > t) {
-        pick = sidx;
-        s_t = t - cum;
-      }
-      cum += m;
-    }
-    if (total) *total = cum;
-    s_last_mode = 0;
-    if (pick < 0) {  // rounding (or a zero chunk): take the last positive element
-      pick = lastpos;
-      s_last_mode = 1;
-      s_t = 0.0;
-    }
-    s_seg_pick = pick;
-    s_result = -1;
-  }
-  __syncthreads();
-  if (!search) return -1;
-  const int sp = s_seg_pick;
-  if (sp >= 0 && wid == sp % NW) {
-    const int kp = sp / NW;
-    float lsum = 0.0f;
-#pragma unroll
-    for (int k = 0; k < VPT; ++k)
-      if (k == kp) lsum = ls[k];
-    // inclusive scan of lane masses across the wave (double)
-    double cum = (double)lsum;
-#pragma unroll
-    for (int o = 1; o < WAVE; o <<= 1) {
-      const double up = __shfl_up(cum, o);
-      if (lane >= o) cum += up;
-    }
-    const double before = cum - (double)lsum;
-    const double tt = s_t;
-    const bool last_mode = s_last_mode != 0;
-    const unsigned long long cross = __ballot(!last_mode && cum > tt);
-    const unsigned long long posm = __ballot(lsum > 0.0f);
-    int pl;
-    bool lane_last = last_mode;
-    if (cross) {
-      pl = __ffsll((long long)cross) - 1;
-    } else {
-      pl = 63 - __clzll((long long)posm);
-      lane_last = true;
-    }
-    if (lane == pl) {
-      float we[VEC];
-#pragma unroll
-      for (int k = 0; k < VPT; ++k)
-        if (k == kp)
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) we[e] = wv[k][e];
-      int pe = -1, lastpe = -1;
-      double run = before;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        if (we[e] > 0.0f) lastpe = e;
-        run += (double)we[e];
-        if (pe < 0 && !lane_last && run > tt) pe = e;
-      }
-      if (pe < 0) pe = lastpe;
-      s_result = (int)elem_index<T>(c, kp, tid, pe);
-    }
-  }
-  __syncthreads();
-  return s_result;
+  __builtin_amdgcn_s_waitcnt(0);  // lane 0's LDS writes are done before any lane reads them
+  __builtin_amdgcn_wave_barrier();
+  auto segm = [&](int i) { return s_wseg[i]; };
+  double srem;
+  const int sp = wave_pick(SEGS, t, segm, &srem);
+  if (sp < 0) return -1;
+  return segment_draw<T, ALIGNED>(a, rowA, rowB, c, sp, wf, srem);
 }
 
-// Choose the chunk of a target row from the first kernel's partials (masses
-// S_c * 2^(off_c - off_row), summed in chunk order) and the in-chunk target.
-SVD void pick_chunk_from_partials(const Args &a, int r, float u, int *c_out, double *t_out) {
+// One wave: pick the chunk of target row r from the first pass's partials (mass
+// S_c * 2^(off_c - off_row)), and express the remainder in the chunk's own scale.
+SVD int pick_target_chunk(const Args &a, int r, float u, double *t_in) {
   const float off_r = a.w.row_off[r];
-  double total = 0.0;
-  for (int cc = 0; cc < a.C; ++cc) {
+  auto cm = [&](int cc) {
     const double s = a.w.part_sum[(size_t)r * a.C + cc];
-    if (s > 0.0) total += s * (double)fast_exp2(a.w.part_off[(size_t)r * a.C + cc] - off_r);
-  }
-  const double t = (double)u * total;
-  double cum = 0.0;
-  int pick = -1, lastpos = -1;
-  double tin = 0.0;
-  for (int cc = 0; cc < a.C; ++cc) {
-    const double s = a.w.part_sum[(size_t)r * a.C + cc];
-    if (!(s > 0.0)) continue;
     const float d = a.w.part_off[(size_t)r * a.C + cc] - off_r;
-    const double m = s * (double)fast_exp2(d);
-    lastpos = cc;
-    if (pick < 0 && cum + m > t) {
-      pick = cc;
-      tin = (t - cum) * (double)fast_exp2(-d);  // back in the chunk's own scale
-    }
-    cum += m;
-  }
-  if (pick < 0) {
-    pick = lastpos;
-    tin = INFINITY;  // past the end: the chunk search falls back to its last positive element
-  }
-  *c_out = pick;
-  *t_out = tin;
+    return (s > 0.0) ? s * (double)fast_exp2(d) : 0.0;
+  };
+  const double total = wave_total(a.C, cm);
+  double trem;
+  const int c = wave_pick(a.C, (double)u * total, cm, &trem);
+  *t_in = (c >= 0) ? trem * (double)fast_exp2(off_r - a.w.part_off[(size_t)r * a.C + c]) : 0.0;
+  return c;
 }
 
-template <typename T, bool ALIGNED>
-SVD int draw_from_target_row(const Args &a, int b, int jrow, float u) {
-  __shared__ int s_c;
-  __shared__ double s_tin;
-  const int r = b * a.rps + jrow;
-  if (threadIdx.x == 0) {
-    int c;
-    double tin;
-    pick_chunk_from_partials(a, r, u, &c, &tin);
-    s_c = c;
-    s_tin = tin;
-  }
-  __syncthreads();
-  const int c = s_c;
-  if (c < 0 || c >= a.C) return -1;  // no chunk with positive mass: nothing to draw
-  TargetW wf{a.k2, a.w.part_off[(size_t)r * a.C + c], a.w.row_tau[r]};
-  return chunk_draw<T, ALIGNED>(a, seq_row<T>(a, b, jrow), (const T *)nullptr, c, wf, s_tin, true,
-                                nullptr);
-}
-
+// Second kernel, NSUB workgroups per (sequence b, chunk c), after the first kernel has
+// published every sequence's job:
+//   reject at j: each workgroup computes the masses of [p_j - q_j]_+ of its quarter of
+//                the chunk per 64-vector segment and publishes them; the last of the
+//                sequence's workgroups reads all of them at once,
+//                picks chunk and segment, and one wave re-reads that segment to pick
+//                lane and element;
+//   bonus:       every chunk picks the chunk from the first kernel's partials; the
+//                picked one re-reads itself and draws from p_G.
 template <typename T, bool ALIGNED>
 __global__ __launch_bounds__(NT) void k_sample(const Args a) {
-  __shared__ double s_total;
-  __shared__ int s_c;
-  __shared__ double s_tc;
-  __shared__ int s_fallback;
-  const int tid = threadIdx.x;
-  const int b = blockIdx.x / a.C, c = blockIdx.x - b * a.C;
-  const int2 jk = a.w.job[b];
-  const int j = jk.x, kind = jk.y, G = a.G;
+  __shared__ double s_seg[SEGS];
+  const int tid = threadIdx.x, wid = tid / WAVE, lane = lane_id();
+  const int b = blockIdx.x / (a.C * NSUB);
+  const int rem = blockIdx.x - b * a.C * NSUB;
+  const int c = rem / NSUB, sub = rem - c * NSUB;
+  const int G = a.G;
   int32_t *out = a.out_tokens + (size_t)b * (G + 1);
+  const SeqJob jb = a.w.job[b];
+  const int j = jb.j, kind = jb.kind;
   const float u = a.u_sample[b];
-
-  // The job comes from the workspace: accept only well-formed ones, so that stale or
-  // foreign workspace contents can never become an out-of-range row index.
+  // Accept only well-formed jobs, so workspace contents can never become an
+  // out-of-range row or chunk index.
   if (!((kind == JOB_REJECT && j >= 0 && j < G) || (kind == JOB_BONUS && j == G))) return;
+
   if (kind == JOB_BONUS) {
-    if (tid == 0) {
-      int cp;
-      double tin;
-      pick_chunk_from_partials(a, b * a.rps + G, u, &cp, &tin);
-      s_c = cp;
-    }
-    __syncthreads();
-    if (s_c != c) return;  // also covers s_c == -1 (no chunk with positive mass)
-    const int tok = draw_from_target_row<T, ALIGNED>(a, b, G, u);
-    if (tid == 0) out[G] = tok;
+    // The scan already picked the chunk from p_G's partials; only that chunk works.
+    if (sub != 0 || c != jb.c_bonus) return;
+    const int r = b * a.rps + G;
+    const TargetW tw{a.k2, jb.off_bonus, a.w.row_tau[r]};
+    const T *row = seq_row<T>(a, b, G);
+    chunk_masses<T, ALIGNED, VPT, VPT>(a, row, (const T *)nullptr, c, 0, tw, s_seg);
+    if (wid != 0) return;
+    auto segm = [&](int i) { return s_seg[i]; };
+    double ts;
+    const int sp = wave_pick(SEGS, jb.t_bonus, segm, &ts);
+    const int tok = (sp >= 0) ? segment_draw<T, ALIGNED>(a, row, (const T *)nullptr, c, sp, tw, ts) : -1;
+    if (lane == 0) out[G] = tok;
     return;
   }
 
-  // Rejection at position j: mass of [p_j - q_j]_+ over this chunk.
-  const int rt = b * a.rps + j, rd = b * a.rps + G + 1 + j;
-  const double mt = (double)a.w.row_off[rt] + a.w.row_l2s[rt];
-  const double md = (double)a.w.row_off[rd] + a.w.row_l2s[rd];
+  // Rejection at position j.
+  const int rt = b * a.rps + j;
   ResidualW wf;
   wf.k2 = a.k2;
-  wf.mt_hi = (float)mt;
-  wf.mt_lo = (float)(mt - (double)wf.mt_hi);
-  wf.md_hi = (float)md;
-  wf.md_lo = (float)(md - (double)wf.md_hi);
-  wf.tau_t = a.w.row_tau[rt];
-  wf.tau_d = a.w.row_tau[rd];
+  wf.mt_hi = jb.mt_hi;
+  wf.mt_lo = jb.mt_lo;
+  wf.md_hi = jb.md_hi;
+  wf.md_lo = jb.md_lo;
+  wf.tau_t = jb.tau_t;
+  wf.tau_d = jb.tau_d;
   const T *row_t = seq_row<T>(a, b, j), *row_d = seq_row<T>(a, b, G + 1 + j);
-  chunk_draw<T, ALIGNED>(a, row_t, row_d, c, wf, 0.0, false, &s_total);
-  if (tid == 0) a.w.p2_chunk[(size_t)b * a.C + c] = s_total;
-  if (!last_arrival(&a.w.t_p2[b], (unsigned)a.C)) return;
+  chunk_masses<T, ALIGNED, KSUB, KSUB>(a, row_t, row_d, c, sub * KSUB, wf, s_seg);
+  if (wid != 0) return;  // wave 0 publishes and finishes
+  double *segs_b = a.w.p2_seg + (size_t)b * a.C * SEGS;
+  if (lane < KSUB * NW) {
+    const int sg = sub * KSUB * NW + lane;
+    st_dev(&segs_b[(size_t)c * SEGS + sg], s_seg[sg]);
+  }
+  if (!wave_last_arrival(&a.w.t_p2[b], (unsigned)(a.C * NSUB))) return;
 
-  if (tid == 0) {
-    double Z = 0.0;
-    for (int cc = 0; cc < a.C; ++cc) Z += a.w.p2_chunk[(size_t)b * a.C + cc];
-    s_fallback = !(Z > 0.0);
-    const double t = (double)u * Z;
-    double cum = 0.0;
-    int pick = -1, lastpos = -1;
-    double tc = 0.0;
-    for (int cc = 0; cc < a.C; ++cc) {
-      const double m = a.w.p2_chunk[(size_t)b * a.C + cc];
-      if (m > 0.0) lastpos = cc;
-      if (pick < 0 && m > 0.0 && cum + m > t) {
-        pick = cc;
-        tc = t - cum;
-      }
-      cum += m;
-    }
-    if (pick < 0) {
-      pick = lastpos;
-      tc = INFINITY;
-    }
-    s_c = pick;
-    s_tc = tc;
+  // Last chunk of the sequence: every segment mass of the sequence in one round trip,
+  // kept in LDS (read on demand beyond LDS_CHUNKS chunks); chunk totals are segment-order
+  // scans, so the segment pick inside the chosen chunk sums to exactly its total.
+  constexpr int LDS_CHUNKS = 64;
+  __shared__ double s_cs[LDS_CHUNKS * SEGS];
+  __shared__ double s_ct[LDS_CHUNKS];
+  const int ncache = (a.C < LDS_CHUNKS ? a.C : LDS_CHUNKS) * SEGS;
+  for (int i = lane; i < ncache; i += WAVE) s_cs[i] = ld_dev(&segs_b[i]);
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's LDS writes land before any lane reads them
+  __builtin_amdgcn_wave_barrier();
+  auto seg_of = [&](int i) { return (i < ncache) ? s_cs[i] : ld_dev(&segs_b[i]); };
+  for (int cc = 0; cc < a.C && cc < LDS_CHUNKS; ++cc) {
+    auto segm = [&](int i) { return seg_of(cc * SEGS + i); };
+    const double tot = wave_total(SEGS, segm);
+    if (lane == 0) s_ct[cc] = tot;
   }
-  __syncthreads();
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+  auto ctot = [&](int cc) {
+    if (cc < LDS_CHUNKS) return s_ct[cc];
+    auto segm = [&](int i) { return seg_of(cc * SEGS + i); };
+    return wave_total(SEGS, segm);
+  };
+  const double Z = wave_total(a.C, ctot);
   int tok = -1;
-  if (s_fallback) {  // zero residual (only through rounding): draw from p_j itself
-    tok = draw_from_target_row<T, ALIGNED>(a, b, j, u);
-  } else if (s_c >= 0 && s_c < a.C) {
-    tok = chunk_draw<T, ALIGNED>(a, row_t, row_d, s_c, wf, s_tc, true, nullptr);
+  if (Z > 0.0) {
+    double tc, ts;
+    const int cp = wave_pick(a.C, (double)u * Z, ctot, &tc);
+    if (cp >= 0 && cp < a.C) {
+      auto sm = [&](int i) { return seg_of(cp * SEGS + i); };
+      const int sp = wave_pick(SEGS, tc, sm, &ts);
+      if (sp >= 0) tok = segment_draw<T, ALIGNED>(a, row_t, row_d, cp, sp, wf, ts);
+    }
+  } else {  // zero residual (reachable only through rounding): draw from p_j itself
+    double tin;
+    const int cp = pick_target_chunk(a, rt, u, &tin);
+    if (cp >= 0 && cp < a.C) {
+      const TargetW tw{a.k2, a.w.part_off[(size_t)rt * a.C + cp], a.w.row_tau[rt]};
+      tok = wave_chunk_draw<T, ALIGNED>(a, row_t, (const T *)nullptr, cp, tw, tin);
+    }
   }
-  if (tid == 0) out[j] = tok;
+  if (lane == 0) out[j] = tok;
+}
+
+// First-pass kernel: one workgroup per chunk of every row (sequence-major).
+template <typename T, bool ALIGNED, bool TOPK>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6))) void k_norm(const Args a) {
+  norm_item<T, ALIGNED, TOPK>(a, blockIdx.x);
 }
 
 }  // namespace sv
@@ -839,8 +1200,8 @@ struct Plan {
   long long R;
   int digit_passes;
   // workspace offsets
-  size_t part_off, part_sum, part_idx, part_flag, row_off, row_l2s, row_ok, row_arg, row_tau,
-      tk_state, tk_hist, t_row, t_seq, t_p2, job, p2_chunk, total;
+  size_t part_off, part_sum, part_idx, part_flag, row_off, row_l2s, row_ok, row_arg, row_tau, row_zx,
+      tk_state, tk_hist, t_row, t_seq, t_p2, job, p2_seg, total;
   size_t zero_bytes;  // leading bytes (the tickets) that must be zero when a call starts
 };
 
@@ -854,7 +1215,7 @@ bool make_plan(int32_t B, int32_t G, int32_t V, sv_dtype dt, float T, int32_t to
   p.R = (long long)B * p.rps;
   p.topk = !p.greedy && top_k > 0 && top_k < V;
   p.digit_passes = (dt == SV_BF16) ? 2 : 4;
-  if (p.R * p.C > 0x7fffffffLL || (long long)B * p.C > 0x7fffffffLL) return false;
+  if (p.R * p.C + (long long)B * p.C > 0x7fffffffLL) return false;
   const size_t R = (size_t)p.R, C = (size_t)p.C, Bz = (size_t)B;
   size_t o = 0;
   // tickets first: the part that must start (and stays) at zero
@@ -871,10 +1232,11 @@ bool make_plan(int32_t B, int32_t G, int32_t V, sv_dtype dt, float T, int32_t to
   p.row_ok = o; o = align256(o + R * 4);
   p.row_arg = o; o = align256(o + R * 4);
   p.row_tau = o; o = align256(o + R * 4);
+  p.row_zx = o; o = align256(o + R * 4);
   p.tk_state = o; o = align256(o + (p.topk ? R * 8 : 0));
   p.tk_hist = o; o = align256(o + (p.topk ? R * C * 256 * 4 : 0));
-  p.job = o; o = align256(o + Bz * 8);
-  p.p2_chunk = o; o = align256(o + (p.greedy ? 0 : Bz * C * 8));
+  p.job = o; o = align256(o + Bz * sizeof(SeqJob));
+  p.p2_seg = o; o = align256(o + (p.greedy ? 0 : Bz * C * SEGS * 8));
   p.total = o;
   return true;
 }
@@ -891,18 +1253,20 @@ hipError_t launch_all(const Plan &p, const Args &a, hipStream_t st, void *const 
                       int *nl) {
   const dim3 blk(NT);
   const unsigned rows_grid = (unsigned)(p.R * p.C);
-  const unsigned seq_grid = (unsigned)((long long)a.B * p.C);
+  const unsigned seq_grid = (unsigned)((long long)a.B * p.C * NSUB);
   int n = 0;
   hipError_t e = hipSuccess;
-  auto rec = [&](int i) {
-    if (ev && i < nev) (void)hipEventRecord((hipEvent_t)ev[i], st);
-  };
+  // With events, kernel i is launched with (events[2i], events[2i+1]) as its start and
+  // stop events, which time the dispatch itself without extra packets on the stream.
   auto go = [&](const void *fn, unsigned grid, void **args) {
     if (e != hipSuccess) return;
-    e = hipLaunchKernel(fn, dim3(grid), blk, args, 0, st);
-    if (e == hipSuccess) rec(++n);
+    if (ev && 2 * n + 1 < nev)
+      e = hipExtLaunchKernel(fn, dim3(grid), blk, args, 0, st, (hipEvent_t)ev[2 * n],
+                             (hipEvent_t)ev[2 * n + 1], 0);
+    else
+      e = hipLaunchKernel(fn, dim3(grid), blk, args, 0, st);
+    if (e == hipSuccess) ++n;
   };
-  rec(0);
   Args aa = a;
   if (p.greedy) {
     void *args[] = {&aa};
@@ -974,13 +1338,14 @@ sv_status run(const void *target, const void *draft, sv_dtype dt, const int32_t 
   a.w.row_ok = (int *)(base + p.row_ok);
   a.w.row_arg = (int *)(base + p.row_arg);
   a.w.row_tau = (float *)(base + p.row_tau);
+  a.w.row_zx = (float *)(base + p.row_zx);
   a.w.tk_state = (uint2 *)(base + p.tk_state);
   a.w.tk_hist = (unsigned *)(base + p.tk_hist);
   a.w.t_row = (unsigned *)(base + p.t_row);
   a.w.t_seq = (unsigned *)(base + p.t_seq);
   a.w.t_p2 = (unsigned *)(base + p.t_p2);
-  a.w.job = (int2 *)(base + p.job);
-  a.w.p2_chunk = (double *)(base + p.p2_chunk);
+  a.w.job = (SeqJob *)(base + p.job);
+  a.w.p2_seg = (double *)(base + p.p2_seg);
 
   hipStream_t st = (hipStream_t)stream;
   int n = 0;
