@@ -148,6 +148,52 @@ def cpu_baseline(host_sets, cfg, seconds: float):
                       f"{el:.1f} s; the oracle stops reading each sequence at its first rejection"}
 
 
+def summarize_counters(kdir: str, cdir: str, out: Path) -> None:
+    """Turn rocprofv3 --pmc CSV output into the traffic summary bench.py reads.
+
+    kdir holds the FETCH_SIZE and WRITE_SIZE runs of the benchmark, cdir those of the
+    copy probe.  Counters are KiB per dispatch; each is scaled by (bytes the copy
+    really moves) / (what the counter read for it): a copy of N bytes reads N and
+    writes N.
+    """
+    import csv
+    import glob
+
+    def per_dispatch(d, counter, kernel_pred):
+        vals = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for row in csv.DictReader(open(f)):
+                if row.get("Counter_Name") == counter and kernel_pred(row):
+                    vals.append(float(row["Counter_Value"]))
+        return vals
+
+    is_knorm = lambda r: "k_norm" in r["Kernel_Name"] and int(r.get("Grid_Size", r.get("Grid_Size_X", 0)) or 0) >= 576 * 8 * 256
+    is_copy = lambda r: ("copy" in r["Kernel_Name"].lower() or "elementwise" in r["Kernel_Name"].lower())
+    probe = json.loads(open(os.path.join(cdir, "probe.json")).read())
+    nbytes = probe["copy_probe_bytes"]
+    cf = per_dispatch(cdir, "FETCH_SIZE", is_copy)
+    cw = per_dispatch(cdir, "WRITE_SIZE", is_copy)
+    kf = per_dispatch(kdir, "FETCH_SIZE", is_knorm)
+    kw = per_dispatch(kdir, "WRITE_SIZE", is_knorm)
+    copy_f = max(cf) * 1024.0
+    copy_w = max(cw) * 1024.0
+    f_fetch, f_write = nbytes / copy_f, nbytes / copy_w
+    fetch = float(np.median(kf)) * 1024.0 * f_fetch
+    write = float(np.median(kw)) * 1024.0 * f_write
+    res = {"kernel": "k_norm", "workload": "zipf_bf16_b64 (B=64, G=4, V=128256, bf16)",
+           "dispatches": {"fetch": len(kf), "write": len(kw)},
+           "fetch_kib_median": float(np.median(kf)), "write_kib_median": float(np.median(kw)),
+           "copy_probe_bytes": nbytes, "copy_fetch_kib": max(cf), "copy_write_kib": max(cw),
+           "scale_fetch": f_fetch, "scale_write": f_write,
+           "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
+           "traffic_bytes_per_launch": fetch + write,
+           "algorithmic_bytes": 147750912,
+           "source_sha256": hashlib.sha256(SOURCE.read_bytes()).hexdigest(),
+           "note": "FETCH_SIZE and WRITE_SIZE from separate rocprofv3 --pmc runs, scaled by a plain copy"}
+    out.write_text(json.dumps(res, indent=1) + "\n")
+    print(json.dumps(res))
+
+
 def copy_probe(nbytes: int, reps: int) -> None:
     """A plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
     import torch
@@ -172,14 +218,19 @@ def main() -> int:
                     help="time the loop without per-kernel events")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES (counter calibration)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("BENCH_DIR", "COPY_DIR"),
+                    help="write the traffic summary from rocprofv3 --pmc CSV directories")
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+        print(f"bench.py runs on one GPU; spec_verify has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
         return 2
     if args.copy_probe:
         copy_probe(args.copy_probe, 10)
+        return 0
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters[0], args.summarize_counters[1], COUNTERS)
         return 0
 
     import torch
@@ -219,31 +270,42 @@ def main() -> int:
     log(f"[bench] warmup done ({args.warmup} calls)")
 
     K = args.steps
-    # one (start, stop) event pair per kernel and step, attached to the dispatches themselves
-    stage = None if args.no_stage_events else [hev.create(2 * nl) for _ in range(K)]
+    # Timed region 1: K steps exactly as a caller runs them -> value, ms_per_step.
     loop_ev = hev.create(2)
-    emitted = torch.zeros((), dtype=torch.int64, device=dev)
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
     hev.record(loop_ev[0], stream)
     for i in range(K):
-        call(args.warmup + i, None if stage is None else stage[i])
+        call(args.warmup + i)
     hev.record(loop_ev[1], stream)
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
     gpu_ms = hev.elapsed_ms(loop_ev[0], loop_ev[1])
     log(f"[bench] timed {K} calls: wall {wall * 1e3:.2f} ms, events {gpu_ms:.2f} ms")
 
+    # Timed region 2: the same K steps with a (start, stop) event pair attached to every
+    # kernel dispatch (hipExtLaunchKernel) -> each kernel's average duration.  The pairs
+    # add a few microseconds of gap between kernels, so region 1 gives the throughput.
     per_kernel = {}
-    if stage is not None:
+    wall2 = None
+    if not args.no_stage_events:
+        stage = [hev.create(2 * nl) for _ in range(K)]
+        torch.cuda.synchronize(dev)
+        t1 = time.perf_counter()
+        for i in range(K):
+            call(args.warmup + i, stage[i])
+        torch.cuda.synchronize(dev)
+        wall2 = time.perf_counter() - t1
         durs = np.array([[hev.elapsed_ms(ev[2 * j], ev[2 * j + 1]) for j in range(nl)] for ev in stage])
         for j, name in enumerate(plan):
             per_kernel[f"{j}:{name}"] = float(np.mean(durs[:, j]) * 1e3)
         for ev in stage:
             hev.destroy(ev)
+        log(f"[bench] timed {K} calls with per-kernel events: wall {wall2 * 1e3:.2f} ms")
     hev.destroy(loop_ev)
 
     # emitted tokens for the last call of each set (accepted + 1 per valid sequence)
+    emitted = torch.zeros((), dtype=torch.int64, device=dev)
     for s_i in range(min(n_sets, K)):
         call(s_i)
         emitted += (acc.clamp(min=-1) + 1).sum()
@@ -277,6 +339,7 @@ def main() -> int:
         "mean_accepted_plus_one": round(mean_emitted / B, 4),
         "gpu_event_ms_per_step": round(gpu_ms / K, 5),
         "per_kernel_us": {k: round(v, 3) for k, v in per_kernel.items()},
+        "ms_per_step_with_kernel_events": None if wall2 is None else round(wall2 * 1e3 / K, 5),
         "roofline": roof,
         "traffic_note": tnote,
     }
