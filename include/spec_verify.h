@@ -22,9 +22,10 @@
  *     current HIP device; sizes are element counts.  Logit rows must be aligned to
  *     their element size (2 bytes for bf16, 4 for f32); rows whose byte length is a
  *     multiple of 16 with 16-byte-aligned bases take the vector-load path.
- *   - The caller owns every buffer.  The library allocates nothing, keeps no state
- *     between calls, and never synchronises: work is enqueued on `stream` (a
- *     hipStream_t; NULL is the default stream) and results are valid in stream order.
+ *   - The caller owns every buffer.  The library allocates nothing, keeps no data
+ *     between calls (only a process-wide counter that gives each call a distinct tag),
+ *     and never synchronises: work is enqueued on `stream` (a hipStream_t; NULL is the
+ *     default stream) and results are valid in stream order.
  *   - On any status other than SV_OK nothing has been enqueued and outputs are
  *     untouched.  Row-level data problems are not statuses: they are reported per
  *     sequence in accepted_len (codes below).
@@ -61,18 +62,25 @@ typedef enum {
                                 /* the draft cannot have proposed x_i                        */
 #define SV_ROW_BAD_LOGITS (-3)  /* a row of the sequence holds NaN or +inf, or no finite logit */
 #define SV_ROW_BAD_UNIFORM (-4) /* sampling: a u_accept or u_sample value outside [0, 1)    */
+/* Not a data problem: a workgroup of the sampling kernel gave up waiting for results of
+ * workgroups earlier in its grid (a bounded wait of about a second that ordinary
+ * scheduling never reaches).  The sequence's out_tokens are then incomplete. */
+#define SV_ROW_INTERNAL (-5)
 
 /* Bytes of device workspace spec_verify needs for these arguments (0 never occurs). */
 size_t sv_workspace_bytes(int32_t B, int32_t G, int32_t V, sv_dtype dtype, float temperature,
                           int32_t top_k);
 
-/* Leading bytes of the workspace (self-resetting counters) that must be zero when a call
- * with these arguments starts; 0 for arguments spec_verify would reject.  A completed
- * call leaves exactly its own leading sv_workspace_zero_bytes(...) bytes at zero and may
- * overwrite everything after them.  So one zero-fill serves any number of calls with
- * the same arguments; before a call whose zero prefix is longer than the previous call's
- * on the same workspace, zero the longer prefix again (a fill kernel on the same stream
- * suffices).  Calls that share a workspace must not overlap in time. */
+/* Leading bytes of the workspace (words that workgroups hand to one another, each marked
+ * with a tag unique to its kernel launch) that must be zero when a workspace is first
+ * used with these arguments;
+ * 0 for arguments spec_verify would reject.  A completed call leaves its own leading
+ * sv_workspace_zero_bytes(...) bytes holding zeros and marks of completed calls, which
+ * every later call treats as zero, and may overwrite everything after them.  So one
+ * zero-fill serves any number of calls with the same arguments; before a call whose
+ * zero prefix is longer than the previous call's on the same workspace, zero the longer
+ * prefix again (a fill kernel on the same stream suffices).  Calls that share a
+ * workspace must not overlap in time. */
 size_t sv_workspace_zero_bytes(int32_t B, int32_t G, int32_t V, sv_dtype dtype,
                                float temperature, int32_t top_k);
 

@@ -40,6 +40,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "spec_verify.h"
 
 #define SVD __device__ __forceinline__
@@ -54,10 +56,21 @@ constexpr int CHUNK_VECS = NT * VPT;   // vectors per chunk (32 KiB of logits)
 constexpr int SEGS = VPT * NW;         // 64-vector segments per chunk
 constexpr int NSUB = 4;                // second-pass workgroups per chunk of a rejected pair
 constexpr int KSUB = VPT / NSUB;       // vectors per thread of each of them
+constexpr unsigned SPIN_LIMIT = 1u << 20;  // polls before a waiting wave gives up (~a second)
 constexpr double LN2 = 0.69314718055994530942;
 constexpr double LOG2E = 1.44269504088896340736;
 
-enum : int { JOB_NONE = 0, JOB_REJECT = 1, JOB_BONUS = 2 };
+enum : int { JOB_NONE = 0, JOB_REJECT = 1, JOB_BONUS = 2 };  // NONE: a row error, nothing to draw
+
+// The acceptance scan's record for the draw of one sequence: JW tagged words, field f
+// in word f (ints as their bits, floats as theirs; a double as a float head and tail).
+enum : int {
+  JW_J, JW_KIND, JW_CBONUS, JW_OFFBONUS, JW_TB_HI, JW_TB_LO,  // bonus: chunk, its offset, u*S left in it
+  JW_MT_HI, JW_MT_LO, JW_MD_HI, JW_MD_LO,                    // rejection: log2-partitions of p_j, q_j
+  JW_TAU_T, JW_TAU_D,                                        // top-k thresholds (bonus: row G in TAU_T)
+  JW_OFF_J,                                                  // rejection: row offset of p_j
+  JW_USED, JW = 16
+};
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
@@ -179,34 +192,19 @@ SVD long elem_index(int c, int k, int tid, int e) {
 
 // ---------------------------------------------------------------- arguments
 
-// What the acceptance scan of a sequence hands to the second kernel, in one record.
-struct SeqJob {
-  int j, kind;                 // first rejected position (G: all accepted); JOB_*
-  int c_bonus, pad;            // bonus: the chunk of p_G holding u*S, picked from partials
-  float mt_hi, mt_lo, md_hi, md_lo;  // rejection: log2-partitions of p_j and q_j, head + tail
-  float tau_t, tau_d;          // rejection: top-k thresholds of rows j (or -inf)
-  float off_bonus, pad2;       // bonus: offset of chunk c_bonus
-  double t_bonus;              // bonus: u*S minus the mass before c_bonus, in the chunk's scale
-};
+typedef unsigned long long u64;
 
 struct Work {                  // carved from the caller's workspace
-  float *part_off;             // [R*C] chunk offset m_c*k2 / greedy: chunk best value
-  double *part_sum;            // [R*C] chunk sum of 2^(z*k2 - off)
-  int *part_idx;               // [R*C] greedy: chunk best index
-  int *part_flag;              // [R*C] greedy: 1 = NaN/+inf seen, 2 = finite seen
-  float *row_off;              // [R] row offset
-  double *row_l2s;             // [R] log2 of the row sum: log2-partition = off + l2s
-  int *row_ok;                 // [R] row usable
-  int *row_arg;                // [R] greedy argmax
-  float *row_tau;              // [R] top-k threshold (raw logit); rows with no cut: -inf
-  float *row_zx;               // [R] the row's logit at its position's drafted token (NaN if none)
+  // tagged words (see tw_put)
+  u64 *tw_part;                // [R*C*3] per chunk: sampling offset m_c*k2 and sum of
+                               //   2^(z*k2 - off) (head, tail); greedy best value, index, flags
+  u64 *tw_zx;                  // [R] the row's logit at its position's drafted token
+  u64 *tw_job;                 // [B*JW] the acceptance scan's record for the draw
+  u64 *tw_seg;                 // [B*C*SEGS*2] residual mass per 64-vector segment (head, tail)
+  u64 *tw_hist;                // [R*C*128] top-k digit histogram per chunk (16-bit counts)
+  // plain, handed from one kernel to the next
+  float *row_tau;              // [R] top-k threshold (raw logit)
   uint2 *tk_state;             // [R] radix-select prefix and remaining rank
-  unsigned *tk_hist;           // [R*C*256] per-chunk digit histograms
-  unsigned *t_row;             // [R] tickets (self-resetting)
-  unsigned *t_seq;             // [B]
-  unsigned *t_p2;              // [B]
-  struct SeqJob *job;          // [B] the acceptance scan's result for the second kernel
-  double *p2_seg;              // [B*C*SEGS] residual mass per 64-vector segment
 };
 
 struct Args {
@@ -218,6 +216,8 @@ struct Args {
   int top_k;
   int32_t *accepted_len, *out_tokens;
   float *row_stats;
+  unsigned tag;                // this call's tag (never 0): marks the words it publishes
+  unsigned spin_limit;         // polls a waiting wave makes before giving up
   Work w;
 };
 
@@ -332,31 +332,20 @@ SVD T ld_dev(const T *p) {
   return __hip_atomic_load(const_cast<T *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Is this the last of n arrivals at *ctr?  The caller's device-scope stores have
-// completed (s_waitcnt on all counters) before the ticket is taken, so the winner sees
-// every other arrival's published results.  The counter wraps back to zero on the last
-// arrival, ready for the next call.  wave_last_arrival is taken by one wave alone;
-// block_last_arrival by a whole workgroup.
-SVD bool wave_last_arrival(unsigned *ctr, unsigned n) {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  unsigned old = 0;
-  if (lane_id() == 0) old = __builtin_amdgcn_atomic_inc32(ctr, n - 1, __ATOMIC_RELAXED, "agent");
-  return (unsigned)__builtin_amdgcn_readlane((int)old, 0) == n - 1;
-}
-
-SVD bool block_last_arrival(unsigned *ctr, unsigned n) {
-  __shared__ int s_last;
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __syncthreads();
-  if (threadIdx.x == 0)
-    s_last = (__builtin_amdgcn_atomic_inc32(ctr, n - 1, __ATOMIC_RELAXED, "agent") == n - 1);
-  __syncthreads();
-  return s_last != 0;
-}
+// Tagged words.  Inside the sampling kernel every value one workgroup hands to another
+// travels as a 64-bit word (call tag << 32 | 32-bit payload) written and read with one
+// device-scope 64-bit store / load, which is single-copy atomic.  A reader takes a word
+// as present when it carries this call's tag: no fence, store wait or counter is needed,
+// and a record is complete once all of its words carry the tag.  A double travels as a
+// float head and tail (d ~ head + tail to 2^-48).  The only waits are polls of words
+// written by workgroups that come earlier in the grid.
+SVD void tw_put(u64 *p, unsigned tag, unsigned bits) { st_dev(p, ((u64)tag << 32) | (u64)bits); }
+SVD void tw_putf(u64 *p, unsigned tag, float f) { tw_put(p, tag, __float_as_uint(f)); }
+SVD bool tw_ok(u64 w, unsigned tag) { return (unsigned)(w >> 32) == tag; }
+SVD float tw_f(u64 w) { return __uint_as_float((unsigned)w); }
+SVD float d_head(double d) { return (float)d; }
+SVD float d_tail(double d) { return (float)(d - (double)(float)d); }
+SVD double d_join(float hi, float lo) { return (double)hi + (double)lo; }
 
 // Order-preserving 32-bit key of a float (bf16 values are floats with zero low half);
 // -0 and +0 share a key.
@@ -422,18 +411,22 @@ SVD int wave_pick(int n, double t, const MFn &mfn, double *t_rem) {
 // One radix-select digit (bits [shift, shift+8) of the key) for every row.  The prefix
 // of higher digits and the remaining rank come from the previous pass.  The threshold
 // kept in row_tau is the smallest value whose key has the final prefix, so the kept set
-// {z >= tau} is exactly the values >= the k-th largest, ties included.
+// {z >= tau} is exactly the values >= the k-th largest, ties included.  Each chunk
+// publishes its digit histogram as 128 tagged words (two 16-bit counts each; a chunk
+// holds at most 16384 values); the row's last chunk in grid order collects them.
 template <typename T, bool ALIGNED>
 __global__ __launch_bounds__(NT) void k_topk_digit(const Args a, int pass, int last_pass) {
   constexpr int VEC = Fmt<T>::VEC;
   __shared__ unsigned hist[256];
   __shared__ unsigned s_ge[256];
+  __shared__ int s_alive;
   const int tid = threadIdx.x;
   const int r = blockIdx.x / a.C, c = blockIdx.x - r * a.C;
   const int b = r / a.rps, jr = r - b * a.rps;
   const int shift = 24 - 8 * pass;
   const uint2 st = (pass == 0) ? make_uint2(0u, (unsigned)a.top_k) : a.w.tk_state[r];
   const uint32_t hi_mask = (pass == 0) ? 0u : (0xffffffffu << (shift + 8));
+  const unsigned tag = a.tag;
 
   hist[tid] = 0u;
   __syncthreads();
@@ -449,14 +442,41 @@ __global__ __launch_bounds__(NT) void k_topk_digit(const Args a, int pass, int l
       }
     }
   __syncthreads();
-  st_dev(&a.w.tk_hist[((size_t)r * a.C + c) * 256 + tid], hist[tid]);
-  if (!block_last_arrival(&a.w.t_row[r], (unsigned)a.C)) return;
+  u64 *hw = a.w.tw_hist + (size_t)r * a.C * 128;
+  if (c != a.C - 1) {
+    if (tid < 128) tw_put(&hw[(size_t)c * 128 + tid], tag, hist[2 * tid] | (hist[2 * tid + 1] << 16));
+    return;
+  }
 
-  // Row total of digit d = tid, then counts of keys with digit >= d.
+  // The row's last chunk: wait for the other chunks' histograms (every load in flight
+  // at once), then the row total of digit d = tid.
   unsigned tot = 0;
-  for (int cc = 0; cc < a.C; ++cc) tot += ld_dev(&a.w.tk_hist[((size_t)r * a.C + cc) * 256 + tid]);
+  unsigned polls = 0;
+  for (;;) {
+    tot = hist[tid];
+    bool ok = true;
+    for (int cc = 0; cc < a.C - 1; ++cc) {
+      const u64 w = ld_dev(&hw[(size_t)cc * 128 + (tid >> 1)]);
+      ok = ok && tw_ok(w, tag);
+      tot += ((unsigned)w >> ((tid & 1) * 16)) & 0xffffu;
+    }
+    if (__syncthreads_and(ok ? 1 : 0)) break;
+    if (++polls >= a.spin_limit) break;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  // A row whose collector gave up (here or in an earlier pass) carries a marker to the
+  // end: tk_state (~0, ~0), then a NaN threshold, which the scan reports as an error.
+  const bool dead = st.x == 0xffffffffu && st.y == 0xffffffffu;
+  if (tid == 0) s_alive = polls < a.spin_limit && !dead;
   s_ge[tid] = tot;
   __syncthreads();
+  if (!s_alive) {
+    if (tid == 0) {
+      if (last_pass) a.w.row_tau[r] = NAN;
+      else a.w.tk_state[r] = make_uint2(0xffffffffu, 0xffffffffu);
+    }
+    return;
+  }
   for (int o = 1; o < 256; o <<= 1) {  // suffix sums (Hillis-Steele)
     const unsigned add = (tid + o < 256) ? s_ge[tid + o] : 0u;
     __syncthreads();
@@ -504,177 +524,365 @@ SVD void wave_best(float &v, int &i, int &fl) {
 constexpr int SEQ_LDS_PARTS = 256;   // (row, chunk) partials of one sequence staged in LDS
 constexpr int SEQ_LDS_ROWS = 129;    // rows of one sequence kept in LDS (G <= 64)
 
-// The last chunk of sequence b to finish (one wave) combines every row of the sequence
-// from its chunk partials, then runs the acceptance scan.  Position i of the chain:
-// token range, row validity, uniform range, draft support, then the test
-// U_i <= min(1, p_i(x)/q_i(x)) with p_i(x) > 0 ("Speculative Decoding 的朴素思想",
-// "一次 sampling 怎么执行" step 4; the ratio is formed from log2-probabilities in double).
-// Greedy: acceptance is equality with the target argmax.  All partials and token
-// logits come in with one round of loads; the inputs (tokens, uniforms) are loaded
-// first so they arrive meanwhile.
-template <typename T, bool GREEDY, bool TOPK>
-SVD void sequence_finish(const Args &a, int b) {
-  constexpr int PG = GREEDY ? SEQ_LDS_PARTS : 1, PS = GREEDY ? 1 : SEQ_LDS_PARTS;
-  constexpr int RG = GREEDY ? SEQ_LDS_ROWS : 1, RS = GREEDY ? 1 : SEQ_LDS_ROWS;
+// Greedy (T == 0): the sequence's finisher -- its last item in grid order, one wave --
+// waits until every chunk partial of the sequence carries this call's tag, combines each
+// row (largest value, lowest index; NaN / +inf mark a row unusable), then scans:
+// position i is accepted when the drafted token equals the target argmax
+// ("tannlonggtaoo" note, "Greedy Sampling"); the first mismatch, or the bonus position,
+// takes the target argmax.  Its own partial (index np - 1) comes from its registers.
+template <typename T>
+SVD void greedy_finish(const Args &a, int b, float own_best, int own_idx, int own_flag) {
+  constexpr int UNR = SEQ_LDS_PARTS / WAVE;
   __shared__ float s_po[SEQ_LDS_PARTS];
-  __shared__ double s_ps[PS];
-  __shared__ int s_pi[PG], s_pf[PG];
-  __shared__ float s_roff[RS], s_rzx[RS], s_rtau[RS];
-  __shared__ double s_rl2s[RS];
-  __shared__ int s_rok[SEQ_LDS_ROWS], s_rarg[RG];
+  __shared__ int s_pi[SEQ_LDS_PARTS], s_pf[SEQ_LDS_PARTS];
+  __shared__ int s_rok[SEQ_LDS_ROWS], s_rarg[SEQ_LDS_ROWS];
   const int lane = lane_id();
   const int G = a.G, rps = a.rps, C = a.C;
   const size_t r0 = (size_t)b * rps;
-  const bool lds = rps * C <= SEQ_LDS_PARTS && rps <= SEQ_LDS_ROWS;
-
-  // inputs of positions lane, lane+64, ... (first round only kept in registers)
+  const int np = rps * C, own = np - 1;
+  const bool lds = np <= SEQ_LDS_PARTS && rps <= SEQ_LDS_ROWS;
+  const unsigned tag = a.tag;
+  const u64 *pw = a.w.tw_part + r0 * C * 3;
   const int x0 = (lane < G) ? a.tokens[(size_t)b * G + lane] : 0;
-  const float u0 = (!GREEDY && lane < G) ? a.u_accept[(size_t)b * G + lane] : 0.0f;
-  const float us = GREEDY ? 0.0f : a.u_sample[b];
 
-  // Stage the partials of every (row, chunk) of the sequence and the token logits in
-  // LDS: every lane issues all of its loads before any of them is waited for.
-  if (lds) {
-    constexpr int UNR = SEQ_LDS_PARTS / WAVE;
-    const int np = rps * C;
-    if (GREEDY) {
-      float vo[UNR];
-      int vi[UNR], vf[UNR];
+  bool alive = true;
+  unsigned polls = 0;
+  for (int blk = 0; blk < np && alive; blk += SEQ_LDS_PARTS) {
+    for (;;) {
+      u64 w0[UNR], w1[UNR], w2[UNR];
 #pragma unroll
       for (int k = 0; k < UNR; ++k) {
-        const int i = lane + k * WAVE;
-        const int ii = (i < np) ? i : 0;
-        vo[k] = ld_dev(&a.w.part_off[r0 * C + ii]);
-        vi[k] = ld_dev(&a.w.part_idx[r0 * C + ii]);
-        vf[k] = ld_dev(&a.w.part_flag[r0 * C + ii]);
+        const int i = blk + lane + k * WAVE;
+        const int ii = (i < np && i != own) ? i : 0;
+        w0[k] = ld_dev(&pw[(size_t)ii * 3 + 0]);
+        w1[k] = ld_dev(&pw[(size_t)ii * 3 + 1]);
+        w2[k] = ld_dev(&pw[(size_t)ii * 3 + 2]);
       }
+      bool ok = true;
 #pragma unroll
       for (int k = 0; k < UNR; ++k) {
-        const int i = lane + k * WAVE;
-        if (i < np) {
-          s_po[i] = vo[k];
-          s_pi[i] = vi[k];
-          s_pf[i] = vf[k];
+        const int i = blk + lane + k * WAVE;
+        if (i < np && i != own) ok = ok && tw_ok(w0[k], tag) && tw_ok(w1[k], tag) && tw_ok(w2[k], tag);
+      }
+      if (__ballot(!ok) == 0) {
+        if (lds) {
+#pragma unroll
+          for (int k = 0; k < UNR; ++k) {
+            const int i = lane + k * WAVE;
+            if (i < np) {
+              s_po[i] = (i == own) ? own_best : tw_f(w0[k]);
+              s_pi[i] = (i == own) ? own_idx : (int)(unsigned)w1[k];
+              s_pf[i] = (i == own) ? own_flag : (int)(unsigned)w2[k];
+            }
+          }
         }
+        break;
       }
+      if (++polls >= a.spin_limit) {
+        alive = false;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  int32_t *out = a.out_tokens + (size_t)b * (G + 1);
+  if (!alive) {  // gave up waiting: report it
+    for (int i = lane; i <= G; i += WAVE) out[i] = -1;
+    if (lane == 0) a.accepted_len[b] = SV_ROW_INTERNAL;
+    return;
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+  auto part = [&](int jr, int cc, float &v, int &i, int &f) {
+    const int k = jr * C + cc;
+    if (lds) {
+      v = s_po[k];
+      i = s_pi[k];
+      f = s_pf[k];
+    } else if (k == own) {
+      v = own_best;
+      i = own_idx;
+      f = own_flag;
     } else {
-      float vo[UNR];
-      double vs[UNR];
-#pragma unroll
-      for (int k = 0; k < UNR; ++k) {
-        const int i = lane + k * WAVE;
-        const int ii = (i < np) ? i : 0;
-        vo[k] = ld_dev(&a.w.part_off[r0 * C + ii]);
-        vs[k] = ld_dev(&a.w.part_sum[r0 * C + ii]);
-      }
-      constexpr int RUNR = (SEQ_LDS_ROWS + WAVE - 1) / WAVE;
-      float zx[RUNR], tau[RUNR];
-#pragma unroll
-      for (int k = 0; k < RUNR; ++k) {
-        const int jr = lane + k * WAVE;
-        const int jj = (jr < rps) ? jr : 0;
-        zx[k] = ld_dev(&a.w.row_zx[r0 + jj]);
-        tau[k] = TOPK ? a.w.row_tau[r0 + jj] : -INFINITY;  // top-k: the previous kernel's
-      }
-#pragma unroll
-      for (int k = 0; k < UNR; ++k) {
-        const int i = lane + k * WAVE;
-        if (i < np) {
-          s_po[i] = vo[k];
-          s_ps[i] = vs[k];
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < RUNR; ++k) {
-        const int jr = lane + k * WAVE;
-        if (jr < rps) {
-          s_rzx[jr] = zx[k];
-          s_rtau[jr] = tau[k];
-        }
-      }
+      v = tw_f(ld_dev(&pw[(size_t)k * 3]));
+      i = (int)(unsigned)ld_dev(&pw[(size_t)k * 3 + 1]);
+      f = (int)(unsigned)ld_dev(&pw[(size_t)k * 3 + 2]);
+    }
+  };
+  auto combine_row = [&](int jr, int &arg, int &ok) {
+    float best = -INFINITY;
+    int bi = 0x7fffffff, fl = 0;
+    for (int cc = 0; cc < C; ++cc) {
+      float v;
+      int i, f;
+      part(jr, cc, v, i, f);
+      best_combine(best, bi, v, i);
+      fl |= f;
+    }
+    arg = bi;
+    ok = (fl == 2) ? 1 : 0;
+  };
+  if (lds) {
+    for (int jr0 = 0; jr0 < rps; jr0 += WAVE) {  // lane jr combines row jr in chunk order
+      const int jr = jr0 + lane;
+      if (jr < rps) combine_row(jr, s_rarg[jr], s_rok[jr]);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_wave_barrier();
   }
-  auto p_off = [&](int jr, int cc) { return lds ? s_po[jr * C + cc] : ld_dev(&a.w.part_off[(r0 + jr) * C + cc]); };
-  auto p_sum = [&](int jr, int cc) { return lds ? s_ps[jr * C + cc] : ld_dev(&a.w.part_sum[(r0 + jr) * C + cc]); };
-  auto p_idx = [&](int jr, int cc) { return lds ? s_pi[jr * C + cc] : ld_dev(&a.w.part_idx[(r0 + jr) * C + cc]); };
-  auto p_flag = [&](int jr, int cc) { return lds ? s_pf[jr * C + cc] : ld_dev(&a.w.part_flag[(r0 + jr) * C + cc]); };
+  auto r_stat = [&](int jr, int &arg, int &ok) {
+    if (lds) {
+      arg = s_rarg[jr];
+      ok = s_rok[jr];
+    } else {
+      combine_row(jr, arg, ok);
+    }
+  };
+
+  int j = G;
+  unsigned flags = 0;  // 1 bad token, 2 bad row
+  for (int i0 = 0; i0 < G; i0 += WAVE) {
+    const int i = i0 + lane;
+    const bool act = i < G;
+    bool accept = false;
+    if (act) {
+      const int x = (i0 == 0) ? x0 : a.tokens[(size_t)b * G + i];
+      const bool tok_ok = (x >= 0) && (x < a.V);
+      if (!tok_ok) flags |= 1;
+      int arg, ok;
+      r_stat(i, arg, ok);
+      if (!ok) flags |= 2;
+      accept = tok_ok && ok && (x == arg);
+    }
+    const unsigned long long rej = __ballot(act && !accept);
+    if (j == G && rej) j = i0 + __ffsll((long long)rej) - 1;
+  }
+  int argj, okj, argG, okG;
+  r_stat(j, argj, okj);
+  r_stat(G, argG, okG);
+  if (!okG) flags |= 2;  // target row G: the bonus distribution
+  flags = wave_or(flags);
+  const int err = (flags & 1) ? SV_ROW_BAD_TOKEN : (flags & 2) ? SV_ROW_BAD_LOGITS : 0;
+  for (int i = lane; i <= G; i += WAVE) {
+    int32_t v;
+    if (err) v = -1;
+    else if (i < j) v = (i < WAVE) ? x0 : a.tokens[(size_t)b * G + i];
+    else if (i > j) v = -1;
+    else v = argj;  // the target's own choice
+    out[i] = v;
+  }
+  if (lane == 0) a.accepted_len[b] = err ? err : j;
+}
+
+// Sampling: the sequence's finisher -- its last first-pass item in grid order, one wave --
+// waits until every chunk partial and drafted-token logit of the sequence carries this
+// call's tag (they come from workgroups earlier in the grid), combines each row's
+// partials into its log2-partition, then runs the acceptance scan.  Position i of the
+// chain: token range, row validity, uniform range, draft support, then the test
+// U_i <= min(1, p_i(x)/q_i(x)) with p_i(x) > 0 ("Speculative Decoding 的朴素思想",
+// "一次 sampling 怎么执行" step 4; the ratio is formed from log2-probabilities in double).
+// It writes the accepted prefix and the -1 padding, and publishes the draw's record
+// (the drawn token and accepted_len are written by the draw).  The finisher's own
+// partial (index np - 1) and token logit come from its registers.
+template <typename T, bool TOPK>
+SVD void sampling_finish(const Args &a, int b, float own_off, float own_hi, float own_lo,
+                         bool own_tok, float own_zx) {
+  constexpr int UNR = SEQ_LDS_PARTS / WAVE;
+  constexpr int RUNR = (SEQ_LDS_ROWS + WAVE - 1) / WAVE;
+  __shared__ float s_po[SEQ_LDS_PARTS];
+  __shared__ double s_ps[SEQ_LDS_PARTS];
+  __shared__ float s_roff[SEQ_LDS_ROWS], s_rzx[SEQ_LDS_ROWS], s_rtau[SEQ_LDS_ROWS];
+  __shared__ double s_rl2s[SEQ_LDS_ROWS];
+  __shared__ int s_rok[SEQ_LDS_ROWS];
+  const int lane = lane_id();
+  const int G = a.G, rps = a.rps, C = a.C;
+  const size_t r0 = (size_t)b * rps;
+  const int np = rps * C, own = np - 1;
+  const bool lds = np <= SEQ_LDS_PARTS && rps <= SEQ_LDS_ROWS;
+  const unsigned tag = a.tag;
+  const u64 *pw = a.w.tw_part + r0 * C * 3;
+  const u64 *zw = a.w.tw_zx + r0;
+
+  // inputs of positions lane, lane+64, ... (first round only kept in registers)
+  const int x0 = (lane < G) ? a.tokens[(size_t)b * G + lane] : 0;
+  const float u0 = (lane < G) ? a.u_accept[(size_t)b * G + lane] : 0.0f;
+  const float us = a.u_sample[b];
+  // Which rows publish a token logit: rows with a position whose token is in range.
+  auto row_token = [&](int jr) -> int {
+    const int pos = (jr < G) ? jr : (jr > G ? jr - G - 1 : -1);
+    return (pos < 0) ? -1 : a.tokens[(size_t)b * G + pos];
+  };
+  auto needs_zx = [&](int jr) {
+    if (jr >= rps || jr == G || (jr == rps - 1 && own_tok)) return false;
+    const int x = row_token(jr);
+    return x >= 0 && x < a.V;
+  };
+
+  // Wait for the partials (blocks of SEQ_LDS_PARTS, every load of a block in flight at
+  // once) and the token logits; stage them in LDS when the sequence fits.
+  bool alive = true;
+  unsigned polls = 0;
+  for (int blk = 0; blk < np && alive; blk += SEQ_LDS_PARTS) {
+    for (;;) {
+      u64 w0[UNR], w1[UNR], w2[UNR];
+#pragma unroll
+      for (int k = 0; k < UNR; ++k) {
+        const int i = blk + lane + k * WAVE;
+        const int ii = (i < np && i != own) ? i : 0;
+        w0[k] = ld_dev(&pw[(size_t)ii * 3 + 0]);
+        w1[k] = ld_dev(&pw[(size_t)ii * 3 + 1]);
+        w2[k] = ld_dev(&pw[(size_t)ii * 3 + 2]);
+      }
+      bool ok = true;
+#pragma unroll
+      for (int k = 0; k < UNR; ++k) {
+        const int i = blk + lane + k * WAVE;
+        if (i < np && i != own) ok = ok && tw_ok(w0[k], tag) && tw_ok(w1[k], tag) && tw_ok(w2[k], tag);
+      }
+      if (__ballot(!ok) == 0) {
+        if (lds) {
+#pragma unroll
+          for (int k = 0; k < UNR; ++k) {
+            const int i = lane + k * WAVE;
+            if (i < np) {
+              s_po[i] = (i == own) ? own_off : tw_f(w0[k]);
+              s_ps[i] = (i == own) ? d_join(own_hi, own_lo) : d_join(tw_f(w1[k]), tw_f(w2[k]));
+            }
+          }
+        }
+        break;
+      }
+      if (++polls >= a.spin_limit) {
+        alive = false;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  for (int rb = 0; rb < rps && alive; rb += RUNR * WAVE) {
+    for (;;) {
+      u64 wz[RUNR];
+      bool need[RUNR];
+#pragma unroll
+      for (int k = 0; k < RUNR; ++k) {
+        const int jr = rb + lane + k * WAVE;
+        need[k] = needs_zx(jr);
+        wz[k] = ld_dev(&zw[need[k] ? jr : 0]);
+      }
+      bool ok = true;
+#pragma unroll
+      for (int k = 0; k < RUNR; ++k) ok = ok && (!need[k] || tw_ok(wz[k], tag));
+      if (__ballot(!ok) == 0) {
+        if (lds) {
+#pragma unroll
+          for (int k = 0; k < RUNR; ++k) {
+            const int jr = lane + k * WAVE;
+            if (jr < rps) {
+              s_rzx[jr] = need[k] ? tw_f(wz[k]) : ((jr == rps - 1 && own_tok) ? own_zx : NAN);
+              s_rtau[jr] = TOPK ? a.w.row_tau[r0 + jr] : -INFINITY;  // top-k: the previous kernel's
+            }
+          }
+        }
+        break;
+      }
+      if (++polls >= a.spin_limit) {
+        alive = false;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+  u64 *jw = a.w.tw_job + (size_t)b * JW;
+  int32_t *out = a.out_tokens + (size_t)b * (G + 1);
+  if (!alive) {  // gave up waiting: report it, and let the draw items go
+    for (int i = lane; i <= G; i += WAVE) out[i] = -1;
+    if (lane == 0) a.accepted_len[b] = SV_ROW_INTERNAL;
+    if (lane < JW_USED) tw_put(&jw[lane], tag, lane == JW_KIND ? (unsigned)JOB_NONE : 0u);
+    return;
+  }
+
+  auto p_off = [&](int jr, int cc) -> float {
+    const int i = jr * C + cc;
+    if (lds) return s_po[i];
+    return (i == own) ? own_off : tw_f(ld_dev(&pw[(size_t)i * 3]));
+  };
+  auto p_sum = [&](int jr, int cc) -> double {
+    const int i = jr * C + cc;
+    if (lds) return s_ps[i];
+    if (i == own) return d_join(own_hi, own_lo);
+    return d_join(tw_f(ld_dev(&pw[(size_t)i * 3 + 1])), tw_f(ld_dev(&pw[(size_t)i * 3 + 2])));
+  };
+  auto zx_of = [&](int jr) -> float {
+    if (lds) return s_rzx[jr];
+    if (jr == rps - 1 && own_tok) return own_zx;
+    return needs_zx(jr) ? tw_f(ld_dev(&zw[jr])) : NAN;
+  };
+  auto tau_of = [&](int jr) -> float { return lds ? s_rtau[jr] : (TOPK ? a.w.row_tau[r0 + jr] : -INFINITY); };
 
   // Row statistics: lane jr combines row jr's chunks in chunk order (rows in parallel).
+  // Rows beyond the LDS capacity are recombined on demand, which gives the same values.
+  auto combine_row = [&](int jr, float &o, double &t) {
+    o = -INFINITY;
+    t = 0.0;
+    for (int cc = 0; cc < C; ++cc) lse_combine(o, t, p_off(jr, cc), p_sum(jr, cc));
+  };
   for (int jr0 = 0; jr0 < rps; jr0 += WAVE) {
     const int jr = jr0 + lane;
     if (jr < rps) {
-      const size_t r = r0 + jr;
-      if (GREEDY) {
-        float best = -INFINITY;
-        int bi = 0x7fffffff, fl = 0;
-        for (int cc = 0; cc < C; ++cc) {
-          best_combine(best, bi, p_off(jr, cc), p_idx(jr, cc));
-          fl |= p_flag(jr, cc);
-        }
-        const int ok = (fl == 2) ? 1 : 0;
-        st_dev(&a.w.row_arg[r], bi);
-        st_dev(&a.w.row_ok[r], ok);
-        if (lds) {
-          s_rarg[jr] = bi;
-          s_rok[jr] = ok;
-        }
-      } else {
-        float o = -INFINITY;
-        double t = 0.0;
-        for (int cc = 0; cc < C; ++cc) lse_combine(o, t, p_off(jr, cc), p_sum(jr, cc));
-        const bool ok = isfinite(o) && isfinite(t) && t > 0.0;
-        const double l2s = ok ? log2(t) : 0.0;
-        st_dev(&a.w.row_off[r], o);
-        st_dev(&a.w.row_l2s[r], l2s);
-        st_dev(&a.w.row_ok[r], ok ? 1 : 0);
-        if (!TOPK) st_dev(&a.w.row_tau[r], -INFINITY);
-        if (a.row_stats) {
-          a.row_stats[r * 2 + 0] = (float)((double)o * LN2);
-          a.row_stats[r * 2 + 1] = (float)t;
-        }
-        if (lds) {
-          s_roff[jr] = o;
-          s_rl2s[jr] = l2s;
-          s_rok[jr] = ok ? 1 : 0;
-        }
+      float o;
+      double t;
+      combine_row(jr, o, t);
+      const bool ok = isfinite(o) && isfinite(t) && t > 0.0;
+      if (a.row_stats) {
+        a.row_stats[(r0 + jr) * 2 + 0] = (float)((double)o * LN2);
+        a.row_stats[(r0 + jr) * 2 + 1] = (float)t;
+      }
+      if (lds) {
+        s_roff[jr] = o;
+        s_rl2s[jr] = ok ? log2(t) : 0.0;
+        s_rok[jr] = ok ? 1 : 0;
       }
     }
   }
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_wave_barrier();
+  auto r_stat = [&](int jr, float &o, double &l2s, int &ok) {
+    if (lds) {
+      o = s_roff[jr];
+      l2s = s_rl2s[jr];
+      ok = s_rok[jr];
+    } else {
+      double t;
+      combine_row(jr, o, t);
+      ok = (isfinite(o) && isfinite(t) && t > 0.0) ? 1 : 0;
+      l2s = ok ? log2(t) : 0.0;
+    }
+  };
 
   // The bonus draw's chunk, in case every draft is accepted: chunk masses of p_G,
   // S_c * 2^(off_c - off_row) in chunk order, and the remainder in that chunk's scale.
   int c_bonus = -1;
   float off_bonus = 0.0f;
   double t_bonus = 0.0;
-  if (!GREEDY) {
-    const float oG = lds ? s_roff[G] : ld_dev(&a.w.row_off[r0 + G]);
-    const int okG = lds ? s_rok[G] : ld_dev(&a.w.row_ok[r0 + G]);
-    if (okG) {
-      auto cm = [&](int cc) {
-        const double sc = p_sum(G, cc);
-        return (sc > 0.0) ? sc * (double)fast_exp2(p_off(G, cc) - oG) : 0.0;
-      };
-      const double total = wave_total(C, cm);
-      double trem;
-      c_bonus = wave_pick(C, (double)us * total, cm, &trem);
-      if (c_bonus >= 0) {
-        off_bonus = p_off(G, c_bonus);
-        t_bonus = trem * (double)fast_exp2(oG - off_bonus);
-      }
+  float oG;
+  double l2G;
+  int okG;
+  r_stat(G, oG, l2G, okG);
+  if (okG) {
+    auto cm = [&](int cc) {
+      const double sc = p_sum(G, cc);
+      return (sc > 0.0) ? sc * (double)fast_exp2(p_off(G, cc) - oG) : 0.0;
+    };
+    const double total = wave_total(C, cm);
+    double trem;
+    c_bonus = wave_pick(C, (double)us * total, cm, &trem);
+    if (c_bonus >= 0) {
+      off_bonus = p_off(G, c_bonus);
+      t_bonus = trem * (double)fast_exp2(oG - off_bonus);
     }
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  __builtin_amdgcn_wave_barrier();
-  auto r_ok = [&](int jr) { return lds ? s_rok[jr] : ld_dev(&a.w.row_ok[r0 + jr]); };
-  auto r_off = [&](int jr) { return lds ? s_roff[jr] : ld_dev(&a.w.row_off[r0 + jr]); };
-  auto r_l2s = [&](int jr) { return lds ? s_rl2s[jr] : ld_dev(&a.w.row_l2s[r0 + jr]); };
-  auto r_arg = [&](int jr) { return lds ? s_rarg[jr] : ld_dev(&a.w.row_arg[r0 + jr]); };
-  auto r_zx = [&](int jr) { return lds ? s_rzx[jr] : ld_dev(&a.w.row_zx[r0 + jr]); };
-  auto r_tau = [&](int jr) { return lds ? s_rtau[jr] : (TOPK ? a.w.row_tau[r0 + jr] : -INFINITY); };
 
   int j = G;
   unsigned flags = 0;  // 1 bad token, 2 bad row, 4 bad uniform, 8 q(x) = 0
@@ -686,77 +894,89 @@ SVD void sequence_finish(const Args &a, int b) {
       const int x = (i0 == 0) ? x0 : a.tokens[(size_t)b * G + i];
       const bool tok_ok = (x >= 0) && (x < a.V);
       if (!tok_ok) flags |= 1;
-      const bool ok_t = r_ok(i) != 0;
-      if (GREEDY) {
-        if (!ok_t) flags |= 2;
-        accept = tok_ok && ok_t && (x == r_arg(i));
-      } else {
-        const int id = G + 1 + i;
-        const bool ok_d = r_ok(id) != 0;
-        if (!ok_t || !ok_d) flags |= 2;
-        const float u = (i0 == 0) ? u0 : a.u_accept[(size_t)b * G + i];
-        if (!(u >= 0.0f && u < 1.0f)) flags |= 4;
-        if (tok_ok) {
-          const float zt = r_zx(i), zd = r_zx(id);
-          const bool supp_t = (zt > -INFINITY) && !(zt < r_tau(i));
-          const bool supp_d = (zd > -INFINITY) && !(zd < r_tau(id));
-          if (!supp_d) flags |= 8;
-          if (supp_t && supp_d && ok_t && ok_d) {
-            const double k2 = (double)a.k2;
-            const double l2p = (double)zt * k2 - ((double)r_off(i) + r_l2s(i));
-            const double l2q = (double)zd * k2 - ((double)r_off(id) + r_l2s(id));
-            const double alpha = exp2(fmin(0.0, l2p - l2q));
-            accept = (double)u <= alpha;
-          }
+      const int id = G + 1 + i;
+      float ot, od;
+      double lt, ld;
+      int okt, okd;
+      r_stat(i, ot, lt, okt);
+      r_stat(id, od, ld, okd);
+      if (!okt || !okd) flags |= 2;
+      const float u = (i0 == 0) ? u0 : a.u_accept[(size_t)b * G + i];
+      if (!(u >= 0.0f && u < 1.0f)) flags |= 4;
+      if (tok_ok) {
+        const float zt = zx_of(i), zd = zx_of(id);
+        const bool supp_t = (zt > -INFINITY) && !(zt < tau_of(i));
+        const bool supp_d = (zd > -INFINITY) && !(zd < tau_of(id));
+        if (!supp_d) flags |= 8;
+        if (supp_t && supp_d && okt && okd) {
+          const double k2 = (double)a.k2;
+          const double l2p = (double)zt * k2 - ((double)ot + lt);
+          const double l2q = (double)zd * k2 - ((double)od + ld);
+          const double alpha = exp2(fmin(0.0, l2p - l2q));
+          accept = (double)u <= alpha;
         }
       }
     }
     const unsigned long long rej = __ballot(act && !accept);
     if (j == G && rej) j = i0 + __ffsll((long long)rej) - 1;
   }
-  if (!r_ok(G)) flags |= 2;  // target row G: the bonus distribution
-  if (!GREEDY && !(us >= 0.0f && us < 1.0f)) flags |= 4;
+  if (!okG) flags |= 2;  // target row G: the bonus distribution
+  if (!(us >= 0.0f && us < 1.0f)) flags |= 4;
+  if (TOPK) {  // a NaN threshold marks a top-k selection that did not complete
+    for (int jr = lane; jr < rps; jr += WAVE)
+      if (tau_of(jr) != tau_of(jr)) flags |= 16;
+  }
   flags = wave_or(flags);
-  const int err = (flags & 1) ? SV_ROW_BAD_TOKEN
+  const int err = (flags & 16) ? SV_ROW_INTERNAL
+                : (flags & 1) ? SV_ROW_BAD_TOKEN
                 : (flags & 2) ? SV_ROW_BAD_LOGITS
                 : (flags & 4) ? SV_ROW_BAD_UNIFORM
                 : (flags & 8) ? SV_ROW_Q_ZERO : 0;
-  int32_t *out = a.out_tokens + (size_t)b * (G + 1);
   for (int i = lane; i <= G; i += WAVE) {
-    int32_t v;
-    if (err) v = -1;
-    else if (i < j) v = (i < WAVE) ? x0 : a.tokens[(size_t)b * G + i];
-    else if (i > j) v = -1;
-    else if (GREEDY) v = r_arg(j);  // the target's own choice
-    else continue;                  // drawn by the second kernel
-    out[i] = v;
+    if (!err && i == j) continue;  // written by the draw, with accepted_len
+    out[i] = (!err && i < j) ? ((i < WAVE) ? x0 : a.tokens[(size_t)b * G + i]) : -1;
   }
-  if (lane == 0) {
-    a.accepted_len[b] = err ? err : j;
-    if (!GREEDY) {
-      SeqJob jb;
-      jb.j = j;
-      jb.kind = err ? (int)JOB_NONE : (j < G ? (int)JOB_REJECT : (int)JOB_BONUS);
-      jb.c_bonus = c_bonus;
-      jb.pad = 0;
-      jb.off_bonus = off_bonus;
-      jb.pad2 = 0.0f;
-      jb.t_bonus = t_bonus;
-      jb.mt_hi = jb.mt_lo = jb.md_hi = jb.md_lo = 0.0f;
-      jb.tau_t = jb.tau_d = -INFINITY;
-      if (jb.kind == JOB_REJECT) {
-        const double mt = (double)r_off(j) + r_l2s(j);
-        const double md = (double)r_off(G + 1 + j) + r_l2s(G + 1 + j);
-        jb.mt_hi = (float)mt;
-        jb.mt_lo = (float)(mt - (double)jb.mt_hi);
-        jb.md_hi = (float)md;
-        jb.md_lo = (float)(md - (double)jb.md_hi);
-        jb.tau_t = r_tau(j);
-        jb.tau_d = r_tau(G + 1 + j);
-      }
-      a.w.job[b] = jb;
-    }
+  if (err && lane == 0) a.accepted_len[b] = err;
+
+  // The draw's record, one tagged word per lane.
+  const int kind = err ? (int)JOB_NONE : (j < G ? (int)JOB_REJECT : (int)JOB_BONUS);
+  float mt_hi = 0.0f, mt_lo = 0.0f, md_hi = 0.0f, md_lo = 0.0f, tau_t = -INFINITY, tau_d = -INFINITY;
+  float off_j = 0.0f;
+  if (kind == JOB_REJECT) {
+    float ot, od;
+    double lt, ld;
+    int okt, okd;
+    r_stat(j, ot, lt, okt);
+    r_stat(G + 1 + j, od, ld, okd);
+    const double mt = (double)ot + lt, md = (double)od + ld;
+    mt_hi = d_head(mt);
+    mt_lo = d_tail(mt);
+    md_hi = d_head(md);
+    md_lo = d_tail(md);
+    tau_t = tau_of(j);
+    tau_d = tau_of(G + 1 + j);
+    off_j = ot;
+  } else if (kind == JOB_BONUS) {
+    tau_t = tau_of(G);
   }
+  unsigned bits = 0;
+  switch (lane) {
+    case JW_J: bits = (unsigned)j; break;
+    case JW_KIND: bits = (unsigned)kind; break;
+    case JW_CBONUS: bits = (unsigned)c_bonus; break;
+    case JW_OFFBONUS: bits = __float_as_uint(off_bonus); break;
+    case JW_TB_HI: bits = __float_as_uint(d_head(t_bonus)); break;
+    case JW_TB_LO: bits = __float_as_uint(d_tail(t_bonus)); break;
+    case JW_MT_HI: bits = __float_as_uint(mt_hi); break;
+    case JW_MT_LO: bits = __float_as_uint(mt_lo); break;
+    case JW_MD_HI: bits = __float_as_uint(md_hi); break;
+    case JW_MD_LO: bits = __float_as_uint(md_lo); break;
+    case JW_TAU_T: bits = __float_as_uint(tau_t); break;
+    case JW_TAU_D: bits = __float_as_uint(tau_d); break;
+    case JW_OFF_J: bits = __float_as_uint(off_j); break;
+    default: break;
+  }
+  if (lane < JW_USED) tw_put(&jw[lane], tag, bits);
 }
 
 // ---------------------------------------------------------------- pass 1: normaliser
@@ -838,17 +1058,12 @@ SVD void norm_item(const Args &a, int item) {
   if (wid != 0) return;  // one wave finishes the workgroup
 
   const double S = (s_s[0] + s_s[1]) + (s_s[2] + s_s[3]);
-  if (lane == 0) {
-    st_dev(&a.w.part_off[(size_t)r * a.C + c], off);
-    st_dev(&a.w.part_sum[(size_t)r * a.C + c], S);
-    if (tok_here) st_dev(&a.w.row_zx[r], zx);
-  }
-  // Two ticket levels (chunks of a row, then rows of a sequence) keep the number of
-  // arrivals on any one counter small; every partial was complete before its
-  // workgroup's row ticket, so the sequence's last arrival sees all of them.
-  if (!wave_last_arrival(&a.w.t_row[r], (unsigned)a.C)) return;
-  if (!wave_last_arrival(&a.w.t_seq[b], (unsigned)a.rps)) return;
-  sequence_finish<T, false, TOPK>(a, b);
+  const float s_hi = d_head(S), s_lo = d_tail(S);
+  u64 *pw = a.w.tw_part + ((size_t)r * a.C + c) * 3;
+  if (lane < 3) tw_putf(pw + lane, a.tag, lane == 0 ? off : (lane == 1 ? s_hi : s_lo));
+  if (lane == 3 && tok_here) tw_putf(&a.w.tw_zx[r], a.tag, zx);
+  // The sequence's last item in grid order finishes the sequence.
+  if (jr == a.rps - 1 && c == a.C - 1) sampling_finish<T, TOPK>(a, b, off, s_hi, s_lo, tok_here, zx);
 }
 
 // ---------------------------------------------------------------- pass 1: greedy argmax
@@ -895,14 +1110,10 @@ __global__ __launch_bounds__(NT) void k_argmax(const Args a) {
     best_combine(best, bi, s_v[w], s_i[w]);
     fl |= s_f[w];
   }
-  if (lane == 0) {
-    st_dev(&a.w.part_off[(size_t)r * a.C + c], best);
-    st_dev(&a.w.part_idx[(size_t)r * a.C + c], bi);
-    st_dev(&a.w.part_flag[(size_t)r * a.C + c], fl);
-  }
-  if (!wave_last_arrival(&a.w.t_row[r], (unsigned)a.C)) return;
-  if (!wave_last_arrival(&a.w.t_seq[b], (unsigned)a.rps)) return;
-  sequence_finish<T, true, false>(a, b);
+  u64 *pw = a.w.tw_part + ((size_t)r * a.C + c) * 3;
+  if (lane < 3) tw_put(pw + lane, a.tag, lane == 0 ? __float_as_uint(best) : (lane == 1 ? (unsigned)bi : (unsigned)fl));
+  // The sequence's last item in grid order finishes the sequence.
+  if (jr == a.rps - 1 && c == a.C - 1) greedy_finish<T>(a, b, best, bi, fl);
 }
 
 // ---------------------------------------------------------------- pass 2: the draw
@@ -932,10 +1143,11 @@ struct TargetW {
 };
 
 // Segment masses of vectors kbeg..kbeg+NK-1 of chunk c (whole workgroup): weights
-// wf(zA, zB) per element, a lane mass per vector (elements summed in order), and the
-// wave sum of each 64-vector segment into s_seg[k*NW + wave].  Loads are issued KG
-// vectors per thread at a time (KG = NK: every load in flight at once).
-template <typename T, bool ALIGNED, int KG, int NK, typename WFn>
+// wf(zA, zB) per element (zB = -inf without a second row), a lane mass per vector
+// (elements summed in order), and the wave sum of each 64-vector segment into
+// s_seg[k*NW + wave].  Loads are issued KG vectors per thread at a time (KG = NK: every
+// load in flight at once).
+template <typename T, bool ALIGNED, int KG, int NK, bool PAIR, typename WFn>
 SVD void chunk_masses(const Args &a, const T *rowA, const T *rowB, int c, int kbeg, const WFn &wf,
                       double *s_seg) {
   constexpr int VEC = Fmt<T>::VEC;
@@ -943,22 +1155,45 @@ SVD void chunk_masses(const Args &a, const T *rowA, const T *rowB, int c, int kb
 #pragma unroll
   for (int kg = 0; kg < NK; kg += KG) {
     const int k0 = kbeg + kg;
-    float xa[KG][VEC], xb[KG][VEC];
-    load_vectors<T, ALIGNED, false, KG>(rowA, a.V, a.nvec, c, k0, tid, xa);
-    if (rowB) {
-      load_vectors<T, ALIGNED, false, KG>(rowB, a.V, a.nvec, c, k0, tid, xb);
+    float acc[KG];
+    if (ALIGNED) {
+      // Raw 16-byte vectors stay packed until their own turn: KG*4 registers per row.
+      u32x4 wa[KG], wb[PAIR ? KG : 1];
+      const u32x4 *ra = reinterpret_cast<const u32x4 *>(rowA);
+      const u32x4 *rb = reinterpret_cast<const u32x4 *>(rowB);
+#pragma unroll
+      for (int k = 0; k < KG; ++k) {
+        const int v = c * CHUNK_VECS + (k0 + k) * NT + tid;
+        const int vs = v < a.nvec ? v : a.nvec - 1;
+        wa[k] = ra[vs];
+        if (PAIR) wb[PAIR ? k : 0] = rb[vs];
+      }
+#pragma unroll
+      for (int k = 0; k < KG; ++k) {
+        const bool in = c * CHUNK_VECS + (k0 + k) * NT + tid < a.nvec;
+        float xa[VEC], xb[VEC];
+        Fmt<T>::unpack(wa[k], xa);
+        if (PAIR) Fmt<T>::unpack(wb[PAIR ? k : 0], xb);
+        float m = 0.0f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) m += wf(in ? xa[e] : -INFINITY, (PAIR && in) ? xb[e] : -INFINITY);
+        acc[k] = m;
+      }
     } else {
+      float xa[KG][VEC], xb[PAIR ? KG : 1][VEC];
+      load_vectors<T, ALIGNED, false, KG>(rowA, a.V, a.nvec, c, k0, tid, xa);
+      if (PAIR) load_vectors<T, ALIGNED, false, PAIR ? KG : 1>(rowB, a.V, a.nvec, c, k0, tid, xb);
 #pragma unroll
-      for (int k = 0; k < KG; ++k)
+      for (int k = 0; k < KG; ++k) {
+        float m = 0.0f;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) xb[k][e] = -INFINITY;
+        for (int e = 0; e < VEC; ++e) m += wf(xa[k][e], PAIR ? xb[PAIR ? k : 0][e] : -INFINITY);
+        acc[k] = m;
+      }
     }
 #pragma unroll
     for (int k = 0; k < KG; ++k) {
-      float acc = 0.0f;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) acc += wf(xa[k][e], xb[k][e]);
-      const double seg = wave_sum((double)acc);
+      const double seg = wave_sum((double)acc[k]);
       if (lane == 0) s_seg[(k0 + k) * NW + wid] = seg;
     }
   }
@@ -1058,59 +1293,98 @@ SVD int wave_chunk_draw(const Args &a, const T *rowA, const T *rowB, int c, cons
 }
 
 // One wave: pick the chunk of target row r from the first pass's partials (mass
-// S_c * 2^(off_c - off_row)), and express the remainder in the chunk's own scale.
-SVD int pick_target_chunk(const Args &a, int r, float u, double *t_in) {
-  const float off_r = a.w.row_off[r];
+// S_c * 2^(off_c - off_r)), and express the remainder in the chunk's own scale.  The
+// partials are complete: the scan that published the job read all of them.
+SVD int pick_target_chunk(const Args &a, int r, float off_r, float u, double *t_in) {
+  const u64 *pw = a.w.tw_part + (size_t)r * a.C * 3;
   auto cm = [&](int cc) {
-    const double s = a.w.part_sum[(size_t)r * a.C + cc];
-    const float d = a.w.part_off[(size_t)r * a.C + cc] - off_r;
+    const double s = d_join(tw_f(ld_dev(&pw[cc * 3 + 1])), tw_f(ld_dev(&pw[cc * 3 + 2])));
+    const float d = tw_f(ld_dev(&pw[cc * 3])) - off_r;
     return (s > 0.0) ? s * (double)fast_exp2(d) : 0.0;
   };
   const double total = wave_total(a.C, cm);
   double trem;
   const int c = wave_pick(a.C, (double)u * total, cm, &trem);
-  *t_in = (c >= 0) ? trem * (double)fast_exp2(off_r - a.w.part_off[(size_t)r * a.C + c]) : 0.0;
+  *t_in = (c >= 0) ? trem * (double)fast_exp2(off_r - tw_f(ld_dev(&pw[c * 3]))) : 0.0;
   return c;
 }
 
-// Second kernel, NSUB workgroups per (sequence b, chunk c), after the first kernel has
-// published every sequence's job:
-//   reject at j: each workgroup computes the masses of [p_j - q_j]_+ of its quarter of
-//                the chunk per 64-vector segment and publishes them; the last of the
-//                sequence's workgroups reads all of them at once,
-//                picks chunk and segment, and one wave re-reads that segment to pick
-//                lane and element;
-//   bonus:       every chunk picks the chunk from the first kernel's partials; the
-//                picked one re-reads itself and draws from p_G.
+// Draw item (sequence b, chunk c, quarter sub).  All draw items follow every first-pass
+// item in the grid.  Each waits until the sequence's record carries this call's tag, then
+//   reject at j: computes the masses of [p_j - q_j]_+ of its quarter of the chunk per
+//                64-vector segment and publishes them; the sequence's last draw item in
+//                grid order (c = C-1, sub = NSUB-1) waits for all of them, picks chunk
+//                and segment, and one wave re-reads that segment to pick lane and element;
+//   bonus:       the chunk picked by the scan from the first pass's partials re-reads
+//                itself and draws from p_G (one item; the others leave).
+// The item that writes the drawn token also writes accepted_len.
 template <typename T, bool ALIGNED>
-__global__ __launch_bounds__(NT) void k_sample(const Args a) {
+SVD void draw_item(const Args &a, int item) {
   __shared__ double s_seg[SEGS];
+  __shared__ unsigned s_job[JW];
+  __shared__ int s_ready;
   const int tid = threadIdx.x, wid = tid / WAVE, lane = lane_id();
-  const int b = blockIdx.x / (a.C * NSUB);
-  const int rem = blockIdx.x - b * a.C * NSUB;
+  const int b = item / (a.C * NSUB);
+  const int rem = item - b * a.C * NSUB;
   const int c = rem / NSUB, sub = rem - c * NSUB;
   const int G = a.G;
+  const unsigned tag = a.tag;
   int32_t *out = a.out_tokens + (size_t)b * (G + 1);
-  const SeqJob jb = a.w.job[b];
-  const int j = jb.j, kind = jb.kind;
-  const float u = a.u_sample[b];
+
+  // Wave 0 polls the record (one word per lane); the other waves wait at the barrier.
+  if (wid == 0) {
+    const u64 *jw = a.w.tw_job + (size_t)b * JW;
+    bool ready = false;
+    u64 w = 0;
+    for (unsigned n = 0; n < a.spin_limit; ++n) {
+      w = (lane < JW_USED) ? ld_dev(&jw[lane]) : 0ull;
+      if (__ballot(lane < JW_USED && !tw_ok(w, tag)) == 0) {
+        ready = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    if (lane < JW) s_job[lane] = (unsigned)w;
+    if (lane == 0) s_ready = ready ? 1 : 0;
+  }
+  __syncthreads();
+  if (!s_ready) {  // gave up: report it instead of drawing
+    if (tid == 0) a.accepted_len[b] = SV_ROW_INTERNAL;
+    return;
+  }
+  const int kind = (int)s_job[JW_KIND], j = (int)s_job[JW_J];
   // Accept only well-formed jobs, so workspace contents can never become an
   // out-of-range row or chunk index.
   if (!((kind == JOB_REJECT && j >= 0 && j < G) || (kind == JOB_BONUS && j == G))) return;
+  const float u = a.u_sample[b];
+  auto jf = [&](int f) { return __uint_as_float(s_job[f]); };
 
   if (kind == JOB_BONUS) {
-    // The scan already picked the chunk from p_G's partials; only that chunk works.
-    if (sub != 0 || c != jb.c_bonus) return;
-    const int r = b * a.rps + G;
-    const TargetW tw{a.k2, jb.off_bonus, a.w.row_tau[r]};
+    // The scan already picked the chunk from p_G's partials; only that chunk works (chunk
+    // 0 reports -1 if the record names no chunk).
+    const int cb = (int)s_job[JW_CBONUS];
+    const bool cb_ok = cb >= 0 && cb < a.C;
+    if (sub != 0 || c != (cb_ok ? cb : 0)) return;
+    if (!cb_ok) {
+      if (tid == 0) {
+        out[G] = -1;
+        a.accepted_len[b] = G;
+      }
+      return;
+    }
+    const TargetW tw{a.k2, jf(JW_OFFBONUS), jf(JW_TAU_T)};
+    const double t_bonus = d_join(jf(JW_TB_HI), jf(JW_TB_LO));
     const T *row = seq_row<T>(a, b, G);
-    chunk_masses<T, ALIGNED, VPT, VPT>(a, row, (const T *)nullptr, c, 0, tw, s_seg);
+    chunk_masses<T, ALIGNED, VPT, VPT, false>(a, row, (const T *)nullptr, c, 0, tw, s_seg);
     if (wid != 0) return;
     auto segm = [&](int i) { return s_seg[i]; };
     double ts;
-    const int sp = wave_pick(SEGS, jb.t_bonus, segm, &ts);
+    const int sp = wave_pick(SEGS, t_bonus, segm, &ts);
     const int tok = (sp >= 0) ? segment_draw<T, ALIGNED>(a, row, (const T *)nullptr, c, sp, tw, ts) : -1;
-    if (lane == 0) out[G] = tok;
+    if (lane == 0) {
+      out[G] = tok;
+      a.accepted_len[b] = G;
+    }
     return;
   }
 
@@ -1118,33 +1392,80 @@ __global__ __launch_bounds__(NT) void k_sample(const Args a) {
   const int rt = b * a.rps + j;
   ResidualW wf;
   wf.k2 = a.k2;
-  wf.mt_hi = jb.mt_hi;
-  wf.mt_lo = jb.mt_lo;
-  wf.md_hi = jb.md_hi;
-  wf.md_lo = jb.md_lo;
-  wf.tau_t = jb.tau_t;
-  wf.tau_d = jb.tau_d;
+  wf.mt_hi = jf(JW_MT_HI);
+  wf.mt_lo = jf(JW_MT_LO);
+  wf.md_hi = jf(JW_MD_HI);
+  wf.md_lo = jf(JW_MD_LO);
+  wf.tau_t = jf(JW_TAU_T);
+  wf.tau_d = jf(JW_TAU_D);
   const T *row_t = seq_row<T>(a, b, j), *row_d = seq_row<T>(a, b, G + 1 + j);
-  chunk_masses<T, ALIGNED, KSUB, KSUB>(a, row_t, row_d, c, sub * KSUB, wf, s_seg);
+  chunk_masses<T, ALIGNED, KSUB, KSUB, true>(a, row_t, row_d, c, sub * KSUB, wf, s_seg);
   if (wid != 0) return;  // wave 0 publishes and finishes
-  double *segs_b = a.w.p2_seg + (size_t)b * a.C * SEGS;
-  if (lane < KSUB * NW) {
-    const int sg = sub * KSUB * NW + lane;
-    st_dev(&segs_b[(size_t)c * SEGS + sg], s_seg[sg]);
+  u64 *sw = a.w.tw_seg + (size_t)b * a.C * SEGS * 2;
+  constexpr int MINE = KSUB * NW;  // segments of this item
+  const int own0 = c * SEGS + sub * MINE;
+  if (lane < 2 * MINE) {
+    const double m = s_seg[sub * MINE + (lane >> 1)];
+    tw_putf(&sw[(size_t)own0 * 2 + lane], tag, (lane & 1) ? d_tail(m) : d_head(m));
   }
-  if (!wave_last_arrival(&a.w.t_p2[b], (unsigned)(a.C * NSUB))) return;
+  if (c != a.C - 1 || sub != NSUB - 1) return;
 
-  // Last chunk of the sequence: every segment mass of the sequence in one round trip,
-  // kept in LDS (read on demand beyond LDS_CHUNKS chunks); chunk totals are segment-order
-  // scans, so the segment pick inside the chosen chunk sums to exactly its total.
-  constexpr int LDS_CHUNKS = 64;
+  // The sequence's last draw item: wait for every segment mass of the sequence (every
+  // load of a block of 256 segments in flight at once), keep them in LDS (read on
+  // demand beyond LDS_CHUNKS chunks); chunk totals are segment-order scans, so the
+  // segment pick inside the chosen chunk sums to exactly its total.
+  constexpr int LDS_CHUNKS = 32, SB = 4;
   __shared__ double s_cs[LDS_CHUNKS * SEGS];
   __shared__ double s_ct[LDS_CHUNKS];
-  const int ncache = (a.C < LDS_CHUNKS ? a.C : LDS_CHUNKS) * SEGS;
-  for (int i = lane; i < ncache; i += WAVE) s_cs[i] = ld_dev(&segs_b[i]);
+  const int nseg = a.C * SEGS;
+  const bool lds = a.C <= LDS_CHUNKS;
+  auto mine = [&](int i) { return i >= own0 && i < own0 + MINE; };
+  bool alive = true;
+  unsigned polls = 0;
+  for (int blk = 0; blk < nseg && alive; blk += SB * WAVE) {
+    for (;;) {
+      u64 wh[SB], wl[SB];
+#pragma unroll
+      for (int k = 0; k < SB; ++k) {
+        const int i = blk + lane + k * WAVE;
+        const int ii = (i < nseg && !mine(i)) ? i : 0;
+        wh[k] = ld_dev(&sw[(size_t)ii * 2]);
+        wl[k] = ld_dev(&sw[(size_t)ii * 2 + 1]);
+      }
+      bool ok = true;
+#pragma unroll
+      for (int k = 0; k < SB; ++k) {
+        const int i = blk + lane + k * WAVE;
+        if (i < nseg && !mine(i)) ok = ok && tw_ok(wh[k], tag) && tw_ok(wl[k], tag);
+      }
+      if (__ballot(!ok) == 0) {
+        if (lds) {
+#pragma unroll
+          for (int k = 0; k < SB; ++k) {
+            const int i = blk + lane + k * WAVE;
+            if (i < nseg) s_cs[i] = mine(i) ? s_seg[i - c * SEGS] : d_join(tw_f(wh[k]), tw_f(wl[k]));
+          }
+        }
+        break;
+      }
+      if (++polls >= a.spin_limit) {
+        alive = false;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  if (!alive) {
+    if (lane == 0) a.accepted_len[b] = SV_ROW_INTERNAL;
+    return;
+  }
   __builtin_amdgcn_s_waitcnt(0);  // this wave's LDS writes land before any lane reads them
   __builtin_amdgcn_wave_barrier();
-  auto seg_of = [&](int i) { return (i < ncache) ? s_cs[i] : ld_dev(&segs_b[i]); };
+  auto seg_of = [&](int i) -> double {
+    if (lds) return s_cs[i];
+    if (mine(i)) return s_seg[i - c * SEGS];
+    return d_join(tw_f(ld_dev(&sw[(size_t)i * 2])), tw_f(ld_dev(&sw[(size_t)i * 2 + 1])));
+  };
   for (int cc = 0; cc < a.C && cc < LDS_CHUNKS; ++cc) {
     auto segm = [&](int i) { return seg_of(cc * SEGS + i); };
     const double tot = wave_total(SEGS, segm);
@@ -1169,19 +1490,26 @@ __global__ __launch_bounds__(NT) void k_sample(const Args a) {
     }
   } else {  // zero residual (reachable only through rounding): draw from p_j itself
     double tin;
-    const int cp = pick_target_chunk(a, rt, u, &tin);
+    const int cp = pick_target_chunk(a, rt, jf(JW_OFF_J), u, &tin);
     if (cp >= 0 && cp < a.C) {
-      const TargetW tw{a.k2, a.w.part_off[(size_t)rt * a.C + cp], a.w.row_tau[rt]};
+      const TargetW tw{a.k2, tw_f(ld_dev(&a.w.tw_part[((size_t)rt * a.C + cp) * 3])), wf.tau_t};
       tok = wave_chunk_draw<T, ALIGNED>(a, row_t, (const T *)nullptr, cp, tw, tin);
     }
   }
-  if (lane == 0) out[j] = tok;
+  if (lane == 0) {
+    out[j] = tok;
+    a.accepted_len[b] = j;
+  }
 }
 
-// First-pass kernel: one workgroup per chunk of every row (sequence-major).
+// Sampling: the first pass (normalisers, acceptance scan) and the draws in one grid.
+// Blocks 0 .. R*C-1 are first-pass items in sequence order; the draw items follow.
 template <typename T, bool ALIGNED, bool TOPK>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6))) void k_norm(const Args a) {
-  norm_item<T, ALIGNED, TOPK>(a, blockIdx.x);
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(5))) void k_verify(const Args a) {
+  const int n1 = a.B * a.rps * a.C;
+  const int x = (int)blockIdx.x;
+  if (x < n1) norm_item<T, ALIGNED, TOPK>(a, x);
+  else draw_item<T, ALIGNED>(a, x - n1);
 }
 
 }  // namespace sv
@@ -1200,9 +1528,8 @@ struct Plan {
   long long R;
   int digit_passes;
   // workspace offsets
-  size_t part_off, part_sum, part_idx, part_flag, row_off, row_l2s, row_ok, row_arg, row_tau, row_zx,
-      tk_state, tk_hist, t_row, t_seq, t_p2, job, p2_seg, total;
-  size_t zero_bytes;  // leading bytes (the tickets) that must be zero when a call starts
+  size_t tw_part, tw_zx, tw_job, tw_seg, tw_hist, row_tau, tk_state, total;
+  size_t zero_bytes;  // leading bytes (tagged words) that must be clean when a call starts
 };
 
 bool make_plan(int32_t B, int32_t G, int32_t V, sv_dtype dt, float T, int32_t top_k, Plan &p) {
@@ -1215,45 +1542,48 @@ bool make_plan(int32_t B, int32_t G, int32_t V, sv_dtype dt, float T, int32_t to
   p.R = (long long)B * p.rps;
   p.topk = !p.greedy && top_k > 0 && top_k < V;
   p.digit_passes = (dt == SV_BF16) ? 2 : 4;
-  if (p.R * p.C + (long long)B * p.C > 0x7fffffffLL) return false;
+  if (p.R * p.C + (long long)B * p.C * NSUB > 0x7fffffffLL) return false;
   const size_t R = (size_t)p.R, C = (size_t)p.C, Bz = (size_t)B;
+  const bool smp = !p.greedy;
   size_t o = 0;
-  // tickets first: the part that must start (and stays) at zero
-  p.t_row = o; o = align256(o + R * 4);
-  p.t_seq = o; o = align256(o + Bz * 4);
-  p.t_p2 = o; o = align256(o + Bz * 4);
+  // The tagged words first: the part that must be clean (zero, or words of completed
+  // calls) when a call starts.  Every one of them is an 8-byte aligned word with its tag
+  // in the upper half, so whatever layout wrote them, a tag position holds zero or an
+  // earlier tag: never the tag of a call to come.
+  p.tw_part = o; o = align256(o + R * C * 3 * 8);
+  p.tw_zx = o; o = align256(o + (smp ? R * 8 : 0));
+  p.tw_job = o; o = align256(o + (smp ? Bz * JW * 8 : 0));
+  p.tw_seg = o; o = align256(o + (smp ? Bz * C * SEGS * 2 * 8 : 0));
+  p.tw_hist = o; o = align256(o + (p.topk ? R * C * 128 * 8 : 0));
   p.zero_bytes = o;
-  p.part_off = o; o = align256(o + R * C * 4);
-  p.part_sum = o; o = align256(o + R * C * 8);
-  p.part_idx = o; o = align256(o + (p.greedy ? R * C * 4 : 0));
-  p.part_flag = o; o = align256(o + (p.greedy ? R * C * 4 : 0));
-  p.row_off = o; o = align256(o + R * 4);
-  p.row_l2s = o; o = align256(o + R * 8);
-  p.row_ok = o; o = align256(o + R * 4);
-  p.row_arg = o; o = align256(o + R * 4);
-  p.row_tau = o; o = align256(o + R * 4);
-  p.row_zx = o; o = align256(o + R * 4);
+  p.row_tau = o; o = align256(o + (p.topk ? R * 4 : 0));
   p.tk_state = o; o = align256(o + (p.topk ? R * 8 : 0));
-  p.tk_hist = o; o = align256(o + (p.topk ? R * C * 256 * 4 : 0));
-  p.job = o; o = align256(o + Bz * sizeof(SeqJob));
-  p.p2_seg = o; o = align256(o + (p.greedy ? 0 : Bz * C * SEGS * 8));
   p.total = o;
   return true;
 }
 
 const char *kPlanNames[] = {
-    "k_topk_digit;k_topk_digit;k_norm;k_sample",
-    "k_topk_digit;k_topk_digit;k_topk_digit;k_topk_digit;k_norm;k_sample",
-    "k_norm;k_sample",
+    "k_topk_digit;k_topk_digit;k_verify",
+    "k_topk_digit;k_topk_digit;k_topk_digit;k_topk_digit;k_verify",
+    "k_verify",
     "k_argmax",
 };
+
+// Every launch gets its own tag, so a word left by an earlier launch can never pass
+// for this one's.  0 is never used (a clean workspace holds zeros).
+std::atomic<unsigned> g_tag{0};
+unsigned next_tag() {
+  unsigned t = g_tag.fetch_add(1u, std::memory_order_relaxed) + 1u;
+  while (t == 0u) t = g_tag.fetch_add(1u, std::memory_order_relaxed) + 1u;
+  return t;
+}
 
 template <typename T, bool AL>
 hipError_t launch_all(const Plan &p, const Args &a, hipStream_t st, void *const *ev, int nev,
                       int *nl) {
   const dim3 blk(NT);
   const unsigned rows_grid = (unsigned)(p.R * p.C);
-  const unsigned seq_grid = (unsigned)((long long)a.B * p.C * NSUB);
+  const unsigned verify_grid = (unsigned)(p.R * p.C + (long long)a.B * p.C * NSUB);
   int n = 0;
   hipError_t e = hipSuccess;
   // With events, kernel i is launched with (events[2i], events[2i+1]) as its start and
@@ -1269,23 +1599,25 @@ hipError_t launch_all(const Plan &p, const Args &a, hipStream_t st, void *const 
   };
   Args aa = a;
   if (p.greedy) {
+    aa.tag = next_tag();
     void *args[] = {&aa};
     go((const void *)&k_argmax<T, AL>, rows_grid, args);
   } else {
     if (p.topk) {
       for (int pass = 0; pass < p.digit_passes; ++pass) {
         int ps = pass, lp = (pass == p.digit_passes - 1) ? 1 : 0;
+        aa.tag = next_tag();
         void *args[] = {&aa, &ps, &lp};
         go((const void *)&k_topk_digit<T, AL>, rows_grid, args);
       }
+      aa.tag = next_tag();
       void *args[] = {&aa};
-      go((const void *)&k_norm<T, AL, true>, rows_grid, args);
+      go((const void *)&k_verify<T, AL, true>, verify_grid, args);
     } else {
+      aa.tag = next_tag();
       void *args[] = {&aa};
-      go((const void *)&k_norm<T, AL, false>, rows_grid, args);
+      go((const void *)&k_verify<T, AL, false>, verify_grid, args);
     }
-    void *args2[] = {&aa};
-    go((const void *)&k_sample<T, AL>, seq_grid, args2);
   }
   if (nl) *nl = n;
   return e;
@@ -1329,23 +1661,15 @@ sv_status run(const void *target, const void *draft, sv_dtype dt, const int32_t 
   a.accepted_len = acc;
   a.out_tokens = out;
   a.row_stats = sampling ? row_stats : nullptr;
-  a.w.part_off = (float *)(base + p.part_off);
-  a.w.part_sum = (double *)(base + p.part_sum);
-  a.w.part_idx = (int *)(base + p.part_idx);
-  a.w.part_flag = (int *)(base + p.part_flag);
-  a.w.row_off = (float *)(base + p.row_off);
-  a.w.row_l2s = (double *)(base + p.row_l2s);
-  a.w.row_ok = (int *)(base + p.row_ok);
-  a.w.row_arg = (int *)(base + p.row_arg);
+  a.tag = 0u;  // each launch takes its own
+  a.spin_limit = SPIN_LIMIT;
+  a.w.tw_part = (u64 *)(base + p.tw_part);
+  a.w.tw_zx = (u64 *)(base + p.tw_zx);
+  a.w.tw_job = (u64 *)(base + p.tw_job);
+  a.w.tw_seg = (u64 *)(base + p.tw_seg);
+  a.w.tw_hist = (u64 *)(base + p.tw_hist);
   a.w.row_tau = (float *)(base + p.row_tau);
-  a.w.row_zx = (float *)(base + p.row_zx);
   a.w.tk_state = (uint2 *)(base + p.tk_state);
-  a.w.tk_hist = (unsigned *)(base + p.tk_hist);
-  a.w.t_row = (unsigned *)(base + p.t_row);
-  a.w.t_seq = (unsigned *)(base + p.t_seq);
-  a.w.t_p2 = (unsigned *)(base + p.t_p2);
-  a.w.job = (SeqJob *)(base + p.job);
-  a.w.p2_seg = (double *)(base + p.p2_seg);
 
   hipStream_t st = (hipStream_t)stream;
   int n = 0;

@@ -47,12 +47,12 @@ def test_status_strings(lib):
 
 
 def test_launch_plan(lib):
-    assert sv.sv_launch_plan(64, 4, 128256, sv.SV_BF16, 1.0, 0) == ["k_norm", "k_sample"]
+    assert sv.sv_launch_plan(64, 4, 128256, sv.SV_BF16, 1.0, 0) == ["k_verify"]
     assert sv.sv_launch_plan(256, 7, 152064, sv.SV_BF16, 0.0, 50) == ["k_argmax"]
     assert sv.sv_launch_plan(128, 6, 128256, sv.SV_BF16, 0.8, 50) == \
-        ["k_topk_digit", "k_topk_digit", "k_norm", "k_sample"]
-    assert len(sv.sv_launch_plan(8, 5, 32000, sv.SV_F32, 0.7, 5)) == 6
-    assert sv.sv_launch_plan(8, 5, 32000, sv.SV_F32, 0.7, 32000) == ["k_norm", "k_sample"]
+        ["k_topk_digit", "k_topk_digit", "k_verify"]
+    assert len(sv.sv_launch_plan(8, 5, 32000, sv.SV_F32, 0.7, 5)) == 5
+    assert sv.sv_launch_plan(8, 5, 32000, sv.SV_F32, 0.7, 32000) == ["k_verify"]
 
 
 def test_workspace_bytes(lib):
@@ -103,11 +103,14 @@ def test_optional_pointers_are_optional(lib, kw):
     assert call(lib, nbytes=16, **kw) == 5
 
 
-def test_zero_prefix_covers_only_the_counters(lib):
+def test_zero_prefix(lib):
     for args in [(1, 1, 32, sv.SV_F32, 1.0, 0), (64, 4, 128256, sv.SV_BF16, 1.0, 0),
                  (256, 7, 152064, sv.SV_BF16, 0.0, 0), (128, 6, 128256, sv.SV_BF16, 0.8, 50)]:
         z, n = sv.sv_workspace_zero_bytes(*args), sv.sv_workspace_bytes(*args)
-        assert 0 < z < n and z % 256 == 0
+        assert 0 < z <= n and z % 256 == 0
+    # top-k: the thresholds handed from kernel to kernel lie beyond the prefix
+    assert sv.sv_workspace_zero_bytes(128, 6, 128256, sv.SV_BF16, 0.8, 50) < \
+        sv.sv_workspace_bytes(128, 6, 128256, sv.SV_BF16, 0.8, 50)
     assert sv.sv_workspace_zero_bytes(0, 1, 32, sv.SV_F32, 1.0, 0) == 0
     # more rows need more counters
     assert sv.sv_workspace_zero_bytes(64, 4, 128256, sv.SV_BF16, 1.0, 0) > \
