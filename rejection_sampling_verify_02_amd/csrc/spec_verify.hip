@@ -233,6 +233,13 @@ SVD const T *seq_row(const Args &a, int b, int j) {
 SVD float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }  // v_exp_f32; 0 for x < -126
 SVD int lane_id() { return (int)(threadIdx.x & (WAVE - 1)); }
 
+// This wave's LDS writes are complete before any of its lanes reads them.  Only the LDS
+// counter is waited for: outstanding global stores (published results) keep going.
+SVD void lds_sync() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt left at their maxima
+  __builtin_amdgcn_wave_barrier();
+}
+
 // (off, s) pairs stand for s * 2^off; combining keeps the larger offset.  Parts that
 // hold only -inf have off = -inf and s = 0 (or NaN when a NaN was seen); the rule never
 // forms (-inf) - (-inf).  The combine is commutative bit for bit.
@@ -406,6 +413,113 @@ SVD int wave_pick(int n, double t, const MFn &mfn, double *t_rem) {
   return pick;
 }
 
+// wave_pick with t = u * (total of the same masses): for n <= 64 one scan gives both.
+template <typename MFn>
+SVD int wave_pick_frac(int n, double u, const MFn &mfn, double *t_rem, double *total) {
+  if (n > WAVE) {
+    *total = wave_total(n, mfn);
+    return wave_pick(n, u * *total, mfn, t_rem);
+  }
+  const int i = lane_id();
+  const double m = (i < n) ? mfn(i) : 0.0;
+  const double cum = scan_sum(m);
+  const double tot = readlane_d(cum, WAVE - 1);
+  const double t = u * tot;
+  *total = tot;
+  const unsigned long long pos = __ballot(m > 0.0);
+  const unsigned long long cr = __ballot(m > 0.0 && cum > t);
+  if (cr) {
+    const int l = __ffsll((long long)cr) - 1;
+    const double prev = (l == 0) ? 0.0 : readlane_d(cum, l - 1);
+    *t_rem = t - prev;
+    return l;
+  }
+  *t_rem = INFINITY;
+  return pos ? 63 - __clzll((long long)pos) : -1;
+}
+
+// Inverse CDF over n masses in index order, four consecutive ones per lane in blocks of
+// 256: lane sums (in order), one scan per block.  t = u * total; returns the first index
+// whose prefix exceeds t and, in *t_rem, t minus the prefix before it; when rounding
+// leaves t at or past the total, the last positive index and +inf; -1 if nothing is
+// positive.  A single block reads its masses once.
+template <typename MFn>
+SVD int wave_pick4_frac(int n, double u, const MFn &mfn, double *t_rem, double *total) {
+  constexpr int SB = 4, BLK = SB * WAVE;
+  const int lane = lane_id();
+  double m[SB];
+  auto lane_masses = [&](int b0) {
+    double ls = 0.0;
+#pragma unroll
+    for (int k = 0; k < SB; ++k) {
+      const int i = b0 + lane * SB + k;
+      m[k] = (i < n) ? mfn(i) : 0.0;
+    }
+#pragma unroll
+    for (int k = 0; k < SB; ++k) ls += m[k];
+    return ls;
+  };
+  // The lane that holds the crossing picks its element; the result is broadcast.
+  auto in_lane = [&](int b0, int l, double rem, double *t_out) {
+    int pk = -1, last = -1;
+    double run = 0.0, r_out = INFINITY;
+#pragma unroll
+    for (int k = 0; k < SB; ++k) {
+      if (m[k] > 0.0) last = k;
+      if (pk < 0 && m[k] > 0.0 && run + m[k] > rem) {
+        pk = k;
+        r_out = rem - run;
+      }
+      run += m[k];
+    }
+    if (pk < 0) pk = last;
+    const int idx = (pk < 0) ? -1 : b0 + lane * SB + pk;
+    *t_out = readlane_d(r_out, l);
+    return __builtin_amdgcn_readlane(idx, l);
+  };
+  if (n <= BLK) {
+    const double ls = lane_masses(0);
+    const double cum = scan_sum(ls);
+    *total = readlane_d(cum, WAVE - 1);
+    const double t = u * *total;
+    const unsigned long long cr = __ballot(ls > 0.0 && cum > t);
+    const unsigned long long pos = __ballot(ls > 0.0);
+    if (cr) {
+      const int l = __ffsll((long long)cr) - 1;
+      const double prev = (l == 0) ? 0.0 : readlane_d(cum, l - 1);
+      return in_lane(0, l, t - prev, t_rem);
+    }
+    if (!pos) return -1;
+    const int l = 63 - __clzll((long long)pos);
+    return in_lane(0, l, INFINITY, t_rem);
+  }
+  double carry = 0.0;
+  for (int b0 = 0; b0 < n; b0 += BLK) carry += readlane_d(scan_sum(lane_masses(b0)), WAVE - 1);
+  *total = carry;
+  const double t = u * carry;
+  double c2 = 0.0;
+  int lb = -1, ll = -1;
+  for (int b0 = 0; b0 < n; b0 += BLK) {
+    const double ls = lane_masses(b0);
+    const double cum = scan_sum(ls) + c2;
+    const unsigned long long pos = __ballot(ls > 0.0);
+    if (pos) {
+      lb = b0;
+      ll = 63 - __clzll((long long)pos);
+    }
+    const unsigned long long cr = __ballot(ls > 0.0 && cum > t);
+    if (cr) {
+      const int l = __ffsll((long long)cr) - 1;
+      const double prev = (l == 0) ? c2 : readlane_d(cum, l - 1);
+      return in_lane(b0, l, t - prev, t_rem);
+    }
+    c2 = readlane_d(cum, WAVE - 1);
+  }
+  if (lb < 0) return -1;
+  lane_masses(lb);
+  return in_lane(lb, ll, INFINITY, t_rem);
+}
+
 // ---------------------------------------------------------------- top-k threshold
 
 // One radix-select digit (bits [shift, shift+8) of the key) for every row.  The prefix
@@ -530,7 +644,7 @@ constexpr int SEQ_LDS_ROWS = 129;    // rows of one sequence kept in LDS (G <= 6
 // position i is accepted when the drafted token equals the target argmax
 // ("tannlonggtaoo" note, "Greedy Sampling"); the first mismatch, or the bonus position,
 // takes the target argmax.  Its own partial (index np - 1) comes from its registers.
-template <typename T>
+template <typename T, bool LDS>
 SVD void greedy_finish(const Args &a, int b, float own_best, int own_idx, int own_flag) {
   constexpr int UNR = SEQ_LDS_PARTS / WAVE;
   __shared__ float s_po[SEQ_LDS_PARTS];
@@ -540,7 +654,7 @@ SVD void greedy_finish(const Args &a, int b, float own_best, int own_idx, int ow
   const int G = a.G, rps = a.rps, C = a.C;
   const size_t r0 = (size_t)b * rps;
   const int np = rps * C, own = np - 1;
-  const bool lds = np <= SEQ_LDS_PARTS && rps <= SEQ_LDS_ROWS;
+  constexpr bool lds = LDS;  // the sequence fits in LDS (every access below is resolved at compile time)
   const unsigned tag = a.tag;
   const u64 *pw = a.w.tw_part + r0 * C * 3;
   const int x0 = (lane < G) ? a.tokens[(size_t)b * G + lane] : 0;
@@ -591,8 +705,7 @@ SVD void greedy_finish(const Args &a, int b, float own_best, int own_idx, int ow
     if (lane == 0) a.accepted_len[b] = SV_ROW_INTERNAL;
     return;
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  __builtin_amdgcn_wave_barrier();
+  lds_sync();
   auto part = [&](int jr, int cc, float &v, int &i, int &f) {
     const int k = jr * C + cc;
     if (lds) {
@@ -627,8 +740,7 @@ SVD void greedy_finish(const Args &a, int b, float own_best, int own_idx, int ow
       const int jr = jr0 + lane;
       if (jr < rps) combine_row(jr, s_rarg[jr], s_rok[jr]);
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_wave_barrier();
+    lds_sync();
   }
   auto r_stat = [&](int jr, int &arg, int &ok) {
     if (lds) {
@@ -684,21 +796,21 @@ SVD void greedy_finish(const Args &a, int b, float own_best, int own_idx, int ow
 // It writes the accepted prefix and the -1 padding, and publishes the draw's record
 // (the drawn token and accepted_len are written by the draw).  The finisher's own
 // partial (index np - 1) and token logit come from its registers.
-template <typename T, bool TOPK>
+template <typename T, bool TOPK, bool LDS>
 SVD void sampling_finish(const Args &a, int b, float own_off, float own_hi, float own_lo,
                          bool own_tok, float own_zx) {
   constexpr int UNR = SEQ_LDS_PARTS / WAVE;
   constexpr int RUNR = (SEQ_LDS_ROWS + WAVE - 1) / WAVE;
   __shared__ float s_po[SEQ_LDS_PARTS];
   __shared__ double s_ps[SEQ_LDS_PARTS];
-  __shared__ float s_roff[SEQ_LDS_ROWS], s_rzx[SEQ_LDS_ROWS], s_rtau[SEQ_LDS_ROWS];
+  __shared__ float s_roff[SEQ_LDS_ROWS], s_rzx[SEQ_LDS_ROWS], s_rtau[SEQ_LDS_ROWS], s_rsum[SEQ_LDS_ROWS];
   __shared__ double s_rl2s[SEQ_LDS_ROWS];
   __shared__ int s_rok[SEQ_LDS_ROWS];
   const int lane = lane_id();
   const int G = a.G, rps = a.rps, C = a.C;
   const size_t r0 = (size_t)b * rps;
   const int np = rps * C, own = np - 1;
-  const bool lds = np <= SEQ_LDS_PARTS && rps <= SEQ_LDS_ROWS;
+  constexpr bool lds = LDS;  // the sequence fits in LDS (every access below is resolved at compile time)
   const unsigned tag = a.tag;
   const u64 *pw = a.w.tw_part + r0 * C * 3;
   const u64 *zw = a.w.tw_zx + r0;
@@ -792,8 +904,7 @@ SVD void sampling_finish(const Args &a, int b, float own_off, float own_hi, floa
       __builtin_amdgcn_s_sleep(2);
     }
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  __builtin_amdgcn_wave_barrier();
+  lds_sync();
   u64 *jw = a.w.tw_job + (size_t)b * JW;
   int32_t *out = a.out_tokens + (size_t)b * (G + 1);
   if (!alive) {  // gave up waiting: report it, and let the draw items go
@@ -821,12 +932,33 @@ SVD void sampling_finish(const Args &a, int b, float own_off, float own_hi, floa
   };
   auto tau_of = [&](int jr) -> float { return lds ? s_rtau[jr] : (TOPK ? a.w.row_tau[r0 + jr] : -INFINITY); };
 
-  // Row statistics: lane jr combines row jr's chunks in chunk order (rows in parallel).
-  // Rows beyond the LDS capacity are recombined on demand, which gives the same values.
+  // Row statistics: lane jr combines row jr's chunks (rows in parallel): the row offset
+  // is the largest chunk offset, the row sum is sum_c S_c * 2^(off_c - off) in chunk
+  // order; the chunks' reads are batched so they are in flight together.  A row with no
+  // finite value (every offset -inf) or a NaN comes out with a NaN sum.  Rows beyond the
+  // LDS capacity are recombined on demand, which gives the same values.
   auto combine_row = [&](int jr, float &o, double &t) {
+    constexpr int CB = 4;
     o = -INFINITY;
+    for (int c0 = 0; c0 < C; c0 += CB) {
+      float v[CB];
+#pragma unroll
+      for (int k = 0; k < CB; ++k) v[k] = (c0 + k < C) ? p_off(jr, c0 + k) : -INFINITY;
+#pragma unroll
+      for (int k = 0; k < CB; ++k) o = fmaxf(o, v[k]);
+    }
     t = 0.0;
-    for (int cc = 0; cc < C; ++cc) lse_combine(o, t, p_off(jr, cc), p_sum(jr, cc));
+    for (int c0 = 0; c0 < C; c0 += CB) {
+      float v[CB];
+      double sc[CB];
+#pragma unroll
+      for (int k = 0; k < CB; ++k) {
+        v[k] = (c0 + k < C) ? p_off(jr, c0 + k) : o;
+        sc[k] = (c0 + k < C) ? p_sum(jr, c0 + k) : 0.0;
+      }
+#pragma unroll
+      for (int k = 0; k < CB; ++k) t += sc[k] * (double)fast_exp2(v[k] - o);
+    }
   };
   for (int jr0 = 0; jr0 < rps; jr0 += WAVE) {
     const int jr = jr0 + lane;
@@ -835,19 +967,18 @@ SVD void sampling_finish(const Args &a, int b, float own_off, float own_hi, floa
       double t;
       combine_row(jr, o, t);
       const bool ok = isfinite(o) && isfinite(t) && t > 0.0;
-      if (a.row_stats) {
-        a.row_stats[(r0 + jr) * 2 + 0] = (float)((double)o * LN2);
-        a.row_stats[(r0 + jr) * 2 + 1] = (float)t;
-      }
-      if (lds) {
+      if (lds) {  // the optional row_stats output is written last, from LDS
         s_roff[jr] = o;
         s_rl2s[jr] = ok ? log2(t) : 0.0;
         s_rok[jr] = ok ? 1 : 0;
+        s_rsum[jr] = (float)t;
+      } else if (a.row_stats) {
+        a.row_stats[(r0 + jr) * 2 + 0] = (float)((double)o * LN2);
+        a.row_stats[(r0 + jr) * 2 + 1] = (float)t;
       }
     }
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  __builtin_amdgcn_wave_barrier();
+  lds_sync();
   auto r_stat = [&](int jr, float &o, double &l2s, int &ok) {
     if (lds) {
       o = s_roff[jr];
@@ -875,9 +1006,8 @@ SVD void sampling_finish(const Args &a, int b, float own_off, float own_hi, floa
       const double sc = p_sum(G, cc);
       return (sc > 0.0) ? sc * (double)fast_exp2(p_off(G, cc) - oG) : 0.0;
     };
-    const double total = wave_total(C, cm);
-    double trem;
-    c_bonus = wave_pick(C, (double)us * total, cm, &trem);
+    double trem, total;
+    c_bonus = wave_pick_frac(C, (double)us, cm, &trem, &total);
     if (c_bonus >= 0) {
       off_bonus = p_off(G, c_bonus);
       t_bonus = trem * (double)fast_exp2(oG - off_bonus);
@@ -977,6 +1107,12 @@ SVD void sampling_finish(const Args &a, int b, float own_off, float own_hi, floa
     default: break;
   }
   if (lane < JW_USED) tw_put(&jw[lane], tag, bits);
+  if (lds && a.row_stats) {
+    for (int jr = lane; jr < rps; jr += WAVE) {
+      a.row_stats[(r0 + jr) * 2 + 0] = (float)((double)s_roff[jr] * LN2);
+      a.row_stats[(r0 + jr) * 2 + 1] = s_rsum[jr];
+    }
+  }
 }
 
 // ---------------------------------------------------------------- pass 1: normaliser
@@ -1059,11 +1195,18 @@ SVD void norm_item(const Args &a, int item) {
 
   const double S = (s_s[0] + s_s[1]) + (s_s[2] + s_s[3]);
   const float s_hi = d_head(S), s_lo = d_tail(S);
+  // The sequence's last item in grid order finishes the sequence, from its own values
+  // and the other items' published ones.
+  if (jr == a.rps - 1 && c == a.C - 1) {
+    if (a.rps * a.C <= SEQ_LDS_PARTS && a.rps <= SEQ_LDS_ROWS)
+      sampling_finish<T, TOPK, true>(a, b, off, s_hi, s_lo, tok_here, zx);
+    else
+      sampling_finish<T, TOPK, false>(a, b, off, s_hi, s_lo, tok_here, zx);
+    return;
+  }
   u64 *pw = a.w.tw_part + ((size_t)r * a.C + c) * 3;
   if (lane < 3) tw_putf(pw + lane, a.tag, lane == 0 ? off : (lane == 1 ? s_hi : s_lo));
   if (lane == 3 && tok_here) tw_putf(&a.w.tw_zx[r], a.tag, zx);
-  // The sequence's last item in grid order finishes the sequence.
-  if (jr == a.rps - 1 && c == a.C - 1) sampling_finish<T, TOPK>(a, b, off, s_hi, s_lo, tok_here, zx);
 }
 
 // ---------------------------------------------------------------- pass 1: greedy argmax
@@ -1110,10 +1253,14 @@ __global__ __launch_bounds__(NT) void k_argmax(const Args a) {
     best_combine(best, bi, s_v[w], s_i[w]);
     fl |= s_f[w];
   }
+  // The sequence's last item in grid order finishes the sequence.
+  if (jr == a.rps - 1 && c == a.C - 1) {
+    if (a.rps * a.C <= SEQ_LDS_PARTS && a.rps <= SEQ_LDS_ROWS) greedy_finish<T, true>(a, b, best, bi, fl);
+    else greedy_finish<T, false>(a, b, best, bi, fl);
+    return;
+  }
   u64 *pw = a.w.tw_part + ((size_t)r * a.C + c) * 3;
   if (lane < 3) tw_put(pw + lane, a.tag, lane == 0 ? __float_as_uint(best) : (lane == 1 ? (unsigned)bi : (unsigned)fl));
-  // The sequence's last item in grid order finishes the sequence.
-  if (jr == a.rps - 1 && c == a.C - 1) greedy_finish<T>(a, b, best, bi, fl);
 }
 
 // ---------------------------------------------------------------- pass 2: the draw
@@ -1123,6 +1270,7 @@ __global__ __launch_bounds__(NT) void k_argmax(const Args a) {
 // per-element arguments carry only their own rounding.
 struct ResidualW {
   float k2, mt_hi, mt_lo, md_hi, md_lo, tau_t, tau_d;
+  float off_j;  // row offset of p_j (the zero-residual fallback's reference)
   SVD float operator()(float zt, float zd) const {
     zt = (zt < tau_t) ? -INFINITY : zt;
     zd = (zd < tau_d) ? -INFINITY : zd;
@@ -1283,8 +1431,7 @@ SVD int wave_chunk_draw(const Args &a, const T *rowA, const T *rowB, int c, cons
     const double m = wave_sum((double)acc);
     if (lane == 0) s_wseg[sg] = m;
   }
-  __builtin_amdgcn_s_waitcnt(0);  // lane 0's LDS writes are done before any lane reads them
-  __builtin_amdgcn_wave_barrier();
+  lds_sync();
   auto segm = [&](int i) { return s_wseg[i]; };
   double srem;
   const int sp = wave_pick(SEGS, t, segm, &srem);
@@ -1307,6 +1454,87 @@ SVD int pick_target_chunk(const Args &a, int r, float off_r, float u, double *t_
   const int c = wave_pick(a.C, (double)u * total, cm, &trem);
   *t_in = (c >= 0) ? trem * (double)fast_exp2(off_r - tw_f(ld_dev(&pw[c * 3]))) : 0.0;
   return c;
+}
+
+constexpr int COMB_LDS_SEGS = 1024;  // segment masses of one sequence kept in LDS by the combiner
+
+// The sequence's last draw item (one wave): wait for every other item's segment masses
+// (lane l reads segments 4l..4l+3 of each block of 256, every load of a block in flight
+// at once), keep them in LDS (FITS: all of them; otherwise the rest are read on demand),
+// then one inverse CDF over all segments in index order picks the segment, and the
+// segment is re-read to pick lane and element.
+template <typename T, bool ALIGNED, bool FITS>
+SVD void combine_draw(const Args &a, int b, int j, float u, const T *row_t, const T *row_d,
+                      const ResidualW &wf, const double *s_seg, double *s_cs, int own0) {
+  constexpr int SB = 4, BLK = SB * WAVE, MINE = KSUB * NW;
+  const int lane = lane_id();
+  const unsigned tag = a.tag;
+  const int G = a.G;
+  const int nseg = a.C * SEGS;
+  const int cown = own0 / SEGS;
+  const u64 *sw = a.w.tw_seg + (size_t)b * a.C * SEGS * 2;
+  auto mine = [&](int i) { return i >= own0 && i < own0 + MINE; };
+  bool alive = true;
+  unsigned polls = 0;
+  for (int blk = 0; blk < nseg && alive; blk += BLK) {
+    for (;;) {
+      u64 wh[SB], wl[SB];
+#pragma unroll
+      for (int k = 0; k < SB; ++k) {
+        const int i = blk + lane * SB + k;
+        const int ii = (i < nseg && !mine(i)) ? i : 0;
+        wh[k] = ld_dev(&sw[(size_t)ii * 2]);
+        wl[k] = ld_dev(&sw[(size_t)ii * 2 + 1]);
+      }
+      bool ok = true;
+#pragma unroll
+      for (int k = 0; k < SB; ++k) {
+        const int i = blk + lane * SB + k;
+        if (i < nseg && !mine(i)) ok = ok && tw_ok(wh[k], tag) && tw_ok(wl[k], tag);
+      }
+      if (__ballot(!ok) == 0) {
+#pragma unroll
+        for (int k = 0; k < SB; ++k) {
+          const int i = blk + lane * SB + k;
+          if (i < nseg && i < COMB_LDS_SEGS) s_cs[i] = mine(i) ? s_seg[i - cown * SEGS] : d_join(tw_f(wh[k]), tw_f(wl[k]));
+        }
+        break;
+      }
+      if (++polls >= a.spin_limit) {
+        alive = false;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  if (!alive) {
+    if (lane == 0) a.accepted_len[b] = SV_ROW_INTERNAL;
+    return;
+  }
+  lds_sync();
+  auto seg_of = [&](int i) -> double {
+    if (FITS || i < COMB_LDS_SEGS) return s_cs[i];
+    if (mine(i)) return s_seg[i - cown * SEGS];
+    return d_join(tw_f(ld_dev(&sw[(size_t)i * 2])), tw_f(ld_dev(&sw[(size_t)i * 2 + 1])));
+  };
+  double Z, ts;
+  const int sp = wave_pick4_frac(nseg, (double)u, seg_of, &ts, &Z);
+  int tok = -1;
+  if (Z > 0.0) {
+    if (sp >= 0 && sp < nseg) tok = segment_draw<T, ALIGNED>(a, row_t, row_d, sp / SEGS, sp % SEGS, wf, ts);
+  } else {  // zero residual (reachable only through rounding): draw from p_j itself
+    const int rt = b * a.rps + j;
+    double tin;
+    const int cp = pick_target_chunk(a, rt, wf.off_j, u, &tin);
+    if (cp >= 0 && cp < a.C) {
+      const TargetW tw{a.k2, tw_f(ld_dev(&a.w.tw_part[((size_t)rt * a.C + cp) * 3])), wf.tau_t};
+      tok = wave_chunk_draw<T, ALIGNED>(a, row_t, (const T *)nullptr, cp, tw, tin);
+    }
+  }
+  if (lane == 0) {
+    a.out_tokens[(size_t)b * (G + 1) + j] = tok;
+    a.accepted_len[b] = j;
+  }
 }
 
 // Draw item (sequence b, chunk c, quarter sub).  All draw items follow every first-pass
@@ -1398,108 +1626,25 @@ SVD void draw_item(const Args &a, int item) {
   wf.md_lo = jf(JW_MD_LO);
   wf.tau_t = jf(JW_TAU_T);
   wf.tau_d = jf(JW_TAU_D);
+  wf.off_j = jf(JW_OFF_J);
   const T *row_t = seq_row<T>(a, b, j), *row_d = seq_row<T>(a, b, G + 1 + j);
   chunk_masses<T, ALIGNED, KSUB, KSUB, true>(a, row_t, row_d, c, sub * KSUB, wf, s_seg);
   if (wid != 0) return;  // wave 0 publishes and finishes
   u64 *sw = a.w.tw_seg + (size_t)b * a.C * SEGS * 2;
-  constexpr int MINE = KSUB * NW;  // segments of this item
-  const int own0 = c * SEGS + sub * MINE;
-  if (lane < 2 * MINE) {
-    const double m = s_seg[sub * MINE + (lane >> 1)];
-    tw_putf(&sw[(size_t)own0 * 2 + lane], tag, (lane & 1) ? d_tail(m) : d_head(m));
-  }
-  if (c != a.C - 1 || sub != NSUB - 1) return;
-
-  // The sequence's last draw item: wait for every segment mass of the sequence (every
-  // load of a block of 256 segments in flight at once), keep them in LDS (read on
-  // demand beyond LDS_CHUNKS chunks); chunk totals are segment-order scans, so the
-  // segment pick inside the chosen chunk sums to exactly its total.
-  constexpr int LDS_CHUNKS = 32, SB = 4;
-  __shared__ double s_cs[LDS_CHUNKS * SEGS];
-  __shared__ double s_ct[LDS_CHUNKS];
-  const int nseg = a.C * SEGS;
-  const bool lds = a.C <= LDS_CHUNKS;
-  auto mine = [&](int i) { return i >= own0 && i < own0 + MINE; };
-  bool alive = true;
-  unsigned polls = 0;
-  for (int blk = 0; blk < nseg && alive; blk += SB * WAVE) {
-    for (;;) {
-      u64 wh[SB], wl[SB];
-#pragma unroll
-      for (int k = 0; k < SB; ++k) {
-        const int i = blk + lane + k * WAVE;
-        const int ii = (i < nseg && !mine(i)) ? i : 0;
-        wh[k] = ld_dev(&sw[(size_t)ii * 2]);
-        wl[k] = ld_dev(&sw[(size_t)ii * 2 + 1]);
-      }
-      bool ok = true;
-#pragma unroll
-      for (int k = 0; k < SB; ++k) {
-        const int i = blk + lane + k * WAVE;
-        if (i < nseg && !mine(i)) ok = ok && tw_ok(wh[k], tag) && tw_ok(wl[k], tag);
-      }
-      if (__ballot(!ok) == 0) {
-        if (lds) {
-#pragma unroll
-          for (int k = 0; k < SB; ++k) {
-            const int i = blk + lane + k * WAVE;
-            if (i < nseg) s_cs[i] = mine(i) ? s_seg[i - c * SEGS] : d_join(tw_f(wh[k]), tw_f(wl[k]));
-          }
-        }
-        break;
-      }
-      if (++polls >= a.spin_limit) {
-        alive = false;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(2);
+  const int own0 = c * SEGS + sub * KSUB * NW;
+  if (c != a.C - 1 || sub != NSUB - 1) {
+    if (lane < 2 * KSUB * NW) {
+      const double m = s_seg[sub * KSUB * NW + (lane >> 1)];
+      tw_putf(&sw[(size_t)own0 * 2 + lane], tag, (lane & 1) ? d_tail(m) : d_head(m));
     }
-  }
-  if (!alive) {
-    if (lane == 0) a.accepted_len[b] = SV_ROW_INTERNAL;
     return;
   }
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's LDS writes land before any lane reads them
-  __builtin_amdgcn_wave_barrier();
-  auto seg_of = [&](int i) -> double {
-    if (lds) return s_cs[i];
-    if (mine(i)) return s_seg[i - c * SEGS];
-    return d_join(tw_f(ld_dev(&sw[(size_t)i * 2])), tw_f(ld_dev(&sw[(size_t)i * 2 + 1])));
-  };
-  for (int cc = 0; cc < a.C && cc < LDS_CHUNKS; ++cc) {
-    auto segm = [&](int i) { return seg_of(cc * SEGS + i); };
-    const double tot = wave_total(SEGS, segm);
-    if (lane == 0) s_ct[cc] = tot;
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __builtin_amdgcn_wave_barrier();
-  auto ctot = [&](int cc) {
-    if (cc < LDS_CHUNKS) return s_ct[cc];
-    auto segm = [&](int i) { return seg_of(cc * SEGS + i); };
-    return wave_total(SEGS, segm);
-  };
-  const double Z = wave_total(a.C, ctot);
-  int tok = -1;
-  if (Z > 0.0) {
-    double tc, ts;
-    const int cp = wave_pick(a.C, (double)u * Z, ctot, &tc);
-    if (cp >= 0 && cp < a.C) {
-      auto sm = [&](int i) { return seg_of(cp * SEGS + i); };
-      const int sp = wave_pick(SEGS, tc, sm, &ts);
-      if (sp >= 0) tok = segment_draw<T, ALIGNED>(a, row_t, row_d, cp, sp, wf, ts);
-    }
-  } else {  // zero residual (reachable only through rounding): draw from p_j itself
-    double tin;
-    const int cp = pick_target_chunk(a, rt, jf(JW_OFF_J), u, &tin);
-    if (cp >= 0 && cp < a.C) {
-      const TargetW tw{a.k2, tw_f(ld_dev(&a.w.tw_part[((size_t)rt * a.C + cp) * 3])), wf.tau_t};
-      tok = wave_chunk_draw<T, ALIGNED>(a, row_t, (const T *)nullptr, cp, tw, tin);
-    }
-  }
-  if (lane == 0) {
-    out[j] = tok;
-    a.accepted_len[b] = j;
-  }
+  // The sequence's last draw item combines (its own masses stay in LDS, unpublished).
+  __shared__ double s_cs[COMB_LDS_SEGS];
+  if (a.C * SEGS <= COMB_LDS_SEGS)
+    combine_draw<T, ALIGNED, true>(a, b, j, u, row_t, row_d, wf, s_seg, s_cs, own0);
+  else
+    combine_draw<T, ALIGNED, false>(a, b, j, u, row_t, row_d, wf, s_seg, s_cs, own0);
 }
 
 // Sampling: the first pass (normalisers, acceptance scan) and the draws in one grid.
