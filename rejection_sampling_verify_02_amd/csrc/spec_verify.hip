@@ -520,6 +520,39 @@ SVD int wave_pick4_frac(int n, double u, const MFn &mfn, double *t_rem, double *
   return in_lane(lb, ll, INFINITY, t_rem);
 }
 
+// ---------------------------------------------------------------- block placement
+
+// The device hands workgroups to its XCDs round-robin (blockIdx % 8), each XCD in
+// blockIdx order.  Work comes in UNITS (a row, or a sequence) of per1 first-phase items
+// and per2 second-phase items, and the last items of a unit wait for the earlier ones.
+// Block p runs item q = p / LANES of lane k = p % LANES; lane k owns units k, k+LANES, ...
+// and runs all their first-phase items, unit after unit, then all their second-phase
+// items.  So each XCD streams whole units front to back, the waiting items (a unit's
+// last ones) are spread over every XCD instead of all landing on one, and every wait is
+// for an earlier item of the same lane, i.e. a smaller blockIdx: the grid cannot stall,
+// wherever the blocks run.  Returns false for the padding blocks of short lanes.
+constexpr int LANES = 8;
+
+SVD bool lane_item(int units, int per1, int per2, int &phase, int &item) {
+  const int p = (int)blockIdx.x;
+  const int k = p % LANES, q = p / LANES;
+  const int nu = (units > k) ? (units - k + LANES - 1) / LANES : 0;
+  if (q < nu * per1) {
+    const int s = q / per1;
+    item = (k + LANES * s) * per1 + (q - s * per1);
+    phase = 1;
+    return true;
+  }
+  const int q2 = q - nu * per1;
+  if (q2 < nu * per2) {
+    const int s = q2 / per2;
+    item = (k + LANES * s) * per2 + (q2 - s * per2);
+    phase = 2;
+    return true;
+  }
+  return false;
+}
+
 // ---------------------------------------------------------------- top-k threshold
 
 // One radix-select digit (bits [shift, shift+8) of the key) for every row.  The prefix
@@ -535,7 +568,9 @@ __global__ __launch_bounds__(NT) void k_topk_digit(const Args a, int pass, int l
   __shared__ unsigned s_ge[256];
   __shared__ int s_alive;
   const int tid = threadIdx.x;
-  const int r = blockIdx.x / a.C, c = blockIdx.x - r * a.C;
+  int phase, xi;
+  if (!lane_item((int)(a.B * a.rps), a.C, 0, phase, xi)) return;  // units: rows
+  const int r = xi / a.C, c = xi - r * a.C;
   const int b = r / a.rps, jr = r - b * a.rps;
   const int shift = 24 - 8 * pass;
   const uint2 st = (pass == 0) ? make_uint2(0u, (unsigned)a.top_k) : a.w.tk_state[r];
@@ -1217,7 +1252,9 @@ __global__ __launch_bounds__(NT) void k_argmax(const Args a) {
   __shared__ float s_v[NW];
   __shared__ int s_i[NW], s_f[NW];
   const int tid = threadIdx.x, lane = lane_id(), wid = tid / WAVE;
-  const int r = blockIdx.x / a.C, c = blockIdx.x - r * a.C;
+  int phase, item;
+  if (!lane_item(a.B, a.rps * a.C, 0, phase, item)) return;  // units: sequences
+  const int r = item / a.C, c = item - r * a.C;
   const int b = r / a.rps, jr = r - b * a.rps;
 
   float x[VPT][VEC];
@@ -1647,14 +1684,14 @@ SVD void draw_item(const Args &a, int item) {
     combine_draw<T, ALIGNED, false>(a, b, j, u, row_t, row_d, wf, s_seg, s_cs, own0);
 }
 
-// Sampling: the first pass (normalisers, acceptance scan) and the draws in one grid.
-// Blocks 0 .. R*C-1 are first-pass items in sequence order; the draw items follow.
+// Sampling: the first pass (normalisers, acceptance scan) and the draws in one grid;
+// units are sequences: first-pass items (rows in order, chunks in order), then draw items.
 template <typename T, bool ALIGNED, bool TOPK>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(5))) void k_verify(const Args a) {
-  const int n1 = a.B * a.rps * a.C;
-  const int x = (int)blockIdx.x;
-  if (x < n1) norm_item<T, ALIGNED, TOPK>(a, x);
-  else draw_item<T, ALIGNED>(a, x - n1);
+  int phase, item;
+  if (!lane_item(a.B, a.rps * a.C, a.C * NSUB, phase, item)) return;
+  if (phase == 1) norm_item<T, ALIGNED, TOPK>(a, item);
+  else draw_item<T, ALIGNED>(a, item);
 }
 
 }  // namespace sv
@@ -1687,7 +1724,10 @@ bool make_plan(int32_t B, int32_t G, int32_t V, sv_dtype dt, float T, int32_t to
   p.R = (long long)B * p.rps;
   p.topk = !p.greedy && top_k > 0 && top_k < V;
   p.digit_passes = (dt == SV_BF16) ? 2 : 4;
-  if (p.R * p.C + (long long)B * p.C * NSUB > 0x7fffffffLL) return false;
+  // grids padded to whole lanes (see lane_item)
+  const long long lanes_b = (B + LANES - 1) / LANES * LANES, lanes_r = (p.R + LANES - 1) / LANES * LANES;
+  if (lanes_b * ((long long)p.rps * p.C + (long long)p.C * NSUB) > 0x7fffffffLL || lanes_r * p.C > 0x7fffffffLL)
+    return false;
   const size_t R = (size_t)p.R, C = (size_t)p.C, Bz = (size_t)B;
   const bool smp = !p.greedy;
   size_t o = 0;
@@ -1727,8 +1767,12 @@ template <typename T, bool AL>
 hipError_t launch_all(const Plan &p, const Args &a, hipStream_t st, void *const *ev, int nev,
                       int *nl) {
   const dim3 blk(NT);
-  const unsigned rows_grid = (unsigned)(p.R * p.C);
-  const unsigned verify_grid = (unsigned)(p.R * p.C + (long long)a.B * p.C * NSUB);
+  // Grids padded to whole lanes of units (see lane_item): rows for the top-k passes,
+  // sequences for k_argmax and k_verify.
+  const long long lb = (a.B + LANES - 1) / LANES, lr = (p.R + LANES - 1) / LANES;
+  const unsigned topk_grid = (unsigned)(LANES * lr * p.C);
+  const unsigned argmax_grid = (unsigned)(LANES * lb * p.rps * p.C);
+  const unsigned verify_grid = (unsigned)(LANES * lb * ((long long)p.rps * p.C + (long long)p.C * NSUB));
   int n = 0;
   hipError_t e = hipSuccess;
   // With events, kernel i is launched with (events[2i], events[2i+1]) as its start and
@@ -1746,14 +1790,14 @@ hipError_t launch_all(const Plan &p, const Args &a, hipStream_t st, void *const 
   if (p.greedy) {
     aa.tag = next_tag();
     void *args[] = {&aa};
-    go((const void *)&k_argmax<T, AL>, rows_grid, args);
+    go((const void *)&k_argmax<T, AL>, argmax_grid, args);
   } else {
     if (p.topk) {
       for (int pass = 0; pass < p.digit_passes; ++pass) {
         int ps = pass, lp = (pass == p.digit_passes - 1) ? 1 : 0;
         aa.tag = next_tag();
         void *args[] = {&aa, &ps, &lp};
-        go((const void *)&k_topk_digit<T, AL>, rows_grid, args);
+        go((const void *)&k_topk_digit<T, AL>, topk_grid, args);
       }
       aa.tag = next_tag();
       void *args[] = {&aa};
