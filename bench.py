@@ -78,7 +78,10 @@ class HipEvents:
 
 def make_sets(cid: int, n_sets: int, dev):
     """R input sets of one workload on the device; draft tokens drawn by the library itself
-    (each draft row is its own G = 0 call: X ~ q by inverse CDF with the draft uniforms)."""
+    (each draft row is its own G = 0 call: X ~ q by inverse CDF with the draft uniforms, or
+    the draft argmax at temperature 0).  The top-k workload's third group needs the
+    target's kept set, found here with torch.topk (input preparation, outside the timed
+    path)."""
     import torch
     import rejection_sampling_verify_02_amd as sv
     from rejection_sampling_verify_02_amd import workloads as wl
@@ -95,20 +98,34 @@ def make_sets(cid: int, n_sets: int, dev):
             return (t.view(torch.bfloat16) if a.dtype == np.uint16 else t).to(dev)
 
         target, draft = dev_t(raw.target), dev_t(raw.draft)
-        if cfg.temperature == 0:
-            raise SystemExit("the benchmark times the sampling workloads (greedy is a parity case)")
         if len(raw.disjoint_rows):
-            raise SystemExit("workload 5 needs the oracle to finish its recipe; it is a parity case")
+            # the draft's top-k support disjoint from the target's: -1e4 on the target's kept
+            # set {z >= k-th largest} (ties included), position by position
+            rows = torch.as_tensor(raw.disjoint_rows, device=dev)
+            zt = target[rows, :G].float()
+            tau = torch.topk(zt, cfg.top_k, dim=-1).values[..., -1:]
+            d = draft[rows]
+            d[zt >= tau] = torch.tensor(-1e4, dtype=d.dtype, device=dev)
+            draft[rows] = d
         drows = draft.reshape(B * G, 1, V)
-        u_draft = dev_t(raw.u_draft.reshape(B * G))
-        _, tok = sv.spec_verify(drows, None, None, None, u_draft, cfg.temperature, cfg.top_k)
+        if cfg.temperature == 0:
+            _, tok = sv.spec_verify(drows, None, None, None, None, 0.0, 0)
+        else:
+            u_draft = dev_t(raw.u_draft.reshape(B * G))
+            _, tok = sv.spec_verify(drows, None, None, None, u_draft, cfg.temperature, cfg.top_k)
         tokens = tok.reshape(B, G).contiguous()
         fixed = torch.from_numpy(raw.fixed_tokens).to(dev)
         tokens = torch.where(fixed >= 0, fixed, tokens)
-        sets.append(dict(target=target, draft=draft, tokens=tokens, u_accept=dev_t(raw.u_accept),
-                         u_sample=dev_t(raw.u_sample)))
-        host.append(dict(target=raw.target, draft=raw.draft, u_accept=raw.u_accept,
-                         u_sample=raw.u_sample))
+        greedy = cfg.temperature == 0
+        sets.append(dict(target=target, draft=None if greedy else draft, tokens=tokens,
+                         u_accept=None if greedy else dev_t(raw.u_accept),
+                         u_sample=None if greedy else dev_t(raw.u_sample)))
+        if len(raw.disjoint_rows):  # the host copy for the CPU baseline gets the same draft
+            hd = draft.cpu()
+            hd = hd.view(torch.int16).numpy().view(np.uint16) if hd.dtype == torch.bfloat16 else hd.numpy()
+        else:
+            hd = raw.draft
+        host.append(dict(target=raw.target, draft=hd, u_accept=raw.u_accept, u_sample=raw.u_sample))
         log(f"[bench] input set {s + 1}/{n_sets} ready ({time.time() - t0:.1f} s)")
     torch.cuda.synchronize(dev)
     for s, h in zip(sets, host):
@@ -211,7 +228,9 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3])
+    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5],
+                    help="workload (3, the default, is the headline; 4 greedy and 5 top-k are timed "
+                         "for the design notes)")
     ap.add_argument("--sets", type=int, default=0, help="input sets to rotate (default: >= 1 GiB)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -243,7 +262,8 @@ def main() -> int:
     cfg = wl.CONFIGS[args.config]
     B, G, V = cfg.B, cfg.G, cfg.V
     esz = 2 if cfg.dtype == "bf16" else 4
-    rows = B * (2 * G + 1)
+    greedy = cfg.temperature == 0
+    rows = B * (G + 1) if greedy else B * (2 * G + 1)  # greedy reads no draft row
     alg_bytes = rows * V * esz  # one read of every logit the result depends on
     n_sets = args.sets or max(2, -(-(1 << 30) // alg_bytes))
     log(f"[bench] workload {cfg.name}: B={B} G={G} V={V} {cfg.dtype}, {alg_bytes / 1e6:.2f} MB per call, "
@@ -317,13 +337,15 @@ def main() -> int:
     t_call = ms / 1e3
     positions = B * G
     value = positions / t_call
-    main_us = next((v for k, v in per_kernel.items() if k.endswith(":" + KERNEL)), None)
+    # the kernel that streams the logits: k_argmax at temperature 0, k_verify otherwise
+    kernel = "k_argmax" if greedy else KERNEL
+    main_us = next((v for k, v in per_kernel.items() if k.endswith(":" + kernel)), None)
     sha = hashlib.sha256(SOURCE.read_bytes()).hexdigest()
-    traffic, tnote = counters_traffic(sha)
+    traffic, tnote = counters_traffic(sha) if args.config == 3 else (None, "counters are taken on workload 3")
     roof = None
     if main_us:
         achieved = alg_bytes / (main_us * 1e-6) / 1e9
-        roof = {"bound": "hbm", "kernel": KERNEL, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+        roof = {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                 "traffic": traffic, "algorithmic_bytes": alg_bytes,
                 "avg_launch_us": round(main_us, 3)}

@@ -561,10 +561,14 @@ SVD bool lane_item(int units, int per1, int per2, int &phase, int &item) {
 // {z >= tau} is exactly the values >= the k-th largest, ties included.  Each chunk
 // publishes its digit histogram as 128 tagged words (two 16-bit counts each; a chunk
 // holds at most 16384 values); the row's last chunk in grid order collects them.
-template <typename T, bool ALIGNED>
+// The first pass counts its histogram in HREP copies, lane l adding into copy l % HREP:
+// logits crowd into a few leading digits (the exponent), and one copy would make a whole
+// wave's LDS atomics land on the same address one after another.  Later passes count
+// only the values that carry the prefix found so far, few per chunk: one copy.
+template <typename T, bool ALIGNED, int HREP>
 __global__ __launch_bounds__(NT) void k_topk_digit(const Args a, int pass, int last_pass) {
   constexpr int VEC = Fmt<T>::VEC;
-  __shared__ unsigned hist[256];
+  __shared__ unsigned hist[256 * HREP];
   __shared__ unsigned s_ge[256];
   __shared__ int s_alive;
   const int tid = threadIdx.x;
@@ -577,20 +581,29 @@ __global__ __launch_bounds__(NT) void k_topk_digit(const Args a, int pass, int l
   const uint32_t hi_mask = (pass == 0) ? 0u : (0xffffffffu << (shift + 8));
   const unsigned tag = a.tag;
 
-  hist[tid] = 0u;
+  for (int i = tid; i < 256 * HREP; i += NT) hist[i] = 0u;
   __syncthreads();
   float x[VPT][VEC];
   load_chunk<T, ALIGNED, true>(seq_row<T>(a, b, jr), a.V, a.nvec, c, tid, x);
+  const unsigned rep = (unsigned)tid & (HREP - 1);
 #pragma unroll
   for (int k = 0; k < VPT; ++k)
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
       if (elem_index<T>(c, k, tid, e) < a.V) {
         const uint32_t key = f2key(x[k][e]);
-        if ((key & hi_mask) == (st.x & hi_mask)) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+        if ((key & hi_mask) == (st.x & hi_mask)) atomicAdd(&hist[((key >> shift) & 255u) * HREP + rep], 1u);
       }
     }
   __syncthreads();
+  if (HREP > 1) {  // fold the copies: thread d owns digit d
+    unsigned h = 0;
+#pragma unroll
+    for (int r2 = 0; r2 < HREP; ++r2) h += hist[tid * HREP + ((r2 + tid) & (HREP - 1))];
+    __syncthreads();
+    hist[tid] = h;
+    __syncthreads();
+  }
   u64 *hw = a.w.tw_hist + (size_t)r * a.C * 128;
   if (c != a.C - 1) {
     if (tid < 128) tw_put(&hw[(size_t)c * 128 + tid], tag, hist[2 * tid] | (hist[2 * tid + 1] << 16));
@@ -1797,7 +1810,8 @@ hipError_t launch_all(const Plan &p, const Args &a, hipStream_t st, void *const 
         int ps = pass, lp = (pass == p.digit_passes - 1) ? 1 : 0;
         aa.tag = next_tag();
         void *args[] = {&aa, &ps, &lp};
-        go((const void *)&k_topk_digit<T, AL>, topk_grid, args);
+        const void *fn = (pass == 0) ? (const void *)&k_topk_digit<T, AL, 16> : (const void *)&k_topk_digit<T, AL, 1>;
+        go(fn, topk_grid, args);
       }
       aa.tag = next_tag();
       void *args[] = {&aa};
