@@ -89,12 +89,12 @@ def sv_launch_plan(B: int, G: int, V: int, dtype: int, temperature: float, top_k
 class Workspace:
     """A device buffer for the library's scratch data, one per device, grown on demand.
 
-    The library keeps self-resetting counters in the first
-    ``sv_workspace_zero_bytes(...)`` bytes: they must be zero when a call starts, a
-    call leaves exactly its own prefix at zero, and it may overwrite what lies after
-    it.  This class remembers how long the zero prefix is and, before a call that
-    needs a longer one, zeroes it with a fill kernel on the call's stream.  Calls
-    sharing a workspace must be ordered on one stream.
+    The library's workgroups hand results to one another as tagged words kept in the
+    first ``sv_workspace_zero_bytes(...)`` bytes: those must hold zeros or words of
+    completed calls when a call starts, and every call leaves them that way.  This class
+    remembers how long a zeroed prefix the buffer has and, before a call that needs a
+    longer one, zeroes it with a fill kernel on the call's stream.  Calls sharing a
+    workspace must be ordered on one stream.
     """
 
     def __init__(self):

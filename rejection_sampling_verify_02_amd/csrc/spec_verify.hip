@@ -17,23 +17,22 @@
 //   k_topk_digit  (only with top-k)  radix select of the k-th largest raw logit per row,
 //                 one 8-bit digit per launch (2 launches for bf16, 4 for f32), LDS
 //                 histograms per chunk, the last chunk of a row picks the digit.
-//   k_norm        per chunk of every row: block max m_c and sum of
-//                 2^(z*log2(e)/T - m_c*log2(e)/T), one v_exp_f32 per element.  Then only
-//                 wave 0 stays: it publishes the chunk partial; the last chunk of a row
-//                 combines the row's partials into its log-partition; the last row of a
-//                 sequence runs the acceptance scan (first rejection; token / row /
-//                 uniform / support checks) and leaves the sequence's job.
-//   k_sample      per chunk of every sequence: for a rejection at j, the chunk's masses
-//                 of [p_j - q_j]_+ per 64-vector segment; the last chunk picks chunk,
-//                 segment, lane and element where the cumulative mass passes u*Z.  For
-//                 a bonus, the chunk picked from k_norm's partials re-reads itself.
+//   k_verify      one grid per call.  First-pass items, per chunk of every row: block
+//                 max m_c and sum of 2^(z*log2(e)/T - m_c*log2(e)/T), one v_exp_f32 per
+//                 element, published as a partial.  The last item of a sequence combines
+//                 its rows' partials, runs the acceptance scan (first rejection; token /
+//                 row / uniform / support checks) and leaves the sequence's job.  Draw
+//                 items follow: for a rejection at j, the masses of [p_j - q_j]_+ per
+//                 64-vector segment of both rows at j; the last draw item picks segment,
+//                 lane and element where the cumulative mass passes u*Z.  For a bonus, the
+//                 chunk of p_G picked from the partials re-reads itself.
 //   k_argmax      greedy (T == 0): per-chunk argmax, row combine and scan, one launch.
 //
-// "Last chunk / last row" is decided with self-resetting ticket counters (atomicInc
-// with wrap-around) kept at the start of the workspace: a call needs those leading
-// bytes at zero and leaves them at zero, so no host sync or memset happens between
-// kernels or between calls of one shape.  All reductions use fixed trees or fixed
-// orders, so results are bitwise reproducible run to run.
+// Workgroups hand results to one another as tagged 64-bit words (the call's tag in the
+// upper half), written and read with device-scope atomic stores and loads; a reader
+// polls until the words it needs carry the tag.  Waits only go to items earlier in the
+// same XCD lane (see lane_item), so no grid can stall.  All reductions use fixed trees or
+// fixed orders, so results are bitwise reproducible run to run.
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
