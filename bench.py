@@ -33,7 +33,8 @@ METRIC = "verified draft positions/sec and achieved HBM GB/s (% of peak) at B=64
 PEAK_HBM_GBS = 8000.0
 KERNEL = "k_verify"  # the kernel that streams the logits (and draws) in the timed workload
 COUNTERS = ROOT / "profiles" / f"{KERNEL}_zipf_bf16_b64_counters.json"
-SOURCE = ROOT / "rejection_sampling_verify_02_amd" / "csrc" / "spec_verify.hip"
+# the sources of the verification kernels (the counter summary is tied to their hash)
+SOURCES = [ROOT / "rejection_sampling_verify_02_amd" / "csrc" / n for n in ("spec_verify.hip", "sv_device.h")]
 
 
 def log(msg: str) -> None:
@@ -211,7 +212,7 @@ def summarize_counters(kdir: str, cdir: str, out: Path) -> None:
            "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
            "traffic_bytes_per_launch": fetch + write,
            "algorithmic_bytes": 147750912,
-           "source_sha256": hashlib.sha256(SOURCE.read_bytes()).hexdigest(),
+           "source_sha256": source_sha(),
            "note": "FETCH_SIZE and WRITE_SIZE from separate rocprofv3 --pmc runs, scaled by a plain copy"}
     out.write_text(json.dumps(res, indent=1) + "\n")
     print(json.dumps(res))
@@ -228,14 +229,212 @@ def copy_probe(nbytes: int, reps: int) -> None:
     print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}))
 
 
+def time_loop(call, plan, K, warmup, stream, dev, hev, stage_events):
+    """Warm-up, then K calls timed as a caller runs them (wall clock and stream events),
+    then (unless disabled) the same K calls with a (start, stop) event pair on every kernel
+    dispatch.  Returns (wall_s, gpu_ms, per_kernel_us, wall2_s)."""
+    import torch
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize(dev)
+    log(f"[bench] warmup done ({warmup} calls)")
+    loop_ev = hev.create(2)
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    hev.record(loop_ev[0], stream)
+    for i in range(K):
+        call(warmup + i)
+    hev.record(loop_ev[1], stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    gpu_ms = hev.elapsed_ms(loop_ev[0], loop_ev[1])
+    hev.destroy(loop_ev)
+    log(f"[bench] timed {K} calls: wall {wall * 1e3:.2f} ms, events {gpu_ms:.2f} ms")
+    # The per-dispatch event pairs add a few microseconds of gap between kernels, so the
+    # first loop gives the throughput and this one each kernel's own duration.
+    per_kernel, wall2 = {}, None
+    if stage_events:
+        nl = len(plan)
+        stage = [hev.create(2 * nl) for _ in range(K)]
+        torch.cuda.synchronize(dev)
+        t1 = time.perf_counter()
+        for i in range(K):
+            call(warmup + i, stage[i])
+        torch.cuda.synchronize(dev)
+        wall2 = time.perf_counter() - t1
+        durs = np.array([[hev.elapsed_ms(ev[2 * j], ev[2 * j + 1]) for j in range(nl)] for ev in stage])
+        for j, name in enumerate(plan):
+            per_kernel[f"{j}:{name}"] = float(np.mean(durs[:, j]) * 1e3)
+        for ev in stage:
+            hev.destroy(ev)
+        log(f"[bench] timed {K} calls with per-kernel events: wall {wall2 * 1e3:.2f} ms")
+    return wall, gpu_ms, per_kernel, wall2
+
+
+def roofline(per_kernel, kernel, alg_bytes, traffic):
+    main_us = next((v for k, v in per_kernel.items() if k.endswith(":" + kernel)), None)
+    if not main_us:
+        return None
+    achieved = alg_bytes / (main_us * 1e-6) / 1e9
+    return {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+            "algorithmic_bytes": alg_bytes, "avg_launch_us": round(main_us, 3)}
+
+
+def source_sha() -> str:
+    h = hashlib.sha256()
+    for p in SOURCES:
+        h.update(p.read_bytes())
+    return h.hexdigest()
+
+
+def run_verify(args, dev, hev):
+    import torch
+    import rejection_sampling_verify_02_amd as sv
+    from rejection_sampling_verify_02_amd import workloads as wl
+
+    cfg = wl.CONFIGS[args.config]
+    B, G, V = cfg.B, cfg.G, cfg.V
+    esz = 2 if cfg.dtype == "bf16" else 4
+    greedy = cfg.temperature == 0
+    rows = B * (G + 1) if greedy else B * (2 * G + 1)  # greedy reads no draft row
+    alg_bytes = rows * V * esz  # one read of every logit the result depends on
+    n_sets = args.sets or max(2, -(-(1 << 30) // alg_bytes))
+    log(f"[bench] workload {cfg.name}: B={B} G={G} V={V} {cfg.dtype}, {alg_bytes / 1e6:.2f} MB per call, "
+        f"{n_sets} input sets")
+    sets, host = make_sets(args.config, n_sets, dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    dtc = sv.SV_BF16 if cfg.dtype == "bf16" else sv.SV_F32
+    plan = sv.sv_launch_plan(B, G, V, dtc, cfg.temperature, cfg.top_k)
+    ws = sv.Workspace()
+    acc = torch.empty((B,), dtype=torch.int32, device=dev)
+    out = torch.empty((B, G + 1), dtype=torch.int32, device=dev)
+
+    def call(i, events=None):
+        s = sets[i % n_sets]
+        return sv.spec_verify(s["target"], s["draft"], s["tokens"], s["u_accept"], s["u_sample"],
+                              cfg.temperature, cfg.top_k, workspace=ws, stream=stream,
+                              out=(acc, out), events=events)
+
+    K = args.steps
+    wall, gpu_ms, per_kernel, wall2 = time_loop(call, plan, K, args.warmup, stream, dev, hev,
+                                                not args.no_stage_events)
+    # emitted tokens for the last call of each set (accepted + 1 per valid sequence)
+    emitted = torch.zeros((), dtype=torch.int64, device=dev)
+    for s_i in range(min(n_sets, K)):
+        call(s_i)
+        emitted += (acc.clamp(min=-1) + 1).sum()
+    torch.cuda.synchronize(dev)
+    mean_emitted = float(emitted.item()) / min(n_sets, K)
+
+    ms = wall * 1e3 / K
+    t_call = ms / 1e3
+    kernel = "k_argmax" if greedy else KERNEL  # the kernel that streams the logits
+    traffic, tnote = counters_traffic(source_sha()) if args.config == 3 else (None, "counters are taken on workload 3")
+    res = {
+        "metric": METRIC, "value": round(B * G / t_call, 1), "unit": "positions/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": cfg.name, "B": B, "G": G, "V": V, "logits": cfg.dtype,
+                   "temperature": cfg.temperature, "top_k": cfg.top_k, "input_sets": n_sets,
+                   "set_bytes": alg_bytes},
+        "call_GBs": round(alg_bytes / t_call / 1e9, 1),
+        "call_frac_of_peak": round(alg_bytes / t_call / 1e9 / PEAK_HBM_GBS, 4),
+        "emitted_tokens_per_s": round(mean_emitted / t_call, 1),
+        "mean_accepted_plus_one": round(mean_emitted / B, 4),
+        "gpu_event_ms_per_step": round(gpu_ms / K, 5),
+        "per_kernel_us": {k: round(v, 3) for k, v in per_kernel.items()},
+        "ms_per_step_with_kernel_events": None if wall2 is None else round(wall2 * 1e3 / K, 5),
+        "roofline": roofline(per_kernel, kernel, alg_bytes, traffic),
+        "traffic_note": tnote,
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] oracle CPU baseline (~{args.cpu_seconds:.0f} s)")
+        res["cpu_baseline"] = cpu_baseline(host, cfg, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    return res
+
+
+def run_sample(args, dev, hev):
+    """The batched sampler on one decode step of B rows: tokens drawn per second."""
+    import torch
+    import rejection_sampling_verify_02_amd as sv
+    from rejection_sampling_verify_02_amd import workloads as wl
+
+    cfg = wl.SAMPLE_CONFIGS["sample_bf16_b256"]
+    B, V = cfg.B, cfg.V
+    esz = 2 if cfg.dtype == "bf16" else 4
+    alg_bytes = B * V * esz
+    n_sets = args.sets or max(2, -(-(1 << 30) // alg_bytes))
+    log(f"[bench] sampler {cfg.name}: B={B} V={V} {cfg.dtype}, {alg_bytes / 1e6:.2f} MB per call, {n_sets} sets")
+    sets, host = [], []
+    for s in range(n_sets):
+        z, u = wl.make_sample(B, V, cfg.dtype, cfg.seed + 1000 * s)
+        t = torch.from_numpy(z)
+        sets.append((t.view(torch.bfloat16).to(dev) if z.dtype == np.uint16 else t.to(dev),
+                     torch.from_numpy(u).to(dev)))
+        host.append((z, u))
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    dtc = sv.SV_BF16 if cfg.dtype == "bf16" else sv.SV_F32
+    plan = sv.sv_launch_plan(B, 0, V, dtc, cfg.temperature, cfg.top_k)
+    ws = sv.Workspace()
+    tok = torch.empty((B,), dtype=torch.int32, device=dev)
+    st = torch.empty((B,), dtype=torch.int32, device=dev)
+
+    def call(i, events=None):
+        z, u = sets[i % n_sets]
+        return sv.spec_sample(z, u, cfg.temperature, cfg.top_k, workspace=ws, stream=stream,
+                              out=(tok, st), events=events)
+
+    K = args.steps
+    wall, gpu_ms, per_kernel, wall2 = time_loop(call, plan, K, args.warmup, stream, dev, hev,
+                                                not args.no_stage_events)
+    t_call = wall / K
+    res = {
+        "metric": "sampled tokens/sec and achieved HBM GB/s (% of peak), one draw per row",
+        "value": round(B / t_call, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(t_call * 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": cfg.name, "B": B, "V": V, "logits": cfg.dtype, "temperature": cfg.temperature,
+                   "top_k": cfg.top_k, "input_sets": n_sets, "set_bytes": alg_bytes},
+        "call_GBs": round(alg_bytes / t_call / 1e9, 1),
+        "call_frac_of_peak": round(alg_bytes / t_call / 1e9 / PEAK_HBM_GBS, 4),
+        "gpu_event_ms_per_step": round(gpu_ms / K, 5),
+        "per_kernel_us": {k: round(v, 3) for k, v in per_kernel.items()},
+        "ms_per_step_with_kernel_events": None if wall2 is None else round(wall2 * 1e3 / K, 5),
+        "roofline": roofline(per_kernel, KERNEL, alg_bytes, None),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle._load()
+        threads = oracle.default_threads()
+        calls, t0 = 0, time.perf_counter()
+        while True:
+            z, u = host[calls % len(host)]
+            oracle.sample_rows(z, u, cfg.temperature, cfg.top_k, nthreads=threads)
+            calls += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds:
+                break
+        res["cpu_baseline"] = {"value": B * calls / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                               "sample": f"{calls} full calls (B={B}, V={V}) over {min(calls, len(host))} "
+                                         f"input sets, {el:.1f} s"}
+    else:
+        res["cpu_baseline"] = None
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--op", default="verify", choices=["verify", "sample"],
+                    help="verify (the default, the headline) or the batched sampler")
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5],
-                    help="workload (3, the default, is the headline; 4 greedy and 5 top-k are timed "
-                         "for the design notes)")
+                    help="verification workload (3, the default, is the headline; 4 greedy and 5 top-k "
+                         "are timed for the design notes)")
     ap.add_argument("--sets", type=int, default=0, help="input sets to rotate (default: >= 1 GiB)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -260,122 +459,11 @@ def main() -> int:
 
     import torch
     import rejection_sampling_verify_02_amd as sv
-    from rejection_sampling_verify_02_amd import workloads as wl
 
     sv.load_library()  # raises if the HIP library is not built
     dev = torch.device("cuda:0")
-    cfg = wl.CONFIGS[args.config]
-    B, G, V = cfg.B, cfg.G, cfg.V
-    esz = 2 if cfg.dtype == "bf16" else 4
-    greedy = cfg.temperature == 0
-    rows = B * (G + 1) if greedy else B * (2 * G + 1)  # greedy reads no draft row
-    alg_bytes = rows * V * esz  # one read of every logit the result depends on
-    n_sets = args.sets or max(2, -(-(1 << 30) // alg_bytes))
-    log(f"[bench] workload {cfg.name}: B={B} G={G} V={V} {cfg.dtype}, {alg_bytes / 1e6:.2f} MB per call, "
-        f"{n_sets} input sets")
-    sets, host = make_sets(args.config, n_sets, dev)
-
-    stream = torch.cuda.current_stream(dev).cuda_stream
-    dtc = sv.SV_BF16 if cfg.dtype == "bf16" else sv.SV_F32
-    plan = sv.sv_launch_plan(B, G, V, dtc, cfg.temperature, cfg.top_k)
-    nl = len(plan)
-    ws = sv.Workspace()
-    acc = torch.empty((B,), dtype=torch.int32, device=dev)
-    out = torch.empty((B, G + 1), dtype=torch.int32, device=dev)
     hev = HipEvents()
-
-    def call(i, events=None):
-        s = sets[i % n_sets]
-        return sv.spec_verify(s["target"], s["draft"], s["tokens"], s["u_accept"], s["u_sample"],
-                              cfg.temperature, cfg.top_k, workspace=ws, stream=stream,
-                              out=(acc, out), events=events)
-
-    for i in range(args.warmup):
-        call(i)
-    torch.cuda.synchronize(dev)
-    log(f"[bench] warmup done ({args.warmup} calls)")
-
-    K = args.steps
-    # Timed region 1: K steps exactly as a caller runs them -> value, ms_per_step.
-    loop_ev = hev.create(2)
-    torch.cuda.synchronize(dev)
-    t0 = time.perf_counter()
-    hev.record(loop_ev[0], stream)
-    for i in range(K):
-        call(args.warmup + i)
-    hev.record(loop_ev[1], stream)
-    torch.cuda.synchronize(dev)
-    wall = time.perf_counter() - t0
-    gpu_ms = hev.elapsed_ms(loop_ev[0], loop_ev[1])
-    log(f"[bench] timed {K} calls: wall {wall * 1e3:.2f} ms, events {gpu_ms:.2f} ms")
-
-    # Timed region 2: the same K steps with a (start, stop) event pair attached to every
-    # kernel dispatch (hipExtLaunchKernel) -> each kernel's average duration.  The pairs
-    # add a few microseconds of gap between kernels, so region 1 gives the throughput.
-    per_kernel = {}
-    wall2 = None
-    if not args.no_stage_events:
-        stage = [hev.create(2 * nl) for _ in range(K)]
-        torch.cuda.synchronize(dev)
-        t1 = time.perf_counter()
-        for i in range(K):
-            call(args.warmup + i, stage[i])
-        torch.cuda.synchronize(dev)
-        wall2 = time.perf_counter() - t1
-        durs = np.array([[hev.elapsed_ms(ev[2 * j], ev[2 * j + 1]) for j in range(nl)] for ev in stage])
-        for j, name in enumerate(plan):
-            per_kernel[f"{j}:{name}"] = float(np.mean(durs[:, j]) * 1e3)
-        for ev in stage:
-            hev.destroy(ev)
-        log(f"[bench] timed {K} calls with per-kernel events: wall {wall2 * 1e3:.2f} ms")
-    hev.destroy(loop_ev)
-
-    # emitted tokens for the last call of each set (accepted + 1 per valid sequence)
-    emitted = torch.zeros((), dtype=torch.int64, device=dev)
-    for s_i in range(min(n_sets, K)):
-        call(s_i)
-        emitted += (acc.clamp(min=-1) + 1).sum()
-    torch.cuda.synchronize(dev)
-    mean_emitted = float(emitted.item()) / min(n_sets, K)
-
-    ms = wall * 1e3 / K
-    t_call = ms / 1e3
-    positions = B * G
-    value = positions / t_call
-    # the kernel that streams the logits: k_argmax at temperature 0, k_verify otherwise
-    kernel = "k_argmax" if greedy else KERNEL
-    main_us = next((v for k, v in per_kernel.items() if k.endswith(":" + kernel)), None)
-    sha = hashlib.sha256(SOURCE.read_bytes()).hexdigest()
-    traffic, tnote = counters_traffic(sha) if args.config == 3 else (None, "counters are taken on workload 3")
-    roof = None
-    if main_us:
-        achieved = alg_bytes / (main_us * 1e-6) / 1e9
-        roof = {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": traffic, "algorithmic_bytes": alg_bytes,
-                "avg_launch_us": round(main_us, 3)}
-    res = {
-        "metric": METRIC, "value": round(value, 1), "unit": "positions/s", "n_gpus": 1, "steps": K,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": cfg.name, "B": B, "G": G, "V": V, "logits": cfg.dtype,
-                   "temperature": cfg.temperature, "top_k": cfg.top_k, "input_sets": n_sets,
-                   "set_bytes": alg_bytes},
-        "call_GBs": round(alg_bytes / t_call / 1e9, 1),
-        "call_frac_of_peak": round(alg_bytes / t_call / 1e9 / PEAK_HBM_GBS, 4),
-        "emitted_tokens_per_s": round(mean_emitted / t_call, 1),
-        "mean_accepted_plus_one": round(mean_emitted / B, 4),
-        "gpu_event_ms_per_step": round(gpu_ms / K, 5),
-        "per_kernel_us": {k: round(v, 3) for k, v in per_kernel.items()},
-        "ms_per_step_with_kernel_events": None if wall2 is None else round(wall2 * 1e3 / K, 5),
-        "roofline": roof,
-        "traffic_note": tnote,
-    }
-    if not args.no_cpu_baseline:
-        log(f"[bench] oracle CPU baseline (~{args.cpu_seconds:.0f} s)")
-        res["cpu_baseline"] = cpu_baseline(host, cfg, args.cpu_seconds)
-    else:
-        res["cpu_baseline"] = None
+    res = run_sample(args, dev, hev) if args.op == "sample" else run_verify(args, dev, hev)
     print(json.dumps(res), flush=True)
     return 0
 

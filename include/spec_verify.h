@@ -135,6 +135,37 @@ sv_status spec_verify_timed(const void *target_logits, const void *draft_logits,
 const char *sv_launch_plan(int32_t B, int32_t G, int32_t V, sv_dtype dtype, float temperature,
                            int32_t top_k);
 
+/* ---- batched sampler (the step before verification, and plain decoding) ----
+ *
+ * One draw per row from the row's own distribution ("Speculative Decoding 的朴素思想",
+ * section "一次 sampling 怎么执行", step 1: a uniform picks the token whose cumulative
+ * interval holds it; this is the draft's own draw X ~ q, and plain decoding from p).
+ * Row b's logits pass through the same policy as in spec_verify (temperature T, optional
+ * top-k); tokens[b] is the first v, in index order, whose cumulative probability exceeds
+ * u[b] times the total.  T == 0 takes the lowest-index argmax and reads no uniform.
+ *   logits      [B, V] dtype
+ *   u           [B] float32 in [0,1); may be NULL when temperature == 0
+ *   tokens      [B] int32 out: the drawn token, or -1 when the row has a code
+ *   row_status  [B] int32 out: 0, or SV_ROW_BAD_LOGITS (a NaN or +inf logit, or no finite
+ *               kept logit), SV_ROW_BAD_UNIFORM (T > 0 and u[b] outside [0,1)), or
+ *               SV_ROW_INTERNAL
+ *   workspace   at least sv_workspace_bytes(B, 0, V, dtype, temperature, top_k) bytes,
+ *               256-byte aligned, first sv_workspace_zero_bytes(B, 0, V, ...) bytes zero
+ *               (the same rules as spec_verify's workspace).
+ * The draw is spec_verify's bonus draw with G = 0 (p_1 = the row): the same kernels and
+ * argument checks; statuses as for spec_verify. */
+sv_status spec_sample(const void *logits, sv_dtype dtype, const float *u, int32_t B, int32_t V,
+                      float temperature, int32_t top_k, int32_t *tokens, int32_t *row_status,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* spec_sample with each kernel dispatch bracketed by caller-owned HIP events, as in
+ * spec_verify_timed. */
+sv_status spec_sample_timed(const void *logits, sv_dtype dtype, const float *u, int32_t B,
+                            int32_t V, float temperature, int32_t top_k, int32_t *tokens,
+                            int32_t *row_status, void *workspace, size_t workspace_bytes,
+                            void *stream, void *const *events, int32_t n_events,
+                            int32_t *n_launched);
+
 /* Human-readable text of a status (static storage). */
 const char *sv_status_string(sv_status status);
 

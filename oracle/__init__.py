@@ -16,7 +16,8 @@ arrays into it.  The functions and the passages they follow:
 * ``policy_rows`` -- logits to distribution with temperature and top-k
   (first page, section "从 LM head 到 sampling distribution").
 * ``invcdf`` / ``sample_rows`` -- the draw by cumulative intervals (first page,
-  section "一次 sampling 怎么执行", step 1).
+  section "一次 sampling 怎么执行", step 1); ``sample_rows`` is also the oracle of the
+  library's batched sampler ``spec_sample``.
 * ``topk_threshold_rows`` / ``argmax_rows`` -- the top-k cut and greedy choice.
 
 Every function is pinned by tests in ``tests/test_oracle_*.py`` against values
@@ -64,7 +65,7 @@ def _bind(lib):
     lib.ref_spec_verify.restype = i32
     lib.ref_policy_rows.argtypes = [P, i32, i32, i32, f64, i32, P, P]
     lib.ref_policy_rows.restype = i32
-    lib.ref_sample_rows.argtypes = [P, i32, i32, i32, f64, i32, P, P, i32]
+    lib.ref_sample_rows.argtypes = [P, i32, i32, i32, f64, i32, P, P, P, P, i32]
     lib.ref_sample_rows.restype = i32
     lib.ref_topk_threshold_rows.argtypes = [P, i32, i32, i32, i32, P]
     lib.ref_topk_threshold_rows.restype = i32
@@ -167,17 +168,25 @@ def policy_rows(logits, temperature, top_k=0):
     return P.reshape(z.shape), L.reshape(z.shape[:-1])
 
 
-def sample_rows(logits, u, temperature, top_k=0, nthreads=None):
-    """One token per row drawn from the row's policy by inverse CDF with uniform u."""
+def sample_rows(logits, u, temperature, top_k=0, nthreads=None, *, with_status=False):
+    """One token per row drawn from the row's policy by inverse CDF with uniform u.
+
+    With ``with_status`` also returns each row's status (0, -3 invalid row, -4 uniform
+    outside [0,1)) and the draw's boundary distance."""
     lib = _load()
     z, dt = _logits(logits)
     V = z.shape[-1]
     R = z.size // V
-    u = np.ascontiguousarray(u, np.float32).reshape(R)
+    u = np.zeros((R,), np.float32) if u is None else np.ascontiguousarray(u, np.float32).reshape(R)
     tok = np.empty((R,), np.int32)
+    st = np.empty((R,), np.int32)
+    mg = np.empty((R,), np.float64)
     lib.ref_sample_rows(_ptr(z), dt, R, V, float(temperature), int(top_k), _ptr(u), _ptr(tok),
-                        int(nthreads or default_threads()))
-    return tok.reshape(z.shape[:-1])
+                        _ptr(st), _ptr(mg), int(nthreads or default_threads()))
+    shp = z.shape[:-1]
+    if with_status:
+        return tok.reshape(shp), st.reshape(shp), mg.reshape(shp)
+    return tok.reshape(shp)
 
 
 def topk_threshold_rows(logits, top_k):

@@ -368,10 +368,14 @@ int ref_policy_rows(const void *logits, int dtype, int R, int V, double temperat
 }
 
 /* Draw one token per row from the row's policy with the given uniform, by the same
- * inverse CDF ([WY] step 1: the draft's own draw X ~ q).  T == 0 gives the argmax.
- * Invalid rows give -1. */
+ * inverse CDF ([WY] step 1: the draft's own draw X ~ q; the same draw is plain decoding
+ * from p).  T == 0 gives the lowest-index argmax and reads no uniform.  Invalid rows
+ * give -1 with status -3; with T > 0, a uniform outside [0,1) gives -1 with status -4
+ * (the row is checked first, as in the chain).  status and margin (the draw's boundary
+ * distance, 0 when none applies) may be NULL. */
 int ref_sample_rows(const void *logits, int dtype, int R, int V, double temperature, int top_k,
-                    const float *u, int32_t *tokens, int nthreads) {
+                    const float *u, int32_t *tokens, int32_t *status, double *margin,
+                    int nthreads) {
   if (R < 0 || V < 1 || !(temperature >= 0.0)) return -1;
   if (nthreads < 1) nthreads = 1;
 #pragma omp parallel num_threads(nthreads)
@@ -380,15 +384,22 @@ int ref_sample_rows(const void *logits, int dtype, int R, int V, double temperat
     double *P = (double *)malloc(sizeof(double) * (size_t)V);
 #pragma omp for schedule(dynamic, 4)
     for (int r = 0; r < R; ++r) {
+      int32_t tok = -1, st = 0;
+      double d = 0.0;
       load_row(logits, dtype, (size_t)r, V, z);
       if (!row_is_valid(z, V)) {
-        tokens[r] = -1;
+        st = -3;
       } else if (temperature == 0.0) {
-        tokens[r] = argmax_lowest(z, V);
+        tok = argmax_lowest(z, V);
+      } else if (!(u[r] >= 0.0f && u[r] < 1.0f)) {
+        st = -4;
       } else {
         policy(z, V, temperature, top_k, NULL, P);
-        tokens[r] = ref_invcdf(P, V, (double)u[r], NULL);
+        tok = ref_invcdf(P, V, (double)u[r], &d);
       }
+      tokens[r] = tok;
+      if (status) status[r] = st;
+      if (margin) margin[r] = d;
     }
     free(z);
     free(P);

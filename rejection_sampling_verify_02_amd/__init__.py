@@ -26,7 +26,7 @@ _STATUS = {0: "SV_OK", 1: "SV_ERR_NULL", 2: "SV_ERR_SHAPE", 3: "SV_ERR_DTYPE",
            4: "SV_ERR_TEMPERATURE", 5: "SV_ERR_WORKSPACE", 6: "SV_ERR_ALIGN", 7: "SV_ERR_LAUNCH"}
 
 EXPORTED = ("spec_verify", "spec_verify_timed", "sv_workspace_bytes", "sv_workspace_zero_bytes",
-            "sv_status_string", "sv_launch_plan")
+            "sv_status_string", "sv_launch_plan", "spec_sample", "spec_sample_timed")
 
 
 class SpecVerifyError(RuntimeError):
@@ -53,6 +53,11 @@ def load_library(path: Path | str | None = None) -> ctypes.CDLL:
     lib.spec_verify.restype = I32
     lib.spec_verify_timed.argtypes = common + [V, I32, V]
     lib.spec_verify_timed.restype = I32
+    smp = [V, I32, V, I32, I32, F32, I32, V, V, V, SZ, V]
+    lib.spec_sample.argtypes = smp
+    lib.spec_sample.restype = I32
+    lib.spec_sample_timed.argtypes = smp + [V, I32, V]
+    lib.spec_sample_timed.restype = I32
     lib.sv_workspace_bytes.argtypes = [I32, I32, I32, I32, F32, I32]
     lib.sv_workspace_bytes.restype = SZ
     lib.sv_workspace_zero_bytes.argtypes = [I32, I32, I32, I32, F32, I32]
@@ -217,3 +222,51 @@ def spec_verify(target_logits, draft_logits, draft_tokens, u_accept, u_sample, t
     wso.called(dev, zbytes)
     res = (acc, toks) + ((stats,) if row_stats else ())
     return res + ((nl,) if events is not None else ())
+
+
+def spec_sample(logits, u, temperature: float, top_k: int = 0, *, workspace: Workspace | None = None,
+                stream=None, out=None, events=None):
+    """Batched sampling on the GPU (see include/spec_verify.h): one token per row of
+    logits [B, V] (bfloat16 or float32) drawn by inverse CDF with u [B] float32 (None at
+    temperature 0).  Returns (tokens [B], row_status [B]) int32 tensors; ``out`` may supply
+    them.  ``events`` as for spec_verify."""
+    import torch
+    lib = load_library()
+    dev = logits.device
+    if dev.type != "cuda":
+        raise ValueError("logits must be a device tensor")
+    dt = _dtype_code(logits)
+    if logits.dim() != 2:
+        raise ValueError("logits must be [B, V]")
+    B, V = logits.shape
+    _check(logits, "logits", (B, V), logits.dtype, dev)
+    greedy = float(temperature) == 0.0
+    if greedy:
+        u = None
+    else:
+        _check(u, "u", (B,), torch.float32, dev)
+    if out is not None:
+        tok, st = out
+    else:
+        tok = torch.empty((B,), dtype=torch.int32, device=dev)
+        st = torch.empty((B,), dtype=torch.int32, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    nbytes = int(lib.sv_workspace_bytes(B, 0, V, dt, float(temperature), int(top_k)))
+    zbytes = int(lib.sv_workspace_zero_bytes(B, 0, V, dt, float(temperature), int(top_k)))
+    wso = workspace or _default_ws
+    ws = wso.get(nbytes, zbytes, dev, stream)
+    args = [_ptr(logits), dt, _ptr(u), B, V, float(temperature), int(top_k), _ptr(tok), _ptr(st),
+            _ptr(ws), ws.numel(), ctypes.c_void_p(stream)]
+    if events is None:
+        rc = lib.spec_sample(*args)
+        nl = None
+    else:
+        arr = (ctypes.c_void_p * len(events))(*events)
+        n = ctypes.c_int32(0)
+        rc = lib.spec_sample_timed(*args, arr, len(events), ctypes.byref(n))
+        nl = n.value
+    if rc != 0:
+        raise SpecVerifyError(rc, sv_status_string(rc))
+    wso.called(dev, zbytes)
+    return (tok, st) if events is None else (tok, st, nl)

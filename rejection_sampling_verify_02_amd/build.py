@@ -1,4 +1,5 @@
-"""Build the gfx950 library in-tree: ``libspec_verify.so`` next to this file.
+"""Build the gfx950 library in-tree: ``libspec_verify.so`` next to this file, from every
+HIP source under ``csrc/``.
 
     python -m rejection_sampling_verify_02_amd.build
 
@@ -15,7 +16,8 @@ from pathlib import Path
 
 PKG = Path(__file__).resolve().parent
 ROOT = PKG.parent
-SRC = PKG / "csrc" / "spec_verify.hip"
+CSRC = PKG / "csrc"
+SRCS = sorted(CSRC.glob("*.hip"))  # every kernel source, one library
 LIB = PKG / "libspec_verify.so"
 ARCH = os.environ.get("SV_OFFLOAD_ARCH", "gfx950")
 
@@ -25,8 +27,8 @@ def hipcc_command(out: Path) -> list[str]:
         "/opt/rocm/bin/hipcc", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wall", "-Wno-unused-function",
-        "-I", str(ROOT / "include"),
-        "-o", str(out), str(SRC),
+        "-I", str(ROOT / "include"), "-I", str(CSRC),
+        "-o", str(out), *[str(p) for p in SRCS],
     ]
 
 

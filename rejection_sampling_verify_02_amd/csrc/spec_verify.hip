@@ -25,7 +25,9 @@
 //                 items follow: for a rejection at j, the masses of [p_j - q_j]_+ per
 //                 64-vector segment of both rows at j; the last draw item picks segment,
 //                 lane and element where the cumulative mass passes u*Z.  For a bonus, the
-//                 chunk of p_G picked from the partials re-reads itself.
+//                 chunk of p_G picked from the partials re-reads itself.  With no drafts
+//                 (G = 0: the batched sampler) no draw items are launched: the row's chunks
+//                 publish masses per segment and the finisher draws, re-reading one segment.
 //   k_argmax      greedy (T == 0): per-chunk argmax, row combine and scan, one launch.
 //
 // Workgroups hand results to one another as tagged 64-bit words (the call's tag in the
@@ -42,24 +44,13 @@
 #include <atomic>
 
 #include "spec_verify.h"
-
-#define SVD __device__ __forceinline__
+#include "sv_device.h"
 
 namespace sv {
 
-constexpr int NT = 256;                // threads per workgroup
-constexpr int WAVE = 64;               // gfx950 wavefront
-constexpr int NW = NT / WAVE;          // waves per workgroup
-constexpr int VPT = 8;                 // 16-byte vectors per thread per chunk
-constexpr int CHUNK_VECS = NT * VPT;   // vectors per chunk (32 KiB of logits)
-constexpr int SEGS = VPT * NW;         // 64-vector segments per chunk
 constexpr int NSUB = 4;                // second-pass workgroups per chunk of a rejected pair
 constexpr int KSUB = VPT / NSUB;       // vectors per thread of each of them
-constexpr unsigned SPIN_LIMIT = 1u << 20;  // polls before a waiting wave gives up (~a second)
-constexpr double LN2 = 0.69314718055994530942;
-constexpr double LOG2E = 1.44269504088896340736;
-
-enum : int { JOB_NONE = 0, JOB_REJECT = 1, JOB_BONUS = 2 };  // NONE: a row error, nothing to draw
+enum : int { JOB_NONE = 0, JOB_REJECT = 1, JOB_BONUS = 2 };  // NONE: nothing to draw (a row error, or G = 0)
 
 // The acceptance scan's record for the draw of one sequence: JW tagged words, field f
 // in word f (ints as their bits, floats as theirs; a double as a float head and tail).
@@ -71,127 +62,7 @@ enum : int {
   JW_USED, JW = 16
 };
 
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-
-// ---------------------------------------------------------------- element formats
-
-template <typename T>
-struct Fmt;
-
-template <>
-struct Fmt<uint16_t> {  // bf16 bit patterns: the upper half of an IEEE binary32
-  static constexpr int VEC = 8;
-  SVD static float at(const uint16_t *p, size_t i) { return __uint_as_float((uint32_t)p[i] << 16); }
-  SVD static void unpack(u32x4 w, float (&o)[8]) {
-    o[0] = __uint_as_float(w.x << 16);
-    o[1] = __uint_as_float(w.x & 0xffff0000u);
-    o[2] = __uint_as_float(w.y << 16);
-    o[3] = __uint_as_float(w.y & 0xffff0000u);
-    o[4] = __uint_as_float(w.z << 16);
-    o[5] = __uint_as_float(w.z & 0xffff0000u);
-    o[6] = __uint_as_float(w.w << 16);
-    o[7] = __uint_as_float(w.w & 0xffff0000u);
-  }
-};
-
-template <>
-struct Fmt<float> {
-  static constexpr int VEC = 4;
-  SVD static float at(const float *p, size_t i) { return p[i]; }
-  SVD static void unpack(u32x4 w, float (&o)[4]) {
-    o[0] = __uint_as_float(w.x);
-    o[1] = __uint_as_float(w.y);
-    o[2] = __uint_as_float(w.z);
-    o[3] = __uint_as_float(w.w);
-  }
-};
-
-// Vector k of this thread in chunk c is vector c*CHUNK_VECS + k*NT + tid of the row, so
-// one wave's k-th load covers 64 consecutive vectors (a "segment") and segments are in
-// vocabulary order (k-major, then wave).  Elements past the row end read as -inf.
-// Every load is issued before any is used: past the end a load re-reads the row's last
-// vector (or element), and the tail is masked afterwards by a uniform branch.
-template <typename T, bool ALIGNED, bool STREAM>
-SVD void load_chunk(const T *row, int V, int nvec, int c, int tid, float (&x)[VPT][Fmt<T>::VEC]) {
-  constexpr int VEC = Fmt<T>::VEC;
-  if (ALIGNED) {
-    u32x4 w[VPT];
-    const u32x4 *rv = reinterpret_cast<const u32x4 *>(row);
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-      const int v = c * CHUNK_VECS + k * NT + tid;
-      const u32x4 *p = rv + (v < nvec ? v : nvec - 1);
-      w[k] = STREAM ? __builtin_nontemporal_load(p) : *p;
-    }
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) Fmt<T>::unpack(w[k], x[k]);
-    if ((c + 1) * CHUNK_VECS > nvec) {
-#pragma unroll
-      for (int k = 0; k < VPT; ++k) {
-        const bool in = c * CHUNK_VECS + k * NT + tid < nvec;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) x[k][e] = in ? x[k][e] : -INFINITY;
-      }
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < VPT; ++k)
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const long idx = ((long)c * CHUNK_VECS + (long)k * NT + tid) * VEC + e;
-        const bool in = idx < V;
-        const float z = Fmt<T>::at(row, (size_t)(in ? idx : (long)V - 1));
-        x[k][e] = in ? z : -INFINITY;
-      }
-  }
-}
-
-// Vectors k0..k0+NK-1 of this thread in chunk c, as load_chunk does for all VPT of them.
-template <typename T, bool ALIGNED, bool STREAM, int NK>
-SVD void load_vectors(const T *row, int V, int nvec, int c, int k0, int tid,
-                      float (&x)[NK][Fmt<T>::VEC]) {
-  constexpr int VEC = Fmt<T>::VEC;
-  if (ALIGNED) {
-    u32x4 w[NK];
-    const u32x4 *rv = reinterpret_cast<const u32x4 *>(row);
-#pragma unroll
-    for (int k = 0; k < NK; ++k) {
-      const int v = c * CHUNK_VECS + (k0 + k) * NT + tid;
-      const u32x4 *p = rv + (v < nvec ? v : nvec - 1);
-      w[k] = STREAM ? __builtin_nontemporal_load(p) : *p;
-    }
-#pragma unroll
-    for (int k = 0; k < NK; ++k) Fmt<T>::unpack(w[k], x[k]);
-    if ((c + 1) * CHUNK_VECS > nvec) {
-#pragma unroll
-      for (int k = 0; k < NK; ++k) {
-        const bool in = c * CHUNK_VECS + (k0 + k) * NT + tid < nvec;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) x[k][e] = in ? x[k][e] : -INFINITY;
-      }
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < NK; ++k)
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const long idx = ((long)c * CHUNK_VECS + (long)(k0 + k) * NT + tid) * VEC + e;
-        const bool in = idx < V;
-        const float z = Fmt<T>::at(row, (size_t)(in ? idx : (long)V - 1));
-        x[k][e] = in ? z : -INFINITY;
-      }
-  }
-}
-
-// Index of element (k, e) of this thread in chunk c.
-template <typename T>
-SVD long elem_index(int c, int k, int tid, int e) {
-  return ((long)c * CHUNK_VECS + (long)k * NT + tid) * Fmt<T>::VEC + e;
-}
-
 // ---------------------------------------------------------------- arguments
-
-typedef unsigned long long u64;
 
 struct Work {                  // carved from the caller's workspace
   // tagged words (see tw_put)
@@ -200,6 +71,7 @@ struct Work {                  // carved from the caller's workspace
   u64 *tw_zx;                  // [R] the row's logit at its position's drafted token
   u64 *tw_job;                 // [B*JW] the acceptance scan's record for the draw
   u64 *tw_seg;                 // [B*C*SEGS*2] residual mass per 64-vector segment (head, tail)
+  u64 *tw_gseg;                // [B*C*SEGS*2] the bonus row's mass per segment (head, tail)
   u64 *tw_hist;                // [R*C*128] top-k digit histogram per chunk (16-bit counts)
   // plain, handed from one kernel to the next
   float *row_tau;              // [R] top-k threshold (raw logit)
@@ -225,331 +97,6 @@ template <typename T>
 SVD const T *seq_row(const Args &a, int b, int j) {
   if (j <= a.G) return static_cast<const T *>(a.target) + ((size_t)b * (a.G + 1) + j) * (size_t)a.V;
   return static_cast<const T *>(a.draft) + ((size_t)b * a.G + (j - a.G - 1)) * (size_t)a.V;
-}
-
-// ---------------------------------------------------------------- small helpers
-
-SVD float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }  // v_exp_f32; 0 for x < -126
-SVD int lane_id() { return (int)(threadIdx.x & (WAVE - 1)); }
-
-// This wave's LDS writes are complete before any of its lanes reads them.  Only the LDS
-// counter is waited for: outstanding global stores (published results) keep going.
-SVD void lds_sync() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt left at their maxima
-  __builtin_amdgcn_wave_barrier();
-}
-
-// (off, s) pairs stand for s * 2^off; combining keeps the larger offset.  Parts that
-// hold only -inf have off = -inf and s = 0 (or NaN when a NaN was seen); the rule never
-// forms (-inf) - (-inf).  The combine is commutative bit for bit.
-SVD void lse_combine(float &off, double &s, float off2, double s2) {
-  const float mx = fmaxf(off, off2);
-  const double w1 = (off == mx) ? 1.0 : (double)fast_exp2(off - mx);
-  const double w2 = (off2 == mx) ? 1.0 : (double)fast_exp2(off2 - mx);
-  s = s * w1 + s2 * w2;
-  off = mx;
-}
-
-// ---- cross-lane primitives (DPP) ----
-// Wave-wide scans and reductions use DPP lane moves (row_shr within 16-lane rows, then
-// row_bcast:15 / row_bcast:31 across rows) instead of LDS-routed shuffles: each step is
-// one VALU move.  A move leaves `id` in lanes that have no source, so every scan below
-// is an inclusive scan with identity id; a reduction is the scan's lane 63 read back.
-template <int CTRL, int ROWM>
-SVD unsigned dpp_u(unsigned v, unsigned id) {
-  return (unsigned)__builtin_amdgcn_update_dpp((int)id, (int)v, CTRL, ROWM, 0xf, false);
-}
-template <int CTRL, int ROWM>
-SVD float dpp_f(float v, float id) { return __uint_as_float(dpp_u<CTRL, ROWM>(__float_as_uint(v), __float_as_uint(id))); }
-template <int CTRL, int ROWM>
-SVD double dpp_d(double v, double id) {
-  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
-  const unsigned long long ib = (unsigned long long)__double_as_longlong(id);
-  const unsigned lo = dpp_u<CTRL, ROWM>((unsigned)b, (unsigned)ib);
-  const unsigned hi = dpp_u<CTRL, ROWM>((unsigned)(b >> 32), (unsigned)(ib >> 32));
-  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
-}
-template <int CTRL, int ROWM>
-SVD int dpp_i(int v, int id) { return (int)dpp_u<CTRL, ROWM>((unsigned)v, (unsigned)id); }
-
-// The six steps of a 64-lane inclusive scan; STEP(ctrl, rowmask) applies one lane move.
-#define SV_SCAN_STEPS(STEP) \
-  STEP(0x111, 0xf) /* row_shr:1 */ \
-  STEP(0x112, 0xf) /* row_shr:2 */ \
-  STEP(0x114, 0xf) /* row_shr:4 */ \
-  STEP(0x118, 0xf) /* row_shr:8 */ \
-  STEP(0x142, 0xa) /* row_bcast:15 into rows 1 and 3 */ \
-  STEP(0x143, 0xc) /* row_bcast:31 into rows 2 and 3 */
-
-SVD double scan_sum(double x) {
-#define STEP(C, R) x += dpp_d<C, R>(x, 0.0);
-  SV_SCAN_STEPS(STEP)
-#undef STEP
-  return x;
-}
-SVD float scan_max(float x) {
-#define STEP(C, R) x = fmaxf(x, dpp_f<C, R>(x, -INFINITY));
-  SV_SCAN_STEPS(STEP)
-#undef STEP
-  return x;
-}
-SVD unsigned scan_or(unsigned x) {
-#define STEP(C, R) x |= dpp_u<C, R>(x, 0u);
-  SV_SCAN_STEPS(STEP)
-#undef STEP
-  return x;
-}
-
-SVD double readlane_d(double v, int l) {
-  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
-  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)b, l);
-  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(b >> 32), l);
-  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
-}
-SVD float readlane_f(float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); }
-
-SVD double wave_sum(double v) { return readlane_d(scan_sum(v), WAVE - 1); }
-SVD float wave_max(float v) { return readlane_f(scan_max(v), WAVE - 1); }
-SVD unsigned wave_or(unsigned v) { return (unsigned)__builtin_amdgcn_readlane((int)scan_or(v), WAVE - 1); }
-
-// (off, s) pairs over the wave, combined with lse_combine (identity (-inf, 0)).
-SVD void wave_lse(float &off, double &s) {
-#define STEP(C, R)                                  \
-  {                                                 \
-    const float o2 = dpp_f<C, R>(off, -INFINITY);   \
-    const double s2 = dpp_d<C, R>(s, 0.0);          \
-    lse_combine(off, s, o2, s2);                    \
-  }
-  SV_SCAN_STEPS(STEP)
-#undef STEP
-  off = readlane_f(off, WAVE - 1);
-  s = readlane_d(s, WAVE - 1);
-}
-
-// Results that one workgroup hands to another inside a kernel are written and read with
-// device-scope (agent) atomic stores and loads: on gfx950 these are ordinary vector
-// memory instructions with the device scope bit set, so they are complete device-wide
-// (across the XCDs' separate L2s) when the store counter drains, and the loads observe
-// them.  This avoids the whole-L2 write-back that a device-scope release fence costs.
-template <typename T>
-SVD void st_dev(T *p, T v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-template <typename T>
-SVD T ld_dev(const T *p) {
-  return __hip_atomic_load(const_cast<T *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Tagged words.  Inside the sampling kernel every value one workgroup hands to another
-// travels as a 64-bit word (call tag << 32 | 32-bit payload) written and read with one
-// device-scope 64-bit store / load, which is single-copy atomic.  A reader takes a word
-// as present when it carries this call's tag: no fence, store wait or counter is needed,
-// and a record is complete once all of its words carry the tag.  A double travels as a
-// float head and tail (d ~ head + tail to 2^-48).  The only waits are polls of words
-// written by workgroups that come earlier in the grid.
-SVD void tw_put(u64 *p, unsigned tag, unsigned bits) { st_dev(p, ((u64)tag << 32) | (u64)bits); }
-SVD void tw_putf(u64 *p, unsigned tag, float f) { tw_put(p, tag, __float_as_uint(f)); }
-SVD bool tw_ok(u64 w, unsigned tag) { return (unsigned)(w >> 32) == tag; }
-SVD float tw_f(u64 w) { return __uint_as_float((unsigned)w); }
-SVD float d_head(double d) { return (float)d; }
-SVD float d_tail(double d) { return (float)(d - (double)(float)d); }
-SVD double d_join(float hi, float lo) { return (double)hi + (double)lo; }
-
-// Order-preserving 32-bit key of a float (bf16 values are floats with zero low half);
-// -0 and +0 share a key.
-SVD uint32_t f2key(float f) {
-  uint32_t b = __float_as_uint(f);
-  if (b == 0x80000000u) b = 0u;
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-SVD float key2f(uint32_t k) { return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k); }
-
-// Inverse CDF over n ordered items, by one whole wave: masses come from mfn(i); the
-// prefix runs in index order (groups of 64 lanes, inclusive scan, carried), so the same
-// masses always give the same total and prefixes.  wave_total returns the total;
-// wave_pick returns the first item whose inclusive prefix exceeds t and, in *t_rem,
-// t minus the prefix before it.  When rounding leaves t at or past the total it returns
-// the last item with positive mass and *t_rem = +inf (which makes the finer levels take
-// their last positive entry too).  -1 if no item has positive mass.
-template <typename MFn>
-SVD double wave_scan_group(int n, int i0, const MFn &mfn, double carry, double &m, double &cum) {
-  const int i = i0 + lane_id();
-  m = (i < n) ? mfn(i) : 0.0;
-  cum = scan_sum(m) + carry;
-  return readlane_d(cum, WAVE - 1);
-}
-
-template <typename MFn>
-SVD double wave_total(int n, const MFn &mfn) {
-  double carry = 0.0, m, cum;
-  for (int i0 = 0; i0 < n; i0 += WAVE) carry = wave_scan_group(n, i0, mfn, carry, m, cum);
-  return carry;
-}
-
-template <typename MFn>
-SVD int wave_pick(int n, double t, const MFn &mfn, double *t_rem) {
-  double carry = 0.0, m, cum;
-  int pick = -1, lastpos = -1;
-  double trem = INFINITY;
-  for (int i0 = 0; i0 < n; i0 += WAVE) {
-    const double carry_in = carry;
-    carry = wave_scan_group(n, i0, mfn, carry, m, cum);
-    const unsigned long long pos = __ballot(m > 0.0);
-    if (pos) lastpos = i0 + 63 - __clzll((long long)pos);
-    if (pick < 0) {
-      const unsigned long long cr = __ballot(m > 0.0 && cum > t);
-      if (cr) {
-        const int l = __ffsll((long long)cr) - 1;
-        const double prev = (l == 0) ? carry_in : readlane_d(cum, l - 1);
-        pick = i0 + l;
-        trem = t - prev;
-      }
-    }
-  }
-  if (pick < 0) {
-    pick = lastpos;
-    trem = INFINITY;
-  }
-  *t_rem = trem;
-  return pick;
-}
-
-// wave_pick with t = u * (total of the same masses): for n <= 64 one scan gives both.
-template <typename MFn>
-SVD int wave_pick_frac(int n, double u, const MFn &mfn, double *t_rem, double *total) {
-  if (n > WAVE) {
-    *total = wave_total(n, mfn);
-    return wave_pick(n, u * *total, mfn, t_rem);
-  }
-  const int i = lane_id();
-  const double m = (i < n) ? mfn(i) : 0.0;
-  const double cum = scan_sum(m);
-  const double tot = readlane_d(cum, WAVE - 1);
-  const double t = u * tot;
-  *total = tot;
-  const unsigned long long pos = __ballot(m > 0.0);
-  const unsigned long long cr = __ballot(m > 0.0 && cum > t);
-  if (cr) {
-    const int l = __ffsll((long long)cr) - 1;
-    const double prev = (l == 0) ? 0.0 : readlane_d(cum, l - 1);
-    *t_rem = t - prev;
-    return l;
-  }
-  *t_rem = INFINITY;
-  return pos ? 63 - __clzll((long long)pos) : -1;
-}
-
-// Inverse CDF over n masses in index order, four consecutive ones per lane in blocks of
-// 256: lane sums (in order), one scan per block.  t = u * total; returns the first index
-// whose prefix exceeds t and, in *t_rem, t minus the prefix before it; when rounding
-// leaves t at or past the total, the last positive index and +inf; -1 if nothing is
-// positive.  A single block reads its masses once.
-template <typename MFn>
-SVD int wave_pick4_frac(int n, double u, const MFn &mfn, double *t_rem, double *total) {
-  constexpr int SB = 4, BLK = SB * WAVE;
-  const int lane = lane_id();
-  double m[SB];
-  auto lane_masses = [&](int b0) {
-    double ls = 0.0;
-#pragma unroll
-    for (int k = 0; k < SB; ++k) {
-      const int i = b0 + lane * SB + k;
-      m[k] = (i < n) ? mfn(i) : 0.0;
-    }
-#pragma unroll
-    for (int k = 0; k < SB; ++k) ls += m[k];
-    return ls;
-  };
-  // The lane that holds the crossing picks its element; the result is broadcast.
-  auto in_lane = [&](int b0, int l, double rem, double *t_out) {
-    int pk = -1, last = -1;
-    double run = 0.0, r_out = INFINITY;
-#pragma unroll
-    for (int k = 0; k < SB; ++k) {
-      if (m[k] > 0.0) last = k;
-      if (pk < 0 && m[k] > 0.0 && run + m[k] > rem) {
-        pk = k;
-        r_out = rem - run;
-      }
-      run += m[k];
-    }
-    if (pk < 0) pk = last;
-    const int idx = (pk < 0) ? -1 : b0 + lane * SB + pk;
-    *t_out = readlane_d(r_out, l);
-    return __builtin_amdgcn_readlane(idx, l);
-  };
-  if (n <= BLK) {
-    const double ls = lane_masses(0);
-    const double cum = scan_sum(ls);
-    *total = readlane_d(cum, WAVE - 1);
-    const double t = u * *total;
-    const unsigned long long cr = __ballot(ls > 0.0 && cum > t);
-    const unsigned long long pos = __ballot(ls > 0.0);
-    if (cr) {
-      const int l = __ffsll((long long)cr) - 1;
-      const double prev = (l == 0) ? 0.0 : readlane_d(cum, l - 1);
-      return in_lane(0, l, t - prev, t_rem);
-    }
-    if (!pos) return -1;
-    const int l = 63 - __clzll((long long)pos);
-    return in_lane(0, l, INFINITY, t_rem);
-  }
-  double carry = 0.0;
-  for (int b0 = 0; b0 < n; b0 += BLK) carry += readlane_d(scan_sum(lane_masses(b0)), WAVE - 1);
-  *total = carry;
-  const double t = u * carry;
-  double c2 = 0.0;
-  int lb = -1, ll = -1;
-  for (int b0 = 0; b0 < n; b0 += BLK) {
-    const double ls = lane_masses(b0);
-    const double cum = scan_sum(ls) + c2;
-    const unsigned long long pos = __ballot(ls > 0.0);
-    if (pos) {
-      lb = b0;
-      ll = 63 - __clzll((long long)pos);
-    }
-    const unsigned long long cr = __ballot(ls > 0.0 && cum > t);
-    if (cr) {
-      const int l = __ffsll((long long)cr) - 1;
-      const double prev = (l == 0) ? c2 : readlane_d(cum, l - 1);
-      return in_lane(b0, l, t - prev, t_rem);
-    }
-    c2 = readlane_d(cum, WAVE - 1);
-  }
-  if (lb < 0) return -1;
-  lane_masses(lb);
-  return in_lane(lb, ll, INFINITY, t_rem);
-}
-
-// ---------------------------------------------------------------- block placement
-
-// The device hands workgroups to its XCDs round-robin (blockIdx % 8), each XCD in
-// blockIdx order.  Work comes in UNITS (a row, or a sequence) of per1 first-phase items
-// and per2 second-phase items, and the last items of a unit wait for the earlier ones.
-// Block p runs item q = p / LANES of lane k = p % LANES; lane k owns units k, k+LANES, ...
-// and runs all their first-phase items, unit after unit, then all their second-phase
-// items.  So each XCD streams whole units front to back, the waiting items (a unit's
-// last ones) are spread over every XCD instead of all landing on one, and every wait is
-// for an earlier item of the same lane, i.e. a smaller blockIdx: the grid cannot stall,
-// wherever the blocks run.  Returns false for the padding blocks of short lanes.
-constexpr int LANES = 8;
-
-SVD bool lane_item(int units, int per1, int per2, int &phase, int &item) {
-  const int p = (int)blockIdx.x;
-  const int k = p % LANES, q = p / LANES;
-  const int nu = (units > k) ? (units - k + LANES - 1) / LANES : 0;
-  if (q < nu * per1) {
-    const int s = q / per1;
-    item = (k + LANES * s) * per1 + (q - s * per1);
-    phase = 1;
-    return true;
-  }
-  const int q2 = q - nu * per1;
-  if (q2 < nu * per2) {
-    const int s = q2 / per2;
-    item = (k + LANES * s) * per2 + (q2 - s * per2);
-    phase = 2;
-    return true;
-  }
-  return false;
 }
 
 // ---------------------------------------------------------------- top-k threshold
@@ -658,29 +205,198 @@ __global__ __launch_bounds__(NT) void k_topk_digit(const Args a, int pass, int l
 
 // ---------------------------------------------------------------- acceptance scan
 
-// Largest value wins, ties go to the lower index; NaN and +inf mark the row unusable.
-SVD void best_combine(float &v, int &i, float v2, int i2) {
-  if (v2 > v || (v2 == v && i2 < i)) {
-    v = v2;
-    i = i2;
+// ---------------------------------------------------------------- draw helpers
+
+// Weights of the correction draw: w = max(p - q, 0) with p = 2^(z_t*k2 - Mt) and
+// q = 2^(z_d*k2 - Md).  The log2-partitions are split into a float head and tail so the
+// per-element arguments carry only their own rounding.
+struct ResidualW {
+  float k2, mt_hi, mt_lo, md_hi, md_lo, tau_t, tau_d;
+  float off_j;  // row offset of p_j (the zero-residual fallback's reference)
+  SVD float operator()(float zt, float zd) const {
+    zt = (zt < tau_t) ? -INFINITY : zt;
+    zd = (zd < tau_d) ? -INFINITY : zd;
+    const float p = fast_exp2(fmaf(zt, k2, -mt_hi) - mt_lo);
+    const float q = fast_exp2(fmaf(zd, k2, -md_hi) - md_lo);
+    return fmaxf(p - q, 0.0f);
   }
+};
+
+// Weights of a draw from a target row itself (bonus, or the zero-residual fallback):
+// the first pass's terms of one chunk, recomputed bit for bit from its offset.
+struct TargetW {
+  float k2, off, tau;
+  SVD float operator()(float zt, float) const {
+    zt = (zt < tau) ? -INFINITY : zt;
+    return fast_exp2(fmaf(zt, k2, -off));
+  }
+};
+
+// Segment masses of vectors kbeg..kbeg+NK-1 of chunk c (whole workgroup): weights
+// wf(zA, zB) per element (zB = -inf without a second row), a lane mass per vector
+// (elements summed in order), and the wave sum of each 64-vector segment into
+// s_seg[k*NW + wave].  Loads are issued KG vectors per thread at a time (KG = NK: every
+// load in flight at once).
+template <typename T, bool ALIGNED, int KG, int NK, bool PAIR, typename WFn>
+SVD void chunk_masses(const Args &a, const T *rowA, const T *rowB, int c, int kbeg, const WFn &wf,
+                      double *s_seg) {
+  constexpr int VEC = Fmt<T>::VEC;
+  const int tid = threadIdx.x, lane = lane_id(), wid = tid / WAVE;
+#pragma unroll
+  for (int kg = 0; kg < NK; kg += KG) {
+    const int k0 = kbeg + kg;
+    float acc[KG];
+    if (ALIGNED) {
+      // Raw 16-byte vectors stay packed until their own turn: KG*4 registers per row.
+      u32x4 wa[KG], wb[PAIR ? KG : 1];
+      const u32x4 *ra = reinterpret_cast<const u32x4 *>(rowA);
+      const u32x4 *rb = reinterpret_cast<const u32x4 *>(rowB);
+#pragma unroll
+      for (int k = 0; k < KG; ++k) {
+        const int v = c * CHUNK_VECS + (k0 + k) * NT + tid;
+        const int vs = v < a.nvec ? v : a.nvec - 1;
+        wa[k] = ra[vs];
+        if (PAIR) wb[PAIR ? k : 0] = rb[vs];
+      }
+#pragma unroll
+      for (int k = 0; k < KG; ++k) {
+        const bool in = c * CHUNK_VECS + (k0 + k) * NT + tid < a.nvec;
+        float xa[VEC], xb[VEC];
+        Fmt<T>::unpack(wa[k], xa);
+        if (PAIR) Fmt<T>::unpack(wb[PAIR ? k : 0], xb);
+        float m = 0.0f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) m += wf(in ? xa[e] : -INFINITY, (PAIR && in) ? xb[e] : -INFINITY);
+        acc[k] = m;
+      }
+    } else {
+      float xa[KG][VEC], xb[PAIR ? KG : 1][VEC];
+      load_vectors<T, ALIGNED, false, KG>(rowA, a.V, a.nvec, c, k0, tid, xa);
+      if (PAIR) load_vectors<T, ALIGNED, false, PAIR ? KG : 1>(rowB, a.V, a.nvec, c, k0, tid, xb);
+#pragma unroll
+      for (int k = 0; k < KG; ++k) {
+        float m = 0.0f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) m += wf(xa[k][e], PAIR ? xb[PAIR ? k : 0][e] : -INFINITY);
+        acc[k] = m;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < KG; ++k) {
+      const double seg = wave_sum((double)acc[k]);
+      if (lane == 0) s_seg[(k0 + k) * NW + wid] = seg;
+    }
+  }
+  __syncthreads();
 }
 
-SVD void wave_best(float &v, int &i, int &fl) {
-#define STEP(C, R)                                   \
-  {                                                  \
-    const float v2 = dpp_f<C, R>(v, -INFINITY);      \
-    const int i2 = dpp_i<C, R>(i, 0x7fffffff);       \
-    fl |= dpp_i<C, R>(fl, 0);                        \
-    best_combine(v, i, v2, i2);                      \
+// Inverse CDF inside segment s of chunk c, by one wave: each lane re-reads its vector of
+// the segment (rows A and B), recomputes the element weights and its lane mass exactly
+// as chunk_masses did, then picks lane and element.  With t = +inf the last positive
+// element is taken.  Returns the element index in the row (same in every lane), or -1.
+template <typename T, bool ALIGNED, typename WFn>
+SVD int segment_draw(const Args &a, const T *rowA, const T *rowB, int c, int s, const WFn &wf,
+                     double t) {
+  constexpr int VEC = Fmt<T>::VEC;
+  const int lane = lane_id();
+  const int k = s / NW, w = s % NW;
+  const int tid_equiv = w * WAVE + lane;  // the thread that held this vector
+  float xa[VEC], xb[VEC];
+  if (ALIGNED) {  // one 16-byte vector per row
+    const int v = c * CHUNK_VECS + k * NT + tid_equiv;
+    const bool in = v < a.nvec;
+    const int vs = in ? v : a.nvec - 1;
+    Fmt<T>::unpack(reinterpret_cast<const u32x4 *>(rowA)[vs], xa);
+    if (rowB) Fmt<T>::unpack(reinterpret_cast<const u32x4 *>(rowB)[vs], xb);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      xa[e] = in ? xa[e] : -INFINITY;
+      xb[e] = (in && rowB) ? xb[e] : -INFINITY;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const long idx = elem_index<T>(c, k, tid_equiv, e);
+      const bool in = idx < a.V;
+      const size_t ii = (size_t)(in ? idx : (long)a.V - 1);
+      xa[e] = in ? Fmt<T>::at(rowA, ii) : -INFINITY;
+      xb[e] = (in && rowB) ? Fmt<T>::at(rowB, ii) : -INFINITY;
+    }
   }
-  SV_SCAN_STEPS(STEP)
-#undef STEP
-  v = readlane_f(v, WAVE - 1);
-  i = __builtin_amdgcn_readlane(i, WAVE - 1);
-  fl = __builtin_amdgcn_readlane(fl, WAVE - 1);
+  float we[VEC];
+  float acc = 0.0f;
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) {
+    we[e] = wf(xa[e], xb[e]);
+    acc += we[e];
+  }
+  auto lanem = [&](int) { return (double)acc; };
+  double lrem;
+  const int pl = wave_pick(WAVE, t, lanem, &lrem);
+  int res = -1;
+  if (lane == pl) {
+    int pe = -1, lastpe = -1;
+    double run = 0.0;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      if (we[e] > 0.0f) lastpe = e;
+      run += (double)we[e];
+      if (pe < 0 && we[e] > 0.0f && run > lrem) pe = e;
+    }
+    if (pe < 0) pe = lastpe;
+    res = (pe < 0) ? -1 : (int)elem_index<T>(c, k, tid_equiv, pe);
+  }
+  return __builtin_amdgcn_readlane(res, pl < 0 ? 0 : pl);
 }
 
+// Whole-chunk inverse CDF by one wave (rare path: the zero-residual fallback, after
+// the other waves of the workgroup have finished): segment masses one segment at a
+// time, then segment_draw.
+template <typename T, bool ALIGNED, typename WFn>
+SVD int wave_chunk_draw(const Args &a, const T *rowA, const T *rowB, int c, const WFn &wf,
+                        double t) {
+  constexpr int VEC = Fmt<T>::VEC;
+  __shared__ double s_wseg[SEGS];
+  const int lane = lane_id();
+  for (int sg = 0; sg < SEGS; ++sg) {
+    const int k = sg / NW, w = sg % NW;
+    float acc = 0.0f;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const long idx = elem_index<T>(c, k, w * WAVE + lane, e);
+      const bool in = idx < a.V;
+      const size_t ii = (size_t)(in ? idx : (long)a.V - 1);
+      const float za = in ? Fmt<T>::at(rowA, ii) : -INFINITY;
+      const float zb = (in && rowB) ? Fmt<T>::at(rowB, ii) : -INFINITY;
+      acc += wf(za, zb);
+    }
+    const double m = wave_sum((double)acc);
+    if (lane == 0) s_wseg[sg] = m;
+  }
+  lds_sync();
+  auto segm = [&](int i) { return s_wseg[i]; };
+  double srem;
+  const int sp = wave_pick(SEGS, t, segm, &srem);
+  if (sp < 0) return -1;
+  return segment_draw<T, ALIGNED>(a, rowA, rowB, c, sp, wf, srem);
+}
+
+// One wave: pick the chunk of target row r from the first pass's partials (mass
+// S_c * 2^(off_c - off_r)), and express the remainder in the chunk's own scale.  The
+// partials are complete: the scan that published the job read all of them.
+SVD int pick_target_chunk(const Args &a, int r, float off_r, float u, double *t_in) {
+  const u64 *pw = a.w.tw_part + (size_t)r * a.C * 3;
+  auto cm = [&](int cc) {
+    const double s = d_join(tw_f(ld_dev(&pw[cc * 3 + 1])), tw_f(ld_dev(&pw[cc * 3 + 2])));
+    const float d = tw_f(ld_dev(&pw[cc * 3])) - off_r;
+    return (s > 0.0) ? s * (double)fast_exp2(d) : 0.0;
+  };
+  const double total = wave_total(a.C, cm);
+  double trem;
+  const int c = wave_pick(a.C, (double)u * total, cm, &trem);
+  *t_in = (c >= 0) ? trem * (double)fast_exp2(off_r - tw_f(ld_dev(&pw[c * 3]))) : 0.0;
+  return c;
+}
 
 constexpr int SEQ_LDS_PARTS = 256;   // (row, chunk) partials of one sequence staged in LDS
 constexpr int SEQ_LDS_ROWS = 129;    // rows of one sequence kept in LDS (G <= 64)
@@ -843,9 +559,9 @@ SVD void greedy_finish(const Args &a, int b, float own_best, int own_idx, int ow
 // It writes the accepted prefix and the -1 padding, and publishes the draw's record
 // (the drawn token and accepted_len are written by the draw).  The finisher's own
 // partial (index np - 1) and token logit come from its registers.
-template <typename T, bool TOPK, bool LDS>
+template <typename T, bool ALIGNED, bool TOPK, bool LDS, bool G0>
 SVD void sampling_finish(const Args &a, int b, float own_off, float own_hi, float own_lo,
-                         bool own_tok, float own_zx) {
+                         bool own_tok, float own_zx, const double *s_own_gseg) {
   constexpr int UNR = SEQ_LDS_PARTS / WAVE;
   constexpr int RUNR = (SEQ_LDS_ROWS + WAVE - 1) / WAVE;
   __shared__ float s_po[SEQ_LDS_PARTS];
@@ -1115,8 +831,9 @@ SVD void sampling_finish(const Args &a, int b, float own_off, float own_hi, floa
   }
   if (err && lane == 0) a.accepted_len[b] = err;
 
-  // The draw's record, one tagged word per lane.
-  const int kind = err ? (int)JOB_NONE : (j < G ? (int)JOB_REJECT : (int)JOB_BONUS);
+  // The draw's record, one tagged word per lane.  With no drafts (G = 0) the bonus is
+  // drawn right here (below) and no draw items exist.
+  const int kind = (err || G0) ? (int)JOB_NONE : (j < G ? (int)JOB_REJECT : (int)JOB_BONUS);
   float mt_hi = 0.0f, mt_lo = 0.0f, md_hi = 0.0f, md_lo = 0.0f, tau_t = -INFINITY, tau_d = -INFINITY;
   float off_j = 0.0f;
   if (kind == JOB_REJECT) {
@@ -1160,6 +877,46 @@ SVD void sampling_finish(const Args &a, int b, float own_off, float own_hi, floa
       a.row_stats[(r0 + jr) * 2 + 1] = s_rsum[jr];
     }
   }
+  if (!G0 || err) return;
+
+  // No drafts: the draw from p_1 (the row), in the chunk picked above, by the segment
+  // masses that chunk's item published (this item's own when it is that chunk), then one
+  // re-read segment.
+  int tok = -1;
+  if (c_bonus >= 0 && c_bonus < C) {
+    double segv = (lane < SEGS) ? s_own_gseg[lane] : 0.0;
+    const bool own = (c_bonus == C - 1);  // this item is the row's last chunk
+    bool ok = true;
+    if (!own) {
+      const u64 *gw = a.w.tw_gseg + (((size_t)b * C + c_bonus) * SEGS) * 2;
+      const int sl = (lane < SEGS) ? lane : 0;
+      for (unsigned polls = 0;;) {
+        const u64 h = ld_dev(&gw[2 * sl]), l = ld_dev(&gw[2 * sl + 1]);
+        segv = (lane < SEGS) ? d_join(tw_f(h), tw_f(l)) : 0.0;
+        if (__ballot(lane < SEGS && !(tw_ok(h, tag) && tw_ok(l, tag))) == 0) break;
+        if (++polls >= a.spin_limit) {
+          ok = false;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    if (!ok) {
+      for (int i = lane; i <= G; i += WAVE) out[i] = -1;
+      if (lane == 0) a.accepted_len[b] = SV_ROW_INTERNAL;
+      return;
+    }
+    auto segm = [&](int) { return segv; };
+    double ts;
+    const int sp = wave_pick(SEGS, t_bonus, segm, &ts);
+    if (sp >= 0)
+      tok = segment_draw<T, ALIGNED>(a, seq_row<T>(a, b, G), (const T *)nullptr, c_bonus, sp,
+                                     TargetW{a.k2, off_bonus, tau_of(G)}, ts);
+  }
+  if (lane == 0) {
+    out[G] = tok;
+    a.accepted_len[b] = G;
+  }
 }
 
 // ---------------------------------------------------------------- pass 1: normaliser
@@ -1168,7 +925,7 @@ SVD void sampling_finish(const Args &a, int b, float own_off, float own_hi, floa
 // s = sum 2^(fma(z, k2, -off)).  The log2-partition of a row is off_row + log2(s_row)
 // with off_row the float actually subtracted, so every consumer reproduces the same
 // probabilities; the second pass recomputes a chunk's terms bit for bit from the same offset.
-template <typename T, bool ALIGNED, bool TOPK>
+template <typename T, bool ALIGNED, bool TOPK, bool G0>
 SVD void norm_item(const Args &a, int item) {
   constexpr int VEC = Fmt<T>::VEC;
   __shared__ float s_m[NW];
@@ -1211,7 +968,30 @@ SVD void norm_item(const Args &a, int item) {
   const float k2 = a.k2;
   float off;
   double s;
-  if (m > -INFINITY) {
+  // With no drafts (G = 0, the batched sampler) the row's chunks give masses per 64-vector
+  // segment, a lane's elements summed in index order and the lanes by one DPP tree (the
+  // order the draw uses when it re-reads one segment); the chunk sum is the sum of its
+  // segments.  The finisher then draws without a second pass over a chunk.
+  __shared__ double s_gseg[SEGS];
+  constexpr bool bonus_row = G0;  // the batched sampler: the finisher draws from segment masses
+  if (bonus_row) {
+    off = (m > -INFINITY) ? m * k2 : -INFINITY;
+    bool nan = false;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      float lm = 0.0f;
+      if (m > -INFINITY) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) lm += fast_exp2(fmaf(x[k][e], k2, -off));
+      } else {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) nan |= (x[k][e] != x[k][e]);
+      }
+      const double sm = wave_sum((double)lm);
+      if (lane == 0) s_gseg[k * NW + wid] = sm;
+    }
+    s = (!(m > -INFINITY) && nan) ? (double)NAN : 0.0;  // an empty chunk still shows a NaN
+  } else if (m > -INFINITY) {
     off = m * k2;
     float acc = 0.0f;
 #pragma unroll
@@ -1240,20 +1020,26 @@ SVD void norm_item(const Args &a, int item) {
   __syncthreads();
   if (wid != 0) return;  // one wave finishes the workgroup
 
-  const double S = (s_s[0] + s_s[1]) + (s_s[2] + s_s[3]);
+  double S = (s_s[0] + s_s[1]) + (s_s[2] + s_s[3]);
+  if (bonus_row) S = (S != S) ? S : wave_sum((lane < SEGS) ? s_gseg[lane] : 0.0);
   const float s_hi = d_head(S), s_lo = d_tail(S);
   // The sequence's last item in grid order finishes the sequence, from its own values
   // and the other items' published ones.
   if (jr == a.rps - 1 && c == a.C - 1) {
     if (a.rps * a.C <= SEQ_LDS_PARTS && a.rps <= SEQ_LDS_ROWS)
-      sampling_finish<T, TOPK, true>(a, b, off, s_hi, s_lo, tok_here, zx);
+      sampling_finish<T, ALIGNED, TOPK, true, G0>(a, b, off, s_hi, s_lo, tok_here, zx, s_gseg);
     else
-      sampling_finish<T, TOPK, false>(a, b, off, s_hi, s_lo, tok_here, zx);
+      sampling_finish<T, ALIGNED, TOPK, false, G0>(a, b, off, s_hi, s_lo, tok_here, zx, s_gseg);
     return;
   }
   u64 *pw = a.w.tw_part + ((size_t)r * a.C + c) * 3;
   if (lane < 3) tw_putf(pw + lane, a.tag, lane == 0 ? off : (lane == 1 ? s_hi : s_lo));
   if (lane == 3 && tok_here) tw_putf(&a.w.tw_zx[r], a.tag, zx);
+  if (bonus_row && lane < 2 * SEGS) {
+    u64 *gw = a.w.tw_gseg + (((size_t)b * a.C + c) * SEGS) * 2;
+    const double v = s_gseg[lane >> 1];
+    tw_putf(&gw[lane], a.tag, (lane & 1) ? d_tail(v) : d_head(v));
+  }
 }
 
 // ---------------------------------------------------------------- pass 1: greedy argmax
@@ -1313,197 +1099,6 @@ __global__ __launch_bounds__(NT) void k_argmax(const Args a) {
 }
 
 // ---------------------------------------------------------------- pass 2: the draw
-
-// Weights of the correction draw: w = max(p - q, 0) with p = 2^(z_t*k2 - Mt) and
-// q = 2^(z_d*k2 - Md).  The log2-partitions are split into a float head and tail so the
-// per-element arguments carry only their own rounding.
-struct ResidualW {
-  float k2, mt_hi, mt_lo, md_hi, md_lo, tau_t, tau_d;
-  float off_j;  // row offset of p_j (the zero-residual fallback's reference)
-  SVD float operator()(float zt, float zd) const {
-    zt = (zt < tau_t) ? -INFINITY : zt;
-    zd = (zd < tau_d) ? -INFINITY : zd;
-    const float p = fast_exp2(fmaf(zt, k2, -mt_hi) - mt_lo);
-    const float q = fast_exp2(fmaf(zd, k2, -md_hi) - md_lo);
-    return fmaxf(p - q, 0.0f);
-  }
-};
-
-// Weights of a draw from a target row itself (bonus, or the zero-residual fallback):
-// the first pass's terms of one chunk, recomputed bit for bit from its offset.
-struct TargetW {
-  float k2, off, tau;
-  SVD float operator()(float zt, float) const {
-    zt = (zt < tau) ? -INFINITY : zt;
-    return fast_exp2(fmaf(zt, k2, -off));
-  }
-};
-
-// Segment masses of vectors kbeg..kbeg+NK-1 of chunk c (whole workgroup): weights
-// wf(zA, zB) per element (zB = -inf without a second row), a lane mass per vector
-// (elements summed in order), and the wave sum of each 64-vector segment into
-// s_seg[k*NW + wave].  Loads are issued KG vectors per thread at a time (KG = NK: every
-// load in flight at once).
-template <typename T, bool ALIGNED, int KG, int NK, bool PAIR, typename WFn>
-SVD void chunk_masses(const Args &a, const T *rowA, const T *rowB, int c, int kbeg, const WFn &wf,
-                      double *s_seg) {
-  constexpr int VEC = Fmt<T>::VEC;
-  const int tid = threadIdx.x, lane = lane_id(), wid = tid / WAVE;
-#pragma unroll
-  for (int kg = 0; kg < NK; kg += KG) {
-    const int k0 = kbeg + kg;
-    float acc[KG];
-    if (ALIGNED) {
-      // Raw 16-byte vectors stay packed until their own turn: KG*4 registers per row.
-      u32x4 wa[KG], wb[PAIR ? KG : 1];
-      const u32x4 *ra = reinterpret_cast<const u32x4 *>(rowA);
-      const u32x4 *rb = reinterpret_cast<const u32x4 *>(rowB);
-#pragma unroll
-      for (int k = 0; k < KG; ++k) {
-        const int v = c * CHUNK_VECS + (k0 + k) * NT + tid;
-        const int vs = v < a.nvec ? v : a.nvec - 1;
-        wa[k] = ra[vs];
-        if (PAIR) wb[PAIR ? k : 0] = rb[vs];
-      }
-#pragma unroll
-      for (int k = 0; k < KG; ++k) {
-        const bool in = c * CHUNK_VECS + (k0 + k) * NT + tid < a.nvec;
-        float xa[VEC], xb[VEC];
-        Fmt<T>::unpack(wa[k], xa);
-        if (PAIR) Fmt<T>::unpack(wb[PAIR ? k : 0], xb);
-        float m = 0.0f;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) m += wf(in ? xa[e] : -INFINITY, (PAIR && in) ? xb[e] : -INFINITY);
-        acc[k] = m;
-      }
-    } else {
-      float xa[KG][VEC], xb[PAIR ? KG : 1][VEC];
-      load_vectors<T, ALIGNED, false, KG>(rowA, a.V, a.nvec, c, k0, tid, xa);
-      if (PAIR) load_vectors<T, ALIGNED, false, PAIR ? KG : 1>(rowB, a.V, a.nvec, c, k0, tid, xb);
-#pragma unroll
-      for (int k = 0; k < KG; ++k) {
-        float m = 0.0f;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) m += wf(xa[k][e], PAIR ? xb[PAIR ? k : 0][e] : -INFINITY);
-        acc[k] = m;
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < KG; ++k) {
-      const double seg = wave_sum((double)acc[k]);
-      if (lane == 0) s_seg[(k0 + k) * NW + wid] = seg;
-    }
-  }
-  __syncthreads();
-}
-
-// Inverse CDF inside segment s of chunk c, by one wave: each lane re-reads its vector of
-// the segment (rows A and B), recomputes the element weights and its lane mass exactly
-// as chunk_masses did, then picks lane and element.  With t = +inf the last positive
-// element is taken.  Returns the element index in the row (same in every lane), or -1.
-template <typename T, bool ALIGNED, typename WFn>
-SVD int segment_draw(const Args &a, const T *rowA, const T *rowB, int c, int s, const WFn &wf,
-                     double t) {
-  constexpr int VEC = Fmt<T>::VEC;
-  const int lane = lane_id();
-  const int k = s / NW, w = s % NW;
-  const int tid_equiv = w * WAVE + lane;  // the thread that held this vector
-  float xa[VEC], xb[VEC];
-  if (ALIGNED) {  // one 16-byte vector per row
-    const int v = c * CHUNK_VECS + k * NT + tid_equiv;
-    const bool in = v < a.nvec;
-    const int vs = in ? v : a.nvec - 1;
-    Fmt<T>::unpack(reinterpret_cast<const u32x4 *>(rowA)[vs], xa);
-    if (rowB) Fmt<T>::unpack(reinterpret_cast<const u32x4 *>(rowB)[vs], xb);
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      xa[e] = in ? xa[e] : -INFINITY;
-      xb[e] = (in && rowB) ? xb[e] : -INFINITY;
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      const long idx = elem_index<T>(c, k, tid_equiv, e);
-      const bool in = idx < a.V;
-      const size_t ii = (size_t)(in ? idx : (long)a.V - 1);
-      xa[e] = in ? Fmt<T>::at(rowA, ii) : -INFINITY;
-      xb[e] = (in && rowB) ? Fmt<T>::at(rowB, ii) : -INFINITY;
-    }
-  }
-  float we[VEC];
-  float acc = 0.0f;
-#pragma unroll
-  for (int e = 0; e < VEC; ++e) {
-    we[e] = wf(xa[e], xb[e]);
-    acc += we[e];
-  }
-  auto lanem = [&](int) { return (double)acc; };
-  double lrem;
-  const int pl = wave_pick(WAVE, t, lanem, &lrem);
-  int res = -1;
-  if (lane == pl) {
-    int pe = -1, lastpe = -1;
-    double run = 0.0;
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      if (we[e] > 0.0f) lastpe = e;
-      run += (double)we[e];
-      if (pe < 0 && we[e] > 0.0f && run > lrem) pe = e;
-    }
-    if (pe < 0) pe = lastpe;
-    res = (pe < 0) ? -1 : (int)elem_index<T>(c, k, tid_equiv, pe);
-  }
-  return __builtin_amdgcn_readlane(res, pl < 0 ? 0 : pl);
-}
-
-// Whole-chunk inverse CDF by one wave (rare path: the zero-residual fallback, after
-// the other waves of the workgroup have finished): segment masses one segment at a
-// time, then segment_draw.
-template <typename T, bool ALIGNED, typename WFn>
-SVD int wave_chunk_draw(const Args &a, const T *rowA, const T *rowB, int c, const WFn &wf,
-                        double t) {
-  constexpr int VEC = Fmt<T>::VEC;
-  __shared__ double s_wseg[SEGS];
-  const int lane = lane_id();
-  for (int sg = 0; sg < SEGS; ++sg) {
-    const int k = sg / NW, w = sg % NW;
-    float acc = 0.0f;
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      const long idx = elem_index<T>(c, k, w * WAVE + lane, e);
-      const bool in = idx < a.V;
-      const size_t ii = (size_t)(in ? idx : (long)a.V - 1);
-      const float za = in ? Fmt<T>::at(rowA, ii) : -INFINITY;
-      const float zb = (in && rowB) ? Fmt<T>::at(rowB, ii) : -INFINITY;
-      acc += wf(za, zb);
-    }
-    const double m = wave_sum((double)acc);
-    if (lane == 0) s_wseg[sg] = m;
-  }
-  lds_sync();
-  auto segm = [&](int i) { return s_wseg[i]; };
-  double srem;
-  const int sp = wave_pick(SEGS, t, segm, &srem);
-  if (sp < 0) return -1;
-  return segment_draw<T, ALIGNED>(a, rowA, rowB, c, sp, wf, srem);
-}
-
-// One wave: pick the chunk of target row r from the first pass's partials (mass
-// S_c * 2^(off_c - off_r)), and express the remainder in the chunk's own scale.  The
-// partials are complete: the scan that published the job read all of them.
-SVD int pick_target_chunk(const Args &a, int r, float off_r, float u, double *t_in) {
-  const u64 *pw = a.w.tw_part + (size_t)r * a.C * 3;
-  auto cm = [&](int cc) {
-    const double s = d_join(tw_f(ld_dev(&pw[cc * 3 + 1])), tw_f(ld_dev(&pw[cc * 3 + 2])));
-    const float d = tw_f(ld_dev(&pw[cc * 3])) - off_r;
-    return (s > 0.0) ? s * (double)fast_exp2(d) : 0.0;
-  };
-  const double total = wave_total(a.C, cm);
-  double trem;
-  const int c = wave_pick(a.C, (double)u * total, cm, &trem);
-  *t_in = (c >= 0) ? trem * (double)fast_exp2(off_r - tw_f(ld_dev(&pw[c * 3]))) : 0.0;
-  return c;
-}
 
 constexpr int COMB_LDS_SEGS = 1024;  // segment masses of one sequence kept in LDS by the combiner
 
@@ -1588,13 +1183,13 @@ SVD void combine_draw(const Args &a, int b, int j, float u, const T *row_t, cons
 
 // Draw item (sequence b, chunk c, quarter sub).  All draw items follow every first-pass
 // item in the grid.  Each waits until the sequence's record carries this call's tag, then
-//   reject at j: computes the masses of [p_j - q_j]_+ of its quarter of the chunk per
-//                64-vector segment and publishes them; the sequence's last draw item in
-//                grid order (c = C-1, sub = NSUB-1) waits for all of them, picks chunk
-//                and segment, and one wave re-reads that segment to pick lane and element;
-//   bonus:       the chunk picked by the scan from the first pass's partials re-reads
-//                itself and draws from p_G (one item; the others leave).
-// The item that writes the drawn token also writes accepted_len.
+// for a rejection at j computes the masses of [p_j - q_j]_+ of its quarter of the chunk
+// per 64-vector segment and publishes them; the sequence's last draw item in grid order
+// (c = C-1, sub = NSUB-1) waits for all of them, picks the segment over all of them, and
+// one wave re-reads that segment to pick lane and element.  For a bonus, the chunk picked
+// by the scan from the first pass's partials re-reads itself and draws from p_G (one
+// item; the others leave).  With a row error the items leave.  The item that writes the
+// drawn token also writes accepted_len.
 template <typename T, bool ALIGNED>
 SVD void draw_item(const Args &a, int item) {
   __shared__ double s_seg[SEGS];
@@ -1698,12 +1293,13 @@ SVD void draw_item(const Args &a, int item) {
 
 // Sampling: the first pass (normalisers, acceptance scan) and the draws in one grid;
 // units are sequences: first-pass items (rows in order, chunks in order), then draw items.
-template <typename T, bool ALIGNED, bool TOPK>
+// G0: no drafted positions (the batched sampler): first-pass items only.
+template <typename T, bool ALIGNED, bool TOPK, bool G0>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(5))) void k_verify(const Args a) {
   int phase, item;
-  if (!lane_item(a.B, a.rps * a.C, a.C * NSUB, phase, item)) return;
-  if (phase == 1) norm_item<T, ALIGNED, TOPK>(a, item);
-  else draw_item<T, ALIGNED>(a, item);
+  if (!lane_item(a.B, a.rps * a.C, G0 ? 0 : a.C * NSUB, phase, item)) return;
+  if (phase == 1) norm_item<T, ALIGNED, TOPK, G0>(a, item);
+  else if (!G0) draw_item<T, ALIGNED>(a, item);
 }
 
 }  // namespace sv
@@ -1722,7 +1318,7 @@ struct Plan {
   long long R;
   int digit_passes;
   // workspace offsets
-  size_t tw_part, tw_zx, tw_job, tw_seg, tw_hist, row_tau, tk_state, total;
+  size_t tw_part, tw_zx, tw_job, tw_seg, tw_gseg, tw_hist, row_tau, tk_state, total;
   size_t zero_bytes;  // leading bytes (tagged words) that must be clean when a call starts
 };
 
@@ -1751,6 +1347,7 @@ bool make_plan(int32_t B, int32_t G, int32_t V, sv_dtype dt, float T, int32_t to
   p.tw_zx = o; o = align256(o + (smp ? R * 8 : 0));
   p.tw_job = o; o = align256(o + (smp ? Bz * JW * 8 : 0));
   p.tw_seg = o; o = align256(o + (smp ? Bz * C * SEGS * 2 * 8 : 0));
+  p.tw_gseg = o; o = align256(o + (smp ? Bz * C * SEGS * 2 * 8 : 0));
   p.tw_hist = o; o = align256(o + (p.topk ? R * C * 128 * 8 : 0));
   p.zero_bytes = o;
   p.row_tau = o; o = align256(o + (p.topk ? R * 4 : 0));
@@ -1784,7 +1381,7 @@ hipError_t launch_all(const Plan &p, const Args &a, hipStream_t st, void *const 
   const long long lb = (a.B + LANES - 1) / LANES, lr = (p.R + LANES - 1) / LANES;
   const unsigned topk_grid = (unsigned)(LANES * lr * p.C);
   const unsigned argmax_grid = (unsigned)(LANES * lb * p.rps * p.C);
-  const unsigned verify_grid = (unsigned)(LANES * lb * ((long long)p.rps * p.C + (long long)p.C * NSUB));
+  const unsigned verify_grid = (unsigned)(LANES * lb * ((long long)p.rps * p.C + (a.G > 0 ? (long long)p.C * NSUB : 0)));
   int n = 0;
   hipError_t e = hipSuccess;
   // With events, kernel i is launched with (events[2i], events[2i+1]) as its start and
@@ -1814,11 +1411,13 @@ hipError_t launch_all(const Plan &p, const Args &a, hipStream_t st, void *const 
       }
       aa.tag = next_tag();
       void *args[] = {&aa};
-      go((const void *)&k_verify<T, AL, true>, verify_grid, args);
+      go(a.G == 0 ? (const void *)&k_verify<T, AL, true, true> : (const void *)&k_verify<T, AL, true, false>,
+         verify_grid, args);
     } else {
       aa.tag = next_tag();
       void *args[] = {&aa};
-      go((const void *)&k_verify<T, AL, false>, verify_grid, args);
+      go(a.G == 0 ? (const void *)&k_verify<T, AL, false, true> : (const void *)&k_verify<T, AL, false, false>,
+         verify_grid, args);
     }
   }
   if (nl) *nl = n;
@@ -1869,6 +1468,7 @@ sv_status run(const void *target, const void *draft, sv_dtype dt, const int32_t 
   a.w.tw_zx = (u64 *)(base + p.tw_zx);
   a.w.tw_job = (u64 *)(base + p.tw_job);
   a.w.tw_seg = (u64 *)(base + p.tw_seg);
+  a.w.tw_gseg = (u64 *)(base + p.tw_gseg);
   a.w.tw_hist = (u64 *)(base + p.tw_hist);
   a.w.row_tau = (float *)(base + p.row_tau);
   a.w.tk_state = (uint2 *)(base + p.tk_state);

@@ -207,3 +207,30 @@ def make_random(B: int, G: int, V: int, dtype: str, seed: int, *, draft_noise: f
     cfg = Config(0, f"random_{B}x{G}x{V}_{dtype}", B, G, V, dtype, 1.0, 0, draft_noise, seed)
     return Raw(cfg, target, draft, uniforms(rng, (B, G)), uniforms(rng, (B, G)),
                uniforms(rng, (B,)), np.full((B, G), -1, np.int32))
+
+
+# ---------------------------------------------------------------- batched sampling
+
+@dataclass(frozen=True)
+class SampleConfig:
+    name: str
+    B: int
+    V: int
+    dtype: str
+    temperature: float
+    top_k: int
+    seed: int
+
+
+# One decode step of a batch of 256 sequences over a LLaMA-3-sized vocabulary: the
+# draft's X ~ q step, or plain decoding from p.
+SAMPLE_CONFIGS = {
+    "sample_bf16_b256": SampleConfig("sample_bf16_b256", 256, 128256, "bf16", 1.0, 0, 2001),
+}
+
+
+def make_sample(B: int, V: int, dtype: str, seed: int, *, noise_scale: float = 1.5):
+    """Zipf+Gaussian logits [B, V] (one prior per row) and uniforms [B]."""
+    target, _ = zipf_gauss(B, 0, V, dtype, 0.0, seed, noise_scale=noise_scale)
+    rng = np.random.default_rng(seed + 7919)
+    return np.ascontiguousarray(target[:, 0]), uniforms(rng, (B,))

@@ -115,3 +115,26 @@ def test_zero_prefix(lib):
     # more rows need more counters
     assert sv.sv_workspace_zero_bytes(64, 4, 128256, sv.SV_BF16, 1.0, 0) > \
         sv.sv_workspace_zero_bytes(8, 5, 32000, sv.SV_F32, 0.7, 0)
+
+
+def call_sample(lib, **kw):
+    a = dict(logits=FAKE, dt=sv.SV_BF16, u=FAKE, B=4, V=1024, T=1.0, k=0, tok=FAKE, st=FAKE,
+             ws=FAKE, nbytes=1 << 30, stream=None)
+    a.update(kw)
+    return lib.spec_sample(V_(a["logits"]), a["dt"], V_(a["u"]), a["B"], a["V"], F_(a["T"]), a["k"],
+                           V_(a["tok"]), V_(a["st"]), V_(a["ws"]), Z_(a["nbytes"]), V_(a["stream"]))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), 2), (dict(V=0), 2), (dict(dt=9), 3), (dict(T=-0.5), 4),
+    (dict(logits=None), 1), (dict(u=None), 1), (dict(tok=None), 1), (dict(st=None), 1),
+    (dict(ws=None), 1), (dict(nbytes=16), 5), (dict(logits=FAKE + 1), 6),
+])
+def test_sample_host_argument_errors(lib, kw, status):
+    assert call_sample(lib, **kw) == status
+
+
+def test_sample_greedy_reads_no_uniform(lib):
+    # stops at the workspace check, after the pointer checks passed without u
+    assert call_sample(lib, T=0.0, u=None, nbytes=16) == 5
+    assert sv.sv_launch_plan(256, 0, 128256, sv.SV_BF16, 1.0, 0) == ["k_verify"]
