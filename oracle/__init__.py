@@ -19,6 +19,9 @@ arrays into it.  The functions and the passages they follow:
   section "一次 sampling 怎么执行", step 1); ``sample_rows`` is also the oracle of the
   library's batched sampler ``spec_sample``.
 * ``topk_threshold_rows`` / ``argmax_rows`` -- the top-k cut and greedy choice.
+* ``overlap`` -- per drafted position, beta = sum min(p, q) (the acceptance
+  probability, first page, section "为什么接受概率恰好是这个比值"; the overlap behind the
+  LK loss and DSpark's c* on the second page) and tv = sum [p - q]_+.
 
 Every function is pinned by tests in ``tests/test_oracle_*.py`` against values
 the pages print, closed forms, invariants and library routines.  One branch is
@@ -71,6 +74,8 @@ def _bind(lib):
     lib.ref_topk_threshold_rows.restype = i32
     lib.ref_argmax_rows.argtypes = [P, i32, i32, i32, P]
     lib.ref_argmax_rows.restype = i32
+    lib.ref_overlap.argtypes = [P, P, i32, i32, i32, i32, i32, f64, i32, P, P, P, i32]
+    lib.ref_overlap.restype = i32
     lib.ref_invcdf.argtypes = [P, i32, f64, P]
     lib.ref_invcdf.restype = i32
     return lib
@@ -207,6 +212,30 @@ def argmax_rows(logits):
     idx = np.empty((R,), np.int32)
     lib.ref_argmax_rows(_ptr(z), dt, R, V, _ptr(idx))
     return idx.reshape(z.shape[:-1])
+
+
+def overlap(target, draft, temperature, top_k=0, *, nthreads=None):
+    """beta [B, G], tv [B, G] and status [B, G] of every drafted position.
+
+    target [B, TR, V] with TR = G or G + 1 rows per sequence (position i uses target row
+    i; a trailing row G is not read), draft [B, G, V]; float32 or uint16 bf16 bits.
+    temperature must be > 0.  Status is 0, or -3 when either row is unusable (beta and
+    tv are then NaN)."""
+    lib = _load()
+    target, dt = _logits(target)
+    draft, dt2 = _logits(draft)
+    assert dt2 == dt and target.ndim == 3 and draft.ndim == 3
+    B, G, V = draft.shape
+    TR = target.shape[1]
+    assert target.shape[0] == B and target.shape[2] == V and TR in (G, G + 1)
+    beta = np.empty((B, G), np.float64)
+    tv = np.empty((B, G), np.float64)
+    st = np.empty((B, G), np.int32)
+    rc = lib.ref_overlap(_ptr(target), _ptr(draft), dt, B, G, V, TR, float(temperature), int(top_k),
+                         _ptr(beta), _ptr(tv), _ptr(st), int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments (overlap needs temperature > 0)")
+    return beta, tv, st
 
 
 def invcdf(w, u):

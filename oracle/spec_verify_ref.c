@@ -40,6 +40,10 @@
  *   R7 "p(x) > 0" / "q(x) = 0" are support tests (kept by top-k and a finite logit);
  *      the ratio itself is formed as exp(min(0, log p(x) - log q(x))), which is
  *      min(1, p/q) written so that neither side underflows.
+ *   R15 the overlap of a position is taken between the two distributions the
+ *      verification compares there: p_i and q_i after the same temperature and top-k.
+ *      It is defined for T > 0 only (at T = 0 the policy is a deterministic choice).
+ *      TV is summed from its own definition, not as 1 - beta.
  */
 #include <math.h>
 #include <stdint.h>
@@ -426,5 +430,60 @@ int ref_argmax_rows(const void *logits, int dtype, int R, int V, int32_t *idx) {
     idx[r] = argmax_lowest(z, V);
   }
   free(z);
+  return 0;
+}
+
+/* ---- overlap of every drafted position -------------------------------------- */
+
+/* For each sequence b and position i, the two distributions the verification compares
+ * there, p_i (target row i) and q_i (draft row i), after the same policy (R5, R15):
+ *   beta = sum_v min(p_v, q_v)   -- the acceptance probability of the position, which is
+ *          also the overlap mass ("Speculative Decoding 的朴素思想", section
+ *          "为什么接受概率恰好是这个比值"; DSpark's confidence label c* and the LK loss
+ *          -log beta on "推测解码：接受规则、状态与收益边界");
+ *   tv   = sum_v max(p_v - q_v, 0) -- the residual mass Z, which for normalised
+ *          distributions is the total variation distance, 1 - beta.
+ * Both sums run in increasing v.  target holds target_rows rows per sequence (G or G+1),
+ * draft G.  A pair with an unusable row (NaN, +inf, or no finite logit) gives NaN and
+ * status -3, otherwise status 0.  Returns -1 for arguments it cannot process. */
+int ref_overlap(const void *target, const void *draft, int dtype, int B, int G, int V,
+                int target_rows, double temperature, int top_k, double *beta, double *tv,
+                int32_t *status, int nthreads) {
+  if (B < 0 || G < 0 || V < 1 || !(temperature > 0.0) || target_rows < G) return -1;
+  if (nthreads < 1) nthreads = 1;
+  const int npairs = B * G;
+#pragma omp parallel num_threads(nthreads)
+  {
+    double *zt = (double *)malloc(sizeof(double) * (size_t)V);
+    double *zd = (double *)malloc(sizeof(double) * (size_t)V);
+    double *P = (double *)malloc(sizeof(double) * (size_t)V);
+    double *Q = (double *)malloc(sizeof(double) * (size_t)V);
+#pragma omp for schedule(dynamic, 2)
+    for (int n = 0; n < npairs; ++n) {
+      const int b = n / G, i = n - b * G;
+      load_row(target, dtype, (size_t)b * target_rows + i, V, zt);
+      load_row(draft, dtype, (size_t)b * G + i, V, zd);
+      if (!row_is_valid(zt, V) || !row_is_valid(zd, V)) {
+        beta[n] = NAN;
+        tv[n] = NAN;
+        if (status) status[n] = REF_ERR_ROW;
+        continue;
+      }
+      policy(zt, V, temperature, top_k, NULL, P);
+      policy(zd, V, temperature, top_k, NULL, Q);
+      double sb = 0.0, st = 0.0;
+      for (int v = 0; v < V; ++v) {
+        sb += fmin(P[v], Q[v]);
+        st += fmax(P[v] - Q[v], 0.0);
+      }
+      beta[n] = sb;
+      tv[n] = st;
+      if (status) status[n] = 0;
+    }
+    free(zt);
+    free(zd);
+    free(P);
+    free(Q);
+  }
   return 0;
 }

@@ -12,6 +12,7 @@ import pytest
 
 import oracle
 import test_oracle_pins as pins
+import test_oracle_overlap as ovl
 import test_oracle_stats as stats
 
 SRC = Path(oracle.__file__).resolve().parent / "spec_verify_ref.c"
@@ -42,6 +43,18 @@ MUTANTS = [
      "return;\n  }\n\n  /* Every"),
     ("accept_len_off_by_one", "J->accepted_len[b] = i;\n    fill_tokens(out + i + 1, G - i, -1);\n    return;\n  }\n\n  /* Every",
      "J->accepted_len[b] = i + 1;\n    fill_tokens(out + i + 1, G - i, -1);\n    return;\n  }\n\n  /* Every"),
+    ("overlap_max_for_min", "sb += fmin(P[v], Q[v]);", "sb += fmax(P[v], Q[v]);"),
+    ("overlap_tv_absolute", "st += fmax(P[v] - Q[v], 0.0);", "st += fabs(P[v] - Q[v]);"),
+    ("overlap_target_stride", "load_row(target, dtype, (size_t)b * target_rows + i, V, zt);",
+     "load_row(target, dtype, (size_t)b * G + i, V, zt);"),
+    ("overlap_next_draft_row", "load_row(draft, dtype, (size_t)b * G + i, V, zd);",
+     "load_row(draft, dtype, (size_t)b * G + (i + 1) % G, V, zd);"),
+    ("overlap_topk_target_only", "policy(zd, V, temperature, top_k, NULL, Q);",
+     "policy(zd, V, temperature, 0, NULL, Q);"),
+    ("overlap_draft_unscaled", "policy(zd, V, temperature, top_k, NULL, Q);",
+     "policy(zd, V, 1.0, top_k, NULL, Q);"),
+    ("overlap_skips_draft_check", "if (!row_is_valid(zt, V) || !row_is_valid(zd, V)) {",
+     "if (!row_is_valid(zt, V)) {"),
 ]
 
 PIN_TESTS = [
@@ -65,6 +78,11 @@ PIN_TESTS = [
     lambda: pins.test_row_error_codes("u_one", oracle.ERR_UNIFORM),
     lambda: stats.test_monte_carlo_law_matches_target(1.0, 0),
     lambda: stats.test_expected_tokens_constant_rate(0.6, 4),
+    lambda: ovl.test_worked_examples(),
+    lambda: ovl.test_two_point_closed_form(),
+    lambda: ovl.test_identities_and_scipy(2.0, 5),
+    lambda: ovl.test_target_layout_with_or_without_bonus_row(),
+    lambda: ovl.test_row_checks(),
 ]
 
 
