@@ -32,9 +32,24 @@ sys.path.insert(0, str(ROOT))
 METRIC = "verified draft positions/sec and achieved HBM GB/s (% of peak) at B=64,V=128k"
 PEAK_HBM_GBS = 8000.0
 KERNEL = "k_verify"  # the kernel that streams the logits (and draws) in the timed workload
-COUNTERS = ROOT / "profiles" / f"{KERNEL}_zipf_bf16_b64_counters.json"
-# the sources of the verification kernels (the counter summary is tied to their hash)
-SOURCES = [ROOT / "rejection_sampling_verify_02_amd" / "csrc" / n for n in ("spec_verify.hip", "sv_device.h")]
+_CSRC = ROOT / "rejection_sampling_verify_02_amd" / "csrc"
+_SHARED = ("sv_common.h", "sv_device.h", "sv_lanes.h")
+# Per timed operation: the kernel whose HBM traffic is summarised, the workload the counters
+# are taken on, its algorithmic bytes per launch, and the sources the summary is tied to
+# (by hash: a summary taken on other sources is not used).
+COUNTED = {
+    "verify": dict(kernel="k_verify", workload="zipf_bf16_b64", desc="B=64, G=4, V=128256, bf16",
+                   alg=147750912, sources=("spec_verify.hip",) + _SHARED),
+    "overlap": dict(kernel="k_overlap", workload="overlap_zipf_bf16_b64", desc="B=64, G=4, V=128256, bf16",
+                    alg=131334144, sources=("spec_overlap.hip",) + _SHARED),
+    "sample": dict(kernel="k_verify", workload="sample_bf16_b256", desc="B=256, V=128256, bf16",
+                   alg=65667072, sources=("spec_verify.hip",) + _SHARED),
+}
+
+
+def counters_path(op: str) -> Path:
+    c = COUNTED[op]
+    return ROOT / "profiles" / f"{c['kernel']}_{c['workload']}_counters.json"
 
 
 def log(msg: str) -> None:
@@ -134,13 +149,14 @@ def make_sets(cid: int, n_sets: int, dev):
     return sets, host
 
 
-def counters_traffic(kernel_source_sha: str):
-    """HBM bytes per launch of KERNEL from the committed rocprofv3 counter summary, or None
-    when the summary is missing or was taken on a different kernel source."""
-    if not COUNTERS.exists():
+def counters_traffic(op: str):
+    """HBM bytes per launch of the operation's kernel from its committed rocprofv3 counter
+    summary, or None when the summary is missing or was taken on a different source."""
+    path = counters_path(op)
+    if not path.exists():
         return None, "no counter summary"
-    c = json.loads(COUNTERS.read_text())
-    if c.get("source_sha256") != kernel_source_sha:
+    c = json.loads(path.read_text())
+    if c.get("source_sha256") != source_sha(op):
         return None, "kernel changed since the counters were taken"
     return float(c["traffic_bytes_per_launch"]), c.get("note", "")
 
@@ -167,7 +183,7 @@ def cpu_baseline(host_sets, cfg, seconds: float):
                       f"{el:.1f} s; the oracle stops reading each sequence at its first rejection"}
 
 
-def summarize_counters(kdir: str, cdir: str, out: Path) -> None:
+def summarize_counters(kdir: str, cdir: str, op: str) -> None:
     """Turn rocprofv3 --pmc CSV output into the traffic summary bench.py reads.
 
     kdir holds the FETCH_SIZE and WRITE_SIZE runs of the benchmark, cdir those of the
@@ -189,9 +205,11 @@ def summarize_counters(kdir: str, cdir: str, out: Path) -> None:
 
     # the timed workload's dispatches: the most frequent grid among the kernel's dispatches
     # (the draft-token draws that prepare the inputs launch it on another grid)
-    grids = [int(r.get("Grid_Size") or 0) for r in rows_of(kdir, "FETCH_SIZE") if KERNEL in r["Kernel_Name"]]
+    spec = COUNTED[op]
+    kernel = spec["kernel"]
+    grids = [int(r.get("Grid_Size") or 0) for r in rows_of(kdir, "FETCH_SIZE") if kernel in r["Kernel_Name"]]
     main_grid = max(set(grids), key=grids.count) if grids else -1
-    is_main = lambda r: KERNEL in r["Kernel_Name"] and int(r.get("Grid_Size") or 0) == main_grid
+    is_main = lambda r: kernel in r["Kernel_Name"] and int(r.get("Grid_Size") or 0) == main_grid
     is_copy = lambda r: ("copy" in r["Kernel_Name"].lower() or "elementwise" in r["Kernel_Name"].lower())
     probe = json.loads(open(os.path.join(cdir, "probe.json")).read())
     nbytes = probe["copy_probe_bytes"]
@@ -204,17 +222,17 @@ def summarize_counters(kdir: str, cdir: str, out: Path) -> None:
     f_fetch, f_write = nbytes / copy_f, nbytes / copy_w
     fetch = float(np.median(kf)) * 1024.0 * f_fetch
     write = float(np.median(kw)) * 1024.0 * f_write
-    res = {"kernel": KERNEL, "workload": "zipf_bf16_b64 (B=64, G=4, V=128256, bf16)",
+    res = {"kernel": kernel, "workload": f"{spec['workload']} ({spec['desc']})",
            "dispatches": {"fetch": len(kf), "write": len(kw)},
            "fetch_kib_median": float(np.median(kf)), "write_kib_median": float(np.median(kw)),
            "copy_probe_bytes": nbytes, "copy_fetch_kib": max(cf), "copy_write_kib": max(cw),
            "scale_fetch": f_fetch, "scale_write": f_write,
            "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
            "traffic_bytes_per_launch": fetch + write,
-           "algorithmic_bytes": 147750912,
-           "source_sha256": source_sha(),
+           "algorithmic_bytes": spec["alg"],
+           "source_sha256": source_sha(op),
            "note": "FETCH_SIZE and WRITE_SIZE from separate rocprofv3 --pmc runs, scaled by a plain copy"}
-    out.write_text(json.dumps(res, indent=1) + "\n")
+    counters_path(op).write_text(json.dumps(res, indent=1) + "\n")
     print(json.dumps(res))
 
 
@@ -281,10 +299,10 @@ def roofline(per_kernel, kernel, alg_bytes, traffic):
             "algorithmic_bytes": alg_bytes, "avg_launch_us": round(main_us, 3)}
 
 
-def source_sha() -> str:
+def source_sha(op: str = "verify") -> str:
     h = hashlib.sha256()
-    for p in SOURCES:
-        h.update(p.read_bytes())
+    for n in COUNTED[op]["sources"]:
+        h.update((_CSRC / n).read_bytes())
     return h.hexdigest()
 
 
@@ -330,7 +348,7 @@ def run_verify(args, dev, hev):
     ms = wall * 1e3 / K
     t_call = ms / 1e3
     kernel = "k_argmax" if greedy else KERNEL  # the kernel that streams the logits
-    traffic, tnote = counters_traffic(source_sha()) if args.config == 3 else (None, "counters are taken on workload 3")
+    traffic, tnote = counters_traffic("verify") if args.config == 3 else (None, "counters are taken on workload 3")
     res = {
         "metric": METRIC, "value": round(B * G / t_call, 1), "unit": "positions/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
@@ -403,7 +421,7 @@ def run_sample(args, dev, hev):
         "gpu_event_ms_per_step": round(gpu_ms / K, 5),
         "per_kernel_us": {k: round(v, 3) for k, v in per_kernel.items()},
         "ms_per_step_with_kernel_events": None if wall2 is None else round(wall2 * 1e3 / K, 5),
-        "roofline": roofline(per_kernel, KERNEL, alg_bytes, None),
+        "roofline": roofline(per_kernel, KERNEL, alg_bytes, counters_traffic("sample")[0]),
     }
     if not args.no_cpu_baseline:
         import oracle
@@ -425,13 +443,87 @@ def run_sample(args, dev, hev):
     return res
 
 
+def run_overlap(args, dev, hev):
+    """beta and tv of every drafted position of the headline batch (B=64, G=4, V=128256
+    bf16, T=1), in the verification layout: positions per second."""
+    import torch
+    import rejection_sampling_verify_02_amd as sv
+    from rejection_sampling_verify_02_amd import workloads as wl
+    import oracle
+
+    cfg = wl.CONFIGS[3]
+    B, G, V = cfg.B, cfg.G, cfg.V
+    esz = 2 if cfg.dtype == "bf16" else 4
+    alg_bytes = 2 * B * G * V * esz  # one read of target row i and draft row i per position
+    n_sets = args.sets or max(2, -(-(1 << 30) // alg_bytes))
+    log(f"[bench] overlap on {cfg.name}: B={B} G={G} V={V} {cfg.dtype}, {alg_bytes / 1e6:.2f} MB per call, "
+        f"{n_sets} input sets")
+    sets, host = [], []
+    for s in range(n_sets):
+        target, draft = wl.zipf_gauss(B, G, V, cfg.dtype, cfg.draft_noise, cfg.seed + 1000 * s)
+        conv = (lambda a: torch.from_numpy(a).view(torch.bfloat16).to(dev)) if cfg.dtype == "bf16" \
+            else (lambda a: torch.from_numpy(a).to(dev))
+        sets.append((conv(target), conv(draft)))
+        host.append((target, draft))
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    dtc = sv.SV_BF16 if cfg.dtype == "bf16" else sv.SV_F32
+    plan = sv.sv_overlap_launch_plan(B, G, V, dtc, cfg.temperature, cfg.top_k)
+    ws = sv.Workspace()
+    outs = (torch.empty((B, G), dtype=torch.float64, device=dev),
+            torch.empty((B, G), dtype=torch.float64, device=dev),
+            torch.empty((B, G), dtype=torch.int32, device=dev))
+
+    def call(i, events=None):
+        t, d = sets[i % n_sets]
+        return sv.spec_overlap(t, d, cfg.temperature, cfg.top_k, workspace=ws, stream=stream, out=outs,
+                               events=events)
+
+    K = args.steps
+    wall, gpu_ms, per_kernel, wall2 = time_loop(call, plan, K, args.warmup, stream, dev, hev,
+                                                not args.no_stage_events)
+    t_call = wall / K
+    res = {
+        "metric": "overlap (beta, tv) positions/sec and achieved HBM GB/s (% of peak) at B=64,V=128k",
+        "value": round(B * G / t_call, 1), "unit": "positions/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(t_call * 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "overlap_" + cfg.name, "B": B, "G": G, "V": V, "logits": cfg.dtype,
+                   "temperature": cfg.temperature, "top_k": cfg.top_k, "input_sets": n_sets,
+                   "set_bytes": alg_bytes},
+        "call_GBs": round(alg_bytes / t_call / 1e9, 1),
+        "call_frac_of_peak": round(alg_bytes / t_call / 1e9 / PEAK_HBM_GBS, 4),
+        "mean_beta": round(float(outs[0].mean().item()), 5),
+        "gpu_event_ms_per_step": round(gpu_ms / K, 5),
+        "per_kernel_us": {k: round(v, 3) for k, v in per_kernel.items()},
+        "ms_per_step_with_kernel_events": None if wall2 is None else round(wall2 * 1e3 / K, 5),
+        "roofline": roofline(per_kernel, "k_overlap", alg_bytes, counters_traffic("overlap")[0]),
+    }
+    if not args.no_cpu_baseline:
+        oracle._load()
+        threads = oracle.default_threads()
+        calls, t0 = 0, time.perf_counter()
+        while True:
+            t, d = host[calls % len(host)]
+            oracle.overlap(t, d, cfg.temperature, cfg.top_k, nthreads=threads)
+            calls += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds:
+                break
+        res["cpu_baseline"] = {"value": B * G * calls / el, "unit": "positions/s", "cores": threads,
+                               "kind": "oracle", "sample": f"{calls} full calls (B={B}, G={G}, V={V}) over "
+                                                           f"{min(calls, len(host))} input sets, {el:.1f} s"}
+    else:
+        res["cpu_baseline"] = None
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--op", default="verify", choices=["verify", "sample"],
-                    help="verify (the default, the headline) or the batched sampler")
+    ap.add_argument("--op", default="verify", choices=["verify", "sample", "overlap"],
+                    help="verify (the default, the headline), the batched sampler, or the per-position overlap")
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5],
                     help="verification workload (3, the default, is the headline; 4 greedy and 5 top-k "
                          "are timed for the design notes)")
@@ -443,7 +535,7 @@ def main() -> int:
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES (counter calibration)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("BENCH_DIR", "COPY_DIR"),
-                    help="write the traffic summary from rocprofv3 --pmc CSV directories")
+                    help="write the traffic summary of --op from rocprofv3 --pmc CSV directories")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -454,7 +546,7 @@ def main() -> int:
         copy_probe(args.copy_probe, 10)
         return 0
     if args.summarize_counters:
-        summarize_counters(args.summarize_counters[0], args.summarize_counters[1], COUNTERS)
+        summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.op)
         return 0
 
     import torch
@@ -463,7 +555,8 @@ def main() -> int:
     sv.load_library()  # raises if the HIP library is not built
     dev = torch.device("cuda:0")
     hev = HipEvents()
-    res = run_sample(args, dev, hev) if args.op == "sample" else run_verify(args, dev, hev)
+    run = {"sample": run_sample, "overlap": run_overlap}.get(args.op, run_verify)
+    res = run(args, dev, hev)
     print(json.dumps(res), flush=True)
     return 0
 

@@ -166,6 +166,52 @@ sv_status spec_sample_timed(const void *logits, sv_dtype dtype, const float *u, 
                             void *stream, void *const *events, int32_t n_events,
                             int32_t *n_launched);
 
+/* ---- overlap of target and draft at every drafted position ----
+ *
+ * For each sequence b and drafted position i, the two distributions the verification
+ * compares there, p_i (target row i) and q_i (draft row i), after the same temperature
+ * and top-k as in spec_verify:
+ *   beta[b, i] = sum_v min(p_i(v), q_i(v))   the position's acceptance probability
+ *                ("Speculative Decoding 的朴素思想", section "为什么接受概率恰好是这个比值";
+ *                the overlap 1 - TV behind the LK loss -log beta and DSpark's label
+ *                c* = 1 - ||p - q||_1 / 2 on "推测解码：接受规则、状态与收益边界")
+ *   tv[b, i]   = sum_v max(p_i(v) - q_i(v), 0)  the rejection mass Z, summed from its own
+ *                terms (not as 1 - beta) so that small distances keep their precision.
+ *   target_logits [B, target_rows, V] dtype  target_rows = G + 1 (the verification's
+ *                                            layout; row G is not read) or G
+ *   draft_logits  [B, G, V] dtype
+ *   temperature   T > 0 (T == 0 is SV_ERR_TEMPERATURE: greedy has no distribution)
+ *   top_k         as in spec_verify
+ *   beta, tv      [B, G] float64 out; NaN for a pair with a code
+ *   pair_status   [B, G] int32 out: 0, SV_ROW_BAD_LOGITS (either row holds NaN or +inf,
+ *                 or has no finite kept logit) or SV_ROW_INTERNAL
+ *   workspace     at least sv_overlap_workspace_bytes(...) bytes, 256-byte aligned, first
+ *                 sv_overlap_workspace_zero_bytes(...) bytes zero, under the same rules
+ *                 as spec_verify's workspace (one workspace may serve both).
+ * G == 0 returns SV_OK and enqueues nothing.  Other statuses as for spec_verify;
+ * target_rows other than G or G + 1 is SV_ERR_SHAPE. */
+size_t sv_overlap_workspace_bytes(int32_t B, int32_t G, int32_t V, sv_dtype dtype,
+                                  float temperature, int32_t top_k);
+size_t sv_overlap_workspace_zero_bytes(int32_t B, int32_t G, int32_t V, sv_dtype dtype,
+                                       float temperature, int32_t top_k);
+sv_status spec_overlap(const void *target_logits, const void *draft_logits, sv_dtype dtype,
+                       int32_t B, int32_t G, int32_t V, int32_t target_rows, float temperature,
+                       int32_t top_k, double *beta, double *tv, int32_t *pair_status,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* spec_overlap with each kernel dispatch bracketed by caller-owned HIP events, as in
+ * spec_verify_timed. */
+sv_status spec_overlap_timed(const void *target_logits, const void *draft_logits, sv_dtype dtype,
+                             int32_t B, int32_t G, int32_t V, int32_t target_rows,
+                             float temperature, int32_t top_k, double *beta, double *tv,
+                             int32_t *pair_status, void *workspace, size_t workspace_bytes,
+                             void *stream, void *const *events, int32_t n_events,
+                             int32_t *n_launched);
+
+/* Names of the kernels spec_overlap would launch, ';'-separated (static storage). */
+const char *sv_overlap_launch_plan(int32_t B, int32_t G, int32_t V, sv_dtype dtype,
+                                   float temperature, int32_t top_k);
+
 /* Human-readable text of a status (static storage). */
 const char *sv_status_string(sv_status status);
 

@@ -26,7 +26,9 @@ _STATUS = {0: "SV_OK", 1: "SV_ERR_NULL", 2: "SV_ERR_SHAPE", 3: "SV_ERR_DTYPE",
            4: "SV_ERR_TEMPERATURE", 5: "SV_ERR_WORKSPACE", 6: "SV_ERR_ALIGN", 7: "SV_ERR_LAUNCH"}
 
 EXPORTED = ("spec_verify", "spec_verify_timed", "sv_workspace_bytes", "sv_workspace_zero_bytes",
-            "sv_status_string", "sv_launch_plan", "spec_sample", "spec_sample_timed")
+            "sv_status_string", "sv_launch_plan", "spec_sample", "spec_sample_timed",
+            "spec_overlap", "spec_overlap_timed", "sv_overlap_workspace_bytes",
+            "sv_overlap_workspace_zero_bytes", "sv_overlap_launch_plan")
 
 
 class SpecVerifyError(RuntimeError):
@@ -58,6 +60,16 @@ def load_library(path: Path | str | None = None) -> ctypes.CDLL:
     lib.spec_sample.restype = I32
     lib.spec_sample_timed.argtypes = smp + [V, I32, V]
     lib.spec_sample_timed.restype = I32
+    ovl = [V, V, I32, I32, I32, I32, I32, F32, I32, V, V, V, V, SZ, V]
+    lib.spec_overlap.argtypes = ovl
+    lib.spec_overlap.restype = I32
+    lib.spec_overlap_timed.argtypes = ovl + [V, I32, V]
+    lib.spec_overlap_timed.restype = I32
+    for fn in (lib.sv_overlap_workspace_bytes, lib.sv_overlap_workspace_zero_bytes):
+        fn.argtypes = [I32, I32, I32, I32, F32, I32]
+        fn.restype = SZ
+    lib.sv_overlap_launch_plan.argtypes = [I32, I32, I32, I32, F32, I32]
+    lib.sv_overlap_launch_plan.restype = ctypes.c_char_p
     lib.sv_workspace_bytes.argtypes = [I32, I32, I32, I32, F32, I32]
     lib.sv_workspace_bytes.restype = SZ
     lib.sv_workspace_zero_bytes.argtypes = [I32, I32, I32, I32, F32, I32]
@@ -87,6 +99,12 @@ def sv_workspace_zero_bytes(B: int, G: int, V: int, dtype: int, temperature: flo
 def sv_launch_plan(B: int, G: int, V: int, dtype: int, temperature: float, top_k: int = 0) -> list[str]:
     s = load_library().sv_launch_plan(B, G, V, dtype, float(temperature), int(top_k)).decode()
     return s.split(";")
+
+
+def sv_overlap_launch_plan(B: int, G: int, V: int, dtype: int, temperature: float,
+                          top_k: int = 0) -> list[str]:
+    s = load_library().sv_overlap_launch_plan(B, G, V, dtype, float(temperature), int(top_k)).decode()
+    return s.split(";") if s else []
 
 
 # ------------------------------------------------------------------ workspace
@@ -270,3 +288,50 @@ def spec_sample(logits, u, temperature: float, top_k: int = 0, *, workspace: Wor
         raise SpecVerifyError(rc, sv_status_string(rc))
     wso.called(dev, zbytes)
     return (tok, st) if events is None else (tok, st, nl)
+
+
+def spec_overlap(target_logits, draft_logits, temperature: float, top_k: int = 0, *,
+                 workspace: Workspace | None = None, stream=None, out=None, events=None):
+    """Per-position overlap on the GPU (see include/spec_verify.h): for target [B, TR, V]
+    (TR = G + 1, the verification layout, or G) and draft [B, G, V] logits (bfloat16 or
+    float32), returns (beta, tv, status): beta = sum min(p, q) and tv = sum [p - q]_+ as
+    [B, G] float64 tensors and the pair status [B, G] int32.  ``out`` may supply the three
+    tensors; ``events`` as for spec_verify."""
+    import torch
+    lib = load_library()
+    dev = target_logits.device
+    if dev.type != "cuda":
+        raise ValueError("logits must be device tensors")
+    dt = _dtype_code(target_logits)
+    if target_logits.dim() != 3 or draft_logits is None or draft_logits.dim() != 3:
+        raise ValueError("target must be [B, TR, V] and draft [B, G, V]")
+    B, G, V = draft_logits.shape
+    TR = target_logits.shape[1]
+    _check(target_logits, "target_logits", (B, TR, V), target_logits.dtype, dev)
+    _check(draft_logits, "draft_logits", (B, G, V), target_logits.dtype, dev)
+    if out is not None:
+        beta, tv, st = out
+    else:
+        beta = torch.empty((B, G), dtype=torch.float64, device=dev)
+        tv = torch.empty((B, G), dtype=torch.float64, device=dev)
+        st = torch.empty((B, G), dtype=torch.int32, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    nbytes = int(lib.sv_overlap_workspace_bytes(B, G, V, dt, float(temperature), int(top_k)))
+    zbytes = int(lib.sv_overlap_workspace_zero_bytes(B, G, V, dt, float(temperature), int(top_k)))
+    wso = workspace or _default_ws
+    ws = wso.get(nbytes, zbytes, dev, stream)
+    args = [_ptr(target_logits), _ptr(draft_logits), dt, B, G, V, TR, float(temperature), int(top_k),
+            _ptr(beta), _ptr(tv), _ptr(st), _ptr(ws), ws.numel(), ctypes.c_void_p(stream)]
+    if events is None:
+        rc = lib.spec_overlap(*args)
+        nl = None
+    else:
+        arr = (ctypes.c_void_p * len(events))(*events)
+        n = ctypes.c_int32(0)
+        rc = lib.spec_overlap_timed(*args, arr, len(events), ctypes.byref(n))
+        nl = n.value
+    if rc != 0:
+        raise SpecVerifyError(rc, sv_status_string(rc))
+    wso.called(dev, zbytes)
+    return (beta, tv, st) if events is None else (beta, tv, st, nl)

@@ -44,7 +44,7 @@
 #include <atomic>
 
 #include "spec_verify.h"
-#include "sv_device.h"
+#include "sv_common.h"
 
 namespace sv {
 
@@ -61,147 +61,6 @@ enum : int {
   JW_OFF_J,                                                  // rejection: row offset of p_j
   JW_USED, JW = 16
 };
-
-// ---------------------------------------------------------------- arguments
-
-struct Work {                  // carved from the caller's workspace
-  // tagged words (see tw_put)
-  u64 *tw_part;                // [R*C*3] per chunk: sampling offset m_c*k2 and sum of
-                               //   2^(z*k2 - off) (head, tail); greedy best value, index, flags
-  u64 *tw_zx;                  // [R] the row's logit at its position's drafted token
-  u64 *tw_job;                 // [B*JW] the acceptance scan's record for the draw
-  u64 *tw_seg;                 // [B*C*SEGS*2] residual mass per 64-vector segment (head, tail)
-  u64 *tw_gseg;                // [B*C*SEGS*2] the bonus row's mass per segment (head, tail)
-  u64 *tw_hist;                // [R*C*128] top-k digit histogram per chunk (16-bit counts)
-  // plain, handed from one kernel to the next
-  float *row_tau;              // [R] top-k threshold (raw logit)
-  uint2 *tk_state;             // [R] radix-select prefix and remaining rank
-};
-
-struct Args {
-  const void *target, *draft;
-  const int32_t *tokens;
-  const float *u_accept, *u_sample;
-  int B, G, V, C, nvec, rps;   // rps: rows per sequence (2G+1 sampling, G+1 greedy)
-  float k2;                    // log2(e) / T, the one rounding of the temperature used everywhere
-  int top_k;
-  int32_t *accepted_len, *out_tokens;
-  float *row_stats;
-  unsigned tag;                // this call's tag (never 0): marks the words it publishes
-  unsigned spin_limit;         // polls a waiting wave makes before giving up
-  Work w;
-};
-
-// Row j of sequence b: rows 0..G are target rows 0..G, rows G+1..2G draft rows 0..G-1.
-template <typename T>
-SVD const T *seq_row(const Args &a, int b, int j) {
-  if (j <= a.G) return static_cast<const T *>(a.target) + ((size_t)b * (a.G + 1) + j) * (size_t)a.V;
-  return static_cast<const T *>(a.draft) + ((size_t)b * a.G + (j - a.G - 1)) * (size_t)a.V;
-}
-
-// ---------------------------------------------------------------- top-k threshold
-
-// One radix-select digit (bits [shift, shift+8) of the key) for every row.  The prefix
-// of higher digits and the remaining rank come from the previous pass.  The threshold
-// kept in row_tau is the smallest value whose key has the final prefix, so the kept set
-// {z >= tau} is exactly the values >= the k-th largest, ties included.  Each chunk
-// publishes its digit histogram as 128 tagged words (two 16-bit counts each; a chunk
-// holds at most 16384 values); the row's last chunk in grid order collects them.
-// The first pass counts its histogram in HREP copies, lane l adding into copy l % HREP:
-// logits crowd into a few leading digits (the exponent), and one copy would make a whole
-// wave's LDS atomics land on the same address one after another.  Later passes count
-// only the values that carry the prefix found so far, few per chunk: one copy.
-template <typename T, bool ALIGNED, int HREP>
-__global__ __launch_bounds__(NT) void k_topk_digit(const Args a, int pass, int last_pass) {
-  constexpr int VEC = Fmt<T>::VEC;
-  __shared__ unsigned hist[256 * HREP];
-  __shared__ unsigned s_ge[256];
-  __shared__ int s_alive;
-  const int tid = threadIdx.x;
-  int phase, xi;
-  if (!lane_item((int)(a.B * a.rps), a.C, 0, phase, xi)) return;  // units: rows
-  const int r = xi / a.C, c = xi - r * a.C;
-  const int b = r / a.rps, jr = r - b * a.rps;
-  const int shift = 24 - 8 * pass;
-  const uint2 st = (pass == 0) ? make_uint2(0u, (unsigned)a.top_k) : a.w.tk_state[r];
-  const uint32_t hi_mask = (pass == 0) ? 0u : (0xffffffffu << (shift + 8));
-  const unsigned tag = a.tag;
-
-  for (int i = tid; i < 256 * HREP; i += NT) hist[i] = 0u;
-  __syncthreads();
-  float x[VPT][VEC];
-  load_chunk<T, ALIGNED, true>(seq_row<T>(a, b, jr), a.V, a.nvec, c, tid, x);
-  const unsigned rep = (unsigned)tid & (HREP - 1);
-#pragma unroll
-  for (int k = 0; k < VPT; ++k)
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      if (elem_index<T>(c, k, tid, e) < a.V) {
-        const uint32_t key = f2key(x[k][e]);
-        if ((key & hi_mask) == (st.x & hi_mask)) atomicAdd(&hist[((key >> shift) & 255u) * HREP + rep], 1u);
-      }
-    }
-  __syncthreads();
-  if (HREP > 1) {  // fold the copies: thread d owns digit d
-    unsigned h = 0;
-#pragma unroll
-    for (int r2 = 0; r2 < HREP; ++r2) h += hist[tid * HREP + ((r2 + tid) & (HREP - 1))];
-    __syncthreads();
-    hist[tid] = h;
-    __syncthreads();
-  }
-  u64 *hw = a.w.tw_hist + (size_t)r * a.C * 128;
-  if (c != a.C - 1) {
-    if (tid < 128) tw_put(&hw[(size_t)c * 128 + tid], tag, hist[2 * tid] | (hist[2 * tid + 1] << 16));
-    return;
-  }
-
-  // The row's last chunk: wait for the other chunks' histograms (every load in flight
-  // at once), then the row total of digit d = tid.
-  unsigned tot = 0;
-  unsigned polls = 0;
-  for (;;) {
-    tot = hist[tid];
-    bool ok = true;
-    for (int cc = 0; cc < a.C - 1; ++cc) {
-      const u64 w = ld_dev(&hw[(size_t)cc * 128 + (tid >> 1)]);
-      ok = ok && tw_ok(w, tag);
-      tot += ((unsigned)w >> ((tid & 1) * 16)) & 0xffffu;
-    }
-    if (__syncthreads_and(ok ? 1 : 0)) break;
-    if (++polls >= a.spin_limit) break;
-    __builtin_amdgcn_s_sleep(2);
-  }
-  // A row whose collector gave up (here or in an earlier pass) carries a marker to the
-  // end: tk_state (~0, ~0), then a NaN threshold, which the scan reports as an error.
-  const bool dead = st.x == 0xffffffffu && st.y == 0xffffffffu;
-  if (tid == 0) s_alive = polls < a.spin_limit && !dead;
-  s_ge[tid] = tot;
-  __syncthreads();
-  if (!s_alive) {
-    if (tid == 0) {
-      if (last_pass) a.w.row_tau[r] = NAN;
-      else a.w.tk_state[r] = make_uint2(0xffffffffu, 0xffffffffu);
-    }
-    return;
-  }
-  for (int o = 1; o < 256; o <<= 1) {  // suffix sums (Hillis-Steele)
-    const unsigned add = (tid + o < 256) ? s_ge[tid + o] : 0u;
-    __syncthreads();
-    s_ge[tid] += add;
-    __syncthreads();
-  }
-  // The chosen digit is the largest d whose suffix count reaches the remaining rank.
-  const unsigned krem = st.y;
-  const bool reach = s_ge[tid] >= krem;
-  const bool next_reach = (tid < 255) ? (s_ge[tid + 1] >= krem) : false;
-  if (reach && !next_reach) {
-    const unsigned above = (tid < 255) ? s_ge[tid + 1] : 0u;
-    const uint32_t prefix = (st.x & hi_mask) | ((uint32_t)tid << shift);
-    if (last_pass) a.w.row_tau[r] = key2f(prefix);
-    else a.w.tk_state[r] = make_uint2(prefix, krem - above);
-  }
-}
 
 // ---------------------------------------------------------------- acceptance scan
 
@@ -1306,11 +1165,22 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(5))) void k_
 
 // ======================================================================== host side
 
+namespace sv_host {
+
+std::atomic<unsigned> g_tag{0};
+unsigned next_tag() {
+  unsigned t = g_tag.fetch_add(1u, std::memory_order_relaxed) + 1u;
+  while (t == 0u) t = g_tag.fetch_add(1u, std::memory_order_relaxed) + 1u;
+  return t;
+}
+
+}  // namespace sv_host
+
 namespace {
 
 using namespace sv;
-
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+using sv_host::align256;
+using sv_host::next_tag;
 
 struct Plan {
   bool greedy, topk, aligned;
@@ -1363,38 +1233,17 @@ const char *kPlanNames[] = {
     "k_argmax",
 };
 
-// Every launch gets its own tag, so a word left by an earlier launch can never pass
-// for this one's.  0 is never used (a clean workspace holds zeros).
-std::atomic<unsigned> g_tag{0};
-unsigned next_tag() {
-  unsigned t = g_tag.fetch_add(1u, std::memory_order_relaxed) + 1u;
-  while (t == 0u) t = g_tag.fetch_add(1u, std::memory_order_relaxed) + 1u;
-  return t;
-}
-
 template <typename T, bool AL>
 hipError_t launch_all(const Plan &p, const Args &a, hipStream_t st, void *const *ev, int nev,
                       int *nl) {
-  const dim3 blk(NT);
   // Grids padded to whole lanes of units (see lane_item): rows for the top-k passes,
   // sequences for k_argmax and k_verify.
   const long long lb = (a.B + LANES - 1) / LANES, lr = (p.R + LANES - 1) / LANES;
   const unsigned topk_grid = (unsigned)(LANES * lr * p.C);
   const unsigned argmax_grid = (unsigned)(LANES * lb * p.rps * p.C);
   const unsigned verify_grid = (unsigned)(LANES * lb * ((long long)p.rps * p.C + (a.G > 0 ? (long long)p.C * NSUB : 0)));
-  int n = 0;
-  hipError_t e = hipSuccess;
-  // With events, kernel i is launched with (events[2i], events[2i+1]) as its start and
-  // stop events, which time the dispatch itself without extra packets on the stream.
-  auto go = [&](const void *fn, unsigned grid, void **args) {
-    if (e != hipSuccess) return;
-    if (ev && 2 * n + 1 < nev)
-      e = hipExtLaunchKernel(fn, dim3(grid), blk, args, 0, st, (hipEvent_t)ev[2 * n],
-                             (hipEvent_t)ev[2 * n + 1], 0);
-    else
-      e = hipLaunchKernel(fn, dim3(grid), blk, args, 0, st);
-    if (e == hipSuccess) ++n;
-  };
+  sv_host::Launcher L{st, ev, nev};
+  auto go = [&](const void *fn, unsigned grid, void **args) { L.go(fn, grid, args); };
   Args aa = a;
   if (p.greedy) {
     aa.tag = next_tag();
@@ -1420,8 +1269,8 @@ hipError_t launch_all(const Plan &p, const Args &a, hipStream_t st, void *const 
          verify_grid, args);
     }
   }
-  if (nl) *nl = n;
-  return e;
+  if (nl) *nl = L.n;
+  return L.e;
 }
 
 sv_status run(const void *target, const void *draft, sv_dtype dt, const int32_t *tokens,
@@ -1457,11 +1306,16 @@ sv_status run(const void *target, const void *draft, sv_dtype dt, const int32_t 
   a.C = p.C;
   a.nvec = p.nvec;
   a.rps = p.rps;
+  a.ntr = G + 1;
+  a.tgt_rows = G + 1;
   a.k2 = sampling ? (float)(LOG2E / (double)T) : 0.0f;
   a.top_k = top_k;
   a.accepted_len = acc;
   a.out_tokens = out;
   a.row_stats = sampling ? row_stats : nullptr;
+  a.beta = a.tv = nullptr;
+  a.pair_status = nullptr;
+  a.lag = 0;
   a.tag = 0u;  // each launch takes its own
   a.spin_limit = SPIN_LIMIT;
   a.w.tw_part = (u64 *)(base + p.tw_part);
@@ -1470,6 +1324,7 @@ sv_status run(const void *target, const void *draft, sv_dtype dt, const int32_t 
   a.w.tw_seg = (u64 *)(base + p.tw_seg);
   a.w.tw_gseg = (u64 *)(base + p.tw_gseg);
   a.w.tw_hist = (u64 *)(base + p.tw_hist);
+  a.w.tw_ov = nullptr;
   a.w.row_tau = (float *)(base + p.row_tau);
   a.w.tk_state = (uint2 *)(base + p.tk_state);
 

@@ -7,6 +7,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "sv_lanes.h"
+
 #define SVD __device__ __forceinline__
 
 namespace sv {
@@ -437,35 +439,13 @@ SVD int wave_pick4_frac(int n, double u, const MFn &mfn, double *t_rem, double *
 
 // ---------------------------------------------------------------- block placement
 
-// The device hands workgroups to its XCDs round-robin (blockIdx % 8), each XCD in
-// blockIdx order.  Work comes in UNITS (a row, or a sequence) of per1 first-phase items
-// and per2 second-phase items, and the last items of a unit wait for the earlier ones.
-// Block p runs item q = p / LANES of lane k = p % LANES; lane k owns units k, k+LANES, ...
-// and runs all their first-phase items, unit after unit, then all their second-phase
-// items.  So each XCD streams whole units front to back, the waiting items (a unit's
-// last ones) are spread over every XCD instead of all landing on one, and every wait is
-// for an earlier item of the same lane, i.e. a smaller blockIdx: the grid cannot stall,
-// wherever the blocks run.  Returns false for the padding blocks of short lanes.
-constexpr int LANES = 8;
-
+// Block p's item of the grid (see sv_lanes.h for the placement and why).
 SVD bool lane_item(int units, int per1, int per2, int &phase, int &item) {
-  const int p = (int)blockIdx.x;
-  const int k = p % LANES, q = p / LANES;
-  const int nu = (units > k) ? (units - k + LANES - 1) / LANES : 0;
-  if (q < nu * per1) {
-    const int s = q / per1;
-    item = (k + LANES * s) * per1 + (q - s * per1);
-    phase = 1;
-    return true;
-  }
-  const int q2 = q - nu * per1;
-  if (q2 < nu * per2) {
-    const int s = q2 / per2;
-    item = (k + LANES * s) * per2 + (q2 - s * per2);
-    phase = 2;
-    return true;
-  }
-  return false;
+  return lane_decode((int)blockIdx.x, units, per1, per2, phase, item);
+}
+
+SVD bool lane_item_lag(int units, int per1, int per2, int lag, int &phase, int &unit, int &sub) {
+  return lane_decode_lag((int)blockIdx.x, units, per1, per2, lag, phase, unit, sub);
 }
 
 // Largest value wins, ties go to the lower index; NaN and +inf mark the row unusable.

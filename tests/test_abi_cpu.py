@@ -138,3 +138,48 @@ def test_sample_greedy_reads_no_uniform(lib):
     # stops at the workspace check, after the pointer checks passed without u
     assert call_sample(lib, T=0.0, u=None, nbytes=16) == 5
     assert sv.sv_launch_plan(256, 0, 128256, sv.SV_BF16, 1.0, 0) == ["k_verify"]
+
+
+def call_overlap(lib, **kw):
+    a = dict(t=FAKE, d=FAKE, dt=sv.SV_BF16, B=4, G=3, V=1024, TR=4, T=1.0, k=0, beta=FAKE, tv=FAKE,
+             st=FAKE, ws=FAKE, nbytes=1 << 30, stream=None)
+    a.update(kw)
+    return lib.spec_overlap(V_(a["t"]), V_(a["d"]), a["dt"], a["B"], a["G"], a["V"], a["TR"], F_(a["T"]),
+                            a["k"], V_(a["beta"]), V_(a["tv"]), V_(a["st"]), V_(a["ws"]), Z_(a["nbytes"]),
+                            V_(a["stream"]))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), 2), (dict(V=0), 2), (dict(G=-1), 2), (dict(TR=2), 2), (dict(TR=5), 2), (dict(dt=9), 3),
+    (dict(T=0.0), 4), (dict(T=-1.0), 4), (dict(T=float("nan")), 4), (dict(T=float("inf")), 4),
+    (dict(t=None), 1), (dict(d=None), 1), (dict(beta=None), 1), (dict(tv=None), 1), (dict(st=None), 1),
+    (dict(ws=None), 1), (dict(t=FAKE + 1), 6), (dict(d=FAKE + 1), 6), (dict(nbytes=16), 5),
+    (dict(ws=FAKE + 8), 5),
+])
+def test_overlap_host_argument_errors(lib, kw, status):
+    assert call_overlap(lib, **kw) == status
+
+
+def test_overlap_layouts_and_empty(lib):
+    # both target layouts pass the checks (stopped at the workspace check)
+    assert call_overlap(lib, TR=3, nbytes=16) == 5
+    assert call_overlap(lib, TR=4, nbytes=16) == 5
+    # no drafted positions: nothing to compute, nothing enqueued, no pointer needed
+    assert call_overlap(lib, G=0, TR=0, t=None, d=None, beta=None, tv=None, st=None, ws=None) == 0
+    assert sv.sv_overlap_launch_plan(4, 0, 1024, sv.SV_BF16, 1.0, 0) == []
+
+
+def test_overlap_plan_and_workspace(lib):
+    assert sv.sv_overlap_launch_plan(64, 4, 128256, sv.SV_BF16, 1.0, 0) == ["k_overlap"]
+    assert sv.sv_overlap_launch_plan(64, 4, 128256, sv.SV_BF16, 1.0, 50) == \
+        ["k_topk_digit", "k_topk_digit", "k_overlap"]
+    assert len(sv.sv_overlap_launch_plan(8, 5, 32000, sv.SV_F32, 0.7, 5)) == 5
+    args = (64, 4, 128256, sv.SV_BF16, 1.0, 0)
+    n, z = lib.sv_overlap_workspace_bytes(*args), lib.sv_overlap_workspace_zero_bytes(*args)
+    assert 0 < z <= n and z % 256 == 0 and n % 256 == 0
+    # per chunk of 512 rows: 3 partial words; per chunk of 256 pairs: 4 sum words
+    assert z == 512 * 8 * 3 * 8 + 256 * 8 * 4 * 8
+    a2 = (64, 4, 128256, sv.SV_BF16, 1.0, 50)
+    assert lib.sv_overlap_workspace_zero_bytes(*a2) < lib.sv_overlap_workspace_bytes(*a2)
+    assert lib.sv_overlap_workspace_zero_bytes(64, 4, 128256, sv.SV_BF16, 0.0, 0) == 0
+
