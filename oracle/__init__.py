@@ -19,6 +19,9 @@ arrays into it.  The functions and the passages they follow:
   section "一次 sampling 怎么执行", step 1); ``sample_rows`` is also the oracle of the
   library's batched sampler ``spec_sample``.
 * ``topk_threshold_rows`` / ``argmax_rows`` -- the top-k cut and greedy choice.
+* ``tree_verify`` -- verification of a draft tree by multi-step rejection (first page,
+  "Token Tree Verifier"; EAGLE page, section 6.2): siblings are tested in order against
+  the current distribution, which each rejection replaces by norm([cur - q]_+).
 * ``overlap`` -- per drafted position, beta = sum min(p, q) (the acceptance
   probability, first page, section "为什么接受概率恰好是这个比值"; the overlap behind the
   LK loss and DSpark's c* on the second page) and tv = sum [p - q]_+.
@@ -43,7 +46,7 @@ _LIB = _HERE / "libspec_verify_ref.so"
 
 F32, BF16 = 0, 1
 
-ERR_TOKEN, ERR_QZERO, ERR_ROW, ERR_UNIFORM = -1, -2, -3, -4
+ERR_TOKEN, ERR_QZERO, ERR_ROW, ERR_UNIFORM, ERR_TREE = -1, -2, -3, -4, -6
 
 
 def build(force: bool = True) -> Path:
@@ -76,6 +79,8 @@ def _bind(lib):
     lib.ref_argmax_rows.restype = i32
     lib.ref_overlap.argtypes = [P, P, i32, i32, i32, i32, i32, f64, i32, P, P, P, i32]
     lib.ref_overlap.restype = i32
+    lib.ref_tree_verify.argtypes = [P, P, i32, P, P, P, P, i32, i32, i32, f64, i32, P, P, P, P, P, i32]
+    lib.ref_tree_verify.restype = i32
     lib.ref_invcdf.argtypes = [P, i32, f64, P]
     lib.ref_invcdf.restype = i32
     return lib
@@ -212,6 +217,42 @@ def argmax_rows(logits):
     idx = np.empty((R,), np.int32)
     lib.ref_argmax_rows(_ptr(z), dt, R, V, _ptr(idx))
     return idx.reshape(z.shape[:-1])
+
+
+def tree_verify(target, draft, tokens, parent, u_accept, u_sample, temperature, top_k=0, *,
+                with_diagnostics=False, nthreads=None):
+    """Oracle verification of B draft trees of N nodes.
+
+    target [B, N, V] (p at every node) and draft [B, N, V] (q at every node; leaf rows
+    unused; may be None at temperature 0) logits, float32 or uint16 bf16 bits; tokens
+    and parent [B, N] int32 (parent[:, 0] = -1, parent[n] < n); u_accept [B, N] and
+    u_sample [B] float32 (None at temperature 0).  Returns (accepted_len [B], out_tokens
+    [B, N], path_nodes [B, N]) and, with diagnostics, a dict of accept_margin [B, N] and
+    sample_margin [B]."""
+    lib = _load()
+    target, dt = _logits(target)
+    B, N, V = target.shape
+    if draft is None:
+        draft = np.zeros_like(target)
+    draft, dt2 = _logits(draft)
+    assert dt2 == dt and draft.shape == (B, N, V)
+    tok = np.ascontiguousarray(tokens, np.int32).reshape(B, N)
+    par = np.ascontiguousarray(parent, np.int32).reshape(B, N)
+    ua = np.zeros((B, N), np.float32) if u_accept is None else np.ascontiguousarray(u_accept, np.float32)
+    us = np.zeros((B,), np.float32) if u_sample is None else np.ascontiguousarray(u_sample, np.float32)
+    acc = np.empty((B,), np.int32)
+    out = np.empty((B, N), np.int32)
+    path = np.empty((B, N), np.int32)
+    am = np.empty((B, N), np.float64)
+    sm = np.empty((B,), np.float64)
+    rc = lib.ref_tree_verify(_ptr(target), _ptr(draft), dt, _ptr(tok), _ptr(par), _ptr(ua), _ptr(us),
+                             B, N, V, float(temperature), int(top_k), _ptr(acc), _ptr(out), _ptr(path),
+                             _ptr(am), _ptr(sm), int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    if with_diagnostics:
+        return acc, out, path, {"accept_margin": am, "sample_margin": sm}
+    return acc, out, path
 
 
 def overlap(target, draft, temperature, top_k=0, *, nthreads=None):

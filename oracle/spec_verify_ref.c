@@ -40,6 +40,18 @@
  *   R7 "p(x) > 0" / "q(x) = 0" are support tests (kept by top-k and a finite logit);
  *      the ratio itself is formed as exp(min(0, log p(x) - log q(x))), which is
  *      min(1, p/q) written so that neither side underflows.
+ *   R16 tree verification: node 0 is the root (the committed context) and every other node n
+ *      has a parent parent[n] < n and a token x_n; p_u (target row u) is the target's
+ *      distribution after node u's path and q_u (draft row u) the distribution u's
+ *      children were drawn from, independently and with replacement.  The walk starts at
+ *      the root and tests u's children in index order against the current distribution
+ *      (p_u at first); each rejection replaces it by norm([cur - q_u]_+) before the next
+ *      sibling (SpecInfer's multi-step sampling as "Speculative Decoding 的朴素思想",
+ *      "Token Tree Verifier", describes it; EAGLE's recursive rejection on the EAGLE page,
+ *      section 6.2).  An accepted child becomes the new u; when every child is rejected
+ *      the token is drawn from the current distribution; at a leaf the bonus comes from
+ *      p_u.  Greedy (T = 0): the first child whose token is argmax p_u is accepted, else
+ *      argmax p_u is emitted.
  *   R15 the overlap of a position is taken between the two distributions the
  *      verification compares there: p_i and q_i after the same temperature and top-k.
  *      It is defined for T > 0 only (at T = 0 the policy is a deterministic choice).
@@ -61,6 +73,7 @@
 #define REF_ERR_QZERO (-2)    /* drafted token has q(x) = 0: the draft cannot emit it */
 #define REF_ERR_ROW (-3)      /* NaN or +inf logit, or a row with no finite logit   */
 #define REF_ERR_UNIFORM (-4)  /* a uniform outside [0, 1)                            */
+#define REF_ERR_TREE (-6)     /* parent array not a tree in topological order       */
 
 /* ---- reading stored logits ------------------------------------------------ */
 
@@ -484,6 +497,160 @@ int ref_overlap(const void *target, const void *draft, int dtype, int B, int G, 
     free(zd);
     free(P);
     free(Q);
+  }
+  return 0;
+}
+
+/* ---- tree verification (R16) ----------------------------------------------------- */
+
+/* Batched tree verification.  Host pointers, row-major:
+ *   target, draft [B, N, V] logits (draft rows of leaves are not read), tokens, parent
+ *   [B, N] int32 (node 0: the root, parent -1, token unused), u_accept [B, N] (node n's
+ *   test uses u_accept[b, n]), u_sample [B].  Outputs: accepted_len [B] (the depth of
+ *   the accepted path, or a negative code), out_tokens [B, N] (the accepted tokens, then
+ *   the correction or bonus token, then -1), path_nodes [B, N] (the accepted nodes, then
+ *   -1; nullable), accept_margin [B, N] (u - alpha of each tested node, NaN for untested
+ *   ones, +inf when p(x) = 0; nullable), sample_margin [B] (nullable).
+ * Checks, in this order: the tree (-6), tokens (-1), the rows the walk may read (-3), the
+ * uniforms (-4), q_parent(x_n) > 0 for every node (-2).  Returns -1 for arguments it
+ * cannot process. */
+int ref_tree_verify(const void *target, const void *draft, int dtype, const int32_t *tokens,
+                    const int32_t *parent, const float *u_accept, const float *u_sample, int B,
+                    int N, int V, double T, int top_k, int32_t *accepted_len,
+                    int32_t *out_tokens, int32_t *path_nodes, double *accept_margin,
+                    double *sample_margin, int nthreads) {
+  if (B < 0 || N < 1 || V < 1 || !(T >= 0.0)) return -1;
+  if (nthreads < 1) nthreads = 1;
+  const int greedy = (T == 0.0);
+#pragma omp parallel num_threads(nthreads)
+  {
+    double *zt = (double *)malloc(sizeof(double) * (size_t)V);
+    double *zd = (double *)malloc(sizeof(double) * (size_t)V);
+    double *P = (double *)malloc(sizeof(double) * (size_t)V);
+    double *Q = (double *)malloc(sizeof(double) * (size_t)V);
+    double *cur = (double *)malloc(sizeof(double) * (size_t)V);
+    unsigned char *keep_t = (unsigned char *)malloc((size_t)V);
+    unsigned char *keep_d = (unsigned char *)malloc((size_t)V);
+    int *nchild = (int *)malloc(sizeof(int) * (size_t)N);
+#pragma omp for schedule(dynamic, 1)
+    for (int b = 0; b < B; ++b) {
+      const int32_t *par = parent + (size_t)b * N;
+      const int32_t *x = tokens + (size_t)b * N;
+      const size_t row0 = (size_t)b * N;
+      int32_t *out = out_tokens + (size_t)b * N;
+      int32_t *path = path_nodes ? path_nodes + (size_t)b * N : NULL;
+      fill_tokens(out, N, -1);
+      if (path) fill_tokens(path, N, -1);
+      if (accept_margin)
+        for (int n = 0; n < N; ++n) accept_margin[row0 + n] = NAN;
+      if (sample_margin) sample_margin[b] = NAN;
+
+      int err = 0;
+      if (par[0] != -1) err = REF_ERR_TREE;
+      for (int n = 1; n < N && !err; ++n)
+        if (par[n] < 0 || par[n] >= n) err = REF_ERR_TREE;
+      for (int n = 0; n < N; ++n) nchild[n] = 0;
+      if (!err)
+        for (int n = 1; n < N; ++n) nchild[par[n]]++;
+      for (int n = 1; n < N && !err; ++n)
+        if (x[n] < 0 || x[n] >= V) err = REF_ERR_TOKEN;
+      for (int n = 0; n < N && !err; ++n) {
+        load_row(target, dtype, row0 + n, V, zt);
+        if (!row_is_valid(zt, V)) err = REF_ERR_ROW;
+      }
+      if (!greedy) {
+        for (int n = 0; n < N && !err; ++n) {
+          if (!nchild[n]) continue;
+          load_row(draft, dtype, row0 + n, V, zd);
+          if (!row_is_valid(zd, V)) err = REF_ERR_ROW;
+        }
+        for (int n = 1; n < N && !err; ++n) {
+          float u = u_accept[row0 + n];
+          if (!(u >= 0.0f && u < 1.0f)) err = REF_ERR_UNIFORM;
+        }
+        if (!err && !(u_sample[b] >= 0.0f && u_sample[b] < 1.0f)) err = REF_ERR_UNIFORM;
+        for (int n = 1; n < N && !err; ++n) {
+          load_row(draft, dtype, row0 + par[n], V, zd);
+          policy(zd, V, T, top_k, keep_d, NULL);
+          if (!keep_d[x[n]]) err = REF_ERR_QZERO;
+        }
+      }
+      if (err) {
+        accepted_len[b] = err;
+        continue;
+      }
+
+      int u = 0, depth = 0;
+      for (;;) {
+        load_row(target, dtype, row0 + u, V, zt);
+        if (greedy) {
+          int a = argmax_lowest(zt, V), next = -1;
+          for (int s = u + 1; s < N && next < 0; ++s)
+            if (par[s] == u && x[s] == a) next = s;
+          out[depth] = a;
+          if (next < 0) break; /* the target's own choice ends the round */
+          if (path) path[depth] = next;
+          ++depth;
+          u = next;
+          continue;
+        }
+        double logZp = policy(zt, V, T, top_k, keep_t, P);
+        if (!nchild[u]) { /* a leaf: bonus from p_u */
+          double d = 0.0;
+          out[depth] = ref_invcdf(P, V, (double)u_sample[b], &d);
+          if (sample_margin) sample_margin[b] = d;
+          break;
+        }
+        load_row(draft, dtype, row0 + u, V, zd);
+        double logZq = policy(zd, V, T, top_k, keep_d, Q);
+        for (int v = 0; v < V; ++v) cur[v] = P[v];
+        int rejected = 0, next = -1;
+        for (int s = u + 1; s < N && next < 0; ++s) {
+          if (par[s] != u) continue;
+          const int xs = x[s];
+          const double us = (double)u_accept[row0 + s];
+          double alpha;
+          if (!rejected) { /* the first child: min(1, p/q) as in the chain (R7) */
+            alpha = keep_t[xs] ? exp(fmin(0.0, (zt[xs] / T - logZp) - (zd[xs] / T - logZq))) : 0.0;
+          } else {         /* later siblings: the current residual distribution */
+            alpha = fmin(1.0, cur[xs] / Q[xs]);
+          }
+          const int has_p = rejected ? (cur[xs] > 0.0) : keep_t[xs];
+          if (accept_margin) accept_margin[row0 + s] = has_p ? us - alpha : INFINITY;
+          if (has_p && us <= alpha) { /* R1 */
+            next = s;
+            break;
+          }
+          /* rejected: cur <- norm([cur - q_u]_+) before the next sibling */
+          double Z = 0.0;
+          for (int v = 0; v < V; ++v) Z += fmax(cur[v] - Q[v], 0.0);
+          if (Z > 0.0)
+            for (int v = 0; v < V; ++v) cur[v] = fmax(cur[v] - Q[v], 0.0) / Z;
+          else /* reachable only through rounding: keep p_u (as R4) */
+            for (int v = 0; v < V; ++v) cur[v] = P[v];
+          ++rejected;
+        }
+        if (next < 0) { /* every child rejected: draw from the current distribution */
+          double d = 0.0;
+          out[depth] = ref_invcdf(cur, V, (double)u_sample[b], &d);
+          if (sample_margin) sample_margin[b] = d;
+          break;
+        }
+        out[depth] = x[next];
+        if (path) path[depth] = next;
+        ++depth;
+        u = next;
+      }
+      accepted_len[b] = depth;
+    }
+    free(zt);
+    free(zd);
+    free(P);
+    free(Q);
+    free(cur);
+    free(keep_t);
+    free(keep_d);
+    free(nchild);
   }
   return 0;
 }

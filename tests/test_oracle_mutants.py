@@ -13,6 +13,7 @@ import pytest
 import oracle
 import test_oracle_pins as pins
 import test_oracle_overlap as ovl
+import test_oracle_tree as tree
 import test_oracle_stats as stats
 
 SRC = Path(oracle.__file__).resolve().parent / "spec_verify_ref.c"
@@ -55,6 +56,16 @@ MUTANTS = [
      "policy(zd, V, 1.0, top_k, NULL, Q);"),
     ("overlap_skips_draft_check", "if (!row_is_valid(zt, V) || !row_is_valid(zd, V)) {",
      "if (!row_is_valid(zt, V)) {"),
+    ("tree_naive_siblings", "for (int v = 0; v < V; ++v) cur[v] = fmax(cur[v] - Q[v], 0.0) / Z;",
+     "for (int v = 0; v < V; ++v) cur[v] = P[v];"),
+    ("tree_first_child_only", "if (par[s] != u) continue;\n          const int xs", "if (par[s] != u || rejected) continue;\n          const int xs"),
+    ("tree_parent_row", "load_row(target, dtype, row0 + u, V, zt);\n        if (greedy)",
+     "load_row(target, dtype, row0 + (u ? par[u] : 0), V, zt);\n        if (greedy)"),
+    ("tree_draw_from_p", "out[depth] = ref_invcdf(cur, V,", "out[depth] = ref_invcdf(P, V,"),
+    ("tree_greedy_last_match", "for (int s = u + 1; s < N && next < 0; ++s)\n            if (par[s] == u && x[s] == a) next = s;",
+     "for (int s = u + 1; s < N; ++s)\n            if (par[s] == u && x[s] == a) next = s;"),
+    ("tree_uniform_index", "const double us = (double)u_accept[row0 + s];", "const double us = (double)u_accept[row0 + s - 1];"),
+    ("tree_leaf_draft_checked", "if (!nchild[n]) continue;\n          load_row(draft", "load_row(draft"),
 ]
 
 PIN_TESTS = [
@@ -83,6 +94,13 @@ PIN_TESTS = [
     lambda: ovl.test_identities_and_scipy(2.0, 5),
     lambda: ovl.test_target_layout_with_or_without_bonus_row(),
     lambda: ovl.test_row_checks(),
+    lambda: tree.test_chain_tree_equals_chain_oracle("f32", 1.0, 0),
+    lambda: tree.test_chain_tree_equals_chain_oracle("bf16", 0.0, 0),
+    lambda: tree.test_second_sibling_is_tested_against_the_residual(),
+    lambda: tree.test_third_sibling_threshold_and_final_draw(),
+    lambda: tree.test_greedy_tree_walk(),
+    lambda: tree.test_tree_checks("nan_draft_leaf", 0),
+    lambda: tree.test_monte_carlo_tree_law_matches_target((3,), 1.0, 0),
 ]
 
 
