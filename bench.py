@@ -517,13 +517,103 @@ def run_overlap(args, dev, hev):
     return res
 
 
+def run_tree(args, dev, hev):
+    """Verification of a batch of draft trees: drafted nodes verified per second."""
+    import torch
+    import rejection_sampling_verify_02_amd as sv
+    from rejection_sampling_verify_02_amd import workloads as wl
+
+    cfg = wl.TREE_CONFIGS["tree_bf16_b16_n32"]
+    B, N, V, S = cfg.B, cfg.N, cfg.V, cfg.max_children
+    esz = 2 if cfg.dtype == "bf16" else 4
+    set_bytes = 2 * B * N * V * esz
+    n_sets = args.sets or max(2, -(-(1 << 30) // set_bytes))
+    log(f"[bench] trees {cfg.name}: B={B} N={N} V={V} {cfg.dtype}, max children {S}, {n_sets} input sets")
+    conv = (lambda a: torch.from_numpy(a).view(torch.bfloat16).to(dev)) if cfg.dtype == "bf16" \
+        else (lambda a: torch.from_numpy(a).to(dev))
+    sets, host, alg = [], [], []
+    for s in range(n_sets):
+        raw = wl.make_tree(B, N, V, cfg.dtype, cfg.seed + 1000 * s, max_children=S, draft_noise=cfg.draft_noise)
+        t, d = conv(raw.target), conv(raw.draft)
+        par = torch.from_numpy(raw.parent).to(dev)
+        # node tokens drawn from the parent's draft distribution by the library's sampler
+        rows = d[torch.arange(B, device=dev)[:, None], par[:, 1:].long()].reshape(B * (N - 1), V).contiguous()
+        tk, st = sv.spec_sample(rows, torch.from_numpy(raw.u_draft[:, 1:].reshape(-1).copy()).to(dev),
+                                cfg.temperature, cfg.top_k)
+        tok = torch.zeros((B, N), dtype=torch.int32, device=dev)
+        tok[:, 1:] = tk.reshape(B, N - 1)
+        sets.append((t, d, tok, par, torch.from_numpy(raw.u_accept).to(dev), torch.from_numpy(raw.u_sample).to(dev)))
+        host.append((raw, tok.cpu().numpy()))
+        internal = sum(len(set(raw.parent[b, 1:].tolist())) for b in range(B))
+        alg.append((B * N + internal) * V * esz)  # every target row, and the draft rows of nodes with children
+    torch.cuda.synchronize(dev)
+    alg_bytes = int(np.mean(alg))
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    dtc = sv.SV_BF16 if cfg.dtype == "bf16" else sv.SV_F32
+    plan = sv.sv_tree_launch_plan(B, N, V, S, dtc, cfg.temperature, cfg.top_k)
+    ws = sv.Workspace()
+    outs = (torch.empty((B,), dtype=torch.int32, device=dev), torch.empty((B, N), dtype=torch.int32, device=dev),
+            torch.empty((B, N), dtype=torch.int32, device=dev))
+
+    def call(i, events=None):
+        t, d, tok, par, ua, us = sets[i % n_sets]
+        return sv.spec_tree_verify(t, d, tok, par, ua, us, cfg.temperature, cfg.top_k, max_children=S,
+                                   workspace=ws, stream=stream, out=outs, events=events)
+
+    K = args.steps
+    wall, gpu_ms, per_kernel, wall2 = time_loop(call, plan, K, args.warmup, stream, dev, hev,
+                                                not args.no_stage_events)
+    t_call = wall / K
+    depth = []
+    for i in range(n_sets):
+        call(i)
+        depth.append(float(outs[0].float().mean().item()))
+    res = {
+        "metric": "verified draft-tree nodes/sec and achieved HBM GB/s (% of peak)",
+        "value": round(B * (N - 1) / t_call, 1), "unit": "nodes/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(t_call * 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": cfg.name, "B": B, "N": N, "V": V, "logits": cfg.dtype, "max_children": S,
+                   "temperature": cfg.temperature, "top_k": cfg.top_k, "input_sets": n_sets,
+                   "set_bytes": set_bytes, "algorithmic_bytes": alg_bytes},
+        "call_GBs": round(alg_bytes / t_call / 1e9, 1),
+        "call_frac_of_peak": round(alg_bytes / t_call / 1e9 / PEAK_HBM_GBS, 4),
+        "emitted_tokens_per_s": round(B * (float(np.mean(depth)) + 1) / t_call, 1),
+        "mean_accepted_depth": round(float(np.mean(depth)), 4),
+        "gpu_event_ms_per_step": round(gpu_ms / K, 5),
+        "per_kernel_us": {k: round(v, 3) for k, v in per_kernel.items()},
+        "ms_per_step_with_kernel_events": None if wall2 is None else round(wall2 * 1e3 / K, 5),
+        "roofline": roofline(per_kernel, "k_tree_rows", alg_bytes, None),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle._load()
+        threads = oracle.default_threads()
+        calls, t0 = 0, time.perf_counter()
+        while True:
+            raw, tok = host[calls % len(host)]
+            oracle.tree_verify(raw.target, raw.draft, tok, raw.parent, raw.u_accept, raw.u_sample,
+                               cfg.temperature, cfg.top_k, nthreads=threads)
+            calls += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds:
+                break
+        res["cpu_baseline"] = {"value": B * (N - 1) * calls / el, "unit": "nodes/s", "cores": threads,
+                               "kind": "oracle", "sample": f"{calls} full calls (B={B}, N={N}, V={V}) over "
+                                                           f"{min(calls, len(host))} input sets, {el:.1f} s"}
+    else:
+        res["cpu_baseline"] = None
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--op", default="verify", choices=["verify", "sample", "overlap"],
-                    help="verify (the default, the headline), the batched sampler, or the per-position overlap")
+    ap.add_argument("--op", default="verify", choices=["verify", "sample", "overlap", "tree"],
+                    help="verify (the default, the headline), the batched sampler, the per-position overlap, "
+                         "or tree verification")
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5],
                     help="verification workload (3, the default, is the headline; 4 greedy and 5 top-k "
                          "are timed for the design notes)")
@@ -555,7 +645,7 @@ def main() -> int:
     sv.load_library()  # raises if the HIP library is not built
     dev = torch.device("cuda:0")
     hev = HipEvents()
-    run = {"sample": run_sample, "overlap": run_overlap}.get(args.op, run_verify)
+    run = {"sample": run_sample, "overlap": run_overlap, "tree": run_tree}.get(args.op, run_verify)
     res = run(args, dev, hev)
     print(json.dumps(res), flush=True)
     return 0

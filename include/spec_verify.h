@@ -66,6 +66,9 @@ typedef enum {
  * workgroups earlier in its grid (a bounded wait of about a second that ordinary
  * scheduling never reaches).  The sequence's out_tokens are then incomplete. */
 #define SV_ROW_INTERNAL (-5)
+/* spec_tree_verify: the parent array is not a tree in topological order (parent[0] must be
+ * -1 and 0 <= parent[n] < n), or a node has more children than max_children. */
+#define SV_ROW_BAD_TREE (-6)
 
 /* Bytes of device workspace spec_verify needs for these arguments (0 never occurs). */
 size_t sv_workspace_bytes(int32_t B, int32_t G, int32_t V, sv_dtype dtype, float temperature,
@@ -211,6 +214,63 @@ sv_status spec_overlap_timed(const void *target_logits, const void *draft_logits
 /* Names of the kernels spec_overlap would launch, ';'-separated (static storage). */
 const char *sv_overlap_launch_plan(int32_t B, int32_t G, int32_t V, sv_dtype dtype,
                                    float temperature, int32_t top_k);
+
+/* ---- verification of a draft tree ----
+ *
+ * Each sequence proposes a tree of N nodes ("Speculative Decoding 的朴素思想", section
+ * "Token Tree Verifier": SpecInfer's multi-step speculative sampling; the EAGLE page,
+ * section 6.2: rejection node by node).  Node 0 is the committed context; node n >= 1 has
+ * parent[b, n] < n and token tokens[b, n]; children of a node are drawn independently from
+ * the node's draft distribution and are taken in index order.
+ *   target_logits [B, N, V] dtype  p_u: the target's distribution after node u's path
+ *   draft_logits  [B, N, V] dtype  q_u: the distribution u's children were drawn from
+ *                                  (rows of leaves are not read; NULL allowed at T == 0)
+ *   tokens, parent [B, N] int32    node tokens (node 0's unused) and parents (parent[b,0] = -1)
+ *   u_accept [B, N] float32        the uniform of node n's test (node 0's unused)
+ *   u_sample [B] float32           the uniform of the final draw
+ *   max_children                   the most children any node has (0 <= it <= N - 1);
+ *                                  sizes the residual rounds
+ * The walk starts at the root and tests the node's children in order: the first child
+ * against p_u by U <= min(1, p_u(x)/q_u(x)); each rejection replaces the current
+ * distribution by norm([cur - q_u]_+) and the next child is tested against it.  An
+ * accepted child becomes the node; if every child is rejected the token is drawn from the
+ * current distribution by inverse CDF with u_sample, at a leaf the bonus is drawn from p_u.
+ * T == 0: the first child whose token is argmax p_u is accepted, else argmax p_u ends the
+ * round; draft logits and uniforms are not read.
+ *   accepted_len [B] int32 out    the depth reached (accepted tokens), or a negative code
+ *   out_tokens   [B, N] int32 out the accepted tokens, then the final token, then -1
+ *   path_nodes   [B, N] int32 out the accepted nodes, then -1 (nullable)
+ * Row codes (tested in this order): SV_ROW_INTERNAL, SV_ROW_BAD_TREE, SV_ROW_BAD_TOKEN (a
+ * token of node n >= 1 outside [0, V)), SV_ROW_BAD_LOGITS (any target row, or the draft row
+ * of a node with children), SV_ROW_BAD_UNIFORM, SV_ROW_Q_ZERO (q_parent(n)(x_n) = 0).
+ * Workspace: sv_tree_workspace_bytes(...) bytes, 256-byte aligned, first
+ * sv_tree_workspace_zero_bytes(...) bytes zero, under the rules of spec_verify's workspace.
+ * N is at most 1024. */
+size_t sv_tree_workspace_bytes(int32_t B, int32_t N, int32_t V, int32_t max_children,
+                               sv_dtype dtype, float temperature, int32_t top_k);
+size_t sv_tree_workspace_zero_bytes(int32_t B, int32_t N, int32_t V, int32_t max_children,
+                                    sv_dtype dtype, float temperature, int32_t top_k);
+sv_status spec_tree_verify(const void *target_logits, const void *draft_logits, sv_dtype dtype,
+                           const int32_t *tokens, const int32_t *parent, const float *u_accept,
+                           const float *u_sample, int32_t B, int32_t N, int32_t V,
+                           int32_t max_children, float temperature, int32_t top_k,
+                           int32_t *accepted_len, int32_t *out_tokens, int32_t *path_nodes,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* spec_tree_verify with each kernel dispatch bracketed by caller-owned HIP events, as in
+ * spec_verify_timed. */
+sv_status spec_tree_verify_timed(const void *target_logits, const void *draft_logits,
+                                 sv_dtype dtype, const int32_t *tokens, const int32_t *parent,
+                                 const float *u_accept, const float *u_sample, int32_t B,
+                                 int32_t N, int32_t V, int32_t max_children, float temperature,
+                                 int32_t top_k, int32_t *accepted_len, int32_t *out_tokens,
+                                 int32_t *path_nodes, void *workspace, size_t workspace_bytes,
+                                 void *stream, void *const *events, int32_t n_events,
+                                 int32_t *n_launched);
+
+/* Names of the kernels spec_tree_verify would launch, ';'-separated (static storage). */
+const char *sv_tree_launch_plan(int32_t B, int32_t N, int32_t V, int32_t max_children,
+                                sv_dtype dtype, float temperature, int32_t top_k);
 
 /* Human-readable text of a status (static storage). */
 const char *sv_status_string(sv_status status);

@@ -19,7 +19,7 @@ _PKG = Path(__file__).resolve().parent
 LIB_PATH = _PKG / "libspec_verify.so"
 
 SV_F32, SV_BF16 = 0, 1
-ROW_BAD_TOKEN, ROW_Q_ZERO, ROW_BAD_LOGITS, ROW_BAD_UNIFORM = -1, -2, -3, -4
+ROW_BAD_TOKEN, ROW_Q_ZERO, ROW_BAD_LOGITS, ROW_BAD_UNIFORM, ROW_INTERNAL, ROW_BAD_TREE = -1, -2, -3, -4, -5, -6
 MAX_LAUNCHES = 8
 
 _STATUS = {0: "SV_OK", 1: "SV_ERR_NULL", 2: "SV_ERR_SHAPE", 3: "SV_ERR_DTYPE",
@@ -28,7 +28,9 @@ _STATUS = {0: "SV_OK", 1: "SV_ERR_NULL", 2: "SV_ERR_SHAPE", 3: "SV_ERR_DTYPE",
 EXPORTED = ("spec_verify", "spec_verify_timed", "sv_workspace_bytes", "sv_workspace_zero_bytes",
             "sv_status_string", "sv_launch_plan", "spec_sample", "spec_sample_timed",
             "spec_overlap", "spec_overlap_timed", "sv_overlap_workspace_bytes",
-            "sv_overlap_workspace_zero_bytes", "sv_overlap_launch_plan")
+            "sv_overlap_workspace_zero_bytes", "sv_overlap_launch_plan",
+            "spec_tree_verify", "spec_tree_verify_timed", "sv_tree_workspace_bytes",
+            "sv_tree_workspace_zero_bytes", "sv_tree_launch_plan")
 
 
 class SpecVerifyError(RuntimeError):
@@ -70,6 +72,16 @@ def load_library(path: Path | str | None = None) -> ctypes.CDLL:
         fn.restype = SZ
     lib.sv_overlap_launch_plan.argtypes = [I32, I32, I32, I32, F32, I32]
     lib.sv_overlap_launch_plan.restype = ctypes.c_char_p
+    tree = [V, V, I32, V, V, V, V, I32, I32, I32, I32, F32, I32, V, V, V, V, SZ, V]
+    lib.spec_tree_verify.argtypes = tree
+    lib.spec_tree_verify.restype = I32
+    lib.spec_tree_verify_timed.argtypes = tree + [V, I32, V]
+    lib.spec_tree_verify_timed.restype = I32
+    for fn in (lib.sv_tree_workspace_bytes, lib.sv_tree_workspace_zero_bytes):
+        fn.argtypes = [I32, I32, I32, I32, I32, F32, I32]
+        fn.restype = SZ
+    lib.sv_tree_launch_plan.argtypes = [I32, I32, I32, I32, I32, F32, I32]
+    lib.sv_tree_launch_plan.restype = ctypes.c_char_p
     lib.sv_workspace_bytes.argtypes = [I32, I32, I32, I32, F32, I32]
     lib.sv_workspace_bytes.restype = SZ
     lib.sv_workspace_zero_bytes.argtypes = [I32, I32, I32, I32, F32, I32]
@@ -105,6 +117,12 @@ def sv_overlap_launch_plan(B: int, G: int, V: int, dtype: int, temperature: floa
                           top_k: int = 0) -> list[str]:
     s = load_library().sv_overlap_launch_plan(B, G, V, dtype, float(temperature), int(top_k)).decode()
     return s.split(";") if s else []
+
+
+def sv_tree_launch_plan(B: int, N: int, V: int, max_children: int, dtype: int, temperature: float,
+                       top_k: int = 0) -> list[str]:
+    s = load_library().sv_tree_launch_plan(B, N, V, max_children, dtype, float(temperature), int(top_k)).decode()
+    return s.split(";")
 
 
 # ------------------------------------------------------------------ workspace
@@ -335,3 +353,61 @@ def spec_overlap(target_logits, draft_logits, temperature: float, top_k: int = 0
         raise SpecVerifyError(rc, sv_status_string(rc))
     wso.called(dev, zbytes)
     return (beta, tv, st) if events is None else (beta, tv, st, nl)
+
+
+def spec_tree_verify(target_logits, draft_logits, tokens, parent, u_accept, u_sample, temperature: float,
+                     top_k: int = 0, *, max_children: int | None = None, workspace: Workspace | None = None,
+                     stream=None, out=None, events=None):
+    """Tree verification on the GPU (see include/spec_verify.h): target and draft logits
+    [B, N, V] (bfloat16 or float32; draft may be None at temperature 0), tokens and parent
+    [B, N] int32, u_accept [B, N] and u_sample [B] float32 (None at temperature 0).
+    max_children (the most children any node has) defaults to N - 1.  Returns
+    (accepted_len [B], out_tokens [B, N], path_nodes [B, N]) int32 tensors; ``out`` may
+    supply them; ``events`` as for spec_verify."""
+    import torch
+    lib = load_library()
+    dev = target_logits.device
+    if dev.type != "cuda":
+        raise ValueError("logits must be device tensors")
+    dt = _dtype_code(target_logits)
+    if target_logits.dim() != 3:
+        raise ValueError("target must be [B, N, V]")
+    B, N, V = target_logits.shape
+    greedy = float(temperature) == 0.0
+    _check(target_logits, "target_logits", (B, N, V), target_logits.dtype, dev)
+    _check(tokens, "tokens", (B, N), torch.int32, dev)
+    _check(parent, "parent", (B, N), torch.int32, dev)
+    if greedy:
+        draft_logits = u_accept = u_sample = None
+    else:
+        _check(draft_logits, "draft_logits", (B, N, V), target_logits.dtype, dev)
+        _check(u_accept, "u_accept", (B, N), torch.float32, dev)
+        _check(u_sample, "u_sample", (B,), torch.float32, dev)
+    S = (N - 1) if max_children is None else int(max_children)
+    if out is not None:
+        acc, toks, path = out
+    else:
+        acc = torch.empty((B,), dtype=torch.int32, device=dev)
+        toks = torch.empty((B, N), dtype=torch.int32, device=dev)
+        path = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    nbytes = int(lib.sv_tree_workspace_bytes(B, N, V, S, dt, float(temperature), int(top_k)))
+    zbytes = int(lib.sv_tree_workspace_zero_bytes(B, N, V, S, dt, float(temperature), int(top_k)))
+    wso = workspace or _default_ws
+    ws = wso.get(nbytes, zbytes, dev, stream)
+    args = [_ptr(target_logits), _ptr(draft_logits), dt, _ptr(tokens), _ptr(parent), _ptr(u_accept),
+            _ptr(u_sample), B, N, V, S, float(temperature), int(top_k), _ptr(acc), _ptr(toks), _ptr(path),
+            _ptr(ws), ws.numel(), ctypes.c_void_p(stream)]
+    if events is None:
+        rc = lib.spec_tree_verify(*args)
+        nl = None
+    else:
+        arr = (ctypes.c_void_p * len(events))(*events)
+        n = ctypes.c_int32(0)
+        rc = lib.spec_tree_verify_timed(*args, arr, len(events), ctypes.byref(n))
+        nl = n.value
+    if rc != 0:
+        raise SpecVerifyError(rc, sv_status_string(rc))
+    wso.called(dev, zbytes)
+    return (acc, toks, path) if events is None else (acc, toks, path, nl)

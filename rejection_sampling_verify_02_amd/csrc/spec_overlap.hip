@@ -42,68 +42,16 @@ namespace sv {
 constexpr int OV_LAG = 4;  // pairs between a pair's first and second phase in a lane (1, 2,
                            // 4 and 8 measured: 4 is best)
 
-// First phase: the normaliser partial of chunk c of row r (in the pair's numbering), as
-// the verification kernel forms it: off = m_c*k2 (rounded once) and s = sum
-// 2^(fma(z, k2, -off)), four elements of a vector added as a tree, vectors in order.
+// First phase: the normaliser partial of chunk c of row r (in the pair's numbering),
+// formed as the verification kernel forms it (chunk_norm), with cached loads: the second
+// phase re-reads the chunk soon after.
 template <typename T, bool ALIGNED, bool TOPK>
 SVD void ov_first(const Args &a, int r, const T *row, int c) {
-  constexpr int VEC = Fmt<T>::VEC;
-  __shared__ float s_m[NW];
-  __shared__ double s_s[NW];
-  const int tid = threadIdx.x, lane = lane_id(), wid = tid / WAVE;
-  float x[VPT][VEC];
-  load_chunk<T, ALIGNED, false>(row, a.V, a.nvec, c, tid, x);  // cached: the second phase re-reads it
-  if (TOPK) {
-    const float tau = a.w.row_tau[r];  // written by the previous kernel
-#pragma unroll
-    for (int k = 0; k < VPT; ++k)
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) x[k][e] = (x[k][e] < tau) ? -INFINITY : x[k][e];
-  }
-  float m = -INFINITY;
-#pragma unroll
-  for (int k = 0; k < VPT; ++k)
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) m = fmaxf(m, x[k][e]);
-  m = wave_max(m);
-  if (lane == 0) s_m[wid] = m;
-  __syncthreads();
-  m = s_m[0];
-#pragma unroll
-  for (int w = 1; w < NW; ++w) m = fmaxf(m, s_m[w]);
-
-  const float k2 = a.k2;
+  const int lane = lane_id(), wid = threadIdx.x / WAVE;
   float off;
-  double s;
-  if (m > -INFINITY) {
-    off = m * k2;
-    float acc = 0.0f;
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-      float t[VEC];
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) t[e] = fast_exp2(fmaf(x[k][e], k2, -off));
-#pragma unroll
-      for (int h = VEC / 2; h > 0; h >>= 1)
-#pragma unroll
-        for (int e = 0; e < h; ++e) t[e] += t[e + h];
-      acc += t[0];
-    }
-    s = (double)acc;
-  } else {  // nothing finite in the chunk: keep a NaN visible, otherwise an empty partial
-    off = -INFINITY;
-    bool nan = false;
-#pragma unroll
-    for (int k = 0; k < VPT; ++k)
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) nan |= (x[k][e] != x[k][e]);
-    s = nan ? (double)NAN : 0.0;
-  }
-  s = wave_sum(s);
-  if (lane == 0) s_s[wid] = s;
-  __syncthreads();
+  double S;
+  chunk_norm<T, ALIGNED, TOPK, false>(row, a.V, a.nvec, c, TOPK ? a.w.row_tau[r] : 0.0f, a.k2, off, S);
   if (wid != 0) return;
-  const double S = (s_s[0] + s_s[1]) + (s_s[2] + s_s[3]);
   u64 *pw = a.w.tw_part + ((size_t)r * a.C + c) * 3;
   if (lane < 3) tw_putf(pw + lane, a.tag, lane == 0 ? off : (lane == 1 ? d_head(S) : d_tail(S)));
 }

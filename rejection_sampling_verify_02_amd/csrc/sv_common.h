@@ -161,6 +161,70 @@ __global__ __launch_bounds__(NT) void k_topk_digit(const Args a, int pass, int l
   }
 }
 
+// ---------------------------------------------------------------- per-chunk normaliser
+
+// The normaliser partial of chunk c of one row (whole workgroup): m = block max of the
+// kept z (top-k: z >= tau), off = m*k2 rounded once, and S = the sum of 2^(fma(z, k2,
+// -off)) (a vector's elements as a tree, vectors in order, waves as a fixed tree).  A
+// chunk with nothing finite gives off = -inf and S = 0, or NaN if it holds a NaN.  The
+// results are the same in every thread.
+template <typename T, bool ALIGNED, bool TOPK, bool STREAM>
+SVD void chunk_norm(const T *row, int V, int nvec, int c, float tau, float k2, float &off,
+                    double &S) {
+  constexpr int VEC = Fmt<T>::VEC;
+  __shared__ float s_m[NW];
+  __shared__ double s_s[NW];
+  const int tid = threadIdx.x, lane = lane_id(), wid = tid / WAVE;
+  float x[VPT][VEC];
+  load_chunk<T, ALIGNED, STREAM>(row, V, nvec, c, tid, x);
+  if (TOPK) {
+#pragma unroll
+    for (int k = 0; k < VPT; ++k)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) x[k][e] = (x[k][e] < tau) ? -INFINITY : x[k][e];
+  }
+  float m = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < VPT; ++k)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) m = fmaxf(m, x[k][e]);
+  m = wave_max(m);
+  if (lane == 0) s_m[wid] = m;
+  __syncthreads();
+  m = s_m[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) m = fmaxf(m, s_m[w]);
+  double s;
+  if (m > -INFINITY) {
+    off = m * k2;
+    float acc = 0.0f;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      float t[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) t[e] = fast_exp2(fmaf(x[k][e], k2, -off));
+#pragma unroll
+      for (int h = VEC / 2; h > 0; h >>= 1)
+#pragma unroll
+        for (int e = 0; e < h; ++e) t[e] += t[e + h];
+      acc += t[0];
+    }
+    s = (double)acc;
+  } else {
+    off = -INFINITY;
+    bool nan = false;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) nan |= (x[k][e] != x[k][e]);
+    s = nan ? (double)NAN : 0.0;
+  }
+  s = wave_sum(s);
+  if (lane == 0) s_s[wid] = s;
+  __syncthreads();
+  S = (s_s[0] + s_s[1]) + (s_s[2] + s_s[3]);
+}
+
 }  // namespace sv
 
 // ---------------------------------------------------------------- host helpers

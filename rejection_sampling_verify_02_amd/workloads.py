@@ -234,3 +234,67 @@ def make_sample(B: int, V: int, dtype: str, seed: int, *, noise_scale: float = 1
     target, _ = zipf_gauss(B, 0, V, dtype, 0.0, seed, noise_scale=noise_scale)
     rng = np.random.default_rng(seed + 7919)
     return np.ascontiguousarray(target[:, 0]), uniforms(rng, (B,))
+
+
+# ---------------------------------------------------------------- draft trees
+
+@dataclass(frozen=True)
+class TreeConfig:
+    name: str
+    B: int
+    N: int
+    V: int
+    dtype: str
+    temperature: float
+    top_k: int
+    max_children: int
+    draft_noise: float
+    seed: int
+
+
+# A batch of 16 draft trees of 32 nodes (at most 4 children per node) over a LLaMA-3-sized
+# vocabulary: the size of the dynamic trees the EAGLE page describes (tens of nodes per
+# round), with the Zipf+Gaussian logits of the chain workloads.
+TREE_CONFIGS = {
+    "tree_bf16_b16_n32": TreeConfig("tree_bf16_b16_n32", 16, 32, 128256, "bf16", 1.0, 0, 4, 0.5, 3001),
+}
+
+
+@dataclass
+class TreeRaw:
+    target: np.ndarray   # [B, N, V]: the target's distribution after each node
+    draft: np.ndarray    # [B, N, V]: the distribution each node's children are drawn from
+    parent: np.ndarray   # [B, N] int32, parent[:, 0] = -1, parent[n] < n
+    u_draft: np.ndarray  # [B, N] uniforms for drawing each node's token from its parent's q
+    u_accept: np.ndarray  # [B, N]
+    u_sample: np.ndarray  # [B]
+
+
+def random_parents(rng: np.random.Generator, N: int, max_children: int) -> np.ndarray:
+    """A random tree in topological order: node n picks its parent among nodes < n that
+    still have room, preferring recent (deeper) ones half of the time."""
+    parent = np.full(N, -1, np.int32)
+    nch = np.zeros(N, np.int64)
+    for n in range(1, N):
+        room = np.nonzero(nch[:n] < max_children)[0]
+        if rng.random() < 0.5:
+            p = int(room[-1 - rng.integers(0, min(3, len(room)))])
+        else:
+            p = int(room[rng.integers(0, len(room))])
+        parent[n] = p
+        nch[p] += 1
+    return parent
+
+
+def make_tree(B: int, N: int, V: int, dtype: str, seed: int, *, max_children: int = 4,
+              draft_noise: float = 0.5, noise_scale: float = 1.5, parents=None) -> TreeRaw:
+    """Random trees with Zipf+Gaussian logits at every node (the draft is the target plus
+    noise), their uniforms, and the uniforms for drawing node tokens.  Drawing the tokens
+    from q is left to the caller."""
+    target, draft = zipf_gauss(B, N, V, dtype, draft_noise, seed, noise_scale=noise_scale)
+    target = np.ascontiguousarray(target[:, :N])  # N target rows (the generator gives N + 1)
+    rng = np.random.default_rng(seed + 7919)
+    if parents is None:
+        parents = np.stack([random_parents(rng, N, max_children) for _ in range(B)])
+    parents = np.ascontiguousarray(np.broadcast_to(np.asarray(parents, np.int32), (B, N)))
+    return TreeRaw(target, draft, parents, uniforms(rng, (B, N)), uniforms(rng, (B, N)), uniforms(rng, (B,)))

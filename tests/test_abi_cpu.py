@@ -183,3 +183,38 @@ def test_overlap_plan_and_workspace(lib):
     assert lib.sv_overlap_workspace_zero_bytes(*a2) < lib.sv_overlap_workspace_bytes(*a2)
     assert lib.sv_overlap_workspace_zero_bytes(64, 4, 128256, sv.SV_BF16, 0.0, 0) == 0
 
+
+
+def call_tree(lib, **kw):
+    a = dict(t=FAKE, d=FAKE, dt=sv.SV_BF16, tok=FAKE, par=FAKE, ua=FAKE, us=FAKE, B=4, N=8, V=1024, S=3,
+             T=1.0, k=0, acc=FAKE, out=FAKE, path=FAKE, ws=FAKE, nbytes=1 << 30, stream=None)
+    a.update(kw)
+    return lib.spec_tree_verify(V_(a["t"]), V_(a["d"]), a["dt"], V_(a["tok"]), V_(a["par"]), V_(a["ua"]),
+                                V_(a["us"]), a["B"], a["N"], a["V"], a["S"], F_(a["T"]), a["k"], V_(a["acc"]),
+                                V_(a["out"]), V_(a["path"]), V_(a["ws"]), Z_(a["nbytes"]), V_(a["stream"]))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), 2), (dict(N=0), 2), (dict(N=1025), 2), (dict(V=0), 2), (dict(S=-1), 2), (dict(S=8), 2),
+    (dict(dt=9), 3), (dict(T=-1.0), 4), (dict(T=float("nan")), 4),
+    (dict(t=None), 1), (dict(tok=None), 1), (dict(par=None), 1), (dict(acc=None), 1), (dict(out=None), 1),
+    (dict(ws=None), 1), (dict(d=None), 1), (dict(ua=None), 1), (dict(us=None), 1),
+    (dict(t=FAKE + 1), 6), (dict(d=FAKE + 1), 6), (dict(nbytes=16), 5),
+])
+def test_tree_host_argument_errors(lib, kw, status):
+    assert call_tree(lib, **kw) == status
+
+
+def test_tree_optional_pointers_and_plan(lib):
+    # path is optional; greedy reads no draft and no uniforms (stops at the workspace check)
+    assert call_tree(lib, path=None, nbytes=16) == 5
+    assert call_tree(lib, T=0.0, d=None, ua=None, us=None, nbytes=16) == 5
+    assert sv.sv_tree_launch_plan(16, 32, 128256, 4, sv.SV_BF16, 1.0, 0) == \
+        ["k_tree_rows", "k_tree_resid", "k_tree_walk", "k_tree_draw"]
+    assert sv.sv_tree_launch_plan(16, 32, 128256, 1, sv.SV_BF16, 1.0, 0) == ["k_tree_rows", "k_tree_walk", "k_tree_draw"]
+    assert sv.sv_tree_launch_plan(16, 32, 128256, 4, sv.SV_BF16, 0.0, 0) == ["k_tree_rows", "k_tree_walk"]
+    assert sv.sv_tree_launch_plan(16, 32, 128256, 4, sv.SV_F32, 0.7, 5)[:4] == ["k_topk_digit"] * 4
+    args = (16, 32, 128256, 4, sv.SV_BF16, 1.0, 0)
+    n, z = lib.sv_tree_workspace_bytes(*args), lib.sv_tree_workspace_zero_bytes(*args)
+    assert 0 < z < n and z % 256 == 0 and n % 256 == 0
+    assert lib.sv_tree_workspace_zero_bytes(16, 32, 128256, 4, sv.SV_BF16, -1.0, 0) == 0
