@@ -22,6 +22,9 @@ arrays into it.  The functions and the passages they follow:
 * ``tree_verify`` -- verification of a draft tree by multi-step rejection (first page,
   "Token Tree Verifier"; EAGLE page, section 6.2): siblings are tested in order against
   the current distribution, which each rejection replaces by norm([cur - q]_+).
+* ``typical_verify`` -- Medusa's typical acceptance (first page, "Medusa-1 与 typical
+  acceptance"): the longest prefix of drafted tokens with p(x) > min(eps, delta *
+  exp(-H(p))), then the target's greedy token.
 * ``overlap`` -- per drafted position, beta = sum min(p, q) (the acceptance
   probability, first page, section "为什么接受概率恰好是这个比值"; the overlap behind the
   LK loss and DSpark's c* on the second page) and tv = sum [p - q]_+.
@@ -81,6 +84,8 @@ def _bind(lib):
     lib.ref_overlap.restype = i32
     lib.ref_tree_verify.argtypes = [P, P, i32, P, P, P, P, i32, i32, i32, f64, i32, P, P, P, P, P, i32]
     lib.ref_tree_verify.restype = i32
+    lib.ref_typical_verify.argtypes = [P, i32, P, i32, i32, i32, f64, i32, f64, f64, P, P, P, P, i32]
+    lib.ref_typical_verify.restype = i32
     lib.ref_invcdf.argtypes = [P, i32, f64, P]
     lib.ref_invcdf.restype = i32
     return lib
@@ -253,6 +258,31 @@ def tree_verify(target, draft, tokens, parent, u_accept, u_sample, temperature, 
     if with_diagnostics:
         return acc, out, path, {"accept_margin": am, "sample_margin": sm}
     return acc, out, path
+
+
+def typical_verify(target, draft_tokens, temperature, epsilon, delta, top_k=0, *,
+                   with_diagnostics=False, nthreads=None):
+    """Oracle typical acceptance of B sequences: target [B, G+1, V] logits (float32 or
+    uint16 bf16 bits), draft_tokens [B, G] int32, temperature > 0, epsilon, delta >= 0.
+    Returns (accepted_len [B], out_tokens [B, G+1]) and, with diagnostics, a dict of
+    margin [B, G] (log p(x) - log threshold) and entropy [B, G+1] (nats)."""
+    lib = _load()
+    target, dt = _logits(target)
+    B, G1, V = target.shape
+    G = G1 - 1
+    tok = np.ascontiguousarray(draft_tokens, np.int32).reshape(B, G)
+    acc = np.empty((B,), np.int32)
+    out = np.empty((B, G + 1), np.int32)
+    mg = np.empty((B, G), np.float64)
+    ent = np.empty((B, G + 1), np.float64)
+    rc = lib.ref_typical_verify(_ptr(target), dt, _ptr(tok), B, G, V, float(temperature), int(top_k),
+                                float(epsilon), float(delta), _ptr(acc), _ptr(out), _ptr(mg), _ptr(ent),
+                                int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments (typical acceptance needs T > 0, eps, delta >= 0)")
+    if with_diagnostics:
+        return acc, out, {"margin": mg, "entropy": ent}
+    return acc, out
 
 
 def overlap(target, draft, temperature, top_k=0, *, nthreads=None):

@@ -52,6 +52,13 @@
  *      the token is drawn from the current distribution; at a leaf the bonus comes from
  *      p_u.  Greedy (T = 0): the first child whose token is argmax p_u is accepted, else
  *      argmax p_u is emitted.
+ *   R17 typical acceptance ("Speculative Decoding 的朴素思想", section "Medusa-1 与 typical
+ *      acceptance"): drafted token x_i is accepted when p_i(x_i) > min(eps, delta *
+ *      exp(-H(p_i))), H the entropy (natural log) of the policy distribution p_i; the
+ *      accepted prefix is the longest run of accepted positions, and the token after it
+ *      is the target's greedy choice argmax p_{j+1} (the "first token, greedy, accepted
+ *      directly" of the next candidate).  Defined for T > 0; eps, delta >= 0 are the
+ *      caller's.  Not distribution-preserving (the same section says so).
  *   R15 the overlap of a position is taken between the two distributions the
  *      verification compares there: p_i and q_i after the same temperature and top-k.
  *      It is defined for T > 0 only (at T = 0 the policy is a deterministic choice).
@@ -651,6 +658,83 @@ int ref_tree_verify(const void *target, const void *draft, int dtype, const int3
     free(keep_t);
     free(keep_d);
     free(nchild);
+  }
+  return 0;
+}
+
+/* ---- typical acceptance (R17) --------------------------------------------------- */
+
+/* Entropy in nats of the policy distribution P (terms with P = 0 contribute 0). */
+static double entropy(const double *P, int V) {
+  double h = 0.0;
+  for (int v = 0; v < V; ++v)
+    if (P[v] > 0.0) h -= P[v] * log(P[v]);
+  return h;
+}
+
+/* Batched typical acceptance.  target [B, G+1, V], tokens [B, G]; T > 0.  Outputs
+ * accepted_len [B] (0..G, or -1 token outside [0,V) / -3 an unusable target row, checked
+ * in that order over all positions) and out_tokens [B, G+1] (the accepted drafts, then
+ * argmax p_{j+1}, then -1).  margin [B, G] (nullable): log p_i(x_i) - log(threshold) of
+ * every position, +inf where the threshold is 0, NaN where not formed.  entropy_out [B,
+ * G+1] (nullable): H of every target row.  Returns -1 for arguments it cannot process. */
+int ref_typical_verify(const void *target, int dtype, const int32_t *tokens, int B, int G, int V,
+                       double T, int top_k, double eps, double delta, int32_t *accepted_len,
+                       int32_t *out_tokens, double *margin, double *entropy_out, int nthreads) {
+  if (B < 0 || G < 0 || V < 1 || !(T > 0.0) || !(eps >= 0.0) || !(delta >= 0.0)) return -1;
+  if (nthreads < 1) nthreads = 1;
+#pragma omp parallel num_threads(nthreads)
+  {
+    double *z = (double *)malloc(sizeof(double) * (size_t)V);
+    double *P = (double *)malloc(sizeof(double) * (size_t)V);
+#pragma omp for schedule(dynamic, 1)
+    for (int b = 0; b < B; ++b) {
+      const int32_t *x = tokens + (size_t)b * G;
+      int32_t *out = out_tokens + (size_t)b * (G + 1);
+      const size_t row0 = (size_t)b * (G + 1);
+      if (margin)
+        for (int i = 0; i < G; ++i) margin[(size_t)b * G + i] = NAN;
+      if (entropy_out)
+        for (int i = 0; i <= G; ++i) entropy_out[row0 + i] = NAN;
+      int err = 0;
+      for (int i = 0; i < G && !err; ++i)
+        if (x[i] < 0 || x[i] >= V) err = REF_ERR_TOKEN;
+      for (int i = 0; i <= G && !err; ++i) {
+        load_row(target, dtype, row0 + i, V, z);
+        if (!row_is_valid(z, V)) err = REF_ERR_ROW;
+      }
+      if (err) {
+        accepted_len[b] = err;
+        fill_tokens(out, G + 1, -1);
+        continue;
+      }
+      if (entropy_out)
+        for (int i = 0; i <= G; ++i) {
+          load_row(target, dtype, row0 + i, V, z);
+          policy(z, V, T, top_k, NULL, P);
+          entropy_out[row0 + i] = entropy(P, V);
+        }
+      int j = G;
+      for (int i = 0; i < G; ++i) {
+        load_row(target, dtype, row0 + i, V, z);
+        policy(z, V, T, top_k, NULL, P);
+        const double H = entropy(P, V);
+        const double thr = fmin(eps, delta * exp(-H));
+        const double px = P[x[i]];
+        if (margin) margin[(size_t)b * G + i] = (thr > 0.0) ? log(px) - log(thr) : INFINITY;
+        if (!(px > thr)) { /* the first position that is not typical ends the prefix */
+          j = i;
+          break;
+        }
+      }
+      for (int i = 0; i < j; ++i) out[i] = x[i];
+      load_row(target, dtype, row0 + j, V, z);
+      out[j] = argmax_lowest(z, V); /* the next token: the target's greedy choice */
+      fill_tokens(out + j + 1, G - j, -1);
+      accepted_len[b] = j;
+    }
+    free(z);
+    free(P);
   }
   return 0;
 }

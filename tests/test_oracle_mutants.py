@@ -14,6 +14,7 @@ import oracle
 import test_oracle_pins as pins
 import test_oracle_overlap as ovl
 import test_oracle_tree as tree
+import test_oracle_typical as typ
 import test_oracle_stats as stats
 
 SRC = Path(oracle.__file__).resolve().parent / "spec_verify_ref.c"
@@ -66,6 +67,13 @@ MUTANTS = [
      "for (int s = u + 1; s < N; ++s)\n            if (par[s] == u && x[s] == a) next = s;"),
     ("tree_uniform_index", "const double us = (double)u_accept[row0 + s];", "const double us = (double)u_accept[row0 + s - 1];"),
     ("tree_leaf_draft_checked", "if (!nchild[n]) continue;\n          load_row(draft", "load_row(draft"),
+    ("typical_non_strict", "if (!(px > thr)) {", "if (!(px >= thr)) {"),
+    ("typical_max_threshold", "const double thr = fmin(eps, delta * exp(-H));", "const double thr = fmax(eps, delta * exp(-H));"),
+    ("typical_exp_sign", "const double thr = fmin(eps, delta * exp(-H));", "const double thr = fmin(eps, delta * exp(H));"),
+    ("typical_entropy_bits", "if (P[v] > 0.0) h -= P[v] * log(P[v]);", "if (P[v] > 0.0) h -= P[v] * log2(P[v]);"),
+    ("typical_next_from_previous_row", "load_row(target, dtype, row0 + j, V, z);\n      out[j] = argmax_lowest(z, V);",
+     "load_row(target, dtype, row0 + (j ? j - 1 : 0), V, z);\n      out[j] = argmax_lowest(z, V);"),
+    ("typical_wrong_token", "const double px = P[x[i]];", "const double px = P[x[i ? i - 1 : 0]];"),
 ]
 
 PIN_TESTS = [
@@ -101,6 +109,11 @@ PIN_TESTS = [
     lambda: tree.test_greedy_tree_walk(),
     lambda: tree.test_tree_checks("nan_draft_leaf", 0),
     lambda: tree.test_monte_carlo_tree_law_matches_target((3,), 1.0, 0),
+    lambda: typ.test_entropy_matches_scipy(1.0, 0),
+    lambda: typ.test_uniform_rows_closed_form(),
+    lambda: typ.test_threshold_sides(1),
+    lambda: typ.test_threshold_sides(-1),
+    lambda: typ.test_near_one_hot_is_greedy_chain(),
 ]
 
 
