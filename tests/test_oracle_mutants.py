@@ -111,6 +111,7 @@ PIN_TESTS = [
     lambda: tree.test_monte_carlo_tree_law_matches_target((3,), 1.0, 0),
     lambda: typ.test_entropy_matches_scipy(1.0, 0),
     lambda: typ.test_uniform_rows_closed_form(),
+    lambda: typ.test_equality_rejects(),
     lambda: typ.test_threshold_sides(1),
     lambda: typ.test_threshold_sides(-1),
     lambda: typ.test_near_one_hot_is_greedy_chain(),

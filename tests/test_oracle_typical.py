@@ -79,6 +79,17 @@ def test_threshold_sides(side):
         assert acc[0] == (1 if side > 0 else 0)
 
 
+def test_equality_rejects():
+    """The comparison is strict: p(x) equal to the threshold rejects (uniform row over 4
+    tokens, p(x) = 0.25 exactly, eps = 0.25 below delta / 4)."""
+    V = 16
+    t = np.stack([uniform_row(V, np.arange(4)), uniform_row(V, np.arange(4))])[None]
+    acc, out = oracle.typical_verify(t, np.array([[2]], np.int32), 1.0, 0.25, 10.0)
+    assert acc[0] == 0 and out[0, 0] == 0
+    acc, _ = oracle.typical_verify(t, np.array([[2]], np.int32), 1.0, 0.2499, 10.0)
+    assert acc[0] == 1
+
+
 def test_near_one_hot_is_greedy_chain():
     """At a tiny temperature every row is nearly one-hot (H ~ 0, p(argmax) ~ 1): with
     min(eps, delta) < 1 the rule accepts exactly the drafts equal to the argmax, as greedy
