@@ -44,6 +44,10 @@ COUNTED = {
                     alg=131334144, sources=("spec_overlap.hip",) + _SHARED),
     "sample": dict(kernel="k_verify", workload="sample_bf16_b256", desc="B=256, V=128256, bf16",
                    alg=65667072, sources=("spec_verify.hip",) + _SHARED),
+    "tree": dict(kernel="k_tree_rows", workload="tree_bf16_b16_n32", desc="16 trees of 32 nodes, V=128256, bf16",
+                 alg=210698956, sources=("spec_tree.hip", "sv_draw.h") + _SHARED),
+    "typical": dict(kernel="k_typical", workload="typical_zipf_bf16_b64", desc="B=64, G=4, V=128256, bf16",
+                    alg=82083840, sources=("spec_typical.hip",) + _SHARED),
 }
 
 
@@ -583,7 +587,7 @@ def run_tree(args, dev, hev):
         "gpu_event_ms_per_step": round(gpu_ms / K, 5),
         "per_kernel_us": {k: round(v, 3) for k, v in per_kernel.items()},
         "ms_per_step_with_kernel_events": None if wall2 is None else round(wall2 * 1e3 / K, 5),
-        "roofline": roofline(per_kernel, "k_tree_rows", alg_bytes, None),
+        "roofline": roofline(per_kernel, "k_tree_rows", alg_bytes, counters_traffic("tree")[0]),
     }
     if not args.no_cpu_baseline:
         import oracle
@@ -606,14 +610,84 @@ def run_tree(args, dev, hev):
     return res
 
 
+def run_typical(args, dev, hev):
+    """Typical acceptance of the headline batch (B=64, G=4, V=128256 bf16, T=1, eps = 0.1,
+    delta = 0.3): positions per second."""
+    import torch
+    import rejection_sampling_verify_02_amd as sv
+    from rejection_sampling_verify_02_amd import workloads as wl
+
+    cfg = wl.CONFIGS[3]
+    B, G, V = cfg.B, cfg.G, cfg.V
+    eps, delta = 0.1, 0.3
+    esz = 2 if cfg.dtype == "bf16" else 4
+    alg_bytes = B * (G + 1) * V * esz  # one read of every target row
+    n_sets = args.sets or max(2, -(-(1 << 30) // alg_bytes))
+    log(f"[bench] typical acceptance on {cfg.name}: {alg_bytes / 1e6:.2f} MB per call, {n_sets} input sets")
+    sets, host = make_sets(3, n_sets, dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    dtc = sv.SV_BF16 if cfg.dtype == "bf16" else sv.SV_F32
+    plan = sv.sv_typical_launch_plan(B, G, V, dtc, cfg.temperature, cfg.top_k)
+    ws = sv.Workspace()
+    outs = (torch.empty((B,), dtype=torch.int32, device=dev), torch.empty((B, G + 1), dtype=torch.int32, device=dev))
+
+    def call(i, events=None):
+        s = sets[i % n_sets]
+        return sv.spec_typical_verify(s["target"], s["tokens"], cfg.temperature, eps, delta, cfg.top_k,
+                                      workspace=ws, stream=stream, out=outs, events=events)
+
+    K = args.steps
+    wall, gpu_ms, per_kernel, wall2 = time_loop(call, plan, K, args.warmup, stream, dev, hev,
+                                                not args.no_stage_events)
+    t_call = wall / K
+    acc = []
+    for i in range(min(n_sets, 8)):
+        call(i)
+        acc.append(float(outs[0].float().mean().item()))
+    res = {
+        "metric": "typical-acceptance positions/sec and achieved HBM GB/s (% of peak) at B=64,V=128k",
+        "value": round(B * G / t_call, 1), "unit": "positions/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(t_call * 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "typical_" + cfg.name, "B": B, "G": G, "V": V, "logits": cfg.dtype,
+                   "temperature": cfg.temperature, "top_k": cfg.top_k, "epsilon": eps, "delta": delta,
+                   "input_sets": n_sets, "set_bytes": alg_bytes},
+        "call_GBs": round(alg_bytes / t_call / 1e9, 1),
+        "call_frac_of_peak": round(alg_bytes / t_call / 1e9 / PEAK_HBM_GBS, 4),
+        "mean_accepted": round(float(np.mean(acc)), 4),
+        "gpu_event_ms_per_step": round(gpu_ms / K, 5),
+        "per_kernel_us": {k: round(v, 3) for k, v in per_kernel.items()},
+        "ms_per_step_with_kernel_events": None if wall2 is None else round(wall2 * 1e3 / K, 5),
+        "roofline": roofline(per_kernel, "k_typical", alg_bytes, counters_traffic("typical")[0]),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle._load()
+        threads = oracle.default_threads()
+        calls, t0 = 0, time.perf_counter()
+        while True:
+            h = host[calls % len(host)]
+            oracle.typical_verify(h["target"], h["tokens"], cfg.temperature, eps, delta, cfg.top_k, nthreads=threads)
+            calls += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds:
+                break
+        res["cpu_baseline"] = {"value": B * G * calls / el, "unit": "positions/s", "cores": threads,
+                               "kind": "oracle", "sample": f"{calls} full calls (B={B}, G={G}, V={V}) over "
+                                                           f"{min(calls, len(host))} input sets, {el:.1f} s"}
+    else:
+        res["cpu_baseline"] = None
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--op", default="verify", choices=["verify", "sample", "overlap", "tree"],
+    ap.add_argument("--op", default="verify", choices=["verify", "sample", "overlap", "tree", "typical"],
                     help="verify (the default, the headline), the batched sampler, the per-position overlap, "
-                         "or tree verification")
+                         "tree verification, or typical acceptance")
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5],
                     help="verification workload (3, the default, is the headline; 4 greedy and 5 top-k "
                          "are timed for the design notes)")
@@ -645,7 +719,8 @@ def main() -> int:
     sv.load_library()  # raises if the HIP library is not built
     dev = torch.device("cuda:0")
     hev = HipEvents()
-    run = {"sample": run_sample, "overlap": run_overlap, "tree": run_tree}.get(args.op, run_verify)
+    run = {"sample": run_sample, "overlap": run_overlap, "tree": run_tree,
+           "typical": run_typical}.get(args.op, run_verify)
     res = run(args, dev, hev)
     print(json.dumps(res), flush=True)
     return 0

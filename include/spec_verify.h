@@ -50,7 +50,8 @@ typedef enum {
   SV_ERR_TEMPERATURE = 4, /* temperature negative, NaN or infinite                       */
   SV_ERR_WORKSPACE = 5,   /* workspace smaller than sv_workspace_bytes() or misaligned    */
   SV_ERR_ALIGN = 6,       /* a logit pointer is not aligned to its element size           */
-  SV_ERR_LAUNCH = 7       /* the HIP runtime refused a kernel launch                       */
+  SV_ERR_LAUNCH = 7,      /* the HIP runtime refused a kernel launch                       */
+  SV_ERR_PARAM = 8        /* spec_typical_verify: epsilon or delta negative or not finite   */
 } sv_status;
 
 /* Row-level codes written into accepted_len[b] instead of a length; the whole row of
@@ -271,6 +272,50 @@ sv_status spec_tree_verify_timed(const void *target_logits, const void *draft_lo
 /* Names of the kernels spec_tree_verify would launch, ';'-separated (static storage). */
 const char *sv_tree_launch_plan(int32_t B, int32_t N, int32_t V, int32_t max_children,
                                 sv_dtype dtype, float temperature, int32_t top_k);
+
+/* ---- typical acceptance ----
+ *
+ * Medusa's typical acceptance ("Speculative Decoding 的朴素思想", section "Medusa-1 与
+ * typical acceptance"): drafted token x_i is accepted when
+ *   p_i(x_i) > min(epsilon, delta * exp(-H(p_i))),
+ * with p_i the target's distribution at position i after temperature and top-k (as in
+ * spec_verify) and H its entropy in nats.  The accepted prefix is the longest run of
+ * accepted positions; the token after it is the target's greedy choice argmax p_{j+1}
+ * (lowest index on ties).  Not distribution-preserving; reads no draft logits and no
+ * uniforms.
+ *   target_logits [B, G+1, V] dtype
+ *   draft_tokens  [B, G] int32 (may be NULL when G == 0)
+ *   temperature   T > 0 (T == 0 is SV_ERR_TEMPERATURE: use spec_verify's greedy mode)
+ *   epsilon, delta >= 0 and finite (else SV_ERR_PARAM); epsilon = 0 accepts every token
+ *                 with p > 0
+ *   accepted_len  [B] int32 out: 0..G, or SV_ROW_BAD_TOKEN / SV_ROW_BAD_LOGITS (any of
+ *                 the G+1 rows) / SV_ROW_INTERNAL
+ *   out_tokens    [B, G+1] int32 out: accepted drafts, then argmax p_{j+1}, then -1
+ * G is at most 256.  Workspace: sv_typical_workspace_bytes(...) bytes, 256-byte aligned,
+ * first sv_typical_workspace_zero_bytes(...) bytes zero, under spec_verify's rules. */
+size_t sv_typical_workspace_bytes(int32_t B, int32_t G, int32_t V, sv_dtype dtype,
+                                  float temperature, int32_t top_k);
+size_t sv_typical_workspace_zero_bytes(int32_t B, int32_t G, int32_t V, sv_dtype dtype,
+                                       float temperature, int32_t top_k);
+sv_status spec_typical_verify(const void *target_logits, sv_dtype dtype,
+                              const int32_t *draft_tokens, int32_t B, int32_t G, int32_t V,
+                              float temperature, int32_t top_k, float epsilon, float delta,
+                              int32_t *accepted_len, int32_t *out_tokens, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/* spec_typical_verify with each kernel dispatch bracketed by caller-owned HIP events, as in
+ * spec_verify_timed. */
+sv_status spec_typical_verify_timed(const void *target_logits, sv_dtype dtype,
+                                    const int32_t *draft_tokens, int32_t B, int32_t G,
+                                    int32_t V, float temperature, int32_t top_k, float epsilon,
+                                    float delta, int32_t *accepted_len, int32_t *out_tokens,
+                                    void *workspace, size_t workspace_bytes, void *stream,
+                                    void *const *events, int32_t n_events,
+                                    int32_t *n_launched);
+
+/* Names of the kernels spec_typical_verify would launch, ';'-separated (static storage). */
+const char *sv_typical_launch_plan(int32_t B, int32_t G, int32_t V, sv_dtype dtype,
+                                   float temperature, int32_t top_k);
 
 /* Human-readable text of a status (static storage). */
 const char *sv_status_string(sv_status status);

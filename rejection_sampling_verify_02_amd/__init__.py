@@ -23,14 +23,17 @@ ROW_BAD_TOKEN, ROW_Q_ZERO, ROW_BAD_LOGITS, ROW_BAD_UNIFORM, ROW_INTERNAL, ROW_BA
 MAX_LAUNCHES = 8
 
 _STATUS = {0: "SV_OK", 1: "SV_ERR_NULL", 2: "SV_ERR_SHAPE", 3: "SV_ERR_DTYPE",
-           4: "SV_ERR_TEMPERATURE", 5: "SV_ERR_WORKSPACE", 6: "SV_ERR_ALIGN", 7: "SV_ERR_LAUNCH"}
+           4: "SV_ERR_TEMPERATURE", 5: "SV_ERR_WORKSPACE", 6: "SV_ERR_ALIGN", 7: "SV_ERR_LAUNCH",
+           8: "SV_ERR_PARAM"}
 
 EXPORTED = ("spec_verify", "spec_verify_timed", "sv_workspace_bytes", "sv_workspace_zero_bytes",
             "sv_status_string", "sv_launch_plan", "spec_sample", "spec_sample_timed",
             "spec_overlap", "spec_overlap_timed", "sv_overlap_workspace_bytes",
             "sv_overlap_workspace_zero_bytes", "sv_overlap_launch_plan",
             "spec_tree_verify", "spec_tree_verify_timed", "sv_tree_workspace_bytes",
-            "sv_tree_workspace_zero_bytes", "sv_tree_launch_plan")
+            "sv_tree_workspace_zero_bytes", "sv_tree_launch_plan",
+            "spec_typical_verify", "spec_typical_verify_timed", "sv_typical_workspace_bytes",
+            "sv_typical_workspace_zero_bytes", "sv_typical_launch_plan")
 
 
 class SpecVerifyError(RuntimeError):
@@ -82,6 +85,16 @@ def load_library(path: Path | str | None = None) -> ctypes.CDLL:
         fn.restype = SZ
     lib.sv_tree_launch_plan.argtypes = [I32, I32, I32, I32, I32, F32, I32]
     lib.sv_tree_launch_plan.restype = ctypes.c_char_p
+    typ = [V, I32, V, I32, I32, I32, F32, I32, F32, F32, V, V, V, SZ, V]
+    lib.spec_typical_verify.argtypes = typ
+    lib.spec_typical_verify.restype = I32
+    lib.spec_typical_verify_timed.argtypes = typ + [V, I32, V]
+    lib.spec_typical_verify_timed.restype = I32
+    for fn in (lib.sv_typical_workspace_bytes, lib.sv_typical_workspace_zero_bytes):
+        fn.argtypes = [I32, I32, I32, I32, F32, I32]
+        fn.restype = SZ
+    lib.sv_typical_launch_plan.argtypes = [I32, I32, I32, I32, F32, I32]
+    lib.sv_typical_launch_plan.restype = ctypes.c_char_p
     lib.sv_workspace_bytes.argtypes = [I32, I32, I32, I32, F32, I32]
     lib.sv_workspace_bytes.restype = SZ
     lib.sv_workspace_zero_bytes.argtypes = [I32, I32, I32, I32, F32, I32]
@@ -123,6 +136,10 @@ def sv_tree_launch_plan(B: int, N: int, V: int, max_children: int, dtype: int, t
                        top_k: int = 0) -> list[str]:
     s = load_library().sv_tree_launch_plan(B, N, V, max_children, dtype, float(temperature), int(top_k)).decode()
     return s.split(";")
+
+
+def sv_typical_launch_plan(B: int, G: int, V: int, dtype: int, temperature: float, top_k: int = 0) -> list[str]:
+    return load_library().sv_typical_launch_plan(B, G, V, dtype, float(temperature), int(top_k)).decode().split(";")
 
 
 # ------------------------------------------------------------------ workspace
@@ -411,3 +428,49 @@ def spec_tree_verify(target_logits, draft_logits, tokens, parent, u_accept, u_sa
         raise SpecVerifyError(rc, sv_status_string(rc))
     wso.called(dev, zbytes)
     return (acc, toks, path) if events is None else (acc, toks, path, nl)
+
+
+def spec_typical_verify(target_logits, draft_tokens, temperature: float, epsilon: float, delta: float,
+                        top_k: int = 0, *, workspace: Workspace | None = None, stream=None, out=None,
+                        events=None):
+    """Typical acceptance on the GPU (see include/spec_verify.h): target logits [B, G+1, V]
+    (bfloat16 or float32), draft_tokens [B, G] int32.  Returns (accepted_len [B],
+    out_tokens [B, G+1]) int32 tensors; ``out`` may supply them; ``events`` as for
+    spec_verify."""
+    import torch
+    lib = load_library()
+    dev = target_logits.device
+    if dev.type != "cuda":
+        raise ValueError("logits must be device tensors")
+    dt = _dtype_code(target_logits)
+    if target_logits.dim() != 3:
+        raise ValueError("target must be [B, G+1, V]")
+    B, G1, V = target_logits.shape
+    G = G1 - 1
+    _check(target_logits, "target_logits", (B, G1, V), target_logits.dtype, dev)
+    _check(draft_tokens, "draft_tokens", (B, G), torch.int32, dev)
+    if out is not None:
+        acc, toks = out
+    else:
+        acc = torch.empty((B,), dtype=torch.int32, device=dev)
+        toks = torch.empty((B, G1), dtype=torch.int32, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    nbytes = int(lib.sv_typical_workspace_bytes(B, G, V, dt, float(temperature), int(top_k)))
+    zbytes = int(lib.sv_typical_workspace_zero_bytes(B, G, V, dt, float(temperature), int(top_k)))
+    wso = workspace or _default_ws
+    ws = wso.get(nbytes, zbytes, dev, stream)
+    args = [_ptr(target_logits), dt, _ptr(draft_tokens), B, G, V, float(temperature), int(top_k), float(epsilon),
+            float(delta), _ptr(acc), _ptr(toks), _ptr(ws), ws.numel(), ctypes.c_void_p(stream)]
+    if events is None:
+        rc = lib.spec_typical_verify(*args)
+        nl = None
+    else:
+        arr = (ctypes.c_void_p * len(events))(*events)
+        n = ctypes.c_int32(0)
+        rc = lib.spec_typical_verify_timed(*args, arr, len(events), ctypes.byref(n))
+        nl = n.value
+    if rc != 0:
+        raise SpecVerifyError(rc, sv_status_string(rc))
+    wso.called(dev, zbytes)
+    return (acc, toks) if events is None else (acc, toks, nl)

@@ -1233,6 +1233,7 @@ const char *sv_status_string(sv_status status) {
     case SV_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
     case SV_ERR_ALIGN: return "logit pointer not aligned to its element size";
     case SV_ERR_LAUNCH: return "kernel launch failed";
+    case SV_ERR_PARAM: return "epsilon and delta must be finite and >= 0";
   }
   return "unknown status";
 }

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(8):
+    for code in range(9):
         s = sv.sv_status_string(code)
         assert s and s != "unknown status"
     assert sv.sv_status_string(99) == "unknown status"
@@ -218,3 +218,34 @@ def test_tree_optional_pointers_and_plan(lib):
     n, z = lib.sv_tree_workspace_bytes(*args), lib.sv_tree_workspace_zero_bytes(*args)
     assert 0 < z < n and z % 256 == 0 and n % 256 == 0
     assert lib.sv_tree_workspace_zero_bytes(16, 32, 128256, 4, sv.SV_BF16, -1.0, 0) == 0
+
+
+def call_typ(lib, **kw):
+    a = dict(t=FAKE, dt=sv.SV_BF16, tok=FAKE, B=4, G=3, V=1024, T=1.0, k=0, eps=0.1, delta=0.3, acc=FAKE,
+             out=FAKE, ws=FAKE, nbytes=1 << 30, stream=None)
+    a.update(kw)
+    return lib.spec_typical_verify(V_(a["t"]), a["dt"], V_(a["tok"]), a["B"], a["G"], a["V"], F_(a["T"]), a["k"],
+                                   F_(a["eps"]), F_(a["delta"]), V_(a["acc"]), V_(a["out"]), V_(a["ws"]),
+                                   Z_(a["nbytes"]), V_(a["stream"]))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), 2), (dict(G=-1), 2), (dict(G=257), 2), (dict(V=0), 2), (dict(dt=9), 3), (dict(T=0.0), 4),
+    (dict(T=float("inf")), 4), (dict(eps=-0.1), 8), (dict(delta=float("nan")), 8), (dict(eps=float("inf")), 8),
+    (dict(t=None), 1), (dict(tok=None), 1), (dict(acc=None), 1), (dict(out=None), 1), (dict(ws=None), 1),
+    (dict(t=FAKE + 1), 6), (dict(nbytes=16), 5),
+])
+def test_typical_host_argument_errors(lib, kw, status):
+    assert call_typ(lib, **kw) == status
+
+
+def test_typical_plan_and_workspace(lib):
+    assert call_typ(lib, G=0, tok=None, nbytes=16) == 5
+    assert call_typ(lib, G=256, nbytes=16) == 5
+    assert call_typ(lib, eps=0.0, delta=0.0, nbytes=16) == 5
+    assert sv.sv_typical_launch_plan(64, 4, 128256, sv.SV_BF16, 1.0, 0) == ["k_typical"]
+    assert sv.sv_typical_launch_plan(64, 4, 128256, sv.SV_BF16, 1.0, 50) == ["k_topk_digit"] * 2 + ["k_typical"]
+    args = (64, 4, 128256, sv.SV_BF16, 1.0, 0)
+    n, z = lib.sv_typical_workspace_bytes(*args), lib.sv_typical_workspace_zero_bytes(*args)
+    assert z == n == 320 * 8 * 8 * 8  # 320 rows of 8 chunks, 8 words each
+    assert lib.sv_typical_workspace_zero_bytes(64, 4, 128256, sv.SV_BF16, 0.0, 0) == 0
