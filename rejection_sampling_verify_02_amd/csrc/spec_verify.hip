@@ -248,7 +248,7 @@ SVD void greedy_finish(const Args &a, int b, float own_best, int own_idx, int ow
 // partial (index np - 1) and token logit come from its registers.
 template <typename T, bool ALIGNED, bool TOPK, bool LDS, bool G0>
 SVD void sampling_finish(const Args &a, int b, float own_off, float own_hi, float own_lo,
-                         bool own_tok, float own_zx, const double *s_own_gseg) {
+                         int gx, float gzt, float gzd, const double *s_own_gseg) {
   constexpr int UNR = SEQ_LDS_PARTS / WAVE;
   constexpr int RUNR = (SEQ_LDS_ROWS + WAVE - 1) / WAVE;
   __shared__ float s_po[SEQ_LDS_PARTS];
@@ -263,25 +263,29 @@ SVD void sampling_finish(const Args &a, int b, float own_off, float own_hi, floa
   constexpr bool lds = LDS;  // the sequence fits in LDS (every access below is resolved at compile time)
   const unsigned tag = a.tag;
   const u64 *pw = a.w.tw_part + r0 * C * 3;
-  const u64 *zw = a.w.tw_zx + r0;
 
-  // inputs of positions lane, lane+64, ... (first round only kept in registers)
-  const int x0 = (lane < G) ? a.tokens[(size_t)b * G + lane] : 0;
+  // inputs of positions lane, lane+64, ... (first round only kept in registers; the
+  // tokens and their logits of the first round were loaded while this item's chunk
+  // streamed in)
+  const int x0 = gx;
   const float u0 = (lane < G) ? a.u_accept[(size_t)b * G + lane] : 0.0f;
   const float us = a.u_sample[b];
-  // Which rows publish a token logit: rows with a position whose token is in range.
-  auto row_token = [&](int jr) -> int {
-    const int pos = (jr < G) ? jr : (jr > G ? jr - G - 1 : -1);
-    return (pos < 0) ? -1 : a.tokens[(size_t)b * G + pos];
-  };
-  auto needs_zx = [&](int jr) {
-    if (jr >= rps || jr == G || (jr == rps - 1 && own_tok)) return false;
-    const int x = row_token(jr);
-    return x >= 0 && x < a.V;
+  // The logit of position p's token in target row p and draft row p (NaN for a token
+  // outside [0, V)); positions of the first round come from registers.
+  auto gather_zx = [&](int p, float &zt, float &zd) {
+    if (p < WAVE) {
+      zt = gzt;
+      zd = gzd;
+      return;
+    }
+    const int x = a.tokens[(size_t)b * G + p];
+    const bool in = x >= 0 && x < a.V;
+    zt = in ? Fmt<T>::at(seq_row<T>(a, b, p), (size_t)x) : NAN;
+    zd = in ? Fmt<T>::at(seq_row<T>(a, b, G + 1 + p), (size_t)x) : NAN;
   };
 
   // Wait for the partials (blocks of SEQ_LDS_PARTS, every load of a block in flight at
-  // once) and the token logits; stage them in LDS when the sequence fits.
+  // once); stage them in LDS when the sequence fits.
   bool alive = true;
   unsigned polls = 0;
   for (int blk = 0; blk < np && alive; blk += SEQ_LDS_PARTS) {
@@ -321,38 +325,15 @@ SVD void sampling_finish(const Args &a, int b, float own_off, float own_hi, floa
       __builtin_amdgcn_s_sleep(2);
     }
   }
-  for (int rb = 0; rb < rps && alive; rb += RUNR * WAVE) {
-    for (;;) {
-      u64 wz[RUNR];
-      bool need[RUNR];
-#pragma unroll
-      for (int k = 0; k < RUNR; ++k) {
-        const int jr = rb + lane + k * WAVE;
-        need[k] = needs_zx(jr);
-        wz[k] = ld_dev(&zw[need[k] ? jr : 0]);
-      }
-      bool ok = true;
-#pragma unroll
-      for (int k = 0; k < RUNR; ++k) ok = ok && (!need[k] || tw_ok(wz[k], tag));
-      if (__ballot(!ok) == 0) {
-        if (lds) {
-#pragma unroll
-          for (int k = 0; k < RUNR; ++k) {
-            const int jr = lane + k * WAVE;
-            if (jr < rps) {
-              s_rzx[jr] = need[k] ? tw_f(wz[k]) : ((jr == rps - 1 && own_tok) ? own_zx : NAN);
-              s_rtau[jr] = TOPK ? a.w.row_tau[r0 + jr] : -INFINITY;  // top-k: the previous kernel's
-            }
-          }
-        }
-        break;
-      }
-      if (++polls >= a.spin_limit) {
-        alive = false;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(2);
+  if (lds && alive) {
+    for (int jr = lane; jr < rps; jr += WAVE) s_rtau[jr] = TOPK ? a.w.row_tau[r0 + jr] : -INFINITY;
+    for (int p = lane; p < G; p += WAVE) {
+      float zt, zd;
+      gather_zx(p, zt, zd);
+      s_rzx[p] = zt;
+      s_rzx[G + 1 + p] = zd;
     }
+    if (lane == 0) s_rzx[G] = NAN;
   }
   lds_sync();
   u64 *jw = a.w.tw_job + (size_t)b * JW;
@@ -377,8 +358,10 @@ SVD void sampling_finish(const Args &a, int b, float own_off, float own_hi, floa
   };
   auto zx_of = [&](int jr) -> float {
     if (lds) return s_rzx[jr];
-    if (jr == rps - 1 && own_tok) return own_zx;
-    return needs_zx(jr) ? tw_f(ld_dev(&zw[jr])) : NAN;
+    if (jr == G) return NAN;
+    float zt, zd;
+    gather_zx(jr < G ? jr : jr - G - 1, zt, zd);
+    return jr < G ? zt : zd;
   };
   auto tau_of = [&](int jr) -> float { return lds ? s_rtau[jr] : (TOPK ? a.w.row_tau[r0 + jr] : -INFINITY); };
 
@@ -621,18 +604,45 @@ SVD void norm_item(const Args &a, int item) {
   const int r = item / a.C, c = item - r * a.C;
   const int b = r / a.rps, jr = r - b * a.rps;
 
-  // The drafted token of this row's position: its load is issued first and lands while
-  // the chunk streams in; the chunk holding the token publishes the logit there for the
-  // acceptance scan.  Thread 0 of every chunk issues that one-element load (at a safe
-  // index when the token lies elsewhere) after the streaming loads, and it is consumed
-  // only at publication time, so nothing waits for it on the way.
-  const int pos = (jr < a.G) ? jr : (jr > a.G ? jr - a.G - 1 : -1);
-  const int xt = (pos >= 0) ? a.tokens[(size_t)b * a.G + pos] : -1;
+  // The sequence's finisher (its last item) gathers the drafted tokens and their logits
+  // in every target and draft row (positions = lanes of wave 0) while its own chunk
+  // streams in: the token loads go first, the gathers right after the chunk's loads,
+  // before any of them is waited for.
+  const bool finisher = (jr == a.rps - 1 && c == a.C - 1);
+  const bool gath = finisher && !G0 && wid == 0 && lane < a.G;
+  const int gx = gath ? a.tokens[(size_t)b * a.G + lane] : 0;
   const T *row = seq_row<T>(a, b, jr);
   float x[VPT][VEC];
-  load_chunk<T, ALIGNED, true>(row, a.V, a.nvec, c, tid, x);
-  const bool tok_here = xt >= 0 && xt < a.V && (xt / Fmt<T>::VEC) / CHUNK_VECS == c;
-  const float zx = Fmt<T>::at(row, (size_t)(tok_here ? xt : 0));
+  float gzt = NAN, gzd = NAN;
+  if (ALIGNED) {
+    u32x4 w[VPT];
+    const u32x4 *rv = reinterpret_cast<const u32x4 *>(row);
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const int v = c * CHUNK_VECS + k * NT + tid;
+      w[k] = __builtin_nontemporal_load(rv + (v < a.nvec ? v : a.nvec - 1));
+    }
+    if (finisher && gath && gx >= 0 && gx < a.V) {
+      gzt = Fmt<T>::at(seq_row<T>(a, b, lane), (size_t)gx);
+      gzd = Fmt<T>::at(seq_row<T>(a, b, a.G + 1 + lane), (size_t)gx);
+    }
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) Fmt<T>::unpack(w[k], x[k]);
+    if ((c + 1) * CHUNK_VECS > a.nvec) {
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) {
+        const bool in = c * CHUNK_VECS + k * NT + tid < a.nvec;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) x[k][e] = in ? x[k][e] : -INFINITY;
+      }
+    }
+  } else {
+    load_chunk<T, ALIGNED, true>(row, a.V, a.nvec, c, tid, x);
+    if (gath && gx >= 0 && gx < a.V) {
+      gzt = Fmt<T>::at(seq_row<T>(a, b, lane), (size_t)gx);
+      gzd = Fmt<T>::at(seq_row<T>(a, b, a.G + 1 + lane), (size_t)gx);
+    }
+  }
   if (TOPK) {
     const float tau = a.w.row_tau[r];  // written by the previous kernel
 #pragma unroll
@@ -714,14 +724,13 @@ SVD void norm_item(const Args &a, int item) {
   // and the other items' published ones.
   if (jr == a.rps - 1 && c == a.C - 1) {
     if (a.rps * a.C <= SEQ_LDS_PARTS && a.rps <= SEQ_LDS_ROWS)
-      sampling_finish<T, ALIGNED, TOPK, true, G0>(a, b, off, s_hi, s_lo, tok_here, zx, s_gseg);
+      sampling_finish<T, ALIGNED, TOPK, true, G0>(a, b, off, s_hi, s_lo, gx, gzt, gzd, s_gseg);
     else
-      sampling_finish<T, ALIGNED, TOPK, false, G0>(a, b, off, s_hi, s_lo, tok_here, zx, s_gseg);
+      sampling_finish<T, ALIGNED, TOPK, false, G0>(a, b, off, s_hi, s_lo, gx, gzt, gzd, s_gseg);
     return;
   }
   u64 *pw = a.w.tw_part + ((size_t)r * a.C + c) * 3;
   if (lane < 3) tw_putf(pw + lane, a.tag, lane == 0 ? off : (lane == 1 ? s_hi : s_lo));
-  if (lane == 3 && tok_here) tw_putf(&a.w.tw_zx[r], a.tag, zx);
   if (bonus_row && lane < 2 * SEGS) {
     u64 *gw = a.w.tw_gseg + (((size_t)b * a.C + c) * SEGS) * 2;
     const double v = s_gseg[lane >> 1];
@@ -1016,7 +1025,7 @@ struct Plan {
   long long R;
   int digit_passes;
   // workspace offsets
-  size_t tw_part, tw_zx, tw_job, tw_seg, tw_gseg, tw_hist, row_tau, tk_state, total;
+  size_t tw_part, tw_job, tw_seg, tw_gseg, tw_hist, row_tau, tk_state, total;
   size_t zero_bytes;  // leading bytes (tagged words) that must be clean when a call starts
 };
 
@@ -1042,7 +1051,6 @@ bool make_plan(int32_t B, int32_t G, int32_t V, sv_dtype dt, float T, int32_t to
   // in the upper half, so whatever layout wrote them, a tag position holds zero or an
   // earlier tag: never the tag of a call to come.
   p.tw_part = o; o = align256(o + R * C * 3 * 8);
-  p.tw_zx = o; o = align256(o + (smp ? R * 8 : 0));
   p.tw_job = o; o = align256(o + (smp ? Bz * JW * 8 : 0));
   p.tw_seg = o; o = align256(o + (smp ? Bz * C * SEGS * 2 * 8 : 0));
   p.tw_gseg = o; o = align256(o + (smp ? Bz * C * SEGS * 2 * 8 : 0));
@@ -1147,7 +1155,6 @@ sv_status run(const void *target, const void *draft, sv_dtype dt, const int32_t 
   a.tag = 0u;  // each launch takes its own
   a.spin_limit = SPIN_LIMIT;
   a.w.tw_part = (u64 *)(base + p.tw_part);
-  a.w.tw_zx = (u64 *)(base + p.tw_zx);
   a.w.tw_job = (u64 *)(base + p.tw_job);
   a.w.tw_seg = (u64 *)(base + p.tw_seg);
   a.w.tw_gseg = (u64 *)(base + p.tw_gseg);

@@ -17,7 +17,6 @@ struct Work {                  // carved from the caller's workspace
   // tagged words (see tw_put)
   u64 *tw_part;                // [R*C*3] per chunk: sampling offset m_c*k2 and sum of
                                //   2^(z*k2 - off) (head, tail); greedy best value, index, flags
-  u64 *tw_zx;                  // [R] the row's logit at its position's drafted token
   u64 *tw_job;                 // [B*JW] the acceptance scan's record for the draw
   u64 *tw_seg;                 // [B*C*SEGS*2] residual mass per 64-vector segment (head, tail)
   u64 *tw_gseg;                // [B*C*SEGS*2] the bonus row's mass per segment (head, tail)
