@@ -425,28 +425,6 @@ SVD void sampling_finish(const Args &a, int b, float own_off, float own_hi, floa
     }
   };
 
-  // The bonus draw's chunk, in case every draft is accepted: chunk masses of p_G,
-  // S_c * 2^(off_c - off_row) in chunk order, and the remainder in that chunk's scale.
-  int c_bonus = -1;
-  float off_bonus = 0.0f;
-  double t_bonus = 0.0;
-  float oG;
-  double l2G;
-  int okG;
-  r_stat(G, oG, l2G, okG);
-  if (okG) {
-    auto cm = [&](int cc) {
-      const double sc = p_sum(G, cc);
-      return (sc > 0.0) ? sc * (double)fast_exp2(p_off(G, cc) - oG) : 0.0;
-    };
-    double trem, total;
-    c_bonus = wave_pick_frac(C, (double)us, cm, &trem, &total);
-    if (c_bonus >= 0) {
-      off_bonus = p_off(G, c_bonus);
-      t_bonus = trem * (double)fast_exp2(oG - off_bonus);
-    }
-  }
-
   int j = G;
   unsigned flags = 0;  // 1 bad token, 2 bad row, 4 bad uniform, 8 q(x) = 0
   for (int i0 = 0; i0 < G; i0 += WAVE) {
@@ -483,6 +461,10 @@ SVD void sampling_finish(const Args &a, int b, float own_off, float own_hi, floa
     const unsigned long long rej = __ballot(act && !accept);
     if (j == G && rej) j = i0 + __ffsll((long long)rej) - 1;
   }
+  float oG;
+  double l2G;
+  int okG;
+  r_stat(G, oG, l2G, okG);
   if (!okG) flags |= 2;  // target row G: the bonus distribution
   if (!(us >= 0.0f && us < 1.0f)) flags |= 4;
   if (TOPK) {  // a NaN threshold marks a top-k selection that did not complete
@@ -495,15 +477,28 @@ SVD void sampling_finish(const Args &a, int b, float own_off, float own_hi, floa
                 : (flags & 2) ? SV_ROW_BAD_LOGITS
                 : (flags & 4) ? SV_ROW_BAD_UNIFORM
                 : (flags & 8) ? SV_ROW_Q_ZERO : 0;
-  for (int i = lane; i <= G; i += WAVE) {
-    if (!err && i == j) continue;  // written by the draw, with accepted_len
-    out[i] = (!err && i < j) ? ((i < WAVE) ? x0 : a.tokens[(size_t)b * G + i]) : -1;
-  }
-  if (err && lane == 0) a.accepted_len[b] = err;
-
-  // The draw's record, one tagged word per lane.  With no drafts (G = 0) the bonus is
-  // drawn right here (below) and no draw items exist.
+  // The draw's record, one tagged word per lane, goes out first; the outputs follow.
+  // With no drafts (G = 0) the bonus is drawn right here (below) and no draw items exist.
   const int kind = (err || G0) ? (int)JOB_NONE : (j < G ? (int)JOB_REJECT : (int)JOB_BONUS);
+
+  // The bonus draw's chunk, when every draft is accepted (or there are none): chunk
+  // masses of p_G, S_c * 2^(off_c - off_row) in chunk order, and the remainder in that
+  // chunk's scale.
+  int c_bonus = -1;
+  float off_bonus = 0.0f;
+  double t_bonus = 0.0;
+  if (okG && (kind == JOB_BONUS || (G0 && !err))) {
+    auto cm = [&](int cc) {
+      const double sc = p_sum(G, cc);
+      return (sc > 0.0) ? sc * (double)fast_exp2(p_off(G, cc) - oG) : 0.0;
+    };
+    double trem, total;
+    c_bonus = wave_pick_frac(C, (double)us, cm, &trem, &total);
+    if (c_bonus >= 0) {
+      off_bonus = p_off(G, c_bonus);
+      t_bonus = trem * (double)fast_exp2(oG - off_bonus);
+    }
+  }
   float mt_hi = 0.0f, mt_lo = 0.0f, md_hi = 0.0f, md_lo = 0.0f, tau_t = -INFINITY, tau_d = -INFINITY;
   float off_j = 0.0f;
   if (kind == JOB_REJECT) {
@@ -541,6 +536,11 @@ SVD void sampling_finish(const Args &a, int b, float own_off, float own_hi, floa
     default: break;
   }
   if (lane < JW_USED) tw_put(&jw[lane], tag, bits);
+  for (int i = lane; i <= G; i += WAVE) {
+    if (!err && i == j) continue;  // written by the draw, with accepted_len
+    out[i] = (!err && i < j) ? ((i < WAVE) ? x0 : a.tokens[(size_t)b * G + i]) : -1;
+  }
+  if (err && lane == 0) a.accepted_len[b] = err;
   if (lds && a.row_stats) {
     for (int jr = lane; jr < rps; jr += WAVE) {
       a.row_stats[(r0 + jr) * 2 + 0] = (float)((double)s_roff[jr] * LN2);
@@ -989,9 +989,11 @@ SVD void draw_item(const Args &a, int item) {
 
 // Sampling: the first pass (normalisers, acceptance scan) and the draws in one grid;
 // units are sequences: first-pass items (rows in order, chunks in order), then draw items.
-// G0: no drafted positions (the batched sampler): first-pass items only.
+// G0: no drafted positions (the batched sampler): first-pass items only.  Four resident
+// waves per SIMD (up to 128 registers) measure faster than five, except after the top-k
+// passes, where five do.
 template <typename T, bool ALIGNED, bool TOPK, bool G0>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(5))) void k_verify(const Args a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(TOPK ? 5 : 4))) void k_verify(const Args a) {
   int phase, item;
   if (!lane_item(a.B, a.rps * a.C, G0 ? 0 : a.C * NSUB, phase, item)) return;
   if (phase == 1) norm_item<T, ALIGNED, TOPK, G0>(a, item);
