@@ -267,7 +267,7 @@ using sv_host::next_tag;
 
 struct OvPlan {
   bool topk;
-  int esz, nvec, C, rps, digit_passes;
+  int esz, nvec, C, rps;
   long long R, U;
   size_t tw_part, tw_ov, tw_hist, row_tau, tk_state, total, zero_bytes;
 };
@@ -281,7 +281,6 @@ bool ov_plan(int32_t B, int32_t G, int32_t V, sv_dtype dt, int32_t top_k, OvPlan
   p.R = (long long)B * p.rps;
   p.U = (long long)B * G;
   p.topk = top_k > 0 && top_k < V;
-  p.digit_passes = (dt == SV_BF16) ? 2 : 4;
   const long long lu = (p.U + LANES - 1) / LANES, lr = (p.R + LANES - 1) / LANES;
   if (LANES * lu * 3LL * p.C > 0x7fffffffLL || LANES * lr * (long long)p.C > 0x7fffffffLL) return false;
   const size_t R = (size_t)p.R, C = (size_t)p.C, U = (size_t)p.U;
@@ -289,7 +288,7 @@ bool ov_plan(int32_t B, int32_t G, int32_t V, sv_dtype dt, int32_t top_k, OvPlan
   // tagged words first (the part that must be clean when a call starts)
   p.tw_part = o; o = align256(o + R * C * 3 * 8);
   p.tw_ov = o; o = align256(o + U * C * 4 * 8);
-  p.tw_hist = o; o = align256(o + (p.topk ? R * C * 128 * 8 : 0));
+  p.tw_hist = o; o = align256(o + (p.topk ? sv_host::topk_words(p.R, p.C, top_k) * 8 : 0));
   p.zero_bytes = o;
   p.row_tau = o; o = align256(o + (p.topk ? R * 4 : 0));
   p.tk_state = o; o = align256(o + (p.topk ? R * 8 : 0));
@@ -307,15 +306,7 @@ hipError_t ov_launch(const OvPlan &p, const Args &a, hipStream_t st, void *const
   sv_host::Launcher L{st, ev, nev};
   const long long lu = (p.U + LANES - 1) / LANES, lr = (p.R + LANES - 1) / LANES;
   Args aa = a;
-  if (p.topk) {
-    for (int pass = 0; pass < p.digit_passes; ++pass) {
-      int ps = pass, lp = (pass == p.digit_passes - 1) ? 1 : 0;
-      aa.tag = next_tag();
-      void *args[] = {&aa, &ps, &lp};
-      const void *fn = (pass == 0) ? (const void *)&k_topk_digit<T, AL, 16> : (const void *)&k_topk_digit<T, AL, 1>;
-      L.go(fn, (unsigned)(LANES * lr * p.C), args);
-    }
-  }
+  if (p.topk) sv_host::launch_topk<T, AL>(L, aa, (unsigned)(LANES * lr * p.C), p.C);
   aa.tag = next_tag();
   void *args[] = {&aa};
   L.go(p.topk ? (const void *)&k_overlap<T, AL, true> : (const void *)&k_overlap<T, AL, false>,
@@ -419,9 +410,11 @@ const char *sv_overlap_launch_plan(int32_t B, int32_t G, int32_t V, sv_dtype dty
   (void)B;
   (void)temperature;
   if (G == 0) return "";
-  if (top_k > 0 && top_k < V)
+  if (top_k > 0 && top_k < V) {
+    if (sv_host::topk_one_pass(top_k, sv_host::row_chunks(V, dtype == SV_BF16 ? 2 : 4))) return "k_topk_select;k_overlap";
     return dtype == SV_BF16 ? "k_topk_digit;k_topk_digit;k_overlap"
                             : "k_topk_digit;k_topk_digit;k_topk_digit;k_topk_digit;k_overlap";
+  }
   return "k_overlap";
 }
 

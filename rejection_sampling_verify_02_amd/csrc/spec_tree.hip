@@ -635,7 +635,7 @@ using sv_host::next_tag;
 
 struct TreePlan {
   bool greedy, topk;
-  int esz, nvec, C, I, rps, S, digit_passes;  // I: k_tree_resid items per node
+  int esz, nvec, C, I, rps, S;  // I: k_tree_resid items per node
   long long R;
   size_t tw_part, tw_z, tw_seg, tw_hist, row_off, row_lt, row_arg, row_ok, zc, job, job_c,
       row_tau, tk_state, total, zero_bytes;
@@ -653,7 +653,6 @@ bool tree_plan(int32_t B, int32_t N, int32_t V, int32_t S, sv_dtype dt, float T,
   p.R = (long long)B * p.rps;
   p.S = S < 1 ? 1 : S;
   p.topk = !p.greedy && top_k > 0 && top_k < V;
-  p.digit_passes = (dt == SV_BF16) ? 2 : 4;
   const long long lr = (p.R + LANES - 1) / LANES, ln = ((long long)B * N + LANES - 1) / LANES,
                   lb = (B + LANES - 1) / LANES;
   // the items of a node in k_tree_resid wait for one another: at most TREE_MAX_ITEMS of them
@@ -667,7 +666,7 @@ bool tree_plan(int32_t B, int32_t N, int32_t V, int32_t S, sv_dtype dt, float T,
   p.tw_part = o; o = align256(o + R * C * 3 * 8);
   p.tw_z = o; o = align256(o + (smp ? Bz * Nz * (Sz - 1) * (size_t)p.I * 2 * 8 : 0));
   p.tw_seg = o; o = align256(o + (smp ? Bz * C * SEGS * 2 * 8 : 0));
-  p.tw_hist = o; o = align256(o + (p.topk ? R * C * 128 * 8 : 0));
+  p.tw_hist = o; o = align256(o + (p.topk ? sv_host::topk_words(p.R, p.C, top_k) * 8 : 0));
   p.zero_bytes = o;
   p.row_off = o; o = align256(o + R * 4);
   p.row_lt = o; o = align256(o + R * 8);
@@ -694,15 +693,7 @@ hipError_t tree_launch(const TreePlan &p, const TreeArgs &t0, hipStream_t st, vo
   const long long B = t0.a.B, N = t0.a.G;
   const long long lr = (p.R + LANES - 1) / LANES, ln = (B * N + LANES - 1) / LANES, lb = (B + LANES - 1) / LANES;
   TreeArgs t = t0;
-  if (p.topk) {
-    for (int pass = 0; pass < p.digit_passes; ++pass) {
-      int ps = pass, lp = (pass == p.digit_passes - 1) ? 1 : 0;
-      t.a.tag = next_tag();
-      void *args[] = {&t.a, &ps, &lp};
-      const void *fn = (pass == 0) ? (const void *)&k_topk_digit<T, AL, 16> : (const void *)&k_topk_digit<T, AL, 1>;
-      L.go(fn, (unsigned)(LANES * lr * p.C), args);
-    }
-  }
+  if (p.topk) sv_host::launch_topk<T, AL>(L, t.a, (unsigned)(LANES * lr * p.C), p.C);
   {
     t.a.tag = next_tag();
     void *args[] = {&t};
@@ -858,14 +849,18 @@ const char *sv_tree_launch_plan(int32_t B, int32_t N, int32_t V, int32_t max_chi
   if (temperature == 0.0f) return "k_tree_rows;k_tree_walk";
   const bool topk = top_k > 0 && top_k < V;
   const bool resid = max_children > 1;
-  static const char *names[2][2][2] = {
-      {{"k_tree_rows;k_tree_walk;k_tree_draw", "k_tree_rows;k_tree_resid;k_tree_walk;k_tree_draw"},
-       {"k_topk_digit;k_topk_digit;k_tree_rows;k_tree_walk;k_tree_draw",
-        "k_topk_digit;k_topk_digit;k_tree_rows;k_tree_resid;k_tree_walk;k_tree_draw"}},
-      {{"k_tree_rows;k_tree_walk;k_tree_draw", "k_tree_rows;k_tree_resid;k_tree_walk;k_tree_draw"},
-       {"k_topk_digit;k_topk_digit;k_topk_digit;k_topk_digit;k_tree_rows;k_tree_walk;k_tree_draw",
-        "k_topk_digit;k_topk_digit;k_topk_digit;k_topk_digit;k_tree_rows;k_tree_resid;k_tree_walk;k_tree_draw"}}};
-  return names[dtype == SV_F32 ? 1 : 0][topk ? 1 : 0][resid ? 1 : 0];
+  // [threshold: none, one select pass, 2 digit passes (bf16), 4 digit passes (f32)][resid]
+  static const char *names[4][2] = {
+      {"k_tree_rows;k_tree_walk;k_tree_draw", "k_tree_rows;k_tree_resid;k_tree_walk;k_tree_draw"},
+      {"k_topk_select;k_tree_rows;k_tree_walk;k_tree_draw",
+       "k_topk_select;k_tree_rows;k_tree_resid;k_tree_walk;k_tree_draw"},
+      {"k_topk_digit;k_topk_digit;k_tree_rows;k_tree_walk;k_tree_draw",
+       "k_topk_digit;k_topk_digit;k_tree_rows;k_tree_resid;k_tree_walk;k_tree_draw"},
+      {"k_topk_digit;k_topk_digit;k_topk_digit;k_topk_digit;k_tree_rows;k_tree_walk;k_tree_draw",
+       "k_topk_digit;k_topk_digit;k_topk_digit;k_topk_digit;k_tree_rows;k_tree_resid;k_tree_walk;k_tree_draw"}};
+  const int esz = dtype == SV_BF16 ? 2 : 4;
+  const int th = !topk ? 0 : sv_host::topk_one_pass(top_k, sv_host::row_chunks(V, esz)) ? 1 : (esz == 2 ? 2 : 3);
+  return names[th][resid ? 1 : 0];
 }
 
 }  // extern "C"

@@ -292,7 +292,7 @@ using sv_host::next_tag;
 
 struct TypPlan {
   bool topk;
-  int esz, nvec, C, rps, digit_passes;
+  int esz, nvec, C, rps;
   long long R;
   size_t tw_part, tw_hist, row_tau, tk_state, total, zero_bytes;
 };
@@ -305,13 +305,12 @@ bool typ_plan(int32_t B, int32_t G, int32_t V, sv_dtype dt, int32_t top_k, TypPl
   p.rps = G + 1;
   p.R = (long long)B * p.rps;
   p.topk = top_k > 0 && top_k < V;
-  p.digit_passes = (dt == SV_BF16) ? 2 : 4;
   const long long lb = (B + LANES - 1) / LANES, lr = (p.R + LANES - 1) / LANES;
   if (LANES * lb * (long long)p.rps * p.C > 0x7fffffffLL || LANES * lr * (long long)p.C > 0x7fffffffLL) return false;
   const size_t R = (size_t)p.R, C = (size_t)p.C;
   size_t o = 0;
   p.tw_part = o; o = align256(o + R * C * TYP_WORDS * 8);
-  p.tw_hist = o; o = align256(o + (p.topk ? R * C * 128 * 8 : 0));
+  p.tw_hist = o; o = align256(o + (p.topk ? sv_host::topk_words(p.R, p.C, top_k) * 8 : 0));
   p.zero_bytes = o;
   p.row_tau = o; o = align256(o + (p.topk ? R * 4 : 0));
   p.tk_state = o; o = align256(o + (p.topk ? R * 8 : 0));
@@ -329,15 +328,7 @@ hipError_t typ_launch(const TypPlan &p, const TypArgs &t0, hipStream_t st, void 
   sv_host::Launcher L{st, ev, nev};
   const long long lb = (t0.a.B + LANES - 1) / LANES, lr = (p.R + LANES - 1) / LANES;
   TypArgs t = t0;
-  if (p.topk) {
-    for (int pass = 0; pass < p.digit_passes; ++pass) {
-      int ps = pass, lp = (pass == p.digit_passes - 1) ? 1 : 0;
-      t.a.tag = next_tag();
-      void *args[] = {&t.a, &ps, &lp};
-      const void *fn = (pass == 0) ? (const void *)&k_topk_digit<T, AL, 16> : (const void *)&k_topk_digit<T, AL, 1>;
-      L.go(fn, (unsigned)(LANES * lr * p.C), args);
-    }
-  }
+  if (p.topk) sv_host::launch_topk<T, AL>(L, t.a, (unsigned)(LANES * lr * p.C), p.C);
   t.a.tag = next_tag();
   void *args[] = {&t};
   L.go(p.topk ? (const void *)&k_typical<T, AL, true> : (const void *)&k_typical<T, AL, false>,
@@ -438,9 +429,11 @@ const char *sv_typical_launch_plan(int32_t B, int32_t G, int32_t V, sv_dtype dty
   (void)B;
   (void)G;
   (void)temperature;
-  if (top_k > 0 && top_k < V)
+  if (top_k > 0 && top_k < V) {
+    if (sv_host::topk_one_pass(top_k, sv_host::row_chunks(V, dtype == SV_BF16 ? 2 : 4))) return "k_topk_select;k_typical";
     return dtype == SV_BF16 ? "k_topk_digit;k_topk_digit;k_typical"
                             : "k_topk_digit;k_topk_digit;k_topk_digit;k_topk_digit;k_typical";
+  }
   return "k_typical";
 }
 

@@ -1025,7 +1025,6 @@ struct Plan {
   bool greedy, topk, aligned;
   int esz, vec, nvec, C, rps;
   long long R;
-  int digit_passes;
   // workspace offsets
   size_t tw_part, tw_job, tw_seg, tw_gseg, tw_hist, row_tau, tk_state, total;
   size_t zero_bytes;  // leading bytes (tagged words) that must be clean when a call starts
@@ -1040,7 +1039,6 @@ bool make_plan(int32_t B, int32_t G, int32_t V, sv_dtype dt, float T, int32_t to
   p.rps = p.greedy ? (G + 1) : (2 * G + 1);
   p.R = (long long)B * p.rps;
   p.topk = !p.greedy && top_k > 0 && top_k < V;
-  p.digit_passes = (dt == SV_BF16) ? 2 : 4;
   // grids padded to whole lanes (see lane_item)
   const long long lanes_b = (B + LANES - 1) / LANES * LANES, lanes_r = (p.R + LANES - 1) / LANES * LANES;
   if (lanes_b * ((long long)p.rps * p.C + (long long)p.C * NSUB) > 0x7fffffffLL || lanes_r * p.C > 0x7fffffffLL)
@@ -1056,7 +1054,7 @@ bool make_plan(int32_t B, int32_t G, int32_t V, sv_dtype dt, float T, int32_t to
   p.tw_job = o; o = align256(o + (smp ? Bz * JW * 8 : 0));
   p.tw_seg = o; o = align256(o + (smp ? Bz * C * SEGS * 2 * 8 : 0));
   p.tw_gseg = o; o = align256(o + (smp ? Bz * C * SEGS * 2 * 8 : 0));
-  p.tw_hist = o; o = align256(o + (p.topk ? R * C * 128 * 8 : 0));
+  p.tw_hist = o; o = align256(o + (p.topk ? sv_host::topk_words(p.R, p.C, top_k) * 8 : 0));
   p.zero_bytes = o;
   p.row_tau = o; o = align256(o + (p.topk ? R * 4 : 0));
   p.tk_state = o; o = align256(o + (p.topk ? R * 8 : 0));
@@ -1069,6 +1067,7 @@ const char *kPlanNames[] = {
     "k_topk_digit;k_topk_digit;k_topk_digit;k_topk_digit;k_verify",
     "k_verify",
     "k_argmax",
+    "k_topk_select;k_verify",
 };
 
 template <typename T, bool AL>
@@ -1089,13 +1088,7 @@ hipError_t launch_all(const Plan &p, const Args &a, hipStream_t st, void *const 
     go((const void *)&k_argmax<T, AL>, argmax_grid, args);
   } else {
     if (p.topk) {
-      for (int pass = 0; pass < p.digit_passes; ++pass) {
-        int ps = pass, lp = (pass == p.digit_passes - 1) ? 1 : 0;
-        aa.tag = next_tag();
-        void *args[] = {&aa, &ps, &lp};
-        const void *fn = (pass == 0) ? (const void *)&k_topk_digit<T, AL, 16> : (const void *)&k_topk_digit<T, AL, 1>;
-        go(fn, topk_grid, args);
-      }
+      sv_host::launch_topk<T, AL>(L, aa, topk_grid, p.C);
       aa.tag = next_tag();
       void *args[] = {&aa};
       go(a.G == 0 ? (const void *)&k_verify<T, AL, true, true> : (const void *)&k_verify<T, AL, true, false>,
@@ -1228,7 +1221,10 @@ const char *sv_launch_plan(int32_t B, int32_t G, int32_t V, sv_dtype dtype, floa
   (void)B;
   (void)G;
   if (temperature == 0.0f) return kPlanNames[3];
-  if (top_k > 0 && top_k < V) return dtype == SV_BF16 ? kPlanNames[0] : kPlanNames[1];
+  if (top_k > 0 && top_k < V) {
+    if (sv_host::topk_one_pass(top_k, sv_host::row_chunks(V, dtype == SV_BF16 ? 2 : 4))) return kPlanNames[4];
+    return dtype == SV_BF16 ? kPlanNames[0] : kPlanNames[1];
+  }
   return kPlanNames[2];
 }
 

@@ -58,6 +58,15 @@ SVD const T *seq_row(const Args &a, int b, int j) {
 
 // ---------------------------------------------------------------- top-k threshold
 
+// The threshold of a selected key: the smallest value whose key carries it.  With a
+// 16-bit (bf16) key that value can be a NaN (the bucket of -inf, whose low half is set):
+// then every value of the row passes, which is what -inf says.  A NaN threshold is kept
+// for a selection that did not complete.
+SVD float tau_of_key(uint32_t key) {
+  const float t = key2f(key);
+  return (t == t) ? t : -INFINITY;
+}
+
 // One radix-select digit (bits [shift, shift+8) of the key) for every row.  The prefix
 // of higher digits and the remaining rank come from the previous pass.  The threshold
 // kept in row_tau is the smallest value whose key has the final prefix, so the kept set
@@ -155,9 +164,331 @@ __global__ __launch_bounds__(NT) void k_topk_digit(const Args a, int pass, int l
   if (reach && !next_reach) {
     const unsigned above = (tid < 255) ? s_ge[tid + 1] : 0u;
     const uint32_t prefix = (st.x & hi_mask) | ((uint32_t)tid << shift);
-    if (last_pass) a.w.row_tau[r] = key2f(prefix);
+    if (last_pass) a.w.row_tau[r] = tau_of_key(prefix);
     else a.w.tk_state[r] = make_uint2(prefix, krem - above);
   }
+}
+
+// One-pass top-k threshold, for 0 < k <= TOPK_SELECT_MAX.  Every chunk publishes a
+// multiset of its values that holds its k largest (count word, then the keys), and the
+// row's last chunk in grid order takes the k-th largest key of their union, which is the
+// row's k-th largest: each chunk contributes at most k values to the row's top k, and
+// those are among its own k largest.  A chunk finds a lower bound on its k-th largest
+// from its threads' maxima (wave w's ceil(k/4)-th largest maximum, the smallest over the
+// four waves: at least 4*ceil(k/4) >= k values lie at or above it) and publishes every
+// value at or above that bound.  Should that be more than `cap` values (heavy ties), it
+// takes its exact k-th largest tau_c by radix select over its registers and publishes the
+// values above tau_c and enough copies of tau_c to make k.  Keys are f2key of the value;
+// elements past the row's end are not part of it.  A row whose collector gave up gets a
+// NaN threshold, which the kernels that read it report as an error.
+constexpr int TOPK_SELECT_MAX = 256;    // largest k of the one-pass select
+constexpr int TOPK_SELECT_MAX_C = 1024;  // most chunks per row of the one-pass select
+constexpr int TOPK_LDS_KEYS = 4096;      // the collector keeps up to this many keys in LDS
+
+// Inclusive scan of unsigned values over the wave (DPP).
+SVD unsigned scan_add_u(unsigned x) {
+#define STEP(C, R) x += dpp_u<C, R>(x, 0u);
+  SV_SCAN_STEPS(STEP)
+#undef STEP
+  return x;
+}
+
+// Exclusive prefix of v over the workgroup (thread order), and the total.
+SVD unsigned block_excl_scan(unsigned v, unsigned *s_w, unsigned &total) {
+  const int lane = lane_id(), wid = (int)threadIdx.x / WAVE;
+  const unsigned inc = scan_add_u(v);
+  if (lane == WAVE - 1) s_w[wid] = inc;
+  __syncthreads();
+  unsigned before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    before += (w < wid) ? s_w[w] : 0u;
+    tot += s_w[w];
+  }
+  __syncthreads();
+  total = tot;
+  return before + inc - v;
+}
+
+// The k-th largest (1-based) of a multiset of keys spread over the workgroup's threads,
+// by radix select, 8 bits a pass from the top (npass = 2 for bf16 values, whose keys have
+// zero low halves; 4 otherwise).  each(f) calls f(key) for every key this thread holds.
+// The multiset must hold at least k keys.  Thread d owns histogram bin d.
+template <typename Each>
+SVD uint32_t block_kth_largest(int k, int npass, const Each &each, unsigned *hist, unsigned *sge,
+                               unsigned *s_pick) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0;
+  unsigned krem = (unsigned)k;
+  for (int pass = 0; pass < npass; ++pass) {
+    const int shift = 24 - 8 * pass;
+    const uint32_t hm = pass ? (0xffffffffu << (shift + 8)) : 0u;
+    hist[tid] = 0u;
+    if (tid == 0) {
+      s_pick[0] = 0u;
+      s_pick[1] = 0u;
+    }
+    __syncthreads();
+    each([&](uint32_t key) {
+      if ((key & hm) == (prefix & hm)) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    });
+    __syncthreads();
+    sge[tid] = hist[tid];
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {  // suffix sums (Hillis-Steele)
+      const unsigned add = (tid + o < 256) ? sge[tid + o] : 0u;
+      __syncthreads();
+      sge[tid] += add;
+      __syncthreads();
+    }
+    // the largest digit whose suffix count reaches the remaining rank
+    const unsigned above = (tid < 255) ? sge[tid + 1] : 0u;
+    if (sge[tid] >= krem && above < krem) {
+      s_pick[0] = (unsigned)tid;
+      s_pick[1] = above;
+    }
+    __syncthreads();
+    prefix |= s_pick[0] << shift;
+    krem -= s_pick[1];
+    __syncthreads();
+  }
+  return prefix;
+}
+
+template <typename T, bool ALIGNED>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_topk_select(const Args a, int cap) {
+  constexpr int VEC = Fmt<T>::VEC;
+  constexpr int NPASS = (sizeof(T) == 2) ? 2 : 4;
+  __shared__ unsigned s_hist[256], s_ge[256], s_w[NW], s_wv[NW], s_pick[2];
+  __shared__ unsigned s_keys[TOPK_LDS_KEYS];
+  __shared__ unsigned s_coff[TOPK_SELECT_MAX_C + 1];
+  __shared__ int s_alive;
+  const int tid = threadIdx.x, lane = lane_id(), wid = tid / WAVE;
+  int phase, xi;
+  if (!lane_item((int)(a.B * a.rps), a.C, 0, phase, xi)) return;  // units: rows
+  const int r = xi / a.C, c = xi - r * a.C;
+  const int b = r / a.rps, jr = r - b * a.rps;
+  const int k = a.top_k;
+  const unsigned tag = a.tag;
+  const size_t W = (size_t)cap + 1;  // words per chunk: the count, then up to cap keys
+  u64 *rw = a.w.tw_hist + (size_t)r * a.C * W;
+  u64 *cw = rw + (size_t)c * W;
+
+  // The chunk stays in registers as raw 16-byte vectors (8 bf16 or 4 f32 values each);
+  // key(kk, e) unpacks one value.  Elements past the row's end are absent.
+  u32x4 w[VPT];
+  {
+    const T *row = seq_row<T>(a, b, jr);
+    if (ALIGNED) {
+      const u32x4 *rv = reinterpret_cast<const u32x4 *>(row);
+#pragma unroll
+      for (int kk = 0; kk < VPT; ++kk) {
+        const int vi = c * CHUNK_VECS + kk * NT + tid;
+        w[kk] = __builtin_nontemporal_load(rv + (vi < a.nvec ? vi : a.nvec - 1));
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < VPT; ++kk) {
+        uint32_t h[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const long idx = elem_index<T>(c, kk, tid, e);
+          h[e] = __float_as_uint(Fmt<T>::at(row, (size_t)(idx < a.V ? idx : (long)a.V - 1)));
+        }
+        if (VEC == 8) {
+          w[kk].x = (h[0] >> 16) | (h[1 % VEC] & 0xffff0000u);
+          w[kk].y = (h[2 % VEC] >> 16) | (h[3 % VEC] & 0xffff0000u);
+          w[kk].z = (h[4 % VEC] >> 16) | (h[5 % VEC] & 0xffff0000u);
+          w[kk].w = (h[6 % VEC] >> 16) | (h[7 % VEC] & 0xffff0000u);
+        } else {
+          w[kk].x = h[0];
+          w[kk].y = h[1 % VEC];
+          w[kk].z = h[2 % VEC];
+          w[kk].w = h[3 % VEC];
+        }
+      }
+    }
+  }
+  // bf16 keys keep only their upper half: a negative value's key has its low half set,
+  // and the radix select resolves 16 bits, so every comparison happens at that width.
+  constexpr uint32_t KMASK = (sizeof(T) == 2) ? 0xffff0000u : 0xffffffffu;
+  auto key = [&](int kk, int e) -> uint32_t {
+    float f[VEC];
+    Fmt<T>::unpack(w[kk], f);
+    return f2key(f[e]) & KMASK;
+  };
+  // Between passes over the chunk the raw vectors are marked as changed, so each pass
+  // unpacks its values again instead of keeping all of them live in registers.
+  auto fresh = [&]() {
+#pragma unroll
+    for (int kk = 0; kk < VPT; ++kk) asm volatile("" : "+v"(w[kk]));
+  };
+  const bool full = (long)(c + 1) * CHUNK_VECS * VEC <= (long)a.V;
+  const unsigned vlim = (unsigned)a.V;
+  auto present = [&](int kk, int e) {
+    return full || ((unsigned)(c * CHUNK_VECS + kk * NT + tid) * (unsigned)VEC + (unsigned)e) < vlim;
+  };
+
+  // lower bound: per wave the ceil(k/4)-th largest thread maximum (bitonic sort of the
+  // wave's 64 maxima, descending), the smallest over the waves.  Comparisons against it
+  // are made on values: x >= key2f(lb) exactly when key(x) >= lb, for every value that is
+  // not a NaN (a row with a NaN is reported as an error whatever its threshold).
+  float tm = -INFINITY;
+#pragma unroll
+  for (int kk = 0; kk < VPT; ++kk) {
+    float f[VEC];
+    Fmt<T>::unpack(w[kk], f);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e)
+      if (present(kk, e)) tm = fmaxf(tm, f[e]);
+  }
+  uint32_t v = f2key(tm) & KMASK;
+  for (int size = 2; size <= WAVE; size <<= 1)
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const uint32_t o = (uint32_t)__shfl_xor((int)v, stride);
+      const bool desc = (lane & size) == 0 || size == WAVE;
+      const bool lower = (lane & stride) == 0;
+      v = (desc == lower) ? ((o > v) ? o : v) : ((o < v) ? o : v);
+    }
+  const int q = (k + NW - 1) / NW - 1;
+  const uint32_t wv = (uint32_t)__builtin_amdgcn_readlane((int)v, q);
+  if (lane == 0) s_wv[wid] = wv;
+  if (tid == 0) s_pick[0] = 0u;  // the candidate count
+  __syncthreads();
+  uint32_t lb = s_wv[0];
+#pragma unroll
+  for (int w2 = 1; w2 < NW; ++w2) lb = (s_wv[w2] < lb) ? s_wv[w2] : lb;
+  float lbf = key2f(lb);
+  lbf = (lbf == lbf) ? lbf : -INFINITY;  // the -inf bucket of a bf16 key: every value
+
+  // candidates: every value >= lbf, appended to LDS in any order (a multiset)
+  fresh();
+#pragma unroll
+  for (int kk = 0; kk < VPT; ++kk) {
+    float f[VEC];
+    Fmt<T>::unpack(w[kk], f);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e)
+      if (present(kk, e) && f[e] >= lbf) {
+        const unsigned i = atomicAdd(&s_pick[0], 1u);
+        if (i < (unsigned)cap) s_keys[i] = f2key(f[e]) & KMASK;
+      }
+  }
+  __syncthreads();
+  const unsigned n = s_pick[0];
+  __syncthreads();  // every thread holds n before s_pick is reused
+  // This chunk's list ends in s_keys[0, own_n); chunks other than the row's last publish
+  // it, the last keeps it in LDS for the collection.
+  const bool last = (c == a.C - 1);
+  unsigned own_n;
+  if (n <= (unsigned)cap) {
+    own_n = n;
+    if (!last) {
+      for (unsigned i = tid; i < n; i += NT) tw_put(&cw[1 + i], tag, s_keys[i]);
+      if (tid == 0) tw_put(&cw[0], tag, n);
+    }
+  } else {  // heavy ties: the exact k-th largest of the chunk, then keys above it
+    auto each = [&](auto fn) {
+#pragma unroll
+      for (int kk = 0; kk < VPT; ++kk)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+          if (present(kk, e)) fn(key(kk, e));
+    };
+    fresh();
+    const uint32_t tc = block_kth_largest(k, NPASS, each, s_hist, s_ge, s_pick);
+    fresh();
+    if (tid == 0) s_pick[0] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < VPT; ++kk)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const uint32_t kv = key(kk, e);
+        if (present(kk, e) && kv > tc) {
+          const unsigned i = atomicAdd(&s_pick[0], 1u);
+          if (i < (unsigned)k) s_keys[i] = kv;  // fewer than k lie above the k-th largest
+        }
+      }
+    __syncthreads();
+    const unsigned na = s_pick[0] < (unsigned)k ? s_pick[0] : (unsigned)k;
+    for (unsigned i = na + tid; i < (unsigned)k; i += NT) s_keys[i] = tc;
+    __syncthreads();
+    own_n = (unsigned)k;
+    if (!last) {
+      for (unsigned i = tid; i < (unsigned)k; i += NT) tw_put(&cw[1 + i], tag, s_keys[i]);
+      if (tid == 0) tw_put(&cw[0], tag, (unsigned)k);
+    }
+  }
+  if (!last) return;
+  __syncthreads();  // s_pick is the collector's next
+
+  // The row's collector: its own list is s_keys[0, own_n); every other chunk's count
+  // (chunks in blocks of NT, one a thread) and first key index, then their keys, each
+  // polled until it carries this call's tag, staged after the own ones while they fit.
+  const int CO = a.C - 1;  // the other chunks
+  unsigned polls = 0;
+  bool ok = true;
+  unsigned others = 0;
+  for (int c0 = 0; c0 < CO; c0 += NT) {
+    const int cc = c0 + tid;
+    unsigned nc = 0;
+    if (cc < CO) {
+      u64 w;
+      for (;;) {
+        w = ld_dev(&rw[(size_t)cc * W]);
+        if (tw_ok(w, tag) || ++polls >= a.spin_limit) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+      ok = ok && tw_ok(w, tag);
+      nc = (unsigned)w;
+      nc = (nc <= (unsigned)cap) ? nc : 0u;  // never trust a count beyond the chunk's words
+    }
+    unsigned tot;
+    const unsigned before = block_excl_scan(nc, s_w, tot);
+    if (cc < CO) s_coff[cc] = others + before;
+    others += tot;
+  }
+  if (tid == 0) s_alive = 1;
+  __syncthreads();
+  if (!ok) s_alive = 0;
+  const unsigned total = own_n + others;
+  const bool in_lds = total <= (unsigned)TOPK_LDS_KEYS;
+  // the word of another chunk's key h: its chunk is the last one whose first index is <= h
+  auto key_word = [&](unsigned h) -> const u64 * {
+    int lo = 0, hi = CO - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_coff[mid] <= h) lo = mid;
+      else hi = mid - 1;
+    }
+    return &rw[(size_t)lo * W + 1 + (h - s_coff[lo])];
+  };
+  __syncthreads();
+  if (s_alive) {
+    for (unsigned h = tid; h < others; h += NT) {
+      const u64 *pw = key_word(h);
+      u64 w;
+      for (;;) {
+        w = ld_dev(pw);
+        if (tw_ok(w, tag) || ++polls >= a.spin_limit) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+      if (!tw_ok(w, tag)) s_alive = 0;
+      if (in_lds) s_keys[own_n + h] = (unsigned)w;
+    }
+  }
+  __syncthreads();
+  if (!s_alive || total < (unsigned)k) {
+    if (tid == 0) a.w.row_tau[r] = NAN;
+    return;
+  }
+  auto each = [&](auto f) {
+    for (unsigned g = tid; g < total; g += NT)
+      f((in_lds || g < own_n) ? s_keys[g] : (uint32_t)ld_dev(key_word(g - own_n)));
+  };
+  const uint32_t tk = block_kth_largest(k, NPASS, each, s_hist, s_ge, s_pick);
+  if (tid == 0) a.w.row_tau[r] = tau_of_key(tk);
 }
 
 // ---------------------------------------------------------------- per-chunk normaliser
@@ -258,5 +589,45 @@ struct Launcher {
     if (e == hipSuccess) ++n;
   }
 };
+
+// The top-k threshold: one k_topk_select pass when k and the row's chunk count allow it,
+// else the radix digit passes (2 for bf16, 4 for f32).  tw_hist holds topk_words(...)
+// tagged words in either case.
+inline bool topk_one_pass(int top_k, int C) { return top_k <= sv::TOPK_SELECT_MAX && C <= sv::TOPK_SELECT_MAX_C; }
+inline int topk_cap(int top_k) {
+  const int c = 4 * top_k;
+  return c < 128 ? 128 : (c > 1024 ? 1024 : c);
+}
+inline size_t topk_words(long long R, int C, int top_k) {
+  return (size_t)R * (size_t)C * (topk_one_pass(top_k, C) ? (size_t)topk_cap(top_k) + 1 : (size_t)128);
+}
+// Chunks per row (as the kernels cut rows) for a row of V values of esz bytes.
+inline int row_chunks(int V, int esz) {
+  const long long nvec = ((long long)V * esz + 15) / 16;
+  return (int)((nvec + sv::CHUNK_VECS - 1) / sv::CHUNK_VECS);
+}
+// The plan names of the threshold launches, ';'-terminated.
+inline const char *topk_plan(int top_k, int C, bool bf16) {
+  if (topk_one_pass(top_k, C)) return "k_topk_select;";
+  return bf16 ? "k_topk_digit;k_topk_digit;" : "k_topk_digit;k_topk_digit;k_topk_digit;k_topk_digit;";
+}
+template <typename T, bool AL>
+void launch_topk(Launcher &L, sv::Args aa, unsigned grid, int C) {
+  if (topk_one_pass(aa.top_k, C)) {
+    aa.tag = next_tag();
+    int cap = topk_cap(aa.top_k);
+    void *args[] = {&aa, &cap};
+    L.go((const void *)&sv::k_topk_select<T, AL>, grid, args);
+    return;
+  }
+  const int passes = (sizeof(T) == 2) ? 2 : 4;
+  for (int pass = 0; pass < passes; ++pass) {
+    int ps = pass, lp = (pass == passes - 1) ? 1 : 0;
+    aa.tag = next_tag();
+    void *args[] = {&aa, &ps, &lp};
+    const void *fn = (pass == 0) ? (const void *)&sv::k_topk_digit<T, AL, 16> : (const void *)&sv::k_topk_digit<T, AL, 1>;
+    L.go(fn, grid, args);
+  }
+}
 
 }  // namespace sv_host

@@ -70,6 +70,9 @@ SHAPES = [
     (8, 3, 20001, "bf16", 0.8, 50),
     (8, 3, 9003, "f32", 0.8, 7),
     (8, 3, 9000, "f32", 1.2, 4095),
+    (8, 3, 20000, "bf16", 0.8, 256),   # the largest k of the one-pass threshold
+    (8, 3, 9003, "f32", 0.8, 257),     # the smallest k of the radix digit passes
+    (4, 2, 300000, "f32", 0.9, 100),   # 37 chunks per row
 ]
 
 
@@ -95,6 +98,49 @@ def test_topk_with_ties(dev, dtype):
     for k in (1, 3, 40, 700):
         res, _, _ = parity.run_both(raw, 0.9, k, dev)
         check(res, f"ties {dtype} k={k}")
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 40000), ("f32", 30001)])
+@pytest.mark.parametrize("k", [50, 256])
+def test_topk_plateau(dev, dtype, V, k):
+    """A plateau of 1000 equal values at the top of a row, spread over its chunks (with ten
+    larger values in half the rows): more values tie at the k-th largest than a chunk
+    lists, so the chunk takes its exact k-th largest; every plateau value is kept."""
+    B, G = 6, 3
+    raw = wl.make_random(B, G, V, dtype, seed=V + k)
+    rng = np.random.default_rng(V + k)
+    for arr, rows in ((raw.target, G + 1), (raw.draft, G)):
+        flat = arr.reshape(-1, V)
+        for r in range(flat.shape[0]):
+            vals = np.full(1000, 12.0, np.float32)
+            idx = rng.choice(V, 1000 + 10, replace=False)
+            if r % 2 == 0:
+                vals = np.concatenate([vals, 12.5 + np.arange(10, dtype=np.float32) / 4])
+            else:
+                idx = idx[:1000]
+            flat[r, idx] = wl.bf16_bits(vals) if dtype == "bf16" else vals
+    res, gpu, _ = parity.run_both(raw, 1.0, k, dev)
+    check(res, f"plateau {dtype} V={V} k={k}")
+
+
+@pytest.mark.parametrize("dtype,V,k", [("bf16", 64, 10), ("bf16", 20000, 50), ("f32", 9003, 7)])
+def test_topk_kth_largest_is_minus_inf(dev, dtype, V, k):
+    """Rows with fewer finite logits than k: the k-th largest is -inf, so every logit is
+    kept (the -inf ones with probability 0), as with no top-k at all."""
+    B, G = 6, 3
+    raw = wl.make_random(B, G, V, dtype, seed=V + 17 * k)
+    rng = np.random.default_rng(V)
+    ninf = wl.bf16_bits(np.array([-np.inf], np.float32))[0] if dtype == "bf16" else np.float32(-np.inf)
+    for arr in (raw.target, raw.draft):
+        flat = arr.reshape(-1, V)
+        for r in range(flat.shape[0]):
+            keep = rng.choice(V, k // 2 + 1, replace=False)
+            mask = np.ones(V, bool)
+            mask[keep] = False
+            flat[r, mask] = ninf
+    res, gpu, _ = parity.run_both(raw, 0.9, k, dev)
+    check(res, f"k-th largest -inf {dtype} V={V} k={k}")
+    assert np.all(gpu[0] >= 0)
 
 
 @pytest.mark.parametrize("dtype,V", [("bf16", 20001), ("bf16", 152064), ("f32", 9000)])
