@@ -255,6 +255,145 @@ SVD uint32_t block_kth_largest(int k, int npass, const Each &each, unsigned *his
   return prefix;
 }
 
+// The q-th largest (1-based, q <= 64) of the wave's 64 keys, bit by bit from the top:
+// at each bit, if at least the remaining rank of the lanes still in the running have it
+// set, the answer has it set and the others drop out; otherwise they stay and the rank
+// shrinks by their count.  Bits below `low` are taken as zero (bf16 keys).
+SVD uint32_t wave_kth_largest(uint32_t v, int q, int low) {
+  uint32_t ans = 0;
+  unsigned rank = (unsigned)q;
+  bool in = true;
+  for (int bit = 31; bit >= low; --bit) {
+    const bool one = (v >> bit) & 1u;
+    const unsigned c = (unsigned)__popcll(__ballot(in && one));
+    if (c >= rank) {
+      ans |= 1u << bit;
+      in = in && one;
+    } else {
+      rank -= c;
+      in = in && !one;
+    }
+  }
+  return ans;
+}
+
+// One chunk's list for k_topk_select (whole workgroup), from its raw vectors w: the
+// values at or above the lower bound, or, with heavy ties, the exact top k.  Leaves the
+// keys in s_keys[0, n) and returns n.  Elements past the row's end hold the bits of a
+// negative NaN: key 0, below every other key, ignored by fmaxf and never >= a bound, so
+// they can neither enter a list nor move a chunk's k-th largest (a chunk that reaches the
+// exact select holds more than cap >= k real values).
+template <typename T>
+SVD unsigned topk_chunk_list(u32x4 (&w)[VPT], int k, int cap, unsigned *s_keys,
+                             unsigned *s_hist, unsigned *s_ge, unsigned *s_wv, unsigned *s_pick) {
+  constexpr int VEC = Fmt<T>::VEC;
+  constexpr int NPASS = (sizeof(T) == 2) ? 2 : 4;
+  const int tid = threadIdx.x, lane = lane_id(), wid = tid / WAVE;
+  // bf16 keys keep only their upper half: a negative value's key has its low half set,
+  // and the radix select resolves 16 bits, so every comparison happens at that width.
+  constexpr uint32_t KMASK = (sizeof(T) == 2) ? 0xffff0000u : 0xffffffffu;
+  auto key = [&](int kk, int e) -> uint32_t {
+    float f[VEC];
+    Fmt<T>::unpack(w[kk], f);
+    return f2key(f[e]) & KMASK;
+  };
+  // Between passes over the chunk the raw vectors are marked as changed, so each pass
+  // unpacks its values again instead of keeping all of them live in registers.
+  auto fresh = [&]() {
+#pragma unroll
+    for (int kk = 0; kk < VPT; ++kk) asm volatile("" : "+v"(w[kk]));
+  };
+  // lower bound: per wave the ceil(k/4)-th largest thread maximum, the smallest over the
+  // waves.  Comparisons against it
+  // are made on values: x >= key2f(lb) exactly when key(x) >= lb, for every value that is
+  // not a NaN (a row with a NaN is reported as an error whatever its threshold).
+  float tm = -INFINITY;
+#pragma unroll
+  for (int kk = 0; kk < VPT; ++kk) {
+    float f[VEC];
+    Fmt<T>::unpack(w[kk], f);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e)
+      tm = fmaxf(tm, f[e]);
+  }
+  const uint32_t v = f2key(tm) & KMASK;
+  const uint32_t wv = wave_kth_largest(v, (k + NW - 1) / NW, sizeof(T) == 2 ? 16 : 0);
+  if (lane == 0) s_wv[wid] = wv;
+  if (tid == 0) s_pick[0] = 0u;  // the candidate count
+  __syncthreads();
+  uint32_t lb = s_wv[0];
+#pragma unroll
+  for (int w2 = 1; w2 < NW; ++w2) lb = (s_wv[w2] < lb) ? s_wv[w2] : lb;
+  float lbf = key2f(lb);
+  lbf = (lbf == lbf) ? lbf : -INFINITY;  // the -inf bucket of a bf16 key: every value
+
+  // candidates: every value >= lbf, into LDS in any order (a multiset).  A branch-free
+  // count, one LDS atomic per wave to reserve the wave's range, then the writes.
+  fresh();
+  unsigned cnt = 0;
+#pragma unroll
+  for (int kk = 0; kk < VPT; ++kk) {
+    float f[VEC];
+    Fmt<T>::unpack(w[kk], f);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) cnt += (f[e] >= lbf) ? 1u : 0u;
+  }
+  const unsigned incl = scan_add_u(cnt);
+  unsigned wbase = 0;
+  if (lane == WAVE - 1 && incl > 0u) wbase = atomicAdd(&s_pick[0], incl);
+  unsigned pos = (unsigned)__builtin_amdgcn_readlane((int)wbase, WAVE - 1) + incl - cnt;
+  if (cnt > 0u) {
+    fresh();
+#pragma unroll
+    for (int kk = 0; kk < VPT; ++kk) {
+      float f[VEC];
+      Fmt<T>::unpack(w[kk], f);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e)
+        if (f[e] >= lbf) {
+          if (pos < (unsigned)cap) s_keys[pos] = f2key(f[e]) & KMASK;
+          ++pos;
+        }
+    }
+  }
+  __syncthreads();
+  const unsigned n = s_pick[0];
+  __syncthreads();  // every thread holds n before s_pick is reused
+  unsigned own_n;
+  if (n <= (unsigned)cap) {
+    own_n = n;
+  } else {  // heavy ties: the exact k-th largest of the chunk, then keys above it
+    auto each = [&](auto fn) {
+#pragma unroll
+      for (int kk = 0; kk < VPT; ++kk)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+          fn(key(kk, e));
+    };
+    fresh();
+    const uint32_t tc = block_kth_largest(k, NPASS, each, s_hist, s_ge, s_pick);
+    fresh();
+    if (tid == 0) s_pick[0] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < VPT; ++kk)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const uint32_t kv = key(kk, e);
+        if (kv > tc) {
+          const unsigned i = atomicAdd(&s_pick[0], 1u);
+          if (i < (unsigned)k) s_keys[i] = kv;  // fewer than k lie above the k-th largest
+        }
+      }
+    __syncthreads();
+    const unsigned na = s_pick[0] < (unsigned)k ? s_pick[0] : (unsigned)k;
+    for (unsigned i = na + tid; i < (unsigned)k; i += NT) s_keys[i] = tc;
+    __syncthreads();
+    own_n = (unsigned)k;
+  }
+  return own_n;
+}
+
 template <typename T, bool ALIGNED>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_topk_select(const Args a, int cap) {
   constexpr int VEC = Fmt<T>::VEC;
@@ -275,7 +414,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
   u64 *cw = rw + (size_t)c * W;
 
   // The chunk stays in registers as raw 16-byte vectors (8 bf16 or 4 f32 values each);
-  // key(kk, e) unpacks one value.  Elements past the row's end are absent.
+  // elements past the row's end get the bits of a negative NaN.
   u32x4 w[VPT];
   {
     const T *row = seq_row<T>(a, b, jr);
@@ -286,6 +425,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
         const int vi = c * CHUNK_VECS + kk * NT + tid;
         w[kk] = __builtin_nontemporal_load(rv + (vi < a.nvec ? vi : a.nvec - 1));
       }
+      if ((c + 1) * CHUNK_VECS > a.nvec) {  // the row's tail: vectors past its end
+#pragma unroll
+        for (int kk = 0; kk < VPT; ++kk)
+          if (c * CHUNK_VECS + kk * NT + tid >= a.nvec) w[kk] = u32x4{~0u, ~0u, ~0u, ~0u};
+      }
     } else {
 #pragma unroll
       for (int kk = 0; kk < VPT; ++kk) {
@@ -293,7 +437,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
           const long idx = elem_index<T>(c, kk, tid, e);
-          h[e] = __float_as_uint(Fmt<T>::at(row, (size_t)(idx < a.V ? idx : (long)a.V - 1)));
+          h[e] = (idx < a.V) ? __float_as_uint(Fmt<T>::at(row, (size_t)idx)) : ~0u;
         }
         if (VEC == 8) {
           w[kk].x = (h[0] >> 16) | (h[1 % VEC] & 0xffff0000u);
@@ -309,118 +453,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
       }
     }
   }
-  // bf16 keys keep only their upper half: a negative value's key has its low half set,
-  // and the radix select resolves 16 bits, so every comparison happens at that width.
-  constexpr uint32_t KMASK = (sizeof(T) == 2) ? 0xffff0000u : 0xffffffffu;
-  auto key = [&](int kk, int e) -> uint32_t {
-    float f[VEC];
-    Fmt<T>::unpack(w[kk], f);
-    return f2key(f[e]) & KMASK;
-  };
-  // Between passes over the chunk the raw vectors are marked as changed, so each pass
-  // unpacks its values again instead of keeping all of them live in registers.
-  auto fresh = [&]() {
-#pragma unroll
-    for (int kk = 0; kk < VPT; ++kk) asm volatile("" : "+v"(w[kk]));
-  };
-  const bool full = (long)(c + 1) * CHUNK_VECS * VEC <= (long)a.V;
-  const unsigned vlim = (unsigned)a.V;
-  auto present = [&](int kk, int e) {
-    return full || ((unsigned)(c * CHUNK_VECS + kk * NT + tid) * (unsigned)VEC + (unsigned)e) < vlim;
-  };
-
-  // lower bound: per wave the ceil(k/4)-th largest thread maximum (bitonic sort of the
-  // wave's 64 maxima, descending), the smallest over the waves.  Comparisons against it
-  // are made on values: x >= key2f(lb) exactly when key(x) >= lb, for every value that is
-  // not a NaN (a row with a NaN is reported as an error whatever its threshold).
-  float tm = -INFINITY;
-#pragma unroll
-  for (int kk = 0; kk < VPT; ++kk) {
-    float f[VEC];
-    Fmt<T>::unpack(w[kk], f);
-#pragma unroll
-    for (int e = 0; e < VEC; ++e)
-      if (present(kk, e)) tm = fmaxf(tm, f[e]);
-  }
-  uint32_t v = f2key(tm) & KMASK;
-  for (int size = 2; size <= WAVE; size <<= 1)
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const uint32_t o = (uint32_t)__shfl_xor((int)v, stride);
-      const bool desc = (lane & size) == 0 || size == WAVE;
-      const bool lower = (lane & stride) == 0;
-      v = (desc == lower) ? ((o > v) ? o : v) : ((o < v) ? o : v);
-    }
-  const int q = (k + NW - 1) / NW - 1;
-  const uint32_t wv = (uint32_t)__builtin_amdgcn_readlane((int)v, q);
-  if (lane == 0) s_wv[wid] = wv;
-  if (tid == 0) s_pick[0] = 0u;  // the candidate count
-  __syncthreads();
-  uint32_t lb = s_wv[0];
-#pragma unroll
-  for (int w2 = 1; w2 < NW; ++w2) lb = (s_wv[w2] < lb) ? s_wv[w2] : lb;
-  float lbf = key2f(lb);
-  lbf = (lbf == lbf) ? lbf : -INFINITY;  // the -inf bucket of a bf16 key: every value
-
-  // candidates: every value >= lbf, appended to LDS in any order (a multiset)
-  fresh();
-#pragma unroll
-  for (int kk = 0; kk < VPT; ++kk) {
-    float f[VEC];
-    Fmt<T>::unpack(w[kk], f);
-#pragma unroll
-    for (int e = 0; e < VEC; ++e)
-      if (present(kk, e) && f[e] >= lbf) {
-        const unsigned i = atomicAdd(&s_pick[0], 1u);
-        if (i < (unsigned)cap) s_keys[i] = f2key(f[e]) & KMASK;
-      }
-  }
-  __syncthreads();
-  const unsigned n = s_pick[0];
-  __syncthreads();  // every thread holds n before s_pick is reused
-  // This chunk's list ends in s_keys[0, own_n); chunks other than the row's last publish
-  // it, the last keeps it in LDS for the collection.
+  const unsigned own_n = topk_chunk_list<T>(w, k, cap, s_keys, s_hist, s_ge, s_wv, s_pick);
+  // Chunks other than the row's last publish their list; the last keeps it in LDS.
   const bool last = (c == a.C - 1);
-  unsigned own_n;
-  if (n <= (unsigned)cap) {
-    own_n = n;
-    if (!last) {
-      for (unsigned i = tid; i < n; i += NT) tw_put(&cw[1 + i], tag, s_keys[i]);
-      if (tid == 0) tw_put(&cw[0], tag, n);
-    }
-  } else {  // heavy ties: the exact k-th largest of the chunk, then keys above it
-    auto each = [&](auto fn) {
-#pragma unroll
-      for (int kk = 0; kk < VPT; ++kk)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e)
-          if (present(kk, e)) fn(key(kk, e));
-    };
-    fresh();
-    const uint32_t tc = block_kth_largest(k, NPASS, each, s_hist, s_ge, s_pick);
-    fresh();
-    if (tid == 0) s_pick[0] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < VPT; ++kk)
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const uint32_t kv = key(kk, e);
-        if (present(kk, e) && kv > tc) {
-          const unsigned i = atomicAdd(&s_pick[0], 1u);
-          if (i < (unsigned)k) s_keys[i] = kv;  // fewer than k lie above the k-th largest
-        }
-      }
-    __syncthreads();
-    const unsigned na = s_pick[0] < (unsigned)k ? s_pick[0] : (unsigned)k;
-    for (unsigned i = na + tid; i < (unsigned)k; i += NT) s_keys[i] = tc;
-    __syncthreads();
-    own_n = (unsigned)k;
-    if (!last) {
-      for (unsigned i = tid; i < (unsigned)k; i += NT) tw_put(&cw[1 + i], tag, s_keys[i]);
-      if (tid == 0) tw_put(&cw[0], tag, (unsigned)k);
-    }
+  if (!last) {
+    for (unsigned i = tid; i < own_n; i += NT) tw_put(&cw[1 + i], tag, s_keys[i]);
+    if (tid == 0) tw_put(&cw[0], tag, own_n);
+    return;
   }
-  if (!last) return;
   __syncthreads();  // s_pick is the collector's next
 
   // The row's collector: its own list is s_keys[0, own_n); every other chunk's count
