@@ -291,7 +291,7 @@ bool ov_plan(int32_t B, int32_t G, int32_t V, sv_dtype dt, int32_t top_k, OvPlan
   p.tw_hist = o; o = align256(o + (p.topk ? sv_host::topk_words(p.R, p.C, top_k) * 8 : 0));
   p.zero_bytes = o;
   p.row_tau = o; o = align256(o + (p.topk ? R * 4 : 0));
-  p.tk_state = o; o = align256(o + (p.topk ? R * 8 : 0));
+  p.tk_state = o; o = align256(o + (p.topk ? sv_host::topk_state_bytes(p.R, p.C, top_k) : 0));
   p.total = o;
   return true;
 }
@@ -411,7 +411,7 @@ const char *sv_overlap_launch_plan(int32_t B, int32_t G, int32_t V, sv_dtype dty
   (void)temperature;
   if (G == 0) return "";
   if (top_k > 0 && top_k < V) {
-    if (sv_host::topk_one_pass(top_k, sv_host::row_chunks(V, dtype == SV_BF16 ? 2 : 4))) return "k_topk_select;k_overlap";
+    if (sv_host::topk_one_pass(top_k, sv_host::row_chunks(V, dtype == SV_BF16 ? 2 : 4))) return "k_topk_select;k_topk_merge;k_overlap";
     return dtype == SV_BF16 ? "k_topk_digit;k_topk_digit;k_overlap"
                             : "k_topk_digit;k_topk_digit;k_topk_digit;k_topk_digit;k_overlap";
   }

@@ -676,7 +676,7 @@ bool tree_plan(int32_t B, int32_t N, int32_t V, int32_t S, sv_dtype dt, float T,
   p.job = o; o = align256(o + Bz * 2 * 4);
   p.job_c = o; o = align256(o + Bz * 8);
   p.row_tau = o; o = align256(o + (p.topk ? R * 4 : 0));
-  p.tk_state = o; o = align256(o + (p.topk ? R * 8 : 0));
+  p.tk_state = o; o = align256(o + (p.topk ? sv_host::topk_state_bytes(p.R, p.C, top_k) : 0));
   p.total = o;
   return true;
 }
@@ -852,8 +852,8 @@ const char *sv_tree_launch_plan(int32_t B, int32_t N, int32_t V, int32_t max_chi
   // [threshold: none, one select pass, 2 digit passes (bf16), 4 digit passes (f32)][resid]
   static const char *names[4][2] = {
       {"k_tree_rows;k_tree_walk;k_tree_draw", "k_tree_rows;k_tree_resid;k_tree_walk;k_tree_draw"},
-      {"k_topk_select;k_tree_rows;k_tree_walk;k_tree_draw",
-       "k_topk_select;k_tree_rows;k_tree_resid;k_tree_walk;k_tree_draw"},
+      {"k_topk_select;k_topk_merge;k_tree_rows;k_tree_walk;k_tree_draw",
+       "k_topk_select;k_topk_merge;k_tree_rows;k_tree_resid;k_tree_walk;k_tree_draw"},
       {"k_topk_digit;k_topk_digit;k_tree_rows;k_tree_walk;k_tree_draw",
        "k_topk_digit;k_topk_digit;k_tree_rows;k_tree_resid;k_tree_walk;k_tree_draw"},
       {"k_topk_digit;k_topk_digit;k_topk_digit;k_topk_digit;k_tree_rows;k_tree_walk;k_tree_draw",

@@ -1057,7 +1057,7 @@ bool make_plan(int32_t B, int32_t G, int32_t V, sv_dtype dt, float T, int32_t to
   p.tw_hist = o; o = align256(o + (p.topk ? sv_host::topk_words(p.R, p.C, top_k) * 8 : 0));
   p.zero_bytes = o;
   p.row_tau = o; o = align256(o + (p.topk ? R * 4 : 0));
-  p.tk_state = o; o = align256(o + (p.topk ? R * 8 : 0));
+  p.tk_state = o; o = align256(o + (p.topk ? sv_host::topk_state_bytes(p.R, p.C, top_k) : 0));
   p.total = o;
   return true;
 }
@@ -1067,7 +1067,7 @@ const char *kPlanNames[] = {
     "k_topk_digit;k_topk_digit;k_topk_digit;k_topk_digit;k_verify",
     "k_verify",
     "k_argmax",
-    "k_topk_select;k_verify",
+    "k_topk_select;k_topk_merge;k_verify",
 };
 
 template <typename T, bool AL>

@@ -25,7 +25,8 @@ struct Work {                  // carved from the caller's workspace
                                //   sum (p - min(p, q)) (head, tail each)
   // plain, handed from one kernel to the next
   float *row_tau;              // [R] top-k threshold (raw logit)
-  uint2 *tk_state;             // [R] radix-select prefix and remaining rank
+  uint2 *tk_state;             // [R] radix-select prefix and remaining rank, or the one-pass
+                               //   select's chunk lists (see k_topk_select)
 };
 
 struct Args {
@@ -173,17 +174,19 @@ __global__ __launch_bounds__(NT) void k_topk_digit(const Args a, int pass, int l
 // multiset of its values that holds its k largest (count word, then the keys), and the
 // row's last chunk in grid order takes the k-th largest key of their union, which is the
 // row's k-th largest: each chunk contributes at most k values to the row's top k, and
-// those are among its own k largest.  A chunk finds a lower bound on its k-th largest
+// those are among its own k largest (k_topk_merge takes that k-th largest, one workgroup
+// per row, in a launch of its own).  A chunk finds a lower bound on its k-th largest
 // from its threads' maxima (wave w's ceil(k/4)-th largest maximum, the smallest over the
 // four waves: at least 4*ceil(k/4) >= k values lie at or above it) and publishes every
 // value at or above that bound.  Should that be more than `cap` values (heavy ties), it
 // takes its exact k-th largest tau_c by radix select over its registers and publishes the
 // values above tau_c and enough copies of tau_c to make k.  Keys are f2key of the value;
-// elements past the row's end are not part of it.  A row whose collector gave up gets a
-// NaN threshold, which the kernels that read it report as an error.
+// elements past the row's end are not part of it.  The lists are plain data in the
+// workspace's tk_state region (cap + 1 words per chunk: the count, then the keys).
 constexpr int TOPK_SELECT_MAX = 256;    // largest k of the one-pass select
-constexpr int TOPK_SELECT_MAX_C = 1024;  // most chunks per row of the one-pass select
-constexpr int TOPK_LDS_KEYS = 4096;      // the collector keeps up to this many keys in LDS
+constexpr int TOPK_SELECT_MAX_C = 256;   // most chunks per row of the one-pass select
+constexpr int TOPK_LDS_KEYS = 1024;      // a chunk's list (at most cap <= 1024 keys), and the
+                                         // collector's keys while they fit (else read again)
 
 // Inclusive scan of unsigned values over the wave (DPP).
 SVD unsigned scan_add_u(unsigned x) {
@@ -398,20 +401,14 @@ template <typename T, bool ALIGNED>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_topk_select(const Args a, int cap) {
   constexpr int VEC = Fmt<T>::VEC;
   constexpr int NPASS = (sizeof(T) == 2) ? 2 : 4;
-  __shared__ unsigned s_hist[256], s_ge[256], s_w[NW], s_wv[NW], s_pick[2];
+  __shared__ unsigned s_hist[256], s_ge[256], s_wv[NW], s_pick[2];
   __shared__ unsigned s_keys[TOPK_LDS_KEYS];
-  __shared__ unsigned s_coff[TOPK_SELECT_MAX_C + 1];
-  __shared__ int s_alive;
-  const int tid = threadIdx.x, lane = lane_id(), wid = tid / WAVE;
+  const int tid = threadIdx.x;
   int phase, xi;
   if (!lane_item((int)(a.B * a.rps), a.C, 0, phase, xi)) return;  // units: rows
   const int r = xi / a.C, c = xi - r * a.C;
   const int b = r / a.rps, jr = r - b * a.rps;
   const int k = a.top_k;
-  const unsigned tag = a.tag;
-  const size_t W = (size_t)cap + 1;  // words per chunk: the count, then up to cap keys
-  u64 *rw = a.w.tw_hist + (size_t)r * a.C * W;
-  u64 *cw = rw + (size_t)c * W;
 
   // The chunk stays in registers as raw 16-byte vectors (8 bf16 or 4 f32 values each);
   // elements past the row's end get the bits of a negative NaN.
@@ -454,78 +451,59 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
     }
   }
   const unsigned own_n = topk_chunk_list<T>(w, k, cap, s_keys, s_hist, s_ge, s_wv, s_pick);
-  // Chunks other than the row's last publish their list; the last keeps it in LDS.
-  const bool last = (c == a.C - 1);
-  if (!last) {
-    for (unsigned i = tid; i < own_n; i += NT) tw_put(&cw[1 + i], tag, s_keys[i]);
-    if (tid == 0) tw_put(&cw[0], tag, own_n);
-    return;
-  }
-  __syncthreads();  // s_pick is the collector's next
+  // The list goes to the workspace as plain data (count, then keys) for k_topk_merge.
+  uint32_t *lw = reinterpret_cast<uint32_t *>(a.w.tk_state) + ((size_t)r * a.C + c) * ((size_t)cap + 1);
+  for (unsigned i = tid; i < own_n; i += NT) lw[1 + i] = s_keys[i];
+  if (tid == 0) lw[0] = own_n;
+}
 
-  // The row's collector: its own list is s_keys[0, own_n); every other chunk's count
-  // (chunks in blocks of NT, one a thread) and first key index, then their keys, each
-  // polled until it carries this call's tag, staged after the own ones while they fit.
-  const int CO = a.C - 1;  // the other chunks
-  unsigned polls = 0;
-  bool ok = true;
-  unsigned others = 0;
-  for (int c0 = 0; c0 < CO; c0 += NT) {
+// The row threshold of the one-pass select (one workgroup per row, after k_topk_select):
+// the k-th largest key of the union of the row's chunk lists, staged in LDS when they fit
+// (else read again by each radix pass).
+template <typename T>
+__global__ __launch_bounds__(NT) void k_topk_merge(const Args a, int cap) {
+  constexpr int NPASS = (sizeof(T) == 2) ? 2 : 4;
+  __shared__ unsigned s_hist[256], s_ge[256], s_w[NW], s_pick[2];
+  __shared__ unsigned s_keys[TOPK_LDS_KEYS];
+  __shared__ unsigned s_coff[TOPK_SELECT_MAX_C + 1];
+  const int tid = threadIdx.x;
+  const long long r = blockIdx.x;
+  if (r >= (long long)a.B * a.rps) return;
+  const int k = a.top_k, C = a.C;
+  const size_t W = (size_t)cap + 1;
+  const uint32_t *rl = reinterpret_cast<const uint32_t *>(a.w.tk_state) + (size_t)r * C * W;
+  unsigned total = 0;
+  for (int c0 = 0; c0 < C; c0 += NT) {
     const int cc = c0 + tid;
-    unsigned nc = 0;
-    if (cc < CO) {
-      u64 w;
-      for (;;) {
-        w = ld_dev(&rw[(size_t)cc * W]);
-        if (tw_ok(w, tag) || ++polls >= a.spin_limit) break;
-        __builtin_amdgcn_s_sleep(2);
-      }
-      ok = ok && tw_ok(w, tag);
-      nc = (unsigned)w;
-      nc = (nc <= (unsigned)cap) ? nc : 0u;  // never trust a count beyond the chunk's words
-    }
+    unsigned nc = (cc < C) ? rl[(size_t)cc * W] : 0u;
+    nc = (nc <= (unsigned)cap) ? nc : 0u;  // never trust a count beyond the chunk's words
     unsigned tot;
     const unsigned before = block_excl_scan(nc, s_w, tot);
-    if (cc < CO) s_coff[cc] = others + before;
-    others += tot;
+    if (cc < C) s_coff[cc] = total + before;
+    total += tot;
   }
-  if (tid == 0) s_alive = 1;
+  if (tid == 0) s_coff[C] = total;
   __syncthreads();
-  if (!ok) s_alive = 0;
-  const unsigned total = own_n + others;
-  const bool in_lds = total <= (unsigned)TOPK_LDS_KEYS;
-  // the word of another chunk's key h: its chunk is the last one whose first index is <= h
-  auto key_word = [&](unsigned h) -> const u64 * {
-    int lo = 0, hi = CO - 1;
+  // key g: its chunk is the last one whose first index is <= g
+  auto key_at = [&](unsigned g) -> uint32_t {
+    int lo = 0, hi = C - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (s_coff[mid] <= h) lo = mid;
+      if (s_coff[mid] <= g) lo = mid;
       else hi = mid - 1;
     }
-    return &rw[(size_t)lo * W + 1 + (h - s_coff[lo])];
+    return rl[(size_t)lo * W + 1 + (g - s_coff[lo])];
   };
+  const bool in_lds = total <= (unsigned)TOPK_LDS_KEYS;
+  if (in_lds)
+    for (unsigned g = tid; g < total; g += NT) s_keys[g] = key_at(g);
   __syncthreads();
-  if (s_alive) {
-    for (unsigned h = tid; h < others; h += NT) {
-      const u64 *pw = key_word(h);
-      u64 w;
-      for (;;) {
-        w = ld_dev(pw);
-        if (tw_ok(w, tag) || ++polls >= a.spin_limit) break;
-        __builtin_amdgcn_s_sleep(2);
-      }
-      if (!tw_ok(w, tag)) s_alive = 0;
-      if (in_lds) s_keys[own_n + h] = (unsigned)w;
-    }
-  }
-  __syncthreads();
-  if (!s_alive || total < (unsigned)k) {
+  if (total < (unsigned)k) {  // cannot happen with a complete select pass
     if (tid == 0) a.w.row_tau[r] = NAN;
     return;
   }
   auto each = [&](auto f) {
-    for (unsigned g = tid; g < total; g += NT)
-      f((in_lds || g < own_n) ? s_keys[g] : (uint32_t)ld_dev(key_word(g - own_n)));
+    for (unsigned g = tid; g < total; g += NT) f(in_lds ? s_keys[g] : key_at(g));
   };
   const uint32_t tk = block_kth_largest(k, NPASS, each, s_hist, s_ge, s_pick);
   if (tid == 0) a.w.row_tau[r] = tau_of_key(tk);
@@ -638,8 +616,14 @@ inline int topk_cap(int top_k) {
   const int c = 4 * top_k;
   return c < 128 ? 128 : (c > 1024 ? 1024 : c);
 }
+// Tagged words of the digit passes' histograms (none for the one-pass select).
 inline size_t topk_words(long long R, int C, int top_k) {
-  return (size_t)R * (size_t)C * (topk_one_pass(top_k, C) ? (size_t)topk_cap(top_k) + 1 : (size_t)128);
+  return topk_one_pass(top_k, C) ? 0 : (size_t)R * (size_t)C * 128;
+}
+// Bytes of the plain tk_state region: the chunk lists of the one-pass select, or the
+// digit passes' (prefix, rank) per row.
+inline size_t topk_state_bytes(long long R, int C, int top_k) {
+  return topk_one_pass(top_k, C) ? (size_t)R * (size_t)C * ((size_t)topk_cap(top_k) + 1) * 4 : (size_t)R * 8;
 }
 // Chunks per row (as the kernels cut rows) for a row of V values of esz bytes.
 inline int row_chunks(int V, int esz) {
@@ -648,7 +632,7 @@ inline int row_chunks(int V, int esz) {
 }
 // The plan names of the threshold launches, ';'-terminated.
 inline const char *topk_plan(int top_k, int C, bool bf16) {
-  if (topk_one_pass(top_k, C)) return "k_topk_select;";
+  if (topk_one_pass(top_k, C)) return "k_topk_select;k_topk_merge;";
   return bf16 ? "k_topk_digit;k_topk_digit;" : "k_topk_digit;k_topk_digit;k_topk_digit;k_topk_digit;";
 }
 template <typename T, bool AL>
@@ -658,6 +642,8 @@ void launch_topk(Launcher &L, sv::Args aa, unsigned grid, int C) {
     int cap = topk_cap(aa.top_k);
     void *args[] = {&aa, &cap};
     L.go((const void *)&sv::k_topk_select<T, AL>, grid, args);
+    aa.tag = next_tag();
+    L.go((const void *)&sv::k_topk_merge<T>, (unsigned)((long long)aa.B * aa.rps), args);
     return;
   }
   const int passes = (sizeof(T) == 2) ? 2 : 4;

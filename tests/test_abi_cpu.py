@@ -49,8 +49,8 @@ def test_status_strings(lib):
 def test_launch_plan(lib):
     assert sv.sv_launch_plan(64, 4, 128256, sv.SV_BF16, 1.0, 0) == ["k_verify"]
     assert sv.sv_launch_plan(256, 7, 152064, sv.SV_BF16, 0.0, 50) == ["k_argmax"]
-    assert sv.sv_launch_plan(128, 6, 128256, sv.SV_BF16, 0.8, 50) == ["k_topk_select", "k_verify"]
-    assert sv.sv_launch_plan(8, 5, 32000, sv.SV_F32, 0.7, 5) == ["k_topk_select", "k_verify"]
+    assert sv.sv_launch_plan(128, 6, 128256, sv.SV_BF16, 0.8, 50) == ["k_topk_select", "k_topk_merge", "k_verify"]
+    assert sv.sv_launch_plan(8, 5, 32000, sv.SV_F32, 0.7, 5) == ["k_topk_select", "k_topk_merge", "k_verify"]
     # k above the one-pass select's limit: the radix digit passes (2 for bf16, 4 for f32)
     assert sv.sv_launch_plan(128, 6, 128256, sv.SV_BF16, 0.8, 257) == \
         ["k_topk_digit", "k_topk_digit", "k_verify"]
@@ -174,7 +174,7 @@ def test_overlap_layouts_and_empty(lib):
 
 def test_overlap_plan_and_workspace(lib):
     assert sv.sv_overlap_launch_plan(64, 4, 128256, sv.SV_BF16, 1.0, 0) == ["k_overlap"]
-    assert sv.sv_overlap_launch_plan(64, 4, 128256, sv.SV_BF16, 1.0, 50) == ["k_topk_select", "k_overlap"]
+    assert sv.sv_overlap_launch_plan(64, 4, 128256, sv.SV_BF16, 1.0, 50) == ["k_topk_select", "k_topk_merge", "k_overlap"]
     assert sv.sv_overlap_launch_plan(64, 4, 128256, sv.SV_BF16, 1.0, 300) == \
         ["k_topk_digit", "k_topk_digit", "k_overlap"]
     assert len(sv.sv_overlap_launch_plan(8, 5, 32000, sv.SV_F32, 0.7, 500)) == 5
@@ -217,7 +217,7 @@ def test_tree_optional_pointers_and_plan(lib):
         ["k_tree_rows", "k_tree_resid", "k_tree_walk", "k_tree_draw"]
     assert sv.sv_tree_launch_plan(16, 32, 128256, 1, sv.SV_BF16, 1.0, 0) == ["k_tree_rows", "k_tree_walk", "k_tree_draw"]
     assert sv.sv_tree_launch_plan(16, 32, 128256, 4, sv.SV_BF16, 0.0, 0) == ["k_tree_rows", "k_tree_walk"]
-    assert sv.sv_tree_launch_plan(16, 32, 128256, 4, sv.SV_F32, 0.7, 5)[:2] == ["k_topk_select", "k_tree_rows"]
+    assert sv.sv_tree_launch_plan(16, 32, 128256, 4, sv.SV_F32, 0.7, 5)[:3] == ["k_topk_select", "k_topk_merge", "k_tree_rows"]
     assert sv.sv_tree_launch_plan(16, 32, 128256, 4, sv.SV_F32, 0.7, 300)[:4] == ["k_topk_digit"] * 4
     args = (16, 32, 128256, 4, sv.SV_BF16, 1.0, 0)
     n, z = lib.sv_tree_workspace_bytes(*args), lib.sv_tree_workspace_zero_bytes(*args)
@@ -249,7 +249,7 @@ def test_typical_plan_and_workspace(lib):
     assert call_typ(lib, G=256, nbytes=16) == 5
     assert call_typ(lib, eps=0.0, delta=0.0, nbytes=16) == 5
     assert sv.sv_typical_launch_plan(64, 4, 128256, sv.SV_BF16, 1.0, 0) == ["k_typical"]
-    assert sv.sv_typical_launch_plan(64, 4, 128256, sv.SV_BF16, 1.0, 50) == ["k_topk_select", "k_typical"]
+    assert sv.sv_typical_launch_plan(64, 4, 128256, sv.SV_BF16, 1.0, 50) == ["k_topk_select", "k_topk_merge", "k_typical"]
     assert sv.sv_typical_launch_plan(64, 4, 128256, sv.SV_BF16, 1.0, 300) == ["k_topk_digit"] * 2 + ["k_typical"]
     args = (64, 4, 128256, sv.SV_BF16, 1.0, 0)
     n, z = lib.sv_typical_workspace_bytes(*args), lib.sv_typical_workspace_zero_bytes(*args)

@@ -73,6 +73,7 @@ SHAPES = [
     (8, 3, 20000, "bf16", 0.8, 256),   # the largest k of the one-pass threshold
     (8, 3, 9003, "f32", 0.8, 257),     # the smallest k of the radix digit passes
     (4, 2, 300000, "f32", 0.9, 100),   # 37 chunks per row
+    (2, 1, 2200000, "f32", 0.9, 40),   # 269 chunks per row: the radix digit passes
 ]
 
 
