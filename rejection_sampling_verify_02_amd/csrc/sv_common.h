@@ -397,8 +397,10 @@ SVD unsigned topk_chunk_list(u32x4 (&w)[VPT], int k, int cap, unsigned *s_keys,
   return own_n;
 }
 
+// Seven resident waves per SIMD (at most 72 registers; the rare exact-select path spills a
+// little): the pass streams faster with more workgroups in flight than with fewer and no spill.
 template <typename T, bool ALIGNED>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_topk_select(const Args a, int cap) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(7))) void k_topk_select(const Args a, int cap) {
   constexpr int VEC = Fmt<T>::VEC;
   constexpr int NPASS = (sizeof(T) == 2) ? 2 : 4;
   __shared__ unsigned s_hist[256], s_ge[256], s_wv[NW], s_pick[2];
