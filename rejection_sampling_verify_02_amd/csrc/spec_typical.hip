@@ -375,6 +375,7 @@ sv_status typ_run(const void *target, sv_dtype dt, const int32_t *tokens, int32_
   a.w.tw_hist = (u64 *)(base + p.tw_hist);
   a.w.row_tau = (float *)(base + p.row_tau);
   a.w.tk_state = (uint2 *)(base + p.tk_state);
+  a.w.tk_part = nullptr;
   t.ln_eps = log((double)eps);  // -inf for eps = 0: every token of the support passes
   t.ln_delta = log((double)delta);
 

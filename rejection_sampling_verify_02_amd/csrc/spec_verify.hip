@@ -612,8 +612,41 @@ SVD void norm_item(const Args &a, int item) {
   const bool gath = finisher && !G0 && wid == 0 && lane < a.G;
   const int gx = gath ? a.tokens[(size_t)b * a.G + lane] : 0;
   const T *row = seq_row<T>(a, b, jr);
-  float x[VPT][VEC];
   float gzt = NAN, gzd = NAN;
+
+  // The partial goes out (or the sequence is finished) from wave 0.
+  __shared__ double s_gseg[SEGS];
+  auto finish = [&](float off, float s_hi, float s_lo) {
+    if (jr == a.rps - 1 && c == a.C - 1) {
+      if (a.rps * a.C <= SEQ_LDS_PARTS && a.rps <= SEQ_LDS_ROWS)
+        sampling_finish<T, ALIGNED, TOPK, true, G0>(a, b, off, s_hi, s_lo, gx, gzt, gzd, s_gseg);
+      else
+        sampling_finish<T, ALIGNED, TOPK, false, G0>(a, b, off, s_hi, s_lo, gx, gzt, gzd, s_gseg);
+      return;
+    }
+    u64 *pw = a.w.tw_part + ((size_t)r * a.C + c) * 3;
+    if (lane < 3) tw_putf(pw + lane, a.tag, lane == 0 ? off : (lane == 1 ? s_hi : s_lo));
+    if (G0 && lane < 2 * SEGS) {
+      u64 *gw = a.w.tw_gseg + (((size_t)b * a.C + c) * SEGS) * 2;
+      const double v = s_gseg[lane >> 1];
+      tw_putf(&gw[lane], a.tag, (lane & 1) ? d_tail(v) : d_head(v));
+    }
+  };
+  // After the one-pass top-k threshold, a chunk whose list was complete has its partial
+  // already (kept values only): no load.  The finisher still gathers its token logits.
+  if (TOPK && !G0 && a.w.tk_part) {
+    const uint4 pp = a.w.tk_part[(size_t)r * a.C + c];  // written by the previous kernel
+    if (pp.w == 1u) {
+      if (gath && gx >= 0 && gx < a.V) {
+        gzt = Fmt<T>::at(seq_row<T>(a, b, lane), (size_t)gx);
+        gzd = Fmt<T>::at(seq_row<T>(a, b, a.G + 1 + lane), (size_t)gx);
+      }
+      if (wid != 0) return;
+      finish(__uint_as_float(pp.x), __uint_as_float(pp.y), __uint_as_float(pp.z));
+      return;
+    }
+  }
+  float x[VPT][VEC];
   if (ALIGNED) {
     u32x4 w[VPT];
     const u32x4 *rv = reinterpret_cast<const u32x4 *>(row);
@@ -669,7 +702,6 @@ SVD void norm_item(const Args &a, int item) {
   // segment, a lane's elements summed in index order and the lanes by one DPP tree (the
   // order the draw uses when it re-reads one segment); the chunk sum is the sum of its
   // segments.  The finisher then draws without a second pass over a chunk.
-  __shared__ double s_gseg[SEGS];
   constexpr bool bonus_row = G0;  // the batched sampler: the finisher draws from segment masses
   if (bonus_row) {
     off = (m > -INFINITY) ? m * k2 : -INFINITY;
@@ -719,23 +751,9 @@ SVD void norm_item(const Args &a, int item) {
 
   double S = (s_s[0] + s_s[1]) + (s_s[2] + s_s[3]);
   if (bonus_row) S = (S != S) ? S : wave_sum((lane < SEGS) ? s_gseg[lane] : 0.0);
-  const float s_hi = d_head(S), s_lo = d_tail(S);
   // The sequence's last item in grid order finishes the sequence, from its own values
   // and the other items' published ones.
-  if (jr == a.rps - 1 && c == a.C - 1) {
-    if (a.rps * a.C <= SEQ_LDS_PARTS && a.rps <= SEQ_LDS_ROWS)
-      sampling_finish<T, ALIGNED, TOPK, true, G0>(a, b, off, s_hi, s_lo, gx, gzt, gzd, s_gseg);
-    else
-      sampling_finish<T, ALIGNED, TOPK, false, G0>(a, b, off, s_hi, s_lo, gx, gzt, gzd, s_gseg);
-    return;
-  }
-  u64 *pw = a.w.tw_part + ((size_t)r * a.C + c) * 3;
-  if (lane < 3) tw_putf(pw + lane, a.tag, lane == 0 ? off : (lane == 1 ? s_hi : s_lo));
-  if (bonus_row && lane < 2 * SEGS) {
-    u64 *gw = a.w.tw_gseg + (((size_t)b * a.C + c) * SEGS) * 2;
-    const double v = s_gseg[lane >> 1];
-    tw_putf(&gw[lane], a.tag, (lane & 1) ? d_tail(v) : d_head(v));
-  }
+  finish(off, d_head(S), d_tail(S));
 }
 
 // ---------------------------------------------------------------- pass 1: greedy argmax
@@ -1057,7 +1075,7 @@ bool make_plan(int32_t B, int32_t G, int32_t V, sv_dtype dt, float T, int32_t to
   p.tw_hist = o; o = align256(o + (p.topk ? sv_host::topk_words(p.R, p.C, top_k) * 8 : 0));
   p.zero_bytes = o;
   p.row_tau = o; o = align256(o + (p.topk ? R * 4 : 0));
-  p.tk_state = o; o = align256(o + (p.topk ? sv_host::topk_state_bytes(p.R, p.C, top_k) : 0));
+  p.tk_state = o; o = align256(o + (p.topk ? sv_host::topk_state_bytes(p.R, p.C, top_k, G > 0) : 0));
   p.total = o;
   return true;
 }
@@ -1157,6 +1175,10 @@ sv_status run(const void *target, const void *draft, sv_dtype dt, const int32_t 
   a.w.tw_ov = nullptr;
   a.w.row_tau = (float *)(base + p.row_tau);
   a.w.tk_state = (uint2 *)(base + p.tk_state);
+  // the first pass takes its chunk partials from the one-pass top-k threshold when it can
+  a.w.tk_part = (p.topk && G > 0 && sv_host::topk_one_pass(top_k, p.C))
+                    ? (uint4 *)(base + p.tk_state + sv_host::topk_list_bytes(p.R, p.C, top_k))
+                    : nullptr;
 
   hipStream_t st = (hipStream_t)stream;
   int n = 0;

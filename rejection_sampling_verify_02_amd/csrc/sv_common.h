@@ -27,6 +27,8 @@ struct Work {                  // carved from the caller's workspace
   float *row_tau;              // [R] top-k threshold (raw logit)
   uint2 *tk_state;             // [R] radix-select prefix and remaining rank, or the one-pass
                                //   select's chunk lists (see k_topk_select)
+  uint4 *tk_part;              // [R*C] or null: the one-pass select's chunk normaliser
+                               //   partials for the verification (see k_topk_merge)
 };
 
 struct Args {
@@ -282,12 +284,14 @@ SVD uint32_t wave_kth_largest(uint32_t v, int q, int low) {
 
 // One chunk's list for k_topk_select (whole workgroup), from its raw vectors w: the
 // values at or above the lower bound, or, with heavy ties, the exact top k.  Leaves the
-// keys in s_keys[0, n) and returns n.  Elements past the row's end hold the bits of a
-// negative NaN: key 0, below every other key, ignored by fmaxf and never >= a bound, so
-// they can neither enter a list nor move a chunk's k-th largest (a chunk that reaches the
-// exact select holds more than cap >= k real values).
+// keys in s_keys[0, n) and returns n.  A value enters the list unless it is below the
+// bound, so every NaN of the chunk does, with its own key (above +inf's or below -inf's),
+// and k_topk_merge sees it.  Elements past the row's end hold -inf: they can enter a list
+// only when the bound is -inf, and a -inf can move a k-th largest only when that is -inf
+// already; their terms are 0.  A list is incomplete (*incomplete) when it comes from the
+// exact select: it then holds the values above the chunk's k-th largest and copies of it.
 template <typename T>
-SVD unsigned topk_chunk_list(u32x4 (&w)[VPT], int k, int cap, unsigned *s_keys,
+SVD unsigned topk_chunk_list(u32x4 (&w)[VPT], int k, int cap, unsigned *s_keys, bool *incomplete,
                              unsigned *s_hist, unsigned *s_ge, unsigned *s_wv, unsigned *s_pick) {
   constexpr int VEC = Fmt<T>::VEC;
   constexpr int NPASS = (sizeof(T) == 2) ? 2 : 4;
@@ -316,8 +320,7 @@ SVD unsigned topk_chunk_list(u32x4 (&w)[VPT], int k, int cap, unsigned *s_keys,
     float f[VEC];
     Fmt<T>::unpack(w[kk], f);
 #pragma unroll
-    for (int e = 0; e < VEC; ++e)
-      tm = fmaxf(tm, f[e]);
+    for (int e = 0; e < VEC; ++e) tm = fmaxf(tm, f[e]);
   }
   const uint32_t v = f2key(tm) & KMASK;
   const uint32_t wv = wave_kth_largest(v, (k + NW - 1) / NW, sizeof(T) == 2 ? 16 : 0);
@@ -330,7 +333,7 @@ SVD unsigned topk_chunk_list(u32x4 (&w)[VPT], int k, int cap, unsigned *s_keys,
   float lbf = key2f(lb);
   lbf = (lbf == lbf) ? lbf : -INFINITY;  // the -inf bucket of a bf16 key: every value
 
-  // candidates: every value >= lbf, into LDS in any order (a multiset).  A branch-free
+  // candidates: every value not below lbf, into LDS in any order (a multiset).  A branch-free
   // count, one LDS atomic per wave to reserve the wave's range, then the writes.
   fresh();
   unsigned cnt = 0;
@@ -339,7 +342,7 @@ SVD unsigned topk_chunk_list(u32x4 (&w)[VPT], int k, int cap, unsigned *s_keys,
     float f[VEC];
     Fmt<T>::unpack(w[kk], f);
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) cnt += (f[e] >= lbf) ? 1u : 0u;
+    for (int e = 0; e < VEC; ++e) cnt += (f[e] < lbf) ? 0u : 1u;
   }
   const unsigned incl = scan_add_u(cnt);
   unsigned wbase = 0;
@@ -353,7 +356,7 @@ SVD unsigned topk_chunk_list(u32x4 (&w)[VPT], int k, int cap, unsigned *s_keys,
       Fmt<T>::unpack(w[kk], f);
 #pragma unroll
       for (int e = 0; e < VEC; ++e)
-        if (f[e] >= lbf) {
+        if (!(f[e] < lbf)) {
           if (pos < (unsigned)cap) s_keys[pos] = f2key(f[e]) & KMASK;
           ++pos;
         }
@@ -363,6 +366,7 @@ SVD unsigned topk_chunk_list(u32x4 (&w)[VPT], int k, int cap, unsigned *s_keys,
   const unsigned n = s_pick[0];
   __syncthreads();  // every thread holds n before s_pick is reused
   unsigned own_n;
+  *incomplete = n > (unsigned)cap;
   if (n <= (unsigned)cap) {
     own_n = n;
   } else {  // heavy ties: the exact k-th largest of the chunk, then keys above it
@@ -413,7 +417,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(7))) void k_
   const int k = a.top_k;
 
   // The chunk stays in registers as raw 16-byte vectors (8 bf16 or 4 f32 values each);
-  // elements past the row's end get the bits of a negative NaN.
+  // elements past the row's end are -inf.
   u32x4 w[VPT];
   {
     const T *row = seq_row<T>(a, b, jr);
@@ -425,9 +429,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(7))) void k_
         w[kk] = __builtin_nontemporal_load(rv + (vi < a.nvec ? vi : a.nvec - 1));
       }
       if ((c + 1) * CHUNK_VECS > a.nvec) {  // the row's tail: vectors past its end
+        constexpr unsigned NEG_INF = (sizeof(T) == 2) ? 0xff80ff80u : 0xff800000u;
 #pragma unroll
         for (int kk = 0; kk < VPT; ++kk)
-          if (c * CHUNK_VECS + kk * NT + tid >= a.nvec) w[kk] = u32x4{~0u, ~0u, ~0u, ~0u};
+          if (c * CHUNK_VECS + kk * NT + tid >= a.nvec) w[kk] = u32x4{NEG_INF, NEG_INF, NEG_INF, NEG_INF};
       }
     } else {
 #pragma unroll
@@ -436,7 +441,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(7))) void k_
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
           const long idx = elem_index<T>(c, kk, tid, e);
-          h[e] = (idx < a.V) ? __float_as_uint(Fmt<T>::at(row, (size_t)idx)) : ~0u;
+          h[e] = (idx < a.V) ? __float_as_uint(Fmt<T>::at(row, (size_t)idx)) : 0xff800000u;
         }
         if (VEC == 8) {
           w[kk].x = (h[0] >> 16) | (h[1 % VEC] & 0xffff0000u);
@@ -452,11 +457,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(7))) void k_
       }
     }
   }
-  const unsigned own_n = topk_chunk_list<T>(w, k, cap, s_keys, s_hist, s_ge, s_wv, s_pick);
-  // The list goes to the workspace as plain data (count, then keys) for k_topk_merge.
-  uint32_t *lw = reinterpret_cast<uint32_t *>(a.w.tk_state) + ((size_t)r * a.C + c) * ((size_t)cap + 1);
-  for (unsigned i = tid; i < own_n; i += NT) lw[1 + i] = s_keys[i];
-  if (tid == 0) lw[0] = own_n;
+  bool incomplete;
+  const unsigned own_n = topk_chunk_list<T>(w, k, cap, s_keys, &incomplete, s_hist, s_ge, s_wv, s_pick);
+  // The list goes to the workspace as plain data for k_topk_merge: the count, the flags
+  // (2: the list is incomplete), then the keys.
+  uint32_t *lw = reinterpret_cast<uint32_t *>(a.w.tk_state) + ((size_t)r * a.C + c) * ((size_t)cap + 2);
+  for (unsigned i = tid; i < own_n; i += NT) lw[2 + i] = s_keys[i];
+  if (tid == 0) {
+    lw[0] = own_n;
+    lw[1] = incomplete ? 2u : 0u;
+  }
 }
 
 // The row threshold of the one-pass select (one workgroup per row, after k_topk_select):
@@ -472,7 +482,7 @@ __global__ __launch_bounds__(NT) void k_topk_merge(const Args a, int cap) {
   const long long r = blockIdx.x;
   if (r >= (long long)a.B * a.rps) return;
   const int k = a.top_k, C = a.C;
-  const size_t W = (size_t)cap + 1;
+  const size_t W = (size_t)cap + 2;
   const uint32_t *rl = reinterpret_cast<const uint32_t *>(a.w.tk_state) + (size_t)r * C * W;
   unsigned total = 0;
   for (int c0 = 0; c0 < C; c0 += NT) {
@@ -494,7 +504,7 @@ __global__ __launch_bounds__(NT) void k_topk_merge(const Args a, int cap) {
       if (s_coff[mid] <= g) lo = mid;
       else hi = mid - 1;
     }
-    return rl[(size_t)lo * W + 1 + (g - s_coff[lo])];
+    return rl[(size_t)lo * W + 2 + (g - s_coff[lo])];
   };
   const bool in_lds = total <= (unsigned)TOPK_LDS_KEYS;
   if (in_lds)
@@ -509,6 +519,56 @@ __global__ __launch_bounds__(NT) void k_topk_merge(const Args a, int cap) {
   };
   const uint32_t tk = block_kth_largest(k, NPASS, each, s_hist, s_ge, s_pick);
   if (tid == 0) a.w.row_tau[r] = tau_of_key(tk);
+  if (!a.w.tk_part) return;
+
+  // The verification's chunk partials, as its first pass would form them with this
+  // threshold: m = the largest kept value (kept: not below the threshold, i.e. key >= tk),
+  // off = m*k2, S = sum over kept values of 2^(z*k2 - off) (in double here), or off = -inf
+  // and S = 0 with nothing finite kept; S is NaN when the chunk holds a NaN (a complete list
+  // holds all of them) or a +inf is kept.  A complete list holds every value at or above
+  // the threshold; a chunk whose list is incomplete gets no partial and its first-pass item
+  // reads the chunk.  One wave a chunk.
+  const int lane = lane_id(), wid = tid / WAVE;
+  for (int cc = wid; cc < C; cc += NW) {
+    const uint32_t *cl = rl + (size_t)cc * W;
+    const unsigned n = cl[0] <= (unsigned)cap ? cl[0] : 0u, fl = cl[1];
+    uint4 out = make_uint4(0u, 0u, 0u, 0u);
+    if (!(fl & 2u)) {
+      auto val = [&](uint32_t key) -> float {  // a bf16 key keeps its upper half only
+        if (sizeof(T) == 2 && !(key & 0x80000000u)) key |= 0xffffu;
+        return key2f(key);
+      };
+      // keys above +inf's or below -inf's are NaNs (for bf16 as masked keys)
+      constexpr uint32_t KPINF = (sizeof(T) == 2) ? 0xff800000u : 0xff800000u;
+      constexpr uint32_t KNINF = (sizeof(T) == 2) ? 0x007f0000u : 0x007fffffu;
+      float m = -INFINITY;
+      unsigned nanl = 0;
+      for (unsigned i = lane; i < n; i += WAVE) {
+        const uint32_t key = cl[2 + i];
+        nanl |= (key > KPINF || key < KNINF) ? 1u : 0u;
+        if (key >= tk) m = fmaxf(m, val(key));
+      }
+      m = wave_max(m);
+      const bool has_nan = wave_or(nanl) != 0u;
+      float off;
+      double S;
+      if (m > -INFINITY) {
+        off = m * a.k2;
+        double acc = 0.0;
+        for (unsigned i = lane; i < n; i += WAVE) {
+          const uint32_t key = cl[2 + i];
+          if (key >= tk) acc += (double)fast_exp2(fmaf(val(key), a.k2, -off));
+        }
+        S = wave_sum(acc);
+      } else {
+        off = -INFINITY;
+        S = 0.0;
+      }
+      if (has_nan || m == INFINITY) S = NAN;
+      out = make_uint4(__float_as_uint(off), __float_as_uint(d_head(S)), __float_as_uint(d_tail(S)), 1u);
+    }
+    if (lane == 0) a.w.tk_part[(size_t)r * C + cc] = out;
+  }
 }
 
 // ---------------------------------------------------------------- per-chunk normaliser
@@ -624,8 +684,13 @@ inline size_t topk_words(long long R, int C, int top_k) {
 }
 // Bytes of the plain tk_state region: the chunk lists of the one-pass select, or the
 // digit passes' (prefix, rank) per row.
-inline size_t topk_state_bytes(long long R, int C, int top_k) {
-  return topk_one_pass(top_k, C) ? (size_t)R * (size_t)C * ((size_t)topk_cap(top_k) + 1) * 4 : (size_t)R * 8;
+// With parts, room for the verification's chunk partials follows the lists.
+inline size_t topk_list_bytes(long long R, int C, int top_k) {
+  return (size_t)R * (size_t)C * ((size_t)topk_cap(top_k) + 2) * 4;
+}
+inline size_t topk_state_bytes(long long R, int C, int top_k, bool parts = false) {
+  if (!topk_one_pass(top_k, C)) return (size_t)R * 8;
+  return topk_list_bytes(R, C, top_k) + (parts ? (size_t)R * (size_t)C * 16 : 0);
 }
 // Chunks per row (as the kernels cut rows) for a row of V values of esz bytes.
 inline int row_chunks(int V, int esz) {

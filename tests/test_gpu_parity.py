@@ -221,6 +221,38 @@ def test_row_error_codes(dev, case):
     assert np.all(gpu[0][others] >= 0)
 
 
+TOPK_ERR_CASES = ["nan_target", "negnan_draft", "nan_draft_late", "posinf", "all_neginf", "q_zero"]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("case", TOPK_ERR_CASES)
+def test_row_error_codes_topk(dev, case, dtype):
+    """Row data errors under a top-k of 10 (the one-pass threshold, whose chunk lists carry
+    every NaN and +inf to the normaliser), on rows of several chunks."""
+    B, G, V = 6, 4, 20000
+    raw = wl.make_random(B, G, V, dtype, seed=45)
+    k = 10
+    tokens = parity.prepare(raw, 1.0, k)
+    b = 2
+
+    def bits(x):
+        if dtype == "bf16":
+            return np.uint16(x >> 16)
+        return np.array([x], np.uint32).view(np.float32)[0]
+
+    if case == "nan_target": raw.target[b, 4, 17] = bits(0x7fc00000)
+    if case == "negnan_draft": raw.draft[b, 0, 16390] = bits(0xffc00000)
+    if case == "nan_draft_late": raw.draft[b, 3, V - 1] = bits(0x7fc00000)
+    if case == "posinf": raw.target[b, 1, 5] = bits(0x7f800000)
+    if case == "all_neginf": raw.draft[b, 2, :] = bits(0xff800000)
+    if case == "q_zero": raw.draft[b, 1, tokens[b, 1]] = bits(0xff800000)
+    res, gpu, ref = parity.run_both(raw, 1.0, k, dev, tokens=tokens)
+    check(res, f"row error {case} {dtype} top-k {k}")
+    assert ref[0][b] < 0 and gpu[0][b] == ref[0][b]
+    others = [i for i in range(B) if i != b]
+    assert np.all(gpu[0][others] >= 0)
+
+
 def test_workspace_shape_changes(dev):
     """One workspace across calls whose counter prefix grows and shrinks: every call still
     matches the oracle (a longer prefix is zeroed again before the call that needs it)."""
