@@ -351,7 +351,9 @@ def run_verify(args, dev, hev):
 
     ms = wall * 1e3 / K
     t_call = ms / 1e3
-    kernel = "k_argmax" if greedy else KERNEL  # the kernel that streams the logits
+    # the kernel that streams the logits: with the one-pass top-k threshold that is its
+    # select pass (the verification then reads only chunks without a complete list)
+    kernel = "k_argmax" if greedy else ("k_topk_select" if "k_topk_select" in plan else KERNEL)
     traffic, tnote = counters_traffic("verify") if args.config == 3 else (None, "counters are taken on workload 3")
     res = {
         "metric": METRIC, "value": round(B * G / t_call, 1), "unit": "positions/s", "n_gpus": 1, "steps": K,
