@@ -222,7 +222,7 @@ SVD unsigned block_excl_scan(unsigned v, unsigned *s_w, unsigned &total) {
 template <typename Each>
 SVD uint32_t block_kth_largest(int k, int npass, const Each &each, unsigned *hist, unsigned *sge,
                                unsigned *s_pick) {
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = lane_id(), wid = tid / WAVE;
   uint32_t prefix = 0;
   unsigned krem = (unsigned)k;
   for (int pass = 0; pass < npass; ++pass) {
@@ -238,17 +238,22 @@ SVD uint32_t block_kth_largest(int k, int npass, const Each &each, unsigned *his
       if ((key & hm) == (prefix & hm)) atomicAdd(&hist[(key >> shift) & 255u], 1u);
     });
     __syncthreads();
-    sge[tid] = hist[tid];
+    // suffix counts of bin d = tid: the total minus the prefix before d (prefix by a wave
+    // scan, the waves' totals through LDS)
+    const unsigned h = hist[tid];
+    const unsigned incl = scan_add_u(h);
+    if (lane == WAVE - 1) sge[wid] = incl;
     __syncthreads();
-    for (int o = 1; o < 256; o <<= 1) {  // suffix sums (Hillis-Steele)
-      const unsigned add = (tid + o < 256) ? sge[tid + o] : 0u;
-      __syncthreads();
-      sge[tid] += add;
-      __syncthreads();
+    unsigned before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      before += (w < wid) ? sge[w] : 0u;
+      total += sge[w];
     }
+    const unsigned at = total - (before + incl - h);  // values with digit >= d
+    const unsigned above = total - (before + incl);   // values with digit > d
     // the largest digit whose suffix count reaches the remaining rank
-    const unsigned above = (tid < 255) ? sge[tid + 1] : 0u;
-    if (sge[tid] >= krem && above < krem) {
+    if (at >= krem && above < krem) {
       s_pick[0] = (unsigned)tid;
       s_pick[1] = above;
     }
@@ -531,7 +536,9 @@ __global__ __launch_bounds__(NT) void k_topk_merge(const Args a, int cap) {
   const int lane = lane_id(), wid = tid / WAVE;
   for (int cc = wid; cc < C; cc += NW) {
     const uint32_t *cl = rl + (size_t)cc * W;
-    const unsigned n = cl[0] <= (unsigned)cap ? cl[0] : 0u, fl = cl[1];
+    const unsigned n = s_coff[cc + 1] - s_coff[cc], fl = cl[1];
+    // the chunk's keys: staged in LDS, or in the workspace
+    auto kat = [&](unsigned i) -> uint32_t { return in_lds ? s_keys[s_coff[cc] + i] : cl[2 + i]; };
     uint4 out = make_uint4(0u, 0u, 0u, 0u);
     if (!(fl & 2u)) {
       auto val = [&](uint32_t key) -> float {  // a bf16 key keeps its upper half only
@@ -544,7 +551,7 @@ __global__ __launch_bounds__(NT) void k_topk_merge(const Args a, int cap) {
       float m = -INFINITY;
       unsigned nanl = 0;
       for (unsigned i = lane; i < n; i += WAVE) {
-        const uint32_t key = cl[2 + i];
+        const uint32_t key = kat(i);
         nanl |= (key > KPINF || key < KNINF) ? 1u : 0u;
         if (key >= tk) m = fmaxf(m, val(key));
       }
@@ -556,7 +563,7 @@ __global__ __launch_bounds__(NT) void k_topk_merge(const Args a, int cap) {
         off = m * a.k2;
         double acc = 0.0;
         for (unsigned i = lane; i < n; i += WAVE) {
-          const uint32_t key = cl[2 + i];
+          const uint32_t key = kat(i);
           if (key >= tk) acc += (double)fast_exp2(fmaf(val(key), a.k2, -off));
         }
         S = wave_sum(acc);
