@@ -704,11 +704,6 @@ inline int row_chunks(int V, int esz) {
   const long long nvec = ((long long)V * esz + 15) / 16;
   return (int)((nvec + sv::CHUNK_VECS - 1) / sv::CHUNK_VECS);
 }
-// The plan names of the threshold launches, ';'-terminated.
-inline const char *topk_plan(int top_k, int C, bool bf16) {
-  if (topk_one_pass(top_k, C)) return "k_topk_select;k_topk_merge;";
-  return bf16 ? "k_topk_digit;k_topk_digit;" : "k_topk_digit;k_topk_digit;k_topk_digit;k_topk_digit;";
-}
 template <typename T, bool AL>
 void launch_topk(Launcher &L, sv::Args aa, unsigned grid, int C) {
   if (topk_one_pass(aa.top_k, C)) {
