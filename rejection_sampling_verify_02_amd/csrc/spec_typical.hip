@@ -45,9 +45,11 @@ struct TypArgs {
   double ln_delta;  // log(delta)
 };
 
-// The sequence's last item: combine, test, write.  One wave; own_w holds this item's words.
+// The sequence's last item: combine, test, write.  One wave; lane f < TYP_WORDS holds
+// word f of this item's own partial in own_v (a value per lane, so the partial never
+// needs an addressable array, which would live in scratch memory).
 template <typename T, bool TOPK>
-SVD void typical_finish(const TypArgs &ta, int b, const float (&own_w)[TYP_WORDS], int own_c) {
+SVD void typical_finish(const TypArgs &ta, int b, float own_v, int own_c) {
   const Args &a = ta.a;
   const int lane = lane_id();
   const int G = a.G, rps = a.rps, C = a.C;
@@ -57,7 +59,9 @@ SVD void typical_finish(const TypArgs &ta, int b, const float (&own_w)[TYP_WORDS
   __shared__ double s_l2[TYP_MAX_ROWS], s_h[TYP_MAX_ROWS];
   __shared__ int s_arg[TYP_MAX_ROWS], s_ok[TYP_MAX_ROWS];
   __shared__ float s_w[TYP_LDS_PARTS * TYP_WORDS];
+  __shared__ float s_own[TYP_WORDS];
   const bool lds = rps * C <= TYP_LDS_PARTS;
+  if (lane < TYP_WORDS) s_own[lane] = own_v;
 
   // Wait for every partial of the sequence, all lanes loading at once; they are kept in
   // LDS as they arrive (when they fit), so the combine below reads no global memory.
@@ -81,12 +85,7 @@ SVD void typical_finish(const TypArgs &ta, int b, const float (&own_w)[TYP_WORDS
     done = wave_or(mine ? 0u : 1u) == 0u;
     if (!done) __builtin_amdgcn_s_sleep(2);
   }
-  if (lds && lane < TYP_WORDS) {
-    float v = own_w[0];
-#pragma unroll
-    for (int f = 1; f < TYP_WORDS; ++f) v = (lane == f) ? own_w[f] : v;
-    s_w[own * TYP_WORDS + lane] = v;
-  }
+  if (lds && lane < TYP_WORDS) s_w[own * TYP_WORDS + lane] = own_v;
   lds_sync();
   int32_t *out = a.out_tokens + (size_t)b * (G + 1);
   if (!done) {
@@ -96,7 +95,7 @@ SVD void typical_finish(const TypArgs &ta, int b, const float (&own_w)[TYP_WORDS
   }
   auto word = [&](int i, int f) -> float {
     if (lds) return s_w[i * TYP_WORDS + f];
-    return i == own ? own_w[f] : tw_f(ld_dev(pw + (size_t)i * TYP_WORDS + f));
+    return i == own ? s_own[f] : tw_f(ld_dev(pw + (size_t)i * TYP_WORDS + f));
   };
   // per row (lanes over rows): chunks in order
   for (int r = lane; r < rps; r += WAVE) {
@@ -267,17 +266,15 @@ __global__ __launch_bounds__(NT) void k_typical(const TypArgs ta) {
   const float best = m;
   const float words[TYP_WORDS] = {off, d_head(S), d_tail(S), d_head(M), d_tail(M), best,
                                    __uint_as_float((unsigned)bi), __uint_as_float((unsigned)fl)};
+  float v = words[0];  // lane f's word (constant indices: the array stays in registers)
+#pragma unroll
+  for (int f = 1; f < TYP_WORDS; ++f) v = (lane == f) ? words[f] : v;
   if (jr == a.rps - 1 && c == a.C - 1) {
-    typical_finish<T, TOPK>(ta, b, words, c);
+    typical_finish<T, TOPK>(ta, b, v, c);
     return;
   }
   u64 *pw = a.w.tw_part + ((size_t)r * a.C + c) * TYP_WORDS;
-  if (lane < TYP_WORDS) {
-    float v = words[0];
-#pragma unroll
-    for (int f = 1; f < TYP_WORDS; ++f) v = (lane == f) ? words[f] : v;
-    tw_putf(pw + lane, a.tag, v);
-  }
+  if (lane < TYP_WORDS) tw_putf(pw + lane, a.tag, v);
 }
 
 }  // namespace sv
