@@ -30,9 +30,9 @@ arrays into it.  The functions and the passages they follow:
   LK loss and DSpark's c* on the second page) and tv = sum [p - q]_+.
 
 Every function is pinned by tests in ``tests/test_oracle_*.py`` against values
-the pages print, closed forms, invariants and library routines.  One branch is
-**parity unpinned**: the fallback taken when a rejection's residual mass is
-exactly zero, which valid inputs reach only through rounding.
+the pages print, closed forms, invariants and library routines, including the
+fallback taken when a rejection's residual mass is exactly zero (rows that
+differ only at a token whose mass is lost in double precision reach it).
 """
 from __future__ import annotations
 

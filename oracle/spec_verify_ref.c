@@ -30,9 +30,11 @@
  *   R2 uniforms must lie in [0, 1)                                   ([WC] reference).
  *   R3 inverse CDF over half-open cumulative intervals in index order
  *      ([WY] step 1: a uniform picks the token whose cumulative interval holds it).
- *   R4 a rejection whose residual mass is exactly zero (reachable only through
- *      rounding) draws the correction from p_j itself ([WC] "正确性契约" asks for a
- *      stable fallback without fixing one).  Parity of this branch is unpinned.
+ *   R4 a rejection whose residual mass is exactly zero draws the correction from p_j
+ *      itself ([WC] "正确性契约" asks for a stable fallback without fixing one).  Valid
+ *      inputs reach it when p and q differ only at tokens whose mass is lost against the
+ *      partition in double precision (a logit of -460 drafted with -459): then p <= q
+ *      everywhere after rounding, and p restricted to the other tokens is the exact law.
  *   R5 top-k keeps every logit >= the k-th largest raw logit (ties kept), applied to
  *      target and draft alike, before temperature; k <= 0 or k >= V disables it.
  *   R6 temperature 0 is greedy: argmax with the lowest index on ties; draft logits and
@@ -633,7 +635,7 @@ int ref_tree_verify(const void *target, const void *draft, int dtype, const int3
           for (int v = 0; v < V; ++v) Z += fmax(cur[v] - Q[v], 0.0);
           if (Z > 0.0)
             for (int v = 0; v < V; ++v) cur[v] = fmax(cur[v] - Q[v], 0.0) / Z;
-          else /* reachable only through rounding: keep p_u (as R4) */
+          else /* zero mass (as R4): p_u is the current distribution again */
             for (int v = 0; v < V; ++v) cur[v] = P[v];
           ++rejected;
         }

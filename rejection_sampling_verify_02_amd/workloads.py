@@ -298,3 +298,31 @@ def make_tree(B: int, N: int, V: int, dtype: str, seed: int, *, max_children: in
         parents = np.stack([random_parents(rng, N, max_children) for _ in range(B)])
     parents = np.ascontiguousarray(np.broadcast_to(np.asarray(parents, np.int32), (B, N)))
     return TreeRaw(target, draft, parents, uniforms(rng, (B, N)), uniforms(rng, (B, N)), uniforms(rng, (B,)))
+
+
+# ---------------------------------------------------------------- degenerate residuals
+
+# A drafted token whose target logit sits far below the rest of the row (-460, so that
+# e^-460 is lost against the row's partition even in double precision) and whose draft
+# logit is larger by 1 (f32) or 2 (bf16: -459 is not a bf16 value): p(x) < q(x), and every
+# other token has the same logit in both rows.
+ZERO_RESIDUAL_LOGITS = {"f32": (-460.0, -459.0), "bf16": (-460.0, -458.0)}
+
+
+def make_zero_residual(B: int, G: int, V: int, dtype: str, seed: int, *, scale: float = 2.0) -> Raw:
+    """Calls whose draft rows equal their target rows except at the drafted token x of each
+    position, where the logits are ZERO_RESIDUAL_LOGITS[dtype].  Target rows differ between
+    positions (seeded 'scale * N(0, 1)' logits).  Tokens are fixed (fixed_tokens); every
+    u_accept is 0.9 and u_sample is U(0, 1)."""
+    rng = np.random.default_rng(seed)
+    zt = (scale * rng.standard_normal((B, G + 1, V))).astype(np.float32)
+    tok = rng.integers(0, V, (B, G)).astype(np.int32)
+    zd = zt[:, :G].copy()
+    lt, ld = ZERO_RESIDUAL_LOGITS[dtype]
+    bi, gi = np.meshgrid(np.arange(B), np.arange(G), indexing="ij")
+    zt[bi, gi, tok] = lt
+    zd[bi, gi, tok] = ld
+    cfg = Config(0, f"zero_residual_{B}x{G}x{V}_{dtype}", B, G, V, dtype, 1.0, 0, 0.0, seed)
+    ua = np.full((B, G), 0.9, np.float32)
+    return Raw(cfg, _store(zt, dtype), _store(zd, dtype), np.zeros((B, G), np.float32), ua,
+               uniforms(rng, (B,)), tok)

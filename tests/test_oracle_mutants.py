@@ -67,6 +67,14 @@ MUTANTS = [
      "for (int s = u + 1; s < N; ++s)\n            if (par[s] == u && x[s] == a) next = s;"),
     ("tree_uniform_index", "const double us = (double)u_accept[row0 + s];", "const double us = (double)u_accept[row0 + s - 1];"),
     ("tree_leaf_draft_checked", "if (!nchild[n]) continue;\n          load_row(draft", "load_row(draft"),
+    ("r4_no_fallback", "if (y < 0) y = ref_invcdf(P, V, (double)J->u_sample[b], &d); /* R4 */",
+     "/* no fallback */"),
+    ("r4_fallback_accept_uniform", "if (y < 0) y = ref_invcdf(P, V, (double)J->u_sample[b], &d); /* R4 */",
+     "if (y < 0) y = ref_invcdf(P, V, (double)J->u_accept[(size_t)b * G + i], &d);"),
+    ("tree_zero_residual_no_reset", "for (int v = 0; v < V; ++v) cur[v] = P[v];\n          ++rejected;",
+     "for (int v = 0; v < V; ++v) cur[v] = 0.0;\n          ++rejected;"),
+    ("tree_zero_residual_divides", "if (Z > 0.0)\n            for (int v = 0; v < V; ++v) cur[v] = fmax(cur[v] - Q[v], 0.0) / Z;",
+     "if (1)\n            for (int v = 0; v < V; ++v) cur[v] = fmax(cur[v] - Q[v], 0.0) / Z;"),
     ("typical_non_strict", "if (!(px > thr)) {", "if (!(px >= thr)) {"),
     ("typical_max_threshold", "const double thr = fmin(eps, delta * exp(-H));", "const double thr = fmax(eps, delta * exp(-H));"),
     ("typical_exp_sign", "const double thr = fmin(eps, delta * exp(-H));", "const double thr = fmin(eps, delta * exp(H));"),
@@ -95,6 +103,8 @@ PIN_TESTS = [
     lambda: pins.test_chain_structure("f32", 0.0, 0),
     lambda: pins.test_g_zero_is_plain_target_sampling(),
     lambda: pins.test_row_error_codes("u_one", oracle.ERR_UNIFORM),
+    lambda: pins.test_zero_residual_fallback_draws_from_p("f32"),
+    lambda: pins.test_zero_residual_fallback_draws_from_p("bf16"),
     lambda: stats.test_monte_carlo_law_matches_target(1.0, 0),
     lambda: stats.test_expected_tokens_constant_rate(0.6, 4),
     lambda: ovl.test_worked_examples(),
@@ -107,6 +117,7 @@ PIN_TESTS = [
     lambda: tree.test_second_sibling_is_tested_against_the_residual(),
     lambda: tree.test_third_sibling_threshold_and_final_draw(),
     lambda: tree.test_greedy_tree_walk(),
+    lambda: tree.test_zero_residual_resets_to_p("f32"),
     lambda: tree.test_tree_checks("nan_draft_leaf", 0),
     lambda: tree.test_monte_carlo_tree_law_matches_target((3,), 1.0, 0),
     lambda: typ.test_entropy_matches_scipy(1.0, 0),

@@ -408,3 +408,54 @@ def test_acceptance_boundary_is_inclusive():
     acc, out = oracle.spec_verify_ref(t, d, np.zeros((2, 1), np.int32), u, np.full(2, 0.3, np.float32), 1.0)
     assert acc.tolist() == [1, 0]
     assert out[1].tolist() == [1, -1]  # the residual [p - q]_+ = (0, 1/2) puts all mass on 1
+
+
+# ---------------------------------------------------------------- zero residual mass (R4)
+
+def _zero_residual_case(dtype, B=48, G=2, V=24, seed=31):
+    raw = wl.make_zero_residual(B, G, V, dtype, seed)
+    raw.u_accept[::2, 0] = 0.0  # even sequences accept position 0 and reject at position 1
+    raw.u_sample[:] = grid(B)
+    return raw
+
+
+def _as_f64(stored):
+    return (wl.bf16_to_f32(stored) if stored.dtype == np.uint16 else stored).astype(np.float64)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_zero_residual_fallback_draws_from_p(dtype):
+    """R4 (the fallback that "推测解码：接受规则、状态与收益边界", section 正确性契约, asks for
+    when the residual degenerates).  Target and draft rows are identical except at the
+    drafted token x, where the target logit is -460 and the draft's larger by 1 (f32) or 2
+    (bf16).  In double precision e^-460 is lost against the row's partition, so p(v) ==
+    q(v) for every v != x and p(x) < q(x): [p - q]_+ sums to exactly zero (checked with
+    SciPy's softmax, independently of the oracle).  alpha = e^-1 (e^-2) rejects u = 0.9,
+    accepts u = 0, and the correction is the draw from p_j by inverse CDF:
+    searchsorted(cumsum P, u * sum P, 'right')."""
+    raw = _zero_residual_case(dtype)
+    B, G = raw.B, raw.G
+    zt, zd = _as_f64(raw.target), _as_f64(raw.draft)
+    P = scipy.special.softmax(zt, axis=-1)
+    Q = scipy.special.softmax(zd, axis=-1)
+    assert np.all(np.maximum(P[:, :G] - Q, 0.0).sum(axis=-1) == 0.0)
+    acc, out, diag = oracle.spec_verify_ref(raw.target, raw.draft, raw.fixed_tokens, raw.u_accept,
+                                            raw.u_sample, 1.0, 0, with_diagnostics=True)
+    j_expect = np.where(np.arange(B) % 2 == 0, 1, 0)
+    np.testing.assert_array_equal(acc, j_expect)
+    gap = 1.0 if dtype == "f32" else 2.0
+    b_idx = np.arange(B)
+    np.testing.assert_allclose(raw.u_accept[b_idx, j_expect] - diag["accept_margin"][b_idx, j_expect],
+                               np.exp(-gap), rtol=0, atol=1e-12)
+    checked = 0
+    for b in range(B):
+        j = j_expect[b]
+        F = np.cumsum(P[b, j])
+        t = float(raw.u_sample[b]) * F[-1]
+        y = int(np.searchsorted(F, t, side="right"))
+        assert np.array_equal(out[b, :j], raw.fixed_tokens[b, :j])
+        assert np.all(out[b, j + 1:] == -1)
+        if min(abs(F - t)) > 1e-12:
+            assert out[b, j] == y, (b, j, out[b], y)
+            checked += 1
+    assert checked >= B - 2
