@@ -166,25 +166,22 @@ def counters_traffic(op: str):
 
 
 def cpu_baseline(host_sets, cfg, seconds: float):
-    """The oracle (fp64, unmodified) on the host cores over whole input sets, for a bounded
-    wall time; its value is verified positions per second like the GPU's."""
+    """The oracle on the host over whole input sets, in verified positions per second."""
     import oracle
 
     oracle._load()
-    threads = oracle.default_threads()
-    calls, t0 = 0, time.perf_counter()
-    while True:
-        h = host_sets[calls % len(host_sets)]
+    B, G = host_sets[0]["tokens"].shape
+    state = {"i": 0}
+
+    def once(threads):
+        h = host_sets[state["i"] % len(host_sets)]
+        state["i"] += 1
         oracle.spec_verify_ref(h["target"], h["draft"], h["tokens"], h["u_accept"], h["u_sample"],
                                cfg.temperature, cfg.top_k, nthreads=threads)
-        calls += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    B, G = host_sets[0]["tokens"].shape
-    return {"value": B * G * calls / el, "unit": "positions/s", "cores": threads, "kind": "oracle",
-            "sample": f"{calls} full calls (B={B}, G={G}) over {min(calls, len(host_sets))} input sets, "
-                      f"{el:.1f} s; the oracle stops reading each sequence at its first rejection"}
+
+    return oracle_baseline(once, B * G, "positions/s", seconds,
+                           f"full calls (B={B}, G={G}) over {len(host_sets)} input sets; the oracle stops "
+                           f"reading each sequence at its first rejection")
 
 
 def summarize_counters(kdir: str, cdir: str, op: str) -> None:
@@ -240,6 +237,84 @@ def summarize_counters(kdir: str, cdir: str, op: str) -> None:
     print(json.dumps(res))
 
 
+def _last_line(path: str):
+    line = None
+    for ln in open(path):
+        ln = ln.strip()
+        if ln.startswith("{"):
+            line = json.loads(ln)
+    return line
+
+
+def summarize_trace(tdir: str, line_file: str, cmd: str, ref_file: str | None = None) -> None:
+    """Write the kernel-trace summary of one profiled benchmark run: rocprofv3's own
+    per-dispatch durations (kernel_trace.csv) for the dispatches of the workload's main
+    kernel, split into the benchmark's phases in launch order (the line's "dispatches"
+    field), next to the line's own HIP-event figures from the same run."""
+    import csv
+    import glob
+
+    line = _last_line(line_file)
+    rows = []
+    for f in glob.glob(os.path.join(tdir, "**", "*kernel_trace.csv"), recursive=True):
+        rows += list(csv.DictReader(open(f)))
+    rf = line["roofline"]
+    kernel = rf["kernel"]
+
+    def grid(r):
+        return int(r.get("Grid_Size") or r.get("Grid_Size_X") or 0)
+
+    mine = [r for r in rows if f"{kernel}<" in r["Kernel_Name"] or r["Kernel_Name"].endswith(kernel)]
+    grids = [grid(r) for r in mine]
+    main = max(set(grids), key=grids.count)
+    d = sorted((r for r in mine if grid(r) == main), key=lambda r: int(r["Start_Timestamp"]))
+    us = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in d]
+    ph = line["dispatches"]
+    spans, o = [], 0
+    for name in ("warmup", "timed_loops", "per_kernel_events", "flushed", "after"):
+        n = ph.get(name, 0)
+        spans.append((name, us[o:o + n]))
+        o += n
+    alg = rf["algorithmic_bytes"]
+    out = [f"# Kernel trace: {kernel}, {line['config']['workload']}", "",
+           "Command (repository root on the GPU box, after `cd /tmp && export TMPDIR=/tmp`):", "",
+           "```", cmd, "```", "",
+           f"Dispatches of `{kernel}` on the workload's grid ({main} threads), in launch order, split into",
+           "the benchmark's phases; durations from rocprofv3's kernel trace of the same run.", "",
+           "| phase | dispatches | mean (us) | median (us) | min (us) | GB/s at the mean | of 8 TB/s |",
+           "|---|---|---|---|---|---|---|"]
+    for name, v in spans:
+        if not v:
+            continue
+        m = float(np.mean(v))
+        out.append(f"| {name} | {len(v)} | {m:.3f} | {np.median(v):.3f} | {np.min(v):.3f} | "
+                   f"{alg / m / 1e3:.1f} | {alg / m / 1e3 / PEAK_HBM_GBS:.4f} |")
+    ev = dict(spans).get("per_kernel_events", [])
+    out += ["", f"The profiled run's own line: `{kernel}` {rf['avg_launch_us']} us from bench.py's per-dispatch HIP "
+            f"events (under the profiler the events are recorded late, so they read long), event-free loop "
+            f"{line['ms_per_step'] * 1e3:.2f} us per call ({line['value'] / 1e6:.3f} M {line['unit']})."]
+    if ev:
+        m = float(np.mean(ev))
+        out.append(f"rocprofv3 over the per-kernel-event dispatches: {m:.3f} us, frac {alg / m / 1e3 / PEAK_HBM_GBS:.4f}.")
+        if ref_file:
+            ref = _last_line(ref_file)
+            rr = ref["roofline"]
+            out.append(f"The same command without the profiler, on the same box: `{kernel}` {rr['avg_launch_us']} us from "
+                       f"the events, frac {rr['frac']} ({(m / rr['avg_launch_us'] - 1) * 100:+.2f}% from rocprofv3's "
+                       f"{m:.3f} us); event-free loop {ref['ms_per_step'] * 1e3:.2f} us per call "
+                       f"({ref['value'] / 1e6:.3f} M {ref['unit']}).")
+    src = _last_line(ref_file) if ref_file else line
+    if src.get("read_probe"):
+        pr = src["read_probe"]
+        out.append(f"Streaming-read probe ({'the run without the profiler' if ref_file else 'the same run'}): "
+                   f"{pr['GBs']} GB/s ({pr['frac_of_peak']} of 8 TB/s) over {pr['bytes_per_launch']:,} bytes per "
+                   f"launch; {kernel} reaches {src['roofline'].get('frac_of_read_probe')} of it.")
+    out.append("")
+    path = ROOT / "profiles" / f"{kernel}_{line['config']['workload']}_kernel_trace.md"
+    path.write_text("\n".join(out))
+    print(path)
+
+
 def copy_probe(nbytes: int, reps: int) -> None:
     """A plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
     import torch
@@ -251,29 +326,37 @@ def copy_probe(nbytes: int, reps: int) -> None:
     print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}))
 
 
-def time_loop(call, plan, K, warmup, stream, dev, hev, stage_events):
-    """Warm-up, then K calls timed as a caller runs them (wall clock and stream events),
-    then (unless disabled) the same K calls with a (start, stop) event pair on every kernel
-    dispatch.  Returns (wall_s, gpu_ms, per_kernel_us, wall2_s)."""
+LOOPS = 5  # timed loops of K calls; the reported time is their median
+
+
+def time_loop(call, plan, K, warmup, stream, dev, hev, stage_events, flush_calls=0):
+    """Warm-up, then LOOPS loops of K calls each, timed as a caller runs them (wall clock
+    and stream events; the median loop gives the throughput), then (unless disabled) K calls
+    with a (start, stop) event pair on every kernel dispatch, then flush_calls single calls
+    each after writing a 1 GiB scratch buffer (cold caches).  Returns a dict."""
     import torch
     for i in range(warmup):
         call(i)
     torch.cuda.synchronize(dev)
     log(f"[bench] warmup done ({warmup} calls)")
-    loop_ev = hev.create(2)
-    torch.cuda.synchronize(dev)
-    t0 = time.perf_counter()
-    hev.record(loop_ev[0], stream)
-    for i in range(K):
-        call(warmup + i)
-    hev.record(loop_ev[1], stream)
-    torch.cuda.synchronize(dev)
-    wall = time.perf_counter() - t0
-    gpu_ms = hev.elapsed_ms(loop_ev[0], loop_ev[1])
-    hev.destroy(loop_ev)
-    log(f"[bench] timed {K} calls: wall {wall * 1e3:.2f} ms, events {gpu_ms:.2f} ms")
+    walls, gpus = [], []
+    n = warmup
+    for lp in range(LOOPS):
+        loop_ev = hev.create(2)
+        torch.cuda.synchronize(dev)
+        t0 = time.perf_counter()
+        hev.record(loop_ev[0], stream)
+        for i in range(K):
+            call(n + i)
+        hev.record(loop_ev[1], stream)
+        torch.cuda.synchronize(dev)
+        walls.append(time.perf_counter() - t0)
+        gpus.append(hev.elapsed_ms(loop_ev[0], loop_ev[1]))
+        hev.destroy(loop_ev)
+        n += K
+    log(f"[bench] {LOOPS} timed loops of {K} calls: wall " + ", ".join(f"{w * 1e3:.3f}" for w in walls) + " ms")
     # The per-dispatch event pairs add a few microseconds of gap between kernels, so the
-    # first loop gives the throughput and this one each kernel's own duration.
+    # loops above give the throughput and this one each kernel's own duration.
     per_kernel, wall2 = {}, None
     if stage_events:
         nl = len(plan)
@@ -281,7 +364,7 @@ def time_loop(call, plan, K, warmup, stream, dev, hev, stage_events):
         torch.cuda.synchronize(dev)
         t1 = time.perf_counter()
         for i in range(K):
-            call(warmup + i, stage[i])
+            call(n + i, stage[i])
         torch.cuda.synchronize(dev)
         wall2 = time.perf_counter() - t1
         durs = np.array([[hev.elapsed_ms(ev[2 * j], ev[2 * j + 1]) for j in range(nl)] for ev in stage])
@@ -289,8 +372,119 @@ def time_loop(call, plan, K, warmup, stream, dev, hev, stage_events):
             per_kernel[f"{j}:{name}"] = float(np.mean(durs[:, j]) * 1e3)
         for ev in stage:
             hev.destroy(ev)
+        n += K
         log(f"[bench] timed {K} calls with per-kernel events: wall {wall2 * 1e3:.2f} ms")
-    return wall, gpu_ms, per_kernel, wall2
+    cold = []
+    if flush_calls:
+        scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+        ev = hev.create(2)
+        for i in range(flush_calls):
+            scratch.fill_(float(i))
+            torch.cuda.synchronize(dev)
+            hev.record(ev[0], stream)
+            call(n + i)
+            hev.record(ev[1], stream)
+            cold.append(hev.elapsed_ms(ev[0], ev[1]) * 1e3)
+        hev.destroy(ev)
+        del scratch
+        torch.cuda.synchronize(dev)
+        n += flush_calls
+        log(f"[bench] {flush_calls} single calls after a 1 GiB flush: median {np.median(cold):.2f} us")
+    med = int(np.argsort(walls)[len(walls) // 2])
+    return {"wall": walls[med], "gpu_ms": gpus[med], "walls": walls, "per_kernel": per_kernel,
+            "wall2": wall2, "cold_us": cold, "calls": n}
+
+
+def timing_fields(t, K):
+    """The timing part of a result line: median loop, all loops, per-kernel durations, flushed latency."""
+    return {
+        "timed_loops_ms": [round(w * 1e3, 4) for w in t["walls"]],
+        "gpu_event_ms_per_step": round(t["gpu_ms"] / K, 5),
+        "per_kernel_us": {k: round(v, 3) for k, v in t["per_kernel"].items()},
+        "ms_per_step_with_kernel_events": None if t["wall2"] is None else round(t["wall2"] * 1e3 / K, 5),
+        "single_call_after_flush_us": None if not t["cold_us"] else {
+            "median": round(float(np.median(t["cold_us"])), 3), "min": round(float(np.min(t["cold_us"])), 3),
+            "calls": len(t["cold_us"]), "flush": "1 GiB written before each call"},
+    }
+
+
+def read_probe(nbytes: int, n_sets: int, K: int, dev, hev):
+    """The plain streaming-read probe (sv_read_probe) over n_sets buffers of nbytes each,
+    rotated like the workload's input sets: mean kernel duration from per-dispatch events,
+    and a checksum of one buffer against torch's sum of its words."""
+    import torch
+    import rejection_sampling_verify_02_amd as sv
+    chunk = 32768
+    nb = nbytes // chunk * chunk
+    bufs = [torch.randint(-2 ** 31, 2 ** 31 - 1, (nb // 4,), dtype=torch.int32, device=dev) for _ in range(n_sets)]
+    out = torch.empty((nb // chunk,), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    sv.read_probe(bufs[0], out, stream=stream)
+    got = int(out.to(torch.int64).sum().item()) % (1 << 32)
+    want = int(bufs[0].to(torch.int64).sum().item()) % (1 << 32)
+    if got != want:
+        raise RuntimeError(f"read probe checksum {got:#x} != {want:#x}")
+    for i in range(10):
+        sv.read_probe(bufs[i % n_sets], out, stream=stream)
+    evs = [hev.create(2) for _ in range(K)]
+    torch.cuda.synchronize(dev)
+    for i in range(K):
+        hev.record(evs[i][0], stream)
+        sv.read_probe(bufs[i % n_sets], out, stream=stream)
+        hev.record(evs[i][1], stream)
+    torch.cuda.synchronize(dev)
+    us = np.array([hev.elapsed_ms(a, b) * 1e3 for a, b in evs])
+    for e in evs:
+        hev.destroy(e)
+    del bufs
+    gbs = nb / (float(np.mean(us)) * 1e-6) / 1e9
+    log(f"[bench] read probe: {nb / 1e6:.2f} MB per launch, {np.mean(us):.3f} us -> {gbs:.1f} GB/s")
+    return {"kernel": "k_read_probe", "bytes_per_launch": nb, "avg_launch_us": round(float(np.mean(us)), 3),
+            "median_launch_us": round(float(np.median(us)), 3), "GBs": round(gbs, 1),
+            "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4), "launches": K, "buffers": n_sets}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_baseline(run_once, units_per_call: float, unit: str, seconds: float, sample: str):
+    """The oracle as committed (fp64, unmodified), timed on the host: on every core in this
+    process's affinity set and on one core, each as the median of 3 runs of about
+    seconds / 6 (at least one call each).  run_once(nthreads) makes one full call."""
+    try:
+        all_cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        all_cores = os.cpu_count() or 1
+    per_run = max(seconds / 6.0, 1e-3)
+
+    def rate(threads):
+        rates, calls_total = [], 0
+        for _ in range(3):
+            calls, t0 = 0, time.perf_counter()
+            while True:
+                run_once(threads)
+                calls += 1
+                el = time.perf_counter() - t0
+                if el >= per_run:
+                    break
+            rates.append(units_per_call * calls / el)
+            calls_total += calls
+        return float(np.median(rates)), calls_total
+
+    v_all, c_all = rate(all_cores)
+    v_one, c_one = rate(1)
+    return {"value": v_all, "unit": unit, "cores": all_cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": f"{sample}; median of 3 runs of ~{per_run:.1f} s ({c_all} calls) on {all_cores} threads",
+            "one_core": {"value": v_one, "unit": unit, "cores": 1,
+                         "sample": f"median of 3 runs of ~{per_run:.1f} s ({c_one} calls) on 1 thread"}}
 
 
 def roofline(per_kernel, kernel, alg_bytes, traffic):
@@ -339,8 +533,8 @@ def run_verify(args, dev, hev):
                               out=(acc, out), events=events)
 
     K = args.steps
-    wall, gpu_ms, per_kernel, wall2 = time_loop(call, plan, K, args.warmup, stream, dev, hev,
-                                                not args.no_stage_events)
+    t = time_loop(call, plan, K, args.warmup, stream, dev, hev, not args.no_stage_events, args.flush_calls)
+    wall, per_kernel = t["wall"], t["per_kernel"]
     # emitted tokens for the last call of each set (accepted + 1 per valid sequence)
     emitted = torch.zeros((), dtype=torch.int64, device=dev)
     for s_i in range(min(n_sets, K)):
@@ -366,12 +560,17 @@ def run_verify(args, dev, hev):
         "call_frac_of_peak": round(alg_bytes / t_call / 1e9 / PEAK_HBM_GBS, 4),
         "emitted_tokens_per_s": round(mean_emitted / t_call, 1),
         "mean_accepted_plus_one": round(mean_emitted / B, 4),
-        "gpu_event_ms_per_step": round(gpu_ms / K, 5),
-        "per_kernel_us": {k: round(v, 3) for k, v in per_kernel.items()},
-        "ms_per_step_with_kernel_events": None if wall2 is None else round(wall2 * 1e3 / K, 5),
+        **timing_fields(t, K),
         "roofline": roofline(per_kernel, kernel, alg_bytes, traffic),
         "traffic_note": tnote,
+        "dispatches": {"warmup": args.warmup, "timed_loops": LOOPS * K, "per_kernel_events": K if per_kernel else 0,
+                       "flushed": len(t["cold_us"]), "after": min(n_sets, K)},
     }
+    if not args.no_probe:
+        probe = read_probe(alg_bytes, n_sets, K, dev, hev)
+        res["read_probe"] = probe
+        if res["roofline"]:
+            res["roofline"]["frac_of_read_probe"] = round(res["roofline"]["achieved"] / probe["GBs"], 4)
     if not args.no_cpu_baseline:
         log(f"[bench] oracle CPU baseline (~{args.cpu_seconds:.0f} s)")
         res["cpu_baseline"] = cpu_baseline(host, cfg, args.cpu_seconds)
@@ -412,8 +611,8 @@ def run_sample(args, dev, hev):
                               out=(tok, st), events=events)
 
     K = args.steps
-    wall, gpu_ms, per_kernel, wall2 = time_loop(call, plan, K, args.warmup, stream, dev, hev,
-                                                not args.no_stage_events)
+    t = time_loop(call, plan, K, args.warmup, stream, dev, hev, not args.no_stage_events, args.flush_calls)
+    wall, per_kernel = t["wall"], t["per_kernel"]
     t_call = wall / K
     res = {
         "metric": "sampled tokens/sec and achieved HBM GB/s (% of peak), one draw per row",
@@ -424,26 +623,21 @@ def run_sample(args, dev, hev):
                    "top_k": cfg.top_k, "input_sets": n_sets, "set_bytes": alg_bytes},
         "call_GBs": round(alg_bytes / t_call / 1e9, 1),
         "call_frac_of_peak": round(alg_bytes / t_call / 1e9 / PEAK_HBM_GBS, 4),
-        "gpu_event_ms_per_step": round(gpu_ms / K, 5),
-        "per_kernel_us": {k: round(v, 3) for k, v in per_kernel.items()},
-        "ms_per_step_with_kernel_events": None if wall2 is None else round(wall2 * 1e3 / K, 5),
+        **timing_fields(t, K),
         "roofline": roofline(per_kernel, KERNEL, alg_bytes, counters_traffic("sample")[0]),
     }
     if not args.no_cpu_baseline:
         import oracle
         oracle._load()
-        threads = oracle.default_threads()
-        calls, t0 = 0, time.perf_counter()
-        while True:
-            z, u = host[calls % len(host)]
+        st = {"i": 0}
+
+        def once(threads):
+            z, u = host[st["i"] % len(host)]
+            st["i"] += 1
             oracle.sample_rows(z, u, cfg.temperature, cfg.top_k, nthreads=threads)
-            calls += 1
-            el = time.perf_counter() - t0
-            if el >= args.cpu_seconds:
-                break
-        res["cpu_baseline"] = {"value": B * calls / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-                               "sample": f"{calls} full calls (B={B}, V={V}) over {min(calls, len(host))} "
-                                         f"input sets, {el:.1f} s"}
+
+        res["cpu_baseline"] = oracle_baseline(once, B, "tokens/s", args.cpu_seconds,
+                                              f"full calls (B={B}, V={V}) over {len(host)} input sets")
     else:
         res["cpu_baseline"] = None
     return res
@@ -485,8 +679,8 @@ def run_overlap(args, dev, hev):
                                events=events)
 
     K = args.steps
-    wall, gpu_ms, per_kernel, wall2 = time_loop(call, plan, K, args.warmup, stream, dev, hev,
-                                                not args.no_stage_events)
+    t = time_loop(call, plan, K, args.warmup, stream, dev, hev, not args.no_stage_events, args.flush_calls)
+    wall, per_kernel = t["wall"], t["per_kernel"]
     t_call = wall / K
     res = {
         "metric": "overlap (beta, tv) positions/sec and achieved HBM GB/s (% of peak) at B=64,V=128k",
@@ -499,25 +693,20 @@ def run_overlap(args, dev, hev):
         "call_GBs": round(alg_bytes / t_call / 1e9, 1),
         "call_frac_of_peak": round(alg_bytes / t_call / 1e9 / PEAK_HBM_GBS, 4),
         "mean_beta": round(float(outs[0].mean().item()), 5),
-        "gpu_event_ms_per_step": round(gpu_ms / K, 5),
-        "per_kernel_us": {k: round(v, 3) for k, v in per_kernel.items()},
-        "ms_per_step_with_kernel_events": None if wall2 is None else round(wall2 * 1e3 / K, 5),
+        **timing_fields(t, K),
         "roofline": roofline(per_kernel, "k_overlap", alg_bytes, counters_traffic("overlap")[0]),
     }
     if not args.no_cpu_baseline:
         oracle._load()
-        threads = oracle.default_threads()
-        calls, t0 = 0, time.perf_counter()
-        while True:
-            t, d = host[calls % len(host)]
-            oracle.overlap(t, d, cfg.temperature, cfg.top_k, nthreads=threads)
-            calls += 1
-            el = time.perf_counter() - t0
-            if el >= args.cpu_seconds:
-                break
-        res["cpu_baseline"] = {"value": B * G * calls / el, "unit": "positions/s", "cores": threads,
-                               "kind": "oracle", "sample": f"{calls} full calls (B={B}, G={G}, V={V}) over "
-                                                           f"{min(calls, len(host))} input sets, {el:.1f} s"}
+        st = {"i": 0}
+
+        def once(threads):
+            t_, d_ = host[st["i"] % len(host)]
+            st["i"] += 1
+            oracle.overlap(t_, d_, cfg.temperature, cfg.top_k, nthreads=threads)
+
+        res["cpu_baseline"] = oracle_baseline(once, B * G, "positions/s", args.cpu_seconds,
+                                              f"full calls (B={B}, G={G}, V={V}) over {len(host)} input sets")
     else:
         res["cpu_baseline"] = None
     return res
@@ -567,8 +756,8 @@ def run_tree(args, dev, hev):
                                    workspace=ws, stream=stream, out=outs, events=events)
 
     K = args.steps
-    wall, gpu_ms, per_kernel, wall2 = time_loop(call, plan, K, args.warmup, stream, dev, hev,
-                                                not args.no_stage_events)
+    t = time_loop(call, plan, K, args.warmup, stream, dev, hev, not args.no_stage_events, args.flush_calls)
+    wall, per_kernel = t["wall"], t["per_kernel"]
     t_call = wall / K
     depth = []
     for i in range(n_sets):
@@ -586,27 +775,22 @@ def run_tree(args, dev, hev):
         "call_frac_of_peak": round(alg_bytes / t_call / 1e9 / PEAK_HBM_GBS, 4),
         "emitted_tokens_per_s": round(B * (float(np.mean(depth)) + 1) / t_call, 1),
         "mean_accepted_depth": round(float(np.mean(depth)), 4),
-        "gpu_event_ms_per_step": round(gpu_ms / K, 5),
-        "per_kernel_us": {k: round(v, 3) for k, v in per_kernel.items()},
-        "ms_per_step_with_kernel_events": None if wall2 is None else round(wall2 * 1e3 / K, 5),
+        **timing_fields(t, K),
         "roofline": roofline(per_kernel, "k_tree_rows", alg_bytes, counters_traffic("tree")[0]),
     }
     if not args.no_cpu_baseline:
         import oracle
         oracle._load()
-        threads = oracle.default_threads()
-        calls, t0 = 0, time.perf_counter()
-        while True:
-            raw, tok = host[calls % len(host)]
+        st = {"i": 0}
+
+        def once(threads):
+            raw, tok = host[st["i"] % len(host)]
+            st["i"] += 1
             oracle.tree_verify(raw.target, raw.draft, tok, raw.parent, raw.u_accept, raw.u_sample,
                                cfg.temperature, cfg.top_k, nthreads=threads)
-            calls += 1
-            el = time.perf_counter() - t0
-            if el >= args.cpu_seconds:
-                break
-        res["cpu_baseline"] = {"value": B * (N - 1) * calls / el, "unit": "nodes/s", "cores": threads,
-                               "kind": "oracle", "sample": f"{calls} full calls (B={B}, N={N}, V={V}) over "
-                                                           f"{min(calls, len(host))} input sets, {el:.1f} s"}
+
+        res["cpu_baseline"] = oracle_baseline(once, B * (N - 1), "nodes/s", args.cpu_seconds,
+                                              f"full calls (B={B}, N={N}, V={V}) over {len(host)} input sets")
     else:
         res["cpu_baseline"] = None
     return res
@@ -639,8 +823,8 @@ def run_typical(args, dev, hev):
                                       workspace=ws, stream=stream, out=outs, events=events)
 
     K = args.steps
-    wall, gpu_ms, per_kernel, wall2 = time_loop(call, plan, K, args.warmup, stream, dev, hev,
-                                                not args.no_stage_events)
+    t = time_loop(call, plan, K, args.warmup, stream, dev, hev, not args.no_stage_events, args.flush_calls)
+    wall, per_kernel = t["wall"], t["per_kernel"]
     t_call = wall / K
     acc = []
     for i in range(min(n_sets, 8)):
@@ -657,26 +841,21 @@ def run_typical(args, dev, hev):
         "call_GBs": round(alg_bytes / t_call / 1e9, 1),
         "call_frac_of_peak": round(alg_bytes / t_call / 1e9 / PEAK_HBM_GBS, 4),
         "mean_accepted": round(float(np.mean(acc)), 4),
-        "gpu_event_ms_per_step": round(gpu_ms / K, 5),
-        "per_kernel_us": {k: round(v, 3) for k, v in per_kernel.items()},
-        "ms_per_step_with_kernel_events": None if wall2 is None else round(wall2 * 1e3 / K, 5),
+        **timing_fields(t, K),
         "roofline": roofline(per_kernel, "k_typical", alg_bytes, counters_traffic("typical")[0]),
     }
     if not args.no_cpu_baseline:
         import oracle
         oracle._load()
-        threads = oracle.default_threads()
-        calls, t0 = 0, time.perf_counter()
-        while True:
-            h = host[calls % len(host)]
+        st = {"i": 0}
+
+        def once(threads):
+            h = host[st["i"] % len(host)]
+            st["i"] += 1
             oracle.typical_verify(h["target"], h["tokens"], cfg.temperature, eps, delta, cfg.top_k, nthreads=threads)
-            calls += 1
-            el = time.perf_counter() - t0
-            if el >= args.cpu_seconds:
-                break
-        res["cpu_baseline"] = {"value": B * G * calls / el, "unit": "positions/s", "cores": threads,
-                               "kind": "oracle", "sample": f"{calls} full calls (B={B}, G={G}, V={V}) over "
-                                                           f"{min(calls, len(host))} input sets, {el:.1f} s"}
+
+        res["cpu_baseline"] = oracle_baseline(once, B * G, "positions/s", args.cpu_seconds,
+                                              f"full calls (B={B}, G={G}, V={V}) over {len(host)} input sets")
     else:
         res["cpu_baseline"] = None
     return res
@@ -694,14 +873,23 @@ def main() -> int:
                     help="verification workload (3, the default, is the headline; 4 greedy and 5 top-k "
                          "are timed for the design notes)")
     ap.add_argument("--sets", type=int, default=0, help="input sets to rotate (default: >= 1 GiB)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="wall time of the oracle baseline (half on every core, half on one core)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe", action="store_true", help="skip the streaming-read probe")
+    ap.add_argument("--flush-calls", type=int, default=20,
+                    help="single calls timed after a 1 GiB flush each (0: none)")
     ap.add_argument("--no-stage-events", action="store_true",
                     help="time the loop without per-kernel events")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES (counter calibration)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("BENCH_DIR", "COPY_DIR"),
                     help="write the traffic summary of --op from rocprofv3 --pmc CSV directories")
+    ap.add_argument("--summarize-trace", nargs=3, metavar=("TRACE_DIR", "LINE_FILE", "COMMAND"),
+                    help="write the kernel-trace summary of a rocprofv3 --kernel-trace run of this "
+                         "script (its output line in LINE_FILE; COMMAND is quoted in the summary)")
+    ap.add_argument("--trace-reference", metavar="LINE_FILE",
+                    help="with --summarize-trace: the line of the same command run without the profiler")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -713,6 +901,9 @@ def main() -> int:
         return 0
     if args.summarize_counters:
         summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.op)
+        return 0
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace, ref_file=args.trace_reference)
         return 0
 
     import torch

@@ -88,6 +88,15 @@ size_t sv_workspace_bytes(int32_t B, int32_t G, int32_t V, sv_dtype dtype, float
 size_t sv_workspace_zero_bytes(int32_t B, int32_t G, int32_t V, sv_dtype dtype,
                                float temperature, int32_t top_k);
 
+/* Tag epoch: the process's kernel launches counted in units of 2^31.  Each launch marks
+ * its words with a 32-bit tag taken from that count, and a tag value comes back after
+ * 2^32 - 1 launches: a workspace word last written exactly that many launches earlier
+ * would then pass for the current launch's.  A caller that keeps a workspace across
+ * calls records this value whenever it zeroes the workspace's prefix, and zeroes the
+ * prefix again (all of it ever used) before the first call after the value changed.
+ * That happens once every 2^31 launches; no call is refused. */
+uint32_t sv_tag_epoch(void);
+
 /* Batched verification.
  *   target_logits [B, G+1, V] dtype   target logits for positions 1..G+1
  *   draft_logits  [B, G,   V] dtype   draft logits for positions 1..G; not read (may be

@@ -33,7 +33,8 @@ EXPORTED = ("spec_verify", "spec_verify_timed", "sv_workspace_bytes", "sv_worksp
             "spec_tree_verify", "spec_tree_verify_timed", "sv_tree_workspace_bytes",
             "sv_tree_workspace_zero_bytes", "sv_tree_launch_plan",
             "spec_typical_verify", "spec_typical_verify_timed", "sv_typical_workspace_bytes",
-            "sv_typical_workspace_zero_bytes", "sv_typical_launch_plan")
+            "sv_typical_workspace_zero_bytes", "sv_typical_launch_plan", "sv_tag_epoch",
+            "sv_read_probe")
 
 
 class SpecVerifyError(RuntimeError):
@@ -99,6 +100,10 @@ def load_library(path: Path | str | None = None) -> ctypes.CDLL:
     lib.sv_workspace_bytes.restype = SZ
     lib.sv_workspace_zero_bytes.argtypes = [I32, I32, I32, I32, F32, I32]
     lib.sv_workspace_zero_bytes.restype = SZ
+    lib.sv_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    lib.sv_read_probe.restype = I32
+    lib.sv_tag_epoch.argtypes = []
+    lib.sv_tag_epoch.restype = ctypes.c_uint32
     lib.sv_status_string.argtypes = [I32]
     lib.sv_status_string.restype = ctypes.c_char_p
     lib.sv_launch_plan.argtypes = [I32, I32, I32, I32, F32, I32]
@@ -158,16 +163,30 @@ class Workspace:
     def __init__(self):
         self._buf = {}
         self._zero = {}
+        self._used = {}   # the longest prefix any call has marked since the last full zeroing
+        self._epoch = {}
 
     def get(self, nbytes: int, zero_bytes: int, device, stream: int):
         import torch
         key = torch.device(device).index
         buf = self._buf.get(key)
+        epoch = int(load_library().sv_tag_epoch())
         if buf is None or buf.numel() < nbytes:
             buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
             torch.cuda.synchronize(device)
             self._buf[key] = buf
             self._zero[key] = buf.numel()
+            self._used[key] = 0
+            self._epoch[key] = epoch
+        if epoch != self._epoch[key]:
+            # the launch count passed a multiple of 2^31: tags of calls made before it may
+            # come back, so every word a call has marked is cleared
+            n = max(self._used[key], zero_bytes)
+            with torch.cuda.stream(torch.cuda.ExternalStream(stream, device=device)):
+                buf[:n].zero_()
+            self._zero[key] = n
+            self._used[key] = 0
+            self._epoch[key] = epoch
         if zero_bytes > self._zero[key]:
             with torch.cuda.stream(torch.cuda.ExternalStream(stream, device=device)):
                 buf[:zero_bytes].zero_()
@@ -177,7 +196,9 @@ class Workspace:
     def called(self, device, zero_bytes: int) -> None:
         """Record that a call with this zero prefix was enqueued."""
         import torch
-        self._zero[torch.device(device).index] = zero_bytes
+        key = torch.device(device).index
+        self._zero[key] = zero_bytes
+        self._used[key] = max(self._used.get(key, 0), zero_bytes)
 
 
 _default_ws = Workspace()
@@ -474,3 +495,21 @@ def spec_typical_verify(target_logits, draft_tokens, temperature: float, epsilon
         raise SpecVerifyError(rc, sv_status_string(rc))
     wso.called(dev, zbytes)
     return (acc, toks) if events is None else (acc, toks, nl)
+
+
+def read_probe(buf, out=None, *, stream: int | None = None):
+    """The streaming-read probe (a measurement aid, not part of the method): reads every
+    byte of the contiguous device tensor ``buf`` (a whole number of 32 KiB chunks) once and
+    returns the per-chunk wrapping sums of its 32-bit words (uint32 values in an int32
+    tensor of buf.nbytes // 32768 elements)."""
+    import torch
+    lib = load_library()
+    n = buf.numel() * buf.element_size()
+    if out is None:
+        out = torch.empty((n // 32768,), dtype=torch.int32, device=buf.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(buf.device).cuda_stream
+    rc = lib.sv_read_probe(_ptr(buf), n, _ptr(out), ctypes.c_void_p(stream))
+    if rc != 0:
+        raise SpecVerifyError(rc, "sv_read_probe refused its arguments" if rc != 7 else "kernel launch failed")
+    return out

@@ -321,7 +321,9 @@ __global__ __launch_bounds__(NT) void k_tree_resid(const TreeArgs t) {
       }
     }
     __syncthreads();
-    cj += s_z;  // c_{j+1} = c_j + Z_j
+    // c_{j+1} = c_j + Z_j; a zero mass makes p the current distribution again, whose
+    // next residual is [p - q]_+ (c = 1)
+    cj = (s_z > 0.0) ? cj + s_z : 1.0;
   }
 }
 
@@ -453,6 +455,8 @@ __global__ __launch_bounds__(WAVE) void k_tree_walk(const TreeArgs t) {
       const float tau_t = s_tau[u];
       const double *zc = t.zc + ((size_t)b * N + u) * t.S;
       int k = 0, next = -1;
+      // the current distribution is [p - cc q]_+ / cz; (cc, cz) = (0, 1) is p itself
+      double cz = 1.0;
       cc = 0.0;
       for (int s = u + 1; s < N; ++s) {
         if (s_par[s] != u) continue;
@@ -461,18 +465,29 @@ __global__ __launch_bounds__(WAVE) void k_tree_walk(const TreeArgs t) {
         const double l2p = (double)zt * k2 - lp, l2q = (double)zd * k2 - lq;
         const double us = (double)s_ua[s];
         bool accept = false;
-        if (k == 0) {
+        if (cc == 0.0) {
           accept = supp_t && us <= exp2(fmin(0.0, l2p - l2q));
         } else {
           const double ratio = exp2(l2p - l2q);
-          accept = supp_t && ratio > cc && us <= fmin(1.0, (ratio - cc) / zc[k]);
+          accept = supp_t && ratio > cc && us <= fmin(1.0, (ratio - cc) / cz);
         }
         if (accept) {
           next = s;
           break;
         }
-        cc += (k == 0) ? 1.0 : zc[k];  // c_{k+1} = c_k + Z_k, Z_0 = 1
+        // rejected: the next distribution is [p - (cc + cz) q]_+ with mass zc[k + 1]
+        // (k_tree_resid's round k + 1); a zero mass leaves p itself (as the chain's
+        // zero-residual fallback).  After the last child the draw finds the mass.
+        cc += cz;
         ++k;
+        if (k < s_nch[u]) {
+          if (zc[k] > 0.0) {
+            cz = zc[k];
+          } else {
+            cc = 0.0;
+            cz = 1.0;
+          }
+        }
       }
       if (next < 0) {
         kind = TJ_RESID;
@@ -502,18 +517,18 @@ __global__ __launch_bounds__(WAVE) void k_tree_walk(const TreeArgs t) {
 // ---------------------------------------------------------------- k_tree_draw
 
 // Weights of the tree's draw: [p - c q]_+ at a node whose children were all rejected,
-// p itself at a leaf.  Formed with one explicit fused multiply-add so that the masses and
-// the pick inside a segment see the same values.
+// p itself at a leaf (or where the current distribution is p again).  As the chain's
+// correction weights: p * max(0, 1 - c q/p), with log2(c q/p) = (z_d - z_t)*k2 - dmc and
+// dmc = (Md - Mt) - log2 c, so a draft close to the target keeps relative precision.
 struct TreeW {
-  float k2, mt_hi, mt_lo, md_hi, md_lo, tau_t, tau_d, c;
+  float k2, mt_hi, mt_lo, dmc, tau_t, tau_d;
   bool resid;
   SVD float operator()(float zt, float zd) const {
     zt = (zt < tau_t) ? -INFINITY : zt;
     const float p = fast_exp2(fmaf(zt, k2, -mt_hi) - mt_lo);
     if (!resid) return p;
     zd = (zd < tau_d) ? -INFINITY : zd;
-    const float q = fast_exp2(fmaf(zd, k2, -md_hi) - md_lo);
-    return fmaxf(fmaf(-c, q, p), 0.0f);
+    return __fmul_rn(p, one_minus_exp2(fmaf(zd - zt, k2, -dmc)));  // never fused into a sum
   }
 };
 
@@ -549,12 +564,12 @@ __global__ __launch_bounds__(NT) void k_tree_draw(const TreeArgs t) {
   if (kind == TJ_NONE) return;
   const int u = t.job[2 * b], N = a.G;
   const size_t rt = (size_t)b * a.rps + u, rd = rt + N;
-  const bool resid = kind == TJ_RESID;
+  const double cjob = t.job_c[b];
+  const bool resid = kind == TJ_RESID && cjob > 0.0;  // c = 0: the current distribution is p
   const double lp = (double)t.row_off[rt] + t.row_lt[rt];
   const double lq = resid ? (double)t.row_off[rd] + t.row_lt[rd] : 0.0;
-  TreeW wf{a.k2, d_head(lp), d_tail(lp), d_head(lq), d_tail(lq),
-           TOPK ? a.w.row_tau[rt] : -INFINITY, (TOPK && resid) ? a.w.row_tau[rd] : -INFINITY,
-           (float)t.job_c[b], resid};
+  TreeW wf{a.k2, d_head(lp), d_tail(lp), resid ? (float)((lq - lp) - log2(cjob)) : 0.0f,
+           TOPK ? a.w.row_tau[rt] : -INFINITY, (TOPK && resid) ? a.w.row_tau[rd] : -INFINITY, resid};
   const T *row_t = seq_row<T>(a, b, u);
   const T *row_d = resid ? seq_row<T>(a, b, N + u) : nullptr;
   __shared__ double s_seg[SEGS];
@@ -608,7 +623,8 @@ __global__ __launch_bounds__(NT) void k_tree_draw(const TreeArgs t) {
   if (sp >= 0 && total > 0.0) {
     y = segment_draw<T, ALIGNED>(a, row_t, row_d, sp / SEGS, sp % SEGS, wf, srem);
   } else if (resid) {
-    // No residual mass (reachable only through rounding): draw from p_u, chunk by chunk.
+    // No residual mass (p and q differ only where p's mass is lost to rounding): draw from
+    // p_u, chunk by chunk, as a zero mass before the last child would have.
     TreeW wp = wf;
     wp.resid = false;
     double tot = 0.0;

@@ -57,7 +57,7 @@ enum : int { JOB_NONE = 0, JOB_REJECT = 1, JOB_BONUS = 2 };  // NONE: nothing to
 // in word f (ints as their bits, floats as theirs; a double as a float head and tail).
 enum : int {
   JW_J, JW_KIND, JW_CBONUS, JW_OFFBONUS, JW_TB_HI, JW_TB_LO,  // bonus: chunk, its offset, u*S left in it
-  JW_MT_HI, JW_MT_LO, JW_MD_HI, JW_MD_LO,                    // rejection: log2-partitions of p_j, q_j
+  JW_MT_HI, JW_MT_LO, JW_DM,                                 // rejection: log2-partition of p_j; that of q_j minus it
   JW_TAU_T, JW_TAU_D,                                        // top-k thresholds (bonus: row G in TAU_T)
   JW_OFF_J,                                                  // rejection: row offset of p_j
   JW_USED, JW = 16
@@ -250,7 +250,6 @@ template <typename T, bool ALIGNED, bool TOPK, bool LDS, bool G0>
 SVD void sampling_finish(const Args &a, int b, float own_off, float own_hi, float own_lo,
                          int gx, float gzt, float gzd, const double *s_own_gseg) {
   constexpr int UNR = SEQ_LDS_PARTS / WAVE;
-  constexpr int RUNR = (SEQ_LDS_ROWS + WAVE - 1) / WAVE;
   __shared__ float s_po[SEQ_LDS_PARTS];
   __shared__ double s_ps[SEQ_LDS_PARTS];
   __shared__ float s_roff[SEQ_LDS_ROWS], s_rzx[SEQ_LDS_ROWS], s_rtau[SEQ_LDS_ROWS], s_rsum[SEQ_LDS_ROWS];
@@ -499,7 +498,7 @@ SVD void sampling_finish(const Args &a, int b, float own_off, float own_hi, floa
       t_bonus = trem * (double)fast_exp2(oG - off_bonus);
     }
   }
-  float mt_hi = 0.0f, mt_lo = 0.0f, md_hi = 0.0f, md_lo = 0.0f, tau_t = -INFINITY, tau_d = -INFINITY;
+  float mt_hi = 0.0f, mt_lo = 0.0f, dm = 0.0f, tau_t = -INFINITY, tau_d = -INFINITY;
   float off_j = 0.0f;
   if (kind == JOB_REJECT) {
     float ot, od;
@@ -510,8 +509,7 @@ SVD void sampling_finish(const Args &a, int b, float own_off, float own_hi, floa
     const double mt = (double)ot + lt, md = (double)od + ld;
     mt_hi = d_head(mt);
     mt_lo = d_tail(mt);
-    md_hi = d_head(md);
-    md_lo = d_tail(md);
+    dm = (float)(md - mt);
     tau_t = tau_of(j);
     tau_d = tau_of(G + 1 + j);
     off_j = ot;
@@ -528,8 +526,7 @@ SVD void sampling_finish(const Args &a, int b, float own_off, float own_hi, floa
     case JW_TB_LO: bits = __float_as_uint(d_tail(t_bonus)); break;
     case JW_MT_HI: bits = __float_as_uint(mt_hi); break;
     case JW_MT_LO: bits = __float_as_uint(mt_lo); break;
-    case JW_MD_HI: bits = __float_as_uint(md_hi); break;
-    case JW_MD_LO: bits = __float_as_uint(md_lo); break;
+    case JW_DM: bits = __float_as_uint(dm); break;
     case JW_TAU_T: bits = __float_as_uint(tau_t); break;
     case JW_TAU_D: bits = __float_as_uint(tau_d); break;
     case JW_OFF_J: bits = __float_as_uint(off_j); break;
@@ -880,7 +877,7 @@ SVD void combine_draw(const Args &a, int b, int j, float u, const T *row_t, cons
   int tok = -1;
   if (Z > 0.0) {
     if (sp >= 0 && sp < nseg) tok = segment_draw<T, ALIGNED>(a, row_t, row_d, sp / SEGS, sp % SEGS, wf, ts);
-  } else {  // zero residual (reachable only through rounding): draw from p_j itself
+  } else {  // zero residual (p and q differ only where p's mass is lost to rounding): draw from p_j
     const int rt = b * a.rps + j;
     double tin;
     const int cp = pick_target_chunk(a, rt, wf.off_j, u, &tin);
@@ -975,13 +972,11 @@ SVD void draw_item(const Args &a, int item) {
   }
 
   // Rejection at position j.
-  const int rt = b * a.rps + j;
   ResidualW wf;
   wf.k2 = a.k2;
   wf.mt_hi = jf(JW_MT_HI);
   wf.mt_lo = jf(JW_MT_LO);
-  wf.md_hi = jf(JW_MD_HI);
-  wf.md_lo = jf(JW_MD_LO);
+  wf.dm = jf(JW_DM);
   wf.tau_t = jf(JW_TAU_T);
   wf.tau_d = jf(JW_TAU_D);
   wf.off_j = jf(JW_OFF_J);
@@ -1024,11 +1019,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(TOPK ? 5 : 4
 
 namespace sv_host {
 
-std::atomic<unsigned> g_tag{0};
+// Launches counted over the process; a launch's tag is the count's low 32 bits (never 0),
+// so a tag value comes back after 2^32 - 1 launches (see sv_tag_epoch).
+std::atomic<unsigned long long> g_launches{0};
 unsigned next_tag() {
-  unsigned t = g_tag.fetch_add(1u, std::memory_order_relaxed) + 1u;
-  while (t == 0u) t = g_tag.fetch_add(1u, std::memory_order_relaxed) + 1u;
-  return t;
+  for (;;) {
+    const unsigned t = (unsigned)(g_launches.fetch_add(1ull, std::memory_order_relaxed) + 1ull);
+    if (t != 0u) return t;
+  }
 }
 
 }  // namespace sv_host
@@ -1248,6 +1246,10 @@ const char *sv_launch_plan(int32_t B, int32_t G, int32_t V, sv_dtype dtype, floa
     return dtype == SV_BF16 ? kPlanNames[0] : kPlanNames[1];
   }
   return kPlanNames[2];
+}
+
+uint32_t sv_tag_epoch(void) {
+  return (uint32_t)(sv_host::g_launches.load(std::memory_order_relaxed) >> 31);
 }
 
 const char *sv_status_string(sv_status status) {

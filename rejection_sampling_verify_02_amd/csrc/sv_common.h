@@ -411,7 +411,6 @@ SVD unsigned topk_chunk_list(u32x4 (&w)[VPT], int k, int cap, unsigned *s_keys, 
 template <typename T, bool ALIGNED>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(7))) void k_topk_select(const Args a, int cap) {
   constexpr int VEC = Fmt<T>::VEC;
-  constexpr int NPASS = (sizeof(T) == 2) ? 2 : 4;
   __shared__ unsigned s_hist[256], s_ge[256], s_wv[NW], s_pick[2];
   __shared__ unsigned s_keys[TOPK_LDS_KEYS];
   const int tid = threadIdx.x;

@@ -8,18 +8,37 @@
 
 namespace sv {
 
-// Weights of the correction draw: w = max(p - q, 0) with p = 2^(z_t*k2 - Mt) and
-// q = 2^(z_d*k2 - Md).  The log2-partitions are split into a float head and tail so the
-// per-element arguments carry only their own rounding.
+// max(0, 1 - 2^d): 0 for d >= 0 and for a NaN d.  Near d = 0 the difference 1 - 2^d
+// would cancel, so for -1/2 < d < 0 it is the series of -expm1(y), y = d ln 2, to the
+// y^7 term (truncation below 2e-8 relative); further out 2^d <= 0.71 and 1 - 2^d keeps
+// full relative precision.
+SVD float one_minus_exp2(float d) {
+  const float y = d * 0.69314718055994531f;
+  float h = 1.0f / 5040.0f;
+  h = fmaf(h, y, 1.0f / 720.0f);
+  h = fmaf(h, y, 1.0f / 120.0f);
+  h = fmaf(h, y, 1.0f / 24.0f);
+  h = fmaf(h, y, 1.0f / 6.0f);
+  h = fmaf(h, y, 0.5f);
+  h = fmaf(h, y, 1.0f);
+  const float m = (d > -0.5f) ? -y * h : 1.0f - fast_exp2(d);
+  return (d < 0.0f) ? m : 0.0f;
+}
+
+// Weights of the correction draw, [p - q]_+ ("Speculative Decoding 的朴素思想", section
+// "Correction 为什么用正残差"), formed as p * max(0, 1 - q/p) with p = 2^(z_t*k2 - Mt) and
+// log2(q/p) = (z_d - z_t)*k2 - (Md - Mt) taken from the two logits' own difference, so a
+// draft close to the target (q ~ p) keeps the weight's relative precision instead of
+// losing it to the cancellation of p - q.  Mt is split into a float head and tail so the
+// argument of p carries only its own rounding; dm = Md - Mt is rounded once.
 struct ResidualW {
-  float k2, mt_hi, mt_lo, md_hi, md_lo, tau_t, tau_d;
+  float k2, mt_hi, mt_lo, dm, tau_t, tau_d;
   float off_j;  // row offset of p_j (the zero-residual fallback's reference)
   SVD float operator()(float zt, float zd) const {
     zt = (zt < tau_t) ? -INFINITY : zt;
     zd = (zd < tau_d) ? -INFINITY : zd;
     const float p = fast_exp2(fmaf(zt, k2, -mt_hi) - mt_lo);
-    const float q = fast_exp2(fmaf(zd, k2, -md_hi) - md_lo);
-    return fmaxf(p - q, 0.0f);
+    return __fmul_rn(p, one_minus_exp2(fmaf(zd - zt, k2, -dm)));  // never fused into a sum
   }
 };
 

@@ -9,7 +9,7 @@ import pytest
 import rejection_sampling_verify_02_amd as sv
 
 ROOT = Path(__file__).resolve().parents[1]
-HEADER = ROOT / "include" / "spec_verify.h"
+HEADERS = sorted((ROOT / "include").glob("*.h"))
 
 
 @pytest.fixture(scope="module")
@@ -21,7 +21,7 @@ def lib():
 
 
 def declared_functions():
-    text = HEADER.read_text()
+    text = "\n".join(h.read_text() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"if", "sizeof"})
 
@@ -255,3 +255,21 @@ def test_typical_plan_and_workspace(lib):
     n, z = lib.sv_typical_workspace_bytes(*args), lib.sv_typical_workspace_zero_bytes(*args)
     assert z == n == 320 * 8 * 8 * 8  # 320 rows of 8 chunks, 8 words each
     assert lib.sv_typical_workspace_zero_bytes(64, 4, 128256, sv.SV_BF16, 0.0, 0) == 0
+
+
+def test_tag_epoch_before_any_launch(lib):
+    """No kernel has been launched in this process: the launch count's 2^31 epoch is 0."""
+    assert sv.load_library().sv_tag_epoch() == 0
+
+
+def test_read_probe_validates_arguments(lib):
+    """The streaming-read probe refuses NULL pointers and sizes that are not whole 32 KiB
+    chunks before any HIP call."""
+    import ctypes
+    V = ctypes.c_void_p
+    f = sv.load_library().sv_read_probe
+    assert f(None, 32768, V(256), None) == 1
+    assert f(V(256), 32768, None, None) == 1
+    assert f(V(256), 0, V(256), None) == 2
+    assert f(V(256), 32768 + 16, V(256), None) == 2
+    assert f(V(264), 32768, V(256), None) == 2

@@ -232,3 +232,36 @@ def test_tree_determinism_and_shared_workspace(dev):
         np.testing.assert_array_equal(a, b)
         np.testing.assert_array_equal(a, c)
     run_both(raw, tok, 0.9, 20, 4, dev, "top-k 20")
+
+
+@pytest.mark.parametrize("dtype,V", [("f32", 40000), ("bf16", 40000)])
+def test_zero_residual_star_trees(dev, dtype, V):
+    """Star trees whose root rows are identical except at token x (target logit -460, draft
+    larger by 1 in f32, 2 in bf16): [p - q]_+ has no mass, so after the first child (token
+    x) is rejected the current distribution is p again.  A second child with another token
+    is then accepted whatever its uniform; children that all carry x are all rejected and
+    the token is drawn from p.  Rows of several chunks, so the draw's chunk pick matters."""
+    rng = np.random.default_rng(V + (dtype == "bf16"))
+    B, N = 24, 4
+    lt, ld = wl.ZERO_RESIDUAL_LOGITS[dtype]
+    z = (2.0 * rng.standard_normal((B, N, V))).astype(np.float32)
+    zd = z.copy()
+    x = rng.integers(0, V, B)
+    y = (x + 1 + rng.integers(0, V - 1, B)) % V
+    z[np.arange(B), 0, x] = lt
+    zd[np.arange(B), 0, x] = ld
+    store = wl.bf16_bits if dtype == "bf16" else (lambda a: a)
+    parent = np.ascontiguousarray(np.broadcast_to(np.array([-1, 0, 0, 0], np.int32), (B, N)))
+    ua = np.zeros((B, N), np.float32)
+    ua[:, 1:] = 0.9
+    ua[::2, 2] = rng.random(B // 2, dtype=np.float32)
+    raw = wl.TreeRaw(store(z), store(zd), parent, np.zeros((B, N), np.float32), ua,
+                     rng.random(B, dtype=np.float32))
+    tok = np.zeros((B, N), np.int32)
+    tok[:, 1] = x
+    tok[:, 2] = np.where(np.arange(B) % 2 == 0, y, x)   # even trees: another token second
+    tok[:, 3] = x
+    acc, out, path = run_both(raw, tok, 1.0, 0, 3, dev, f"zero residual star {dtype}")
+    even = np.arange(B) % 2 == 0
+    assert np.all(acc[even] == 1) and np.all(path[even, 0] == 2) and np.all(out[even, 0] == y[even])
+    assert np.all(acc[~even] == 0)
