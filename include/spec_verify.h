@@ -40,7 +40,9 @@
 extern "C" {
 #endif
 
-typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+/* The two sentinels give the enumeration the range of int32_t, so any value a caller
+ * passes (an unsupported one is answered with SV_ERR_DTYPE) is a valid value of the type. */
+typedef enum { SV_DTYPE_INVALID = -1, SV_F32 = 0, SV_BF16 = 1, SV_DTYPE_LIMIT = 0x7fffffff } sv_dtype;
 
 typedef enum {
   SV_OK = 0,
