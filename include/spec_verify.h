@@ -53,7 +53,9 @@ typedef enum {
   SV_ERR_WORKSPACE = 5,   /* workspace smaller than sv_workspace_bytes() or misaligned    */
   SV_ERR_ALIGN = 6,       /* a logit pointer is not aligned to its element size           */
   SV_ERR_LAUNCH = 7,      /* the HIP runtime refused a kernel launch                       */
-  SV_ERR_PARAM = 8        /* spec_typical_verify: epsilon or delta negative or not finite   */
+  SV_ERR_PARAM = 8,       /* spec_typical_verify: epsilon or delta negative or not finite   */
+  SV_ERR_SCRATCH = 9      /* spec_verify_noalloc: the arguments need more scratch memory    */
+                          /* than SV_NOALLOC_SCRATCH_BYTES                                   */
 } sv_status;
 
 /* Row-level codes written into accepted_len[b] instead of a length; the whole row of
@@ -127,6 +129,30 @@ sv_status spec_verify(const void *target_logits, const void *draft_logits, sv_dt
                       int32_t B, int32_t G, int32_t V, float temperature, int32_t top_k,
                       int32_t *accepted_len, int32_t *out_tokens, float *row_stats,
                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* For callers that cannot allocate device memory -- code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc: spec_verify with the library's own
+ * scratch memory in place of the caller's workspace.  The arguments and results are those
+ * of spec_verify; the kernels are the same.  The scratch is one array of
+ * SV_NOALLOC_SCRATCH_BYTES bytes per GPU, a static device variable of the library that
+ * each GPU holds from the first call on it until the process ends; the call allocates
+ * nothing (no hipMalloc, no hipFree, no allocating library routine).
+ *   - Arguments whose workspace (sv_workspace_bytes) exceeds SV_NOALLOC_SCRATCH_BYTES are
+ *     refused with SV_ERR_SCRATCH; nothing is enqueued.
+ *   - The first call on a device looks the array's device address up (hipGetSymbolAddress,
+ *     on the current device) and keeps it; a failure of that lookup returns
+ *     SV_ERR_LAUNCH.  Before a call whose leading words must be zero and are not known to
+ *     be (the first call, a longer prefix than before, a new tag epoch), a fill kernel
+ *     clears them on `stream`.
+ *   - Every call on a GPU uses that GPU's one array, which keeps the last call's contents:
+ *     calls that overlap in time on one GPU (on different streams, or from different host
+ *     threads) race and must not be made.  Calls ordered on one stream are safe. */
+#define SV_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+sv_status spec_verify_noalloc(const void *target_logits, const void *draft_logits, sv_dtype dtype,
+                              const int32_t *draft_tokens, const float *u_accept,
+                              const float *u_sample, int32_t B, int32_t G, int32_t V,
+                              float temperature, int32_t top_k, int32_t *accepted_len,
+                              int32_t *out_tokens, float *row_stats, void *stream);
 
 /* spec_verify that also times each of its kernels with HIP events.
  * events: array of n_events hipEvent_t handles (created by the caller, with timing

@@ -24,7 +24,7 @@ MAX_LAUNCHES = 8
 
 _STATUS = {0: "SV_OK", 1: "SV_ERR_NULL", 2: "SV_ERR_SHAPE", 3: "SV_ERR_DTYPE",
            4: "SV_ERR_TEMPERATURE", 5: "SV_ERR_WORKSPACE", 6: "SV_ERR_ALIGN", 7: "SV_ERR_LAUNCH",
-           8: "SV_ERR_PARAM"}
+           8: "SV_ERR_PARAM", 9: "SV_ERR_SCRATCH"}
 
 EXPORTED = ("spec_verify", "spec_verify_timed", "sv_workspace_bytes", "sv_workspace_zero_bytes",
             "sv_status_string", "sv_launch_plan", "spec_sample", "spec_sample_timed",
@@ -34,7 +34,7 @@ EXPORTED = ("spec_verify", "spec_verify_timed", "sv_workspace_bytes", "sv_worksp
             "sv_tree_workspace_zero_bytes", "sv_tree_launch_plan",
             "spec_typical_verify", "spec_typical_verify_timed", "sv_typical_workspace_bytes",
             "sv_typical_workspace_zero_bytes", "sv_typical_launch_plan", "sv_tag_epoch",
-            "sv_read_probe")
+            "sv_read_probe", "spec_verify_noalloc")
 
 
 class SpecVerifyError(RuntimeError):
@@ -59,6 +59,8 @@ def load_library(path: Path | str | None = None) -> ctypes.CDLL:
     common = [V, V, I32, V, V, V, I32, I32, I32, F32, I32, V, V, V, V, SZ, V]
     lib.spec_verify.argtypes = common
     lib.spec_verify.restype = I32
+    lib.spec_verify_noalloc.argtypes = common[:14] + [V]
+    lib.spec_verify_noalloc.restype = I32
     lib.spec_verify_timed.argtypes = common + [V, I32, V]
     lib.spec_verify_timed.restype = I32
     smp = [V, I32, V, I32, I32, F32, I32, V, V, V, SZ, V]
@@ -513,3 +515,31 @@ def read_probe(buf, out=None, *, stream: int | None = None):
     if rc != 0:
         raise SpecVerifyError(rc, "sv_read_probe refused its arguments" if rc != 7 else "kernel launch failed")
     return out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def spec_verify_noalloc(target_logits, draft_logits, draft_tokens, u_accept, u_sample, temperature: float,
+                        top_k: int = 0, *, out, row_stats=None, stream=None):
+    """spec_verify through the allocation-free entry point (the library's per-GPU scratch
+    array instead of a workspace).  ``out`` supplies the output tensors (accepted_len [B],
+    out_tokens [B, G+1]) and ``row_stats`` optionally a [B, 2G+1, 2] float32 tensor, so that
+    the call allocates nothing; calls that overlap on one GPU race (see the header)."""
+    import torch
+    lib = load_library()
+    dev = target_logits.device
+    dt = _dtype_code(target_logits)
+    B, G1, V = target_logits.shape
+    G = G1 - 1
+    acc, toks = out
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    greedy = float(temperature) == 0.0
+    args = [_ptr(target_logits), None if greedy else _ptr(draft_logits), dt, _ptr(draft_tokens),
+            None if greedy else _ptr(u_accept), None if greedy else _ptr(u_sample), B, G, V,
+            float(temperature), int(top_k), _ptr(acc), _ptr(toks), _ptr(row_stats), ctypes.c_void_p(stream)]
+    st = lib.spec_verify_noalloc(*args)
+    if st != 0:
+        raise SpecVerifyError(st, sv_status_string(st))
+    return acc, toks

@@ -42,6 +42,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "spec_verify.h"
 #include "sv_common.h"
@@ -1120,22 +1121,36 @@ hipError_t launch_all(const Plan &p, const Args &a, hipStream_t st, void *const 
   return L.e;
 }
 
+// Every check of the arguments before the workspace's size and alignment, in the
+// documented order (ws_null: a workspace pointer is required and NULL).
+sv_status check_args(const void *target, const void *draft, sv_dtype dt, const int32_t *tokens,
+                     const float *u_accept, const float *u_sample, int32_t B, int32_t G, int32_t V,
+                     float T, int32_t top_k, const int32_t *acc, const int32_t *out, bool ws_null,
+                     Plan &p) {
+  if (dt != SV_F32 && dt != SV_BF16) return SV_ERR_DTYPE;
+  if (B < 1 || G < 0 || V < 1) return SV_ERR_SHAPE;
+  if (!(T >= 0.0f) || !isfinite(T)) return SV_ERR_TEMPERATURE;
+  if (!make_plan(B, G, V, dt, T, top_k, p)) return SV_ERR_SHAPE;
+  const bool sampling = !p.greedy;
+  if (!target || !acc || !out || ws_null) return SV_ERR_NULL;
+  if (G > 0 && !tokens) return SV_ERR_NULL;
+  if (sampling && (!u_sample || (G > 0 && (!draft || !u_accept)))) return SV_ERR_NULL;
+  const uintptr_t ta = (uintptr_t)target, da = (uintptr_t)draft;
+  if (ta % p.esz || (sampling && G > 0 && da % p.esz)) return SV_ERR_ALIGN;
+  return SV_OK;
+}
+
 sv_status run(const void *target, const void *draft, sv_dtype dt, const int32_t *tokens,
               const float *u_accept, const float *u_sample, int32_t B, int32_t G, int32_t V,
               float T, int32_t top_k, int32_t *acc, int32_t *out, float *row_stats, void *ws,
               size_t ws_bytes, void *stream, void *const *ev, int32_t nev, int32_t *nl) {
   if (nl) *nl = 0;
-  if (dt != SV_F32 && dt != SV_BF16) return SV_ERR_DTYPE;
-  if (B < 1 || G < 0 || V < 1) return SV_ERR_SHAPE;
-  if (!(T >= 0.0f) || !isfinite(T)) return SV_ERR_TEMPERATURE;
   Plan p;
-  if (!make_plan(B, G, V, dt, T, top_k, p)) return SV_ERR_SHAPE;
+  const sv_status cs = check_args(target, draft, dt, tokens, u_accept, u_sample, B, G, V, T, top_k, acc, out,
+                                  ws == nullptr, p);
+  if (cs != SV_OK) return cs;
   const bool sampling = !p.greedy;
-  if (!target || !acc || !out || !ws) return SV_ERR_NULL;
-  if (G > 0 && !tokens) return SV_ERR_NULL;
-  if (sampling && (!u_sample || (G > 0 && (!draft || !u_accept)))) return SV_ERR_NULL;
   const uintptr_t ta = (uintptr_t)target, da = (uintptr_t)draft;
-  if (ta % p.esz || (sampling && G > 0 && da % p.esz)) return SV_ERR_ALIGN;
   if (ws_bytes < p.total || ((uintptr_t)ws & 255)) return SV_ERR_WORKSPACE;
   const bool aligned = ((size_t)V * p.esz) % 16 == 0 && ta % 16 == 0 &&
                        (!sampling || G == 0 || da % 16 == 0);
@@ -1192,9 +1207,79 @@ sv_status run(const void *target, const void *draft, sv_dtype dt, const int32_t 
   return e == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
 }
 
+// ---------------------------------------------------------------- allocation-free calls
+
+// The scratch memory of spec_verify_noalloc: one array per GPU, a static device variable
+// of the library (held by each GPU the library runs on until the process ends).  Host code
+// never passes this name to a kernel or a copy: on the host it is only a stand-in, and the
+// device address comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) unsigned char scratch[SV_NOALLOC_SCRATCH_BYTES];
+
+__global__ __launch_bounds__(256) void k_fill_zero(u64 *p, size_t n_words) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n_words; i += (size_t)gridDim.x * 256) p[i] = 0ull;
+}
+
+struct ScratchState {
+  void *ptr = nullptr;   // the device address of this GPU's array
+  size_t clean = 0;      // leading bytes known to hold zeros or words of completed calls
+  size_t used = 0;       // longest prefix any call has marked since the array was last cleared
+  uint32_t epoch = 0;    // tag epoch when that clearing happened
+};
+constexpr int SCRATCH_MAX_DEVICES = 64;
+ScratchState g_scratch[SCRATCH_MAX_DEVICES];
+std::mutex g_scratch_mu;
+
 }  // namespace
 
 extern "C" {
+
+sv_status spec_verify_noalloc(const void *target_logits, const void *draft_logits, sv_dtype dtype,
+                              const int32_t *draft_tokens, const float *u_accept,
+                              const float *u_sample, int32_t B, int32_t G, int32_t V,
+                              float temperature, int32_t top_k, int32_t *accepted_len,
+                              int32_t *out_tokens, float *row_stats, void *stream) {
+  Plan p;
+  const sv_status cs = check_args(target_logits, draft_logits, dtype, draft_tokens, u_accept, u_sample, B, G,
+                                  V, temperature, top_k, accepted_len, out_tokens, false, p);
+  if (cs != SV_OK) return cs;
+  if (p.total > SV_NOALLOC_SCRATCH_BYTES) return SV_ERR_SCRATCH;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= SCRATCH_MAX_DEVICES) return SV_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ScratchState &sc = g_scratch[dev];
+  if (!sc.ptr) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return SV_ERR_LAUNCH;
+    sc.ptr = ptr;
+    sc.clean = sc.used = 0;
+    sc.epoch = sv_tag_epoch();
+  }
+  const uint32_t epoch = sv_tag_epoch();
+  size_t need = p.zero_bytes;
+  if (epoch != sc.epoch) {  // tags of calls before this epoch may come back: clear every marked word
+    need = need > sc.used ? need : sc.used;
+    sc.clean = 0;
+  }
+  if (need > sc.clean) {
+    const size_t words = (need + 7) / 8;
+    const unsigned grid = (unsigned)((words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024);
+    hipLaunchKernelGGL(k_fill_zero, dim3(grid), dim3(256), 0, (hipStream_t)stream, (u64 *)sc.ptr, words);
+    if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
+    sc.clean = need;
+    if (epoch != sc.epoch) {
+      sc.used = 0;
+      sc.epoch = epoch;
+    }
+  }
+  const sv_status st = run(target_logits, draft_logits, dtype, draft_tokens, u_accept, u_sample, B, G, V,
+                           temperature, top_k, accepted_len, out_tokens, row_stats, sc.ptr,
+                           SV_NOALLOC_SCRATCH_BYTES, stream, nullptr, 0, nullptr);
+  if (st == SV_OK) {  // a call leaves its own prefix clean and may overwrite what follows it
+    sc.clean = p.zero_bytes;
+    sc.used = sc.used > p.zero_bytes ? sc.used : p.zero_bytes;
+  }
+  return st;
+}
 
 size_t sv_workspace_bytes(int32_t B, int32_t G, int32_t V, sv_dtype dtype, float temperature,
                           int32_t top_k) {
@@ -1263,6 +1348,7 @@ const char *sv_status_string(sv_status status) {
     case SV_ERR_ALIGN: return "logit pointer not aligned to its element size";
     case SV_ERR_LAUNCH: return "kernel launch failed";
     case SV_ERR_PARAM: return "epsilon and delta must be finite and >= 0";
+    case SV_ERR_SCRATCH: return "the arguments need more scratch memory than spec_verify_noalloc holds";
   }
   return "unknown status";
 }

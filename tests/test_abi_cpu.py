@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(9):
+    for code in range(10):
         s = sv.sv_status_string(code)
         assert s and s != "unknown status"
     assert sv.sv_status_string(99) == "unknown status"
@@ -273,3 +273,20 @@ def test_read_probe_validates_arguments(lib):
     assert f(V(256), 0, V(256), None) == 2
     assert f(V(256), 32768 + 16, V(256), None) == 2
     assert f(V(264), 32768, V(256), None) == 2
+
+
+def test_noalloc_refuses_oversized_arguments(lib):
+    """spec_verify_noalloc answers arguments whose workspace exceeds its scratch array with
+    SV_ERR_SCRATCH, after the usual argument checks and before any HIP call."""
+    import ctypes
+    V = ctypes.c_void_p
+    p = V(256)
+    f = sv.load_library().spec_verify_noalloc
+    big = (1024, 8, 256000, sv.SV_BF16, 1.0, 50)   # about 241 MiB of workspace
+    assert sv.sv_workspace_bytes(*big) > sv.NOALLOC_SCRATCH_BYTES
+    assert f(p, p, sv.SV_BF16, p, p, p, 1024, 8, 256000, 1.0, 50, p, p, None, None) == 9
+    assert f(p, p, sv.SV_BF16, p, p, p, 0, 8, 256000, 1.0, 50, p, p, None, None) == 2
+    assert f(None, p, sv.SV_BF16, p, p, p, 1024, 8, 256000, 1.0, 50, p, p, None, None) == 1
+    small = (64, 4, 128256, sv.SV_BF16, 1.0, 0)
+    assert sv.sv_workspace_bytes(*small) <= sv.NOALLOC_SCRATCH_BYTES
+    assert sv.sv_status_string(9) != "unknown status"

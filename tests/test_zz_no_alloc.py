@@ -1,0 +1,63 @@
+"""The allocation-free entry point spec_verify_noalloc (the library's per-GPU scratch array
+instead of a workspace) gives exactly what spec_verify gives on the same inputs: two calls
+in a row on one stream, the second with a smaller input (a shorter zero prefix over the
+first call's leftovers), then a greedy call and a top-k call.  Through the C ABI."""
+import numpy as np
+import pytest
+
+import parity
+from rejection_sampling_verify_02_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import rejection_sampling_verify_02_amd as sv
+    sv.load_library()
+    return torch.device("cuda:0")
+
+
+def one(dev, raw, T, k):
+    import torch
+    import rejection_sampling_verify_02_amd as sv
+    tok = parity.prepare(raw, T, k)
+    args = [parity.to_device(raw.target, dev), parity.to_device(raw.draft, dev), parity.to_device(tok, dev),
+            parity.to_device(raw.u_accept, dev), parity.to_device(raw.u_sample, dev)]
+    B, G = tok.shape
+    ref = sv.spec_verify(*args, T, k, row_stats=T > 0)
+    acc = torch.full((B,), -99, dtype=torch.int32, device=dev)
+    out = torch.full((B, G + 1), -99, dtype=torch.int32, device=dev)
+    st = torch.full((B, 2 * G + 1, 2), -1.0, dtype=torch.float32, device=dev) if T > 0 else None
+    sv.spec_verify_noalloc(*args, T, k, out=(acc, out), row_stats=st)
+    torch.cuda.synchronize(dev)
+    assert np.array_equal(acc.cpu().numpy(), ref[0].cpu().numpy())
+    assert np.array_equal(out.cpu().numpy(), ref[1].cpu().numpy())
+    if T > 0:
+        assert np.array_equal(st.cpu().numpy(), ref[2].cpu().numpy(), equal_nan=True)
+    print(f"[noalloc] B={B} G={G} V={raw.V} T={T} k={k}: identical to spec_verify", flush=True)
+    return acc.cpu().numpy()
+
+
+def test_noalloc_matches_spec_verify(dev):
+    acc1 = one(dev, wl.make_config(3), 1.0, 0)                  # the headline batch
+    acc2 = one(dev, wl.make_random(5, 3, 9003, "f32", seed=11), 0.8, 0)  # smaller, right after
+    assert np.all(acc1 >= 0) and np.all(acc2 >= 0)
+    one(dev, wl.make_random(16, 4, 20001, "bf16", seed=12), 0.0, 0)    # greedy
+    one(dev, wl.make_random(8, 3, 20000, "bf16", seed=13), 0.8, 50)    # top-k (one-pass threshold)
+    one(dev, wl.make_random(3, 2, 700, "bf16", seed=14), 1.0, 0)       # small again
+
+
+def test_noalloc_refuses_more_than_its_scratch(dev):
+    """A shape whose workspace exceeds the scratch array is refused before any launch."""
+    import ctypes
+    import torch
+    import rejection_sampling_verify_02_amd as sv
+    t = torch.zeros((16,), dtype=torch.bfloat16, device=dev)
+    p = ctypes.c_void_p(t.data_ptr())
+    lib = sv.load_library()
+    assert lib.spec_verify_noalloc(p, p, sv.SV_BF16, p, p, p, 1024, 8, 256000, 1.0, 50, p, p, None, None) == 9
+    torch.cuda.synchronize(dev)
