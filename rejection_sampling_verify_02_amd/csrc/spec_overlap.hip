@@ -356,7 +356,8 @@ sv_status ov_run(const void *target, const void *draft, sv_dtype dt, int32_t B, 
   a.w.tw_hist = (u64 *)(base + p.tw_hist);
   a.w.row_tau = (float *)(base + p.row_tau);
   a.w.tk_state = (uint2 *)(base + p.tk_state);
-  a.w.tk_part = nullptr;
+  a.w.tk_rowp = nullptr;
+  a.w.tk_keep = nullptr;
 
   hipStream_t st = (hipStream_t)stream;
   int n = 0;

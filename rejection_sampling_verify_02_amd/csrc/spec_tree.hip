@@ -788,7 +788,8 @@ sv_status tree_run(const void *target, const void *draft, sv_dtype dt, const int
   a.w.tw_hist = (u64 *)(base + p.tw_hist);
   a.w.row_tau = (float *)(base + p.row_tau);
   a.w.tk_state = (uint2 *)(base + p.tk_state);
-  a.w.tk_part = nullptr;
+  a.w.tk_rowp = nullptr;
+  a.w.tk_keep = nullptr;
   t.parent = parent;
   t.path = path;
   t.S = p.S;

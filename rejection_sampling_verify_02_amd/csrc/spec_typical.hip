@@ -372,7 +372,8 @@ sv_status typ_run(const void *target, sv_dtype dt, const int32_t *tokens, int32_
   a.w.tw_hist = (u64 *)(base + p.tw_hist);
   a.w.row_tau = (float *)(base + p.row_tau);
   a.w.tk_state = (uint2 *)(base + p.tk_state);
-  a.w.tk_part = nullptr;
+  a.w.tk_rowp = nullptr;
+  a.w.tk_keep = nullptr;
   t.ln_eps = log((double)eps);  // -inf for eps = 0: every token of the support passes
   t.ln_delta = log((double)delta);
 

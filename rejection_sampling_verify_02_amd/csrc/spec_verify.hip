@@ -630,20 +630,6 @@ SVD void norm_item(const Args &a, int item) {
       tw_putf(&gw[lane], a.tag, (lane & 1) ? d_tail(v) : d_head(v));
     }
   };
-  // After the one-pass top-k threshold, a chunk whose list was complete has its partial
-  // already (kept values only): no load.  The finisher still gathers its token logits.
-  if (TOPK && !G0 && a.w.tk_part) {
-    const uint4 pp = a.w.tk_part[(size_t)r * a.C + c];  // written by the previous kernel
-    if (pp.w == 1u) {
-      if (gath && gx >= 0 && gx < a.V) {
-        gzt = Fmt<T>::at(seq_row<T>(a, b, lane), (size_t)gx);
-        gzd = Fmt<T>::at(seq_row<T>(a, b, a.G + 1 + lane), (size_t)gx);
-      }
-      if (wid != 0) return;
-      finish(__uint_as_float(pp.x), __uint_as_float(pp.y), __uint_as_float(pp.z));
-      return;
-    }
-  }
   float x[VPT][VEC];
   if (ALIGNED) {
     u32x4 w[VPT];
@@ -1014,6 +1000,243 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(TOPK ? 5 : 4
   else if (!G0) draw_item<T, ALIGNED>(a, item);
 }
 
+// ---------------------------------------------------------------- after the one-pass top-k
+
+// Weights of a draw from target row j alone (the bonus, or the zero-residual fallback):
+// p_j(v) = 2^(z*k2 - Mt) for kept z (z >= tau), Mt the row's log2-partition as a float
+// head and tail.
+struct KeptW {
+  float k2, mt_hi, mt_lo, tau;
+  SVD float operator()(float zt, float) const {
+    zt = (zt < tau) ? -INFINITY : zt;
+    return fast_exp2(fmaf(zt, k2, -mt_hi) - mt_lo);
+  }
+};
+
+// Inverse CDF over whole rows by one workgroup, for a row whose kept set has no list
+// (heavy ties): every chunk's mass (its segment masses summed in order), the chunk that
+// holds u*Z, that chunk's segment masses again, then one segment re-read for lane and
+// element.  Returns the token in every thread (-1 with no positive mass) and the total in
+// *Z.
+template <typename T, bool ALIGNED, bool PAIR, typename WFn>
+SVD int block_row_draw(const Args &a, const T *rowA, const T *rowB, const WFn &wf, float u,
+                       double *s_seg, double *s_ctot, double *Z) {
+  __shared__ int s_res;
+  __shared__ double s_rem, s_tot;
+  const int wid = threadIdx.x / WAVE, lane = lane_id();
+  const int C = a.C;
+  for (int c = 0; c < C; ++c) {
+    chunk_masses<T, ALIGNED, VPT, VPT, PAIR>(a, rowA, rowB, c, 0, wf, s_seg);
+    if (wid == 0) {
+      const double t = wave_sum((lane < SEGS) ? s_seg[lane] : 0.0);
+      if (lane == 0) s_ctot[c] = t;
+    }
+    __syncthreads();
+  }
+  if (wid == 0) {
+    double trem, tot;
+    auto cm = [&](int i) { return s_ctot[i]; };
+    const int cp = wave_pick4_frac(C, (double)u, cm, &trem, &tot);
+    if (lane == 0) {
+      s_res = cp;
+      s_rem = trem;
+      s_tot = tot;
+    }
+  }
+  __syncthreads();
+  const int cp = s_res;
+  *Z = s_tot;
+  if (cp < 0 || cp >= C) return -1;
+  const double trem = s_rem;
+  __syncthreads();  // every thread holds cp and the remainder before they are reused
+  chunk_masses<T, ALIGNED, VPT, VPT, PAIR>(a, rowA, rowB, cp, 0, wf, s_seg);
+  if (wid == 0) {
+    auto segm = [&](int i) { return s_seg[i]; };
+    double ts;
+    const int sp = wave_pick(SEGS, trem, segm, &ts);
+    const int tok = (sp >= 0) ? segment_draw<T, ALIGNED>(a, rowA, PAIR ? rowB : (const T *)nullptr, cp, sp, wf, ts) : -1;
+    if (lane == 0) s_res = tok;
+  }
+  __syncthreads();
+  return s_res;
+}
+
+// Verification after the one-pass top-k threshold: one workgroup per sequence, and no
+// logit row is read in bulk.  k_topk_merge left each row's kept-set normaliser and (unless
+// heavy ties) its kept (index, logit) pairs in index order, so:
+//  - the acceptance test of every position (thread i: positions i, i + 256, ...) needs its
+//    token's logit in the two rows and the two rows' log2-partitions; every position's row,
+//    token, uniform and support checks count, as in the streamed scan, and the first
+//    rejection comes from an LDS minimum;
+//  - a rejection at j draws from [p_j - q_j]_+ ("Speculative Decoding 的朴素思想", section
+//    "Correction 为什么用正残差"), which is zero outside p_j's kept set: the weights of the
+//    listed values, with q_j's logit gathered at each index, and one inverse CDF over them
+//    in index order; a zero residual draws from p_j over the same list;
+//  - all accepted draws the bonus from p_G's list the same way.
+// A row with no list is streamed by the workgroup itself (block_row_draw).
+template <typename T, bool ALIGNED>
+__global__ __launch_bounds__(NT) void k_topk_verify(const Args a, int cap) {
+  __shared__ int s_j;
+  __shared__ unsigned s_flags;
+  __shared__ float s_w[TOPK_LDS_KEYS];  // the kept list's weights (cap <= 1024)
+  __shared__ double s_seg[SEGS], s_ctot[TOPK_SELECT_MAX_C];
+  const int tid = threadIdx.x, wid = tid / WAVE, lane = lane_id();
+  const int b = blockIdx.x;
+  if (b >= a.B) return;
+  const int G = a.G, rps = a.rps;
+  const size_t r0 = (size_t)b * rps;
+  const uint4 *rowp = a.w.tk_rowp;  // written by the previous kernel
+  const float *rtau = a.w.row_tau;
+  int32_t *out = a.out_tokens + (size_t)b * (G + 1);
+  if (tid == 0) {
+    s_j = G;
+    s_flags = 0u;
+  }
+  __syncthreads();
+
+  // A row's offset and log2 of its sum; false for an unusable row (no finite value kept,
+  // a NaN, or a kept +inf).
+  auto rstat = [&](size_t r, float &o, double &l2s) -> bool {
+    const uint4 v = rowp[r];
+    o = __uint_as_float(v.x);
+    const double S = d_join(__uint_as_float(v.y), __uint_as_float(v.z));
+    const bool ok = isfinite(o) && isfinite(S) && S > 0.0;
+    l2s = ok ? log2(S) : 0.0;
+    return ok;
+  };
+
+  unsigned flags = 0;  // 1 bad token, 2 bad row, 4 bad uniform, 8 q(x) = 0, 16 no threshold
+  for (int i = tid; i < G; i += NT) {
+    const int x = a.tokens[(size_t)b * G + i];
+    const bool tok_ok = x >= 0 && x < a.V;
+    if (!tok_ok) flags |= 1;
+    float ot, od;
+    double lt, ld;
+    const bool okt = rstat(r0 + i, ot, lt);
+    const bool okd = rstat(r0 + G + 1 + i, od, ld);
+    if (!okt || !okd) flags |= 2;
+    const float u = a.u_accept[(size_t)b * G + i];
+    if (!(u >= 0.0f && u < 1.0f)) flags |= 4;
+    bool accept = false;
+    if (tok_ok) {
+      const float zt = Fmt<T>::at(seq_row<T>(a, b, i), (size_t)x);
+      const float zd = Fmt<T>::at(seq_row<T>(a, b, G + 1 + i), (size_t)x);
+      const bool supp_t = (zt > -INFINITY) && !(zt < rtau[r0 + i]);
+      const bool supp_d = (zd > -INFINITY) && !(zd < rtau[r0 + G + 1 + i]);
+      if (!supp_d) flags |= 8;
+      if (supp_t && supp_d && okt && okd) {
+        const double k2 = (double)a.k2;
+        const double l2p = (double)zt * k2 - ((double)ot + lt);
+        const double l2q = (double)zd * k2 - ((double)od + ld);
+        accept = (double)u <= exp2(fmin(0.0, l2p - l2q));
+      }
+    }
+    if (!accept) atomicMin(&s_j, i);
+  }
+  for (int jr = tid; jr < rps; jr += NT)
+    if (rtau[r0 + jr] != rtau[r0 + jr]) flags |= 16;  // a selection that did not complete
+  const float us = a.u_sample[b];
+  if (tid == 0) {
+    float o;
+    double l;
+    if (!rstat(r0 + G, o, l)) flags |= 2;  // target row G: the bonus distribution
+    if (!(us >= 0.0f && us < 1.0f)) flags |= 4;
+  }
+  flags = wave_or(flags);
+  if (lane == 0 && flags) atomicOr(&s_flags, flags);
+  __syncthreads();
+  const int j = s_j;
+  const unsigned fl = s_flags;
+  const int err = (fl & 16) ? SV_ROW_INTERNAL
+                : (fl & 1) ? SV_ROW_BAD_TOKEN
+                : (fl & 2) ? SV_ROW_BAD_LOGITS
+                : (fl & 4) ? SV_ROW_BAD_UNIFORM
+                : (fl & 8) ? SV_ROW_Q_ZERO : 0;
+  if (a.row_stats) {
+    for (int jr = tid; jr < rps; jr += NT) {
+      const uint4 v = rowp[r0 + jr];
+      a.row_stats[(r0 + jr) * 2 + 0] = (float)((double)__uint_as_float(v.x) * LN2);
+      a.row_stats[(r0 + jr) * 2 + 1] = (float)d_join(__uint_as_float(v.y), __uint_as_float(v.z));
+    }
+  }
+  if (err) {
+    for (int i = tid; i <= G; i += NT) out[i] = -1;
+    if (tid == 0) a.accepted_len[b] = err;
+    return;
+  }
+  for (int i = tid; i <= G; i += NT)
+    if (i != j) out[i] = (i < j) ? a.tokens[(size_t)b * G + i] : -1;
+
+  // The draw at j (a rejection) or G (the bonus).
+  const bool rej = j < G;
+  const size_t rt = r0 + j, rd = r0 + G + 1 + j;
+  float ot, od = 0.0f;
+  double lt, ld = 0.0;
+  rstat(rt, ot, lt);
+  if (rej) rstat(rd, od, ld);
+  const double mt = (double)ot + lt, md = (double)od + ld;
+  ResidualW rw;
+  rw.k2 = a.k2;
+  rw.mt_hi = d_head(mt);
+  rw.mt_lo = d_tail(mt);
+  rw.dm = rej ? (float)(md - mt) : 0.0f;
+  rw.tau_t = rtau[rt];
+  rw.tau_d = rej ? rtau[rd] : -INFINITY;
+  rw.off_j = ot;
+  const KeptW pw{a.k2, rw.mt_hi, rw.mt_lo, rw.tau_t};
+  const T *row_t = seq_row<T>(a, b, j);
+  const T *row_d = rej ? seq_row<T>(a, b, G + 1 + j) : (const T *)nullptr;
+  const unsigned n = rowp[rt].w;
+  if (n != KEEP_NONE && n <= (unsigned)cap) {
+    const uint2 *kl = a.w.tk_keep + rt * (size_t)cap;
+    for (unsigned e = tid; e < n; e += NT) {
+      const uint2 kv = kl[e];
+      const float zt = __uint_as_float(kv.y);
+      float w;
+      if (rej) {
+        const bool in = kv.x < (unsigned)a.V;  // the list is workspace data: never index past the row
+        const float zd = in ? Fmt<T>::at(row_d, (size_t)kv.x) : -INFINITY;
+        w = in ? rw(zt, zd) : 0.0f;
+      } else {
+        w = (kv.x < (unsigned)a.V) ? pw(zt, 0.0f) : 0.0f;
+      }
+      s_w[e] = w;
+    }
+    __syncthreads();
+    if (wid != 0) return;
+    auto wm = [&](int i) { return (double)s_w[i]; };
+    double trem, Z;
+    int pk = wave_pick4_frac((int)n, (double)us, wm, &trem, &Z);
+    if (rej && !(Z > 0.0)) {  // zero residual: draw from p_j
+      for (unsigned e = lane; e < n; e += WAVE) {
+        const uint2 kv = kl[e];
+        s_w[e] = (kv.x < (unsigned)a.V) ? pw(__uint_as_float(kv.y), 0.0f) : 0.0f;
+      }
+      lds_sync();
+      pk = wave_pick4_frac((int)n, (double)us, wm, &trem, &Z);
+    }
+    const int tok = (pk >= 0) ? (int)kl[pk].x : -1;
+    if (lane == 0) {
+      out[j] = tok;
+      a.accepted_len[b] = j;
+    }
+    return;
+  }
+  // No list: the workgroup streams the rows at j.
+  double Z = 0.0;
+  int tok;
+  if (rej) {
+    tok = block_row_draw<T, ALIGNED, true>(a, row_t, row_d, rw, us, s_seg, s_ctot, &Z);
+    if (!(Z > 0.0)) tok = block_row_draw<T, ALIGNED, false>(a, row_t, (const T *)nullptr, pw, us, s_seg, s_ctot, &Z);
+  } else {
+    tok = block_row_draw<T, ALIGNED, false>(a, row_t, (const T *)nullptr, pw, us, s_seg, s_ctot, &Z);
+  }
+  if (tid == 0) {
+    out[j] = tok;
+    a.accepted_len[b] = j;
+  }
+}
+
 }  // namespace sv
 
 // ======================================================================== host side
@@ -1074,7 +1297,7 @@ bool make_plan(int32_t B, int32_t G, int32_t V, sv_dtype dt, float T, int32_t to
   p.tw_hist = o; o = align256(o + (p.topk ? sv_host::topk_words(p.R, p.C, top_k) * 8 : 0));
   p.zero_bytes = o;
   p.row_tau = o; o = align256(o + (p.topk ? R * 4 : 0));
-  p.tk_state = o; o = align256(o + (p.topk ? sv_host::topk_state_bytes(p.R, p.C, top_k, G > 0) : 0));
+  p.tk_state = o; o = align256(o + (p.topk ? sv_host::topk_state_bytes(p.R, p.C, top_k, true) : 0));
   p.total = o;
   return true;
 }
@@ -1084,7 +1307,7 @@ const char *kPlanNames[] = {
     "k_topk_digit;k_topk_digit;k_topk_digit;k_topk_digit;k_verify",
     "k_verify",
     "k_argmax",
-    "k_topk_select;k_topk_merge;k_verify",
+    "k_topk_select;k_topk_merge;k_topk_verify",
 };
 
 template <typename T, bool AL>
@@ -1107,9 +1330,16 @@ hipError_t launch_all(const Plan &p, const Args &a, hipStream_t st, void *const 
     if (p.topk) {
       sv_host::launch_topk<T, AL>(L, aa, topk_grid, p.C);
       aa.tag = next_tag();
-      void *args[] = {&aa};
-      go(a.G == 0 ? (const void *)&k_verify<T, AL, true, true> : (const void *)&k_verify<T, AL, true, false>,
-         verify_grid, args);
+      if (sv_host::topk_one_pass(a.top_k, p.C)) {
+        // the merge left every row's normaliser and kept list: one workgroup per sequence
+        int cap = sv_host::topk_cap(a.top_k);
+        void *args[] = {&aa, &cap};
+        go((const void *)&k_topk_verify<T, AL>, (unsigned)a.B, args);
+      } else {
+        void *args[] = {&aa};
+        go(a.G == 0 ? (const void *)&k_verify<T, AL, true, true> : (const void *)&k_verify<T, AL, true, false>,
+           verify_grid, args);
+      }
     } else {
       aa.tag = next_tag();
       void *args[] = {&aa};
@@ -1188,10 +1418,10 @@ sv_status run(const void *target, const void *draft, sv_dtype dt, const int32_t 
   a.w.tw_ov = nullptr;
   a.w.row_tau = (float *)(base + p.row_tau);
   a.w.tk_state = (uint2 *)(base + p.tk_state);
-  // the first pass takes its chunk partials from the one-pass top-k threshold when it can
-  a.w.tk_part = (p.topk && G > 0 && sv_host::topk_one_pass(top_k, p.C))
-                    ? (uint4 *)(base + p.tk_state + sv_host::topk_list_bytes(p.R, p.C, top_k))
-                    : nullptr;
+  // after the one-pass top-k threshold: each row's kept-set normaliser and kept list
+  const bool one_pass = p.topk && sv_host::topk_one_pass(top_k, p.C);
+  a.w.tk_rowp = one_pass ? (uint4 *)(base + p.tk_state + sv_host::topk_rowp_offset(p.R, p.C, top_k)) : nullptr;
+  a.w.tk_keep = one_pass ? (uint2 *)(base + p.tk_state + sv_host::topk_keep_offset(p.R, p.C, top_k)) : nullptr;
 
   hipStream_t st = (hipStream_t)stream;
   int n = 0;

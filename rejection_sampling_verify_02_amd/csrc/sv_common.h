@@ -27,8 +27,10 @@ struct Work {                  // carved from the caller's workspace
   float *row_tau;              // [R] top-k threshold (raw logit)
   uint2 *tk_state;             // [R] radix-select prefix and remaining rank, or the one-pass
                                //   select's chunk lists (see k_topk_select)
-  uint4 *tk_part;              // [R*C] or null: the one-pass select's chunk normaliser
-                               //   partials for the verification (see k_topk_merge)
+  uint4 *tk_rowp;              // [R] or null: per row after the one-pass select, the kept
+                               //   set's normaliser (offset, sum head, tail) and the length
+                               //   of its index-ordered list, or KEEP_NONE (see k_topk_merge)
+  uint2 *tk_keep;              // [R*cap] the kept (index, logit bits) of each row, in index order
 };
 
 struct Args {
@@ -189,6 +191,11 @@ constexpr int TOPK_SELECT_MAX = 256;    // largest k of the one-pass select
 constexpr int TOPK_SELECT_MAX_C = 256;   // most chunks per row of the one-pass select
 constexpr int TOPK_LDS_KEYS = 1024;      // a chunk's list (at most cap <= 1024 keys), and the
                                          // collector's keys while they fit (else read again)
+constexpr unsigned KEEP_NONE = 0xffffffffu;  // a row whose kept set has no list (see k_topk_merge)
+
+// 32-bit words of one chunk's list: count, flags, cap keys, cap 16-bit indices (cap is a
+// multiple of 4, so every list stays 8-byte aligned).
+SV_HD size_t topk_list_words(int cap) { return (size_t)cap + 2 + (size_t)cap / 2; }
 
 // Inclusive scan of unsigned values over the wave (DPP).
 SVD unsigned scan_add_u(unsigned x) {
@@ -295,9 +302,11 @@ SVD uint32_t wave_kth_largest(uint32_t v, int q, int low) {
 // only when the bound is -inf, and a -inf can move a k-th largest only when that is -inf
 // already; their terms are 0.  A list is incomplete (*incomplete) when it comes from the
 // exact select: it then holds the values above the chunk's k-th largest and copies of it.
+// A complete list also leaves each key's element index within the chunk in s_idx.
 template <typename T>
-SVD unsigned topk_chunk_list(u32x4 (&w)[VPT], int k, int cap, unsigned *s_keys, bool *incomplete,
-                             unsigned *s_hist, unsigned *s_ge, unsigned *s_wv, unsigned *s_pick) {
+SVD unsigned topk_chunk_list(u32x4 (&w)[VPT], int k, int cap, unsigned *s_keys, uint16_t *s_idx,
+                             bool *incomplete, unsigned *s_hist, unsigned *s_ge, unsigned *s_wv,
+                             unsigned *s_pick) {
   constexpr int VEC = Fmt<T>::VEC;
   constexpr int NPASS = (sizeof(T) == 2) ? 2 : 4;
   const int tid = threadIdx.x, lane = lane_id(), wid = tid / WAVE;
@@ -362,7 +371,10 @@ SVD unsigned topk_chunk_list(u32x4 (&w)[VPT], int k, int cap, unsigned *s_keys, 
 #pragma unroll
       for (int e = 0; e < VEC; ++e)
         if (!(f[e] < lbf)) {
-          if (pos < (unsigned)cap) s_keys[pos] = f2key(f[e]) & KMASK;
+          if (pos < (unsigned)cap) {
+            s_keys[pos] = f2key(f[e]) & KMASK;
+            s_idx[pos] = (uint16_t)((kk * NT + tid) * VEC + e);
+          }
           ++pos;
         }
     }
@@ -413,6 +425,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(7))) void k_
   constexpr int VEC = Fmt<T>::VEC;
   __shared__ unsigned s_hist[256], s_ge[256], s_wv[NW], s_pick[2];
   __shared__ unsigned s_keys[TOPK_LDS_KEYS];
+  __shared__ uint16_t s_idx[TOPK_LDS_KEYS];
   const int tid = threadIdx.x;
   int phase, xi;
   if (!lane_item((int)(a.B * a.rps), a.C, 0, phase, xi)) return;  // units: rows
@@ -462,118 +475,19 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(7))) void k_
     }
   }
   bool incomplete;
-  const unsigned own_n = topk_chunk_list<T>(w, k, cap, s_keys, &incomplete, s_hist, s_ge, s_wv, s_pick);
+  const unsigned own_n = topk_chunk_list<T>(w, k, cap, s_keys, s_idx, &incomplete, s_hist, s_ge, s_wv, s_pick);
   // The list goes to the workspace as plain data for k_topk_merge: the count, the flags
-  // (2: the list is incomplete), then the keys.
-  uint32_t *lw = reinterpret_cast<uint32_t *>(a.w.tk_state) + ((size_t)r * a.C + c) * ((size_t)cap + 2);
+  // (2: the list is incomplete), the keys, then (complete lists) the 16-bit element
+  // indices within the chunk.
+  uint32_t *lw = reinterpret_cast<uint32_t *>(a.w.tk_state) + ((size_t)r * a.C + c) * topk_list_words(cap);
   for (unsigned i = tid; i < own_n; i += NT) lw[2 + i] = s_keys[i];
+  if (!incomplete) {
+    uint16_t *li = reinterpret_cast<uint16_t *>(lw + 2 + cap);
+    for (unsigned i = tid; i < own_n; i += NT) li[i] = s_idx[i];
+  }
   if (tid == 0) {
     lw[0] = own_n;
     lw[1] = incomplete ? 2u : 0u;
-  }
-}
-
-// The row threshold of the one-pass select (one workgroup per row, after k_topk_select):
-// the k-th largest key of the union of the row's chunk lists, staged in LDS when they fit
-// (else read again by each radix pass).
-template <typename T>
-__global__ __launch_bounds__(NT) void k_topk_merge(const Args a, int cap) {
-  constexpr int NPASS = (sizeof(T) == 2) ? 2 : 4;
-  __shared__ unsigned s_hist[256], s_ge[256], s_w[NW], s_pick[2];
-  __shared__ unsigned s_keys[TOPK_LDS_KEYS];
-  __shared__ unsigned s_coff[TOPK_SELECT_MAX_C + 1];
-  const int tid = threadIdx.x;
-  const long long r = blockIdx.x;
-  if (r >= (long long)a.B * a.rps) return;
-  const int k = a.top_k, C = a.C;
-  const size_t W = (size_t)cap + 2;
-  const uint32_t *rl = reinterpret_cast<const uint32_t *>(a.w.tk_state) + (size_t)r * C * W;
-  unsigned total = 0;
-  for (int c0 = 0; c0 < C; c0 += NT) {
-    const int cc = c0 + tid;
-    unsigned nc = (cc < C) ? rl[(size_t)cc * W] : 0u;
-    nc = (nc <= (unsigned)cap) ? nc : 0u;  // never trust a count beyond the chunk's words
-    unsigned tot;
-    const unsigned before = block_excl_scan(nc, s_w, tot);
-    if (cc < C) s_coff[cc] = total + before;
-    total += tot;
-  }
-  if (tid == 0) s_coff[C] = total;
-  __syncthreads();
-  // key g: its chunk is the last one whose first index is <= g
-  auto key_at = [&](unsigned g) -> uint32_t {
-    int lo = 0, hi = C - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_coff[mid] <= g) lo = mid;
-      else hi = mid - 1;
-    }
-    return rl[(size_t)lo * W + 2 + (g - s_coff[lo])];
-  };
-  const bool in_lds = total <= (unsigned)TOPK_LDS_KEYS;
-  if (in_lds)
-    for (unsigned g = tid; g < total; g += NT) s_keys[g] = key_at(g);
-  __syncthreads();
-  if (total < (unsigned)k) {  // cannot happen with a complete select pass
-    if (tid == 0) a.w.row_tau[r] = NAN;
-    return;
-  }
-  auto each = [&](auto f) {
-    for (unsigned g = tid; g < total; g += NT) f(in_lds ? s_keys[g] : key_at(g));
-  };
-  const uint32_t tk = block_kth_largest(k, NPASS, each, s_hist, s_ge, s_pick);
-  if (tid == 0) a.w.row_tau[r] = tau_of_key(tk);
-  if (!a.w.tk_part) return;
-
-  // The verification's chunk partials, as its first pass would form them with this
-  // threshold: m = the largest kept value (kept: not below the threshold, i.e. key >= tk),
-  // off = m*k2, S = sum over kept values of 2^(z*k2 - off) (in double here), or off = -inf
-  // and S = 0 with nothing finite kept; S is NaN when the chunk holds a NaN (a complete list
-  // holds all of them) or a +inf is kept.  A complete list holds every value at or above
-  // the threshold; a chunk whose list is incomplete gets no partial and its first-pass item
-  // reads the chunk.  One wave a chunk.
-  const int lane = lane_id(), wid = tid / WAVE;
-  for (int cc = wid; cc < C; cc += NW) {
-    const uint32_t *cl = rl + (size_t)cc * W;
-    const unsigned n = s_coff[cc + 1] - s_coff[cc], fl = cl[1];
-    // the chunk's keys: staged in LDS, or in the workspace
-    auto kat = [&](unsigned i) -> uint32_t { return in_lds ? s_keys[s_coff[cc] + i] : cl[2 + i]; };
-    uint4 out = make_uint4(0u, 0u, 0u, 0u);
-    if (!(fl & 2u)) {
-      auto val = [&](uint32_t key) -> float {  // a bf16 key keeps its upper half only
-        if (sizeof(T) == 2 && !(key & 0x80000000u)) key |= 0xffffu;
-        return key2f(key);
-      };
-      // keys above +inf's or below -inf's are NaNs (for bf16 as masked keys)
-      constexpr uint32_t KPINF = (sizeof(T) == 2) ? 0xff800000u : 0xff800000u;
-      constexpr uint32_t KNINF = (sizeof(T) == 2) ? 0x007f0000u : 0x007fffffu;
-      float m = -INFINITY;
-      unsigned nanl = 0;
-      for (unsigned i = lane; i < n; i += WAVE) {
-        const uint32_t key = kat(i);
-        nanl |= (key > KPINF || key < KNINF) ? 1u : 0u;
-        if (key >= tk) m = fmaxf(m, val(key));
-      }
-      m = wave_max(m);
-      const bool has_nan = wave_or(nanl) != 0u;
-      float off;
-      double S;
-      if (m > -INFINITY) {
-        off = m * a.k2;
-        double acc = 0.0;
-        for (unsigned i = lane; i < n; i += WAVE) {
-          const uint32_t key = kat(i);
-          if (key >= tk) acc += (double)fast_exp2(fmaf(val(key), a.k2, -off));
-        }
-        S = wave_sum(acc);
-      } else {
-        off = -INFINITY;
-        S = 0.0;
-      }
-      if (has_nan || m == INFINITY) S = NAN;
-      out = make_uint4(__float_as_uint(off), __float_as_uint(d_head(S)), __float_as_uint(d_tail(S)), 1u);
-    }
-    if (lane == 0) a.w.tk_part[(size_t)r * C + cc] = out;
   }
 }
 
@@ -641,6 +555,218 @@ SVD void chunk_norm(const T *row, int V, int nvec, int c, float tau, float k2, f
   S = (s_s[0] + s_s[1]) + (s_s[2] + s_s[3]);
 }
 
+// ---------------------------------------------------------------- top-k row merge
+
+// The row threshold of the one-pass select (one workgroup per row, after k_topk_select):
+// tau = the k-th largest key of the union of the row's chunk lists, staged in LDS when
+// they fit (else read again by each radix pass).  Every value at or above tau lies in
+// those lists: a chunk lists every value not below its own bound, and k of its values
+// lie at or above that bound, so tau is not below it.
+//
+// With tk_rowp (the verification after the threshold) the kept set of the row, {z >= tau,
+// z > -inf}, is summarised too: the offset off = m*k2 of its largest value m and
+// S = sum 2^(z*k2 - off), so the row's log2-partition is off + log2(S) ("推测解码：接受
+// 规则、状态与收益边界", section "两模型精确采样": each distribution is renormalised over
+// what it keeps).  When every chunk's list is complete and at most cap values are kept,
+// the kept (index, logit) pairs go to tk_keep in index order and S is summed in that
+// order; otherwise (heavy ties) the row is streamed again, chunk by chunk, and the row
+// has no list (KEEP_NONE).  S is NaN when the row holds a NaN or keeps a +inf; with
+// nothing finite kept, off = -inf and S = 0.
+template <typename T, bool ALIGNED>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(7))) void k_topk_merge(const Args a, int cap) {
+  constexpr int NPASS = (sizeof(T) == 2) ? 2 : 4;
+  constexpr long CE = (long)CHUNK_VECS * Fmt<T>::VEC;  // values per chunk
+  __shared__ unsigned s_hist[256], s_ge[256], s_w[NW], s_pick[2];
+  __shared__ unsigned s_keys[TOPK_LDS_KEYS], s_gidx[TOPK_LDS_KEYS];
+  __shared__ unsigned s_coff[TOPK_SELECT_MAX_C + 1];
+  __shared__ unsigned s_incomplete, s_nk;
+  const int tid = threadIdx.x, lane = lane_id(), wid = tid / WAVE;
+  const long long r = blockIdx.x;
+  if (r >= (long long)a.B * a.rps) return;
+  const int k = a.top_k, C = a.C;
+  const size_t W = topk_list_words(cap);
+  const uint32_t *rl = reinterpret_cast<const uint32_t *>(a.w.tk_state) + (size_t)r * C * W;
+  if (tid == 0) {
+    s_incomplete = 0u;
+    s_nk = 0u;
+  }
+  unsigned total = 0;
+  for (int c0 = 0; c0 < C; c0 += NT) {
+    const int cc = c0 + tid;
+    unsigned nc = (cc < C) ? rl[(size_t)cc * W] : 0u;
+    nc = (nc <= (unsigned)cap) ? nc : 0u;  // never trust a count beyond the chunk's words
+    if (cc < C && (rl[(size_t)cc * W + 1] & 2u)) s_incomplete = 1u;
+    unsigned tot;
+    const unsigned before = block_excl_scan(nc, s_w, tot);
+    if (cc < C) s_coff[cc] = total + before;
+    total += tot;
+  }
+  if (tid == 0) s_coff[C] = total;
+  __syncthreads();
+  const bool complete = s_incomplete == 0u;
+  // candidate g: its chunk is the last one whose first candidate is <= g; its row index
+  // (complete lists only) is the chunk's first index plus the listed offset
+  auto cand = [&](unsigned g, unsigned &gi) -> uint32_t {
+    int lo = 0, hi = C - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_coff[mid] <= g) lo = mid;
+      else hi = mid - 1;
+    }
+    const uint32_t *cl = rl + (size_t)lo * W;
+    const unsigned i = g - s_coff[lo];
+    gi = complete ? (unsigned)(lo * CE) + reinterpret_cast<const uint16_t *>(cl + 2 + cap)[i] : 0u;
+    return cl[2 + i];
+  };
+  const bool in_lds = total <= (unsigned)TOPK_LDS_KEYS;
+  if (in_lds)
+    for (unsigned g = tid; g < total; g += NT) s_keys[g] = cand(g, s_gidx[g]);
+  __syncthreads();
+  uint4 *rowp = a.w.tk_rowp;
+  if (total < (unsigned)k) {  // cannot happen with a complete select pass
+    if (tid == 0) {
+      a.w.row_tau[r] = NAN;
+      if (rowp) rowp[r] = make_uint4(__float_as_uint(NAN), __float_as_uint(NAN), 0u, KEEP_NONE);
+    }
+    return;
+  }
+  auto each = [&](auto f) {
+    unsigned gi;
+    for (unsigned g = tid; g < total; g += NT) f(in_lds ? s_keys[g] : cand(g, gi));
+  };
+  const uint32_t tk = block_kth_largest(k, NPASS, each, s_hist, s_ge, s_pick);
+  const float tau = tau_of_key(tk);
+  if (tid == 0) a.w.row_tau[r] = tau;
+  if (!rowp) return;
+
+  // The kept values among the candidates, compacted (the first cap of them) in any order:
+  // one LDS atomic per wave reserves its range.
+  auto val = [&](uint32_t key) -> float {  // a bf16 key keeps its upper half only
+    if (sizeof(T) == 2 && !(key & 0x80000000u)) key |= 0xffffu;
+    return key2f(key);
+  };
+  // keys above +inf's or below -inf's are NaNs (for bf16 as masked keys)
+  constexpr uint32_t KPINF = 0xff800000u;
+  constexpr uint32_t KNINF = (sizeof(T) == 2) ? 0x007f0000u : 0x007fffffu;
+  __shared__ float s_kz[TOPK_LDS_KEYS];
+  __shared__ unsigned s_kidx[TOPK_LDS_KEYS];
+  __shared__ float s_rm[NW];
+  __shared__ unsigned s_rn[NW];
+  unsigned nanl = 0;
+  float m = -INFINITY;
+  for (unsigned g = tid; g < total; g += NT) {  // lane 0 is active whenever any lane is
+    unsigned gi;
+    uint32_t key;
+    if (in_lds) {
+      key = s_keys[g];
+      gi = s_gidx[g];
+    } else {
+      key = cand(g, gi);
+    }
+    const bool isnan_k = key > KPINF || key < KNINF;
+    nanl |= isnan_k ? 1u : 0u;
+    const float v = val(key);
+    const bool kept = !isnan_k && key >= tk && v > -INFINITY;
+    if (kept) m = fmaxf(m, v);
+    const unsigned long long bal = __ballot(kept);
+    unsigned base = 0;
+    if (lane == 0 && bal) base = atomicAdd(&s_nk, (unsigned)__popcll(bal));
+    const unsigned pos = (unsigned)__builtin_amdgcn_readlane((int)base, 0) +
+                         (unsigned)__popcll(bal & ((1ull << lane) - 1ull));
+    if (kept && pos < (unsigned)cap) {
+      s_kidx[pos] = gi;
+      s_kz[pos] = v;
+    }
+  }
+  m = wave_max(m);
+  nanl = wave_or(nanl);
+  if (lane == 0) {
+    s_rm[wid] = m;
+    s_rn[wid] = nanl;
+  }
+  __syncthreads();
+  m = fmaxf(fmaxf(s_rm[0], s_rm[1]), fmaxf(s_rm[2], s_rm[3]));
+  const bool has_nan = (s_rn[0] | s_rn[1] | s_rn[2] | s_rn[3]) != 0u;
+  const unsigned nkeep = s_nk;
+
+  const float k2 = a.k2;
+  float off;
+  double S;
+  unsigned count;
+  if (complete && nkeep <= (unsigned)cap) {
+    // Index order: an entry's rank is the number of kept entries with a smaller index
+    // (indices are distinct).  The sorted logits reuse s_keys.
+    float *s_sz = reinterpret_cast<float *>(s_keys);
+    uint2 *kl = a.w.tk_keep + (size_t)r * cap;
+    for (unsigned e = tid; e < nkeep; e += NT) {
+      const unsigned ie = s_kidx[e];
+      unsigned rank = 0;
+      for (unsigned f = 0; f < nkeep; ++f) rank += (s_kidx[f] < ie) ? 1u : 0u;
+      kl[rank] = make_uint2(ie, __float_as_uint(s_kz[e]));
+      s_sz[rank] = s_kz[e];
+    }
+    __syncthreads();
+    if (wid != 0) return;  // one wave sums, lane l taking entries l, l + 64, ... in order
+    off = (m > -INFINITY) ? m * k2 : -INFINITY;
+    double acc = 0.0;
+    if (m > -INFINITY)
+      for (unsigned e = lane; e < nkeep; e += WAVE) acc += (double)fast_exp2(fmaf(s_sz[e], k2, -off));
+    S = wave_sum(acc);
+    if (has_nan || m == INFINITY) S = NAN;
+    count = nkeep;
+  } else {
+    // Heavy ties: the kept set's normaliser from the row itself, in two passes of one
+    // vector per thread at a time (the largest kept value, then the sum with its offset;
+    // each thread's values in order, the threads by a fixed tree).
+    const int b = (int)(r / a.rps), jr = (int)(r - (long long)b * a.rps);
+    const T *row = seq_row<T>(a, b, jr);
+    constexpr int VEC = Fmt<T>::VEC;
+    float mr = -INFINITY;
+    unsigned nan = 0;
+    for (int c = 0; c < C; ++c)
+      for (int kk = 0; kk < VPT; ++kk) {
+        float x[1][VEC];
+        load_vectors<T, ALIGNED, false, 1>(row, a.V, a.nvec, c, kk, tid, x);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          nan |= (x[0][e] != x[0][e]) ? 1u : 0u;
+          if (!(x[0][e] < tau)) mr = fmaxf(mr, x[0][e]);
+        }
+      }
+    mr = wave_max(mr);
+    nan = wave_or(nan);
+    __syncthreads();  // the s_rm, s_rn values above have been read by every wave
+    if (lane == 0) {
+      s_rm[wid] = mr;
+      s_rn[wid] = nan;
+    }
+    __syncthreads();
+    mr = fmaxf(fmaxf(s_rm[0], s_rm[1]), fmaxf(s_rm[2], s_rm[3]));
+    const bool row_nan = (s_rn[0] | s_rn[1] | s_rn[2] | s_rn[3]) != 0u;
+    off = (mr > -INFINITY) ? mr * k2 : -INFINITY;
+    double acc = 0.0;
+    if (mr > -INFINITY)
+      for (int c = 0; c < C; ++c)
+        for (int kk = 0; kk < VPT; ++kk) {
+          float x[1][VEC];
+          load_vectors<T, ALIGNED, false, 1>(row, a.V, a.nvec, c, kk, tid, x);
+          float t = 0.0f;
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) t += fast_exp2(fmaf((x[0][e] < tau) ? -INFINITY : x[0][e], k2, -off));
+          acc += (double)t;
+        }
+    acc = wave_sum(acc);
+    __shared__ double s_rs[NW];
+    if (lane == 0) s_rs[wid] = acc;
+    __syncthreads();
+    S = (s_rs[0] + s_rs[1]) + (s_rs[2] + s_rs[3]);
+    if (row_nan || mr == INFINITY) S = NAN;
+    else if (!(mr > -INFINITY)) S = 0.0;  // nothing finite kept
+    count = KEEP_NONE;
+  }
+  if (tid == 0) rowp[r] = make_uint4(__float_as_uint(off), __float_as_uint(d_head(S)), __float_as_uint(d_tail(S)), count);
+}
+
 }  // namespace sv
 
 // ---------------------------------------------------------------- host helpers
@@ -689,14 +815,20 @@ inline size_t topk_words(long long R, int C, int top_k) {
   return topk_one_pass(top_k, C) ? 0 : (size_t)R * (size_t)C * 128;
 }
 // Bytes of the plain tk_state region: the chunk lists of the one-pass select, or the
-// digit passes' (prefix, rank) per row.
-// With parts, room for the verification's chunk partials follows the lists.
+// digit passes' (prefix, rank) per row.  With keep (the verification), each row's kept-set
+// summary (16 bytes) and its kept list (cap entries of 8 bytes) follow the lists.
 inline size_t topk_list_bytes(long long R, int C, int top_k) {
-  return (size_t)R * (size_t)C * ((size_t)topk_cap(top_k) + 2) * 4;
+  return (size_t)R * (size_t)C * sv::topk_list_words(topk_cap(top_k)) * 4;
 }
-inline size_t topk_state_bytes(long long R, int C, int top_k, bool parts = false) {
+// Offsets (from the region's start, 256-byte aligned) of the kept-set summaries and lists.
+inline size_t topk_rowp_offset(long long R, int C, int top_k) { return align256(topk_list_bytes(R, C, top_k)); }
+inline size_t topk_keep_offset(long long R, int C, int top_k) {
+  return topk_rowp_offset(R, C, top_k) + align256((size_t)R * 16);
+}
+inline size_t topk_state_bytes(long long R, int C, int top_k, bool keep = false) {
   if (!topk_one_pass(top_k, C)) return (size_t)R * 8;
-  return topk_list_bytes(R, C, top_k) + (parts ? (size_t)R * (size_t)C * 16 : 0);
+  if (!keep) return topk_list_bytes(R, C, top_k);
+  return topk_keep_offset(R, C, top_k) + (size_t)R * (size_t)topk_cap(top_k) * 8;
 }
 // Chunks per row (as the kernels cut rows) for a row of V values of esz bytes.
 inline int row_chunks(int V, int esz) {
@@ -711,7 +843,7 @@ void launch_topk(Launcher &L, sv::Args aa, unsigned grid, int C) {
     void *args[] = {&aa, &cap};
     L.go((const void *)&sv::k_topk_select<T, AL>, grid, args);
     aa.tag = next_tag();
-    L.go((const void *)&sv::k_topk_merge<T>, (unsigned)((long long)aa.B * aa.rps), args);
+    L.go((const void *)&sv::k_topk_merge<T, AL>, (unsigned)((long long)aa.B * aa.rps), args);
     return;
   }
   const int passes = (sizeof(T) == 2) ? 2 : 4;

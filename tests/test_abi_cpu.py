@@ -49,8 +49,8 @@ def test_status_strings(lib):
 def test_launch_plan(lib):
     assert sv.sv_launch_plan(64, 4, 128256, sv.SV_BF16, 1.0, 0) == ["k_verify"]
     assert sv.sv_launch_plan(256, 7, 152064, sv.SV_BF16, 0.0, 50) == ["k_argmax"]
-    assert sv.sv_launch_plan(128, 6, 128256, sv.SV_BF16, 0.8, 50) == ["k_topk_select", "k_topk_merge", "k_verify"]
-    assert sv.sv_launch_plan(8, 5, 32000, sv.SV_F32, 0.7, 5) == ["k_topk_select", "k_topk_merge", "k_verify"]
+    assert sv.sv_launch_plan(128, 6, 128256, sv.SV_BF16, 0.8, 50) == ["k_topk_select", "k_topk_merge", "k_topk_verify"]
+    assert sv.sv_launch_plan(8, 5, 32000, sv.SV_F32, 0.7, 5) == ["k_topk_select", "k_topk_merge", "k_topk_verify"]
     # k above the one-pass select's limit: the radix digit passes (2 for bf16, 4 for f32)
     assert sv.sv_launch_plan(128, 6, 128256, sv.SV_BF16, 0.8, 257) == \
         ["k_topk_digit", "k_topk_digit", "k_verify"]

@@ -344,6 +344,58 @@ def test_zero_residual_fallback(dev, dtype, V):
     assert res.exact >= res.n - max(1, res.n // 100)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_zero_residual_fallback_topk(dev, dtype):
+    """The zero-residual rows under a top-k of 50, with 30 finite logits a row besides the
+    drafted token (identical in target and draft): the k-th largest is -inf, so every finite
+    logit is kept and listed, the residual over the kept list has no mass, and the correction
+    is drawn from p_j over the same list.  Even sequences accept position 0 (u = 0)."""
+    B, G, V = 32, 3, 40000
+    raw = wl.make_zero_residual(B, G, V, dtype, seed=V + 9)
+    raw.u_accept[::2, 0] = 0.0
+    rng = np.random.default_rng(V + 10)
+    ninf = wl.bf16_bits(np.array([-np.inf], np.float32))[0] if dtype == "bf16" else np.float32(-np.inf)
+    tok = raw.fixed_tokens
+    for b in range(B):
+        for g in range(G + 1):
+            keep = rng.choice(V, 30, replace=False)
+            if g < G:
+                keep = np.append(keep, tok[b, g])
+            mask = np.ones(V, bool)
+            mask[keep] = False
+            raw.target[b, g, mask] = ninf
+            if g < G:
+                raw.draft[b, g, mask] = ninf
+    res, gpu, ref = parity.run_both(raw, 1.0, 50, dev, tokens=tok)
+    check(res, f"zero residual top-k {dtype}")
+    expect = np.where(np.arange(B) % 2 == 0, 1, 0)
+    np.testing.assert_array_equal(gpu[0], expect)
+    assert res.exact >= res.n - max(1, res.n // 100)
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 40000), ("f32", 30001)])
+def test_topk_ties_exceed_kept_list(dev, dtype, V):
+    """300 values tied at the top of every row, spread over its chunks (five larger ones in
+    half the rows), k = 20: each chunk lists its share completely, but the row keeps more
+    values than its list holds (4k = 128), so the merge streams the row for its normaliser
+    and the draws stream their rows.  Target and draft tie at different places, so most
+    positions reject."""
+    B, G, k = 8, 3, 20
+    raw = wl.make_random(B, G, V, dtype, seed=V + 3)
+    rng = np.random.default_rng(V + 4)
+    for arr in (raw.target, raw.draft):
+        flat = arr.reshape(-1, V)
+        for r in range(flat.shape[0]):
+            vals = np.full(300, 9.0, np.float32)
+            if r % 2 == 0:
+                vals = np.concatenate([vals, 9.5 + np.arange(5, dtype=np.float32) / 4])
+            idx = rng.choice(V, vals.size, replace=False)
+            flat[r, idx] = wl.bf16_bits(vals) if dtype == "bf16" else vals
+    res, gpu, _ = parity.run_both(raw, 1.0, k, dev)
+    check(res, f"ties beyond the kept list {dtype} V={V}")
+    assert np.all(gpu[0] >= 0)
+
+
 def forced_rejections(raw, T, seed):
     """Tokens and uniforms that make sequence b reject at position j = b mod G: positions
     before j carry a token drawn from q and u = 0 (accepted, p(x) > 0 everywhere here);
