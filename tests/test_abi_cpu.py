@@ -214,8 +214,8 @@ def test_tree_optional_pointers_and_plan(lib):
     assert call_tree(lib, path=None, nbytes=16) == 5
     assert call_tree(lib, T=0.0, d=None, ua=None, us=None, nbytes=16) == 5
     assert sv.sv_tree_launch_plan(16, 32, 128256, 4, sv.SV_BF16, 1.0, 0) == \
-        ["k_tree_rows", "k_tree_resid", "k_tree_walk", "k_tree_draw"]
-    assert sv.sv_tree_launch_plan(16, 32, 128256, 1, sv.SV_BF16, 1.0, 0) == ["k_tree_rows", "k_tree_walk", "k_tree_draw"]
+        ["k_tree_rows", "k_tree_resid", "k_tree_draw"]
+    assert sv.sv_tree_launch_plan(16, 32, 128256, 1, sv.SV_BF16, 1.0, 0) == ["k_tree_rows", "k_tree_draw"]
     assert sv.sv_tree_launch_plan(16, 32, 128256, 4, sv.SV_BF16, 0.0, 0) == ["k_tree_rows", "k_tree_walk"]
     assert sv.sv_tree_launch_plan(16, 32, 128256, 4, sv.SV_F32, 0.7, 5)[:3] == ["k_topk_select", "k_topk_merge", "k_tree_rows"]
     assert sv.sv_tree_launch_plan(16, 32, 128256, 4, sv.SV_F32, 0.7, 300)[:4] == ["k_topk_digit"] * 4
