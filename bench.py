@@ -39,15 +39,26 @@ _SHARED = ("sv_common.h", "sv_device.h", "sv_lanes.h")
 # (by hash: a summary taken on other sources is not used).
 COUNTED = {
     "verify": dict(kernel="k_verify", workload="zipf_bf16_b64", desc="B=64, G=4, V=128256, bf16",
-                   alg=147750912, sources=("spec_verify.hip",) + _SHARED),
+                   alg=147750912, sources=("spec_verify.hip", "sv_draw.h") + _SHARED,
+                   why="The excess is the second read of the two rows at each rejecting sequence's first "
+                       "rejection (2 x 256.5 KB each; most sequences of this workload reject), plus the bonus "
+                       "chunk's re-read and the partials, records and segment masses.  Every other logit is "
+                       "fetched from HBM once."),
     "overlap": dict(kernel="k_overlap", workload="overlap_zipf_bf16_b64", desc="B=64, G=4, V=128256, bf16",
-                    alg=131334144, sources=("spec_overlap.hip",) + _SHARED),
+                    alg=131334144, sources=("spec_overlap.hip",) + _SHARED,
+                    why="Every logit is read twice, first for the normalisers and then for the overlap terms; "
+                        "the excess is the part of the second read that misses the XCD's L2."),
     "sample": dict(kernel="k_verify", workload="sample_bf16_b256", desc="B=256, V=128256, bf16",
-                   alg=65667072, sources=("spec_verify.hip",) + _SHARED),
+                   alg=65667072, sources=("spec_verify.hip", "sv_draw.h") + _SHARED,
+                   why="The excess is each row's one re-read segment (1 KiB) and the partials and segment "
+                       "masses handed between workgroups."),
     "tree": dict(kernel="k_tree_rows", workload="tree_bf16_b16_n32", desc="16 trees of 32 nodes, V=128256, bf16",
-                 alg=210698956, sources=("spec_tree.hip", "sv_draw.h") + _SHARED),
+                 alg=210698956, sources=("spec_tree.hip", "sv_draw.h") + _SHARED,
+                 why="k_tree_rows reads every target row and the draft rows of nodes with children once; the "
+                     "residual rounds and the draw read their rows in launches of their own."),
     "typical": dict(kernel="k_typical", workload="typical_zipf_bf16_b64", desc="B=64, G=4, V=128256, bf16",
-                    alg=82083840, sources=("spec_typical.hip",) + _SHARED),
+                    alg=82083840, sources=("spec_typical.hip",) + _SHARED,
+                    why="Every logit is read once; the excess is the partials handed between workgroups."),
 }
 
 
@@ -234,6 +245,29 @@ def summarize_counters(kdir: str, cdir: str, op: str) -> None:
            "source_sha256": source_sha(op),
            "note": "FETCH_SIZE and WRITE_SIZE from separate rocprofv3 --pmc runs, scaled by a plain copy"}
     counters_path(op).write_text(json.dumps(res, indent=1) + "\n")
+    ratio = (fetch + write) / spec["alg"]
+    md = [f"# HBM traffic of {kernel}, {spec['workload']} ({spec['desc']})", "",
+          "Commands (GPU box, after `cd /tmp && export TMPDIR=/tmp`; each counter in a run of its own):", "", "```"]
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        md.append(f"rocprofv3 --pmc {c} --output-format csv -d <k>/{c} -o k -- python3 <repo>/bench.py --op {op} "
+                  f"--steps 30 --warmup 5 --no-cpu-baseline --no-stage-events --no-probe")
+    md += ["rocprofv3 --pmc FETCH_SIZE --output-format csv -d <c>/fetch -o c -- python3 <repo>/bench.py "
+           "--copy-probe 1073741824 > <c>/probe.json",
+           "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <c>/write -o c -- python3 <repo>/bench.py "
+           "--copy-probe 1073741824",
+           f"python3 bench.py --op {op} --summarize-counters <k> <c>",
+           "```", "",
+           f"Calibration: a {nbytes / 2**30:g} GiB device copy reads FETCH_SIZE = {max(cf):,.1f} KiB and "
+           f"WRITE_SIZE = {max(cw):,.1f} KiB, so FETCH_SIZE is scaled by {f_fetch:.5f} and WRITE_SIZE by {f_write:.5f}.",
+           "",
+           f"| per {kernel} launch (median of {len(kf)} dispatches on the workload's grid) | counter | scaled bytes |",
+           "|---|---|---|",
+           f"| FETCH_SIZE | {float(np.median(kf)):,.1f} KiB | {fetch:,.0f} |",
+           f"| WRITE_SIZE | {float(np.median(kw)):,.1f} KiB | {write:,.0f} |",
+           f"| total traffic | | {fetch + write:,.0f} |",
+           f"| algorithmic bytes (every logit the result depends on, once) | | {spec['alg']:,} |", "",
+           f"Traffic is {ratio:.2f}x the algorithmic bytes.  {spec.get('why', '')}", ""]
+    counters_path(op).with_suffix(".md").write_text("\n".join(md))
     print(json.dumps(res))
 
 
@@ -271,10 +305,11 @@ def summarize_trace(tdir: str, line_file: str, cmd: str, ref_file: str | None = 
     us = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in d]
     ph = line["dispatches"]
     spans, o = [], 0
-    for name in ("warmup", "timed_loops", "per_kernel_events", "flushed", "after"):
+    for name in ("warmup", "timed_loops", "per_kernel_events", "flushed"):
         n = ph.get(name, 0)
         spans.append((name, us[o:o + n]))
         o += n
+    spans.append(("after", us[o:]))  # calls made after the timing (outputs checked)
     alg = rf["algorithmic_bytes"]
     out = [f"# Kernel trace: {kernel}, {line['config']['workload']}", "",
            "Command (repository root on the GPU box, after `cd /tmp && export TMPDIR=/tmp`):", "",
@@ -303,6 +338,22 @@ def summarize_trace(tdir: str, line_file: str, cmd: str, ref_file: str | None = 
                        f"the events, frac {rr['frac']} ({(m / rr['avg_launch_us'] - 1) * 100:+.2f}% from rocprofv3's "
                        f"{m:.3f} us); event-free loop {ref['ms_per_step'] * 1e3:.2f} us per call "
                        f"({ref['value'] / 1e6:.3f} M {ref['unit']}).")
+    others = [k.split(":", 1)[1] for k in line.get("per_kernel_us", {}) if k.split(":", 1)[1] != kernel]
+    if others:
+        out += ["", "The call's other kernels (rocprofv3, every dispatch on each kernel's most frequent grid; "
+                "bench.py's per-dispatch events of the reference run):", "",
+                "| kernel | dispatches | mean (us) | median (us) | events (us) |", "|---|---|---|---|---|"]
+        ref_pk = (_last_line(ref_file) if ref_file else line).get("per_kernel_us", {})
+        for name in others:
+            rs = [r for r in rows if f"{name}<" in r["Kernel_Name"] or r["Kernel_Name"].endswith(name)]
+            if not rs:
+                continue
+            gs = [grid(r) for r in rs]
+            g0 = max(set(gs), key=gs.count)
+            v = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rs if grid(r) == g0]
+            ev_us = next((val for k, val in ref_pk.items() if k.split(":", 1)[1] == name), None)
+            out.append(f"| `{name}` | {len(v)} | {np.mean(v):.3f} | {np.median(v):.3f} | {ev_us} |")
+        out.append("")
     src = _last_line(ref_file) if ref_file else line
     if src.get("read_probe"):
         pr = src["read_probe"]
@@ -395,9 +446,13 @@ def time_loop(call, plan, K, warmup, stream, dev, hev, stage_events, flush_calls
             "wall2": wall2, "cold_us": cold, "calls": n}
 
 
-def timing_fields(t, K):
-    """The timing part of a result line: median loop, all loops, per-kernel durations, flushed latency."""
+def timing_fields(t, K, W):
+    """The timing part of a result line: median loop, all loops, per-kernel durations, flushed
+    latency, and how many calls each phase made (in launch order; a kernel trace of the run
+    splits its dispatches by these counts)."""
     return {
+        "dispatches": {"warmup": W, "timed_loops": LOOPS * K, "per_kernel_events": K if t["per_kernel"] else 0,
+                       "flushed": len(t["cold_us"])},
         "timed_loops_ms": [round(w * 1e3, 4) for w in t["walls"]],
         "gpu_event_ms_per_step": round(t["gpu_ms"] / K, 5),
         "per_kernel_us": {k: round(v, 3) for k, v in t["per_kernel"].items()},
@@ -560,11 +615,9 @@ def run_verify(args, dev, hev):
         "call_frac_of_peak": round(alg_bytes / t_call / 1e9 / PEAK_HBM_GBS, 4),
         "emitted_tokens_per_s": round(mean_emitted / t_call, 1),
         "mean_accepted_plus_one": round(mean_emitted / B, 4),
-        **timing_fields(t, K),
+        **timing_fields(t, K, args.warmup),
         "roofline": roofline(per_kernel, kernel, alg_bytes, traffic),
         "traffic_note": tnote,
-        "dispatches": {"warmup": args.warmup, "timed_loops": LOOPS * K, "per_kernel_events": K if per_kernel else 0,
-                       "flushed": len(t["cold_us"]), "after": min(n_sets, K)},
     }
     if not args.no_probe:
         probe = read_probe(alg_bytes, n_sets, K, dev, hev)
@@ -623,7 +676,7 @@ def run_sample(args, dev, hev):
                    "top_k": cfg.top_k, "input_sets": n_sets, "set_bytes": alg_bytes},
         "call_GBs": round(alg_bytes / t_call / 1e9, 1),
         "call_frac_of_peak": round(alg_bytes / t_call / 1e9 / PEAK_HBM_GBS, 4),
-        **timing_fields(t, K),
+        **timing_fields(t, K, args.warmup),
         "roofline": roofline(per_kernel, KERNEL, alg_bytes, counters_traffic("sample")[0]),
     }
     if not args.no_cpu_baseline:
@@ -693,7 +746,7 @@ def run_overlap(args, dev, hev):
         "call_GBs": round(alg_bytes / t_call / 1e9, 1),
         "call_frac_of_peak": round(alg_bytes / t_call / 1e9 / PEAK_HBM_GBS, 4),
         "mean_beta": round(float(outs[0].mean().item()), 5),
-        **timing_fields(t, K),
+        **timing_fields(t, K, args.warmup),
         "roofline": roofline(per_kernel, "k_overlap", alg_bytes, counters_traffic("overlap")[0]),
     }
     if not args.no_cpu_baseline:
@@ -775,7 +828,7 @@ def run_tree(args, dev, hev):
         "call_frac_of_peak": round(alg_bytes / t_call / 1e9 / PEAK_HBM_GBS, 4),
         "emitted_tokens_per_s": round(B * (float(np.mean(depth)) + 1) / t_call, 1),
         "mean_accepted_depth": round(float(np.mean(depth)), 4),
-        **timing_fields(t, K),
+        **timing_fields(t, K, args.warmup),
         "roofline": roofline(per_kernel, "k_tree_rows", alg_bytes, counters_traffic("tree")[0]),
     }
     if not args.no_cpu_baseline:
@@ -841,7 +894,7 @@ def run_typical(args, dev, hev):
         "call_GBs": round(alg_bytes / t_call / 1e9, 1),
         "call_frac_of_peak": round(alg_bytes / t_call / 1e9 / PEAK_HBM_GBS, 4),
         "mean_accepted": round(float(np.mean(acc)), 4),
-        **timing_fields(t, K),
+        **timing_fields(t, K, args.warmup),
         "roofline": roofline(per_kernel, "k_typical", alg_bytes, counters_traffic("typical")[0]),
     }
     if not args.no_cpu_baseline:
