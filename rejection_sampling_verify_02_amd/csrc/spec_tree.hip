@@ -271,10 +271,12 @@ __global__ __launch_bounds__(NT) void k_tree_resid(const TreeArgs t) {
   if (!lane_item(a.B * t.kmax, I, 0, phase, item)) return;  // units: list slots
   const int tid = threadIdx.x, lane = lane_id(), wid = tid / WAVE;
   const int slot = item / I, it = item - slot * I;
-  const int N = a.G, b = slot / t.kmax, ks = slot - b * t.kmax;
+  // slots are numbered list position first (slot = ks * B + b), so each XCD lane meets the
+  // trees' first list entries first and the (mostly empty) later positions last
+  const int N = a.G, ks = slot / a.B, b = slot - ks * a.B;
   // Two rounds of loads before the data: the slot's entry (with the count), then the rows'
   // statistics together with the rows' data.
-  const int cnt = t.act_n[b], ent = t.act[slot];
+  const int cnt = t.act_n[b], ent = t.act[(size_t)b * t.kmax + ks];
   if (ks >= cnt) return;  // an empty slot
   const int u = ent & 0xffff, nch = ent >> 16;
   if (u < 0 || u >= N || nch < 2) return;
