@@ -214,27 +214,31 @@ __global__ __launch_bounds__(NT) void k_typical(const TypArgs ta) {
 
   const float k2 = a.k2;
   float off = -INFINITY;
-  float acc_s = 0.0f, acc_m = 0.0f;
+  // A vector's terms are summed as a pairwise tree in fp32, the vectors in fp64, so each
+  // chunk sum carries at most about three fp32 roundings of relative error.
+  double acc_s = 0.0, acc_m = 0.0;
   int fl = (m == INFINITY) ? 1 : 0;  // a NaN or +inf also makes the sum NaN below
   if (m > -INFINITY) {
     off = m * k2;
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
-      float es[VEC];
-      float mv = 0.0f;
+      float es[VEC], ms[VEC];
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
         const float t = fmaf(x[k][e], k2, -off);
         const float ev = fast_exp2(t);
         es[e] = ev;
-        mv = fmaf(ev, fmaxf(t, -200.0f), mv);  // e = 0 below 2^-126: -inf terms add 0
+        ms[e] = ev * fmaxf(t, -200.0f);  // e = 0 below 2^-126: -inf terms add 0
       }
 #pragma unroll
       for (int h = VEC / 2; h > 0; h >>= 1)
 #pragma unroll
-        for (int e = 0; e < h; ++e) es[e] += es[e + h];
-      acc_s += es[0];
-      acc_m += mv;
+        for (int e = 0; e < h; ++e) {
+          es[e] += es[e + h];
+          ms[e] += ms[e + h];
+        }
+      acc_s += (double)es[0];
+      acc_m += (double)ms[0];
     }
     fl |= 2;
   } else {
@@ -245,7 +249,7 @@ __global__ __launch_bounds__(NT) void k_typical(const TypArgs ta) {
       for (int e = 0; e < VEC; ++e) nan |= (x[k][e] != x[k][e]);
     if (__ballot(nan)) fl |= 1;
   }
-  const double ws = wave_sum((double)acc_s), wm = wave_sum((double)acc_m);
+  const double ws = wave_sum(acc_s), wm = wave_sum(acc_m);
   if (lane == 0) {
     s_s[wid] = ws;
     s_mm[wid] = wm;

@@ -3,11 +3,13 @@
 All calls go through the C ABI.  Codes must match exactly; accepted lengths and tokens
 must match, except for a sequence whose first differing decision the oracle places within
 BAND_LOG of its threshold in log space (counted, at most 1% of sequences).  BAND_LOG comes
-from the arithmetic: the kernels form ln p(x) from a once-rounded log2(e)/T and an fp64
-log-partition (error ~1e-6), and the entropy from fp32 chunk sums of e and e*t combined in
-fp64 around the row's largest offset (relative error ~1e-6 of |log2 t| + |D| <= ~35 at
-V = 128256, so ~2.4e-5 in nats); 1e-4 leaves a margin of four.  The greedy next token is
-an integer argmax and must match exactly.
+from the arithmetic.  The kernels form ln p(x) from a once-rounded log2(e)/T and an fp64
+log-partition: error ~1e-6 of |z_x * k2| at worst, a few 1e-6 in nats.  The entropy comes
+from chunk sums of e and e*t (each vector's terms a pairwise fp32 tree, vectors and chunks
+in fp64), so each sum carries ~3 fp32 roundings (~2e-7 relative) on top of one rounding
+of each e and t; with |log2 t| + |D| <= ~35 at V = 128256 that is at most ~7e-6 in nats.
+2e-5 leaves a margin of about three.  The greedy next token is an integer argmax and must
+match exactly.
 """
 import numpy as np
 import pytest
@@ -18,7 +20,7 @@ from rejection_sampling_verify_02_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
 
-BAND_LOG = 1e-4
+BAND_LOG = 2e-5
 
 
 @pytest.fixture(scope="module")
