@@ -92,13 +92,14 @@ size_t sv_workspace_bytes(int32_t B, int32_t G, int32_t V, sv_dtype dtype, float
 size_t sv_workspace_zero_bytes(int32_t B, int32_t G, int32_t V, sv_dtype dtype,
                                float temperature, int32_t top_k);
 
-/* Tag epoch: the process's kernel launches counted in units of 2^31.  Each launch marks
- * its words with a 32-bit tag taken from that count, and a tag value comes back after
- * 2^32 - 1 launches: a workspace word last written exactly that many launches earlier
- * would then pass for the current launch's.  A caller that keeps a workspace across
- * calls records this value whenever it zeroes the workspace's prefix, and zeroes the
- * prefix again (all of it ever used) before the first call after the value changed.
- * That happens once every 2^31 launches; no call is refused. */
+/* Tag epoch: the process's tag count in units of 2^31.  Each kernel launch marks its
+ * words with 32-bit tags taken from that count (one tag; a tree verification's draw
+ * launch takes N + 1 consecutive ones, one per round of residual masses), and a tag value
+ * comes back after 2^32 - 1 tags: a workspace word last written exactly that many tags
+ * earlier would then pass for the current launch's.  A caller that keeps a workspace
+ * across calls records this value whenever it zeroes the workspace's prefix, and zeroes
+ * the prefix again (all of it ever used) before the first call after the value changed.
+ * That happens once every 2^31 tags; no call is refused. */
 uint32_t sv_tag_epoch(void);
 
 /* Batched verification.
@@ -266,8 +267,12 @@ const char *sv_overlap_launch_plan(int32_t B, int32_t G, int32_t V, sv_dtype dty
  *   tokens, parent [B, N] int32    node tokens (node 0's unused) and parents (parent[b,0] = -1)
  *   u_accept [B, N] float32        the uniform of node n's test (node 0's unused)
  *   u_sample [B] float32           the uniform of the final draw
- *   max_children                   the most children any node has (0 <= it <= N - 1);
- *                                  sizes the residual rounds
+ *   max_children                   the most children any node has (0 <= it <= N - 1).
+ *                                  At T > 0 with max_children >= 2 a row may span at most
+ *                                  32 chunks of 32 KiB (V <= 524288 bf16, 262144 f32):
+ *                                  the residual masses are formed by one workgroup per
+ *                                  chunk of the tree, which wait for one another.
+ *                                  Longer rows are SV_ERR_SHAPE there.
  * The walk starts at the root and tests the node's children in order: the first child
  * against p_u by U <= min(1, p_u(x)/q_u(x)); each rejection replaces the current
  * distribution by norm([cur - q_u]_+) and the next child is tested against it.  An

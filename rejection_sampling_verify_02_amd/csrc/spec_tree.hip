@@ -15,25 +15,23 @@
 // The residual family is one-parameter: after k rejections at u the current
 // distribution is [p_u - c_k q_u]_+ / Z_k with c_0 = 0, Z_0 = 1 and
 // c_{k+1} = c_k + Z_k, Z_k = sum_v [p_u(v) - c_k q_u(v)]_+ (induction on
-// [([p - c q]_+)/Z - q]_+ = [p - (c + Z) q]_+ / Z).  The chain Z_1, Z_2, ... depends on
-// no uniform, so it is computed for every node in parallel before the walk, and the walk
-// itself touches only gathered scalars.
+// [([p - c q]_+)/Z - q]_+ = [p - (c + Z) q]_+ / Z).  The walk needs Z_k only after a
+// rejection with a later child left, so each tree forms only the masses on its own path,
+// when the walk reaches them.
 //
 // Launches (each data-parallel; results pass through the workspace between launches):
-//   k_topk_digit   (top-k only) the radix select of every row's threshold.
+//   k_topk_select, k_topk_merge, or k_topk_digit   (top-k only) every row's threshold.
 //   k_tree_rows    per chunk of every target row and of every internal node's draft row:
 //                  the normaliser partial (argmax at T = 0); the row's last chunk combines
 //                  them into the row's log2-partition (argmax).
-//                  Target row 0's first chunk also lists the tree's nodes with two or
-//                  more children.
-//   k_tree_resid   (T > 0, the listed nodes) Z_1, Z_2, ...: the node's items read its two
-//                  rows once, keep them in registers and run the rounds from them,
-//                  exchanging only each round's partial sums.
-//   k_tree_draw    (T > 0) per tree and chunk: wave 0 walks the tree (checks, gathered
-//                  logits, the walk; chunk 0's item writes the accepted tokens and path),
-//                  then the item forms the segment masses of its chunk of the chosen
-//                  weights ([p - c q]_+ or p); the last chunk picks the segment and, in
-//                  it, the token by inverse CDF with u_sample.
+//   k_tree_draw    (T > 0) per tree and chunk: every item walks the tree (its first wave
+//                  stages checks, gathered logits and row values in LDS; its waves walk in
+//                  step; chunk 0's item writes the accepted tokens and path), the tree's
+//                  items forming each residual mass the walk needs together, each from
+//                  its chunk of the node's two rows; then each item forms the segment
+//                  masses of its chunk of the chosen weights ([p - c q]_+ or p), and the
+//                  last chunk picks the segment and, in it, the token by inverse CDF with
+//                  u_sample.
 //   k_tree_walk    (T = 0 only) one wave per tree: the walk, with nothing to draw.
 
 #include <hip/hip_runtime.h>
@@ -49,7 +47,7 @@ namespace sv {
 enum : int { TJ_NONE = 0, TJ_TARGET = 1, TJ_RESID = 2 };
 constexpr int TREE_MAX_NODES = 1024;   // nodes per tree (the walk keeps them in LDS)
 constexpr int TREE_DRAW_LDS_SEGS = 2048;  // segment masses the draw's collector keeps in LDS
-constexpr int TREE_MAX_ITEMS = 64;     // k_tree_resid items per node (V up to 64 * 16 KiB of a row)
+constexpr int TREE_LAZY_MAX_C = 32;    // chunks a row at most when nodes may have two or more children
 
 struct TreeArgs {
   Args a;                  // rows per tree: rps = 2N (N target rows, then N draft rows); a.G = N
@@ -62,14 +60,10 @@ struct TreeArgs {
   int32_t *row_arg;        // [R] greedy: lowest-index argmax
   int32_t *row_ok;         // [R] 1 usable, 0 not (NaN, +inf, nothing finite kept), -1 not read,
                            //   -2 a wait gave up
-  double *zc;              // [B*N*S] Z_j of node u at [u*S + j], j = 1..S-1
   // tagged words within one launch
-  u64 *tw_z;               // [B*N*(S-1)*I*2] per node, round and item: sum [p - c_j q]_+
   u64 *tw_seg;             // [B*C*SEGS*2] per tree, chunk and segment: the draw's masses
-  int32_t *act;            // [B*kmax] or null: per tree, its nodes with two or more children
-                           //   in index order (node | children << 16), from k_tree_rows
-  int32_t *act_n;          // [B] how many
-  int kmax;                // most such nodes a tree of N nodes can have: (N - 1) / 2, at least 1
+  u64 *tw_lz;              // [B*2*C*2] residual masses formed by the walk: per tree two slots
+                           //   (alternating rounds), per chunk item a tagged double
 };
 
 // The nodes' children, counted by one wave: nch = children of node u in tree b.
@@ -121,32 +115,6 @@ SVD void tree_row_chunk(const TreeArgs &t, int r, const T *row, int c) {
     t.row_lt[r] = ok ? log2(tt) : 0.0;
     t.row_ok[r] = !done ? -2 : (ok ? 1 : 0);
   }
-}
-
-// Tree b's nodes with two or more children, in index order, for k_tree_resid (one wave).
-// Parent entries outside [0, n) are not counted (the walk reports such a tree).  Each
-// counted entry is one child, so at most (N - 1) / 2 nodes have two or more.
-SVD void list_multi_child(const TreeArgs &t, int b) {
-  __shared__ int s_cnt[TREE_MAX_NODES];
-  const int N = t.a.G, lane = lane_id();
-  const int32_t *par = t.parent + (size_t)b * N;
-  for (int n = lane; n < N; n += WAVE) s_cnt[n] = 0;
-  lds_sync();
-  for (int n = lane + 1; n < N; n += WAVE) {
-    const int p = par[n];
-    if (p >= 0 && p < n) atomicAdd(&s_cnt[p], 1);
-  }
-  lds_sync();
-  int base = 0;
-  for (int n0 = 0; n0 < N; n0 += WAVE) {
-    const int n = n0 + lane;
-    const int c = (n < N) ? s_cnt[n] : 0;
-    const unsigned long long bal = __ballot(c >= 2);
-    const int pos = base + (int)__popcll(bal & ((1ull << lane) - 1ull));
-    if (c >= 2 && pos < t.kmax) t.act[(size_t)b * t.kmax + pos] = n | (c << 16);
-    base += (int)__popcll(bal);
-  }
-  if (lane == 0) t.act_n[b] = base < t.kmax ? base : t.kmax;
 }
 
 // ---------------------------------------------------------------- k_tree_rows
@@ -235,228 +203,59 @@ __global__ __launch_bounds__(NT) void k_tree_rows(const TreeArgs t) {
     return;
   }
 
-  // target row 0's first chunk also lists the tree's nodes that need residual masses
-  if (t.act && j == 0 && c == 0 && wid == 0) list_multi_child(t, b);
   tree_row_chunk<T, ALIGNED, TOPK>(t, r, row, c);
-}
-
-// ---------------------------------------------------------------- k_tree_resid
-
-// Items of k_tree_resid: RKV 16-byte vectors per thread of each of a node's two rows.
-// Aligned rows keep their raw vectors in registers, 8 a thread; otherwise p and q are
-// kept as floats, 4 vectors a thread.
-template <bool ALIGNED>
-constexpr int resid_rkv() { return ALIGNED ? 8 : 4; }
-__host__ __device__ inline int resid_items(int nvec, bool aligned) {
-  const int iv = NT * (aligned ? resid_rkv<true>() : resid_rkv<false>());
-  return (nvec + iv - 1) / iv;
-}
-
-// The residual masses Z_1 .. Z_{k-1} of a node with k >= 2 children.  Units are the slots
-// of each tree's list of such nodes (k_tree_rows wrote it), so no workgroup is spent on a
-// node without rounds.  The node's rows are cut into items; each item loads its part of
-// both rows once and keeps it in registers, and for j = 1, 2, ...: sums [p - c_j q]_+ over
-// its part (p and q formed from the rows' log2-partitions as the draw forms them),
-// publishes the sum, and waits for the node's other items' sums of the same round, whose
-// total is Z_j and gives c_{j+1} = c_j + Z_j.  The items of a node sit in consecutive
-// blocks of one XCD lane, so they are resident together; every wait is bounded.
-template <typename T, bool ALIGNED, bool TOPK>
-__global__ __launch_bounds__(NT) void k_tree_resid(const TreeArgs t) {
-  constexpr int VEC = Fmt<T>::VEC;
-  constexpr int RKV = resid_rkv<ALIGNED>();
-  const Args &a = t.a;
-  const int R1 = t.S - 1;
-  const int I = resid_items(a.nvec, ALIGNED);  // items per node
-  int phase, item;
-  if (!lane_item(a.B * t.kmax, I, 0, phase, item)) return;  // units: list slots
-  const int tid = threadIdx.x, lane = lane_id(), wid = tid / WAVE;
-  const int slot = item / I, it = item - slot * I;
-  // slots are numbered list position first (slot = ks * B + b), so each XCD lane meets the
-  // trees' first list entries first and the (mostly empty) later positions last
-  const int N = a.G, ks = slot / a.B, b = slot - ks * a.B;
-  // Two rounds of loads before the data: the slot's entry (with the count), then the rows'
-  // statistics together with the rows' data.
-  const int cnt = t.act_n[b], ent = t.act[(size_t)b * t.kmax + ks];
-  if (ks >= cnt) return;  // an empty slot
-  const int u = ent & 0xffff, nch = ent >> 16;
-  if (u < 0 || u >= N || nch < 2) return;
-  const int unit = b * N + u;
-  const int rt = b * a.rps + u, rd = rt + N;
-  const int okt = t.row_ok[rt], okd = t.row_ok[rd];
-  const float ot = t.row_off[rt], od = t.row_off[rd];
-  const double ltt = t.row_lt[rt], ltd = t.row_lt[rd];
-  const float tau_t = TOPK ? a.w.row_tau[rt] : -INFINITY, tau_d = TOPK ? a.w.row_tau[rd] : -INFINITY;
-  const int rounds = (nch - 1 < R1) ? nch - 1 : R1;
-  const float k2 = a.k2;
-  const T *row_t = seq_row<T>(a, b, u), *row_d = seq_row<T>(a, b, N + u);
-  // aligned: the raw vectors (past the row's end: -inf), loaded while the statistics
-  // arrive; otherwise p and q
-  u32x4 wt[ALIGNED ? RKV : 1], wd[ALIGNED ? RKV : 1];
-  float p[ALIGNED ? 1 : RKV][VEC], q[ALIGNED ? 1 : RKV][VEC];
-  if (ALIGNED) {
-    const u32x4 *ra = reinterpret_cast<const u32x4 *>(row_t), *rb = reinterpret_cast<const u32x4 *>(row_d);
-#pragma unroll
-    for (int k = 0; k < RKV; ++k) {
-      const int v = it * NT * RKV + k * NT + tid;
-      const int vs = v < a.nvec ? v : a.nvec - 1;
-      wt[k] = __builtin_nontemporal_load(ra + vs);
-      wd[k] = __builtin_nontemporal_load(rb + vs);
-    }
-  }
-  if (okt != 1 || okd != 1) return;  // no rounds (the walk reports bad rows)
-  const double lp = (double)ot + ltt, lq = (double)od + ltd;
-  const float mt_hi = d_head(lp), mt_lo = d_tail(lp), md_hi = d_head(lq), md_lo = d_tail(lq);
-  auto pq = [&](float za, float zb, float &pv, float &qv) {
-    const float zt = (TOPK && za < tau_t) ? -INFINITY : za;
-    const float zd = (TOPK && zb < tau_d) ? -INFINITY : zb;
-    pv = fast_exp2(fmaf(zt, k2, -mt_hi) - mt_lo);
-    qv = fast_exp2(fmaf(zd, k2, -md_hi) - md_lo);
-  };
-  if (ALIGNED) {
-    constexpr unsigned NEG_INF = (sizeof(T) == 2) ? 0xff80ff80u : 0xff800000u;
-#pragma unroll
-    for (int k = 0; k < RKV; ++k)
-      if (it * NT * RKV + k * NT + tid >= a.nvec) {
-        wt[k] = u32x4{NEG_INF, NEG_INF, NEG_INF, NEG_INF};
-        wd[k] = wt[k];
-      }
-  } else {
-#pragma unroll
-    for (int k = 0; k < RKV; ++k) {
-      const int v = it * NT * RKV + k * NT + tid;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const long idx = (long)v * VEC + e;
-        const bool in = idx < a.V;
-        pq(in ? Fmt<T>::at(row_t, (size_t)idx) : -INFINITY, in ? Fmt<T>::at(row_d, (size_t)idx) : -INFINITY,
-           p[ALIGNED ? 0 : k][e], q[ALIGNED ? 0 : k][e]);
-      }
-    }
-  }
-
-  __shared__ double s_w[NW];
-  __shared__ double s_z;
-  u64 *zw = t.tw_z + (size_t)unit * R1 * I * 2;
-  double cj = 1.0;  // c_1 = c_0 + Z_0 = 1
-  for (int j = 1; j <= rounds; ++j) {
-    const float cf = (float)cj;
-    float acc = 0.0f;
-#pragma unroll
-    for (int k = 0; k < RKV; ++k) {
-      float w[VEC];
-      if (ALIGNED) {
-        float za[VEC], zb[VEC];
-        Fmt<T>::unpack(wt[ALIGNED ? k : 0], za);
-        Fmt<T>::unpack(wd[ALIGNED ? k : 0], zb);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          float pe, qe;
-          pq(za[e], zb[e], pe, qe);
-          w[e] = fmaxf(fmaf(-cf, qe, pe), 0.0f);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) w[e] = fmaxf(fmaf(-cf, q[ALIGNED ? 0 : k][e], p[ALIGNED ? 0 : k][e]), 0.0f);
-      }
-#pragma unroll
-      for (int h = VEC / 2; h > 0; h >>= 1)
-#pragma unroll
-        for (int e = 0; e < h; ++e) w[e] += w[e + h];
-      acc += w[0];
-    }
-    const double ws = wave_sum((double)acc);
-    if (lane == 0) s_w[wid] = ws;
-    __syncthreads();
-    if (wid == 0) {
-      const double mine = (s_w[0] + s_w[1]) + (s_w[2] + s_w[3]);
-      u64 *rw = zw + (size_t)(j - 1) * I * 2;
-      if (lane < 2) tw_putf(rw + (size_t)it * 2 + lane, a.tag, lane ? d_tail(mine) : d_head(mine));
-      double zj = (double)NAN;
-      for (unsigned polls = 0; polls < a.spin_limit; ++polls) {
-        bool ready = true;
-        double part = 0.0;
-        for (int cc = lane; cc < I; cc += WAVE) {
-          const u64 w0 = ld_dev(rw + (size_t)cc * 2), w1 = ld_dev(rw + (size_t)cc * 2 + 1);
-          ready = ready && (cc == it || (tw_ok(w0, a.tag) && tw_ok(w1, a.tag)));
-          part += (cc == it) ? mine : d_join(tw_f(w0), tw_f(w1));
-        }
-        if (wave_or(ready ? 0u : 1u) == 0u) {
-          zj = wave_sum(part);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
-      if (lane == 0) {
-        s_z = zj;
-        if (it == I - 1) t.zc[(size_t)unit * t.S + j] = zj;  // a wait that gave up leaves NaN
-      }
-    }
-    __syncthreads();
-    // c_{j+1} = c_j + Z_j; a zero mass makes p the current distribution again, whose
-    // next residual is [p - q]_+ (c = 1)
-    cj = (s_z > 0.0) ? cj + s_z : 1.0;
-  }
 }
 
 // ---------------------------------------------------------------- k_tree_walk
 
-// The walk of tree b by one wave: checks, gathered logits, then the walk itself.  With
-// writer, the accepted tokens and path, the padding and accepted_len (or the row code) are
-// written.  Leaves in s_res the node u where the walk ended, the draw's kind and the
-// accepted depth, and in *s_c the draw's c (kind TJ_RESID).
+// What the walk of one tree reads, staged in LDS by its first wave, and the accepted
+// nodes it leaves (node[0] = 0, node[d] the node accepted at depth d).
+struct WalkLds {
+  int par[TREE_MAX_NODES], tok[TREE_MAX_NODES], nch[TREE_MAX_NODES], node[TREE_MAX_NODES];
+  float zt[TREE_MAX_NODES], zd[TREE_MAX_NODES], ua[TREE_MAX_NODES], tau[TREE_MAX_NODES], taud[TREE_MAX_NODES];
+  double lp[TREE_MAX_NODES], lq[TREE_MAX_NODES];
+  int err;
+};
+
+// The checks of tree b and everything its walk reads, into W, by one wave in two rounds of
+// loads: first what is indexed by the node alone (parent, token, both rows' status,
+// log2-partition and threshold, the uniform), then each node's token logits in its
+// parent's rows.  The node checks count only for a well-formed tree.  W.err is the tree's
+// row code, 0 if none.  Greedy: W.lp holds each row's argmax instead.
 template <typename T, bool TOPK, bool GREEDY>
-SVD void tree_walk(const TreeArgs &t, int b, bool writer, int *s_res, double *s_c) {
+SVD void walk_setup(const TreeArgs &t, int b, WalkLds &W) {
   const Args &a = t.a;
   const int lane = lane_id();
   const int N = a.G, V = a.V;
-  constexpr int ZP = 4;  // residual masses per node staged in LDS (zc[1..4]); later ones are read on demand
-  __shared__ int s_par[TREE_MAX_NODES], s_tok[TREE_MAX_NODES], s_nch[TREE_MAX_NODES];
-  __shared__ float s_zt[TREE_MAX_NODES], s_zd[TREE_MAX_NODES], s_ua[TREE_MAX_NODES], s_tau[TREE_MAX_NODES],
-      s_taud[TREE_MAX_NODES];
-  __shared__ double s_lp[TREE_MAX_NODES], s_lq[TREE_MAX_NODES], s_zp[TREE_MAX_NODES * ZP];
-  __shared__ int s_arg[GREEDY ? TREE_MAX_NODES : 1];  // greedy: each target row's argmax
   const int32_t *par = t.parent + (size_t)b * N;
   const int32_t *tok = a.tokens + (size_t)b * N;
-  int32_t *out = a.out_tokens + (size_t)b * N;
-  int32_t *path = t.path ? t.path + (size_t)b * N : nullptr;
   const size_t r0 = (size_t)b * a.rps;
-  const int zs = min(t.S - 1, ZP);  // staged residual masses per node
-
-  // Two rounds of loads.  First everything indexed by the node alone: parent, token, both
-  // rows' status, log2-partition and threshold, the uniform and the first residual masses
-  // (whether or not the node turns out to have children).  The node checks count only for
-  // a well-formed tree (f1 joins flags after that test).
   unsigned flags = 0, f1 = 0;  // 1 token, 2 row, 4 uniform, 8 q(x) = 0, 16 internal, 32 tree
   int okt_l = 0, okd_l = 0;    // this lane's last node (N <= 64: its only one)
   for (int n = lane; n < N; n += WAVE) {
     const int p = par[n];
     const int x = tok[n];
     const int okt = t.row_ok[r0 + n];
-    s_par[n] = p;
-    s_tok[n] = x;
-    s_nch[n] = 0;
+    W.par[n] = p;
+    W.tok[n] = x;
+    W.nch[n] = 0;
     if (n == 0 ? (p != -1) : (p < 0 || p >= n)) flags |= 32;
     if (n > 0 && (x < 0 || x >= V)) f1 |= 1;
     f1 |= (okt == -2) ? 16 : (okt != 1 ? 2 : 0);
     okt_l = okt;
-    if (GREEDY) s_arg[n] = t.row_arg[r0 + n];
-    if (!GREEDY) {
-      s_lp[n] = (double)t.row_off[r0 + n] + t.row_lt[r0 + n];
-      s_lq[n] = (double)t.row_off[r0 + N + n] + t.row_lt[r0 + N + n];  // used only with children
+    if (GREEDY) {
+      W.lp[n] = (double)t.row_arg[r0 + n];
+    } else {
+      W.lp[n] = (double)t.row_off[r0 + n] + t.row_lt[r0 + n];
+      W.lq[n] = (double)t.row_off[r0 + N + n] + t.row_lt[r0 + N + n];  // used only with children
       okd_l = t.row_ok[r0 + N + n];
       const float u = n ? a.u_accept[(size_t)b * N + n] : 0.0f;
-      s_ua[n] = u;
+      W.ua[n] = u;
       if (n > 0 && !(u >= 0.0f && u < 1.0f)) f1 |= 4;
       const float tt = TOPK ? a.w.row_tau[r0 + n] : -INFINITY;
-      s_tau[n] = tt;
+      W.tau[n] = tt;
       if (tt != tt) f1 |= 16;  // a NaN threshold marks a top-k selection that did not complete
-      s_taud[n] = TOPK ? a.w.row_tau[r0 + N + n] : -INFINITY;
-      const double *zc = t.zc + ((size_t)b * N + n) * t.S;
-      double zv[ZP];
-#pragma unroll
-      for (int j = 0; j < ZP; ++j) zv[j] = (j < zs) ? zc[j + 1] : 0.0;
-#pragma unroll
-      for (int j = 0; j < ZP; ++j) s_zp[n * ZP + j] = zv[j];
+      W.taud[n] = TOPK ? a.w.row_tau[r0 + N + n] : -INFINITY;
     }
   }
   if (!GREEDY && lane == 0 && !(a.u_sample[b] >= 0.0f && a.u_sample[b] < 1.0f)) f1 |= 4;
@@ -464,113 +263,100 @@ SVD void tree_walk(const TreeArgs &t, int b, bool writer, int *s_res, double *s_
   lds_sync();
   if (!(flags & 32)) {
     flags |= wave_or(f1);
-    for (int n = lane + 1; n < N; n += WAVE) atomicAdd(&s_nch[s_par[n]], 1);
+    for (int n = lane + 1; n < N; n += WAVE) atomicAdd(&W.nch[W.par[n]], 1);
     lds_sync();
-    // Then the token logits of every node in its parent's rows (checks passed so far), and
-    // the checks that need the children counts.
     const bool gather = !GREEDY && !(flags & 1);
     for (int n = lane; n < N; n += WAVE) {
       float zt = 0.0f, zd = 0.0f;
-      const int p = s_par[n], x = s_tok[n];
+      const int p = W.par[n], x = W.tok[n];
       if (gather && n > 0) {
         zt = Fmt<T>::at(static_cast<const T *>(seq_row<T>(a, b, p)), (size_t)x);
         zd = Fmt<T>::at(static_cast<const T *>(seq_row<T>(a, b, N + p)), (size_t)x);
       }
-      const int nch = s_nch[n];
+      const int nch = W.nch[n];
       if (!GREEDY && nch > t.S) flags |= 32;
       if (!GREEDY && nch > 0) {
         const int okt = (N <= WAVE) ? okt_l : t.row_ok[r0 + n];
         const int okd = (N <= WAVE) ? okd_l : t.row_ok[r0 + N + n];
         flags |= (okd == -2) ? 16 : (okd != 1 ? 2 : 0);
-        if (TOPK && s_taud[n] != s_taud[n]) flags |= 16;
-        // the residual masses of a node's later children (a NaN marks a wait that gave up)
-        if (okt == 1 && okd == 1) {
-          const int nz = min(nch, t.S) - 1;
-          for (int jj = 1; jj <= nz; ++jj) {
-            const double z = (jj <= ZP) ? s_zp[n * ZP + jj - 1] : t.zc[((size_t)b * N + n) * t.S + jj];
-            if (!(z >= 0.0) || !isfinite(z)) flags |= 16;
-          }
-        }
+        if (TOPK && W.taud[n] != W.taud[n]) flags |= 16;
       }
       if (gather && n > 0) {
-        s_zt[n] = zt;
-        s_zd[n] = zd;
-        if (!(zd > -INFINITY) || zd < s_taud[p]) flags |= 8;
+        W.zt[n] = zt;
+        W.zd[n] = zd;
+        if (!(zd > -INFINITY) || zd < W.taud[p]) flags |= 8;
       }
     }
     flags = wave_or(flags);
-    lds_sync();
   }
-  const int err = (flags & 16) ? SV_ROW_INTERNAL
-                : (flags & 32) ? SV_ROW_BAD_TREE
-                : (flags & 1) ? SV_ROW_BAD_TOKEN
-                : (flags & 2) ? SV_ROW_BAD_LOGITS
-                : (flags & 4) ? SV_ROW_BAD_UNIFORM
-                : (flags & 8) ? SV_ROW_Q_ZERO : 0;
-  if (err) {
-    if (writer) {
-      for (int n = lane; n < N; n += WAVE) {
-        out[n] = -1;
-        if (path) path[n] = -1;
-      }
-      if (lane == 0) a.accepted_len[b] = err;
-    }
-    if (lane == 0) {
-      s_res[0] = 0;
-      s_res[1] = TJ_NONE;
-      s_res[2] = 0;
-      *s_c = 0.0;
-    }
-    lds_sync();
-    return;
+  if (lane == 0) {
+    W.err = (flags & 16) ? SV_ROW_INTERNAL
+          : (flags & 32) ? SV_ROW_BAD_TREE
+          : (flags & 1) ? SV_ROW_BAD_TOKEN
+          : (flags & 2) ? SV_ROW_BAD_LOGITS
+          : (flags & 4) ? SV_ROW_BAD_UNIFORM
+          : (flags & 8) ? SV_ROW_Q_ZERO : 0;
+    W.node[0] = 0;
   }
+  lds_sync();
+}
 
-  // The walk, by the whole wave in step: at each node a ballot over the nodes (64 at a
-  // time, in index order) finds its children, whose tests then run in order on values that
-  // are the same in every lane (no lane scans the tree alone).
+struct WalkEnd {
+  int u, kind, depth;
+  double c;  // the draw's c (kind TJ_RESID)
+};
+
+// The walk, by every wave that calls it, in step (every value it uses is the same in
+// every lane of every wave): at each node a ballot over the nodes (64 at a time, in index
+// order) finds its children, which are tested in order against the current distribution
+// [p - cc q]_+ / cz ("Speculative Decoding 的朴素思想", section "Token Tree Verifier").  After
+// a rejection with a later child left, zfn(u, cc) gives the next residual's mass
+// Z = sum_v [p_u(v) - cc q_u(v)]_+ (NaN if it could not be formed: the walk stops with kind
+// TJ_NONE).  Thread 0 records the accepted nodes in W.node.
+template <bool GREEDY, typename ZFn>
+SVD WalkEnd walk_run(const TreeArgs &t, WalkLds &W, const ZFn &zfn) {
+  const int lane = lane_id();
+  const int N = t.a.G;
+  const double k2 = (double)t.a.k2;
   int u = 0, depth = 0, kind = TJ_NONE;
   double cc = 0.0;
-  const double k2 = (double)a.k2;
   for (;;) {
     if (GREEDY) {
-      const int am = s_arg[u];
+      const int am = (int)W.lp[u];
       int next = -1;
       for (int n0 = u + 1; n0 < N && next < 0; n0 += WAVE) {
         const int n = n0 + lane;
-        const unsigned long long m = __ballot(n < N && s_par[n] == u && s_tok[n] == am);
+        const unsigned long long m = __ballot(n < N && W.par[n] == u && W.tok[n] == am);
         if (m) next = n0 + (int)__ffsll((long long)m) - 1;
       }
-      if (writer && lane == 0) out[depth] = am;
       if (next < 0) break;
-      if (writer && lane == 0 && path) path[depth] = next;
       ++depth;
+      if (threadIdx.x == 0) W.node[depth] = next;
       u = next;
       continue;
     }
-    const int nch = s_nch[u];
+    const int nch = W.nch[u];
     if (nch == 0) {
       kind = TJ_TARGET;
       break;
     }
-    const double lp = s_lp[u], lq = s_lq[u];
-    const float tau_t = s_tau[u];
-    auto zc_at = [&](int k) {  // Z_k of node u, k = 1 .. min(nch, S) - 1
-      return (k <= ZP) ? s_zp[u * ZP + k - 1] : t.zc[((size_t)b * N + u) * t.S + k];
-    };
+    const double lp = W.lp[u], lq = W.lq[u];
+    const float tau_t = W.tau[u];
     int k = 0, next = -1;
+    bool failed = false;
     // the current distribution is [p - cc q]_+ / cz; (cc, cz) = (0, 1) is p itself
     double cz = 1.0;
     cc = 0.0;
-    for (int n0 = u + 1; n0 < N && next < 0 && k < nch; n0 += WAVE) {
+    for (int n0 = u + 1; n0 < N && next < 0 && k < nch && !failed; n0 += WAVE) {
       const int n = n0 + lane;
-      unsigned long long m = __ballot(n < N && s_par[n] == u);
-      while (m && next < 0) {
+      unsigned long long m = __ballot(n < N && W.par[n] == u);
+      while (m && next < 0 && !failed) {
         const int sn = n0 + (int)__ffsll((long long)m) - 1;
         m &= m - 1ull;
-        const float zt = s_zt[sn], zd = s_zd[sn];
+        const float zt = W.zt[sn], zd = W.zd[sn];
         const bool supp_t = (zt > -INFINITY) && !(zt < tau_t);
         const double l2p = (double)zt * k2 - lp, l2q = (double)zd * k2 - lq;
-        const double us = (double)s_ua[sn];
+        const double us = (double)W.ua[sn];
         bool accept = false;
         if (cc == 0.0) {
           accept = supp_t && us <= exp2(fmin(0.0, l2p - l2q));
@@ -582,14 +368,16 @@ SVD void tree_walk(const TreeArgs &t, int b, bool writer, int *s_res, double *s_
           next = sn;
           break;
         }
-        // rejected: the next distribution is [p - (cc + cz) q]_+ with mass zc[k + 1]
-        // (k_tree_resid's round k + 1); a zero mass leaves p itself (as the chain's
-        // zero-residual fallback).  After the last child the draw finds the mass.
+        // rejected: the next distribution is [p - (cc + cz) q]_+ with mass Z; a zero mass
+        // leaves p itself (as the chain's zero-residual fallback).  After the last child
+        // the draw finds the mass.
         cc += cz;
         ++k;
         if (k < nch) {
-          const double zk = zc_at(k);
-          if (zk > 0.0) {
+          const double zk = zfn(u, k, cc);
+          if (zk != zk) {
+            failed = true;
+          } else if (zk > 0.0) {
             cz = zk;
           } else {
             cc = 0.0;
@@ -598,40 +386,59 @@ SVD void tree_walk(const TreeArgs &t, int b, bool writer, int *s_res, double *s_
         }
       }
     }
+    if (failed) {
+      kind = TJ_NONE;
+      depth = -1;
+      break;
+    }
     if (next < 0) {
       kind = TJ_RESID;
       break;
     }
-    if (writer && lane == 0) {
-      out[depth] = s_tok[next];
-      if (path) path[depth] = next;
-    }
     ++depth;
+    if (threadIdx.x == 0) W.node[depth] = next;
     u = next;
   }
-  if (lane == 0) {
-    if (writer) a.accepted_len[b] = depth;
-    s_res[0] = u;
-    s_res[1] = kind;
-    s_res[2] = depth;
-    *s_c = cc;
-  }
-  lds_sync();
-  if (!writer) return;
-  // padding: out[depth] is the final token (the greedy choice, or the draw's), path[depth]
-  // onward are not accepted nodes
+  return WalkEnd{u, kind, depth, cc};
+}
+
+// The walk's outputs, by one wave: the accepted tokens and path, the padding and
+// accepted_len (the greedy final token too; the sampled one is the draw's), or the row
+// code err with every output -1.
+template <bool GREEDY>
+SVD void walk_write(const TreeArgs &t, int b, const WalkLds &W, int depth, int err) {
+  const Args &a = t.a;
+  const int lane = lane_id(), N = a.G;
+  int32_t *out = a.out_tokens + (size_t)b * N;
+  int32_t *path = t.path ? t.path + (size_t)b * N : nullptr;
   for (int n = lane; n < N; n += WAVE) {
-    if (n > depth) out[n] = -1;
-    if (path && n >= depth) path[n] = -1;
+    if (err) {
+      out[n] = -1;
+      if (path) path[n] = -1;
+      continue;
+    }
+    if (n < depth) out[n] = GREEDY ? (int)W.lp[W.node[n]] : W.tok[W.node[n + 1]];
+    else if (n == depth && GREEDY) out[n] = (int)W.lp[W.node[n]];
+    else if (n > depth) out[n] = -1;
+    if (path) path[n] = (n < depth) ? W.node[n + 1] : -1;
   }
+  if (lane == 0) a.accepted_len[b] = err ? err : depth;
 }
 
 // Greedy (T = 0): one wave per tree walks it; nothing is drawn.
 template <typename T>
 __global__ __launch_bounds__(WAVE) void k_tree_walk(const TreeArgs t) {
-  __shared__ int s_res[3];
-  __shared__ double s_c;
-  tree_walk<T, false, true>(t, (int)blockIdx.x, true, s_res, &s_c);
+  __shared__ WalkLds W;
+  const int b = (int)blockIdx.x;
+  walk_setup<T, false, true>(t, b, W);
+  const int err = W.err;
+  int depth = 0;
+  if (!err) {
+    auto none = [](int, int, double) { return 0.0; };
+    depth = walk_run<true>(t, W, none).depth;
+    lds_sync();
+  }
+  walk_write<true>(t, b, W, depth, err);
 }
 
 // ---------------------------------------------------------------- k_tree_draw
@@ -673,28 +480,138 @@ SVD double wave_chunk_mass(const Args &a, const T *row, int c, const WFn &wf) {
   return tot;
 }
 
+// Sampling (T > 0): the walk and the draw of each tree by its C chunk items (item c owns
+// chunk c of every row of the tree).  Every item walks the tree (its first wave stages what
+// the walk reads; then all its waves walk in step; chunk 0's item writes the accepted
+// tokens and path).
+// A residual mass is formed when the walk needs it, by all the tree's items together: each
+// sums [p_u - c q_u]_+ over its chunk of node u's two rows (the raw vectors stay in
+// registers while the walk stays at u; p and q formed from the rows' log2-partitions as
+// the draw forms them), publishes the sum as a tagged double (round r of the call uses tag
+// + 1 + r; two slots, alternating by round), and waits for the others' sums of the round;
+// every item adds them in chunk order, so all take the same decisions.  The walk needs
+// one mass per rejection before a node's last child, so most nodes never have theirs
+// formed.  A tree's items are consecutive blocks of one XCD lane, and they wait for one
+// another only when a node has two or more children, which the host allows only for rows
+// of at most TREE_LAZY_MAX_C chunks (every wait is bounded).
+// Then the draw: segment masses of the item's chunk of the chosen weights; the last chunk
+// picks segment, lane and element.
 template <typename T, bool ALIGNED, bool TOPK>
 __global__ __launch_bounds__(NT) void k_tree_draw(const TreeArgs t) {
+  constexpr int VEC = Fmt<T>::VEC;
   const Args &a = t.a;
   int phase, item;
   if (!lane_item(a.B, a.C, 0, phase, item)) return;  // units: trees
-  const int lane = lane_id(), wid = threadIdx.x / WAVE;
+  const int tid = threadIdx.x, lane = lane_id(), wid = tid / WAVE;
   const int b = item / a.C, c = item - b * a.C;
-  // Every chunk item of the tree walks it (wave 0, the same walk in each); chunk 0's writes
-  // the accepted tokens, path and accepted_len.
-  __shared__ int s_res[3];
-  __shared__ double s_c;
-  if (wid == 0) tree_walk<T, TOPK, false>(t, b, c == 0, s_res, &s_c);
+  const int N = a.G;
+  __shared__ WalkLds W;
+  __shared__ double s_w[NW], s_z;
+  if (wid == 0) walk_setup<T, TOPK, false>(t, b, W);
   __syncthreads();
-  const int kind = s_res[1];
-  if (kind == TJ_NONE) return;
-  const int u = s_res[0], depth = s_res[2], N = a.G;
+  int err = W.err;
+  WalkEnd we{0, TJ_NONE, 0, 0.0};
+  if (!err) {
+    // chunk c of node zu's two rows, loaded at the first mass formed at zu
+    int zu = -1, round = 0;
+    u32x4 wt[ALIGNED ? VPT : 1], wd[ALIGNED ? VPT : 1];
+    auto zfn = [&](int u, int, double cval) -> double {
+      const size_t rt = (size_t)b * a.rps + u, rd = rt + N;
+      const T *row_t = seq_row<T>(a, b, u), *row_d = seq_row<T>(a, b, N + u);
+      if (ALIGNED && zu != u) {
+        constexpr unsigned NEG_INF = (sizeof(T) == 2) ? 0xff80ff80u : 0xff800000u;
+        const u32x4 *ra = reinterpret_cast<const u32x4 *>(row_t), *rb = reinterpret_cast<const u32x4 *>(row_d);
+#pragma unroll
+        for (int kk = 0; kk < VPT; ++kk) {
+          const int v = c * CHUNK_VECS + kk * NT + tid;
+          const int vs = v < a.nvec ? v : a.nvec - 1;
+          wt[ALIGNED ? kk : 0] = ra[vs];
+          wd[ALIGNED ? kk : 0] = rb[vs];
+        }
+#pragma unroll
+        for (int kk = 0; kk < VPT; ++kk)
+          if (c * CHUNK_VECS + kk * NT + tid >= a.nvec) {
+            wt[ALIGNED ? kk : 0] = u32x4{NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+            wd[ALIGNED ? kk : 0] = wt[ALIGNED ? kk : 0];
+          }
+        zu = u;
+      }
+      const double lp = W.lp[u], lq = W.lq[u];
+      const float mt_hi = d_head(lp), mt_lo = d_tail(lp), md_hi = d_head(lq), md_lo = d_tail(lq);
+      const float tau_t = W.tau[u], tau_d = W.taud[u];
+      const float k2 = a.k2, cf = (float)cval;
+      float acc = 0.0f;
+#pragma unroll
+      for (int kk = 0; kk < VPT; ++kk) {
+        float za[VEC], zb[VEC], w[VEC];
+        if (ALIGNED) {
+          Fmt<T>::unpack(wt[ALIGNED ? kk : 0], za);
+          Fmt<T>::unpack(wd[ALIGNED ? kk : 0], zb);
+        } else {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            const long idx = elem_index<T>(c, kk, tid, e);
+            const bool in = idx < a.V;
+            za[e] = in ? Fmt<T>::at(row_t, (size_t)idx) : -INFINITY;
+            zb[e] = in ? Fmt<T>::at(row_d, (size_t)idx) : -INFINITY;
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const float zt = (TOPK && za[e] < tau_t) ? -INFINITY : za[e];
+          const float zd = (TOPK && zb[e] < tau_d) ? -INFINITY : zb[e];
+          const float p = fast_exp2(fmaf(zt, k2, -mt_hi) - mt_lo);
+          const float q = fast_exp2(fmaf(zd, k2, -md_hi) - md_lo);
+          w[e] = fmaxf(fmaf(-cf, q, p), 0.0f);
+        }
+#pragma unroll
+        for (int h = VEC / 2; h > 0; h >>= 1)
+#pragma unroll
+          for (int e = 0; e < h; ++e) w[e] += w[e + h];
+        acc += w[0];
+      }
+      const double ws = wave_sum((double)acc);
+      if (lane == 0) s_w[wid] = ws;
+      __syncthreads();
+      if (wid == 0) {
+        const double mine = (s_w[0] + s_w[1]) + (s_w[2] + s_w[3]);
+        const unsigned tag = a.tag + 1u + (unsigned)round;
+        u64 *zw = t.tw_lz + ((size_t)b * 2 + (round & 1)) * (size_t)a.C * 2;
+        if (lane < 2) tw_putf(zw + (size_t)c * 2 + lane, tag, lane ? d_tail(mine) : d_head(mine));
+        double z = (double)NAN;
+        for (unsigned polls = 0; polls < a.spin_limit; ++polls) {
+          bool ready = true;
+          double part = 0.0;
+          for (int cc = lane; cc < a.C; cc += WAVE) {
+            const u64 w0 = ld_dev(zw + (size_t)cc * 2), w1 = ld_dev(zw + (size_t)cc * 2 + 1);
+            ready = ready && (cc == c || (tw_ok(w0, tag) && tw_ok(w1, tag)));
+            part += (cc == c) ? mine : d_join(tw_f(w0), tw_f(w1));
+          }
+          if (wave_or(ready ? 0u : 1u) == 0u) {
+            z = wave_sum(part);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+        if (lane == 0) s_z = z;  // NaN: a wait that gave up
+      }
+      __syncthreads();
+      ++round;
+      return s_z;
+    };
+    we = walk_run<false>(t, W, zfn);
+    if (we.depth < 0) err = SV_ROW_INTERNAL;  // a mass that could not be formed
+    __syncthreads();  // W.node is complete
+  }
+  if (c == 0 && wid == 0) walk_write<false>(t, b, W, we.depth, err);
+  if (err || we.kind == TJ_NONE) return;
+  const int kind = we.kind, u = we.u, depth = we.depth;
   if (u < 0 || u >= N || depth < 0 || depth >= N) return;  // cannot happen: the walk keeps both in range
   const size_t rt = (size_t)b * a.rps + u, rd = rt + N;
-  const double cjob = s_c;
+  const double cjob = we.c;
   const bool resid = kind == TJ_RESID && cjob > 0.0;  // c = 0: the current distribution is p
-  const double lp = (double)t.row_off[rt] + t.row_lt[rt];
-  const double lq = resid ? (double)t.row_off[rd] + t.row_lt[rd] : 0.0;
+  const double lp = W.lp[u];
+  const double lq = resid ? W.lq[u] : 0.0;
   TreeW wf{a.k2, d_head(lp), d_tail(lp), resid ? (float)((lq - lp) - log2(cjob)) : 0.0f,
            TOPK ? a.w.row_tau[rt] : -INFINITY, (TOPK && resid) ? a.w.row_tau[rd] : -INFINITY, resid};
   const T *row_t = seq_row<T>(a, b, u);
@@ -778,12 +695,10 @@ using sv_host::next_tag;
 
 struct TreePlan {
   bool greedy, topk;
-  int esz, nvec, C, I, rps, S;  // I: k_tree_resid items per node
+  int esz, nvec, C, rps, S;
   long long R;
-  size_t tw_part, tw_z, tw_seg, tw_hist, row_off, row_lt, row_arg, row_ok, zc, act, act_n,
-      row_tau, tk_state, total, zero_bytes;
-  bool resid;  // nodes may have two or more children: k_tree_resid runs
-  int kmax;    // list slots per tree
+  size_t tw_part, tw_seg, tw_lz, tw_hist, row_off, row_lt, row_arg, row_ok, row_tau, tk_state, total,
+      zero_bytes;
 };
 
 bool tree_plan(int32_t B, int32_t N, int32_t V, int32_t S, sv_dtype dt, float T, int32_t top_k,
@@ -793,35 +708,26 @@ bool tree_plan(int32_t B, int32_t N, int32_t V, int32_t S, sv_dtype dt, float T,
   const int vec = 16 / p.esz;
   p.nvec = (int)(((long long)V + vec - 1) / vec);
   p.C = (p.nvec + CHUNK_VECS - 1) / CHUNK_VECS;
-  p.I = resid_items(p.nvec, false);  // the larger count (unaligned rows)
   p.rps = 2 * N;
   p.R = (long long)B * p.rps;
   p.S = S < 1 ? 1 : S;
-  p.resid = p.S > 1 && T != 0.0f;
-  p.kmax = N > 2 ? (N - 1) / 2 : 1;
   p.topk = !p.greedy && top_k > 0 && top_k < V;
-  const long long lr = (p.R + LANES - 1) / LANES, ln = ((long long)B * N + LANES - 1) / LANES,
-                  lb = (B + LANES - 1) / LANES;
-  // the items of a node in k_tree_resid wait for one another: at most TREE_MAX_ITEMS of them
-  if (!p.greedy && p.S > 1 && p.I > TREE_MAX_ITEMS) return false;
-  if (LANES * lr * p.C > 0x7fffffffLL || LANES * ln * (long long)p.I > 0x7fffffffLL ||
-      LANES * lb * (long long)p.C > 0x7fffffffLL)
-    return false;
-  const size_t R = (size_t)p.R, C = (size_t)p.C, Bz = (size_t)B, Nz = (size_t)N, Sz = (size_t)p.S;
+  const long long lr = (p.R + LANES - 1) / LANES, lb = (B + LANES - 1) / LANES;
+  // a tree's draw items wait for one another when a node may have two or more children
+  if (!p.greedy && p.S > 1 && p.C > TREE_LAZY_MAX_C) return false;
+  if (LANES * lr * p.C > 0x7fffffffLL || LANES * lb * (long long)p.C > 0x7fffffffLL) return false;
+  const size_t R = (size_t)p.R, C = (size_t)p.C, Bz = (size_t)B;
   const bool smp = !p.greedy;
   size_t o = 0;
   p.tw_part = o; o = align256(o + R * C * 3 * 8);
-  p.tw_z = o; o = align256(o + (smp ? Bz * Nz * (Sz - 1) * (size_t)p.I * 2 * 8 : 0));
   p.tw_seg = o; o = align256(o + (smp ? Bz * C * SEGS * 2 * 8 : 0));
+  p.tw_lz = o; o = align256(o + (smp ? Bz * 2 * C * 2 * 8 : 0));
   p.tw_hist = o; o = align256(o + (p.topk ? sv_host::topk_words(p.R, p.C, top_k) * 8 : 0));
   p.zero_bytes = o;
   p.row_off = o; o = align256(o + R * 4);
   p.row_lt = o; o = align256(o + R * 8);
   p.row_arg = o; o = align256(o + R * 4);
   p.row_ok = o; o = align256(o + R * 4);
-  p.zc = o; o = align256(o + Bz * Nz * Sz * 8);
-  p.act = o; o = align256(o + (p.resid ? Bz * (size_t)p.kmax * 4 : 0));
-  p.act_n = o; o = align256(o + (p.resid ? Bz * 4 : 0));
   p.row_tau = o; o = align256(o + (p.topk ? R * 4 : 0));
   p.tk_state = o; o = align256(o + (p.topk ? sv_host::topk_state_bytes(p.R, p.C, top_k) : 0));
   p.total = o;
@@ -839,7 +745,6 @@ hipError_t tree_launch(const TreePlan &p, const TreeArgs &t0, hipStream_t st, vo
   sv_host::Launcher L{st, ev, nev};
   const long long B = t0.a.B;
   const long long lr = (p.R + LANES - 1) / LANES, lb = (B + LANES - 1) / LANES;
-  const long long lk = (B * p.kmax + LANES - 1) / LANES;  // lanes of list slots
   TreeArgs t = t0;
   if (p.topk) sv_host::launch_topk<T, AL>(L, t.a, (unsigned)(LANES * lr * p.C), p.C);
   {
@@ -850,20 +755,14 @@ hipError_t tree_launch(const TreePlan &p, const TreeArgs &t0, hipStream_t st, vo
                             : (const void *)&k_tree_rows<T, AL, false, false>;
     L.go(fn, (unsigned)(LANES * lr * p.C), args);
   }
-  if (p.resid) {  // the residual masses of the listed nodes
-    t.a.tag = next_tag();
-    void *args[] = {&t};
-    L.go(p.topk ? (const void *)&k_tree_resid<T, AL, true> : (const void *)&k_tree_resid<T, AL, false>,
-         (unsigned)(LANES * lk * resid_items(p.nvec, AL)), args);
-  }
   if (p.greedy) {  // the walk alone
     t.a.tag = next_tag();
     void *args[] = {&t};
     L.block = WAVE;
     L.go((const void *)&k_tree_walk<T>, (unsigned)B, args);
     L.block = NT;
-  } else {  // the walk, then the draw, in each of the tree's chunk items
-    t.a.tag = next_tag();
+  } else {  // the walk (forming the residual masses it needs), then the draw
+    t.a.tag = sv_host::next_tag_block((unsigned)t.a.G + 1u);  // the call's tag, then one a round
     void *args[] = {&t};
     L.go(p.topk ? (const void *)&k_tree_draw<T, AL, true> : (const void *)&k_tree_draw<T, AL, false>,
          (unsigned)(LANES * lb * p.C), args);
@@ -925,12 +824,8 @@ sv_status tree_run(const void *target, const void *draft, sv_dtype dt, const int
   t.row_lt = (double *)(base + p.row_lt);
   t.row_arg = (int32_t *)(base + p.row_arg);
   t.row_ok = (int32_t *)(base + p.row_ok);
-  t.zc = (double *)(base + p.zc);
-  t.tw_z = (u64 *)(base + p.tw_z);
   t.tw_seg = (u64 *)(base + p.tw_seg);
-  t.act = p.resid ? (int32_t *)(base + p.act) : nullptr;
-  t.act_n = p.resid ? (int32_t *)(base + p.act_n) : nullptr;
-  t.kmax = p.kmax;
+  t.tw_lz = smp ? (u64 *)(base + p.tw_lz) : nullptr;
 
   hipStream_t st = (hipStream_t)stream;
   int n = 0;
@@ -994,20 +889,15 @@ const char *sv_tree_launch_plan(int32_t B, int32_t N, int32_t V, int32_t max_chi
   (void)B;
   (void)N;
   if (temperature == 0.0f) return "k_tree_rows;k_tree_walk";  // greedy: the walk alone
+  (void)max_children;
   const bool topk = top_k > 0 && top_k < V;
-  const bool resid = max_children > 1;
-  // [threshold: none, one select pass, 2 digit passes (bf16), 4 digit passes (f32)][resid]
-  static const char *names[4][2] = {
-      {"k_tree_rows;k_tree_draw", "k_tree_rows;k_tree_resid;k_tree_draw"},
-      {"k_topk_select;k_topk_merge;k_tree_rows;k_tree_draw",
-       "k_topk_select;k_topk_merge;k_tree_rows;k_tree_resid;k_tree_draw"},
-      {"k_topk_digit;k_topk_digit;k_tree_rows;k_tree_draw",
-       "k_topk_digit;k_topk_digit;k_tree_rows;k_tree_resid;k_tree_draw"},
-      {"k_topk_digit;k_topk_digit;k_topk_digit;k_topk_digit;k_tree_rows;k_tree_draw",
-       "k_topk_digit;k_topk_digit;k_topk_digit;k_topk_digit;k_tree_rows;k_tree_resid;k_tree_draw"}};
+  // [threshold: none, one select pass, 2 digit passes (bf16), 4 digit passes (f32)]
+  static const char *names[4] = {"k_tree_rows;k_tree_draw", "k_topk_select;k_topk_merge;k_tree_rows;k_tree_draw",
+                                 "k_topk_digit;k_topk_digit;k_tree_rows;k_tree_draw",
+                                 "k_topk_digit;k_topk_digit;k_topk_digit;k_topk_digit;k_tree_rows;k_tree_draw"};
   const int esz = dtype == SV_BF16 ? 2 : 4;
   const int th = !topk ? 0 : sv_host::topk_one_pass(top_k, sv_host::row_chunks(V, esz)) ? 1 : (esz == 2 ? 2 : 3);
-  return names[th][resid ? 1 : 0];
+  return names[th];
 }
 
 }  // extern "C"

@@ -1252,6 +1252,13 @@ unsigned next_tag() {
     if (t != 0u) return t;
   }
 }
+unsigned next_tag_block(unsigned n) {
+  for (;;) {
+    const unsigned long long c = g_launches.fetch_add((unsigned long long)n, std::memory_order_relaxed);
+    const unsigned t = (unsigned)(c + 1ull);
+    if (t != 0u && (unsigned long long)t + n - 1ull <= 0xffffffffull) return t;  // the block holds no 0
+  }
+}
 
 }  // namespace sv_host
 

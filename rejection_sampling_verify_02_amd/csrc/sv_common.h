@@ -779,6 +779,8 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // (never 0: a clean workspace holds zeros), so a word left in a shared workspace by any
 // earlier launch of any entry point can never pass for the current one's.
 unsigned next_tag();
+// n consecutive tags (none of them 0) for one launch; returns the first.
+unsigned next_tag_block(unsigned n);
 
 // Launches kernels in order on one stream.  With events, kernel i is launched with
 // (events[2i], events[2i+1]) as its start and stop events, which time the dispatch

@@ -213,8 +213,14 @@ def test_tree_optional_pointers_and_plan(lib):
     # path is optional; greedy reads no draft and no uniforms (stops at the workspace check)
     assert call_tree(lib, path=None, nbytes=16) == 5
     assert call_tree(lib, T=0.0, d=None, ua=None, us=None, nbytes=16) == 5
-    assert sv.sv_tree_launch_plan(16, 32, 128256, 4, sv.SV_BF16, 1.0, 0) == \
-        ["k_tree_rows", "k_tree_resid", "k_tree_draw"]
+    # the walk forms the residual masses it needs inside the draw's launch
+    assert sv.sv_tree_launch_plan(16, 32, 128256, 4, sv.SV_BF16, 1.0, 0) == ["k_tree_rows", "k_tree_draw"]
+    # nodes of two or more children need rows of at most 32 chunks (a tree's draw items wait
+    # for one another); chains (max_children 1) and greedy trees have no such limit
+    assert lib.sv_tree_workspace_bytes(3, 10, 600000, 3, sv.SV_BF16, 1.0, 0) == 256
+    assert lib.sv_tree_workspace_bytes(3, 10, 524288, 3, sv.SV_BF16, 1.0, 0) > 256
+    assert lib.sv_tree_workspace_bytes(3, 10, 600000, 1, sv.SV_BF16, 1.0, 0) > 256
+    assert lib.sv_tree_workspace_bytes(3, 10, 600000, 3, sv.SV_BF16, 0.0, 0) > 256
     assert sv.sv_tree_launch_plan(16, 32, 128256, 1, sv.SV_BF16, 1.0, 0) == ["k_tree_rows", "k_tree_draw"]
     assert sv.sv_tree_launch_plan(16, 32, 128256, 4, sv.SV_BF16, 0.0, 0) == ["k_tree_rows", "k_tree_walk"]
     assert sv.sv_tree_launch_plan(16, 32, 128256, 4, sv.SV_F32, 0.7, 5)[:3] == ["k_topk_select", "k_topk_merge", "k_tree_rows"]

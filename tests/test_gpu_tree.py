@@ -141,6 +141,9 @@ SHAPES = [
     (4, 8, 50000, "bf16", 5.0, 50, 3),     # very high temperature with top-k
     (3, 64, 9003, "f32", 0.8, 7, 8),       # 64 nodes, odd V, f32 top-k
     (2, 1, 1000, "bf16", 1.0, 0, 0),       # the root alone: a plain draw
+    (3, 10, 600000, "bf16", 1.0, 0, 1),    # 37 chunks a row: chains only (no residual masses)
+    (2, 12, 300000, "f32", 0.9, 20, 1),    # 37 chunks a row in f32, with top-k
+    (2, 12, 262144, "f32", 1.0, 0, 4),     # 32 chunks a row: the longest with several children
     (8, 16, 32000, "bf16", 0.0, 0, 3),     # greedy
     (5, 20, 152064, "f32", 0.0, 0, 4),     # greedy f32
 ]
