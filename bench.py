@@ -55,7 +55,7 @@ COUNTED = {
     "tree": dict(kernel="k_tree_rows", workload="tree_bf16_b16_n32", desc="16 trees of 32 nodes, V=128256, bf16",
                  alg=210698956, sources=("spec_tree.hip", "sv_draw.h") + _SHARED,
                  why="k_tree_rows reads every target row and the draft rows of nodes with children once; the "
-                     "residual rounds and the draw read their rows in launches of their own."),
+                     "residual masses the walk needs and the draw read their rows in k_tree_draw."),
     "typical": dict(kernel="k_typical", workload="typical_zipf_bf16_b64", desc="B=64, G=4, V=128256, bf16",
                     alg=82083840, sources=("spec_typical.hip",) + _SHARED,
                     why="Every logit is read once; the excess is the partials handed between workgroups."),
