@@ -74,6 +74,9 @@ SHAPES = [
     (8, 3, 9003, "f32", 0.8, 257),     # the smallest k of the radix digit passes
     (4, 2, 300000, "f32", 0.9, 100),   # 37 chunks per row
     (2, 1, 2200000, "f32", 0.9, 40),   # 269 chunks per row: the radix digit passes
+    (16, 0, 5000, "bf16", 1.0, 30),    # no drafts under top-k: the bonus from the kept list
+    (2, 300, 700, "bf16", 0.9, 20),    # 300 positions under top-k: a thread tests two
+    (2, 130, 3000, "f32", 1.1, 0),     # 130 positions: the scan's lanes take three rounds
 ]
 
 
