@@ -241,8 +241,11 @@ SVD void ov_second(const Args &a, int u, int c) {
   }
 }
 
+// Four resident waves per SIMD (at most 128 registers; a few spill): 44.5 us against 46.3 at
+// the three the compiler picks by itself, on the headline batch.  Five spill ~200 bytes a
+// lane and take 72 us.
 template <typename T, bool ALIGNED, bool TOPK>
-__global__ __launch_bounds__(NT) void k_overlap(const Args a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_overlap(const Args a) {
   int phase, unit, sub;
   if (!lane_item_lag(a.B * a.G, 2 * a.C, a.C, a.lag, phase, unit, sub)) return;
   if (phase == 1) {
