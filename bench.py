@@ -366,6 +366,105 @@ def summarize_trace(tdir: str, line_file: str, cmd: str, ref_file: str | None = 
     print(path)
 
 
+def run_timeline(args, dev) -> dict:
+    """Where one headline call's time goes, from the timeline build of the library
+    (libspec_verify_timeline.so: the product sources with wall-clock stamps at fixed
+    points of each sequence's path).  Per call: when the stream of partials ends, when the
+    call's last token is written, and for the sequence that finishes last, each step of its
+    tail.  Medians over the calls; microseconds from the grid's first stamp."""
+    import ctypes
+    import torch
+    import rejection_sampling_verify_02_amd as sv
+    from rejection_sampling_verify_02_amd import build as svb
+
+    sv._lib = sv.load_library(svb.LIB_TIMELINE)  # every binding call now goes through it
+    from rejection_sampling_verify_02_amd import workloads as wl
+    cfg = wl.CONFIGS[args.config]
+    B, G, V = cfg.B, cfg.G, cfg.V
+    n_sets = args.sets or 8
+    sets, _ = make_sets(args.config, n_sets, dev)
+    words = 8 + B * 512
+    stamps = torch.zeros((words,), dtype=torch.int64, device=dev)
+    khz = ctypes.c_int32(0)
+    rc = sv._lib.sv_timeline_stamps(ctypes.c_void_p(stamps.data_ptr()), ctypes.byref(khz))
+    if rc != 0:
+        raise RuntimeError(f"sv_timeline_stamps returned {rc}")
+    ticks_us = khz.value / 1000.0
+    ws = sv.Workspace()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    acc = torch.empty((B,), dtype=torch.int32, device=dev)
+    out = torch.empty((B, G + 1), dtype=torch.int32, device=dev)
+    C = -(-V * (2 if cfg.dtype == "bf16" else 4) // 32768)
+    rps, nd = 2 * G + 1, min(C * 4, 96)
+
+    def call(i):
+        s = sets[i % n_sets]
+        sv.spec_verify(s["target"], s["draft"], s["tokens"], s["u_accept"], s["u_sample"], cfg.temperature,
+                       cfg.top_k, workspace=ws, stream=stream, out=(acc, out))
+
+    for i in range(args.warmup):
+        call(i)
+    rec = {k: [] for k in ("stream_end", "call_end", "last_partial", "fin_parts", "fin_record", "draws_have_record",
+                           "masses_out", "combiner_in", "token_out")}
+    for i in range(args.steps):
+        stamps.zero_()
+        call(i)
+        torch.cuda.synchronize(dev)
+        h = stamps.cpu().numpy().astype(np.float64)
+        t0 = h[0]
+        us = lambda x: (x - t0) / ticks_us
+        last_parts, dones = [], []
+        for b in range(B):
+            base = 8 + 512 * b
+            fp = h[base: base + min(rps * C, 256)]
+            last_parts.append(us(fp[fp > 0].max()) if np.any(fp > 0) else np.nan)
+            dones.append(us(h[base + 461]) if h[base + 461] > 0 else np.nan)
+        bl = int(np.nanargmax(dones))
+        base = 8 + 512 * bl
+
+        def step(k):
+            return us(h[base + k]) if h[base + k] > 0 else np.nan
+
+        def most(lo):
+            v = h[base + lo: base + lo + nd]
+            return us(v[v > 0].max()) if np.any(v > 0) else np.nan
+
+        rec["stream_end"].append(np.nanmax(last_parts))
+        rec["call_end"].append(np.nanmax(dones))
+        rec["last_partial"].append(last_parts[bl])
+        rec["fin_parts"].append(step(257))
+        rec["fin_record"].append(step(258))
+        rec["draws_have_record"].append(most(260))
+        rec["masses_out"].append(most(360))
+        rec["combiner_in"].append(step(460))
+        rec["token_out"].append(step(461))
+    med = {k: round(float(np.nanmedian(v)), 3) for k, v in rec.items()}
+    res = {"workload": cfg.name, "calls": args.steps, "wall_clock_khz": khz.value, "median_us": med}
+    cmd = (f"python3 <repo>/bench.py --timeline --steps {args.steps} --warmup {args.warmup}"
+           + (f" --config {args.config}" if args.config != 3 else ""))
+    names = {"stream_end": "the last partial of any sequence is out (the stream's end)",
+             "call_end": "the call's last token is written",
+             "last_partial": "last sequence to finish: its last partial out",
+             "fin_parts": "its finisher has every partial",
+             "fin_record": "its finisher has combined, scanned and published the draw's record",
+             "draws_have_record": "its draw items have the record (the last of them)",
+             "masses_out": "its draw items' segment masses are out (the last of them)",
+             "combiner_in": "its combiner has every segment mass",
+             "token_out": "its token is written"}
+    lines = [f"# Timeline: k_verify, {cfg.name}", "",
+             "Command (repository root on the GPU box; the timeline build of the library, which the build "
+             "step compiles next to the product library):", "", "```", cmd, "```", "",
+             f"Wall clock stamps (`wall_clock64`, {khz.value} kHz) stored by the kernels of "
+             "`libspec_verify_timeline.so` at fixed points of each sequence's path (`sv_timeline_stamps`); "
+             f"microseconds from the grid's first stamp, medians over {args.steps} calls after {args.warmup} "
+             "warm-up calls.", "", "| point | µs |", "|---|---|"]
+    for k, v in med.items():
+        lines.append(f"| {names[k]} | {v} |")
+    lines.append("")
+    (ROOT / "profiles" / f"k_verify_{cfg.name}_timeline.md").write_text("\n".join(lines))
+    return res
+
+
 def copy_probe(nbytes: int, reps: int) -> None:
     """A plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
     import torch
@@ -938,6 +1037,8 @@ def main() -> int:
                     help="only run a plain copy of BYTES (counter calibration)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("BENCH_DIR", "COPY_DIR"),
                     help="write the traffic summary of --op from rocprofv3 --pmc CSV directories")
+    ap.add_argument("--timeline", action="store_true",
+                    help="where a call's time goes, from the timeline build of the library (writes profiles/)")
     ap.add_argument("--summarize-trace", nargs=3, metavar=("TRACE_DIR", "LINE_FILE", "COMMAND"),
                     help="write the kernel-trace summary of a rocprofv3 --kernel-trace run of this "
                          "script (its output line in LINE_FILE; COMMAND is quoted in the summary)")
@@ -962,6 +1063,9 @@ def main() -> int:
     import torch
     import rejection_sampling_verify_02_amd as sv
 
+    if args.timeline:
+        print(json.dumps(run_timeline(args, torch.device("cuda:0"))), flush=True)
+        return 0
     sv.load_library()  # raises if the HIP library is not built
     dev = torch.device("cuda:0")
     hev = HipEvents()

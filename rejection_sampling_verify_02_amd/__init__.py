@@ -34,7 +34,7 @@ EXPORTED = ("spec_verify", "spec_verify_timed", "sv_workspace_bytes", "sv_worksp
             "sv_tree_workspace_zero_bytes", "sv_tree_launch_plan",
             "spec_typical_verify", "spec_typical_verify_timed", "sv_typical_workspace_bytes",
             "sv_typical_workspace_zero_bytes", "sv_typical_launch_plan", "sv_tag_epoch",
-            "sv_read_probe", "spec_verify_noalloc")
+            "sv_read_probe", "spec_verify_noalloc", "sv_timeline_stamps")
 
 
 class SpecVerifyError(RuntimeError):
@@ -104,6 +104,8 @@ def load_library(path: Path | str | None = None) -> ctypes.CDLL:
     lib.sv_workspace_zero_bytes.restype = SZ
     lib.sv_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
     lib.sv_read_probe.restype = I32
+    lib.sv_timeline_stamps.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    lib.sv_timeline_stamps.restype = I32
     lib.sv_tag_epoch.argtypes = []
     lib.sv_tag_epoch.restype = ctypes.c_uint32
     lib.sv_status_string.argtypes = [I32]

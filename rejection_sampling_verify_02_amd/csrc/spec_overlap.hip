@@ -354,6 +354,7 @@ sv_status ov_run(const void *target, const void *draft, sv_dtype dt, int32_t B, 
   a.pair_status = pair_status;
   a.lag = OV_LAG;
   a.spin_limit = SPIN_LIMIT;
+  a.stamps = nullptr;
   a.w.tw_part = (u64 *)(base + p.tw_part);
   a.w.tw_ov = (u64 *)(base + p.tw_ov);
   a.w.tw_hist = (u64 *)(base + p.tw_hist);

@@ -811,6 +811,7 @@ sv_status tree_run(const void *target, const void *draft, sv_dtype dt, const int
   a.accepted_len = acc;
   a.out_tokens = out;
   a.spin_limit = SPIN_LIMIT;
+  a.stamps = nullptr;
   a.w.tw_part = (u64 *)(base + p.tw_part);
   a.w.tw_hist = (u64 *)(base + p.tw_hist);
   a.w.row_tau = (float *)(base + p.row_tau);

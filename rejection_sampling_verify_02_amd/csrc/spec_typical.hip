@@ -372,6 +372,7 @@ sv_status typ_run(const void *target, sv_dtype dt, const int32_t *tokens, int32_
   a.accepted_len = acc;
   a.out_tokens = out;
   a.spin_limit = SPIN_LIMIT;
+  a.stamps = nullptr;
   a.w.tw_part = (u64 *)(base + p.tw_part);
   a.w.tw_hist = (u64 *)(base + p.tw_hist);
   a.w.row_tau = (float *)(base + p.row_tau);

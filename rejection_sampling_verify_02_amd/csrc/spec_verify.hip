@@ -50,6 +50,24 @@
 
 namespace sv {
 
+// Timeline stamps, in the library built for timelines (-DSV_TIMELINE) only: the first lane
+// of a wave stores the wall clock (wall_clock64) at fixed points of each sequence's path
+// into a caller's buffer, word 0 when the grid starts and, for sequence b, words TL_SEQ(b)
+// + TL_*: first-pass item (row jr, chunk c) at jr*C + c when that is below 256, the
+// finisher's entry, its last partial in and its record out, draw item i (c*4 + sub) at
+// TL_DRAW_SEEN + i when it has the record and TL_DRAW_PUB + i when its masses are out (i <
+// 96), the combiner with every mass in and the sequence's token written.  In the
+// library's own build the stamps compile to nothing.
+#ifdef SV_TIMELINE
+#define SV_TL(a, idx) do { if ((a).stamps && lane_id() == 0) st_dev(&(a).stamps[(idx)], (unsigned long long)wall_clock64()); } while (0)
+#else
+#define SV_TL(a, idx) do { } while (0)
+#endif
+constexpr size_t TL_STRIDE = 512;  // words a sequence
+SVD size_t TL_SEQ(int b) { return 8 + (size_t)b * TL_STRIDE; }
+enum : int { TL_FIN_IN = 256, TL_FIN_PARTS = 257, TL_FIN_REC = 258, TL_DRAW_SEEN = 260, TL_DRAW_PUB = 360,
+             TL_COMB_IN = 460, TL_DONE = 461, TL_DRAW_MAX = 96 };
+
 constexpr int NSUB = 4;                // second-pass workgroups per chunk of a rejected pair
 constexpr int KSUB = VPT / NSUB;       // vectors per thread of each of them
 enum : int { JOB_NONE = 0, JOB_REJECT = 1, JOB_BONUS = 2 };  // NONE: nothing to draw (a row error, or G = 0)
@@ -284,6 +302,7 @@ SVD void sampling_finish(const Args &a, int b, float own_off, float own_hi, floa
     zd = in ? Fmt<T>::at(seq_row<T>(a, b, G + 1 + p), (size_t)x) : NAN;
   };
 
+  SV_TL(a, TL_SEQ(b) + TL_FIN_IN);
   // Wait for the partials (blocks of SEQ_LDS_PARTS, every load of a block in flight at
   // once); stage them in LDS when the sequence fits.
   bool alive = true;
@@ -325,6 +344,7 @@ SVD void sampling_finish(const Args &a, int b, float own_off, float own_hi, floa
       __builtin_amdgcn_s_sleep(2);
     }
   }
+  SV_TL(a, TL_SEQ(b) + TL_FIN_PARTS);
   if (lds && alive) {
     for (int jr = lane; jr < rps; jr += WAVE) s_rtau[jr] = TOPK ? a.w.row_tau[r0 + jr] : -INFINITY;
     for (int p = lane; p < G; p += WAVE) {
@@ -534,6 +554,7 @@ SVD void sampling_finish(const Args &a, int b, float own_off, float own_hi, floa
     default: break;
   }
   if (lane < JW_USED) tw_put(&jw[lane], tag, bits);
+  SV_TL(a, TL_SEQ(b) + TL_FIN_REC);
   for (int i = lane; i <= G; i += WAVE) {
     if (!err && i == j) continue;  // written by the draw, with accepted_len
     out[i] = (!err && i < j) ? ((i < WAVE) ? x0 : a.tokens[(size_t)b * G + i]) : -1;
@@ -624,6 +645,7 @@ SVD void norm_item(const Args &a, int item) {
     }
     u64 *pw = a.w.tw_part + ((size_t)r * a.C + c) * 3;
     if (lane < 3) tw_putf(pw + lane, a.tag, lane == 0 ? off : (lane == 1 ? s_hi : s_lo));
+    if (jr * a.C + c < TL_FIN_IN) SV_TL(a, TL_SEQ(b) + jr * a.C + c);
     if (G0 && lane < 2 * SEGS) {
       u64 *gw = a.w.tw_gseg + (((size_t)b * a.C + c) * SEGS) * 2;
       const double v = s_gseg[lane >> 1];
@@ -854,6 +876,7 @@ SVD void combine_draw(const Args &a, int b, int j, float u, const T *row_t, cons
     return;
   }
   lds_sync();
+  SV_TL(a, TL_SEQ(b) + TL_COMB_IN);
   auto seg_of = [&](int i) -> double {
     if (FITS || i < COMB_LDS_SEGS) return s_cs[i];
     if (mine(i)) return s_seg[i - cown * SEGS];
@@ -877,6 +900,7 @@ SVD void combine_draw(const Args &a, int b, int j, float u, const T *row_t, cons
     a.out_tokens[(size_t)b * (G + 1) + j] = tok;
     a.accepted_len[b] = j;
   }
+  SV_TL(a, TL_SEQ(b) + TL_DONE);
 }
 
 // Draw item (sequence b, chunk c, quarter sub).  All draw items follow every first-pass
@@ -918,6 +942,7 @@ SVD void draw_item(const Args &a, int item) {
     if (lane == 0) s_ready = ready ? 1 : 0;
   }
   __syncthreads();
+  if (c * NSUB + sub < TL_DRAW_MAX && wid == 0) SV_TL(a, TL_SEQ(b) + TL_DRAW_SEEN + c * NSUB + sub);
   if (!s_ready) {  // gave up: report it instead of drawing
     if (tid == 0) a.accepted_len[b] = SV_ROW_INTERNAL;
     return;
@@ -955,6 +980,7 @@ SVD void draw_item(const Args &a, int item) {
       out[G] = tok;
       a.accepted_len[b] = G;
     }
+    SV_TL(a, TL_SEQ(b) + TL_DONE);
     return;
   }
 
@@ -977,6 +1003,7 @@ SVD void draw_item(const Args &a, int item) {
       const double m = s_seg[sub * KSUB * NW + (lane >> 1)];
       tw_putf(&sw[(size_t)own0 * 2 + lane], tag, (lane & 1) ? d_tail(m) : d_head(m));
     }
+    if (c * NSUB + sub < TL_DRAW_MAX) SV_TL(a, TL_SEQ(b) + TL_DRAW_PUB + c * NSUB + sub);
     return;
   }
   // The sequence's last draw item combines (its own masses stay in LDS, unpublished).
@@ -995,6 +1022,7 @@ SVD void draw_item(const Args &a, int item) {
 template <typename T, bool ALIGNED, bool TOPK, bool G0>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(TOPK ? 5 : 4))) void k_verify(const Args a) {
   int phase, item;
+  if (blockIdx.x == 0 && threadIdx.x < WAVE) SV_TL(a, 0);
   if (!lane_item(a.B, a.rps * a.C, G0 ? 0 : a.C * NSUB, phase, item)) return;
   if (phase == 1) norm_item<T, ALIGNED, TOPK, G0>(a, item);
   else if (!G0) draw_item<T, ALIGNED>(a, item);
@@ -1246,6 +1274,7 @@ namespace sv_host {
 // Launches counted over the process; a launch's tag is the count's low 32 bits (never 0),
 // so a tag value comes back after 2^32 - 1 launches (see sv_tag_epoch).
 std::atomic<unsigned long long> g_launches{0};
+unsigned long long *g_stamps = nullptr;  // timeline stamps (the timeline build only)
 unsigned next_tag() {
   for (;;) {
     const unsigned t = (unsigned)(g_launches.fetch_add(1ull, std::memory_order_relaxed) + 1ull);
@@ -1417,6 +1446,7 @@ sv_status run(const void *target, const void *draft, sv_dtype dt, const int32_t 
   a.lag = 0;
   a.tag = 0u;  // each launch takes its own
   a.spin_limit = SPIN_LIMIT;
+  a.stamps = sv_host::g_stamps;
   a.w.tw_part = (u64 *)(base + p.tw_part);
   a.w.tw_job = (u64 *)(base + p.tw_job);
   a.w.tw_seg = (u64 *)(base + p.tw_seg);
@@ -1469,6 +1499,24 @@ std::mutex g_scratch_mu;
 }  // namespace
 
 extern "C" {
+
+int32_t sv_timeline_stamps(void *buf, int32_t *clock_khz) {
+#ifdef SV_TIMELINE
+  if (clock_khz) {
+    int dev = 0, khz = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
+      return 7;
+    *clock_khz = khz;
+  }
+  sv_host::g_stamps = static_cast<unsigned long long *>(buf);
+  return 0;
+#else
+  (void)buf;
+  (void)clock_khz;
+  return 1;
+#endif
+}
 
 sv_status spec_verify_noalloc(const void *target_logits, const void *draft_logits, sv_dtype dtype,
                               const int32_t *draft_tokens, const float *u_accept,

@@ -49,6 +49,7 @@ struct Args {
   int lag;                     // overlap: pairs between a pair's two phases in an XCD lane
   unsigned tag;                // this call's tag (never 0): marks the words it publishes
   unsigned spin_limit;         // polls a waiting wave makes before giving up
+  unsigned long long *stamps;  // timeline stamps (the timeline build of the library), or null
   Work w;
 };
 
