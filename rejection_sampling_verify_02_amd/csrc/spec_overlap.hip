@@ -17,17 +17,19 @@
 //     the verification kernel);
 //   second-phase items, one per chunk c of a pair: issue the loads of both rows' chunk c,
 //     then one wave per row combines that row's partials into its log2-partition, and the
-//     workgroup sums min(p, q) and p - min(p, q) over the chunk; the pair's last chunk
-//     collects the others' sums and writes beta, tv and the pair's status.
+//     workgroup sums min(p, q) over the chunk with one exponential per element pair (the
+//     smaller of the two arguments); the chunk's tv term is p's chunk mass from the first
+//     phase less that sum; the pair's last chunk collects the others' sums and writes
+//     beta, tv and the pair's status.
 // Every row is read twice, and much of the second read is served from the XCD's L2: in
 // each XCD lane (lane_item_lag) a pair's second phase comes OV_LAG pairs after its first,
-// a few MB of that lane's traffic later, and both phases use ordinary cached loads.
-// Measured HBM traffic is 1.55x one read of the rows at OV_LAG = 4 (1.03x at OV_LAG = 2,
-// where the second phase waits longer for the first and the kernel is slower).  The
-// second phase recomputes p and q (two v_exp_f32 per element pair), so the kernel is
-// bound by VALU and waits more than by HBM.  A design that keeps the first phase's terms
-// in registers and waits for the pair's other workgroups was measured slower still:
-// every workgroup then holds its slot through a device-scope round trip.
+// a few MB of that lane's traffic later.  The first phase loads with ordinary cached loads
+// and the second, the data's last use, with non-temporal ones, so that it does not push
+// out rows still waiting for their second read.  With one v_exp_f32 per logit in the
+// first phase and one per element pair in the second, the kernel is bound by VALU and
+// waits more than by HBM.  A design that keeps the first phase's terms in registers and
+// waits for the pair's other workgroups was measured slower: every workgroup then holds
+// its slot through a device-scope round trip.
 // All reductions have fixed orders: results are bitwise reproducible.
 
 #include <hip/hip_runtime.h>
@@ -39,8 +41,8 @@
 
 namespace sv {
 
-constexpr int OV_LAG = 4;  // pairs between a pair's first and second phase in a lane (1, 2,
-                           // 4 and 8 measured: 4 is best)
+constexpr int OV_LAG = 5;  // pairs between a pair's first and second phase in a lane (2 to
+                           // 12 measured: 5 and 6 are best)
 
 // First phase: the normaliser partial of chunk c of row r (in the pair's numbering),
 // formed as the verification kernel forms it (chunk_norm), with cached loads: the second
@@ -57,11 +59,13 @@ SVD void ov_first(const Args &a, int r, const T *row, int c) {
 }
 
 // One wave: the log2-partition of row r from its chunks' partials (lanes over chunks,
-// then one fixed tree), waiting until every partial carries the call's tag.  Returns
-// false if the wait gave up.
-SVD bool row_partition(const Args &a, int r, float &o, double &t) {
+// then one fixed tree), waiting until every partial carries the call's tag, and chunk
+// c's own partial (its offset and sum) as published.  Returns false if the wait gave up.
+SVD bool row_partition(const Args &a, int r, int c, float &o, double &t, float &off_c, double &s_c) {
   const int lane = lane_id();
   unsigned polls = 0;
+  float my_off = -INFINITY;
+  double my_s = 0.0;
   for (;;) {
     o = -INFINITY;
     t = 0.0;
@@ -70,25 +74,44 @@ SVD bool row_partition(const Args &a, int r, float &o, double &t) {
       const u64 *pw = a.w.tw_part + ((size_t)r * a.C + cc) * 3;
       const u64 w0 = ld_dev(pw), w1 = ld_dev(pw + 1), w2 = ld_dev(pw + 2);
       mine = mine && tw_ok(w0, a.tag) && tw_ok(w1, a.tag) && tw_ok(w2, a.tag);
-      lse_combine(o, t, tw_f(w0), d_join(tw_f(w1), tw_f(w2)));
+      const float f0 = tw_f(w0);
+      const double sd = d_join(tw_f(w1), tw_f(w2));
+      if (cc == c) {
+        my_off = f0;
+        my_s = sd;
+      }
+      lse_combine(o, t, f0, sd);
     }
     if (wave_or(mine ? 0u : 1u) == 0u) break;
     if (++polls >= a.spin_limit) return false;
     __builtin_amdgcn_s_sleep(2);
   }
   wave_lse(o, t);
+  off_c = readlane_f(my_off, c % WAVE);
+  s_c = readlane_d(my_s, c % WAVE);
   return true;
 }
 
-// Second phase: chunk c of pair u.  min(p, q) and p - min(p, q) per element with
-// p = 2^(z_t*k2 - log2 Z_p) and q likewise, the log2-partitions split into a float head
-// and tail so that each argument carries only its own rounding.
+// Second phase: chunk c of pair u, with one exponential per element pair.  With
+// off_t, off_d the chunk's first-phase offsets and Lp, Lq the rows' log2-partitions,
+// p_v = 2^(at_v + dt) and q_v = 2^(ad_v + dd), where at_v = z_t*k2 - off_t is the very
+// argument the first phase exponentiated, ad_v = z_d*k2 - off_d, dt = off_t - Lp and
+// dd = off_d - Lq.  Then min(p_v, q_v) = 2^dt * 2^min(at_v, z_d*k2 - (off_d - dd + dt)),
+// the second argument one fma with the shift off_d - dd + dt rounded to fp32 once per
+// chunk (exactly off_d when dd = dt, as for p = q): the chunk's
+// beta term is 2^dt * B with B = sum_v 2^min(...), and its tv term sum_v [p_v - q_v]_+ =
+// sum_v (p_v - min(p_v, q_v)) is 2^dt * (S - B), S being the first phase's sum of
+// 2^at_v over the chunk.  B is summed in the first phase's order (per thread, then the
+// waves), so where q_v >= p_v throughout the chunk B equals S bit for bit and the tv term
+// is exactly 0 (p = q bitwise gives tv = 0).
 template <typename T, bool ALIGNED, bool TOPK>
 SVD void ov_second(const Args &a, int u, int c) {
   constexpr int VEC = Fmt<T>::VEC;
-  __shared__ float s_nrm[4];  // head and tail of log2 Z for p, then q
-  __shared__ int s_flags;     // bit 0: a row is unusable, bit 1: a wait gave up
-  __shared__ double s_sum[2 * NW];
+  __shared__ float s_off[2];  // the chunk's offsets in p's and q's rows (0 for an empty chunk)
+  __shared__ double s_dl[2];  // dt, dd
+  __shared__ double s_sc;     // S of p's chunk
+  __shared__ int s_flags;     // 1: a row is unusable, 2: a wait gave up, 4 / 8: p's / q's chunk is empty
+  __shared__ double s_sum[NW];
   const int tid = threadIdx.x, lane = lane_id(), wid = tid / WAVE;
   const int b = u / a.G, i = u - b * a.G;
   const int rt = b * a.rps + i, rd = rt + a.G;
@@ -105,48 +128,52 @@ SVD void ov_second(const Args &a, int u, int c) {
     for (int k = 0; k < VPT; ++k) {
       const int v = c * CHUNK_VECS + k * NT + tid;
       const int vs = v < a.nvec ? v : a.nvec - 1;
-      wa[k] = ra[vs];
-      wb[k] = rb[vs];
+      wa[k] = __builtin_nontemporal_load(ra + vs);
+      wb[k] = __builtin_nontemporal_load(rb + vs);
     }
   }
   if (tid == 0) s_flags = 0;
   __syncthreads();
   if (wid < 2) {
-    float o;
-    double t;
-    const bool done = row_partition(a, wid == 0 ? rt : rd, o, t);
+    float o, offc = -INFINITY;
+    double t, sc = 0.0;
+    const bool done = row_partition(a, wid == 0 ? rt : rd, c, o, t, offc, sc);
     const bool ok = done && isfinite(o) && isfinite(t) && t > 0.0;
     if (lane == 0) {
-      const double l2z = ok ? (double)o + log2(t) : 0.0;
-      s_nrm[2 * wid] = d_head(l2z);
-      s_nrm[2 * wid + 1] = d_tail(l2z);
+      const bool empty = !(offc > -INFINITY);
+      s_off[wid] = empty ? 0.0f : offc;
+      s_dl[wid] = (ok && !empty) ? (double)offc - ((double)o + log2(t)) : 0.0;
+      if (wid == 0) s_sc = sc;
       if (!done) atomicOr(&s_flags, 2);
       else if (!ok) atomicOr(&s_flags, 1);
+      if (empty) atomicOr(&s_flags, 4 << wid);
     }
   }
   __syncthreads();
   const int flags = s_flags;
-  float sb = 0.0f, st = 0.0f;
+  float acc = 0.0f;
   if (flags == 0) {
     const float k2 = a.k2;
-    const float mt_hi = s_nrm[0], mt_lo = s_nrm[1], md_hi = s_nrm[2], md_lo = s_nrm[3];
+    const float off_t = s_off[0], off_d = s_off[1];
+    const float sh_d = (float)((double)off_d - (s_dl[1] - s_dl[0]));
     const float tau_t = TOPK ? a.w.row_tau[rt] : -INFINITY;
     const float tau_d = TOPK ? a.w.row_tau[rd] : -INFINITY;
-    const bool tail = (c + 1) * CHUNK_VECS > a.nvec;
+    if (ALIGNED && (c + 1) * CHUNK_VECS > a.nvec) {  // vectors past the row's end hold -inf
+      constexpr unsigned NEG_INF = (sizeof(T) == 2) ? 0xff80ff80u : 0xff800000u;
+      const u32x4 ninf = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) {
+        const bool in = c * CHUNK_VECS + k * NT + tid < a.nvec;
+        wa[k] = in ? wa[k] : ninf;
+        wb[k] = in ? wb[k] : ninf;
+      }
+    }
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
       float xa[VEC], xb[VEC];
       if (ALIGNED) {
         Fmt<T>::unpack(wa[k], xa);
         Fmt<T>::unpack(wb[k], xb);
-        if (tail) {
-          const bool in = c * CHUNK_VECS + k * NT + tid < a.nvec;
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) {
-            xa[e] = in ? xa[e] : -INFINITY;
-            xb[e] = in ? xb[e] : -INFINITY;
-          }
-        }
       } else {
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
@@ -157,37 +184,38 @@ SVD void ov_second(const Args &a, int u, int c) {
           xb[e] = in ? Fmt<T>::at(row_d, at) : -INFINITY;
         }
       }
-      float tb[VEC], tv[VEC];
+      float tb[VEC];
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
         const float zt = (TOPK && xa[e] < tau_t) ? -INFINITY : xa[e];
         const float zd = (TOPK && xb[e] < tau_d) ? -INFINITY : xb[e];
-        const float p = fast_exp2(fmaf(zt, k2, -mt_hi) - mt_lo);
-        const float q = fast_exp2(fmaf(zd, k2, -md_hi) - md_lo);
-        const float mn = fminf(p, q);
-        tb[e] = mn;
-        tv[e] = p - mn;
+        tb[e] = fast_exp2(fminf(fmaf(zt, k2, -off_t), fmaf(zd, k2, -sh_d)));
       }
 #pragma unroll
       for (int h = VEC / 2; h > 0; h >>= 1)
 #pragma unroll
-        for (int e = 0; e < h; ++e) {
-          tb[e] += tb[e + h];
-          tv[e] += tv[e + h];
-        }
-      sb += tb[0];
-      st += tv[0];
+        for (int e = 0; e < h; ++e) tb[e] += tb[e + h];
+      acc += tb[0];
     }
   }
-  const double wb_ = wave_sum((double)sb), wt_ = wave_sum((double)st);
-  if (lane == 0) {
-    s_sum[wid] = wb_;
-    s_sum[NW + wid] = wt_;
-  }
+  const double wsum = wave_sum((double)acc);
+  if (lane == 0) s_sum[wid] = wsum;
   __syncthreads();
   if (wid != 0) return;
-  const double cb = (s_sum[0] + s_sum[1]) + (s_sum[2] + s_sum[3]);
-  const double ct = (s_sum[4] + s_sum[5]) + (s_sum[6] + s_sum[7]);
+  // beta and tv terms of the chunk; nothing where p's chunk is empty, all of p's mass as
+  // tv where q's chunk is empty.
+  double cb = 0.0, ct = 0.0;
+  if ((flags & 7) == 0) {
+    const double scale = exp2(s_dl[0]);
+    if (flags & 8) {
+      ct = scale * s_sc;
+    } else {
+      const double B = (s_sum[0] + s_sum[1]) + (s_sum[2] + s_sum[3]);
+      const double Bj = d_join(d_head(B), d_tail(B));  // rounded as S was for its partial
+      cb = scale * Bj;
+      ct = scale * (s_sc - Bj);
+    }
+  }
   u64 *ow = a.w.tw_ov + (size_t)u * a.C * 4;
   if (c != a.C - 1) {
     if (lane < 4) {
@@ -200,7 +228,7 @@ SVD void ov_second(const Args &a, int u, int c) {
   // The pair's last chunk: the other chunks' sums, lanes over chunks, one fixed tree.
   double sbeta = 0.0, stv = 0.0;
   bool gave_up = false;
-  if (flags == 0) {
+  if ((flags & 3) == 0) {
     unsigned polls = 0;
     for (;;) {
       sbeta = 0.0;
@@ -241,9 +269,9 @@ SVD void ov_second(const Args &a, int u, int c) {
   }
 }
 
-// Four resident waves per SIMD (at most 128 registers; a few spill): 44.5 us against 46.3 at
-// the three the compiler picks by itself, on the headline batch.  Five spill ~200 bytes a
-// lane and take 72 us.
+// At least four resident waves per SIMD: on aligned rows the kernel fits in 96 registers
+// and runs five, with nothing spilled.  Six (80 registers) spill and take 47.7 us against 35.6 on the
+// headline batch.
 template <typename T, bool ALIGNED, bool TOPK>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_overlap(const Args a) {
   int phase, unit, sub;

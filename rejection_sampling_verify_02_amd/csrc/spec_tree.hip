@@ -231,7 +231,7 @@ SVD void walk_setup(const TreeArgs &t, int b, WalkLds &W) {
   const int32_t *tok = a.tokens + (size_t)b * N;
   const size_t r0 = (size_t)b * a.rps;
   unsigned flags = 0, f1 = 0;  // 1 token, 2 row, 4 uniform, 8 q(x) = 0, 16 internal, 32 tree
-  int okt_l = 0, okd_l = 0;    // this lane's last node (N <= 64: its only one)
+  int okd_l = 0;               // this lane's last node (N <= 64: its only one)
   for (int n = lane; n < N; n += WAVE) {
     const int p = par[n];
     const int x = tok[n];
@@ -242,7 +242,6 @@ SVD void walk_setup(const TreeArgs &t, int b, WalkLds &W) {
     if (n == 0 ? (p != -1) : (p < 0 || p >= n)) flags |= 32;
     if (n > 0 && (x < 0 || x >= V)) f1 |= 1;
     f1 |= (okt == -2) ? 16 : (okt != 1 ? 2 : 0);
-    okt_l = okt;
     if (GREEDY) {
       W.lp[n] = (double)t.row_arg[r0 + n];
     } else {
@@ -276,7 +275,6 @@ SVD void walk_setup(const TreeArgs &t, int b, WalkLds &W) {
       const int nch = W.nch[n];
       if (!GREEDY && nch > t.S) flags |= 32;
       if (!GREEDY && nch > 0) {
-        const int okt = (N <= WAVE) ? okt_l : t.row_ok[r0 + n];
         const int okd = (N <= WAVE) ? okd_l : t.row_ok[r0 + N + n];
         flags |= (okd == -2) ? 16 : (okd != 1 ? 2 : 0);
         if (TOPK && W.taud[n] != W.taud[n]) flags |= 16;
@@ -516,7 +514,6 @@ __global__ __launch_bounds__(NT) void k_tree_draw(const TreeArgs t) {
     int zu = -1, round = 0;
     u32x4 wt[ALIGNED ? VPT : 1], wd[ALIGNED ? VPT : 1];
     auto zfn = [&](int u, int, double cval) -> double {
-      const size_t rt = (size_t)b * a.rps + u, rd = rt + N;
       const T *row_t = seq_row<T>(a, b, u), *row_d = seq_row<T>(a, b, N + u);
       if (ALIGNED && zu != u) {
         constexpr unsigned NEG_INF = (sizeof(T) == 2) ? 0xff80ff80u : 0xff800000u;

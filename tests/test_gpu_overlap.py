@@ -1,13 +1,17 @@
 """GPU parity of the per-position overlap ``spec_overlap`` against the oracle's ``overlap``.
 
 All calls go through the C ABI.  Pair statuses must match exactly.  beta and tv must
-match the oracle's fp64 values within TOL: the kernels form each p_v and q_v in fp32
-from a once-rounded log2(e)/T and an fp64 log-partition, with one v_exp_f32 per value;
-the per-element relative errors (argument rounding, exp, the temperature rounding seen
-as a perturbed T) are at most a few 1e-7 on the mass-carrying terms, and the fp32
-vector sums add about 1e-6 relative, so both sums are within ~3e-6 of exact, and
-TOL = 1e-5 leaves a margin of three.  Where p and q are bitwise the same the kernels give
-tv = 0 exactly, and where their supports are disjoint beta = 0 exactly.
+match the oracle's fp64 values within TOL: the kernels form every term in fp32 from a
+once-rounded log2(e)/T and fp64 log-partitions -- the normalisers from one v_exp_f32 per
+logit, min(p_v, q_v) as one v_exp_f32 of the smaller of the two exponents, the draft
+side's exponent shifted by a per-chunk constant rounded to fp32 once (at most ~7e-7
+relative on q_v), and a chunk's tv term as p's chunk mass less the chunk's sum of the
+minima, both summed in the same order.  The per-element relative errors (argument
+rounding, exp, the temperature rounding seen as a perturbed T) stay below ~1e-6 on the
+mass-carrying terms, and the fp32 vector sums add about 1e-6 relative, so both sums are
+within ~3e-6 of exact, and TOL = 1e-5 leaves a margin of three.  Where p and q are
+bitwise the same the kernels give tv = 0 exactly, and where their supports are disjoint
+beta = 0 exactly.
 """
 import numpy as np
 import pytest
