@@ -56,7 +56,8 @@ namespace sv {
 // + TL_*: first-pass item (row jr, chunk c) at jr*C + c when that is below 256, the
 // finisher's entry, its last partial in and its record out, draw item i (c*4 + sub) at
 // TL_DRAW_SEEN + i when it has the record and TL_DRAW_PUB + i when its masses are out (i <
-// 96), the combiner with every mass in and the sequence's token written.  In the
+// 96), the combiner with every mass in and the sequence's token written (with no drafts:
+// the finisher with the picked chunk's segment masses in, and the token written).  In the
 // library's own build the stamps compile to nothing.
 #ifdef SV_TIMELINE
 #define SV_TL(a, idx) do { if ((a).stamps && lane_id() == 0) st_dev(&(a).stamps[(idx)], (unsigned long long)wall_clock64()); } while (0)
@@ -595,6 +596,7 @@ SVD void sampling_finish(const Args &a, int b, float own_off, float own_hi, floa
       if (lane == 0) a.accepted_len[b] = SV_ROW_INTERNAL;
       return;
     }
+    SV_TL(a, TL_SEQ(b) + TL_COMB_IN);
     auto segm = [&](int) { return segv; };
     double ts;
     const int sp = wave_pick(SEGS, t_bonus, segm, &ts);
@@ -606,6 +608,7 @@ SVD void sampling_finish(const Args &a, int b, float own_off, float own_hi, floa
     out[G] = tok;
     a.accepted_len[b] = G;
   }
+  SV_TL(a, TL_SEQ(b) + TL_DONE);
 }
 
 // ---------------------------------------------------------------- pass 1: normaliser
