@@ -47,7 +47,8 @@ namespace sv {
 enum : int { TJ_NONE = 0, TJ_TARGET = 1, TJ_RESID = 2 };
 constexpr int TREE_MAX_NODES = 1024;   // nodes per tree (the walk keeps them in LDS)
 constexpr int TREE_DRAW_LDS_SEGS = 2048;  // segment masses the draw's collector keeps in LDS
-constexpr int TREE_LAZY_MAX_C = 32;    // chunks a row at most when nodes may have two or more children
+constexpr int TREE_LAZY_MAX_C = 32;    // chunks a row, and draw items a tree, at most when nodes may
+                                       // have two or more children
 
 struct TreeArgs {
   Args a;                  // rows per tree: rps = 2N (N target rows, then N draft rows); a.G = N
@@ -62,8 +63,8 @@ struct TreeArgs {
                            //   -2 a wait gave up
   // tagged words within one launch
   u64 *tw_seg;             // [B*C*SEGS*2] per tree, chunk and segment: the draw's masses
-  u64 *tw_lz;              // [B*2*C*2] residual masses formed by the walk: per tree two slots
-                           //   (alternating rounds), per chunk item a tagged double
+  u64 *tw_lz;              // [B*2*C*TS*2] residual masses formed by the walk: per tree two
+                           //   slots (alternating rounds), per draw item a tagged double
 };
 
 // The nodes' children, counted by one wave: nch = children of node u in tree b.
@@ -478,30 +479,35 @@ SVD double wave_chunk_mass(const Args &a, const T *row, int c, const WFn &wf) {
   return tot;
 }
 
-// Sampling (T > 0): the walk and the draw of each tree by its C chunk items (item c owns
-// chunk c of every row of the tree).  Every item walks the tree (its first wave stages what
-// the walk reads; then all its waves walk in step; chunk 0's item writes the accepted
-// tokens and path).
+// Sampling (T > 0): the walk and the draw of each tree by its C * TS items, TS = VPT / KS
+// to a chunk (item (c, sub) owns vectors sub*KS .. sub*KS + KS - 1 of chunk c of every row
+// of the tree, so that small trees still spread over the device).  Every item walks the
+// tree (its first wave stages what the walk reads; then all its waves walk in step; the
+// first item writes the accepted tokens and path).
 // A residual mass is formed when the walk needs it, by all the tree's items together: each
-// sums [p_u - c q_u]_+ over its chunk of node u's two rows (the raw vectors stay in
+// sums [p_u - c q_u]_+ over its part of node u's two rows (the raw vectors stay in
 // registers while the walk stays at u; p and q formed from the rows' log2-partitions as
 // the draw forms them), publishes the sum as a tagged double (round r of the call uses tag
 // + 1 + r; two slots, alternating by round), and waits for the others' sums of the round;
-// every item adds them in chunk order, so all take the same decisions.  The walk needs
+// every item adds them in item order, so all take the same decisions.  The walk needs
 // one mass per rejection before a node's last child, so most nodes never have theirs
 // formed.  A tree's items are consecutive blocks of one XCD lane, and they wait for one
-// another only when a node has two or more children, which the host allows only for rows
-// of at most TREE_LAZY_MAX_C chunks (every wait is bounded).
-// Then the draw: segment masses of the item's chunk of the chosen weights; the last chunk
-// picks segment, lane and element.
-template <typename T, bool ALIGNED, bool TOPK>
+// another only when a node has two or more children, which the host allows only for at
+// most TREE_LAZY_MAX_C items a tree (every wait is bounded).
+// Then the draw: segment masses of the item's part of the chosen weights; the tree's last
+// item picks segment, lane and element.
+template <typename T, bool ALIGNED, bool TOPK, int KS>
 __global__ __launch_bounds__(NT) void k_tree_draw(const TreeArgs t) {
   constexpr int VEC = Fmt<T>::VEC;
+  constexpr int TS = VPT / KS;  // items a chunk
+  static_assert(KS >= 1 && VPT % KS == 0, "a chunk splits into whole parts");
   const Args &a = t.a;
   int phase, item;
-  if (!lane_item(a.B, a.C, 0, phase, item)) return;  // units: trees
+  if (!lane_item(a.B, a.C * TS, 0, phase, item)) return;  // units: trees
   const int tid = threadIdx.x, lane = lane_id(), wid = tid / WAVE;
-  const int b = item / a.C, c = item - b * a.C;
+  const int NI = a.C * TS;  // items a tree
+  const int b = item / NI, ii = item - b * NI;  // ii: the item's index in its tree
+  const int c = ii / TS, kb = (ii - c * TS) * KS;
   const int N = a.G;
   __shared__ WalkLds W;
   __shared__ double s_w[NW], s_z;
@@ -512,22 +518,22 @@ __global__ __launch_bounds__(NT) void k_tree_draw(const TreeArgs t) {
   if (!err) {
     // chunk c of node zu's two rows, loaded at the first mass formed at zu
     int zu = -1, round = 0;
-    u32x4 wt[ALIGNED ? VPT : 1], wd[ALIGNED ? VPT : 1];
+    u32x4 wt[ALIGNED ? KS : 1], wd[ALIGNED ? KS : 1];
     auto zfn = [&](int u, int, double cval) -> double {
       const T *row_t = seq_row<T>(a, b, u), *row_d = seq_row<T>(a, b, N + u);
       if (ALIGNED && zu != u) {
         constexpr unsigned NEG_INF = (sizeof(T) == 2) ? 0xff80ff80u : 0xff800000u;
         const u32x4 *ra = reinterpret_cast<const u32x4 *>(row_t), *rb = reinterpret_cast<const u32x4 *>(row_d);
 #pragma unroll
-        for (int kk = 0; kk < VPT; ++kk) {
-          const int v = c * CHUNK_VECS + kk * NT + tid;
+        for (int kk = 0; kk < KS; ++kk) {
+          const int v = c * CHUNK_VECS + (kb + kk) * NT + tid;
           const int vs = v < a.nvec ? v : a.nvec - 1;
           wt[ALIGNED ? kk : 0] = ra[vs];
           wd[ALIGNED ? kk : 0] = rb[vs];
         }
 #pragma unroll
-        for (int kk = 0; kk < VPT; ++kk)
-          if (c * CHUNK_VECS + kk * NT + tid >= a.nvec) {
+        for (int kk = 0; kk < KS; ++kk)
+          if (c * CHUNK_VECS + (kb + kk) * NT + tid >= a.nvec) {
             wt[ALIGNED ? kk : 0] = u32x4{NEG_INF, NEG_INF, NEG_INF, NEG_INF};
             wd[ALIGNED ? kk : 0] = wt[ALIGNED ? kk : 0];
           }
@@ -539,7 +545,7 @@ __global__ __launch_bounds__(NT) void k_tree_draw(const TreeArgs t) {
       const float k2 = a.k2, cf = (float)cval;
       float acc = 0.0f;
 #pragma unroll
-      for (int kk = 0; kk < VPT; ++kk) {
+      for (int kk = 0; kk < KS; ++kk) {
         float za[VEC], zb[VEC], w[VEC];
         if (ALIGNED) {
           Fmt<T>::unpack(wt[ALIGNED ? kk : 0], za);
@@ -547,7 +553,7 @@ __global__ __launch_bounds__(NT) void k_tree_draw(const TreeArgs t) {
         } else {
 #pragma unroll
           for (int e = 0; e < VEC; ++e) {
-            const long idx = elem_index<T>(c, kk, tid, e);
+            const long idx = elem_index<T>(c, kb + kk, tid, e);
             const bool in = idx < a.V;
             za[e] = in ? Fmt<T>::at(row_t, (size_t)idx) : -INFINITY;
             zb[e] = in ? Fmt<T>::at(row_d, (size_t)idx) : -INFINITY;
@@ -573,16 +579,16 @@ __global__ __launch_bounds__(NT) void k_tree_draw(const TreeArgs t) {
       if (wid == 0) {
         const double mine = (s_w[0] + s_w[1]) + (s_w[2] + s_w[3]);
         const unsigned tag = a.tag + 1u + (unsigned)round;
-        u64 *zw = t.tw_lz + ((size_t)b * 2 + (round & 1)) * (size_t)a.C * 2;
-        if (lane < 2) tw_putf(zw + (size_t)c * 2 + lane, tag, lane ? d_tail(mine) : d_head(mine));
+        u64 *zw = t.tw_lz + ((size_t)b * 2 + (round & 1)) * (size_t)NI * 2;
+        if (lane < 2) tw_putf(zw + (size_t)ii * 2 + lane, tag, lane ? d_tail(mine) : d_head(mine));
         double z = (double)NAN;
         for (unsigned polls = 0; polls < a.spin_limit; ++polls) {
           bool ready = true;
           double part = 0.0;
-          for (int cc = lane; cc < a.C; cc += WAVE) {
+          for (int cc = lane; cc < NI; cc += WAVE) {
             const u64 w0 = ld_dev(zw + (size_t)cc * 2), w1 = ld_dev(zw + (size_t)cc * 2 + 1);
-            ready = ready && (cc == c || (tw_ok(w0, tag) && tw_ok(w1, tag)));
-            part += (cc == c) ? mine : d_join(tw_f(w0), tw_f(w1));
+            ready = ready && (cc == ii || (tw_ok(w0, tag) && tw_ok(w1, tag)));
+            part += (cc == ii) ? mine : d_join(tw_f(w0), tw_f(w1));
           }
           if (wave_or(ready ? 0u : 1u) == 0u) {
             z = wave_sum(part);
@@ -600,7 +606,7 @@ __global__ __launch_bounds__(NT) void k_tree_draw(const TreeArgs t) {
     if (we.depth < 0) err = SV_ROW_INTERNAL;  // a mass that could not be formed
     __syncthreads();  // W.node is complete
   }
-  if (c == 0 && wid == 0) walk_write<false>(t, b, W, we.depth, err);
+  if (ii == 0 && wid == 0) walk_write<false>(t, b, W, we.depth, err);
   if (err || we.kind == TJ_NONE) return;
   const int kind = we.kind, u = we.u, depth = we.depth;
   if (u < 0 || u >= N || depth < 0 || depth >= N) return;  // cannot happen: the walk keeps both in range
@@ -614,26 +620,28 @@ __global__ __launch_bounds__(NT) void k_tree_draw(const TreeArgs t) {
   const T *row_t = seq_row<T>(a, b, u);
   const T *row_d = resid ? seq_row<T>(a, b, N + u) : nullptr;
   __shared__ double s_seg[SEGS];
-  if (resid) chunk_masses<T, ALIGNED, VPT / 2, VPT, true>(a, row_t, row_d, c, 0, wf, s_seg);
-  else chunk_masses<T, ALIGNED, VPT, VPT, false>(a, row_t, nullptr, c, 0, wf, s_seg);
+  constexpr int KG = (KS > 4) ? KS / 2 : KS;  // the pair's loads in flight at once
+  if (resid) chunk_masses<T, ALIGNED, KG, KS, true>(a, row_t, row_d, c, kb, wf, s_seg);
+  else chunk_masses<T, ALIGNED, KS, KS, false>(a, row_t, nullptr, c, kb, wf, s_seg);
   if (wid != 0) return;
   u64 *sw = t.tw_seg + (size_t)b * a.C * SEGS * 2;
-  if (c != a.C - 1) {
-    for (int i = lane; i < 2 * SEGS; i += WAVE) {
-      const double v = s_seg[i >> 1];
-      tw_putf(sw + (size_t)c * SEGS * 2 + i, a.tag, (i & 1) ? d_tail(v) : d_head(v));
+  const int own0 = c * SEGS + kb * NW;  // this item's first segment in the tree's order
+  if (ii != NI - 1) {
+    for (int i = lane; i < 2 * KS * NW; i += WAVE) {
+      const double v = s_seg[kb * NW + (i >> 1)];
+      tw_putf(sw + (size_t)own0 * 2 + i, a.tag, (i & 1) ? d_tail(v) : d_head(v));
     }
     return;
   }
-  // The tree's last chunk: every segment's mass (earlier chunks' words, its own from LDS),
-  // then the segment, lane and element where the cumulative mass passes u * total.
+  // The tree's last item: every segment's mass (the other items' words, its own from
+  // LDS), then the segment, lane and element where the cumulative mass passes u * total.
   const int nseg = a.C * SEGS;
   __shared__ double s_all[TREE_DRAW_LDS_SEGS];
   const bool fits = nseg <= TREE_DRAW_LDS_SEGS;
   bool done = false;
   for (unsigned polls = 0; polls < a.spin_limit && !done; ++polls) {
     bool mine = true;
-    for (int i = lane; i < (a.C - 1) * SEGS; i += WAVE) {
+    for (int i = lane; i < own0; i += WAVE) {
       const u64 w0 = ld_dev(sw + (size_t)i * 2), w1 = ld_dev(sw + (size_t)i * 2 + 1);
       const bool okw = tw_ok(w0, a.tag) && tw_ok(w1, a.tag);
       mine = mine && okw;
@@ -650,11 +658,11 @@ __global__ __launch_bounds__(NT) void k_tree_draw(const TreeArgs t) {
     return;
   }
   if (fits)
-    for (int i = lane; i < SEGS; i += WAVE) s_all[(a.C - 1) * SEGS + i] = s_seg[i];
+    for (int i = lane; i < KS * NW; i += WAVE) s_all[own0 + i] = s_seg[kb * NW + i];
   lds_sync();
   auto segm = [&](int i) -> double {
     if (fits) return s_all[i];
-    if (i >= (a.C - 1) * SEGS) return s_seg[i - (a.C - 1) * SEGS];
+    if (i >= own0) return s_seg[i - (a.C - 1) * SEGS];
     return d_join(tw_f(ld_dev(sw + (size_t)i * 2)), tw_f(ld_dev(sw + (size_t)i * 2 + 1)));
   };
   const float us = a.u_sample[b];
@@ -692,7 +700,7 @@ using sv_host::next_tag;
 
 struct TreePlan {
   bool greedy, topk;
-  int esz, nvec, C, rps, S;
+  int esz, nvec, C, rps, S, ts;  // ts: draw items a chunk
   long long R;
   size_t tw_part, tw_seg, tw_lz, tw_hist, row_off, row_lt, row_arg, row_ok, row_tau, tk_state, total,
       zero_bytes;
@@ -710,15 +718,18 @@ bool tree_plan(int32_t B, int32_t N, int32_t V, int32_t S, sv_dtype dt, float T,
   p.S = S < 1 ? 1 : S;
   p.topk = !p.greedy && top_k > 0 && top_k < V;
   const long long lr = (p.R + LANES - 1) / LANES, lb = (B + LANES - 1) / LANES;
-  // a tree's draw items wait for one another when a node may have two or more children
+  // a tree's draw items wait for one another when a node may have two or more children:
+  // then a tree has at most TREE_LAZY_MAX_C of them (4 a chunk where that allows, fewer
+  // for longer rows); otherwise 4 a chunk
   if (!p.greedy && p.S > 1 && p.C > TREE_LAZY_MAX_C) return false;
-  if (LANES * lr * p.C > 0x7fffffffLL || LANES * lb * (long long)p.C > 0x7fffffffLL) return false;
+  p.ts = (p.S <= 1 || 4 * p.C <= TREE_LAZY_MAX_C) ? 4 : (2 * p.C <= TREE_LAZY_MAX_C ? 2 : 1);
+  if (LANES * lr * p.C > 0x7fffffffLL || LANES * lb * (long long)p.C * p.ts > 0x7fffffffLL) return false;
   const size_t R = (size_t)p.R, C = (size_t)p.C, Bz = (size_t)B;
   const bool smp = !p.greedy;
   size_t o = 0;
   p.tw_part = o; o = align256(o + R * C * 3 * 8);
   p.tw_seg = o; o = align256(o + (smp ? Bz * C * SEGS * 2 * 8 : 0));
-  p.tw_lz = o; o = align256(o + (smp ? Bz * 2 * C * 2 * 8 : 0));
+  p.tw_lz = o; o = align256(o + (smp ? Bz * 2 * C * (size_t)p.ts * 2 * 8 : 0));
   p.tw_hist = o; o = align256(o + (p.topk ? sv_host::topk_words(p.R, p.C, top_k) * 8 : 0));
   p.zero_bytes = o;
   p.row_off = o; o = align256(o + R * 4);
@@ -761,8 +772,13 @@ hipError_t tree_launch(const TreePlan &p, const TreeArgs &t0, hipStream_t st, vo
   } else {  // the walk (forming the residual masses it needs), then the draw
     t.a.tag = sv_host::next_tag_block((unsigned)t.a.G + 1u);  // the call's tag, then one a round
     void *args[] = {&t};
-    L.go(p.topk ? (const void *)&k_tree_draw<T, AL, true> : (const void *)&k_tree_draw<T, AL, false>,
-         (unsigned)(LANES * lb * p.C), args);
+    const void *fn = p.ts == 4 ? (p.topk ? (const void *)&k_tree_draw<T, AL, true, VPT / 4>
+                                         : (const void *)&k_tree_draw<T, AL, false, VPT / 4>)
+                   : p.ts == 2 ? (p.topk ? (const void *)&k_tree_draw<T, AL, true, VPT / 2>
+                                         : (const void *)&k_tree_draw<T, AL, false, VPT / 2>)
+                               : (p.topk ? (const void *)&k_tree_draw<T, AL, true, VPT>
+                                         : (const void *)&k_tree_draw<T, AL, false, VPT>);
+    L.go(fn, (unsigned)(LANES * lb * p.C * p.ts), args);
   }
   if (nl) *nl = L.n;
   return L.e;
