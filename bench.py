@@ -247,7 +247,7 @@ def summarize_counters(kdir: str, cdir: str, op: str) -> None:
     counters_path(op).write_text(json.dumps(res, indent=1) + "\n")
     ratio = (fetch + write) / spec["alg"]
     md = [f"# HBM traffic of {kernel}, {spec['workload']} ({spec['desc']})", "",
-          "Commands (GPU box, after `cd /tmp && export TMPDIR=/tmp`; each counter in a run of its own):", "", "```"]
+          "Commands (on the MI355X machine, after `cd /tmp && export TMPDIR=/tmp`; each counter in a run of its own):", "", "```"]
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
         md.append(f"rocprofv3 --pmc {c} --output-format csv -d <k>/{c} -o k -- python3 <repo>/bench.py --op {op} "
                   f"--steps 30 --warmup 5 --no-cpu-baseline --no-stage-events --no-probe")
@@ -312,7 +312,7 @@ def summarize_trace(tdir: str, line_file: str, cmd: str, ref_file: str | None = 
     spans.append(("after", us[o:]))  # calls made after the timing (outputs checked)
     alg = rf["algorithmic_bytes"]
     out = [f"# Kernel trace: {kernel}, {line['config']['workload']}", "",
-           "Command (repository root on the GPU box, after `cd /tmp && export TMPDIR=/tmp`):", "",
+           "Command (repository root on the MI355X machine, after `cd /tmp && export TMPDIR=/tmp`):", "",
            "```", cmd, "```", "",
            f"Dispatches of `{kernel}` on the workload's grid ({main} threads), in launch order, split into",
            "the benchmark's phases; durations from rocprofv3's kernel trace of the same run.", "",
@@ -334,7 +334,7 @@ def summarize_trace(tdir: str, line_file: str, cmd: str, ref_file: str | None = 
         if ref_file:
             ref = _last_line(ref_file)
             rr = ref["roofline"]
-            out.append(f"The same command without the profiler, on the same box: `{kernel}` {rr['avg_launch_us']} us from "
+            out.append(f"The same command without the profiler, on the same machine: `{kernel}` {rr['avg_launch_us']} us from "
                        f"the events, frac {rr['frac']} ({(m / rr['avg_launch_us'] - 1) * 100:+.2f}% from rocprofv3's "
                        f"{m:.3f} us); event-free loop {ref['ms_per_step'] * 1e3:.2f} us per call "
                        f"({ref['value'] / 1e6:.3f} M {ref['unit']}).")
@@ -452,7 +452,7 @@ def run_timeline(args, dev) -> dict:
              "combiner_in": "its combiner has every segment mass",
              "token_out": "its token is written"}
     lines = [f"# Timeline: k_verify, {cfg.name}", "",
-             "Command (repository root on the GPU box; the timeline build of the library, which the build "
+             "Command (repository root on the MI355X machine; the timeline build of the library, which the build "
              "step compiles next to the product library):", "", "```", cmd, "```", "",
              f"Wall clock stamps (`wall_clock64`, {khz.value} kHz) stored by the kernels of "
              "`libspec_verify_timeline.so` at fixed points of each sequence's path (`sv_timeline_stamps`); "

@@ -1,7 +1,7 @@
 /*
  * sv_probe.h -- a measurement aid shipped with the verification library: the plain
  * streaming-read rate that the library's HBM-bound kernels are compared with.  It is no
- * part of the verification method; the benchmark runs it on the same box, on buffers of
+ * part of the verification method; the benchmark runs it on the same device, on buffers of
  * the size one verification call reads, to report the achieved bandwidth of the
  * verification kernels against what a kernel that only reads can reach.
  */
