@@ -10,7 +10,9 @@
 //
 // One kernel (after the top-k radix select, when top-k is on).  Per chunk of every target
 // row: block max m and argmax, off = m*k2, S = sum e and M = sum e*t over the chunk with
-// t = fma(z, k2, -off) and e = 2^t (one v_exp_f32 per logit), published as tagged words.
+// t = fma(z, k2, -off) and e = 2^t (one v_exp_f32 per logit), published as tagged words
+// (the last row, which only gives the greedy next token, publishes its argmax and validity
+// alone).
 // The sequence's last item combines each row's chunks: the log2-partition
 // L = o + log2(sum_c S_c 2^(off_c - o)) and, from the same sums, the entropy
 //   H = ln2 * (log2 t - D),  D = sum_c 2^(off_c - o) (M_c + (off_c - o) S_c) / t,
@@ -218,7 +220,20 @@ __global__ __launch_bounds__(NT) void k_typical(const TypArgs ta) {
   // chunk sum carries at most about three fp32 roundings of relative error.
   double acc_s = 0.0, acc_m = 0.0;
   int fl = (m == INFINITY) ? 1 : 0;  // a NaN or +inf also makes the sum NaN below
-  if (m > -INFINITY) {
+  if (m > -INFINITY && jr == a.rps - 1) {
+    // The row after the last drafted position only ever gives the greedy next token: its
+    // argmax and its validity suffice, so its sums are not formed (S = 1 keeps the row's
+    // combine defined; a NaN, which would have made the sum NaN, is found by comparison).
+    off = m * k2;
+    bool nan = false;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) nan |= (x[k][e] != x[k][e]);
+    if (__ballot(nan)) fl |= 1;
+    acc_s = (tid == 0) ? 1.0 : 0.0;
+    fl |= 2;
+  } else if (m > -INFINITY) {
     off = m * k2;
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {

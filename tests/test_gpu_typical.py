@@ -122,13 +122,16 @@ def test_typical_near_one_hot_matches_greedy(dev):
 
 
 def test_typical_codes(dev):
-    raw = wl.make_random(6, 4, 5000, "f32", seed=112)
+    raw = wl.make_random(8, 4, 5000, "f32", seed=112)
     t = raw.target.copy()
     x = oracle.sample_rows(raw.draft, raw.u_draft, 1.0).astype(np.int32)
     x[1, 2] = 5000         # -1
     t[2, 3, 7] = np.nan    # -3
     t[3, 4, 0] = np.inf    # -3 (the row of the next token)
     t[4, 0, :] = -np.inf   # -3 (nothing finite)
+    t[5, 4, 4321] = np.nan  # -3 (the row of the next token, whose sums are not formed)
+    t[6, 4, :] = -np.inf   # -3 (nothing finite in the row of the next token)
     g_acc, _ = run_both(t, x, 1.0, 0.1, 0.3, 0, dev, "codes")
-    assert list(g_acc[1:5]) == [oracle.ERR_TOKEN, oracle.ERR_ROW, oracle.ERR_ROW, oracle.ERR_ROW]
-    assert g_acc[0] >= 0 and g_acc[5] >= 0
+    assert list(g_acc[1:7]) == [oracle.ERR_TOKEN, oracle.ERR_ROW, oracle.ERR_ROW, oracle.ERR_ROW,
+                                oracle.ERR_ROW, oracle.ERR_ROW]
+    assert g_acc[0] >= 0 and g_acc[7] >= 0
