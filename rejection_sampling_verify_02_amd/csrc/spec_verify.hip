@@ -423,7 +423,7 @@ SVD void sampling_finish(const Args &a, int b, float own_off, float own_hi, floa
       const bool ok = isfinite(o) && isfinite(t) && t > 0.0;
       if (lds) {  // the optional row_stats output is written last, from LDS
         s_roff[jr] = o;
-        s_rl2s[jr] = ok ? log2(t) : 0.0;
+        s_rl2s[jr] = (ok && !G0) ? log2(t) : 0.0;  // no acceptance test reads it without drafts
         s_rok[jr] = ok ? 1 : 0;
         s_rsum[jr] = (float)t;
       } else if (a.row_stats) {
@@ -554,7 +554,7 @@ SVD void sampling_finish(const Args &a, int b, float own_off, float own_hi, floa
     case JW_OFF_J: bits = __float_as_uint(off_j); break;
     default: break;
   }
-  if (lane < JW_USED) tw_put(&jw[lane], tag, bits);
+  if (!G0 && lane < JW_USED) tw_put(&jw[lane], tag, bits);  // no draw items without drafts
   SV_TL(a, TL_SEQ(b) + TL_FIN_REC);
   for (int i = lane; i <= G; i += WAVE) {
     if (!err && i == j) continue;  // written by the draw, with accepted_len
