@@ -227,7 +227,7 @@ SVD unsigned block_excl_scan(unsigned v, unsigned *s_w, unsigned &total) {
 // by radix select, 8 bits a pass from the top (npass = 2 for bf16 values, whose keys have
 // zero low halves; 4 otherwise).  each(f) calls f(key) for every key this thread holds.
 // The multiset must hold at least k keys.  Thread d owns histogram bin d.
-template <typename Each>
+template <bool AGG = false, typename Each>
 SVD uint32_t block_kth_largest(int k, int npass, const Each &each, unsigned *hist, unsigned *sge,
                                unsigned *s_pick) {
   const int tid = threadIdx.x, lane = lane_id(), wid = tid / WAVE;
@@ -242,8 +242,23 @@ SVD uint32_t block_kth_largest(int k, int npass, const Each &each, unsigned *his
       s_pick[1] = 0u;
     }
     __syncthreads();
+    // AGG: keys that are close together share their high digits, so when every counted key
+    // of the wave falls in one bin, one atomic adds them all (the first pass of a top-k
+    // merge would otherwise send hundreds of atomics to one LDS word).
     each([&](uint32_t key) {
-      if ((key & hm) == (prefix & hm)) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      const bool in = (key & hm) == (prefix & hm);
+      const unsigned bin = (key >> shift) & 255u;
+      if (!AGG) {
+        if (in) atomicAdd(&hist[bin], 1u);
+        return;
+      }
+      const unsigned long long cnt = __ballot(in);
+      const unsigned b0 = (unsigned)__builtin_amdgcn_readfirstlane((int)bin);
+      if (__ballot(in && bin == b0) == cnt) {
+        if (cnt && lane == __ffsll((long long)__ballot(true)) - 1) atomicAdd(&hist[b0], (unsigned)__popcll(cnt));
+      } else if (in) {
+        atomicAdd(&hist[bin], 1u);
+      }
     });
     __syncthreads();
     // suffix counts of bin d = tid: the total minus the prefix before d (prefix by a wave
@@ -635,7 +650,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(7))) void k_
     unsigned gi;
     for (unsigned g = tid; g < total; g += NT) f(in_lds ? s_keys[g] : cand(g, gi));
   };
-  const uint32_t tk = block_kth_largest(k, NPASS, each, s_hist, s_ge, s_pick);
+  const uint32_t tk = block_kth_largest<true>(k, NPASS, each, s_hist, s_ge, s_pick);
   const float tau = tau_of_key(tk);
   if (tid == 0) a.w.row_tau[r] = tau;
   if (!rowp) return;
