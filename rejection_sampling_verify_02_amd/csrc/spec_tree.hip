@@ -93,24 +93,45 @@ SVD void tree_row_chunk(const TreeArgs &t, int r, const T *row, int c) {
     if (lane < 3) tw_putf(pw + (size_t)c * 3 + lane, a.tag, lane == 0 ? off : (lane == 1 ? d_head(S) : d_tail(S)));
     return;
   }
-  bool done = false;
-  for (unsigned polls = 0; polls < a.spin_limit && !done; ++polls) {
-    bool mine = true;
-    for (int cc = lane; cc < a.C - 1; cc += WAVE)
-      mine = mine && tw_ok(ld_dev(pw + (size_t)cc * 3), a.tag) && tw_ok(ld_dev(pw + (size_t)cc * 3 + 1), a.tag) &&
-             tw_ok(ld_dev(pw + (size_t)cc * 3 + 2), a.tag);
-    done = wave_or(mine ? 0u : 1u) == 0u;
-    if (!done) __builtin_amdgcn_s_sleep(2);
+  // The row's last chunk: lanes over chunks, 64 at a time (lane l of block c0 holds chunk
+  // c0 + l; this item's own values for chunk c), each block polled until all of its words
+  // carry the tag; the largest offset by a wave max, then the sum in chunk order from the
+  // lanes' registers (readlane), so no load waits inside the sum.
+  const int C = a.C;
+  auto block = [&](int c0, float &vo, double &vs) -> bool {
+    const int cc = c0 + lane;
+    for (unsigned polls = 0; polls < a.spin_limit; ++polls) {
+      bool mine = true;
+      vo = -INFINITY;
+      vs = 0.0;
+      if (cc == c) {
+        vo = off;
+        vs = S;
+      } else if (cc < C) {
+        const u64 w0 = ld_dev(pw + (size_t)cc * 3), w1 = ld_dev(pw + (size_t)cc * 3 + 1), w2 = ld_dev(pw + (size_t)cc * 3 + 2);
+        mine = tw_ok(w0, a.tag) && tw_ok(w1, a.tag) && tw_ok(w2, a.tag);
+        vo = tw_f(w0);
+        vs = d_join(tw_f(w1), tw_f(w2));
+      }
+      if (wave_or(mine ? 0u : 1u) == 0u) return true;
+      __builtin_amdgcn_s_sleep(2);
+    }
+    return false;
+  };
+  bool done = true;
+  float o = -INFINITY, vo = -INFINITY;
+  double vs = 0.0;
+  for (int c0 = 0; c0 < C && done; c0 += WAVE) {
+    done = block(c0, vo, vs);
+    o = fmaxf(o, wave_max(vo));
+  }
+  double tt = 0.0;
+  for (int c0 = 0; c0 < C && done; c0 += WAVE) {
+    if (C > WAVE) block(c0, vo, vs);  // a row of one block keeps its values from the first pass
+    const int nb = (C - c0 < WAVE) ? C - c0 : WAVE;
+    for (int l = 0; l < nb; ++l) tt += readlane_d(vs, l) * (double)fast_exp2(readlane_f(vo, l) - o);
   }
   if (lane == 0) {
-    auto p_off = [&](int cc) { return cc == c ? off : tw_f(ld_dev(pw + (size_t)cc * 3)); };
-    auto p_sum = [&](int cc) {
-      return cc == c ? S : d_join(tw_f(ld_dev(pw + (size_t)cc * 3 + 1)), tw_f(ld_dev(pw + (size_t)cc * 3 + 2)));
-    };
-    float o = -INFINITY;
-    for (int cc = 0; cc < a.C; ++cc) o = fmaxf(o, p_off(cc));
-    double tt = 0.0;
-    for (int cc = 0; cc < a.C; ++cc) tt += p_sum(cc) * (double)fast_exp2(p_off(cc) - o);
     const bool ok = done && isfinite(o) && isfinite(tt) && tt > 0.0;
     t.row_off[r] = o;
     t.row_lt[r] = ok ? log2(tt) : 0.0;
@@ -178,26 +199,36 @@ __global__ __launch_bounds__(NT) void k_tree_rows(const TreeArgs t) {
                lane == 0 ? __float_as_uint(best) : (lane == 1 ? (unsigned)bi : (unsigned)fl));
       return;
     }
-    // the row's last chunk: the other chunks' bests in chunk order
-    bool done = false;
-    for (unsigned polls = 0; polls < a.spin_limit && !done; ++polls) {
-      bool mine = true;
-      for (int cc = lane; cc < a.C - 1; cc += WAVE)
-        mine = mine && tw_ok(ld_dev(pw + (size_t)cc * 3), a.tag) && tw_ok(ld_dev(pw + (size_t)cc * 3 + 1), a.tag) &&
-               tw_ok(ld_dev(pw + (size_t)cc * 3 + 2), a.tag);
-      done = wave_or(mine ? 0u : 1u) == 0u;
-      if (!done) __builtin_amdgcn_s_sleep(2);
+    // the row's last chunk: the other chunks' bests, lanes over chunks 64 at a time (the
+    // largest value, lowest index, is the same in any order)
+    bool done = true;
+    float v = best;
+    int vi = bi, f = fl;
+    for (int c0 = 0; c0 < a.C - 1 && done; c0 += WAVE) {
+      const int cc = c0 + lane;
+      done = false;
+      for (unsigned polls = 0; polls < a.spin_limit; ++polls) {
+        bool mine = true;
+        float bv = -INFINITY;
+        int bx = 0x7fffffff, bf = 0;
+        if (cc < a.C - 1) {
+          const u64 w0 = ld_dev(pw + (size_t)cc * 3), w1 = ld_dev(pw + (size_t)cc * 3 + 1), w2 = ld_dev(pw + (size_t)cc * 3 + 2);
+          mine = tw_ok(w0, a.tag) && tw_ok(w1, a.tag) && tw_ok(w2, a.tag);
+          bv = __uint_as_float((unsigned)w0);
+          bx = (int)(unsigned)w1;
+          bf = (int)(unsigned)w2;
+        }
+        if (wave_or(mine ? 0u : 1u) == 0u) {
+          wave_best(bv, bx, bf);
+          best_combine(v, vi, bv, bx);
+          f |= bf;
+          done = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
     }
     if (lane == 0) {
-      float v = -INFINITY;
-      int vi = 0x7fffffff, f = 0;
-      for (int cc = 0; cc < a.C - 1; ++cc) {
-        best_combine(v, vi, __uint_as_float((unsigned)ld_dev(pw + (size_t)cc * 3)),
-                     (int)(unsigned)ld_dev(pw + (size_t)cc * 3 + 1));
-        f |= (int)(unsigned)ld_dev(pw + (size_t)cc * 3 + 2);
-      }
-      best_combine(v, vi, best, bi);
-      f |= fl;
       t.row_arg[r] = vi;
       t.row_ok[r] = !done ? -2 : (((f & 1) == 0 && (f & 2)) ? 1 : 0);
     }
