@@ -128,17 +128,23 @@ __global__ __launch_bounds__(NT) void k_topk_digit(const Args a, int pass, int l
     return;
   }
 
-  // The row's last chunk: wait for the other chunks' histograms (every load in flight
-  // at once), then the row total of digit d = tid.
+  // The row's last chunk: wait for the other chunks' histograms (eight chunks' words in
+  // flight at once, not one load waited for at a time), then the row total of digit d = tid.
   unsigned tot = 0;
   unsigned polls = 0;
   for (;;) {
     tot = hist[tid];
     bool ok = true;
-    for (int cc = 0; cc < a.C - 1; ++cc) {
-      const u64 w = ld_dev(&hw[(size_t)cc * 128 + (tid >> 1)]);
-      ok = ok && tw_ok(w, tag);
-      tot += ((unsigned)w >> ((tid & 1) * 16)) & 0xffffu;
+    for (int cc0 = 0; cc0 < a.C - 1; cc0 += 8) {
+      u64 w[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        w[k] = (cc0 + k < a.C - 1) ? ld_dev(&hw[(size_t)(cc0 + k) * 128 + (tid >> 1)]) : ((u64)tag << 32);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        ok = ok && tw_ok(w[k], tag);
+        tot += ((unsigned)w[k] >> ((tid & 1) * 16)) & 0xffffu;
+      }
     }
     if (__syncthreads_and(ok ? 1 : 0)) break;
     if (++polls >= a.spin_limit) break;
