@@ -33,6 +33,17 @@ constexpr int TYP_WORDS = 8;         // per chunk: off, S hi/lo, M hi/lo, best v
 constexpr int TYP_MAX_ROWS = 257;    // rows of one sequence (G <= 256)
 constexpr int TYP_LDS_PARTS = 768;   // (row, chunk) partials of one sequence staged in LDS
 
+// The chunks' (largest value, its lowest index) pairs as one key whose maximum is the
+// row's: the value's bits in an order-preserving form (-0 taken as +0, which compares
+// equal to it; NaN lowest, which never wins), then the complemented index, so that of
+// equal values the lower index wins.  A max over keys has no branch.
+SVD u64 best_key(float v, int i) {
+  const float c = v + 0.0f;
+  const unsigned u = __float_as_uint(c);
+  const unsigned ord = (c != c) ? 0u : ((u & 0x80000000u) ? ~u : (u | 0x80000000u));
+  return ((u64)ord << 32) | (u64)(0xffffffffu - (unsigned)i);
+}
+
 // Lowest value over the wave.
 SVD int wave_min_i(int v) {
 #define STEP(C, R) v = min(v, dpp_i<C, R>(v, 0x7fffffff));
@@ -49,9 +60,10 @@ struct TypArgs {
 
 // The sequence's last item: combine, test, write.  One wave; lane f < TYP_WORDS holds
 // word f of this item's own partial in own_v (a value per lane, so the partial never
-// needs an addressable array, which would live in scratch memory).
+// needs an addressable array, which would live in scratch memory); lane i < G holds
+// position i's token in gx and its logit in gz (NaN for a token outside [0, V)).
 template <typename T, bool TOPK>
-SVD void typical_finish(const TypArgs &ta, int b, float own_v, int own_c) {
+SVD void typical_finish(const TypArgs &ta, int b, float own_v, int own_c, int gx, float gz) {
   const Args &a = ta.a;
   const int lane = lane_id();
   const int G = a.G, rps = a.rps, C = a.C;
@@ -60,8 +72,9 @@ SVD void typical_finish(const TypArgs &ta, int b, float own_v, int own_c) {
   const int own = (rps - 1) * C + own_c;
   __shared__ double s_l2[TYP_MAX_ROWS], s_h[TYP_MAX_ROWS];
   __shared__ int s_arg[TYP_MAX_ROWS], s_ok[TYP_MAX_ROWS];
-  __shared__ float s_w[TYP_LDS_PARTS * TYP_WORDS];
+  __shared__ __align__(16) float s_w[TYP_LDS_PARTS * TYP_WORDS];
   __shared__ float s_own[TYP_WORDS];
+  __shared__ float s_o[TYP_MAX_ROWS];
   const bool lds = rps * C <= TYP_LDS_PARTS;
   if (lane < TYP_WORDS) s_own[lane] = own_v;
 
@@ -95,34 +108,75 @@ SVD void typical_finish(const TypArgs &ta, int b, float own_v, int own_c) {
     if (lane == 0) a.accepted_len[b] = SV_ROW_INTERNAL;
     return;
   }
-  auto word = [&](int i, int f) -> float {
-    if (lds) return s_w[i * TYP_WORDS + f];
-    return i == own ? s_own[f] : tw_f(ld_dev(pw + (size_t)i * TYP_WORDS + f));
+  // A chunk's two terms for its row's sums, S 2^(off - o) and (M + (off - o) S) 2^(off - o),
+  // as +0.0 for an empty chunk (S = 0, whose offset may be -inf like o).
+  auto terms = [&](float off, float o, double S, double M, double &ts, double &td) {
+    const bool use = S > 0.0 || S != S;
+    const double e = (double)fast_exp2(off - o);
+    ts = use ? S * e : 0.0;
+    td = use ? (M + ((double)off - (double)o) * S) * e : 0.0;
   };
+  if (lds) {
+    // The combine in three steps, so that the exponentials of all chunks run in parallel
+    // lanes: (1) lanes over rows, each row's largest offset; (2) lanes over chunks, each
+    // chunk's two terms, written over its first four words; (3) lanes over rows, the sums
+    // in chunk order.
+    const float4 *q = reinterpret_cast<const float4 *>(s_w);
+    for (int r = lane; r < rps; r += WAVE) {
+      float o = -INFINITY;
+#pragma unroll 8
+      for (int c = 0; c < C; ++c) o = fmaxf(o, q[2 * (r * C + c)].x);
+      s_o[r] = o;
+    }
+    lds_sync();
+    for (int i = lane; i < rps * C; i += WAVE) {
+      const float4 u = q[2 * i];
+      const float m_lo = s_w[i * TYP_WORDS + 4];
+      double ts, td;
+      terms(u.x, s_o[i / C], d_join(u.y, u.z), d_join(u.w, m_lo), ts, td);
+      reinterpret_cast<double2 *>(s_w)[2 * i] = make_double2(ts, td);
+    }
+    lds_sync();
+  }
   // per row (lanes over rows): chunks in order
   for (int r = lane; r < rps; r += WAVE) {
     float o = -INFINITY;
-    for (int c = 0; c < C; ++c) o = fmaxf(o, word(r * C + c, 0));
     double t = 0.0, dn = 0.0;
-    float best = -INFINITY;
-    int bi = 0x7fffffff, fl = 0;
-    for (int c = 0; c < C; ++c) {
-      const int i = r * C + c;
-      const float off = word(i, 0);
-      const double S = d_join(word(i, 1), word(i, 2)), M = d_join(word(i, 3), word(i, 4));
-      if (S > 0.0 || S != S) {
-        const double w = (double)fast_exp2(off - o);
-        t += S * w;
-        dn += (M + ((double)off - (double)o) * S) * w;
+    u64 bkey = best_key(-INFINITY, 0x7fffffff);
+    int fl = 0;
+    if (lds) {
+      o = s_o[r];
+      const double2 *qd = reinterpret_cast<const double2 *>(s_w) + (size_t)r * C * 2;
+      const float4 *q = reinterpret_cast<const float4 *>(s_w) + (size_t)r * C * 2;
+#pragma unroll 4
+      for (int c = 0; c < C; ++c) {
+        const double2 d = qd[2 * c];
+        const float4 v = q[2 * c + 1];
+        t += d.x;
+        dn += d.y;
+        bkey = max(bkey, best_key(v.y, (int)__float_as_uint(v.z)));
+        fl |= (int)__float_as_uint(v.w);
       }
-      best_combine(best, bi, word(i, 5), (int)__float_as_uint(word(i, 6)));
-      fl |= (int)__float_as_uint(word(i, 7));
+    } else {
+      auto word = [&](int i, int f) -> float {
+        return i == own ? s_own[f] : tw_f(ld_dev(pw + (size_t)i * TYP_WORDS + f));
+      };
+      for (int c = 0; c < C; ++c) o = fmaxf(o, word(r * C + c, 0));
+      for (int c = 0; c < C; ++c) {
+        const int i = r * C + c;
+        double ts, td;
+        terms(word(i, 0), o, d_join(word(i, 1), word(i, 2)), d_join(word(i, 3), word(i, 4)), ts, td);
+        t += ts;
+        dn += td;
+        bkey = max(bkey, best_key(word(i, 5), (int)__float_as_uint(word(i, 6))));
+        fl |= (int)__float_as_uint(word(i, 7));
+      }
     }
     const bool ok = isfinite(o) && isfinite(t) && t > 0.0 && !(fl & 1) && (fl & 2);
     const double l2t = ok ? log2(t) : 0.0;
     s_l2[r] = (double)o + l2t;
     s_h[r] = ok ? LN2 * (l2t - dn / t) : 0.0;
-    s_arg[r] = bi;
+    s_arg[r] = (int)(0xffffffffu - (unsigned)bkey);
     s_ok[r] = ok ? 1 : 0;
   }
   lds_sync();
@@ -142,11 +196,11 @@ SVD void typical_finish(const TypArgs &ta, int b, float own_v, int own_c) {
     const int i = i0 + lane;
     bool accept = false;
     if (i < G) {
-      const int x = xt[i];
+      const int x = (i0 == 0) ? gx : xt[i];
       if (x < 0 || x >= a.V) {
         flags |= 1;
       } else if (s_ok[i]) {
-        const float zx = Fmt<T>::at(rows + (size_t)i * a.V, (size_t)x);
+        const float zx = (i0 == 0) ? gz : Fmt<T>::at(rows + (size_t)i * a.V, (size_t)x);
         const float tau = TOPK ? a.w.row_tau[r0 + i] : -INFINITY;
         const bool supp = (zx > -INFINITY) && !(zx < tau);
         const double lnp = ((double)zx * (double)a.k2 - s_l2[i]) * LN2;
@@ -181,8 +235,17 @@ __global__ __launch_bounds__(NT) void k_typical(const TypArgs ta) {
   const int b = r / a.rps, jr = r - b * a.rps;
   const T *row = static_cast<const T *>(a.target) + (size_t)r * a.V;
 
+  // The sequence's last item (its finisher) gathers the drafted tokens and their logits
+  // (positions = lanes of wave 0, the first 64) while its own chunk streams in: the token
+  // loads go first, the logit loads right after the chunk's.
+  const bool gath = jr == a.rps - 1 && c == a.C - 1 && wid == 0 && lane < a.G;
+  const int gx = gath ? a.tokens[(size_t)b * a.G + lane] : -1;
+  float gz = NAN;
   float x[VPT][VEC];
-  load_chunk<T, ALIGNED, true>(row, a.V, a.nvec, c, tid, x);
+  load_chunk<T, ALIGNED, true>(row, a.V, a.nvec, c, tid, x, [&] {
+    if (gath && gx >= 0 && gx < a.V)
+      gz = Fmt<T>::at(static_cast<const T *>(a.target) + ((size_t)b * a.rps + lane) * a.V, (size_t)gx);
+  });
   if (TOPK) {
     const float tau = a.w.row_tau[r];
 #pragma unroll
@@ -289,7 +352,7 @@ __global__ __launch_bounds__(NT) void k_typical(const TypArgs ta) {
 #pragma unroll
   for (int f = 1; f < TYP_WORDS; ++f) v = (lane == f) ? words[f] : v;
   if (jr == a.rps - 1 && c == a.C - 1) {
-    typical_finish<T, TOPK>(ta, b, v, c);
+    typical_finish<T, TOPK>(ta, b, v, c, gx, gz);
     return;
   }
   u64 *pw = a.w.tw_part + ((size_t)r * a.C + c) * TYP_WORDS;

@@ -63,9 +63,15 @@ struct Fmt<float> {
 // one wave's k-th load covers 64 consecutive vectors (a "segment") and segments are in
 // vocabulary order (k-major, then wave).  Elements past the row end read as -inf.
 // Every load is issued before any is used: past the end a load re-reads the row's last
-// vector (or element), and the tail is masked afterwards by a uniform branch.
-template <typename T, bool ALIGNED, bool STREAM>
-SVD void load_chunk(const T *row, int V, int nvec, int c, int tid, float (&x)[VPT][Fmt<T>::VEC]) {
+// vector (or element), and the tail is masked afterwards by a uniform branch.  `mid`
+// runs after the aligned path's loads are issued and before any is waited for, so that
+// loads it issues are in flight with the chunk's (in the element-wise path it runs first:
+// after the element loads it would keep them all live).
+struct NoMid {
+  SVD void operator()() const {}
+};
+template <typename T, bool ALIGNED, bool STREAM, typename Mid = NoMid>
+SVD void load_chunk(const T *row, int V, int nvec, int c, int tid, float (&x)[VPT][Fmt<T>::VEC], Mid mid = {}) {
   constexpr int VEC = Fmt<T>::VEC;
   if (ALIGNED) {
     u32x4 w[VPT];
@@ -76,6 +82,7 @@ SVD void load_chunk(const T *row, int V, int nvec, int c, int tid, float (&x)[VP
       const u32x4 *p = rv + (v < nvec ? v : nvec - 1);
       w[k] = STREAM ? __builtin_nontemporal_load(p) : *p;
     }
+    mid();
 #pragma unroll
     for (int k = 0; k < VPT; ++k) Fmt<T>::unpack(w[k], x[k]);
     if ((c + 1) * CHUNK_VECS > nvec) {
@@ -87,6 +94,7 @@ SVD void load_chunk(const T *row, int V, int nvec, int c, int tid, float (&x)[VP
       }
     }
   } else {
+    mid();
 #pragma unroll
     for (int k = 0; k < VPT; ++k)
 #pragma unroll
