@@ -666,20 +666,44 @@ __global__ __launch_bounds__(NT) void k_tree_draw(const TreeArgs t) {
   }
   // The tree's last item: every segment's mass (the other items' words, its own from
   // LDS), then the segment, lane and element where the cumulative mass passes u * total.
+  // The other items' segments precede this item's own: polled in blocks of 256, four
+  // consecutive segments a lane, every load of a block issued before any is checked.
   const int nseg = a.C * SEGS;
   __shared__ double s_all[TREE_DRAW_LDS_SEGS];
   const bool fits = nseg <= TREE_DRAW_LDS_SEGS;
-  bool done = false;
-  for (unsigned polls = 0; polls < a.spin_limit && !done; ++polls) {
-    bool mine = true;
-    for (int i = lane; i < own0; i += WAVE) {
-      const u64 w0 = ld_dev(sw + (size_t)i * 2), w1 = ld_dev(sw + (size_t)i * 2 + 1);
-      const bool okw = tw_ok(w0, a.tag) && tw_ok(w1, a.tag);
-      mine = mine && okw;
-      if (okw && fits) s_all[i] = d_join(tw_f(w0), tw_f(w1));
+  constexpr int SB = 4, BLK = SB * WAVE;
+  bool done = true;
+  unsigned polls = 0;
+  for (int blk = 0; blk < own0 && done; blk += BLK) {
+    for (;;) {
+      u64 wh[SB], wl[SB];
+#pragma unroll
+      for (int k = 0; k < SB; ++k) {
+        const int i = blk + lane * SB + k;
+        const int ii = (i < own0) ? i : 0;
+        wh[k] = ld_dev(sw + (size_t)ii * 2);
+        wl[k] = ld_dev(sw + (size_t)ii * 2 + 1);
+      }
+      bool ok = true;
+#pragma unroll
+      for (int k = 0; k < SB; ++k)
+        if (blk + lane * SB + k < own0) ok = ok && tw_ok(wh[k], a.tag) && tw_ok(wl[k], a.tag);
+      if (__ballot(!ok) == 0) {
+        if (fits) {
+#pragma unroll
+          for (int k = 0; k < SB; ++k) {
+            const int i = blk + lane * SB + k;
+            if (i < own0) s_all[i] = d_join(tw_f(wh[k]), tw_f(wl[k]));
+          }
+        }
+        break;
+      }
+      if (++polls >= a.spin_limit) {
+        done = false;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
     }
-    done = wave_or(mine ? 0u : 1u) == 0u;
-    if (!done) __builtin_amdgcn_s_sleep(2);
   }
   if (!done) {
     if (lane == 0) {
@@ -698,7 +722,7 @@ __global__ __launch_bounds__(NT) void k_tree_draw(const TreeArgs t) {
   };
   const float us = a.u_sample[b];
   double srem = 0.0, total = 0.0;
-  int sp = wave_pick_frac(nseg, (double)us, segm, &srem, &total);
+  int sp = wave_pick4_frac(nseg, (double)us, segm, &srem, &total);
   int y = -1;
   if (sp >= 0 && total > 0.0) {
     y = segment_draw<T, ALIGNED>(a, row_t, row_d, sp / SEGS, sp % SEGS, wf, srem);
