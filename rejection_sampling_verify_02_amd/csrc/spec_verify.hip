@@ -414,7 +414,34 @@ SVD void sampling_finish(const Args &a, int b, float own_off, float own_hi, floa
       for (int k = 0; k < CB; ++k) t += sc[k] * (double)fast_exp2(v[k] - o);
     }
   };
-  for (int jr0 = 0; jr0 < rps; jr0 += WAVE) {
+  // No drafts, one row of at most 64 chunks and no row statistics asked for: the row's
+  // offset is a maximum over chunk lanes, and the chunk is picked right here by the same
+  // masses the pick below would use (the chunk masses' total stands for the row sum in
+  // the validity test: both are sums of the same terms, and a NaN chunk sum, which the
+  // masses skip, marks the row unusable as it makes the row sum NaN).
+  const bool g0fast = G0 && lds && !a.row_stats && C <= WAVE;
+  int c_fast = -1;
+  double trem_fast = 0.0;
+  if (G0 && g0fast) {
+    const float offc = (lane < C) ? s_po[lane] : -INFINITY;
+    const double scv = (lane < C) ? s_ps[lane] : 0.0;
+    const float o = wave_max(offc);
+    const bool nan = __ballot(lane < C && scv != scv) != 0;
+    auto cmf = [&](int cc) {
+      const double sc = s_ps[cc];
+      return (sc > 0.0) ? sc * (double)fast_exp2(s_po[cc] - o) : 0.0;
+    };
+    double tot;
+    c_fast = wave_pick_frac(C, (double)us, cmf, &trem_fast, &tot);
+    const bool ok = isfinite(o) && !nan && isfinite(tot) && tot > 0.0;
+    if (lane == 0) {
+      s_roff[0] = o;
+      s_rl2s[0] = 0.0;
+      s_rok[0] = ok ? 1 : 0;
+      s_rsum[0] = (float)tot;
+    }
+  }
+  for (int jr0 = 0; jr0 < rps && !(G0 && g0fast); jr0 += WAVE) {
     const int jr = jr0 + lane;
     if (jr < rps) {
       float o;
@@ -514,7 +541,12 @@ SVD void sampling_finish(const Args &a, int b, float own_off, float own_hi, floa
       return (sc > 0.0) ? sc * (double)fast_exp2(p_off(G, cc) - oG) : 0.0;
     };
     double trem, total;
-    c_bonus = wave_pick_frac(C, (double)us, cm, &trem, &total);
+    if (G0 && g0fast) {
+      c_bonus = c_fast;
+      trem = trem_fast;
+    } else {
+      c_bonus = wave_pick_frac(C, (double)us, cm, &trem, &total);
+    }
     if (c_bonus >= 0) {
       off_bonus = p_off(G, c_bonus);
       t_bonus = trem * (double)fast_exp2(oG - off_bonus);
