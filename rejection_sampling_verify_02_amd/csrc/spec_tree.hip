@@ -61,11 +61,35 @@ struct TreeArgs {
   int32_t *row_arg;        // [R] greedy: lowest-index argmax
   int32_t *row_ok;         // [R] 1 usable, 0 not (NaN, +inf, nothing finite kept), -1 not read,
                            //   -2 a wait gave up
+  float *node_z;           // [B, N, 2] sampling: node n's token logit in its parent's target and
+                           //   draft rows (NaN for a node whose parent or token is out of range)
   // tagged words within one launch
   u64 *tw_seg;             // [B*C*SEGS*2] per tree, chunk and segment: the draw's masses
   u64 *tw_lz;              // [B*2*C*TS*2] residual masses formed by the walk: per tree two
                            //   slots (alternating rounds), per draw item a tagged double
 };
+
+// The logits the walk of tree b tests (node n's token in its parent's target and draft
+// rows), gathered by one wave into node_z while the rows stream, so that the walk's setup
+// loads them with everything else it reads instead of in a second, dependent round.
+template <typename T>
+SVD void gather_node_logits(const TreeArgs &t, int b) {
+  const Args &a = t.a;
+  const int N = a.G;
+  const int32_t *par = t.parent + (size_t)b * N;
+  const int32_t *tok = a.tokens + (size_t)b * N;
+  for (int n = lane_id(); n < N; n += WAVE) {
+    const int p = (n > 0) ? par[n] : -1;
+    const int x = (n > 0) ? tok[n] : -1;
+    float zt = NAN, zd = NAN;
+    if (p >= 0 && p < n && x >= 0 && x < a.V) {
+      zt = Fmt<T>::at(static_cast<const T *>(seq_row<T>(a, b, p)), (size_t)x);
+      zd = Fmt<T>::at(static_cast<const T *>(seq_row<T>(a, b, N + p)), (size_t)x);
+    }
+    t.node_z[((size_t)b * N + n) * 2] = zt;
+    t.node_z[((size_t)b * N + n) * 2 + 1] = zd;
+  }
+}
 
 // The nodes' children, counted by one wave: nch = children of node u in tree b.
 SVD int child_count(const TreeArgs &t, int b, int u) {
@@ -153,6 +177,9 @@ __global__ __launch_bounds__(NT) void k_tree_rows(const TreeArgs t) {
   const int N = a.G;
   if (j >= N && (GREEDY || child_count(t, b, j - N) == 0)) {  // a draft row nobody reads
     if (c == a.C - 1 && tid == 0) t.row_ok[r] = -1;
+    // The last node never has children (a parent precedes its child), so in every
+    // well-formed tree this item exists; it gathers the walk's token logits.
+    if (!GREEDY && j == 2 * N - 1 && c == 0 && wid == 0) gather_node_logits<T>(t, b);
     return;
   }
   const T *row = seq_row<T>(a, b, j);
@@ -249,11 +276,11 @@ struct WalkLds {
   int err;
 };
 
-// The checks of tree b and everything its walk reads, into W, by one wave in two rounds of
-// loads: first what is indexed by the node alone (parent, token, both rows' status,
-// log2-partition and threshold, the uniform), then each node's token logits in its
-// parent's rows.  The node checks count only for a well-formed tree.  W.err is the tree's
-// row code, 0 if none.  Greedy: W.lp holds each row's argmax instead.
+// The checks of tree b and everything its walk reads, into W, by one wave in one round of
+// loads, everything indexed by the node alone: parent, token, both rows' status,
+// log2-partition and threshold, the uniform, and the node's token logits in its parent's
+// rows (gathered by the row pass).  The node checks count only for a well-formed tree.
+// W.err is the tree's row code, 0 if none.  Greedy: W.lp holds each row's argmax instead.
 template <typename T, bool TOPK, bool GREEDY>
 SVD void walk_setup(const TreeArgs &t, int b, WalkLds &W) {
   const Args &a = t.a;
@@ -287,6 +314,10 @@ SVD void walk_setup(const TreeArgs &t, int b, WalkLds &W) {
       W.tau[n] = tt;
       if (tt != tt) f1 |= 16;  // a NaN threshold marks a top-k selection that did not complete
       W.taud[n] = TOPK ? a.w.row_tau[r0 + N + n] : -INFINITY;
+      // the token logits gathered by the row pass (used only for a well-formed tree with
+      // every token in range, for which that pass wrote them)
+      W.zt[n] = t.node_z[((size_t)b * N + n) * 2];
+      W.zd[n] = t.node_z[((size_t)b * N + n) * 2 + 1];
     }
   }
   if (!GREEDY && lane == 0 && !(a.u_sample[b] >= 0.0f && a.u_sample[b] < 1.0f)) f1 |= 4;
@@ -298,12 +329,7 @@ SVD void walk_setup(const TreeArgs &t, int b, WalkLds &W) {
     lds_sync();
     const bool gather = !GREEDY && !(flags & 1);
     for (int n = lane; n < N; n += WAVE) {
-      float zt = 0.0f, zd = 0.0f;
-      const int p = W.par[n], x = W.tok[n];
-      if (gather && n > 0) {
-        zt = Fmt<T>::at(static_cast<const T *>(seq_row<T>(a, b, p)), (size_t)x);
-        zd = Fmt<T>::at(static_cast<const T *>(seq_row<T>(a, b, N + p)), (size_t)x);
-      }
+      const int p = W.par[n];
       const int nch = W.nch[n];
       if (!GREEDY && nch > t.S) flags |= 32;
       if (!GREEDY && nch > 0) {
@@ -312,8 +338,7 @@ SVD void walk_setup(const TreeArgs &t, int b, WalkLds &W) {
         if (TOPK && W.taud[n] != W.taud[n]) flags |= 16;
       }
       if (gather && n > 0) {
-        W.zt[n] = zt;
-        W.zd[n] = zd;
+        const float zd = W.zd[n];
         if (!(zd > -INFINITY) || zd < W.taud[p]) flags |= 8;
       }
     }
@@ -757,7 +782,7 @@ struct TreePlan {
   bool greedy, topk;
   int esz, nvec, C, rps, S, ts;  // ts: draw items a chunk
   long long R;
-  size_t tw_part, tw_seg, tw_lz, tw_hist, row_off, row_lt, row_arg, row_ok, row_tau, tk_state, total,
+  size_t tw_part, tw_seg, tw_lz, tw_hist, row_off, row_lt, row_arg, row_ok, node_z, row_tau, tk_state, total,
       zero_bytes;
 };
 
@@ -791,6 +816,7 @@ bool tree_plan(int32_t B, int32_t N, int32_t V, int32_t S, sv_dtype dt, float T,
   p.row_lt = o; o = align256(o + R * 8);
   p.row_arg = o; o = align256(o + R * 4);
   p.row_ok = o; o = align256(o + R * 4);
+  p.node_z = o; o = align256(o + (smp ? Bz * (size_t)N * 2 * 4 : 0));
   p.row_tau = o; o = align256(o + (p.topk ? R * 4 : 0));
   p.tk_state = o; o = align256(o + (p.topk ? sv_host::topk_state_bytes(p.R, p.C, top_k) : 0));
   p.total = o;
@@ -893,6 +919,7 @@ sv_status tree_run(const void *target, const void *draft, sv_dtype dt, const int
   t.row_lt = (double *)(base + p.row_lt);
   t.row_arg = (int32_t *)(base + p.row_arg);
   t.row_ok = (int32_t *)(base + p.row_ok);
+  t.node_z = smp ? (float *)(base + p.node_z) : nullptr;
   t.tw_seg = (u64 *)(base + p.tw_seg);
   t.tw_lz = smp ? (u64 *)(base + p.tw_lz) : nullptr;
 
