@@ -9,6 +9,7 @@ import pytest
 from scipy import stats
 
 import oracle
+import parity
 from parity import BAND, to_device
 from rejection_sampling_verify_02_amd import workloads as wl
 
@@ -50,6 +51,27 @@ def test_sample_workload_full_size(dev):
     c = wl.SAMPLE_CONFIGS["sample_bf16_b256"]
     z, u = wl.make_sample(c.B, c.V, c.dtype, c.seed)
     run_both(z, u, c.temperature, c.top_k, dev)
+
+
+@pytest.mark.parametrize("V,dtype", [(50000, "bf16"), (128256, "bf16"), (20001, "f32")])
+def test_no_drafts_with_row_stats(dev, V, dtype):
+    """No drafts (G = 0) through ``spec_verify`` with the row statistics asked for: the
+    finisher then combines the row in its general row pass, where ``spec_sample`` (no
+    statistics) takes the row offset and the chunk in one pass over chunk lanes.  Both
+    against the oracle (tokens, and the statistics' log-partition), and each other's
+    tokens and row codes exactly."""
+    import torch
+    import rejection_sampling_verify_02_amd as sv
+    raw = wl.make_random(64, 0, V, dtype, seed=700 + V % 89)
+    res, (acc_g, out_g, st), _ = parity.run_both(raw, 1.0, 0, dev)
+    print(f"[sample] no drafts, row statistics, V={V} {dtype}: {res.summary()}", flush=True)
+    assert not res.failures, res.failures[:5]
+    assert st is not None and st.shape == (64, 1, 2)
+    tok, code = sv.spec_sample(to_device(np.ascontiguousarray(raw.target[:, 0]), dev),
+                               to_device(raw.u_sample, dev), 1.0, 0)
+    torch.cuda.synchronize(dev)
+    np.testing.assert_array_equal(code.cpu().numpy(), acc_g)
+    np.testing.assert_array_equal(tok.cpu().numpy(), out_g[:, 0])
 
 
 SHAPES = [

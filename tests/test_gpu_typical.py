@@ -79,6 +79,8 @@ SHAPES = [
     (8, 6, 50000, "bf16", 5.0, 50, 0.01, 0.9),  # very high temperature with top-k
     (32, 3, 9003, "f32", 1.0, 7, 0.0, 0.3),     # eps = 0: the support
     (4, 64, 3000, "bf16", 1.0, 0, 0.002, 0.5),  # long drafts
+    (3, 70, 3000, "bf16", 1.0, 0, 0.002, 0.5),  # positions past the first 64 (a second round of tests)
+    (2, 63, 200000, "bf16", 1.0, 0, 0.1, 0.3),  # 64 rows x 13 chunks: more partials than LDS holds
     (5, 0, 1000, "bf16", 1.0, 0, 0.1, 0.3),     # no drafts: the greedy token
     (3, 2, 1, "f32", 1.0, 0, 0.5, 0.5),         # a single token
 ]
