@@ -142,6 +142,7 @@ SHAPES = [
     (3, 64, 9003, "f32", 0.8, 7, 8),       # 64 nodes, odd V, f32 top-k
     (2, 1, 1000, "bf16", 1.0, 0, 0),       # the root alone: a plain draw
     (3, 10, 600000, "bf16", 1.0, 0, 1),    # 37 chunks a row: chains only (no residual masses)
+    (2, 6, 1100000, "bf16", 1.0, 0, 1),    # 68 chunks a row: more segment masses than the draw's LDS holds
     (2, 12, 300000, "f32", 0.9, 20, 1),    # 37 chunks a row in f32, with top-k
     (2, 12, 262144, "f32", 1.0, 0, 4),     # 32 chunks a row: the longest with several children (one draw item a chunk)
     (2, 12, 200000, "bf16", 1.0, 0, 3),    # 13 chunks a row, several children: two draw items a chunk
