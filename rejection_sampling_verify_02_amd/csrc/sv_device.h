@@ -59,14 +59,42 @@ struct Fmt<float> {
   }
 };
 
+// Rows that do not start on a 16-byte boundary (a bf16 row of odd length, say) are read
+// with the same 16-byte loads: row vector v (row elements v*VEC .. v*VEC + VEC - 1) spans
+// at most two aligned 16-byte blocks, and its offset inside the first, off, is the same
+// for every vector of the row (the row pointer's own offset).  Both blocks are loaded and
+// the vector's 16 bytes taken out of the pair: dword shifts by selects on off's bits, then
+// one v_alignbyte per dword.  The second block is loaded only when it holds a byte of the
+// row (else the first is loaded twice; its bytes then lie past the row's end and are
+// masked by the caller), so every load touches a block that holds row data.
+SVD u32x4 funnel16(const u32x4 &lo, const u32x4 &hi, unsigned off) {
+  const bool s2 = (off & 8u) != 0, s1 = (off & 4u) != 0;
+  const unsigned b = off & 3u;
+  const unsigned q0 = s2 ? lo.z : lo.x, q1 = s2 ? lo.w : lo.y, q2 = s2 ? hi.x : lo.z, q3 = s2 ? hi.y : lo.w,
+                 q4 = s2 ? hi.z : hi.x, q5 = s2 ? hi.w : hi.y;
+  const unsigned r0 = s1 ? q1 : q0, r1 = s1 ? q2 : q1, r2 = s1 ? q3 : q2, r3 = s1 ? q4 : q3, r4 = s1 ? q5 : q4;
+  return u32x4{__builtin_amdgcn_alignbyte(r1, r0, b), __builtin_amdgcn_alignbyte(r2, r1, b),
+               __builtin_amdgcn_alignbyte(r3, r2, b), __builtin_amdgcn_alignbyte(r4, r3, b)};
+}
+// The two blocks of row vector v (v < the row's vector count), loads issued, not waited for.
+template <typename T, bool STREAM>
+SVD void load_pair(const T *row, const T *row_end, unsigned off, int v, u32x4 &lo, u32x4 &hi) {
+  const char *a = reinterpret_cast<const char *>(row + (size_t)v * Fmt<T>::VEC);
+  const u32x4 *p0 = reinterpret_cast<const u32x4 *>(a - off);
+  const u32x4 *p1 = (reinterpret_cast<const char *>(p0 + 1) < reinterpret_cast<const char *>(row_end)) ? p0 + 1 : p0;
+  lo = STREAM ? __builtin_nontemporal_load(p0) : *p0;
+  hi = STREAM ? __builtin_nontemporal_load(p1) : *p1;
+}
+template <typename T>
+SVD unsigned row_off16(const T *row) { return (unsigned)(reinterpret_cast<uintptr_t>(row) & 15u); }
+
 // Vector k of this thread in chunk c is vector c*CHUNK_VECS + k*NT + tid of the row, so
 // one wave's k-th load covers 64 consecutive vectors (a "segment") and segments are in
 // vocabulary order (k-major, then wave).  Elements past the row end read as -inf.
 // Every load is issued before any is used: past the end a load re-reads the row's last
-// vector (or element), and the tail is masked afterwards by a uniform branch.  `mid`
-// runs after the aligned path's loads are issued and before any is waited for, so that
-// loads it issues are in flight with the chunk's (in the element-wise path it runs first:
-// after the element loads it would keep them all live).
+// vector, and the tail is masked afterwards by a uniform branch.  `mid` runs after the
+// loads are issued and before any is waited for, so that loads it issues are in flight
+// with the chunk's.
 struct NoMid {
   SVD void operator()() const {}
 };
@@ -94,16 +122,24 @@ SVD void load_chunk(const T *row, int V, int nvec, int c, int tid, float (&x)[VP
       }
     }
   } else {
+    const unsigned off = row_off16(row);
+    const T *row_end = row + V;
+    u32x4 lo[VPT], hi[VPT];
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const int v = c * CHUNK_VECS + k * NT + tid;
+      load_pair<T, STREAM>(row, row_end, off, v < nvec ? v : nvec - 1, lo[k], hi[k]);
+    }
     mid();
 #pragma unroll
-    for (int k = 0; k < VPT; ++k)
+    for (int k = 0; k < VPT; ++k) Fmt<T>::unpack(funnel16(lo[k], hi[k], off), x[k]);
+    if ((long)(c + 1) * CHUNK_VECS * VEC > V) {  // the row's end: elements past it read as -inf
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const long idx = ((long)c * CHUNK_VECS + (long)k * NT + tid) * VEC + e;
-        const bool in = idx < V;
-        const float z = Fmt<T>::at(row, (size_t)(in ? idx : (long)V - 1));
-        x[k][e] = in ? z : -INFINITY;
-      }
+      for (int k = 0; k < VPT; ++k)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+          x[k][e] = (((long)c * CHUNK_VECS + (long)k * NT + tid) * VEC + e < V) ? x[k][e] : -INFINITY;
+    }
   }
 }
 
@@ -132,15 +168,21 @@ SVD void load_vectors(const T *row, int V, int nvec, int c, int k0, int tid,
       }
     }
   } else {
+    const unsigned off = row_off16(row);
+    const T *row_end = row + V;
+    u32x4 lo[NK], hi[NK];
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+      const int v = c * CHUNK_VECS + (k0 + k) * NT + tid;
+      load_pair<T, STREAM>(row, row_end, off, v < nvec ? v : nvec - 1, lo[k], hi[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < NK; ++k) Fmt<T>::unpack(funnel16(lo[k], hi[k], off), x[k]);
 #pragma unroll
     for (int k = 0; k < NK; ++k)
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const long idx = ((long)c * CHUNK_VECS + (long)(k0 + k) * NT + tid) * VEC + e;
-        const bool in = idx < V;
-        const float z = Fmt<T>::at(row, (size_t)(in ? idx : (long)V - 1));
-        x[k][e] = in ? z : -INFINITY;
-      }
+      for (int e = 0; e < VEC; ++e)
+        x[k][e] = (((long)c * CHUNK_VECS + (long)(k0 + k) * NT + tid) * VEC + e < V) ? x[k][e] : -INFINITY;
   }
 }
 

@@ -133,14 +133,19 @@ SVD int segment_draw(const Args &a, const T *rowA, const T *rowB, int c, int s, 
       xa[e] = in ? xa[e] : -INFINITY;
       xb[e] = (in && rowB) ? xb[e] : -INFINITY;
     }
-  } else {
+  } else {  // the same vector of a row that is not 16-byte aligned (see load_pair)
+    const int v = c * CHUNK_VECS + k * NT + tid_equiv;
+    const int vs = v < a.nvec ? v : a.nvec - 1;
+    u32x4 la, ha, lb, hb;
+    load_pair<T, false>(rowA, rowA + a.V, row_off16(rowA), vs, la, ha);
+    if (rowB) load_pair<T, false>(rowB, rowB + a.V, row_off16(rowB), vs, lb, hb);
+    Fmt<T>::unpack(funnel16(la, ha, row_off16(rowA)), xa);
+    if (rowB) Fmt<T>::unpack(funnel16(lb, hb, row_off16(rowB)), xb);
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-      const long idx = elem_index<T>(c, k, tid_equiv, e);
-      const bool in = idx < a.V;
-      const size_t ii = (size_t)(in ? idx : (long)a.V - 1);
-      xa[e] = in ? Fmt<T>::at(rowA, ii) : -INFINITY;
-      xb[e] = (in && rowB) ? Fmt<T>::at(rowB, ii) : -INFINITY;
+      const bool in = elem_index<T>(c, k, tid_equiv, e) < a.V;
+      xa[e] = in ? xa[e] : -INFINITY;
+      xb[e] = (in && rowB) ? xb[e] : -INFINITY;
     }
   }
   float we[VEC];
