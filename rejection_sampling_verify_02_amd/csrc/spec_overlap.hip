@@ -168,22 +168,7 @@ SVD void ov_second(const Args &a, int u, int c) {
         wb[k] = in ? wb[k] : ninf;
       }
     }
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-      float xa[VEC], xb[VEC];
-      if (ALIGNED) {
-        Fmt<T>::unpack(wa[k], xa);
-        Fmt<T>::unpack(wb[k], xb);
-      } else {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          const long idx = elem_index<T>(c, k, tid, e);
-          const bool in = idx < a.V;
-          const size_t at = (size_t)(in ? idx : (long)a.V - 1);
-          xa[e] = in ? Fmt<T>::at(row_t, at) : -INFINITY;
-          xb[e] = in ? Fmt<T>::at(row_d, at) : -INFINITY;
-        }
-      }
+    auto add_vec = [&](const float (&xa)[VEC], const float (&xb)[VEC]) {
       float tb[VEC];
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
@@ -196,6 +181,27 @@ SVD void ov_second(const Args &a, int u, int c) {
 #pragma unroll
         for (int e = 0; e < h; ++e) tb[e] += tb[e + h];
       acc += tb[0];
+    };
+    if (ALIGNED) {
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) {
+        float xa[VEC], xb[VEC];
+        Fmt<T>::unpack(wa[k], xa);
+        Fmt<T>::unpack(wb[k], xb);
+        add_vec(xa, xb);
+      }
+    } else {
+      // Rows off the 16-byte grid: two vectors of each row at a time (each vector built
+      // from the two aligned blocks that hold it), in the same order.
+      constexpr int KG = 2;
+#pragma unroll
+      for (int k0 = 0; k0 < VPT; k0 += KG) {
+        float xa[KG][VEC], xb[KG][VEC];
+        load_vectors<T, false, true, KG>(row_t, a.V, a.nvec, c, k0, tid, xa);
+        load_vectors<T, false, true, KG>(row_d, a.V, a.nvec, c, k0, tid, xb);
+#pragma unroll
+        for (int kk = 0; kk < KG; ++kk) add_vec(xa[kk], xb[kk]);
+      }
     }
   }
   const double wsum = wave_sum((double)acc);

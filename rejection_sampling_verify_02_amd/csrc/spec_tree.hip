@@ -606,13 +606,14 @@ __global__ __launch_bounds__(NT) void k_tree_draw(const TreeArgs t) {
         if (ALIGNED) {
           Fmt<T>::unpack(wt[ALIGNED ? kk : 0], za);
           Fmt<T>::unpack(wd[ALIGNED ? kk : 0], zb);
-        } else {
+        } else {  // a row off the 16-byte grid: the vector built from the two blocks that hold it
+          float xa[1][VEC], xb[1][VEC];
+          load_vectors<T, false, false, 1>(row_t, a.V, a.nvec, c, kb + kk, tid, xa);
+          load_vectors<T, false, false, 1>(row_d, a.V, a.nvec, c, kb + kk, tid, xb);
 #pragma unroll
           for (int e = 0; e < VEC; ++e) {
-            const long idx = elem_index<T>(c, kb + kk, tid, e);
-            const bool in = idx < a.V;
-            za[e] = in ? Fmt<T>::at(row_t, (size_t)idx) : -INFINITY;
-            zb[e] = in ? Fmt<T>::at(row_d, (size_t)idx) : -INFINITY;
+            za[e] = xa[0][e];
+            zb[e] = xb[0][e];
           }
         }
 #pragma unroll

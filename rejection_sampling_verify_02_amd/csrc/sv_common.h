@@ -473,25 +473,31 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(7))) void k_
         for (int kk = 0; kk < VPT; ++kk)
           if (c * CHUNK_VECS + kk * NT + tid >= a.nvec) w[kk] = u32x4{NEG_INF, NEG_INF, NEG_INF, NEG_INF};
       }
-    } else {
+    } else {  // a row off the 16-byte grid: each vector built from the two blocks that hold it
+      const unsigned off = row_off16(row);
+      u32x4 lo[VPT], hi[VPT];
 #pragma unroll
       for (int kk = 0; kk < VPT; ++kk) {
-        uint32_t h[VEC];
+        const int vi = c * CHUNK_VECS + kk * NT + tid;
+        load_pair<T, true>(row, row + a.V, off, vi < a.nvec ? vi : a.nvec - 1, lo[kk], hi[kk]);
+      }
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          const long idx = elem_index<T>(c, kk, tid, e);
-          h[e] = (idx < a.V) ? __float_as_uint(Fmt<T>::at(row, (size_t)idx)) : 0xff800000u;
-        }
-        if (VEC == 8) {
-          w[kk].x = (h[0] >> 16) | (h[1 % VEC] & 0xffff0000u);
-          w[kk].y = (h[2 % VEC] >> 16) | (h[3 % VEC] & 0xffff0000u);
-          w[kk].z = (h[4 % VEC] >> 16) | (h[5 % VEC] & 0xffff0000u);
-          w[kk].w = (h[6 % VEC] >> 16) | (h[7 % VEC] & 0xffff0000u);
-        } else {
-          w[kk].x = h[0];
-          w[kk].y = h[1 % VEC];
-          w[kk].z = h[2 % VEC];
-          w[kk].w = h[3 % VEC];
+      for (int kk = 0; kk < VPT; ++kk) w[kk] = funnel16(lo[kk], hi[kk], off);
+      if ((long)(c + 1) * CHUNK_VECS * VEC > a.V) {  // the row's tail: elements past its end are -inf
+#pragma unroll
+        for (int kk = 0; kk < VPT; ++kk) {
+          const long i0 = elem_index<T>(c, kk, tid, 0);
+          unsigned d[4] = {w[kk].x, w[kk].y, w[kk].z, w[kk].w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (VEC == 8) {
+              if (i0 + 2 * j >= a.V) d[j] = (d[j] & 0xffff0000u) | 0xff80u;
+              if (i0 + 2 * j + 1 >= a.V) d[j] = (d[j] & 0x0000ffffu) | 0xff800000u;
+            } else if (i0 + j >= a.V) {
+              d[j] = 0xff800000u;
+            }
+          }
+          w[kk] = u32x4{d[0], d[1], d[2], d[3]};
         }
       }
     }
