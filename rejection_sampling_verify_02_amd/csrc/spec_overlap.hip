@@ -121,6 +121,10 @@ SVD void ov_second(const Args &a, int u, int c) {
   // Both chunks' loads are issued first (L2 hits, mostly); the normalisers are gathered
   // while they fly.
   u32x4 wa[ALIGNED ? VPT : 1], wb[ALIGNED ? VPT : 1];
+  // Rows off the 16-byte grid: the first half of both rows' vectors, as the pairs of
+  // aligned blocks that hold them (the same registers as all vectors of aligned rows).
+  constexpr int UH = VPT / 2;
+  u32x4 la[ALIGNED ? 1 : UH], ha[ALIGNED ? 1 : UH], lb[ALIGNED ? 1 : UH], hb[ALIGNED ? 1 : UH];
   if (ALIGNED) {
     const u32x4 *ra = reinterpret_cast<const u32x4 *>(row_t);
     const u32x4 *rb = reinterpret_cast<const u32x4 *>(row_d);
@@ -130,6 +134,14 @@ SVD void ov_second(const Args &a, int u, int c) {
       const int vs = v < a.nvec ? v : a.nvec - 1;
       wa[k] = __builtin_nontemporal_load(ra + vs);
       wb[k] = __builtin_nontemporal_load(rb + vs);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < UH; ++k) {
+      const int v = c * CHUNK_VECS + k * NT + tid;
+      const int vs = v < a.nvec ? v : a.nvec - 1;
+      load_pair<T, true>(row_t, row_t + a.V, row_off16(row_t), vs, la[ALIGNED ? 0 : k], ha[ALIGNED ? 0 : k]);
+      load_pair<T, true>(row_d, row_d + a.V, row_off16(row_d), vs, lb[ALIGNED ? 0 : k], hb[ALIGNED ? 0 : k]);
     }
   }
   if (tid == 0) s_flags = 0;
@@ -191,11 +203,24 @@ SVD void ov_second(const Args &a, int u, int c) {
         add_vec(xa, xb);
       }
     } else {
-      // Rows off the 16-byte grid: two vectors of each row at a time (each vector built
-      // from the two aligned blocks that hold it), in the same order.
+      // Rows off the 16-byte grid: the prefetched half, then two vectors of each row at a
+      // time (each vector built from the two aligned blocks that hold it), in the same order.
+#pragma unroll
+      for (int k = 0; k < UH; ++k) {
+        float xa[VEC], xb[VEC];
+        Fmt<T>::unpack(funnel16(la[ALIGNED ? 0 : k], ha[ALIGNED ? 0 : k], row_off16(row_t)), xa);
+        Fmt<T>::unpack(funnel16(lb[ALIGNED ? 0 : k], hb[ALIGNED ? 0 : k], row_off16(row_d)), xb);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const bool in = elem_index<T>(c, k, tid, e) < a.V;
+          xa[e] = in ? xa[e] : -INFINITY;
+          xb[e] = in ? xb[e] : -INFINITY;
+        }
+        add_vec(xa, xb);
+      }
       constexpr int KG = 2;
 #pragma unroll
-      for (int k0 = 0; k0 < VPT; k0 += KG) {
+      for (int k0 = UH; k0 < VPT; k0 += KG) {
         float xa[KG][VEC], xb[KG][VEC];
         load_vectors<T, false, true, KG>(row_t, a.V, a.nvec, c, k0, tid, xa);
         load_vectors<T, false, true, KG>(row_d, a.V, a.nvec, c, k0, tid, xb);
