@@ -441,3 +441,36 @@ def test_near_identical_rows_reject(dev, shape, sigma):
     print(f"[parity] near-identical {shape} sigma={sigma}: oracle draws within the band {near}, "
           f"of which the GPU drew differently {res.boundary}", flush=True)
     assert res.boundary <= near
+
+
+@pytest.mark.parametrize("dtype,k", [("bf16", 0), ("bf16", 40), ("f32", 0)])
+def test_logits_off_the_16_byte_grid(dev, dtype, k):
+    """Logit buffers whose base lies one element past a 16-byte boundary (rows of aligned
+    length, each starting 2 bytes (bf16) or 4 bytes (f32) into a 16-byte block): every row
+    is read through the unaligned path's block pairs with the same offset, including the
+    first.  Same outputs as the oracle, and the same as the same values on aligned buffers."""
+    import torch
+    import rejection_sampling_verify_02_amd as sv
+    B, G, V = 12, 3, 40000
+    raw = wl.make_random(B, G, V, dtype, seed=811 + k)
+    tok = parity.prepare(raw, 1.0, k)
+    acc_r, out_r, diag = oracle.spec_verify_ref(raw.target, raw.draft, tok, raw.u_accept, raw.u_sample, 1.0, k,
+                                                with_diagnostics=True)
+
+    def shifted(a):
+        t = parity.to_device(a, dev)
+        buf = torch.empty(t.numel() + 8, dtype=t.dtype, device=dev)  # the allocation is 256-byte aligned
+        view = buf[1:1 + t.numel()].view(t.shape)
+        view.copy_(t)
+        return view
+
+    t_s, d_s = shifted(raw.target), shifted(raw.draft)
+    assert t_s.data_ptr() % 16 != 0 and d_s.data_ptr() % 16 != 0
+    rest = [parity.to_device(a, dev) for a in (tok, raw.u_accept, raw.u_sample)]
+    acc_g, out_g = sv.spec_verify(t_s, d_s, *rest, 1.0, k)
+    acc_a, out_a = sv.spec_verify(parity.to_device(raw.target, dev), parity.to_device(raw.draft, dev), *rest, 1.0, k)
+    torch.cuda.synchronize(dev)
+    res = parity.compare(tok, V, 1.0, acc_g.cpu().numpy(), out_g.cpu().numpy(), acc_r, out_r, diag)
+    check(res, f"off-grid logits {dtype} k={k}")
+    np.testing.assert_array_equal(acc_g.cpu().numpy(), acc_a.cpu().numpy())
+    np.testing.assert_array_equal(out_g.cpu().numpy(), out_a.cpu().numpy())
