@@ -367,7 +367,7 @@ def summarize_trace(tdir: str, line_file: str, cmd: str, ref_file: str | None = 
 
 
 def run_timeline(args, dev) -> dict:
-    """Where one headline call's time goes, from the timeline build of the library
+    """Where one call's time goes (B=64, G=4, V=128256 bf16), from the timeline build of the library
     (libspec_verify_timeline.so: the product sources with wall-clock stamps at fixed
     points of each sequence's path).  Per call: when the stream of partials ends, when the
     call's last token is written, and for the sequence that finishes last, each step of its
@@ -796,8 +796,8 @@ def run_sample(args, dev, hev):
 
 
 def run_overlap(args, dev, hev):
-    """beta and tv of every drafted position of the headline batch (B=64, G=4, V=128256
-    bf16, T=1), in the verification layout: positions per second."""
+    """beta and tv of every drafted position of the batch B=64, G=4, V=128256
+    bf16 (T=1), in the verification layout: positions per second."""
     import torch
     import rejection_sampling_verify_02_amd as sv
     from rejection_sampling_verify_02_amd import workloads as wl
@@ -949,7 +949,7 @@ def run_tree(args, dev, hev):
 
 
 def run_typical(args, dev, hev):
-    """Typical acceptance of the headline batch (B=64, G=4, V=128256 bf16, T=1, eps = 0.1,
+    """Typical acceptance of the batch B=64, G=4, V=128256 bf16 (T=1, eps = 0.1,
     delta = 0.3): positions per second."""
     import torch
     import rejection_sampling_verify_02_amd as sv
@@ -1019,10 +1019,10 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--op", default="verify", choices=["verify", "sample", "overlap", "tree", "typical"],
-                    help="verify (the default, the headline), the batched sampler, the per-position overlap, "
+                    help="verify (the default: B=64, G=4, V=128256 bf16), the batched sampler, the per-position overlap, "
                          "tree verification, or typical acceptance")
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5],
-                    help="verification workload (3, the default, is the headline; 4 greedy and 5 top-k "
+                    help="verification workload (3, the default, is B=64, G=4, V=128256 bf16; 4 greedy and 5 top-k "
                          "are timed for the design notes)")
     ap.add_argument("--sets", type=int, default=0, help="input sets to rotate (default: >= 1 GiB)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,

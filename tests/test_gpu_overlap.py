@@ -51,7 +51,7 @@ def run_both(target, draft, T, k, dev, label="", ws=None):
     return g_b, g_t, g_s
 
 
-def test_overlap_headline_workload_full_size(dev):
+def test_overlap_b64_g4_v128256_full_size(dev):
     """B=64, G=4, V=128256 bf16, T=1, in the verification layout (target rows G+1)."""
     raw = wl.make_config(3)
     b, t, _ = run_both(raw.target, raw.draft, 1.0, 0, dev, "zipf_bf16_b64")

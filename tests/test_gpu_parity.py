@@ -420,7 +420,7 @@ def forced_rejections(raw, T, seed):
 
 @pytest.mark.parametrize("shape,sigma", [("c2", 5e-3), ("c2", 5e-4), ("c3", 1e-2), ("c3", 5e-3), ("c3", 5e-4)])
 def test_near_identical_rows_reject(dev, shape, sigma):
-    """Draft = target + N(0, sigma^2) (rounded to bf16 at the headline shape), every
+    """Draft = target + N(0, sigma^2) (rounded to bf16 at B=64, G=4, V=128256), every
     sequence forced to reject: the correction weights [p - q]_+ are then a small difference
     of nearly equal probabilities.  Draws must match the oracle outside the 1e-6 band, as
     everywhere."""

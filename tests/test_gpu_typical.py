@@ -63,7 +63,7 @@ def run_both(target, tok, T, eps, delta, k, dev, label):
     return g_acc, g_out
 
 
-def test_typical_headline_batch(dev):
+def test_typical_b64_g4_v128256(dev):
     """B=64, G=4, V=128256 bf16, T=1, drafts drawn from q, eps = 0.1, delta = 0.3."""
     raw = wl.make_config(3)
     x = prepare(raw, 1.0, 0)

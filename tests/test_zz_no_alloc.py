@@ -43,7 +43,7 @@ def one(dev, raw, T, k):
 
 
 def test_noalloc_matches_spec_verify(dev):
-    acc1 = one(dev, wl.make_config(3), 1.0, 0)                  # the headline batch
+    acc1 = one(dev, wl.make_config(3), 1.0, 0)                  # B=64, G=4, V=128256 bf16
     acc2 = one(dev, wl.make_random(5, 3, 9003, "f32", seed=11), 0.8, 0)  # smaller, right after
     assert np.all(acc1 >= 0) and np.all(acc2 >= 0)
     one(dev, wl.make_random(16, 4, 20001, "bf16", seed=12), 0.0, 0)    # greedy
